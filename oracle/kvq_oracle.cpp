@@ -1,0 +1,431 @@
+/*
+ * kvq_oracle.cpp -- plain CPU oracle (test infrastructure only; see the
+ * header for who may use it, the method it follows and the readings taken).
+ *
+ * Written for clarity, not speed: every step is a direct loop over the
+ * definition.  Floating point of the quantizer is fp32 exactly as the
+ * method's steps state it (built with -ffp-contract=off and no fast-math);
+ * attention is fp64.
+ */
+#include "kvq_oracle.h"
+
+#include <cfenv>
+#include <cmath>
+#include <cstring>
+#include <vector>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+uint32_t bits_of(float x) { uint32_t u; std::memcpy(&u, &x, 4); return u; }
+
+/* Round a finite non-negative double that is exactly a float value to the
+ * floating-point grid with `mant_bits` stored mantissa bits, minimum normal
+ * exponent `emin` and exponent bias `bias`; returns the bit pattern without
+ * sign.  Round to nearest, ties to even (nearbyint under FE_TONEAREST).
+ * Values at or beyond the overflow threshold give infinity. */
+uint32_t round_to_grid(double a, int mant_bits, int emin, int emax, int bias) {
+  if (a == 0.0) return 0;
+  int ex = 0;
+  std::frexp(a, &ex);          /* a = fr * 2^ex, fr in [0.5, 1) */
+  int e = ex - 1;              /* a in [2^e, 2^(e+1)) */
+  if (e < emin) {              /* subnormal: multiples of 2^(emin - mant_bits) */
+    double m = std::nearbyint(std::ldexp(a, mant_bits - emin));
+    return static_cast<uint32_t>(m);  /* m == 2^mant_bits is the smallest normal */
+  }
+  double m = std::nearbyint(std::ldexp(a, mant_bits - e));  /* in [2^mb, 2^(mb+1)] */
+  if (m == std::ldexp(1.0, mant_bits + 1)) { m = std::ldexp(1.0, mant_bits); e += 1; }
+  if (e > emax) return static_cast<uint32_t>((emax + bias + 1)) << mant_bits;  /* inf */
+  uint32_t mant = static_cast<uint32_t>(m) - (1u << mant_bits);
+  return (static_cast<uint32_t>(e + bias) << mant_bits) | mant;
+}
+
+uint16_t f32_to_f16(float x) {
+  uint32_t u = bits_of(x);
+  uint16_t sign = static_cast<uint16_t>((u >> 16) & 0x8000u);
+  if (std::isnan(x)) return sign | 0x7e00u;
+  if (std::isinf(x)) return sign | 0x7c00u;
+  double a = std::fabs(static_cast<double>(x));
+  return sign | static_cast<uint16_t>(round_to_grid(a, 10, -14, 15, 15));
+}
+
+float f16_to_f32(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int ex = (h >> 10) & 0x1f;
+  int mant = h & 0x3ff;
+  double v;
+  if (ex == 0) v = std::ldexp(static_cast<double>(mant), -24);
+  else if (ex == 31) v = mant ? NAN : INFINITY;
+  else v = std::ldexp(static_cast<double>(1024 + mant), ex - 25);
+  return static_cast<float>(sign ? -v : v);
+}
+
+uint16_t f32_to_bf16(float x) {
+  uint32_t u = bits_of(x);
+  uint16_t sign = static_cast<uint16_t>((u >> 16) & 0x8000u);
+  if (std::isnan(x)) return sign | 0x7fc0u;
+  if (std::isinf(x)) return sign | 0x7f80u;
+  double a = std::fabs(static_cast<double>(x));
+  return sign | static_cast<uint16_t>(round_to_grid(a, 7, -126, 127, 127));
+}
+
+float bf16_to_f32(uint16_t h) {
+  uint32_t u = static_cast<uint32_t>(h) << 16;
+  float f; std::memcpy(&f, &u, 4);
+  return f;
+}
+
+float widen(uint16_t h, int dtype) { return dtype == KVQO_F16 ? f16_to_f32(h) : bf16_to_f32(h); }
+
+int popcount(unsigned v) { int c = 0; while (v) { c += v & 1u; v >>= 1; } return c; }
+
+/* Sylvester Hadamard entry (+1 / -1). */
+double hadamard(int i, int j) { return (popcount(static_cast<unsigned>(i & j)) & 1) ? -1.0 : 1.0; }
+
+/* In-place fast Walsh-Hadamard transform of n = 2^k fp32 values; stages
+ * h = 1, 2, 4, ... in ascending order, each pair (a[k], a[k+h]) replaced by
+ * (a[k] + a[k+h], a[k] - a[k+h]). */
+void fwht_f32(float* a, int n) {
+  for (int h = 1; h < n; h *= 2)
+    for (int i = 0; i < n; i += 2 * h)
+      for (int k = i; k < i + h; ++k) {
+        float x = a[k];
+        float y = a[k + h];
+        a[k] = x + y;
+        a[k + h] = x - y;
+      }
+}
+
+/* fp64 block rotation with the explicit matrix: y = blockdiag(H_b/sqrt(b)) x.
+ * H_b is symmetric, so this is also the inverse rotation. */
+void rotate_f64(const double* x, double* y, int d, int b) {
+  if (b <= 1) { for (int i = 0; i < d; ++i) y[i] = x[i]; return; }
+  double s = 1.0 / std::sqrt(static_cast<double>(b));
+  for (int blk = 0; blk < d; blk += b)
+    for (int i = 0; i < b; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < b; ++j) acc += hadamard(i, j) * x[blk + j];
+      y[blk + i] = acc * s;
+    }
+}
+
+size_t int4_slab(int p, int d) { return static_cast<size_t>(p) * (d + 8); }
+size_t bf16_slab(int p, int d) { return static_cast<size_t>(2) * p * d * 2; }
+
+/* Byte address helpers of the INT4 slab (layout text in the header). */
+size_t k_code_byte(int p, int d, int t, int c) { (void)p; return static_cast<size_t>(t) * (d / 2) + c / 2; }
+size_t v_code_byte(int p, int d, int t, int c) {
+  int n = c / 8, j = (c % 8) / 2;
+  return static_cast<size_t>(p) * d / 2 + (static_cast<size_t>(n) * p + t) * 4 + j;
+}
+size_t meta_byte(int p, int d, int kind, int t) {
+  return static_cast<size_t>(p) * d + static_cast<size_t>(kind) * 4 * p + static_cast<size_t>(t) * 4;
+}
+size_t bf16_elem(int p, int d, int kind, int t, int c) {
+  if (kind == 0) return static_cast<size_t>(t) * d + c;
+  int n = c / 8, j = c % 8, g = t / 4, i = t % 4;
+  return static_cast<size_t>(p) * d + ((static_cast<size_t>(n) * (p / 4) + g) * 8 + j) * 4 + i;
+}
+
+void put_u16(uint8_t* b, uint16_t v) { b[0] = static_cast<uint8_t>(v & 0xff); b[1] = static_cast<uint8_t>(v >> 8); }
+uint16_t get_u16(const uint8_t* b) { return static_cast<uint16_t>(b[0] | (b[1] << 8)); }
+
+bool valid_block(int b, int d) { return b == 0 || b == 1 || ((b & (b - 1)) == 0 && b >= 2 && b <= d && d % b == 0); }
+
+}  // namespace
+
+namespace {
+
+/* Shared body of the two paged decode oracles: `read(page, head, off, kind, c)`
+ * returns a decoded fp64 element in the cache's basis; `rot` is the block
+ * size used to rotate q in and the output back (0 = none). */
+template <class Read>
+int32_t decode_paged(Read read, int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t rot, const uint16_t* q, int32_t dtype, int32_t num_q_heads,
+                     const int32_t* block_table, int32_t max_pages_per_seq,
+                     const int32_t* seq_lens, int32_t batch, double sm_scale,
+                     const uint8_t* mask, double* out) {
+  const int d = head_dim, hq = num_q_heads, p = page_size;
+  if (num_kv_heads <= 0 || hq % num_kv_heads != 0) return 1;
+  const int group = hq / num_kv_heads;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < batch; ++b)
+    for (int h = 0; h < hq; ++h) {
+      double* o = out + (static_cast<size_t>(b) * hq + h) * d;
+      for (int c = 0; c < d; ++c) o[c] = 0.0;
+      if (mask && !mask[static_cast<size_t>(b) * hq + h]) continue;
+      const int len = seq_lens[b];
+      if (len <= 0) continue;
+      const int kvh = h / group;
+      std::vector<double> qv(d), qr(d), s(len), orot(d, 0.0);
+      for (int c = 0; c < d; ++c) qv[c] = widen(q[(static_cast<size_t>(b) * hq + h) * d + c], dtype);
+      rotate_f64(qv.data(), qr.data(), d, rot);
+      double mx = -INFINITY;
+      for (int t = 0; t < len; ++t) {
+        const int page = block_table[static_cast<size_t>(b) * max_pages_per_seq + t / p];
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += qr[c] * read(page, kvh, t % p, 0, c);
+        s[t] = sm_scale * dot;
+        if (s[t] > mx) mx = s[t];
+      }
+      double l = 0.0;
+      for (int t = 0; t < len; ++t) { s[t] = std::exp(s[t] - mx); l += s[t]; }
+      for (int t = 0; t < len; ++t) {
+        const int page = block_table[static_cast<size_t>(b) * max_pages_per_seq + t / p];
+        for (int c = 0; c < d; ++c) orot[c] += s[t] * read(page, kvh, t % p, 1, c);
+      }
+      for (int c = 0; c < d; ++c) orot[c] /= l;
+      rotate_f64(orot.data(), o, d, rot);
+    }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint16_t kvq_oracle_f32_to_f16(float x) { return f32_to_f16(x); }
+float kvq_oracle_f16_to_f32(uint16_t h) { return f16_to_f32(h); }
+uint16_t kvq_oracle_f32_to_bf16(float x) { return f32_to_bf16(x); }
+float kvq_oracle_bf16_to_f32(uint16_t h) { return bf16_to_f32(h); }
+
+float kvq_oracle_block_scale(int32_t b) {
+  return static_cast<float>(1.0 / std::sqrt(static_cast<double>(b)));
+}
+
+void kvq_oracle_rotate(const float* x, float* y, int32_t d, int32_t b) {
+  std::vector<float> a(x, x + d);
+  if (b > 1) {
+    float s = kvq_oracle_block_scale(b);
+    for (int blk = 0; blk < d; blk += b) {
+      fwht_f32(&a[blk], b);
+      for (int i = 0; i < b; ++i) a[blk + i] = a[blk + i] * s;
+    }
+  }
+  for (int i = 0; i < d; ++i) y[i] = a[i];
+}
+
+void kvq_oracle_quantize(const float* y, int32_t d, uint8_t* codes, uint16_t* scale,
+                         uint16_t* zero) {
+  std::fesetround(FE_TONEAREST);
+  float mn = y[0], mx = y[0];
+  for (int i = 1; i < d; ++i) {
+    if (y[i] < mn) mn = y[i];
+    if (y[i] > mx) mx = y[i];
+  }
+  float zero_f = mn + 0.0f;
+  float range = (mx - mn) + 0.0f;
+  float step = range / 15.0f;
+  uint16_t sh = f32_to_f16(step);
+  uint16_t zh = f32_to_f16(zero_f);
+  float sf = f16_to_f32(sh);
+  float zf = f16_to_f32(zh);
+  float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+  for (int i = 0; i < d; ++i) {
+    float diff = y[i] - zf;
+    float r = diff * inv;
+    float c = std::nearbyint(r);
+    if (c < 0.0f) c = 0.0f;
+    if (c > 15.0f) c = 15.0f;
+    codes[i] = static_cast<uint8_t>(c);
+  }
+  *scale = sh;
+  *zero = zh;
+}
+
+size_t kvq_oracle_int4_slab_bytes(int32_t page_size, int32_t head_dim) { return int4_slab(page_size, head_dim); }
+size_t kvq_oracle_bf16_slab_bytes(int32_t page_size, int32_t head_dim) { return bf16_slab(page_size, head_dim); }
+
+int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                               const uint16_t* k, const uint16_t* v, int32_t dtype,
+                               int64_t token_stride, const int32_t* slot_mapping,
+                               int32_t num_tokens) {
+  const int p = page_size, d = head_dim, hkv = num_kv_heads;
+  if (!valid_block(block, d) || p % 4 != 0 || d % 8 != 0) return 1;
+  const size_t slab = int4_slab(p, d);
+  const int64_t capacity = static_cast<int64_t>(num_pages) * p;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int t = 0; t < num_tokens; ++t) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= capacity) continue;
+    const int page = static_cast<int>(slot / p), off = static_cast<int>(slot % p);
+    std::vector<float> x(d), y(d);
+    std::vector<uint8_t> codes(d);
+    for (int h = 0; h < hkv; ++h) {
+      uint8_t* s = pool + (static_cast<size_t>(page) * hkv + h) * slab;
+      for (int kind = 0; kind < 2; ++kind) {
+        const uint16_t* src = (kind == 0 ? k : v) + t * token_stride + static_cast<int64_t>(h) * d;
+        for (int c = 0; c < d; ++c) x[c] = widen(src[c], dtype);
+        kvq_oracle_rotate(x.data(), y.data(), d, block);
+        uint16_t sh, zh;
+        kvq_oracle_quantize(y.data(), d, codes.data(), &sh, &zh);
+        for (int c = 0; c < d; c += 2) {
+          uint8_t byte = static_cast<uint8_t>(codes[c] | (codes[c + 1] << 4));
+          size_t at = kind == 0 ? k_code_byte(p, d, off, c) : v_code_byte(p, d, off, c);
+          s[at] = byte;
+        }
+        put_u16(s + meta_byte(p, d, kind, off), sh);
+        put_u16(s + meta_byte(p, d, kind, off) + 2, zh);
+      }
+    }
+  }
+  return 0;
+}
+
+int32_t kvq_oracle_append_bf16(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               const uint16_t* k, const uint16_t* v, int32_t dtype,
+                               int64_t token_stride, const int32_t* slot_mapping,
+                               int32_t num_tokens) {
+  const int p = page_size, d = head_dim, hkv = num_kv_heads;
+  if (p % 4 != 0 || d % 8 != 0) return 1;
+  const size_t slab = bf16_slab(p, d);
+  const int64_t capacity = static_cast<int64_t>(num_pages) * p;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int t = 0; t < num_tokens; ++t) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= capacity) continue;
+    const int page = static_cast<int>(slot / p), off = static_cast<int>(slot % p);
+    for (int h = 0; h < hkv; ++h) {
+      uint8_t* s = pool + (static_cast<size_t>(page) * hkv + h) * slab;
+      for (int kind = 0; kind < 2; ++kind) {
+        const uint16_t* src = (kind == 0 ? k : v) + t * token_stride + static_cast<int64_t>(h) * d;
+        for (int c = 0; c < d; ++c) {
+          uint16_t b16 = dtype == KVQO_BF16 ? src[c] : f32_to_bf16(f16_to_f32(src[c]));
+          put_u16(s + 2 * bf16_elem(p, d, kind, off, c), b16);
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+double kvq_oracle_int4_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t page, int32_t head, int32_t off,
+                            int32_t kind, int32_t channel, int32_t* code, uint16_t* scale,
+                            uint16_t* zero) {
+  const int p = page_size, d = head_dim;
+  const uint8_t* s = pool + (static_cast<size_t>(page) * num_kv_heads + head) * int4_slab(p, d);
+  size_t at = kind == 0 ? k_code_byte(p, d, off, channel) : v_code_byte(p, d, off, channel);
+  int c = (channel % 2 == 0) ? (s[at] & 0xf) : (s[at] >> 4);
+  uint16_t sh = get_u16(s + meta_byte(p, d, kind, off));
+  uint16_t zh = get_u16(s + meta_byte(p, d, kind, off) + 2);
+  if (code) *code = c;
+  if (scale) *scale = sh;
+  if (zero) *zero = zh;
+  return static_cast<double>(c) * static_cast<double>(f16_to_f32(sh)) +
+         static_cast<double>(f16_to_f32(zh));
+}
+
+double kvq_oracle_bf16_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t page, int32_t head, int32_t off,
+                            int32_t kind, int32_t channel) {
+  const int p = page_size, d = head_dim;
+  const uint8_t* s = pool + (static_cast<size_t>(page) * num_kv_heads + head) * bf16_slab(p, d);
+  return static_cast<double>(bf16_to_f32(get_u16(s + 2 * bf16_elem(p, d, kind, off, channel))));
+}
+
+
+int32_t kvq_oracle_decode_int4(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block, const uint16_t* q, int32_t dtype,
+                               int32_t num_q_heads, const int32_t* block_table,
+                               int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                               double sm_scale, const uint8_t* mask, double* out) {
+  if (!valid_block(block, head_dim)) return 1;
+  auto read = [&](int page, int head, int off, int kind, int c) {
+    return kvq_oracle_int4_read(pool, page_size, num_kv_heads, head_dim, page, head, off, kind, c,
+                                nullptr, nullptr, nullptr);
+  };
+  return decode_paged(read, page_size, num_kv_heads, head_dim, block, q, dtype, num_q_heads,
+                      block_table, max_pages_per_seq, seq_lens, batch, sm_scale, mask, out);
+}
+
+int32_t kvq_oracle_decode_bf16(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                               int32_t head_dim, const uint16_t* q, int32_t dtype,
+                               int32_t num_q_heads, const int32_t* block_table,
+                               int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                               double sm_scale, const uint8_t* mask, double* out) {
+  auto read = [&](int page, int head, int off, int kind, int c) {
+    return kvq_oracle_bf16_read(pool, page_size, num_kv_heads, head_dim, page, head, off, kind, c);
+  };
+  return decode_paged(read, page_size, num_kv_heads, head_dim, 0, q, dtype, num_q_heads,
+                      block_table, max_pages_per_seq, seq_lens, batch, sm_scale, mask, out);
+}
+
+int32_t kvq_oracle_decode_int4_bruteforce(const uint8_t* pool, int32_t page_size,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                                          const uint16_t* q, int32_t dtype, int32_t num_q_heads,
+                                          const int32_t* block_table, int32_t max_pages_per_seq,
+                                          const int32_t* seq_lens, int32_t batch, double sm_scale,
+                                          double* out) {
+  const int d = head_dim, hq = num_q_heads, p = page_size;
+  if (!valid_block(block, d) || num_kv_heads <= 0 || hq % num_kv_heads != 0) return 1;
+  const int group = hq / num_kv_heads;
+  /* the explicit inverse rotation matrix, dense d x d */
+  std::vector<double> rinv(static_cast<size_t>(d) * d, 0.0);
+  for (int i = 0; i < d; ++i) {
+    if (block <= 1) { rinv[static_cast<size_t>(i) * d + i] = 1.0; continue; }
+    int blk = i / block;
+    for (int j = 0; j < block; ++j)
+      rinv[static_cast<size_t>(i) * d + blk * block + j] =
+          hadamard(j, i % block) / std::sqrt(static_cast<double>(block));
+  }
+  for (int b = 0; b < batch; ++b) {
+    const int len = seq_lens[b];
+    for (int h = 0; h < hq; ++h) {
+      double* o = out + (static_cast<size_t>(b) * hq + h) * d;
+      for (int c = 0; c < d; ++c) o[c] = 0.0;
+      if (len <= 0) continue;
+      const int kvh = h / group;
+      /* gather + un-rotate */
+      std::vector<double> kk(static_cast<size_t>(len) * d), vv(static_cast<size_t>(len) * d);
+      std::vector<double> rk(d), rv(d);
+      for (int t = 0; t < len; ++t) {
+        const int page = block_table[static_cast<size_t>(b) * max_pages_per_seq + t / p];
+        for (int c = 0; c < d; ++c) {
+          rk[c] = kvq_oracle_int4_read(pool, p, num_kv_heads, d, page, kvh, t % p, 0, c, nullptr, nullptr, nullptr);
+          rv[c] = kvq_oracle_int4_read(pool, p, num_kv_heads, d, page, kvh, t % p, 1, c, nullptr, nullptr, nullptr);
+        }
+        for (int i = 0; i < d; ++i) {
+          double ak = 0.0, av = 0.0;
+          for (int j = 0; j < d; ++j) {
+            ak += rinv[static_cast<size_t>(i) * d + j] * rk[j];
+            av += rinv[static_cast<size_t>(i) * d + j] * rv[j];
+          }
+          kk[static_cast<size_t>(t) * d + i] = ak;
+          vv[static_cast<size_t>(t) * d + i] = av;
+        }
+      }
+      std::vector<double> qv(d), sc(len);
+      for (int c = 0; c < d; ++c) qv[c] = widen(q[(static_cast<size_t>(b) * hq + h) * d + c], dtype);
+      double mx = -INFINITY;
+      for (int t = 0; t < len; ++t) {
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += qv[c] * kk[static_cast<size_t>(t) * d + c];
+        sc[t] = sm_scale * dot;
+        mx = sc[t] > mx ? sc[t] : mx;
+      }
+      double l = 0.0;
+      for (int t = 0; t < len; ++t) { sc[t] = std::exp(sc[t] - mx); l += sc[t]; }
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int t = 0; t < len; ++t) acc += sc[t] * vv[static_cast<size_t>(t) * d + c];
+        o[c] = acc / l;
+      }
+    }
+  }
+  return 0;
+}
+
+int32_t kvq_oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+}  // extern "C"

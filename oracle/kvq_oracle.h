@@ -1,0 +1,161 @@
+/*
+ * kvq_oracle.h -- plain, slow CPU oracle for the Hadamard-rotated token-wise
+ * INT4 paged KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this library: only the test suite, the package smoke check
+ * and the benchmark's CPU-baseline leg do.  It shares no code, header, table
+ * or constant with the GPU library; it is written from the method's
+ * description alone.
+ *
+ * Method (what is computed):
+ *   - "SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for Real-World LLM
+ *     Serving" (summary page, Research Findings; idea page, Core Innovation):
+ *     each new key/value vector is rotated by a block-diagonal Hadamard
+ *     matrix and then quantized to 4 bits with one quantization group per
+ *     token (per token and KV head); the kernel that does this writes
+ *     straight into a paged KV-cache layout, and attention runs fused over
+ *     the quantized paged cache.
+ *   - "InnerQ" (Table 3): scale factors and zero points are kept as FP16.
+ *   - "BitDecoding-FP4" (Abstract): Hadamard rotation is one of the tools
+ *     that suppresses key outliers under token-wise scaling.
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes of the repository):
+ *   R1  group = all head_dim channels of one (token, KV head, K|V) vector.
+ *   R2  asymmetric: x_hat = code * scale + zero, zero = min, codes 0..15,
+ *       scale = (max - min) / 15, both rounded to FP16 (round to nearest even).
+ *   R3  Hadamard: Sylvester order H[i][j] = (-1)^popcount(i & j), block size b
+ *       on contiguous channel blocks, normalised by the fp32 constant 1/sqrt(b);
+ *       the fp32 butterfly runs stages h = 1, 2, 4, ..., b/2 in that order and
+ *       the scale is applied after the last stage.  b = 0 means no rotation
+ *       (plain INT4).
+ *   R4  code = clamp(round_half_even((y - zero) * (1 / scale)), 0, 15), with
+ *       1/scale and each product/difference rounded separately in fp32; a
+ *       zero scale gives 1/scale = 0 (all codes 0).
+ *   R5  the signed zero of min and of (max - min) is made +0 by adding +0.0f.
+ *   R6  the query is rotated by the same block Hadamard so q.k is preserved;
+ *       the attention output is returned in the original (un-rotated) basis.
+ *   R7  softmax scale is a parameter (normally 1/sqrt(head_dim)); grouped
+ *       query attention maps query head h to KV head h / (Hq / Hkv); an empty
+ *       sequence gives a zero output; slot < 0 means "do not store".
+ *
+ * Cache layout (the on-device format; both implementations follow this text):
+ *   page size P = 16 tokens, head_dim D in {64, 128}.
+ *   INT4 pool: [num_pages][num_kv_heads][slab], slab = P * (D + 8) bytes:
+ *     bytes [0, P*D/2)        K codes, token-major: byte t*(D/2) + j holds
+ *                             channel 2j in bits 0..3 and 2j+1 in bits 4..7.
+ *     bytes [P*D/2, P*D)      V codes, channel-group-major: the 4-byte word
+ *                             index n*P + t (n = 0 .. D/8-1) holds channels
+ *                             8n .. 8n+7 of token t; its byte j holds channel
+ *                             8n+2j in bits 0..3 and 8n+2j+1 in bits 4..7.
+ *     bytes [P*D, P*D+4P)     K sidecar: token t -> fp16 scale at 4t, fp16 zero
+ *                             at 4t+2 (little endian).
+ *     bytes [P*D+4P, P*D+8P)  V sidecar, same form.
+ *   bf16 pool: [num_pages][num_kv_heads][slab], slab = 2 * P * D * 2 bytes:
+ *     K: bf16 element index t*D + c (token-major);
+ *     V: bf16 element index P*D + ((n*(P/4) + g)*8 + j)*4 + i for channel
+ *        c = 8n + j and token t = 4g + i.
+ *   A token in slot s lives in page s / P at offset s % P.
+ */
+#ifndef KVQ_ORACLE_H
+#define KVQ_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of k, v and q inputs: 0 = fp16, 1 = bf16 (bit patterns) */
+enum { KVQO_F16 = 0, KVQO_BF16 = 1 };
+
+/* ---- scalar formats -------------------------------------------------- */
+uint16_t kvq_oracle_f32_to_f16(float x);    /* round to nearest even      */
+float    kvq_oracle_f16_to_f32(uint16_t h); /* exact                      */
+uint16_t kvq_oracle_f32_to_bf16(float x);   /* round to nearest even      */
+float    kvq_oracle_bf16_to_f32(uint16_t h);/* exact                      */
+
+/* fp32 normalisation constant of a Hadamard block (1/sqrt(b) in fp32). */
+float kvq_oracle_block_scale(int32_t b);
+
+/* ---- per-vector steps ------------------------------------------------ */
+/* y = blockdiag(H_b / sqrt(b)) x in fp32 with the butterfly of R3.  b = 0
+ * (or 1) copies x.  x and y may alias. */
+void kvq_oracle_rotate(const float* x, float* y, int32_t d, int32_t b);
+
+/* Token-wise asymmetric INT4 of one vector (R2, R4, R5): codes[d] in 0..15
+ * (one per byte, unpacked), fp16 bit patterns of scale and zero. */
+void kvq_oracle_quantize(const float* y, int32_t d, uint8_t* codes,
+                         uint16_t* scale, uint16_t* zero);
+
+/* ---- cache steps ----------------------------------------------------- */
+size_t kvq_oracle_int4_slab_bytes(int32_t page_size, int32_t head_dim);
+size_t kvq_oracle_bf16_slab_bytes(int32_t page_size, int32_t head_dim);
+
+/* Rotate + quantize + scatter num_tokens tokens into the INT4 pool.
+ * k, v: [num_tokens][token_stride] 16-bit elements of type dtype, the first
+ * num_kv_heads*head_dim of each token used as [num_kv_heads][head_dim]. */
+int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                               const uint16_t* k, const uint16_t* v, int32_t dtype,
+                               int64_t token_stride, const int32_t* slot_mapping,
+                               int32_t num_tokens);
+
+/* Copy num_tokens tokens into the bf16 pool (fp16 input is rounded to bf16). */
+int32_t kvq_oracle_append_bf16(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               const uint16_t* k, const uint16_t* v, int32_t dtype,
+                               int64_t token_stride, const int32_t* slot_mapping,
+                               int32_t num_tokens);
+
+/* Read back one decoded element (fp64) of the INT4 pool: kind 0 = K, 1 = V.
+ * Returns code*scale + zero in the rotated basis; code, scale, zero out-params
+ * may be NULL. */
+double kvq_oracle_int4_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t page, int32_t head, int32_t off,
+                            int32_t kind, int32_t channel, int32_t* code,
+                            uint16_t* scale, uint16_t* zero);
+double kvq_oracle_bf16_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t page, int32_t head, int32_t off,
+                            int32_t kind, int32_t channel);
+
+/* Exact softmax attention in fp64 for one query token per sequence over the
+ * paged INT4 cache (R6, R7).  q: [batch][num_q_heads][head_dim] 16-bit of
+ * type dtype.  block_table: [batch][max_pages_per_seq].  out: fp64
+ * [batch][num_q_heads][head_dim].  Only the (b, h) pairs with
+ * mask == NULL or mask[b*num_q_heads + h] != 0 are computed (others are 0). */
+int32_t kvq_oracle_decode_int4(const uint8_t* pool, int32_t page_size,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                               const uint16_t* q, int32_t dtype, int32_t num_q_heads,
+                               const int32_t* block_table, int32_t max_pages_per_seq,
+                               const int32_t* seq_lens, int32_t batch, double sm_scale,
+                               const uint8_t* mask, double* out);
+
+/* The same over the bf16 pool (no rotation). */
+int32_t kvq_oracle_decode_bf16(const uint8_t* pool, int32_t page_size,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               const uint16_t* q, int32_t dtype, int32_t num_q_heads,
+                               const int32_t* block_table, int32_t max_pages_per_seq,
+                               const int32_t* seq_lens, int32_t batch, double sm_scale,
+                               const uint8_t* mask, double* out);
+
+/* Brute-force twin of kvq_oracle_decode_int4: gathers each sequence's keys and
+ * values into contiguous fp64 rows, rotates every decoded row back with the
+ * explicit matrix (H_b/sqrt(b))^T, and attends with the un-rotated query.  A
+ * separate code path, meant for tiny inputs. */
+int32_t kvq_oracle_decode_int4_bruteforce(const uint8_t* pool, int32_t page_size,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block, const uint16_t* q, int32_t dtype,
+                                          int32_t num_q_heads, const int32_t* block_table,
+                                          int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                          int32_t batch, double sm_scale, double* out);
+
+/* Number of OpenMP threads the oracle uses (for the CPU-baseline report). */
+int32_t kvq_oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
