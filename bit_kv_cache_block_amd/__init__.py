@@ -1,0 +1,244 @@
+"""Python binding of libkvq.so (include/kvq.h): Hadamard-rotated token-wise
+INT4 paged KV cache for MI355X (gfx950).
+
+Argument marshalling only: torch tensors are passed as device pointers and the
+current torch stream; every step of the write and read paths runs in the HIP
+kernels of libkvq.so.  There is no fallback: if the library is missing, every
+call raises.
+
+Entry points carry the C names: ``kvq_append_paged``, ``kvq_decode_attn``,
+``kvq_append_paged_bf16``, ``kvq_decode_attn_bf16``,
+``kvq_decode_workspace_bytes``, ``kvq_int4_page_bytes``, ``kvq_bf16_page_bytes``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_INVALID_ARGUMENT, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE_TOO_SMALL, KVQ_ERR_HIP = range(5)
+KVQ_F16, KVQ_BF16 = 0, 1
+PAGE_SIZE = 16
+
+# every symbol include/kvq.h declares
+EXPORTED = (
+    "kvq_int4_page_bytes", "kvq_bf16_page_bytes", "kvq_append_paged", "kvq_decode_attn",
+    "kvq_decode_workspace_bytes", "kvq_append_paged_bf16", "kvq_decode_attn_bf16",
+    "kvq_status_string", "kvq_last_error", "kvq_abi_version",
+)
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class _Int4Desc(C.Structure):
+    _fields_ = [("pool", C.c_void_p), ("num_pages", C.c_int32), ("page_size", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("hadamard_block", C.c_int32)]
+
+
+class _Bf16Desc(C.Structure):
+    _fields_ = [("pool", C.c_void_p), ("num_pages", C.c_int32), ("page_size", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32)]
+
+
+_lib_handle = None
+
+
+def lib() -> C.CDLL:
+    """The loaded libkvq.so (raises if it was not built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"libkvq.so not found at {LIB_PATH}: build it with "
+                "`python -m bit_kv_cache_block_amd.build` (no CPU fallback exists)")
+        L = C.CDLL(LIB_PATH)
+        p, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        L.kvq_int4_page_bytes.argtypes = [i32, i32, i32]
+        L.kvq_int4_page_bytes.restype = sz
+        L.kvq_bf16_page_bytes.argtypes = [i32, i32, i32]
+        L.kvq_bf16_page_bytes.restype = sz
+        L.kvq_append_paged.argtypes = [C.POINTER(_Int4Desc), p, p, i32, i64, p, i32, p]
+        L.kvq_append_paged.restype = i32
+        L.kvq_append_paged_bf16.argtypes = [C.POINTER(_Bf16Desc), p, p, i32, i64, p, i32, p]
+        L.kvq_append_paged_bf16.restype = i32
+        dec = [p, i32, i32, p, i32, p, i32, i32, C.c_float, i32, p, p, sz, p]
+        L.kvq_decode_attn.argtypes = [C.POINTER(_Int4Desc), *dec]
+        L.kvq_decode_attn.restype = i32
+        L.kvq_decode_attn_bf16.argtypes = [C.POINTER(_Bf16Desc), *dec]
+        L.kvq_decode_attn_bf16.restype = i32
+        L.kvq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.kvq_decode_workspace_bytes.restype = sz
+        L.kvq_status_string.argtypes = [i32]
+        L.kvq_status_string.restype = C.c_char_p
+        L.kvq_last_error.argtypes = []
+        L.kvq_last_error.restype = C.c_char_p
+        L.kvq_abi_version.argtypes = []
+        L.kvq_abi_version.restype = i32
+        _lib_handle = L
+    return _lib_handle
+
+
+def _check(status: int) -> None:
+    if status != KVQ_OK:
+        L = lib()
+        name = L.kvq_status_string(status).decode()
+        raise KvqError(status, f"{name}: {L.kvq_last_error().decode()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return KVQ_F16
+    if t.dtype == torch.bfloat16:
+        return KVQ_BF16
+    raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+
+
+def _stream(stream, device) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> C.c_void_p:
+    return C.c_void_p(0 if t is None else t.data_ptr())
+
+
+def kvq_int4_page_bytes(page_size: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(lib().kvq_int4_page_bytes(page_size, num_kv_heads, head_dim))
+
+
+def kvq_bf16_page_bytes(page_size: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(lib().kvq_bf16_page_bytes(page_size, num_kv_heads, head_dim))
+
+
+class Int4Cache:
+    """Caller-owned INT4 page pool (uint8 tensor [num_pages][page bytes])."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int, hadamard_block: int,
+                 device="cuda", page_size: int = PAGE_SIZE, pool: torch.Tensor | None = None):
+        self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
+        self.hadamard_block, self.page_size = hadamard_block, page_size
+        nbytes = kvq_int4_page_bytes(page_size, num_kv_heads, head_dim)
+        if pool is None:
+            pool = torch.zeros((num_pages, nbytes), dtype=torch.uint8, device=device)
+        if pool.numel() < num_pages * nbytes or pool.dtype != torch.uint8 or not pool.is_contiguous():
+            raise ValueError("pool must be a contiguous uint8 tensor of num_pages * page bytes")
+        self.pool = pool
+
+    def desc(self) -> _Int4Desc:
+        return _Int4Desc(self.pool.data_ptr(), self.num_pages, self.page_size, self.num_kv_heads,
+                         self.head_dim, self.hadamard_block)
+
+
+class Bf16Cache:
+    """Caller-owned bf16 page pool (uint8 tensor [num_pages][page bytes])."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int, device="cuda",
+                 page_size: int = PAGE_SIZE, pool: torch.Tensor | None = None):
+        self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
+        self.page_size = page_size
+        nbytes = kvq_bf16_page_bytes(page_size, num_kv_heads, head_dim)
+        if pool is None:
+            pool = torch.zeros((num_pages, nbytes), dtype=torch.uint8, device=device)
+        if pool.numel() < num_pages * nbytes or pool.dtype != torch.uint8 or not pool.is_contiguous():
+            raise ValueError("pool must be a contiguous uint8 tensor of num_pages * page bytes")
+        self.pool = pool
+
+    def desc(self) -> _Bf16Desc:
+        return _Bf16Desc(self.pool.data_ptr(), self.num_pages, self.page_size, self.num_kv_heads,
+                         self.head_dim)
+
+
+def _token_stride(k: torch.Tensor, v: torch.Tensor, hkv: int, d: int) -> int:
+    for t in (k, v):
+        if t.dim() != 3 or t.shape[1] != hkv or t.shape[2] != d:
+            raise ValueError(f"k/v must be [T][{hkv}][{d}], got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError("each token's [Hkv][D] block of k/v must be contiguous")
+    if k.stride(0) != v.stride(0) or k.dtype != v.dtype or k.shape[0] != v.shape[0]:
+        raise ValueError("k and v must share shape, dtype and token stride")
+    return int(k.stride(0))
+
+
+def _append(fn, desc, hkv, d, k, v, slot_mapping, stream):
+    stride = _token_stride(k, v, hkv, d)
+    if slot_mapping.dtype != torch.int32 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int32 tensor")
+    _check(fn(C.byref(desc), _ptr(k), _ptr(v), _dtype_code(k), stride, _ptr(slot_mapping),
+              int(k.shape[0]), _stream(stream, k.device)))
+
+
+def kvq_append_paged(cache: Int4Cache, k: torch.Tensor, v: torch.Tensor,
+                     slot_mapping: torch.Tensor, stream=None) -> None:
+    """Rotate + quantize + scatter new tokens (k, v: [T][Hkv][D] fp16/bf16)."""
+    _append(lib().kvq_append_paged, cache.desc(), cache.num_kv_heads, cache.head_dim, k, v,
+            slot_mapping, stream)
+
+
+def kvq_append_paged_bf16(cache: Bf16Cache, k: torch.Tensor, v: torch.Tensor,
+                          slot_mapping: torch.Tensor, stream=None) -> None:
+    _append(lib().kvq_append_paged_bf16, cache.desc(), cache.num_kv_heads, cache.head_dim, k, v,
+            slot_mapping, stream)
+
+
+def kvq_decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                               max_seq_len: int, num_splits: int = 0) -> int:
+    return int(lib().kvq_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                max_seq_len, num_splits))
+
+
+def _decode(fn, desc, hkv, d, q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace,
+            num_splits, stream):
+    if q.dim() != 3 or q.shape[2] != d or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][Hq][D] tensor")
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor")
+    need = kvq_decode_workspace_bytes(batch, hq, hkv, d, max_seq_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(fn(C.byref(desc), _ptr(q), _dtype_code(q), hq, _ptr(block_table),
+              int(block_table.shape[1]), _ptr(seq_lens), batch, int(max_seq_len),
+              float(sm_scale), int(num_splits), _ptr(out), _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
+    return out
+
+
+def kvq_decode_attn(cache: Int4Cache, q: torch.Tensor, block_table: torch.Tensor,
+                    seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float | None = None,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    num_splits: int = 0, stream=None) -> torch.Tensor:
+    """Paged decode attention over the INT4 cache; returns fp32 [B][Hq][D]."""
+    return _decode(lib().kvq_decode_attn, cache.desc(), cache.num_kv_heads, cache.head_dim, q,
+                   block_table, seq_lens, max_seq_len, sm_scale, out, workspace, num_splits,
+                   stream)
+
+
+def kvq_decode_attn_bf16(cache: Bf16Cache, q: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float | None = None,
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         num_splits: int = 0, stream=None) -> torch.Tensor:
+    return _decode(lib().kvq_decode_attn_bf16, cache.desc(), cache.num_kv_heads, cache.head_dim,
+                   q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace, num_splits,
+                   stream)
+
+
+def abi_version() -> int:
+    return int(lib().kvq_abi_version())

@@ -1,0 +1,280 @@
+// C ABI of libkvq.so (declared in include/kvq.h): host-side validation, split
+// planning and dispatch.  Nothing here allocates device memory or
+// synchronizes; every launch goes to the caller's stream.
+#include "../../include/kvq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kvq_internal.hpp"
+
+namespace kvq {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+kvq_status check_geometry(int32_t num_pages, int32_t page_size, int32_t hkv, int32_t d) {
+  if (num_pages <= 0 || hkv <= 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "num_pages and num_kv_heads must be > 0");
+  if (page_size != 16) return fail(KVQ_ERR_UNSUPPORTED, "page_size %d unsupported (only 16)", page_size);
+  if (d != 64 && d != 128) return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d);
+  return KVQ_OK;
+}
+
+kvq_status check_append(const void* pool, const void* k, const void* v, kvq_dtype dtype,
+                        int64_t token_stride, const int32_t* slot_mapping, int32_t num_tokens,
+                        int32_t hkv, int32_t d) {
+  if (num_tokens < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+  if (dtype != KVQ_F16 && dtype != KVQ_BF16) return fail(KVQ_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+  if (pool == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache pool is null");
+  if (!aligned16(pool)) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache pool not 16-byte aligned");
+  if (num_tokens == 0) return KVQ_OK;
+  if (!k || !v || !slot_mapping) return fail(KVQ_ERR_INVALID_ARGUMENT, "k, v or slot_mapping is null");
+  if (!aligned16(k) || !aligned16(v)) return fail(KVQ_ERR_INVALID_ARGUMENT, "k or v not 16-byte aligned");
+  if (!aligned4(slot_mapping)) return fail(KVQ_ERR_INVALID_ARGUMENT, "slot_mapping not 4-byte aligned");
+  if (token_stride < static_cast<int64_t>(hkv) * d)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "token_stride %lld < num_kv_heads*head_dim", (long long)token_stride);
+  if (token_stride % 8 != 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "token_stride must be a multiple of 8 elements");
+  return KVQ_OK;
+}
+
+kvq_status check_decode(const void* pool, const void* q, kvq_dtype dtype, int32_t hq, int32_t hkv,
+                        const int32_t* block_table, int32_t max_pages_per_seq,
+                        const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                        float sm_scale, int32_t num_splits, const float* out) {
+  if (dtype != KVQ_F16 && dtype != KVQ_BF16) return fail(KVQ_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+  if (batch < 0 || max_seq_len < 0 || num_splits < 0)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "batch, max_seq_len and num_splits must be >= 0");
+  if (hq <= 0 || hq % hkv != 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "num_q_heads %d not a multiple of num_kv_heads %d", hq, hkv);
+  if (hq / hkv > 16) return fail(KVQ_ERR_UNSUPPORTED, "query group size %d > 16 unsupported", hq / hkv);
+  if (!std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARGUMENT, "sm_scale not finite");
+  if (pool == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache pool is null");
+  if (!aligned16(pool)) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache pool not 16-byte aligned");
+  if (batch == 0) return KVQ_OK;
+  if (!q || !block_table || !seq_lens || !out) return fail(KVQ_ERR_INVALID_ARGUMENT, "q, block_table, seq_lens or out is null");
+  if (!aligned16(q) || !aligned16(out)) return fail(KVQ_ERR_INVALID_ARGUMENT, "q or out not 16-byte aligned");
+  if (!aligned4(block_table) || !aligned4(seq_lens)) return fail(KVQ_ERR_INVALID_ARGUMENT, "block_table or seq_lens misaligned");
+  if (max_pages_per_seq <= 0 || static_cast<int64_t>(max_pages_per_seq) * 16 < max_seq_len)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "max_pages_per_seq*16 < max_seq_len");
+  return KVQ_OK;
+}
+
+}  // namespace
+
+SplitPlan plan_splits(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t num_splits) {
+  const int32_t pages_max = (max_seq_len + 15) / 16;
+  if (pages_max <= 0) return SplitPlan{4, 1};
+  int64_t s;
+  if (num_splits > 0) {
+    s = num_splits;
+  } else {
+    // enough waves for 256 CUs x 8 resident waves; splits no longer than 256
+    // pages (4096 tokens) so ragged batches stay balanced; at least 16 pages each
+    const int64_t units = static_cast<int64_t>(batch > 0 ? batch : 1) * hkv;
+    s = (2048 + units - 1) / units;
+    const int64_t by_len = (pages_max + 255) / 256;
+    if (s < by_len) s = by_len;
+    const int64_t min_len = (pages_max + 15) / 16;
+    if (s > min_len) s = min_len;
+  }
+  const int64_t max_s = (pages_max + 3) / 4;   // at least one 4-page step per split
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  int64_t sp = (pages_max + s - 1) / s;
+  sp = (sp + 3) / 4 * 4;
+  s = (pages_max + sp - 1) / sp;
+  return SplitPlan{static_cast<int32_t>(sp), static_cast<int32_t>(s)};
+}
+
+size_t workspace_bytes(int32_t batch, int32_t hq, int32_t d, const SplitPlan& p) {
+  return static_cast<size_t>(batch) * hq * p.nsplit * (d + 2) * sizeof(float);
+}
+
+namespace {
+
+kvq_status launch_decode(bool int4, const void* pool, int32_t num_pages, int32_t hkv, int32_t d,
+                         int32_t block, const void* q, kvq_dtype dtype, int32_t hq,
+                         const int32_t* block_table, int32_t max_pages_per_seq,
+                         const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                         float sm_scale, int32_t num_splits, float* out, void* workspace,
+                         size_t workspace_bytes_given, void* stream) {
+  kvq_status st = check_decode(pool, q, dtype, hq, hkv, block_table, max_pages_per_seq, seq_lens,
+                               batch, max_seq_len, sm_scale, num_splits, out);
+  if (st != KVQ_OK || batch == 0) return st;
+  const SplitPlan plan = plan_splits(batch, hkv, max_seq_len, num_splits);
+  const size_t need = workspace_bytes(batch, hq, d, plan);
+  if (workspace_bytes_given < need)
+    return fail(KVQ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes_given, need);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace)))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "workspace null or not 16-byte aligned");
+  DecodeArgs a{};
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.q = static_cast<const uint16_t*>(q);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.part_acc = static_cast<float*>(workspace);
+  a.part_ml = static_cast<float*>(workspace) + static_cast<size_t>(batch) * hq * plan.nsplit * d;
+  a.num_pages = num_pages;
+  a.num_kv_heads = hkv;
+  a.num_q_heads = hq;
+  a.head_dim = d;
+  a.block = block;
+  a.bt_stride = max_pages_per_seq;
+  a.batch = batch;
+  a.max_seq_len = max_seq_len;
+  a.split_pages = plan.split_pages;
+  a.nsplit = plan.nsplit;
+  a.sm_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  a.in_bf16 = dtype == KVQ_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = int4 ? launch_decode_int4(a, s) : launch_decode_bf16(a, s);
+  if (e == hipSuccess) e = launch_reduce(a, s);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+size_t kvq_int4_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim) {
+  if (page_size <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  return static_cast<size_t>(num_kv_heads) * page_size * (head_dim + 8);
+}
+
+size_t kvq_bf16_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim) {
+  if (page_size <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  return static_cast<size_t>(num_kv_heads) * page_size * head_dim * 4;
+}
+
+kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const void* v,
+                            kvq_dtype dtype, int64_t token_stride, const int32_t* slot_mapping,
+                            int32_t num_tokens, void* stream) {
+  if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
+  kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
+  if (st != KVQ_OK) return st;
+  const int b = cache->hadamard_block;
+  if (!(b == 0 || b == 16 || b == 32 || b == 64 || b == 128) || b > cache->head_dim)
+    return fail(KVQ_ERR_UNSUPPORTED, "hadamard_block %d unsupported for head_dim %d", b, cache->head_dim);
+  st = check_append(cache->pool, k, v, dtype, token_stride, slot_mapping, num_tokens,
+                    cache->num_kv_heads, cache->head_dim);
+  if (st != KVQ_OK || num_tokens == 0) return st;
+  AppendArgs a{};
+  a.pool = static_cast<uint8_t*>(cache->pool);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.slot_mapping = slot_mapping;
+  a.token_stride = token_stride;
+  a.num_tokens = num_tokens;
+  a.num_pages = cache->num_pages;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.block = b;
+  a.in_bf16 = dtype == KVQ_BF16;
+  const hipError_t e = launch_append_int4(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+kvq_status kvq_append_paged_bf16(const kvq_bf16_cache* cache, const void* k, const void* v,
+                                 kvq_dtype dtype, int64_t token_stride,
+                                 const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
+  if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
+  kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
+  if (st != KVQ_OK) return st;
+  st = check_append(cache->pool, k, v, dtype, token_stride, slot_mapping, num_tokens,
+                    cache->num_kv_heads, cache->head_dim);
+  if (st != KVQ_OK || num_tokens == 0) return st;
+  AppendArgs a{};
+  a.pool = static_cast<uint8_t*>(cache->pool);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.slot_mapping = slot_mapping;
+  a.token_stride = token_stride;
+  a.num_tokens = num_tokens;
+  a.num_pages = cache->num_pages;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.in_bf16 = dtype == KVQ_BF16;
+  const hipError_t e = launch_append_bf16(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn(const kvq_int4_cache* cache, const void* q, kvq_dtype dtype,
+                           int32_t num_q_heads, const int32_t* block_table,
+                           int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                           int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                           void* workspace, size_t workspace_bytes_given, void* stream) {
+  if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
+  kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
+  if (st != KVQ_OK) return st;
+  const int b = cache->hadamard_block;
+  if (!(b == 0 || b == 16 || b == 32 || b == 64 || b == 128) || b > cache->head_dim)
+    return fail(KVQ_ERR_UNSUPPORTED, "hadamard_block %d unsupported for head_dim %d", b, cache->head_dim);
+  return launch_decode(true, cache->pool, cache->num_pages, cache->num_kv_heads, cache->head_dim, b,
+                       q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens, batch,
+                       max_seq_len, sm_scale, num_splits, out, workspace, workspace_bytes_given,
+                       stream);
+}
+
+kvq_status kvq_decode_attn_bf16(const kvq_bf16_cache* cache, const void* q, kvq_dtype dtype,
+                                int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                                void* workspace, size_t workspace_bytes_given, void* stream) {
+  if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
+  kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
+  if (st != KVQ_OK) return st;
+  return launch_decode(false, cache->pool, cache->num_pages, cache->num_kv_heads, cache->head_dim, 0,
+                       q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens, batch,
+                       max_seq_len, sm_scale, num_splits, out, workspace, workspace_bytes_given,
+                       stream);
+}
+
+size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seq_len, int32_t num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
+      num_splits < 0)
+    return 0;
+  return workspace_bytes(batch, num_q_heads, head_dim,
+                         plan_splits(batch, num_kv_heads, max_seq_len, num_splits));
+}
+
+const char* kvq_status_string(kvq_status status) {
+  switch (status) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARGUMENT: return "KVQ_ERR_INVALID_ARGUMENT";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED";
+    case KVQ_ERR_WORKSPACE_TOO_SMALL: return "KVQ_ERR_WORKSPACE_TOO_SMALL";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP";
+  }
+  return "KVQ_ERR_UNKNOWN";
+}
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,280 @@
+// Write path: fused block-Hadamard rotation + token-wise asymmetric INT4
+// quantization + paged scatter ("SAW-INT4: System-Aware 4-Bit KV-Cache
+// Quantization for Real-World LLM Serving", summary page, Research Findings:
+// token-wise INT4 after a block-diagonal Hadamard rotation, with a fused
+// rotation-quantization kernel writing into the paged KV-cache layout; scale
+// and zero point kept as FP16 as in "InnerQ", Table 3).  Also the bf16-cache
+// baseline copy.
+//
+// Bit-exactness: the quantizer's fp32 steps are done one rounding at a time
+// in the order the header of kvq.h states (this file is built with
+// -ffp-contract=off; division and reciprocal are the correctly rounded HIP
+// defaults), so codes and sidecars equal those of any implementation that
+// follows the same steps.
+#include "dev_common.hpp"
+#include "kvq_internal.hpp"
+
+namespace kvq {
+namespace {
+
+constexpr int kAppendThreads = 256;  // 4 waves
+constexpr int kLaneElems = 64;       // elements of one vector owned by one lane
+constexpr int kHalfStride = kLaneElems * 2 + 16;  // LDS bytes per lane slot (+16 B pad)
+
+template <int D>
+struct AppendShape {
+  static constexpr int kLanesPerVec = D / kLaneElems;                   // 1 or 2
+  static constexpr int kRows = kAppendThreads / (2 * kLanesPerVec);     // (token, head) rows per block
+  static constexpr int kChunks = D / 8;                                 // 16-byte chunks per input row
+  static constexpr int kSlab = kPage * (D + 8);                         // bytes per (page, head)
+};
+
+template <bool BF16>
+__device__ __forceinline__ void widen8(u32x4 w, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t u = w[i];
+    if constexpr (BF16) {
+      x[2 * i] = u2f(u << 16);
+      x[2 * i + 1] = u2f(u & 0xFFFF0000u);
+    } else {
+      x[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u & 0xFFFFu)));
+      x[2 * i + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u >> 16)));
+    }
+  }
+}
+
+// One block handles kRows consecutive (token, head) rows; lanes of waves 0-1
+// take the K vectors, waves 2-3 the V vectors; each lane owns 64 contiguous
+// channels of one vector (two lanes per vector at D = 128).
+template <int D, int BLK, bool BF16>
+__global__ __launch_bounds__(kAppendThreads) void append_int4_kernel(AppendArgs a) {
+  using S = AppendShape<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * S::kRows * S::kLanesPerVec * kHalfStride];
+  const int tid = threadIdx.x;
+  const int hkv = a.num_kv_heads;
+  const int64_t total_rows = static_cast<int64_t>(a.num_tokens) * hkv;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * S::kRows;
+
+  // 1. coalesced 16-byte loads of the block's K and V rows into LDS
+#pragma unroll
+  for (int kind = 0; kind < 2; ++kind) {
+    const uint16_t* src = kind ? a.v : a.k;
+#pragma unroll
+    for (int it = 0; it < S::kRows * S::kChunks / kAppendThreads; ++it) {
+      const int c = tid + it * kAppendThreads;
+      const int lr = c / S::kChunks, piece = c % S::kChunks;
+      const int64_t r = row0 + lr;
+      if (r < total_rows) {
+        const int64_t t = r / hkv;
+        const int h = static_cast<int>(r - t * hkv);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src + t * a.token_stride +
+                                                        static_cast<int64_t>(h) * D + piece * 8);
+        const int half = piece / 8, pp = piece % 8;
+        *reinterpret_cast<u32x4*>(lds + ((kind * S::kRows + lr) * S::kLanesPerVec + half) * kHalfStride +
+                                  pp * 16) = w;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. each lane: 64 channels of one vector, widened to fp32
+  const int kind = tid / (kAppendThreads / 2);
+  const int j = tid % (kAppendThreads / 2);
+  const int lr = j / S::kLanesPerVec;
+  const int hf = j % S::kLanesPerVec;
+  const int64_t r = row0 + lr;
+  float x[kLaneElems];
+  {
+    const uint8_t* base = lds + ((kind * S::kRows + lr) * S::kLanesPerVec + hf) * kHalfStride;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) widen8<BF16>(*reinterpret_cast<const u32x4*>(base + 16 * m), x + 8 * m);
+  }
+
+  // 3. block Hadamard butterfly, stages h = 1, 2, ..., BLK/2 ascending
+  if constexpr (BLK > 0) {
+    constexpr int kIn = BLK < kLaneElems ? BLK : kLaneElems;
+#pragma unroll
+    for (int hh = 1; hh < kIn; hh *= 2)
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i += 2 * hh)
+#pragma unroll
+        for (int k = i; k < i + hh; ++k) {
+          const float u = x[k], w = x[k + hh];
+          x[k] = u + w;
+          x[k + hh] = u - w;
+        }
+    if constexpr (BLK == 128) {
+      // last stage h = 64 pairs channel k (lane hf = 0) with k + 64 (hf = 1):
+      // lower half keeps own + partner, upper half partner - own; the product
+      // by +-1 is exact, so the fma rounds exactly once like an add/sub.
+      const float sgn = hf ? -1.0f : 1.0f;
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) {
+        const float p = dpp_f<kDppXor1>(x[k]);
+        x[k] = __builtin_fmaf(sgn, x[k], p);
+      }
+    }
+  }
+
+  // 4. range.  Rounding is monotone, so min/max of the unscaled butterfly
+  // output, scaled once, equal min/max of the scaled elements.
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int k = 1; k < kLaneElems; ++k) {
+    mn = fminf(mn, x[k]);
+    mx = fmaxf(mx, x[k]);
+  }
+  if constexpr (S::kLanesPerVec == 2) {
+    mn = fminf(mn, dpp_f<kDppXor1>(mn));
+    mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
+  }
+  if constexpr (BLK > 0) {
+    const float sb = block_norm(BLK);
+    mn = mn * sb;
+    mx = mx * sb;
+#pragma unroll
+    for (int k = 0; k < kLaneElems; ++k) x[k] = x[k] * sb;
+  }
+
+  // 5. fp16 zero and scale, reciprocal (0 for a zero scale)
+  const float zero_f = mn + 0.0f;
+  const float range = (mx - mn) + 0.0f;
+  const float step = range / 15.0f;
+  const _Float16 sh = static_cast<_Float16>(step);
+  const _Float16 zh = static_cast<_Float16>(zero_f);
+  const float sf = static_cast<float>(sh);
+  const float zf = static_cast<float>(zh);
+  const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+
+  // 6. codes: (y - zero) * inv, then round-half-even and clamp to [0, 15].
+  // Adding 2^23 rounds to an integer in the current (nearest-even) mode for
+  // any value in [0, 2^23); the clamp in that biased domain equals clamping
+  // the rounded value; the code is then the low 4 bits of the float.
+  uint32_t words[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float d = x[8 * m + i] - zf;
+      const float q = d * inv;
+      const float t = __builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388623.0f);
+      c[i] = f2u(t);
+    }
+    words[m] = pack8_nibbles(c);
+  }
+
+  // 7. scatter into the slot's page
+  if (r >= total_rows) return;
+  const int64_t t = r / hkv;
+  const int h = static_cast<int>(r - t * hkv);
+  const int32_t slot = a.slot_mapping[t];
+  if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(a.num_pages) * kPage) return;
+  const int page = slot / kPage, off = slot % kPage;
+  uint8_t* slab = a.pool + (static_cast<int64_t>(page) * hkv + h) * S::kSlab;
+  if (kind == 0) {
+    u32x4* dst = reinterpret_cast<u32x4*>(slab + off * (D / 2) + hf * 32);
+    dst[0] = u32x4{words[0], words[1], words[2], words[3]};
+    dst[1] = u32x4{words[4], words[5], words[6], words[7]};
+  } else {
+    uint32_t* vw = reinterpret_cast<uint32_t*>(slab + kPage * D / 2);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) vw[(hf * 8 + m) * kPage + off] = words[m];
+  }
+  if (hf == 0) {
+    const uint32_t meta = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
+                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
+    *reinterpret_cast<uint32_t*>(slab + kPage * D + kind * 4 * kPage + off * 4) = meta;
+  }
+}
+
+// bf16 baseline: one thread per (token, head, 8-channel group).
+template <bool BF16>
+__global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
+  const int d = a.head_dim, groups = d / 8, hkv = a.num_kv_heads;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * hkv * groups;
+  if (idx >= total) return;
+  const int n = static_cast<int>(idx % groups);
+  const int64_t r = idx / groups;
+  const int64_t t = r / hkv;
+  const int h = static_cast<int>(r - t * hkv);
+  const int32_t slot = a.slot_mapping[t];
+  if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(a.num_pages) * kPage) return;
+  const int page = slot / kPage, off = slot % kPage;
+  const int64_t in_off = t * a.token_stride + static_cast<int64_t>(h) * d + n * 8;
+  u32x4 kw = *reinterpret_cast<const u32x4*>(a.k + in_off);
+  u32x4 vw = *reinterpret_cast<const u32x4*>(a.v + in_off);
+  if constexpr (!BF16) {
+    auto cvt = [](u32x4 w) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] & 0xFFFFu)));
+        const float hi = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] >> 16)));
+        const uint16_t blo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
+        const uint16_t bhi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
+        o[i] = static_cast<uint32_t>(blo) | (static_cast<uint32_t>(bhi) << 16);
+      }
+      return o;
+    };
+    kw = cvt(kw);
+    vw = cvt(vw);
+  }
+  uint16_t* slab = reinterpret_cast<uint16_t*>(a.pool + (static_cast<int64_t>(page) * hkv + h) * (4 * kPage * d));
+  *reinterpret_cast<u32x4*>(slab + off * d + n * 8) = kw;
+  const int g = off / 4, i = off % 4;
+  uint16_t* vb = slab + kPage * d + ((n * (kPage / 4) + g) * 8) * 4 + i;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const uint32_t w = vw[jj / 2];
+    vb[jj * 4] = static_cast<uint16_t>((jj & 1) ? (w >> 16) : (w & 0xFFFFu));
+  }
+}
+
+template <int D, int BLK>
+hipError_t launch_int4_d(const AppendArgs& a, hipStream_t s) {
+  using S = AppendShape<D>;
+  const int64_t rows = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads;
+  const dim3 grid(static_cast<unsigned>((rows + S::kRows - 1) / S::kRows));
+  if (a.in_bf16)
+    append_int4_kernel<D, BLK, true><<<grid, kAppendThreads, 0, s>>>(a);
+  else
+    append_int4_kernel<D, BLK, false><<<grid, kAppendThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_int4_block(const AppendArgs& a, hipStream_t s) {
+  switch (a.block) {
+    case 0: return launch_int4_d<D, 0>(a, s);
+    case 16: return launch_int4_d<D, 16>(a, s);
+    case 32: return launch_int4_d<D, 32>(a, s);
+    case 64: return launch_int4_d<D, 64>(a, s);
+    case 128:
+      if constexpr (D == 128) return launch_int4_d<D, 128>(a, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append_int4(const AppendArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  return a.head_dim == 128 ? launch_int4_block<128>(a, s) : launch_int4_block<64>(a, s);
+}
+
+hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * (a.head_dim / 8);
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  if (a.in_bf16)
+    append_bf16_kernel<true><<<grid, 256, 0, s>>>(a);
+  else
+    append_bf16_kernel<false><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,114 @@
+// Device helpers for gfx950 (CDNA4, wave64): cross-lane moves, MFMA wrappers,
+// nibble packing.  Host code never includes this header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = 16;
+
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// ---- DPP within groups of four lanes (quad_perm) ---------------------------
+// quad_perm [1,0,3,2] (lane ^ 1) and [2,3,0,1] (lane ^ 2).
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppBcast0 = 0x00;   // quad_perm [0,0,0,0]
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return u2f(__builtin_amdgcn_update_dpp(0u, f2u(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return __builtin_amdgcn_update_dpp(0u, x, CTRL, 0xF, 0xF, false);
+}
+
+// ---- row-crossing exchanges with the gfx950 permlane swaps ------------------
+// After swapping a copy of x with itself, the two results hold, in every lane,
+// the lane's own value and its partner's (lane ^ 16, resp. lane ^ 32) in some
+// order; a symmetric op over them is the same in both partners.
+__device__ __forceinline__ float max_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+  return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+  return u2f(r[0]) + u2f(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return u2f(r[0]) + u2f(r[1]);
+}
+// max over the four rows of 16 lanes (same lane position in each row)
+__device__ __forceinline__ float max_rows(float x) { return max_xor32(max_xor16(x)); }
+__device__ __forceinline__ float sum_rows(float x) { return sum_xor32(sum_xor16(x)); }
+
+// value of lane `src` (wave-wide gather through the LDS crossbar)
+__device__ __forceinline__ float lane_read(float x, int src) {
+  return u2f(__builtin_amdgcn_ds_bpermute(src << 2, f2u(x)));
+}
+
+// ---- MFMA ------------------------------------------------------------------
+// 16x16x64 int8 -> int32.  Lane l supplies row (A) / column (B) l % 16 and 16
+// k-slots of group l / 16; C[4*(l/16) + i][l % 16] lands in lane l, element i.
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+// 16x16x32 bf16 -> fp32, same lane mapping with 8 k-slots per lane.
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- nibbles -----------------------------------------------------------------
+constexpr uint32_t kLowNibbles = 0x0F0F0F0Fu;
+
+// 4x4 byte transpose: out[j] = (x0.byte j, x1.byte j, x2.byte j, x3.byte j).
+__device__ __forceinline__ void transpose_bytes4(uint32_t x0, uint32_t x1, uint32_t x2,
+                                                 uint32_t x3, uint32_t out[4]) {
+  // v_perm_b32(s0, s1, sel): selector bytes 0..3 pick bytes of s1, 4..7 of s0.
+  uint32_t a = __builtin_amdgcn_perm(x1, x0, 0x06020400u);  // x0.b0 x1.b0 x0.b2 x1.b2
+  uint32_t b = __builtin_amdgcn_perm(x1, x0, 0x07030501u);  // x0.b1 x1.b1 x0.b3 x1.b3
+  uint32_t c = __builtin_amdgcn_perm(x3, x2, 0x06020400u);  // x2.b0 x3.b0 x2.b2 x3.b2
+  uint32_t d = __builtin_amdgcn_perm(x3, x2, 0x07030501u);  // x2.b1 x3.b1 x2.b3 x3.b3
+  out[0] = __builtin_amdgcn_perm(c, a, 0x05040100u);        // a.lo16 | c.lo16 << 16
+  out[2] = __builtin_amdgcn_perm(c, a, 0x07060302u);        // a.hi16 | c.hi16 << 16
+  out[1] = __builtin_amdgcn_perm(d, b, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
+}
+
+// Packs eight 4-bit codes held in bits 0..3 of eight words (higher bits are
+// ignored as long as bits 4..7 of c[2j] are zero) into one word: byte j =
+// c[2j] | c[2j+1] << 4.
+__device__ __forceinline__ uint32_t pack8_nibbles(const uint32_t c[8]) {
+  uint32_t b0 = (c[1] << 4) | c[0];
+  uint32_t b1 = (c[3] << 4) | c[2];
+  uint32_t b2 = (c[5] << 4) | c[4];
+  uint32_t b3 = (c[7] << 4) | c[6];
+  uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // b0.byte0, b1.byte0
+  uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return lo | (hi << 16);
+}
+
+// fp32 constant 1/sqrt(b) of a Hadamard block (the correctly rounded values
+// 0x3E800000, 0x3E3504F3, 0x3E000000, 0x3DB504F3 for b = 16, 32, 64, 128).
+__device__ __forceinline__ float block_norm(int b) {
+  uint32_t bits = b == 16 ? 0x3E800000u : b == 32 ? 0x3E3504F3u : b == 64 ? 0x3E000000u
+                : b == 128 ? 0x3DB504F3u : 0x3F800000u;
+  return u2f(bits);
+}
+
+}  // namespace kvq

@@ -1,0 +1,61 @@
+// Internal host-side interface between the C ABI (api.cpp) and the kernel
+// launchers (*.hip).  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct AppendArgs {
+  uint8_t* pool;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* slot_mapping;
+  int64_t token_stride;      // elements
+  int32_t num_tokens;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block;             // Hadamard block (0 = none); unused by the bf16 pool
+  int32_t in_bf16;           // 1: inputs are bf16, 0: fp16
+};
+
+struct DecodeArgs {
+  const uint8_t* pool;
+  const uint16_t* q;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* out;
+  float* part_acc;           // [batch][hq][nsplit][head_dim]
+  float* part_ml;            // [batch][hq][nsplit][2]
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t block;             // Hadamard block (0 = none)
+  int32_t bt_stride;         // max_pages_per_seq
+  int32_t batch;
+  int32_t max_seq_len;
+  int32_t split_pages;       // pages per split-K partition (multiple of 4)
+  int32_t nsplit;            // partitions of the longest sequence
+  float sm_log2;             // sm_scale * log2(e)
+  int32_t in_bf16;
+};
+
+// Split-K plan shared by the launch and the workspace query.
+struct SplitPlan {
+  int32_t split_pages;
+  int32_t nsplit;
+};
+SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len, int32_t num_splits);
+size_t workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, const SplitPlan& p);
+
+hipError_t launch_append_int4(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s);
+hipError_t launch_decode_int4(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_reduce(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace kvq

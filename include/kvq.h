@@ -1,0 +1,191 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: Hadamard-rotated token-wise INT4 paged KV
+ * cache for AMD Instinct MI355X (gfx950).
+ *
+ * The method: "SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for
+ * Real-World LLM Serving" (summary page, Research Findings; idea page, Core
+ * Innovation) quantizes each new key/value vector to 4 bits with one group per
+ * token after a block-diagonal Hadamard rotation, with a fused kernel that
+ * writes straight into a paged cache, and runs attention fused over the
+ * quantized pages.  "InnerQ" (Table 3) keeps scale factors and zero points in
+ * FP16.  "BitDecoding-FP4" (Abstract) uses Hadamard rotation against key
+ * outliers under token-wise scaling and stacks the query heads of a GQA group
+ * into one matrix product over each KV page.
+ *
+ * Conventions shared by every entry point
+ *   - All buffer pointers are DEVICE pointers owned by the caller (allocated
+ *     with hipMalloc or by a framework on the same device).  The library
+ *     allocates nothing and keeps no mutable global state (a per-device CU
+ *     count is cached).
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Calls are asynchronous, never synchronize, and are safe to make
+ *     from several host threads.
+ *   - Argument validation happens on the host before anything is enqueued; a
+ *     non-OK status means nothing was launched.  kvq_last_error() then gives a
+ *     thread-local description.  KVQ_ERR_HIP reports a launch failure.
+ *   - Page size P is 16 tokens.  head_dim D is 64 or 128.
+ *   - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ *   - Inputs that are 16-bit floats are fp16 or bf16 bit patterns (kvq_dtype).
+ *
+ * INT4 page pool layout: [num_pages][num_kv_heads][slab] bytes with
+ *   slab = P * (D + 8) bytes (2176 at D = 128, 1152 at D = 64):
+ *     [0, P*D/2)         K codes, token-major: byte t*(D/2) + j holds channel
+ *                        2j (bits 0..3) and 2j+1 (bits 4..7) of token t.
+ *     [P*D/2, P*D)       V codes, grouped by 8 channels: 32-bit word n*P + t
+ *                        (n < D/8) holds channels 8n..8n+7 of token t, byte j
+ *                        of it channel 8n+2j (bits 0..3) and 8n+2j+1 (4..7).
+ *     [P*D, P*D + 4P)    K sidecar: token t -> fp16 scale at 4t, fp16 zero at
+ *                        4t+2 (little endian).
+ *     [P*D + 4P, P*D+8P) V sidecar, same form.
+ *   A decoded element is code * scale + zero, in the rotated basis.
+ *
+ * bf16 page pool layout: [num_pages][num_kv_heads][slab], slab = 4*P*D bytes:
+ *     K: bf16 element t*D + c (token-major);
+ *     V: bf16 element P*D + ((n*(P/4) + g)*8 + j)*4 + i for channel c = 8n + j
+ *        and token t = 4g + i.
+ *
+ * A token in slot s lives at page s / P, offset s % P.
+ *
+ * Device-side robustness: slots outside [0, num_pages*P) are skipped; page
+ * table entries outside [0, num_pages) contribute nothing; seq_lens are
+ * clamped to [0, max_seq_len].  These are safety nets, not features.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad size, misalignment       */
+  KVQ_ERR_UNSUPPORTED = 2,       /* valid but not built: D, P, block, group    */
+  KVQ_ERR_WORKSPACE_TOO_SMALL = 3,
+  KVQ_ERR_HIP = 4                /* launch failed; detail in kvq_last_error()  */
+} kvq_status;
+
+typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+/* INT4 cache descriptor.  `pool` must be 16-byte aligned and hold
+ * kvq_int4_page_bytes(page_size, num_kv_heads, head_dim) * num_pages bytes. */
+typedef struct {
+  void*   pool;
+  int32_t num_pages;
+  int32_t page_size;        /* must be 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t hadamard_block;   /* 16, 32, 64 or 128 (dividing head_dim); 0 = plain INT4 */
+} kvq_int4_cache;
+
+/* bf16 cache descriptor (baseline).  `pool` 16-byte aligned,
+ * kvq_bf16_page_bytes(...) * num_pages bytes. */
+typedef struct {
+  void*   pool;
+  int32_t num_pages;
+  int32_t page_size;        /* must be 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;         /* 64 or 128 */
+} kvq_bf16_cache;
+
+/* Bytes of one page (all KV heads) of each pool. */
+size_t kvq_int4_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
+size_t kvq_bf16_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
+
+/*
+ * kvq_append_paged -- write path (SAW-INT4 summary page, Research Findings:
+ * the fused rotation-quantization kernel writing into the paged layout).
+ *
+ * For every token t < num_tokens with slot s = slot_mapping[t] >= 0, and every
+ * KV head h, both for K (from `k`) and V (from `v`):
+ *   x = widen(input[t*token_stride + h*D .. + D))       (exact, to fp32)
+ *   y = blockdiag(H_b)/sqrt(b) x  with the fp32 butterfly, stages h = 1, 2, 4,
+ *       ..., b/2 in ascending order, then one multiply by fp32(1/sqrt(b));
+ *       skipped when hadamard_block == 0
+ *   zero = fp16(min y + 0), scale = fp16(((max y - min y) + 0) / 15)
+ *   code_d = clamp(round_half_even((y_d - zero) * (1/scale)), 0, 15),
+ *            1/scale = 0 when scale == 0; every fp32 operation rounded once
+ *   codes and (scale, zero) stored in page s/16, offset s%16 (layout above).
+ * Codes and sidecars are bit-exact functions of the input.
+ *
+ * k, v:         device, [num_tokens][token_stride] elements of `dtype`, the
+ *               first num_kv_heads*head_dim of each token used; 16-byte
+ *               aligned, token_stride a multiple of 8 and >= num_kv_heads*D.
+ * slot_mapping: device int32 [num_tokens]; two tokens of one call must not
+ *               share a slot.
+ * num_tokens:   >= 0 (0 launches nothing).
+ */
+kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const void* v,
+                            kvq_dtype dtype, int64_t token_stride,
+                            const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/*
+ * kvq_decode_attn -- read path (SAW-INT4 summary page: fused attention
+ * execution over the paged quantized cache; BitDecoding-FP4 Abstract: GQA
+ * query heads stacked into one product per KV page).
+ *
+ * For each sequence b < batch and query head h < num_q_heads, with L =
+ * seq_lens[b] tokens whose pages are block_table[b][0 .. ceil(L/16)):
+ *   q_rot = blockdiag(H_b)/sqrt(b) q[b][h]          (so q.k is preserved)
+ *   s_i   = sm_scale * (q_rot . k_hat_i),  k_hat_i = code * scale + zero
+ *   o_rot = sum_i softmax(s)_i v_hat_i
+ *   out[b][h] = (blockdiag(H_b)/sqrt(b))^T o_rot    (original basis)
+ * L = 0 gives a zero row.  Accuracy: within max-abs 2e-3 and relative L2
+ * 1e-3 of exact fp64 attention over the same decoded cache.
+ *
+ * q:            device, [batch][num_q_heads][head_dim] of `dtype`, 16-byte aligned.
+ * block_table:  device int32 [batch][max_pages_per_seq].
+ * seq_lens:     device int32 [batch], each <= max_seq_len.
+ * max_seq_len:  host bound on seq_lens (sizes the split-K grid);
+ *               max_pages_per_seq*16 >= max_seq_len.
+ * sm_scale:     softmax scale (normally 1/sqrt(head_dim)), finite.
+ * num_splits:   0 = choose automatically; otherwise the number of split-K
+ *               partitions of the longest sequence (clamped to what fits).
+ * out:          device fp32 [batch][num_q_heads][head_dim], 16-byte aligned.
+ * workspace:    device scratch of at least kvq_decode_workspace_bytes(...)
+ *               for the same arguments, 16-byte aligned; its contents are
+ *               overwritten.  Calls that overlap on one workspace race.
+ */
+kvq_status kvq_decode_attn(const kvq_int4_cache* cache, const void* q, kvq_dtype dtype,
+                           int32_t num_q_heads, const int32_t* block_table,
+                           int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                           int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kvq_decode_attn / kvq_decode_attn_bf16 need (0 allowed). */
+size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seq_len, int32_t num_splits);
+
+/* bf16 baseline of kvq_append_paged: copies K and V (fp16 input is rounded
+ * to bf16, nearest even) into the bf16 pool.  Same argument rules. */
+kvq_status kvq_append_paged_bf16(const kvq_bf16_cache* cache, const void* k, const void* v,
+                                 kvq_dtype dtype, int64_t token_stride,
+                                 const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/* bf16 baseline of kvq_decode_attn (no rotation).  Same argument rules. */
+kvq_status kvq_decode_attn_bf16(const kvq_bf16_cache* cache, const void* q, kvq_dtype dtype,
+                                int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                int32_t batch, int32_t max_seq_len, float sm_scale,
+                                int32_t num_splits, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Static name of a status code. */
+const char* kvq_status_string(kvq_status status);
+
+/* Thread-local description of the last non-OK status returned on this thread
+ * ("" if none).  Valid until the next call on the same thread. */
+const char* kvq_last_error(void);
+
+/* KVQ_ABI_VERSION of the built library. */
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

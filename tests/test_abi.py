@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kvq.h declares, and host-side validation rejects bad arguments before
+anything is launched (only invalid calls are made here, so no HIP work is
+ever enqueued)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import bit_kv_cache_block_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20          # an aligned, never-dereferenced address
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _header_functions()
+    assert len(names) == 10
+    assert sorted(kvq.EXPORTED) == names
+    L = kvq.lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings():
+    L = kvq.lib()
+    assert L.kvq_abi_version() == 1
+    assert L.kvq_status_string(3) == b"KVQ_ERR_WORKSPACE_TOO_SMALL"
+    assert L.kvq_status_string(99) == b"KVQ_ERR_UNKNOWN"
+
+
+def test_page_bytes():
+    assert kvq.kvq_int4_page_bytes(16, 8, 128) == 8 * 2176
+    assert kvq.kvq_int4_page_bytes(16, 2, 64) == 2 * 1152
+    assert kvq.kvq_bf16_page_bytes(16, 8, 128) == 8 * 8192
+
+
+def _int4(num_pages=64, page=16, hkv=2, d=64, block=64, pool=FAKE):
+    return kvq._Int4Desc(pool, num_pages, page, hkv, d, block)
+
+
+def _append(desc, k=FAKE, v=FAKE, dtype=kvq.KVQ_BF16, stride=128, slots=FAKE, n=4):
+    L = kvq.lib()
+    return L.kvq_append_paged(C.byref(desc) if desc is not None else None, k, v, dtype, stride,
+                              slots, n, None)
+
+
+@pytest.mark.parametrize("desc,kw,status", [
+    (None, {}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(d=96), {}, kvq.KVQ_ERR_UNSUPPORTED),
+    (_int4(page=32), {}, kvq.KVQ_ERR_UNSUPPORTED),
+    (_int4(block=8), {}, kvq.KVQ_ERR_UNSUPPORTED),
+    (_int4(block=128, d=64), {}, kvq.KVQ_ERR_UNSUPPORTED),
+    (_int4(num_pages=0), {}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(pool=0), {}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(pool=FAKE + 4), {}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(), {"k": 0}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(), {"slots": 0}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(), {"k": FAKE + 8}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(), {"stride": 64}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(), {"stride": 132}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(), {"dtype": 7}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(), {"n": -1}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+])
+def test_append_validation(desc, kw, status):
+    assert _append(desc, **kw) == status
+    assert kvq.lib().kvq_last_error() != b""
+
+
+def test_append_zero_tokens_is_a_noop():
+    assert _append(_int4(), k=0, v=0, slots=0, n=0) == kvq.KVQ_OK
+
+
+def _decode(desc, q=FAKE, dtype=kvq.KVQ_BF16, hq=8, bt=FAKE, maxp=16, sl=FAKE, batch=4,
+            maxlen=256, sm=0.125, splits=0, out=FAKE, ws=FAKE, wsb=0):
+    L = kvq.lib()
+    return L.kvq_decode_attn(C.byref(desc), q, dtype, hq, bt, maxp, sl, batch, maxlen, sm, splits,
+                             out, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"hq": 7}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    ({"hq": 64}, kvq.KVQ_ERR_UNSUPPORTED),           # group 32 > 16
+    ({"q": 0}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    ({"out": FAKE + 4}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    ({"bt": 0}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    ({"maxp": 8}, kvq.KVQ_ERR_INVALID_ARGUMENT),      # 8 pages < 256 tokens
+    ({"sm": float("nan")}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    ({"batch": -1}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    ({"splits": -2}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    ({"wsb": 0}, kvq.KVQ_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_decode_validation(kw, status):
+    assert _decode(_int4(), **kw) == status
+
+
+def test_decode_workspace_too_small_by_one():
+    need = kvq.kvq_decode_workspace_bytes(4, 8, 2, 64, 256, 0)
+    assert need > 0
+    assert _decode(_int4(), wsb=need - 1) == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_decode_zero_batch_is_a_noop():
+    assert _decode(_int4(), batch=0, q=0, bt=0, sl=0, out=0) == kvq.KVQ_OK
+
+
+def test_bf16_entry_points_validate():
+    L = kvq.lib()
+    bad = kvq._Bf16Desc(FAKE, 4, 16, 2, 100)
+    assert L.kvq_append_paged_bf16(C.byref(bad), FAKE, FAKE, 1, 128, FAKE, 1, None) == kvq.KVQ_ERR_UNSUPPORTED
+    ok = kvq._Bf16Desc(FAKE, 4, 16, 2, 64)
+    assert L.kvq_decode_attn_bf16(C.byref(ok), FAKE, 1, 8, FAKE, 16, FAKE, 4, 256, 0.1, 0, FAKE,
+                                  FAKE, 0, None) == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("batch,hkv,maxlen", [(64, 8, 4096), (8, 8, 131072), (256, 8, 32768),
+                                               (1, 8, 32768), (4, 2, 256), (3, 1, 1)])
+def test_workspace_covers_every_split(batch, hkv, maxlen):
+    """The workspace holds (D + 2) floats per (sequence, head, split), and the
+    split plan covers the longest sequence with splits of whole 4-page steps."""
+    hq, d = hkv * 4, 128
+    ws = kvq.kvq_decode_workspace_bytes(batch, hq, hkv, d, maxlen, 0)
+    assert ws % (batch * hq * (d + 2) * 4) == 0
+    nsplit = ws // (batch * hq * (d + 2) * 4)
+    pages = (maxlen + 15) // 16
+    assert 1 <= nsplit <= max(1, (pages + 3) // 4)
+    for s in (1, 2, 5):
+        ws_s = kvq.kvq_decode_workspace_bytes(batch, hq, hkv, d, maxlen, s)
+        assert ws_s // (batch * hq * (d + 2) * 4) <= s
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(kvq, "_lib_handle", None)
+    with pytest.raises(RuntimeError, match="libkvq.so not found"):
+        kvq.kvq_int4_page_bytes(16, 8, 128)

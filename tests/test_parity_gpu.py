@@ -1,0 +1,263 @@
+"""GPU path vs the CPU oracle, through the C ABI.
+
+Codes and fp16 sidecars: bit-exact over the whole pool.  Attention: within
+max-abs 2e-3 and relative L2 1e-3 of the oracle's fp64 attention over its own
+(bit-identical) cache.  Every input comes from the seeded generators; nothing
+the oracle sees comes from the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import bit_kv_cache_block_amd as kvq
+import oracle
+import workloads
+from workloads import bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+MAX_ABS, REL_L2 = 2e-3, 1e-3
+
+
+def setup_module(_):
+    oracle.build(force=False)
+
+
+def _odt(t):
+    return oracle.BF16 if t.dtype == torch.bfloat16 else oracle.F16
+
+
+def gpu_int4_cache(w, block, k=None, v=None):
+    cache = kvq.Int4Cache(w.num_pages, w.hkv, w.d, block, DEV)
+    k = w.k if k is None else k
+    v = w.v if v is None else v
+    kvq.kvq_append_paged(cache, k.to(DEV), v.to(DEV), w.slot_mapping.to(DEV))
+    torch.cuda.synchronize()
+    return cache
+
+
+def oracle_int4_pool(w, block, sel=None):
+    k, v, sm = w.k, w.v, w.slot_mapping
+    if sel is not None:
+        k, v, sm = k[sel], v[sel], sm[sel]
+    pool = oracle.new_int4_pool(w.num_pages, w.hkv, w.d)
+    oracle.append_int4(pool, w.num_pages, w.hkv, w.d, block, bits(k), bits(v), _odt(w.k),
+                       sm.cpu().numpy())
+    return pool
+
+
+def gpu_decode(cache, w, num_splits=0, bf16=False):
+    fn = kvq.kvq_decode_attn_bf16 if bf16 else kvq.kvq_decode_attn
+    out = fn(cache, w.q.to(DEV), torch.from_numpy(w.block_table).to(DEV),
+             torch.from_numpy(w.seq_lens).to(DEV), w.max_seq_len, w.sm_scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def assert_close(got, want, label=""):
+    err = np.abs(got - want)
+    rel = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)
+    print(f"[{label}] max-abs {err.max():.3e} rel-L2 {rel:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err.max() <= MAX_ABS, f"{label}: max-abs {err.max():.3e}"
+    assert rel <= REL_L2, f"{label}: rel-L2 {rel:.3e}"
+
+
+def assert_pool_equal(gpu_pool, host_pool, label=""):
+    g = gpu_pool.cpu().numpy().reshape(-1)
+    diff = np.nonzero(g != host_pool)[0]
+    assert diff.size == 0, f"{label}: {diff.size} bytes differ, first at {diff[:8]}"
+
+
+# ---------------------------------------------------------------- write path
+
+@pytest.mark.parametrize("block", [0, 16, 32, 64])
+def test_append_tiny_fp16_bitexact(block):
+    w = workloads.tiny_decode(1, block=block)
+    print(f"append tiny block={block}", flush=True)
+    assert_pool_equal(gpu_int4_cache(w, block).pool, oracle_int4_pool(w, block), f"tiny b{block}")
+
+
+@pytest.mark.parametrize("block", [0, 16, 32, 64, 128])
+def test_append_llama_shape_bitexact(block):
+    w = workloads.llama8b_decode(2, batch=2, context=1024, block=block)
+    print(f"append llama b={block}", flush=True)
+    assert_pool_equal(gpu_int4_cache(w, block).pool, oracle_int4_pool(w, block), f"llama b{block}")
+
+
+@pytest.mark.parametrize("block", [0, 64])
+def test_append_prefill_student_t_bitexact(block):
+    w = workloads.prefill_append(3, total=8192, nseq=4, lo=512, hi=4096, block=block)
+    print(f"append prefill b={block}", flush=True)
+    assert_pool_equal(gpu_int4_cache(w, block).pool, oracle_int4_pool(w, block), f"prefill b{block}")
+
+
+def test_append_strided_tokens_skip_slots_and_degenerate_vectors():
+    """Token stride wider than Hkv*D (a view into a fused projection), slot -1,
+    constant rows (scale 0), tiny rows (subnormal fp16 scale), a ragged tail."""
+    torch.manual_seed(0)
+    t, hkv, d = 37, 3, 128
+    wide = torch.randn(t, hkv * d + 64, dtype=torch.float32)
+    wide[5, :hkv * d] = 0.75                    # constant
+    wide[6, :hkv * d] = -0.0                    # signed zeros
+    wide[7, :hkv * d] *= 1e-7                   # subnormal scale
+    wide[8, :d] = 3.0e4 * torch.sign(wide[8, :d])   # large magnitudes
+    wide = wide.to(torch.bfloat16)
+    k = wide[:, :hkv * d].view(t, hkv, d)
+    v = wide.flip(0)[:, :hkv * d].view(t, hkv, d)
+    assert k.stride(0) == hkv * d + 64
+    pages = 5
+    rng = np.random.default_rng(1)
+    slots = rng.permutation(pages * 16)[:t].astype(np.int32)
+    slots[3] = -1
+    slots[9] = pages * 16 + 100                 # outside the pool: skipped
+    sm = torch.from_numpy(slots)
+    for block in (0, 32, 128):
+        cache = kvq.Int4Cache(pages, hkv, d, block, DEV)
+        kvq.kvq_append_paged(cache, k.to(DEV), v.to(DEV), sm.to(DEV))
+        torch.cuda.synchronize()
+        pool = oracle.new_int4_pool(pages, hkv, d)
+        oracle.append_int4(pool, pages, hkv, d, block, bits(k.contiguous()), bits(v.contiguous()),
+                           oracle.BF16, slots)
+        assert_pool_equal(cache.pool, pool, f"edge b{block}")
+
+
+def test_append_bf16_cache_matches_oracle():
+    for w in (workloads.tiny_decode(1, block=0), workloads.llama8b_decode(2, batch=2, context=256)):
+        cache = kvq.Bf16Cache(w.num_pages, w.hkv, w.d, DEV)
+        kvq.kvq_append_paged_bf16(cache, w.k.to(DEV), w.v.to(DEV), w.slot_mapping.to(DEV))
+        torch.cuda.synchronize()
+        pool = oracle.new_bf16_pool(w.num_pages, w.hkv, w.d)
+        oracle.append_bf16(pool, w.num_pages, w.hkv, w.d, bits(w.k), bits(w.v), _odt(w.k),
+                           w.slot_mapping.numpy())
+        assert_pool_equal(cache.pool, pool, w.name)
+
+
+# ---------------------------------------------------------------- read path
+
+@pytest.mark.parametrize("block", [0, 64])
+def test_decode_tiny(block):
+    w = workloads.tiny_decode(1, block=block)
+    cache = gpu_int4_cache(w, block)
+    pool = oracle_int4_pool(w, block)
+    want = oracle.decode_int4(pool, w.hkv, w.d, block, bits(w.q), oracle.F16, w.block_table,
+                              w.seq_lens, w.sm_scale)
+    for splits in (0, 1, 2, 4):
+        assert_close(gpu_decode(cache, w, splits), want, f"tiny b{block} S{splits}")
+
+
+@pytest.mark.parametrize("block", [0, 16, 32, 64, 128])
+def test_decode_llama_shape(block):
+    w = workloads.llama8b_decode(2, batch=3, context=4096, block=block)
+    cache = gpu_int4_cache(w, block)
+    pool = oracle_int4_pool(w, block)
+    want = oracle.decode_int4(pool, w.hkv, w.d, block, bits(w.q), oracle.BF16, w.block_table,
+                              w.seq_lens, w.sm_scale)
+    assert_close(gpu_decode(cache, w), want, f"llama b{block}")
+
+
+def test_decode_long_context_scaled_channels():
+    w = workloads.long_context_decode(4, batch=2, context=16384, block=64)
+    cache = gpu_int4_cache(w, 64)
+    pool = oracle_int4_pool(w, 64)
+    want = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table,
+                              w.seq_lens, w.sm_scale)
+    for splits in (0, 1, 7):
+        assert_close(gpu_decode(cache, w, splits), want, f"long S{splits}")
+
+
+def test_decode_ragged_group8_with_appended_token():
+    """70B-shaped layer (GQA 8): fill, append one token per sequence, decode."""
+    fill, steps = workloads.concurrency_step(5, batch=8, block=64, steps=1, cap=4096)
+    step = steps[0]
+    cache = gpu_int4_cache(fill, 64)
+    kvq.kvq_append_paged(cache, step.k.to(DEV), step.v.to(DEV), step.slot_mapping.to(DEV))
+    pool = oracle_int4_pool(fill, 64)
+    oracle.append_int4(pool, step.num_pages, step.hkv, step.d, 64, bits(step.k), bits(step.v),
+                       oracle.BF16, step.slot_mapping.numpy())
+    assert_pool_equal(cache.pool, pool, "concurrency pool")
+    want = oracle.decode_int4(pool, step.hkv, step.d, 64, bits(step.q), oracle.BF16,
+                              step.block_table, step.seq_lens, step.sm_scale)
+    assert_close(gpu_decode(cache, step), want, "concurrency")
+
+
+@pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float16)])
+def test_decode_edge_lengths(d, dtype):
+    lens = [0, 1, 15, 16, 17, 63, 64, 65, 100, 300]
+    w = workloads.random_decode(11, batch=len(lens), hq=8, hkv=2, d=d, block=d // 2, dtype=dtype,
+                                seq_lens=lens)
+    cache = gpu_int4_cache(w, w.block)
+    pool = oracle_int4_pool(w, w.block)
+    want = oracle.decode_int4(pool, w.hkv, w.d, w.block, bits(w.q), _odt(w.q), w.block_table,
+                              w.seq_lens, w.sm_scale)
+    for splits in (0, 1, 2, 3, 100):
+        got = gpu_decode(cache, w, splits)
+        assert not got[0].any()                     # empty sequence -> zeros
+        assert_close(got, want, f"edges d{d} S{splits}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (16, 1)])
+def test_decode_group_sizes(hq, hkv):
+    w = workloads.random_decode(12, batch=3, hq=hq, hkv=hkv, d=128, block=64,
+                                seq_lens=[33, 200, 77])
+    cache = gpu_int4_cache(w, 64)
+    pool = oracle_int4_pool(w, 64)
+    want = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table,
+                              w.seq_lens, w.sm_scale)
+    assert_close(gpu_decode(cache, w), want, f"G{hq // hkv}")
+
+
+def test_decode_bf16_baseline():
+    for w in (workloads.tiny_decode(1, block=0), workloads.llama8b_decode(2, batch=2, context=2048),
+              workloads.random_decode(13, batch=4, hq=16, hkv=2, d=128, seq_lens=[0, 5, 40, 333])):
+        cache = kvq.Bf16Cache(w.num_pages, w.hkv, w.d, DEV)
+        kvq.kvq_append_paged_bf16(cache, w.k.to(DEV), w.v.to(DEV), w.slot_mapping.to(DEV))
+        pool = oracle.new_bf16_pool(w.num_pages, w.hkv, w.d)
+        oracle.append_bf16(pool, w.num_pages, w.hkv, w.d, bits(w.k), bits(w.v), _odt(w.k),
+                           w.slot_mapping.numpy())
+        want = oracle.decode_bf16(pool, w.hkv, w.d, bits(w.q), _odt(w.q), w.block_table,
+                                  w.seq_lens, w.sm_scale)
+        for splits in (0, 1):
+            assert_close(gpu_decode(cache, w, splits, bf16=True), want, f"bf16 {w.name} S{splits}")
+
+
+def test_decode_deterministic_and_page_permutation_invariant():
+    w = workloads.llama8b_decode(7, batch=2, context=1000, block=64)
+    cache = gpu_int4_cache(w, 64)
+    a = gpu_decode(cache, w)
+    b = gpu_decode(cache, w)
+    assert np.array_equal(a, b)
+    # move every page and its table entry together
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(w.num_pages)).to(DEV)
+    pool2 = torch.empty_like(cache.pool)
+    pool2[perm] = cache.pool
+    cache2 = kvq.Int4Cache(w.num_pages, w.hkv, w.d, 64, DEV, pool=pool2)
+    bt = torch.from_numpy(w.block_table).to(DEV)
+    bt2 = torch.where(bt >= 0, perm[bt.clamp(min=0).long()].int(), bt)
+    out2 = kvq.kvq_decode_attn(cache2, w.q.to(DEV), bt2.contiguous(),
+                               torch.from_numpy(w.seq_lens).to(DEV), w.max_seq_len, w.sm_scale)
+    assert np.array_equal(out2.cpu().numpy().astype(np.float64), a)
+
+
+def test_full_size_llama_layer_sampled():
+    """The benchmark's workload at full size (64 x 4096, block 64) in the same
+    launch configuration: codes of sampled sequences bit-exact, their
+    attention within tolerance."""
+    w = workloads.llama8b_decode(2, device=DEV, batch=64, context=4096, block=64)
+    cache = kvq.Int4Cache(w.num_pages, w.hkv, w.d, 64, DEV)
+    kvq.kvq_append_paged(cache, w.k, w.v, w.slot_mapping)
+    out = kvq.kvq_decode_attn(cache, w.q, torch.from_numpy(w.block_table).to(DEV),
+                              torch.from_numpy(w.seq_lens).to(DEV), w.max_seq_len, w.sm_scale)
+    torch.cuda.synchronize()
+    sample = [0, 37, 63]
+    sel = torch.from_numpy(np.isin(w.token_seq, sample)).to(DEV)
+    pool = oracle_int4_pool(w, 64, sel=sel)
+    slab = w.hkv * oracle.int4_slab_bytes(16, w.d)
+    gpool = cache.pool.cpu().numpy()
+    for b in sample:
+        for pg in w.block_table[b][w.block_table[b] >= 0]:
+            assert np.array_equal(gpool[pg], pool[pg * slab:(pg + 1) * slab]), f"page {pg}"
+    mask = np.zeros((w.batch, w.hq), np.uint8)
+    mask[sample] = 1
+    want = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table,
+                              w.seq_lens, w.sm_scale, mask=mask)
+    assert_close(out.cpu().numpy().astype(np.float64)[sample], want[sample], "full llama sampled")
