@@ -1,5 +1,46 @@
-"""Benchmark of the INT4 KV-cache hot path (placeholder: accounting only)."""
+"""Benchmark of the rotated INT4 paged KV-cache hot path on one MI355X.
 
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the whole hot path over the Llama-3-8B-shaped layer
+(32 query / 8 KV heads, head_dim 128, batch 64 x 4096 context, page 16,
+Hadamard block 64): append one new token per sequence (rotate + quantize +
+scatter) and run paged decode attention over the 4096-token context.  Inputs
+are resident in HBM; successive steps cycle through RING copies of the cache
+so the 256 MB Infinity Cache cannot hold the working set.
+
+Prints one JSON line.  ``value`` is the INT4 decode attention rate in GB/s of
+algorithmic bytes (packed codes + fp16 sidecars + query + output + page table)
+over the measured decode time; the same line carries the prefill
+rotate+quantize rate (Mtokens/s, 32768 ragged tokens), plain-INT4 and bf16-KV
+comparisons, the roofline of the decode kernel and the CPU oracle timed on a
+bounded sample.
+
+Other modes (for rocprofv3 runs): ``--mode decode`` times only the headline
+decode; ``--mode copy`` runs a plain 1 GiB device copy used to calibrate the
+FETCH_SIZE / WRITE_SIZE counters.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "INT4-KV decode attn HBM GB/s (% of peak); rotate+quant Mtokens/s"
+RING = 4
+
+
+# ---------------------------------------------------------------- accounting
 
 def overhead_bits(bits: int, group: int) -> float:
     """Bits of a per-group parameter averaged over the numbers of the group."""
@@ -9,3 +50,341 @@ def overhead_bits(bits: int, group: int) -> float:
 def int4_bytes_per_vector(d: int) -> int:
     """Stored bytes of one (token, KV head, K|V) vector: D nibbles + fp16 scale + fp16 zero."""
     return d // 2 + 4
+
+
+def decode_bytes(seq_lens, hkv, hq, d, kv_bytes_per_vector, q_bytes=2, page=16) -> int:
+    """Algorithmic HBM bytes of one decode call: K and V of every context token,
+    the query, the fp32 output, the page-table entries used and seq_lens."""
+    toks = int(sum(int(x) for x in seq_lens))
+    pages = int(sum((int(x) + page - 1) // page for x in seq_lens))
+    b = len(seq_lens)
+    return toks * hkv * 2 * kv_bytes_per_vector + b * hq * d * (q_bytes + 4) + pages * 4 + b * 4
+
+
+def append_bytes(tokens, hkv, d, kv_bytes_per_vector, in_bytes=2) -> int:
+    """Algorithmic HBM bytes of one append: read K and V, the slot map, write the
+    stored vectors."""
+    return tokens * hkv * 2 * d * in_bytes + tokens * 4 + tokens * hkv * 2 * kv_bytes_per_vector
+
+
+# ---------------------------------------------------------------- helpers
+
+def _src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_kv_cache_block_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_file: str, alg_bytes: int):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current source of the kernel."""
+    path = os.path.join(ROOT, "profiles", "counters_decode_int4_llama8b.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("source_sha") != _src_hash(kernel_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _time_events(torch, fn, iters):
+    """Mean ms of fn() over iters launches, HIP events on the current stream."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+class DecodeBench:
+    """Full-size Llama-3-8B layer: RING cache copies, per-step new tokens."""
+
+    def __init__(self, torch, kvq, workloads, block, seed=2):
+        self.torch, self.kvq = torch, kvq
+        dev = "cuda"
+        w = workloads.llama8b_decode(seed, device=dev, batch=64, context=4096, block=block)
+        self.w = w
+        self.bt = torch.from_numpy(w.block_table).to(dev)
+        self.sl = torch.from_numpy(w.seq_lens).to(dev)
+        self.ws = torch.empty(max(16, kvq.kvq_decode_workspace_bytes(w.batch, w.hq, w.hkv, w.d,
+                                                                     w.max_seq_len)),
+                              dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=dev)
+        # per-step new token (position 4095 of every sequence) and query
+        g = torch.Generator(device=dev)
+        g.manual_seed(77)
+        last = (w.token_pos == w.seq_lens[w.token_seq] - 1)
+        self.new_slots = w.slot_mapping[torch.from_numpy(last).to(dev)].contiguous()
+        shape = (RING, w.batch, w.hkv, w.d)
+        self.knew = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+        self.vnew = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+        self.qs = torch.randn((RING, w.batch, w.hq, w.d), generator=g, device=dev).to(torch.bfloat16)
+        self.block = block
+        self.int4 = [kvq.Int4Cache(w.num_pages, w.hkv, w.d, block, dev) for _ in range(RING)]
+        for c in self.int4:
+            kvq.kvq_append_paged(c, w.k, w.v, w.slot_mapping)
+        self.bf16 = None
+        torch.cuda.synchronize()
+
+    def refill(self, block):
+        w, kvq = self.w, self.kvq
+        self.block = block
+        for c in self.int4:
+            c.hadamard_block = block
+            kvq.kvq_append_paged(c, w.k, w.v, w.slot_mapping)
+        self.torch.cuda.synchronize()
+
+    def make_bf16(self):
+        w, kvq = self.w, self.kvq
+        self.bf16 = [kvq.Bf16Cache(w.num_pages, w.hkv, w.d, "cuda") for _ in range(2)]
+        for c in self.bf16:
+            kvq.kvq_append_paged_bf16(c, w.k, w.v, w.slot_mapping)
+        self.torch.cuda.synchronize()
+
+    def append(self, i):
+        self.kvq.kvq_append_paged(self.int4[i % RING], self.knew[i % RING], self.vnew[i % RING],
+                                  self.new_slots)
+
+    def decode(self, i):
+        w = self.w
+        self.kvq.kvq_decode_attn(self.int4[i % RING], self.qs[i % RING], self.bt, self.sl,
+                                 w.max_seq_len, w.sm_scale, out=self.out, workspace=self.ws)
+
+    def decode_bf16(self, i):
+        w = self.w
+        self.kvq.kvq_decode_attn_bf16(self.bf16[i % 2], self.qs[i % RING], self.bt, self.sl,
+                                      w.max_seq_len, w.sm_scale, out=self.out, workspace=self.ws)
+
+    def free(self):
+        self.int4 = self.bf16 = None
+        self.torch.cuda.empty_cache()
+
+
+def prefill_rate(torch, kvq, workloads, block, iters=50):
+    """Rotate+quantize append of 32768 ragged tokens (8 KV heads, d 128) into a
+    page-16 pool: Mtokens/s and GB/s, RING input/cache sets."""
+    sets = []
+    for r in range(RING):
+        w = workloads.prefill_append(3 + 10 * r, device="cuda", block=block)
+        sets.append((w, kvq.Int4Cache(w.num_pages, w.hkv, w.d, block, "cuda")))
+
+    def run(i):
+        w, c = sets[i % RING]
+        kvq.kvq_append_paged(c, w.k, w.v, w.slot_mapping)
+
+    for i in range(10):
+        run(i)
+    mean_ms, med_ms = _time_events(torch, run, iters)
+    w = sets[0][0]
+    tok = w.num_tokens
+    nbytes = append_bytes(tok, w.hkv, w.d, int4_bytes_per_vector(w.d))
+    return {"mtok_s": tok / (mean_ms * 1e-3) / 1e6, "gb_s": nbytes / (mean_ms * 1e-3) / 1e9,
+            "us": mean_ms * 1e3, "bytes": nbytes, "tokens": tok}
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The oracle (as it stands) on the host cores over a bounded sample of the
+    same workload: host copies of whole sequences are appended (rotate +
+    quantize) and attended in fp64 for all 32 query heads, one sequence at a
+    time until the time budget is spent."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from workloads import bits
+
+    pool = oracle.new_int4_pool(w.num_pages, w.hkv, w.d)
+    qh = bits(w.q)
+    t_app = t_dec = 0.0
+    done = []
+    for b in range(w.batch):
+        sel = torch.from_numpy(w.token_seq == b).to(w.k.device)
+        kh, vh = bits(w.k[sel]), bits(w.v[sel])
+        sm = w.slot_mapping[sel].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.append_int4(pool, w.num_pages, w.hkv, w.d, w.block, kh, vh, oracle.BF16, sm)
+        t1 = time.perf_counter()
+        mask = np.zeros((w.batch, w.hq), np.uint8)
+        mask[b] = 1
+        oracle.decode_int4(pool, w.hkv, w.d, w.block, qh, oracle.BF16, w.block_table, w.seq_lens,
+                           w.sm_scale, mask=mask)
+        t2 = time.perf_counter()
+        t_app += t1 - t0
+        t_dec += t2 - t1
+        done.append(b)
+        if t_app + t_dec > budget_s:
+            break
+    lens = [int(w.seq_lens[b]) for b in done]
+    dbytes = decode_bytes(lens, w.hkv, w.hq, w.d, int4_bytes_per_vector(w.d))
+    tokens = sum(lens)
+    return {
+        "value": dbytes / t_dec / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{len(done)} of {w.batch} sequences x {lens[0]} tokens, all {w.hq} q heads, "
+                  f"block {w.block}: oracle append then fp64 decode; decode {t_dec:.2f} s, "
+                  f"append {t_app:.2f} s",
+        "append_mtok_s": tokens / t_app / 1e6,
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=["full", "decode", "copy"], default="full")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path shards by "
+                                   "KV head or sequence with no exchange, see the design notes",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+    import bit_kv_cache_block_amd as kvq
+    import workloads
+
+    if args.mode == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+        return 0
+
+    db = DecodeBench(torch, kvq, workloads, block=64)
+    w = db.w
+    kvb = int4_bytes_per_vector(w.d)
+    dec_bytes = decode_bytes(w.seq_lens, w.hkv, w.hq, w.d, kvb)
+    app_bytes = append_bytes(w.batch, w.hkv, w.d, kvb)
+
+    if args.mode == "decode":
+        for i in range(args.warmup):
+            db.decode(i)
+        ms, _ = _time_events(torch, db.decode, args.steps)
+        print(json.dumps({"mode": "decode", "us": ms * 1e3, "gb_s": dec_bytes / (ms * 1e-3) / 1e9}))
+        return 0
+
+    # ---- headline: K steps of append + decode ------------------------------
+    for i in range(args.warmup):
+        db.append(i)
+        db.decode(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        db.append(i)
+        ev[i][1].record()
+        db.decode(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    app_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    dec_mean = sum(dec_ms) / len(dec_ms)
+    app_mean = sum(app_ms) / len(app_ms)
+    value = dec_bytes / (dec_mean * 1e-3) / 1e9
+
+    # ---- variants on the same workload --------------------------------------
+    variants = {}
+    for blk in (0, 16, 32, 128):
+        db.refill(blk)
+        for i in range(10):
+            db.decode(i)
+        ms, _ = _time_events(torch, db.decode, args.steps)
+        variants[f"int4_block{blk}" if blk else "int4_plain"] = dec_bytes / (ms * 1e-3) / 1e9
+    variants["int4_block64"] = value
+    db.refill(64)
+    db.int4 = db.int4[:1]
+    torch.cuda.empty_cache()
+    db.make_bf16()
+    for i in range(10):
+        db.decode_bf16(i)
+    ms_bf16, _ = _time_events(torch, db.decode_bf16, args.steps)
+    bf16_bytes = decode_bytes(w.seq_lens, w.hkv, w.hq, w.d, 2 * w.d)
+    cb = None
+    if not args.no_cpu:
+        cb = cpu_baseline(w)
+        cb["cpu_model"] = _cpu_model()
+    db.free()
+    del db
+
+    prefill_rot = prefill_rate(torch, kvq, workloads, 64)
+    prefill_plain = prefill_rate(torch, kvq, workloads, 0)
+    torch.cuda.empty_cache()
+
+    traffic = _traffic("decode_int4.hip", dec_bytes)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8-mfma/fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3-8b-shaped layer decode: 32 q / 8 kv heads, head_dim 128, "
+                        "batch 64 x 4096 context, page 16, hadamard block 64, bf16 K/V with "
+                        "4 key outlier channels x15; step = append 1 token/seq + decode",
+            "global_batch": w.batch, "seq_len": int(w.max_seq_len), "parallelism": "none",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "decode_us": round(dec_mean * 1e3, 2),
+        "append_us": round(app_mean * 1e3, 2),
+        "decode_bytes": dec_bytes,
+        "rotate_quant_mtok_s": round(prefill_rot["mtok_s"], 1),
+        "prefill_append": {
+            "workload": "32768 new tokens over 16 ragged sequences (512-4096), 8 kv heads, "
+                          "head_dim 128, bf16 Student-t(3), page-16 pool, block 64",
+            "rotated": {k: round(v, 2) for k, v in prefill_rot.items()},
+            "plain": {k: round(v, 2) for k, v in prefill_plain.items()},
+            "rotated_over_plain": round(prefill_rot["mtok_s"] / prefill_plain["mtok_s"], 4),
+        },
+        "decode_variants_gb_s": {k: round(v, 1) for k, v in sorted(variants.items())},
+        "rotated_over_plain_decode": round(value / variants["int4_plain"], 4),
+        "bf16_kv": {"gb_s": round(bf16_bytes / (ms_bf16 * 1e-3) / 1e9, 1),
+                    "us": round(ms_bf16 * 1e3, 2), "bytes": bf16_bytes,
+                    "int4_speedup": round(ms_bf16 / dec_mean, 3)},
+        "roofline": {
+            "bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(value / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_int4_kernel + reduce_kernel (one kvq_decode_attn call)",
+        },
+    }
+    line["cpu_baseline"] = None if cb is None else \
+        {k: (round(v, 5) if isinstance(v, float) else v) for k, v in cb.items()}
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -25,6 +25,8 @@ FLAGS = [
     "-ffp-contract=off",
     # no packed-fp32 instructions anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: their results feed VALU code directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

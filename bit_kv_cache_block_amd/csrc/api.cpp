@@ -85,11 +85,12 @@ SplitPlan plan_splits(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t n
   if (num_splits > 0) {
     s = num_splits;
   } else {
-    // enough waves for 256 CUs x 8 resident waves; splits no longer than 256
-    // pages (4096 tokens) so ragged batches stay balanced; at least 16 pages each
+    // four-wave workgroups: 512 of them fill 256 CUs with 8 waves each;
+    // splits no longer than 512 pages keep ragged batches balanced; at least
+    // 16 pages (one 4-page step per wave) each
     const int64_t units = static_cast<int64_t>(batch > 0 ? batch : 1) * hkv;
-    s = (2048 + units - 1) / units;
-    const int64_t by_len = (pages_max + 255) / 256;
+    s = (512 + units - 1) / units;
+    const int64_t by_len = (pages_max + 511) / 512;
     if (s < by_len) s = by_len;
     const int64_t min_len = (pages_max + 15) / 16;
     if (s > min_len) s = min_len;
@@ -104,6 +105,7 @@ SplitPlan plan_splits(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t n
 }
 
 size_t workspace_bytes(int32_t batch, int32_t hq, int32_t d, const SplitPlan& p) {
+  if (p.nsplit <= 1) return 0;   // unsplit work writes the output directly
   return static_cast<size_t>(batch) * hq * p.nsplit * (d + 2) * sizeof(float);
 }
 
@@ -146,7 +148,7 @@ kvq_status launch_decode(bool int4, const void* pool, int32_t num_pages, int32_t
   a.in_bf16 = dtype == KVQ_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = int4 ? launch_decode_int4(a, s) : launch_decode_bf16(a, s);
-  if (e == hipSuccess) e = launch_reduce(a, s);
+  if (e == hipSuccess && plan.nsplit > 1) e = launch_reduce(a, s);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;
 }

@@ -1,8 +1,9 @@
-// bf16-KV baseline of the split-K paged decode attention: the same wave
-// organisation and online softmax as the INT4 kernel, with bf16 MFMA.  The
-// query and the probabilities are each carried as three bf16 limbs (hi, mid,
-// lo: 24 significant bits), in the padded columns of the GQA group's tile, so
-// the products keep fp32 accuracy against the exact bf16 cache values.
+// bf16-KV baseline of the split-K paged decode attention: the same workgroup
+// organisation (four waves, LDS merge, direct output without a global split)
+// and online softmax as the INT4 kernel, with bf16 MFMA.  The query and the
+// probabilities are each carried as three bf16 limbs (hi, mid, lo: 24
+// significant bits) in the rows of the GQA group's tile, so the products keep
+// fp32 accuracy against the exact bf16 cache values.
 #include "dev_common.hpp"
 #include "kvq_internal.hpp"
 
@@ -10,6 +11,8 @@ namespace kvq {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kWaves = 4;
+constexpr int kStep = 2;   // pages per step (one 32-token PV product)
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
@@ -25,6 +28,19 @@ __device__ __forceinline__ uint16_t bf16_limb(float x, int lam) {
   return lam == 0 ? h : lam == 1 ? m : lam == 2 ? l : static_cast<uint16_t>(0);
 }
 
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
+  return fmaxf(x, dpp_f<kDppRowMirror>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppRowHalfMirror>(x);
+  return x + dpp_f<kDppRowMirror>(x);
+}
+
 template <int D>
 __device__ __forceinline__ int pv_channel(int n, int tau) {
   if constexpr (D == 128) return 8 * n + tau;
@@ -33,14 +49,32 @@ __device__ __forceinline__ int pv_channel(int n, int tau) {
 
 __device__ __forceinline__ v8bf as_bf(u32x4 w) { return __builtin_bit_cast(v8bf, w); }
 
+template <int D, int NS>
+struct SmemB {
+  static constexpr int kGP = 4 * NS;
+  union {
+    float qs[kGP][D];
+    struct {
+      float acc[kWaves][kGP][D];
+      float m[kWaves][kGP];
+      float l[kWaves][kGP];
+      float o[kGP][D];
+    } merge;
+  } u;
+  uint16_t pl[kWaves][NS][4][4][kStep][16];   // [wave][set][limb][head][page][token]
+};
+
 template <int D, int NS, bool QBF16>
-__global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int kSlab = 4 * kPage * D;   // bytes
   constexpr int kNT = D / 16;
   constexpr int kNK = D / 32;            // QK MFMAs per page
   constexpr int kGP = 4 * NS;
+  __shared__ SmemB<D, NS> sm;
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int lane = tid & 63;
   const int g = lane >> 4, n = lane & 15, hs = n >> 2, lam = n & 3;
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -50,22 +84,29 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   const int npg = (len + kPage - 1) / kPage;
   const int p0 = s * a.split_pages;
   const int p1 = min(npg, p0 + a.split_pages);
-  if (p0 >= p1) return;
+  if (p0 >= p1) {
+    if (a.nsplit == 1) {
+      for (int e = tid; e < G * D; e += 64 * kWaves)
+        a.out[(static_cast<int64_t>(b) * a.num_q_heads + kvh * G + e / D) * D + e % D] = 0.0f;
+    }
+    return;
+  }
 
-  __shared__ float qs[kGP][D];
-  for (int e = lane; e < kGP * D; e += 64) {
+  for (int e = tid; e < kGP * D; e += 64 * kWaves) {
     const int j = e / D, c = e % D;
     float v = 0.0f;
     if (j < G) {
       const uint16_t u = a.q[(static_cast<int64_t>(b) * a.num_q_heads + kvh * G + j) * D + c];
       v = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
     }
-    qs[j][c] = v;
+    sm.u.qs[j][c] = v;
   }
+  for (int e = tid; e < kWaves * NS * 4 * 4 * kStep * 16; e += 64 * kWaves)
+    (&sm.pl[0][0][0][0][0][0])[e] = 0;   // limb-3 rows stay zero
   __syncthreads();
 
-  // B operand of QK: limb `lam` of head (4st + hs), channels 32mu + 8g .. +7
-  u32x4 bq[NS][kNK];
+  // A operand of QK: row (head hs, limb lam), channels 32mu + 8g .. +7
+  u32x4 aq[NS][kNK];
 #pragma unroll
   for (int st = 0; st < NS; ++st)
 #pragma unroll
@@ -74,11 +115,16 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 32 * mu + 8 * g + 2 * i;
-        w[i] = static_cast<uint32_t>(bf16_limb(qs[4 * st + hs][c], lam)) |
-               (static_cast<uint32_t>(bf16_limb(qs[4 * st + hs][c + 1], lam)) << 16);
+        w[i] = static_cast<uint32_t>(bf16_limb(sm.u.qs[4 * st + hs][c], lam)) |
+               (static_cast<uint32_t>(bf16_limb(sm.u.qs[4 * st + hs][c + 1], lam)) << 16);
       }
-      bq[st][mu] = w;
+      aq[st][mu] = w;
     }
+
+  const int span = p1 - p0;
+  const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
+  const int pw0 = p0 + wave * per_wave;
+  const int pw1 = min(p1, pw0 + per_wave);
 
   float m_run[NS], l_run[NS], acc[NS][kNT];
 #pragma unroll
@@ -94,81 +140,97 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   const int vn = n & (D / 8 - 1);
   const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int p = p0; p < p1; p += 2) {
-    u32x4 kx[2][kNK], vx[2][4];
-    bool pv[2];
+  const int k_off = (n * D + 8 * g) * 2;
+  const int v_off = (kPage * D + (vn * (kPage / 4) + g) * 32) * 2;
+  for (int p = pw0; p < pw1; p += kStep) {
+    int pid[kStep];
+    bool pv[kStep];
+    bool all_ok = true;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kStep; ++i) {
       const int pg = p + i;
-      const int pid = pg < p1 ? bt[pg] : -1;
-      pv[i] = pid >= 0 && pid < a.num_pages;
-      if (pv[i]) {
-        const uint8_t* sl = pool_h + static_cast<int64_t>(pid) * page_stride;
+      const int id = pg < pw1 ? bt[pg] : -1;
+      pv[i] = id >= 0 && id < a.num_pages;
+      pid[i] = pv[i] ? id : 0;
+      all_ok = all_ok && pv[i];
+    }
+    const bool tail = !all_ok || (p + kStep) * kPage > len;
+    u32x4 kx[kStep][kNK], vx[kStep][4];
 #pragma unroll
-        for (int mu = 0; mu < kNK; ++mu)
-          kx[i][mu] = *reinterpret_cast<const u32x4*>(sl + (n * D + 32 * mu + 8 * g) * 2);
+    for (int i = 0; i < kStep; ++i) {
+      const uint8_t* sl = pool_h + static_cast<int64_t>(pid[i]) * page_stride;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          vx[i][qq] = *reinterpret_cast<const u32x4*>(sl + (kPage * D + (vn * (kPage / 4) + g) * 32) * 2 + 16 * qq);
-      } else {
+      for (int mu = 0; mu < kNK; ++mu) kx[i][mu] = *reinterpret_cast<const u32x4*>(sl + k_off + 64 * mu);
 #pragma unroll
-        for (int mu = 0; mu < kNK; ++mu) kx[i][mu] = u32x4{0u, 0u, 0u, 0u};
+      for (int qq = 0; qq < 4; ++qq) vx[i][qq] = *reinterpret_cast<const u32x4*>(sl + v_off + 16 * qq);
+    }
+    if (tail) {
+      // zero the values of tokens past the end (or of unusable pages) so that
+      // stale bits there never meet the zero weights as NaN or Inf
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) vx[i][qq] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < kStep; ++i) {
+        const int t0 = (p + i) * kPage + 4 * g;
+        const uint32_t m01 = (pv[i] && t0 < len ? 0x0000FFFFu : 0u) | (pv[i] && t0 + 1 < len ? 0xFFFF0000u : 0u);
+        const uint32_t m23 = (pv[i] && t0 + 2 < len ? 0x0000FFFFu : 0u) | (pv[i] && t0 + 3 < len ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          vx[i][qq][0] &= m01;
+          vx[i][qq][1] &= m23;
+          vx[i][qq][2] &= m01;
+          vx[i][qq][3] &= m23;
+        }
       }
     }
 
-    float lg[NS][2][4];
+    float lg[NS][kStep];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kStep; ++i) {
+      const bool ok = !tail || (pv[i] && (p + i) * kPage + n < len);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         v4f c = zero4;
 #pragma unroll
-        for (int mu = 0; mu < kNK; ++mu) c = mfma_bf16(as_bf(kx[i][mu]), as_bf(bq[st][mu]), c);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          float v = c[rr];
-          v += dpp_f<kDppXor1>(v);
-          v += dpp_f<kDppXor2>(v);
-          const int tok = (p + i) * kPage + 4 * g + rr;
-          lg[st][i][rr] = (pv[i] && tok < len) ? v * a.sm_log2 : kNegInf;
-        }
+        for (int mu = 0; mu < kNK; ++mu) c = mfma_bf16(as_bf(aq[st][mu]), as_bf(kx[i][mu]), c);
+        lg[st][i] = ok ? ((c[0] + c[1]) + c[2]) * a.sm_log2 : kNegInf;
       }
+    }
 
-    u32x4 apv[NS];
-    float alpha_pv[NS];
+    float alpha[NS];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      float mc = kNegInf;
+      float mc = lg[st][0];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) mc = fmaxf(mc, lg[st][i][rr]);
-      mc = max_rows(mc);
+      for (int i = 1; i < kStep; ++i) mc = fmaxf(mc, lg[st][i]);
+      mc = row_max16(mc);
       const float mnew = fmaxf(m_run[st], mc);
       const float muse = mnew == kNegInf ? 0.0f : mnew;
-      const float alpha = exp2f(m_run[st] - muse);
+      alpha[st] = exp2f(m_run[st] - muse);
       m_run[st] = mnew;
       float psum = 0.0f;
-      uint16_t lb[2][4];
+      uint16_t* pl = &sm.pl[wave][st][0][0][0][0];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float pp = exp2f(lg[st][i][rr] - muse);
-          psum += pp;
-          lb[i][rr] = bf16_limb(pp, lam);
-        }
-      l_run[st] = l_run[st] * alpha + psum;
-      u32x4 av;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        av[2 * i] = static_cast<uint32_t>(lb[i][0]) | (static_cast<uint32_t>(lb[i][1]) << 16);
-        av[2 * i + 1] = static_cast<uint32_t>(lb[i][2]) | (static_cast<uint32_t>(lb[i][3]) << 16);
+      for (int i = 0; i < kStep; ++i) {
+        const float pp = exp2f(lg[st][i] - muse);
+        psum += pp;
+        const uint16_t h = bf16_bits(pp);
+        const float r1 = pp - bf16_val(h);
+        const uint16_t m = bf16_bits(r1);
+        const uint16_t lo = bf16_bits(r1 - bf16_val(m));
+        pl[((0 * 4 + g) * kStep + i) * 16 + n] = h;
+        pl[((1 * 4 + g) * kStep + i) * 16 + n] = m;
+        pl[((2 * 4 + g) * kStep + i) * 16 + n] = lo;
       }
-      apv[st] = av;
-      alpha_pv[st] = lane_read(alpha, 4 * g);
+      l_run[st] = __builtin_fmaf(l_run[st], alpha[st], psum);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    u32x4 apv[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const uint16_t* pl = &sm.pl[wave][st][0][0][0][0];
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(pl + ((lam * 4 + hs) * kStep + 0) * 16 + 4 * g);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(pl + ((lam * 4 + hs) * kStep + 1) * 16 + 4 * g);
+      apv[st] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
 
 #pragma unroll
@@ -176,36 +238,55 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
       const int jj = (D == 128) ? tau : 2 * tau + (n >> 3);   // channel 8*vn + jj
       u32x4 bv;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        // 64 bytes per page = 16 words: channel jj occupies words 2jj, 2jj+1
-        const int w0 = 2 * jj;
+      for (int i = 0; i < kStep; ++i) {
+        const int w0 = 2 * jj;   // four tokens of one channel = words 2jj, 2jj+1
         bv[2 * i] = vx[i][w0 >> 2][w0 & 3];
         bv[2 * i + 1] = vx[i][(w0 + 1) >> 2][(w0 + 1) & 3];
       }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         const v4f c = mfma_bf16(as_bf(apv[st]), as_bf(bv), zero4);
-        const float f = (c[0] + c[1]) + c[2];
-        acc[st][tau] = __builtin_fmaf(acc[st][tau], alpha_pv[st], f);
+        acc[st][tau] = __builtin_fmaf(acc[st][tau], alpha[st], (c[0] + c[1]) + c[2]);
       }
     }
   }
 
-  const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
+  __syncthreads();
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
-    const float lt = sum_rows(lam == 0 ? l_run[st] : 0.0f);
-    const int jp = 4 * st + g;
-    if (jp < G) {
-      float* dst = a.part_acc + ((hq0 + jp) * a.nsplit + s) * D;
+    const float lt = row_sum16(l_run[st]);
+    const int j = 4 * st + g;
 #pragma unroll
-      for (int tau = 0; tau < kNT; ++tau) dst[pv_channel<D>(n, tau)] = acc[st][tau];
+    for (int tau = 0; tau < kNT; ++tau) sm.u.merge.acc[wave][j][pv_channel<D>(n, tau)] = acc[st][tau];
+    if (n == 0) {
+      sm.u.merge.m[wave][j] = m_run[st];
+      sm.u.merge.l[wave][j] = lt;
     }
-    const int jq = 4 * st + hs;
-    if (g == 0 && lam == 0 && jq < G) {
-      const int64_t idx = (hq0 + jq) * a.nsplit + s;
-      a.part_ml[idx * 2 + 0] = m_run[st];
-      a.part_ml[idx * 2 + 1] = lt;
+  }
+  __syncthreads();
+  const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
+  for (int e = tid; e < G * D; e += 64 * kWaves) {
+    const int j = e / D, c = e % D;
+    float mstar = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, sm.u.merge.m[w][j]);
+    const float muse = mstar == kNegInf ? 0.0f : mstar;
+    float lsum = 0.0f, osum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = exp2f(sm.u.merge.m[w][j] - muse);
+      lsum = __builtin_fmaf(sm.u.merge.l[w][j], f, lsum);
+      osum = __builtin_fmaf(sm.u.merge.acc[w][j][c], f, osum);
+    }
+    if (a.nsplit == 1) {
+      a.out[(hq0 + j) * D + c] = lsum > 0.0f ? osum / lsum : 0.0f;
+    } else {
+      const int64_t idx = (hq0 + j) * a.nsplit + s;
+      a.part_acc[idx * D + c] = osum;
+      if (c == 0) {
+        a.part_ml[idx * 2 + 0] = mstar;
+        a.part_ml[idx * 2 + 1] = lsum;
+      }
     }
   }
 }
@@ -214,9 +295,9 @@ template <int D, int NS>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.nsplit, a.num_kv_heads, a.batch);
   if (a.in_bf16)
-    decode_bf16_kernel<D, NS, true><<<grid, 64, 0, s>>>(a);
+    decode_bf16_kernel<D, NS, true><<<grid, 64 * kWaves, 0, s>>>(a);
   else
-    decode_bf16_kernel<D, NS, false><<<grid, 64, 0, s>>>(a);
+    decode_bf16_kernel<D, NS, false><<<grid, 64 * kWaves, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -23,14 +23,18 @@ __device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(flo
 constexpr int kDppXor1 = 0xB1;
 constexpr int kDppXor2 = 0x4E;
 constexpr int kDppBcast0 = 0x00;   // quad_perm [0,0,0,0]
+constexpr int kDppRowMirror = 0x140;      // lane i <- 15 - i within a row of 16
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- 7 - i within each half row
 
+// Every pattern used reads an existing lane of the same row, so bound_ctrl
+// is irrelevant; setting it lets the compiler fold the move into its user.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-  return u2f(__builtin_amdgcn_update_dpp(0u, f2u(x), CTRL, 0xF, 0xF, false));
+  return u2f(__builtin_amdgcn_mov_dpp(f2u(x), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-  return __builtin_amdgcn_update_dpp(0u, x, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
 }
 
 // ---- row-crossing exchanges with the gfx950 permlane swaps ------------------

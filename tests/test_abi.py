@@ -78,8 +78,10 @@ def test_append_zero_tokens_is_a_noop():
     assert _append(_int4(), k=0, v=0, slots=0, n=0) == kvq.KVQ_OK
 
 
-def _decode(desc, q=FAKE, dtype=kvq.KVQ_BF16, hq=8, bt=FAKE, maxp=16, sl=FAKE, batch=4,
-            maxlen=256, sm=0.125, splits=0, out=FAKE, ws=FAKE, wsb=0):
+def _decode(desc, q=FAKE, dtype=kvq.KVQ_BF16, hq=8, bt=FAKE, maxp=256, sl=FAKE, batch=4,
+            maxlen=4096, sm=0.125, splits=0, out=FAKE, ws=FAKE, wsb=0):
+    # the defaults need a split-K workspace (4 x 4096 tokens over 2 KV heads),
+    # so with wsb = 0 every call here is rejected before anything is launched
     L = kvq.lib()
     return L.kvq_decode_attn(C.byref(desc), q, dtype, hq, bt, maxp, sl, batch, maxlen, sm, splits,
                              out, ws, wsb, None)
@@ -91,7 +93,7 @@ def _decode(desc, q=FAKE, dtype=kvq.KVQ_BF16, hq=8, bt=FAKE, maxp=16, sl=FAKE, b
     ({"q": 0}, kvq.KVQ_ERR_INVALID_ARGUMENT),
     ({"out": FAKE + 4}, kvq.KVQ_ERR_INVALID_ARGUMENT),
     ({"bt": 0}, kvq.KVQ_ERR_INVALID_ARGUMENT),
-    ({"maxp": 8}, kvq.KVQ_ERR_INVALID_ARGUMENT),      # 8 pages < 256 tokens
+    ({"maxp": 8}, kvq.KVQ_ERR_INVALID_ARGUMENT),      # 8 pages < 4096 tokens
     ({"sm": float("nan")}, kvq.KVQ_ERR_INVALID_ARGUMENT),
     ({"batch": -1}, kvq.KVQ_ERR_INVALID_ARGUMENT),
     ({"splits": -2}, kvq.KVQ_ERR_INVALID_ARGUMENT),
@@ -102,7 +104,7 @@ def test_decode_validation(kw, status):
 
 
 def test_decode_workspace_too_small_by_one():
-    need = kvq.kvq_decode_workspace_bytes(4, 8, 2, 64, 256, 0)
+    need = kvq.kvq_decode_workspace_bytes(4, 8, 2, 64, 4096, 0)
     assert need > 0
     assert _decode(_int4(), wsb=need - 1) == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
 
@@ -116,7 +118,8 @@ def test_bf16_entry_points_validate():
     bad = kvq._Bf16Desc(FAKE, 4, 16, 2, 100)
     assert L.kvq_append_paged_bf16(C.byref(bad), FAKE, FAKE, 1, 128, FAKE, 1, None) == kvq.KVQ_ERR_UNSUPPORTED
     ok = kvq._Bf16Desc(FAKE, 4, 16, 2, 64)
-    assert L.kvq_decode_attn_bf16(C.byref(ok), FAKE, 1, 8, FAKE, 16, FAKE, 4, 256, 0.1, 0, FAKE,
+    assert kvq.kvq_decode_workspace_bytes(4, 8, 2, 64, 4096, 0) > 0
+    assert L.kvq_decode_attn_bf16(C.byref(ok), FAKE, 1, 8, FAKE, 256, FAKE, 4, 4096, 0.1, 0, FAKE,
                                   FAKE, 0, None) == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
 
 
@@ -128,12 +131,13 @@ def test_workspace_covers_every_split(batch, hkv, maxlen):
     hq, d = hkv * 4, 128
     ws = kvq.kvq_decode_workspace_bytes(batch, hq, hkv, d, maxlen, 0)
     assert ws % (batch * hq * (d + 2) * 4) == 0
-    nsplit = ws // (batch * hq * (d + 2) * 4)
+    nsplit = max(1, ws // (batch * hq * (d + 2) * 4))   # 0 bytes: unsplit, no workspace
     pages = (maxlen + 15) // 16
     assert 1 <= nsplit <= max(1, (pages + 3) // 4)
     for s in (1, 2, 5):
         ws_s = kvq.kvq_decode_workspace_bytes(batch, hq, hkv, d, maxlen, s)
         assert ws_s // (batch * hq * (d + 2) * 4) <= s
+    assert kvq.kvq_decode_workspace_bytes(batch, hq, hkv, d, maxlen, 1) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -261,3 +261,26 @@ def test_full_size_llama_layer_sampled():
     want = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table,
                               w.seq_lens, w.sm_scale, mask=mask)
     assert_close(out.cpu().numpy().astype(np.float64)[sample], want[sample], "full llama sampled")
+
+
+def test_decode_ignores_stale_bytes_in_unwritten_slots():
+    """Pools pre-filled with 0xFF (NaN as fp16 / bf16): the slots past each
+    sequence's end are never written, and must not leak into the result."""
+    w = workloads.random_decode(14, batch=4, hq=8, hkv=2, d=128, block=64,
+                                seq_lens=[1, 17, 30, 77])
+    cache = kvq.Int4Cache(w.num_pages, w.hkv, w.d, 64, DEV)
+    cache.pool.fill_(0xFF)
+    kvq.kvq_append_paged(cache, w.k.to(DEV), w.v.to(DEV), w.slot_mapping.to(DEV))
+    pool = oracle_int4_pool(w, 64)
+    want = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table,
+                              w.seq_lens, w.sm_scale)
+    assert_close(gpu_decode(cache, w), want, "int4 stale")
+    bc = kvq.Bf16Cache(w.num_pages, w.hkv, w.d, DEV)
+    bc.pool.fill_(0xFF)
+    kvq.kvq_append_paged_bf16(bc, w.k.to(DEV), w.v.to(DEV), w.slot_mapping.to(DEV))
+    bpool = oracle.new_bf16_pool(w.num_pages, w.hkv, w.d)
+    oracle.append_bf16(bpool, w.num_pages, w.hkv, w.d, bits(w.k), bits(w.v), oracle.BF16,
+                       w.slot_mapping.numpy())
+    bwant = oracle.decode_bf16(bpool, w.hkv, w.d, bits(w.q), oracle.BF16, w.block_table,
+                               w.seq_lens, w.sm_scale)
+    assert_close(gpu_decode(bc, w, bf16=True), bwant, "bf16 stale")
