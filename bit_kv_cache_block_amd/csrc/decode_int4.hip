@@ -6,7 +6,8 @@
 // idea of "InnerQ", Figure 1).
 //
 // A workgroup of four waves owns one (sequence b, KV head, split s) and each
-// wave streams a quarter of its pages, four pages per step.  Per page and per
+// wave streams a quarter of its pages, four pages per step, with the next
+// step's loads in flight while the current step computes.  Per page and per
 // group of four query heads:
 //   QK:  C[(head, limb)][token] = sum_c qlimb[c] * code[token][c]   (int8 MFMA)
 //        The rotated query is a 23-bit fixed-point integer split into three
@@ -20,11 +21,13 @@
 //        step's largest w of the head (power-of-two scale), its limbs moved to
 //        the operand layout through a 1 KiB LDS tile; sum_t p * v_zero is added
 //        to every channel at the end.
-// The four waves merge in LDS.  With one split the workgroup normalises,
-// rotates back and writes the output; otherwise it writes a partial
-// (max, sum, unnormalised output) for the reduce kernel.
+// The four waves merge in LDS.  With one split each wave finishes heads of the
+// group (normalise, rotate back, store); otherwise it stores a partial (max,
+// sum, unnormalised output) for the reduce kernel.
 #include "dev_common.hpp"
 #include "kvq_internal.hpp"
+
+#include <type_traits>
 
 namespace kvq {
 namespace {
@@ -82,19 +85,24 @@ template <int D, int NS>
 struct Smem {
   static constexpr int kGP = 4 * NS;
   union {
-    struct {
-      float qs[kGP][D];
-      int32_t qi[kGP][D];
-    } setup;
+    int32_t qi[kGP][D];
     struct {
       float acc[kWaves][kGP][D];
       float m[kWaves][kGP];
       float l[kWaves][kGP];
-      float o[kGP][D];
     } merge;
   } u;
   float hA[kGP], hS[kGP];
   uint32_t wl[kWaves][NS][4][4][16];   // [wave][set][limb][head][token] = 4 pages' bytes
+};
+
+// one step's loads: four pages of one KV head
+struct StepBuf {
+  u32x4 kx[kStep];
+  u32x4 vx[kStep];
+  uint32_t km[kStep], vm[kStep];
+  bool pv[kStep];
+  bool all_ok;
 };
 
 template <int D, int NS, bool QBF16>
@@ -103,6 +111,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   constexpr int kNT = D / 16;          // PV tiles = output channels per lane
   constexpr int kOps = D / 64;         // QK MFMAs per page and head group
   constexpr int kGP = 4 * NS;          // padded heads per KV head
+  constexpr int kVL = D / 64;          // channels per lane in the per-wave vector form
   __shared__ Smem<D, NS> sm;
 
   const int tid = threadIdx.x;
@@ -111,6 +120,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   const int g = lane >> 4, n = lane & 15, hs = n >> 2, lam = n & 3;
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.num_q_heads / a.num_kv_heads;
+  const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
 
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
@@ -119,53 +129,96 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   const int p1 = min(npg, p0 + a.split_pages);
   if (p0 >= p1) {
     if (a.nsplit == 1) {   // empty sequence: zero output rows
-      for (int e = tid; e < G * D; e += 64 * kWaves)
-        a.out[(static_cast<int64_t>(b) * a.num_q_heads + kvh * G + e / D) * D + e % D] = 0.0f;
+      for (int e = tid; e < G * D; e += 64 * kWaves) a.out[hq0 * D + e] = 0.0f;
     }
     return;
   }
 
-  // ---- query: load, rotate (fp32 butterfly), fixed point -------------------
-  for (int e = tid; e < kGP * D; e += 64 * kWaves) {
-    const int j = e / D, c = e % D;
-    float v = 0.0f;
-    if (j < G) {
-      const uint16_t u = a.q[(static_cast<int64_t>(b) * a.num_q_heads + kvh * G + j) * D + c];
-      v = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
+  // ---- this wave's share of the split's pages, first step's loads in flight
+  const int span = p1 - p0;
+  const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
+  const int pw0 = p0 + wave * per_wave;
+  const int pw1 = min(p1, pw0 + per_wave);
+  const uint8_t* pool_h = a.pool + static_cast<int64_t>(kvh) * kSlab;
+  const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kSlab;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const int vn = n & (D / 8 - 1);
+  const int k_off = (D == 128) ? n * (D / 2) + g * 16 : n * (D / 2) + g * 8;
+  const int v_off = kPage * D / 2 + (vn * kPage + 4 * g) * 4;
+  const int km_off = kPage * D + 4 * n;
+
+  // Page ids of this wave's range, 64 at a time: lane i of ids_cur holds the
+  // id of page cb + i (-1 past the end), ids_next the following 64.  A step
+  // pulls its four ids out with readlane (wave-uniform, no memory round trip).
+  // An id outside the pool reads page 0 and is masked out of the softmax.
+  auto load_ids = [&](int first) {
+    const int pg = first + lane;
+    return pg < pw1 ? bt[pg] : -1;
+  };
+  int cb = pw0;
+  int ids_cur = load_ids(pw0);
+  int ids_next = load_ids(pw0 + 64);
+  auto page_id = [&](int pg) {
+    const int rel = pg - cb;
+    return rel < 64 ? __builtin_amdgcn_readlane(ids_cur, rel) : __builtin_amdgcn_readlane(ids_next, rel - 64);
+  };
+  auto load = [&](StepBuf& sb, int p) {
+    sb.all_ok = true;
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) {
+      const int pg = p + i;
+      const int id = pg < pw1 ? page_id(pg) : -1;
+      sb.pv[i] = id >= 0 && id < a.num_pages;
+      sb.all_ok = sb.all_ok && sb.pv[i];
+      const uint8_t* sl = pool_h + static_cast<int64_t>(sb.pv[i] ? id : 0) * page_stride;
+      if constexpr (D == 128) {
+        sb.kx[i] = *reinterpret_cast<const u32x4*>(sl + k_off);
+      } else {
+        const u32x2 t2 = *reinterpret_cast<const u32x2*>(sl + k_off);
+        sb.kx[i] = u32x4{t2[0], t2[1], 0u, 0u};
+      }
+      sb.vx[i] = *reinterpret_cast<const u32x4*>(sl + v_off);
+      sb.km[i] = *reinterpret_cast<const uint32_t*>(sl + km_off);
+      sb.vm[i] = *reinterpret_cast<const uint32_t*>(sl + km_off + 4 * kPage);
     }
-    sm.u.setup.qs[j][c] = v;
-  }
+  };
+  StepBuf buf0, buf1;
+  if (pw0 < pw1) load(buf0, pw0);
+
+  // ---- query: per wave one head at a time, rotated in registers -----------
   for (int e = tid; e < kWaves * NS * 4 * 4 * 16; e += 64 * kWaves)
     (&sm.wl[0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
-  __syncthreads();
-  if (a.block > 0) {
-    for (int hh = 1; hh < a.block; hh *= 2) {
-      for (int pi = tid; pi < kGP * D / 2; pi += 64 * kWaves) {
-        const int j = pi / (D / 2), q = pi % (D / 2);
-        const int i = (q / hh) * (2 * hh) + (q % hh);
-        const float u = sm.u.setup.qs[j][i], w = sm.u.setup.qs[j][i + hh];
-        sm.u.setup.qs[j][i] = u + w;
-        sm.u.setup.qs[j][i + hh] = u - w;
+  for (int j = wave; j < kGP; j += kWaves) {
+    float v[kVL];
+#pragma unroll
+    for (int k = 0; k < kVL; ++k) {
+      const int c = kVL * lane + k;
+      v[k] = 0.0f;
+      if (j < G) {
+        const uint16_t u = a.q[(hq0 + j) * D + c];
+        v[k] = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
       }
-      __syncthreads();
     }
-    const float sb = block_norm(a.block);
-    for (int e = tid; e < kGP * D; e += 64 * kWaves) sm.u.setup.qs[e / D][e % D] *= sb;
-    __syncthreads();
-  }
-  for (int j = wave; j < kGP; j += kWaves) {   // one wave per head
+    if (a.block > 0) {
+      fwht_wave<D>(v, a.block, lane);
+      const float sb = block_norm(a.block);
+#pragma unroll
+      for (int k = 0; k < kVL; ++k) v[k] *= sb;
+    }
     float am = 0.0f;
-    for (int c = lane; c < D; c += 64) am = fmaxf(am, fabsf(sm.u.setup.qs[j][c]));
+#pragma unroll
+    for (int k = 0; k < kVL; ++k) am = fmaxf(am, fabsf(v[k]));
     for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
     int ex = 0;
     frexpf(am, &ex);                    // am < 2^ex
     ex = ex < -100 ? -100 : ex;         // keeps 2^(22-ex) finite; smaller q is ~0
     const float sc = ldexpf(1.0f, 22 - ex);
     int32_t sum = 0;
-    for (int c = lane; c < D; c += 64) {
-      const int32_t v = static_cast<int32_t>(rintf(sm.u.setup.qs[j][c] * sc));
-      sm.u.setup.qi[j][c] = v;
-      sum += v;
+#pragma unroll
+    for (int k = 0; k < kVL; ++k) {
+      const int32_t qv = static_cast<int32_t>(rintf(v[k] * sc));
+      sm.u.qi[j][kVL * lane + k] = qv;
+      sum += qv;
     }
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
     if (lane == 0) {
@@ -184,24 +237,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
     qS[st] = sm.hS[4 * st + g];
 #pragma unroll
     for (int op = 0; op < kOps; ++op) {
-      v4i v;
+      v4i vv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t w = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          w |= limb_byte(sm.u.setup.qi[4 * st + hs][qk_channel<D>(g, op, i, k)], lam) << (8 * k);
-        v[i] = static_cast<int32_t>(w);
+          w |= limb_byte(sm.u.qi[4 * st + hs][qk_channel<D>(g, op, i, k)], lam) << (8 * k);
+        vv[i] = static_cast<int32_t>(w);
       }
-      aq[st][op] = v;
+      aq[st][op] = vv;
     }
   }
-
-  // ---- this wave's share of the split's pages --------------------------------
-  const int span = p1 - p0;
-  const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
-  const int pw0 = p0 + wave * per_wave;
-  const int pw1 = min(p1, pw0 + per_wave);
 
   float m_run[NS], l_run[NS], z_run[NS], acc[NS][kNT];
 #pragma unroll
@@ -212,47 +259,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[st][t] = 0.0f;
   }
-  const uint8_t* pool_h = a.pool + static_cast<int64_t>(kvh) * kSlab;
-  const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kSlab;
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  const int vn = n & (D / 8 - 1);
   const v4i zero4 = {0, 0, 0, 0};
-  const int wl_row = ((0 * 4 + lam) * 4 + hs) * 16 + 4 * g;   // reader offset (set 0) in dwords
+  const int wl_row = (lam * 4 + hs) * 16 + 4 * g;   // reader offset within a set, dwords
 
-  const int k_off = (D == 128) ? n * (D / 2) + g * 16 : n * (D / 2) + g * 8;
-  const int v_off = kPage * D / 2 + (vn * kPage + 4 * g) * 4;
-  const int km_off = kPage * D + 4 * n;
-  for (int p = pw0; p < pw1; p += kStep) {
-    // page ids are wave-uniform; an id outside the pool reads page 0 and is
-    // masked out of the softmax (the masked path also zeroes its weights)
-    int pid[kStep];
-    bool pv[kStep];
-    bool all_ok = true;
-#pragma unroll
-    for (int i = 0; i < kStep; ++i) {
-      const int pg = p + i;
-      const int id = pg < pw1 ? bt[pg] : -1;
-      pv[i] = id >= 0 && id < a.num_pages;
-      pid[i] = pv[i] ? id : 0;
-      all_ok = all_ok && pv[i];
-    }
-    const bool tail = !all_ok || (p + kStep) * kPage > len;
-    u32x4 kx[kStep], vx[kStep];
-    uint32_t km[kStep], vm[kStep];
-#pragma unroll
-    for (int i = 0; i < kStep; ++i) {
-      const uint8_t* sl = pool_h + static_cast<int64_t>(pid[i]) * page_stride;
-      if constexpr (D == 128) {
-        kx[i] = *reinterpret_cast<const u32x4*>(sl + k_off);
-      } else {
-        const u32x2 t2 = *reinterpret_cast<const u32x2*>(sl + k_off);
-        kx[i] = u32x4{t2[0], t2[1], 0u, 0u};
-      }
-      vx[i] = *reinterpret_cast<const u32x4*>(sl + v_off);
-      km[i] = *reinterpret_cast<const uint32_t*>(sl + km_off);
-      vm[i] = *reinterpret_cast<const uint32_t*>(sl + km_off + 4 * kPage);
-    }
-
+  auto compute = [&](const StepBuf& sb, int p, auto mask_tag) {
+    constexpr bool tail = decltype(mask_tag)::value;
     // QK: lane (g, n) gets the four limb rows of head g (per set), token n
     float lg[NS][kStep];
 #pragma unroll
@@ -261,15 +272,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
       if constexpr (D == 128) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          b0[w] = static_cast<int32_t>(kx[i][w] & kLowNibbles);
-          b1[w] = static_cast<int32_t>((kx[i][w] >> 4) & kLowNibbles);
+          b0[w] = static_cast<int32_t>(sb.kx[i][w] & kLowNibbles);
+          b1[w] = static_cast<int32_t>((sb.kx[i][w] >> 4) & kLowNibbles);
         }
       } else {
-        b0 = v4i{static_cast<int32_t>(kx[i][0] & kLowNibbles), static_cast<int32_t>(kx[i][1] & kLowNibbles),
-                 static_cast<int32_t>((kx[i][0] >> 4) & kLowNibbles),
-                 static_cast<int32_t>((kx[i][1] >> 4) & kLowNibbles)};
+        b0 = v4i{static_cast<int32_t>(sb.kx[i][0] & kLowNibbles), static_cast<int32_t>(sb.kx[i][1] & kLowNibbles),
+                 static_cast<int32_t>((sb.kx[i][0] >> 4) & kLowNibbles),
+                 static_cast<int32_t>((sb.kx[i][1] >> 4) & kLowNibbles)};
       }
-      const bool ok = !tail || (pv[i] && (p + i) * kPage + n < len);
+      const bool ok = !tail || (sb.pv[i] && (p + i) * kPage + n < len);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         v4i c = mfma_i8(aq[st][0], b0, zero4);
@@ -277,7 +288,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
         // limbs: c0 * 2^16 + c1 * 2^8 + c2 (c0 * 2^8 + c1 is exact in int32)
         const float tq = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f,
                                         static_cast<float>(c[2]));
-        const float l2 = qA[st] * __builtin_fmaf(half_hi(km[i]), qS[st], half_lo(km[i]) * tq);
+        const float l2 = qA[st] * __builtin_fmaf(half_hi(sb.km[i]), qS[st], half_lo(sb.km[i]) * tq);
         lg[st][i] = ok ? l2 : kNegInf;
       }
     }
@@ -299,11 +310,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
         psum += pp;
         if (tail) {
           const bool ok = lg[st][i] != kNegInf;
-          zsum += ok ? pp * half_hi(vm[i]) : 0.0f;
-          w[i] = ok ? pp * half_lo(vm[i]) : 0.0f;
+          zsum += ok ? pp * half_hi(sb.vm[i]) : 0.0f;
+          w[i] = ok ? pp * half_lo(sb.vm[i]) : 0.0f;
         } else {
-          zsum = __builtin_fmaf(pp, half_hi(vm[i]), zsum);
-          w[i] = pp * half_lo(vm[i]);
+          zsum = __builtin_fmaf(pp, half_hi(sb.vm[i]), zsum);
+          w[i] = pp * half_lo(sb.vm[i]);
         }
         wmax = fmaxf(wmax, w[i]);
       }
@@ -317,7 +328,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
       sw[st] = ldexpf(1.0f, ew - 22);
       uint32_t y[kStep];
 #pragma unroll
-      for (int i = 0; i < kStep; ++i) y[i] = static_cast<uint32_t>(static_cast<int32_t>(rintf(w[i] * wsc)) + 0x8080);
+      for (int i = 0; i < kStep; ++i)
+        y[i] = static_cast<uint32_t>(static_cast<int32_t>(rintf(w[i] * wsc)) + 0x8080);
       // limb bytes of the four pages, one word per limb: bytes 2 / 1 / 0 of y
       const uint32_t l0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0602u),
                                                 __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0602u), 0x05040100u);
@@ -341,7 +353,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
     // word holds the four pages' codes of one channel pair; nibbles split it.
     uint32_t vt[4][4];   // [r][byte j]
 #pragma unroll
-    for (int r = 0; r < 4; ++r) transpose_bytes4(vx[0][r], vx[1][r], vx[2][r], vx[3][r], vt[r]);
+    for (int r = 0; r < 4; ++r) transpose_bytes4(sb.vx[0][r], sb.vx[1][r], sb.vx[2][r], sb.vx[3][r], vt[r]);
 #pragma unroll
     for (int tau = 0; tau < kNT; ++tau) {
       v4i bv;
@@ -360,10 +372,32 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
         acc[st][tau] = __builtin_fmaf(f, sw[st], acc[st][tau] * alpha[st]);
       }
     }
+  };
+
+  // ---- stream: compute step k while step k+1 loads --------------------------
+  auto step = [&](const StepBuf& sb, int p) {
+    if (!sb.all_ok || (p + kStep) * kPage > len)
+      compute(sb, p, std::true_type{});
+    else
+      compute(sb, p, std::false_type{});
+  };
+  for (int p = pw0; p < pw1; p += 2 * kStep) {
+    if (p + kStep < pw1) load(buf1, p + kStep);
+    step(buf0, p);
+    if (p + kStep >= pw1) break;
+    if (p + 2 * kStep < pw1) load(buf0, p + 2 * kStep);
+    step(buf1, p + kStep);
+    if (p + 3 * kStep >= cb + 64) {
+      // the next step to load starts in the following 64 ids: slide the window
+      // (every later load stays below cb + 128)
+      cb += 64;
+      ids_cur = ids_next;
+      ids_next = load_ids(cb + 64);
+    }
   }
 
   // ---- merge the four waves --------------------------------------------------
-  __syncthreads();   // setup scratch is reused below
+  __syncthreads();   // the query scratch is reused below
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     const float lt = row_sum16(l_run[st]);
@@ -377,48 +411,45 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
     }
   }
   __syncthreads();
-  const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
-  for (int e = tid; e < G * D; e += 64 * kWaves) {
-    const int j = e / D, c = e % D;
+  for (int j = wave; j < G; j += kWaves) {   // one wave per head
     float mstar = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, sm.u.merge.m[w][j]);
     const float muse = mstar == kNegInf ? 0.0f : mstar;
-    float lsum = 0.0f, osum = 0.0f;
+    float f[kWaves], lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = exp2f(sm.u.merge.m[w][j] - muse);
-      lsum = __builtin_fmaf(sm.u.merge.l[w][j], f, lsum);
-      osum = __builtin_fmaf(sm.u.merge.acc[w][j][c], f, osum);
+      f[w] = exp2f(sm.u.merge.m[w][j] - muse);
+      lsum = __builtin_fmaf(sm.u.merge.l[w][j], f[w], lsum);
+    }
+    float o[kVL];
+#pragma unroll
+    for (int k = 0; k < kVL; ++k) {
+      o[k] = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) o[k] = __builtin_fmaf(sm.u.merge.acc[w][j][kVL * lane + k], f[w], o[k]);
     }
     if (a.nsplit == 1) {
-      sm.u.merge.o[j][c] = lsum > 0.0f ? osum / lsum : 0.0f;
+      const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+#pragma unroll
+      for (int k = 0; k < kVL; ++k) o[k] *= inv;
+      float scale = 1.0f;
+      if (a.block > 0) {
+        fwht_wave<D>(o, a.block, lane);
+        scale = block_norm(a.block);
+      }
+#pragma unroll
+      for (int k = 0; k < kVL; ++k) a.out[(hq0 + j) * D + kVL * lane + k] = o[k] * scale;
     } else {
       const int64_t idx = (hq0 + j) * a.nsplit + s;
-      a.part_acc[idx * D + c] = osum;
-      if (c == 0) {
+#pragma unroll
+      for (int k = 0; k < kVL; ++k) a.part_acc[idx * D + kVL * lane + k] = o[k];
+      if (lane == 0) {
         a.part_ml[idx * 2 + 0] = mstar;
         a.part_ml[idx * 2 + 1] = lsum;
       }
     }
   }
-  if (a.nsplit != 1) return;
-  __syncthreads();
-  if (a.block > 0) {
-    for (int hh = 1; hh < a.block; hh *= 2) {
-      for (int pi = tid; pi < G * D / 2; pi += 64 * kWaves) {
-        const int j = pi / (D / 2), q = pi % (D / 2);
-        const int i = (q / hh) * (2 * hh) + (q % hh);
-        const float u = sm.u.merge.o[j][i], w = sm.u.merge.o[j][i + hh];
-        sm.u.merge.o[j][i] = u + w;
-        sm.u.merge.o[j][i + hh] = u - w;
-      }
-      __syncthreads();
-    }
-  }
-  const float sb = a.block > 0 ? block_norm(a.block) : 1.0f;
-  for (int e = tid; e < G * D; e += 64 * kWaves)
-    a.out[(hq0 + e / D) * D + e % D] = sm.u.merge.o[e / D][e % D] * sb;
 }
 
 template <int D, int NS>

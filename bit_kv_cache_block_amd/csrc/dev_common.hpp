@@ -107,6 +107,35 @@ __device__ __forceinline__ uint32_t pack8_nibbles(const uint32_t c[8]) {
   return lo | (hi << 16);
 }
 
+// Block Walsh-Hadamard butterfly over one vector spread across a wave:
+// D = 128: lane l holds channels 2l, 2l+1 in v[0], v[1]; D = 64: lane l holds
+// channel l in v[0].  Stages h = 1, 2, 4, ..., block/2 in ascending order; the
+// lower element of each pair becomes x + y, the upper x - y.  Unnormalised.
+template <int D>
+__device__ __forceinline__ void fwht_wave(float* v, int block, int lane) {
+  if constexpr (D == 128) {
+    if (block < 2) return;
+    const float a = v[0], b = v[1];
+    v[0] = a + b;
+    v[1] = a - b;
+    for (int h = 2; h < block; h *= 2) {
+      const int dl = h >> 1;
+      const bool upper = (lane & dl) != 0;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float partner = __shfl_xor(v[k], dl);
+        v[k] = upper ? partner - v[k] : v[k] + partner;
+      }
+    }
+  } else {
+    for (int h = 1; h < block; h *= 2) {
+      const bool upper = (lane & h) != 0;
+      const float partner = __shfl_xor(v[0], h);
+      v[0] = upper ? partner - v[0] : v[0] + partner;
+    }
+  }
+}
+
 // fp32 constant 1/sqrt(b) of a Hadamard block (the correctly rounded values
 // 0x3E800000, 0x3E3504F3, 0x3E000000, 0x3DB504F3 for b = 16, 32, 64, 128).
 __device__ __forceinline__ float block_norm(int b) {
