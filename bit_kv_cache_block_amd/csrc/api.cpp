@@ -1,7 +1,7 @@
 // C ABI of libkvq.so (declared in include/kvq.h): host-side validation, split
 // planning and dispatch.  Nothing here allocates device memory or
 // synchronizes; every launch goes to the caller's stream.
-#include "../../include/kvq.h"
+#include "kvq.h"
 
 #include <hip/hip_runtime.h>
 

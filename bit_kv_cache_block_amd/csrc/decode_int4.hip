@@ -35,6 +35,7 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaves = 4;
 constexpr int kStep = 4;   // pages per step
+constexpr int kDepth = 2;  // steps in registers: 2 = one in flight, 3 = two in flight
 
 __device__ __forceinline__ float half_lo(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
@@ -43,15 +44,20 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
 }
 
-// byte `lam` of the balanced base-256 split v = l0*2^16 + l1*2^8 + l2 with
-// l1, l2 in [-128, 127] (|v| <= 2^22); lam = 3 gives 0.
-__device__ __forceinline__ uint32_t limb_byte(int32_t v, int lam) {
-  const int32_t y = v + 0x8080;
-  const uint32_t b0 = static_cast<uint32_t>(y >> 16) & 0xFFu;
-  const uint32_t b1 = ((static_cast<uint32_t>(y) >> 8) & 0xFFu) ^ 0x80u;
-  const uint32_t b2 = (static_cast<uint32_t>(y) & 0xFFu) ^ 0x80u;
-  return lam == 0 ? b0 : lam == 1 ? b1 : lam == 2 ? b2 : 0u;
-}
+// Limbs of the balanced base-256 split v = l0*2^16 + l1*2^8 + l2 with l1, l2
+// in [-128, 127] (|v| <= 2^22): with y = v + 0x8080, limb 0 is byte 2 of y,
+// limbs 1 and 2 are bytes 1 and 0 of y with the top bit flipped.  A lane
+// extracts its own limb `lam` (3 = the zero pad row) branch-free with the
+// per-lane shift / flip / keep constants below.
+struct LimbSel {
+  uint32_t shift, flip, keep;
+  __device__ explicit LimbSel(int lam)
+      : shift(lam < 3 ? 16u - 8u * lam : 0u), flip(lam == 1 || lam == 2 ? 0x80u : 0u),
+        keep(lam < 3 ? 0xFFu : 0u) {}
+  __device__ __forceinline__ uint32_t byte(int32_t v) const {
+    return ((static_cast<uint32_t>(v + 0x8080) >> shift) ^ flip) & keep;
+  }
+};
 
 // max / sum over the 16 lanes of a row, result in every lane of the row
 __device__ __forceinline__ float row_max16(float x) {
@@ -122,10 +128,36 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
 
+  // ---- prologue: loads that do not depend on seq_lens go out first ----------
+  // query: per wave one head at a time (two consecutive channels per lane at
+  // D = 128); padding heads read head G-1 and are zeroed below
+  uint32_t qraw[NS];
+#pragma unroll
+  for (int r = 0; r < NS; ++r) {
+    const int j = min(wave + kWaves * r, G - 1);
+    const uint16_t* qp = a.q + (hq0 + j) * D + kVL * lane;
+    qraw[r] = (D == 128) ? *reinterpret_cast<const uint32_t*>(qp) : static_cast<uint32_t>(*qp);
+  }
+  // Page ids of this wave's range, 64 at a time: lane i of ids_cur holds the
+  // id of page cb + i, ids_next the following 64.  A step pulls its four ids
+  // out with readlane (wave-uniform, no memory round trip).  They are fetched
+  // first for the range a full-length split gives this wave, and again only if
+  // the sequence is shorter and its balanced range starts elsewhere.  An id
+  // outside the pool reads page 0 and is masked out of the softmax.
+  const int p0 = s * a.split_pages;
+  const int per_wave_full = ((a.split_pages + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  int cb = p0 + wave * per_wave_full;
+  int ids_cur, ids_next;
+  {
+    const int pg = cb + lane, lim = min(p0 + a.split_pages, a.bt_stride);
+    ids_cur = pg < lim ? bt[pg] : -1;
+    ids_next = pg + 64 < lim ? bt[pg + 64] : -1;
+  }
+
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
   const int npg = (len + kPage - 1) / kPage;
-  const int p0 = s * a.split_pages;
   const int p1 = min(npg, p0 + a.split_pages);
   if (p0 >= p1) {
     if (a.nsplit == 1) {   // empty sequence: zero output rows
@@ -134,30 +166,28 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
     return;
   }
 
-  // ---- this wave's share of the split's pages, first step's loads in flight
+  // ---- this wave's share of the split's pages ---------------------------------
   const int span = p1 - p0;
   const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
   const int pw0 = p0 + wave * per_wave;
   const int pw1 = min(p1, pw0 + per_wave);
   const uint8_t* pool_h = a.pool + static_cast<int64_t>(kvh) * kSlab;
   const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kSlab;
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
   const int vn = n & (D / 8 - 1);
-  const int k_off = (D == 128) ? n * (D / 2) + g * 16 : n * (D / 2) + g * 8;
-  const int v_off = kPage * D / 2 + (vn * kPage + 4 * g) * 4;
-  const int km_off = kPage * D + 4 * n;
-
-  // Page ids of this wave's range, 64 at a time: lane i of ids_cur holds the
-  // id of page cb + i (-1 past the end), ids_next the following 64.  A step
-  // pulls its four ids out with readlane (wave-uniform, no memory round trip).
-  // An id outside the pool reads page 0 and is masked out of the softmax.
+  // lane offsets within a page slab, unsigned so that each load is a uniform
+  // 64-bit base plus a 32-bit lane offset
+  const uint32_t k_off = (D == 128) ? n * (D / 2) + g * 16 : n * (D / 2) + g * 8;
+  const uint32_t v_off = kPage * D / 2 + (vn * kPage + 4 * g) * 4;
+  const uint32_t km_off = kPage * D + 4 * n;
   auto load_ids = [&](int first) {
     const int pg = first + lane;
     return pg < pw1 ? bt[pg] : -1;
   };
-  int cb = pw0;
-  int ids_cur = load_ids(pw0);
-  int ids_next = load_ids(pw0 + 64);
+  if (cb != pw0) {   // shorter sequence: its balanced range starts elsewhere
+    cb = pw0;
+    ids_cur = load_ids(pw0);
+    ids_next = load_ids(pw0 + 64);
+  }
   auto page_id = [&](int pg) {
     const int rel = pg - cb;
     return rel < 64 ? __builtin_amdgcn_readlane(ids_cur, rel) : __builtin_amdgcn_readlane(ids_next, rel - 64);
@@ -170,35 +200,51 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
       const int id = pg < pw1 ? page_id(pg) : -1;
       sb.pv[i] = id >= 0 && id < a.num_pages;
       sb.all_ok = sb.all_ok && sb.pv[i];
+      // one buffer descriptor per page slab (scalar registers): each load is
+      // that base plus the lane's 32-bit offset; nothing can reach past the slab
       const uint8_t* sl = pool_h + static_cast<int64_t>(sb.pv[i] ? id : 0) * page_stride;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, kSlab);
       if constexpr (D == 128) {
-        sb.kx[i] = *reinterpret_cast<const u32x4*>(sl + k_off);
+        sb.kx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, k_off, 0, 0));
       } else {
-        const u32x2 t2 = *reinterpret_cast<const u32x2*>(sl + k_off);
+        const u32x2 t2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, k_off, 0, 0));
         sb.kx[i] = u32x4{t2[0], t2[1], 0u, 0u};
       }
-      sb.vx[i] = *reinterpret_cast<const u32x4*>(sl + v_off);
-      sb.km[i] = *reinterpret_cast<const uint32_t*>(sl + km_off);
-      sb.vm[i] = *reinterpret_cast<const uint32_t*>(sl + km_off + 4 * kPage);
+      sb.vx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, 0, 0));
+      sb.km[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off, 0, 0);
+      sb.vm[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off + 4 * kPage, 0, 0);
     }
   };
-  StepBuf buf0, buf1;
-  if (pw0 < pw1) load(buf0, pw0);
-
-  // ---- query: per wave one head at a time, rotated in registers -----------
-  for (int e = tid; e < kWaves * NS * 4 * 4 * 16; e += 64 * kWaves)
-    (&sm.wl[0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
-  for (int j = wave; j < kGP; j += kWaves) {
-    float v[kVL];
+  // the query is consumed before the first page loads are issued, so waiting
+  // for it never waits for them
+  float qv[NS][kVL];
+#pragma unroll
+  for (int r = 0; r < NS; ++r) {
+    const int j = wave + kWaves * r;
 #pragma unroll
     for (int k = 0; k < kVL; ++k) {
-      const int c = kVL * lane + k;
-      v[k] = 0.0f;
-      if (j < G) {
-        const uint16_t u = a.q[(hq0 + j) * D + c];
-        v[k] = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
-      }
+      const uint16_t u = static_cast<uint16_t>(qraw[r] >> (16 * k));
+      const float x = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
+      qv[r][k] = j < G ? x : 0.0f;
     }
+  }
+  // materialise the query here (its wait drains only the query and the ids)
+  // and keep the page loads below this point
+#pragma unroll
+  for (int r = 0; r < NS; ++r)
+#pragma unroll
+    for (int k = 0; k < kVL; ++k) asm volatile("" : : "v"(qv[r][k]) : "memory");
+  StepBuf buf0, buf1;
+  if (pw0 < pw1) load(buf0, pw0);
+  // ---- query: rotate in registers, fixed point, limbs ------------------------
+  for (int e = tid; e < kWaves * NS * 4 * 4 * 16; e += 64 * kWaves)
+    (&sm.wl[0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
+#pragma unroll
+  for (int r = 0; r < NS; ++r) {
+    const int j = wave + kWaves * r;
+    float v[kVL];
+#pragma unroll
+    for (int k = 0; k < kVL; ++k) v[k] = qv[r][k];
     if (a.block > 0) {
       fwht_wave<D>(v, a.block, lane);
       const float sb = block_norm(a.block);
@@ -228,13 +274,25 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   }
   __syncthreads();
 
-  // A operand of QK: row (head hs, limb lam), k-slots of lane group g
+  // A operand of QK: row (head hs, limb lam), k-slots of lane group g: the
+  // lane's D/4 consecutive channels, read from LDS as whole vectors
+  const LimbSel limb(lam);
   v4i aq[NS][kOps];
   float qA[NS], qS[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     qA[st] = sm.hA[4 * st + g];          // C-layout head of this lane: row group g
     qS[st] = sm.hS[4 * st + g];
+    int32_t qc[D / 4];
+    const v4i* src = reinterpret_cast<const v4i*>(&sm.u.qi[4 * st + hs][(D / 4) * g]);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const v4i x = src[t];
+      qc[4 * t] = x[0];
+      qc[4 * t + 1] = x[1];
+      qc[4 * t + 2] = x[2];
+      qc[4 * t + 3] = x[3];
+    }
 #pragma unroll
     for (int op = 0; op < kOps; ++op) {
       v4i vv;
@@ -243,7 +301,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
         uint32_t w = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          w |= limb_byte(sm.u.qi[4 * st + hs][qk_channel<D>(g, op, i, k)], lam) << (8 * k);
+          w |= limb.byte(qc[qk_channel<D>(0, op, i, k)]) << (8 * k);
         vv[i] = static_cast<int32_t>(w);
       }
       aq[st][op] = vv;
@@ -381,18 +439,38 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
     else
       compute(sb, p, std::false_type{});
   };
-  for (int p = pw0; p < pw1; p += 2 * kStep) {
-    if (p + kStep < pw1) load(buf1, p + kStep);
-    step(buf0, p);
-    if (p + kStep >= pw1) break;
-    if (p + 2 * kStep < pw1) load(buf0, p + 2 * kStep);
-    step(buf1, p + kStep);
-    if (p + 3 * kStep >= cb + 64) {
-      // the next step to load starts in the following 64 ids: slide the window
-      // (every later load stays below cb + 128)
-      cb += 64;
-      ids_cur = ids_next;
-      ids_next = load_ids(cb + 64);
+  if constexpr (kDepth == 2) {
+    for (int p = pw0; p < pw1; p += 2 * kStep) {
+      if (p + kStep < pw1) load(buf1, p + kStep);
+      step(buf0, p);
+      if (p + kStep >= pw1) break;
+      if (p + 2 * kStep < pw1) load(buf0, p + 2 * kStep);
+      step(buf1, p + kStep);
+      if (p + 3 * kStep >= cb + 64) {
+        // the next step to load starts in the following 64 ids: slide the
+        // window (every later load stays below cb + 128)
+        cb += 64;
+        ids_cur = ids_next;
+        ids_next = load_ids(cb + 64);
+      }
+    }
+  } else {
+    StepBuf buf2;
+    if (pw0 + kStep < pw1) load(buf1, pw0 + kStep);
+    for (int p = pw0; p < pw1; p += 3 * kStep) {
+      if (p + 2 * kStep < pw1) load(buf2, p + 2 * kStep);
+      step(buf0, p);
+      if (p + kStep >= pw1) break;
+      if (p + 3 * kStep < pw1) load(buf0, p + 3 * kStep);
+      step(buf1, p + kStep);
+      if (p + 2 * kStep >= pw1) break;
+      if (p + 4 * kStep < pw1) load(buf1, p + 4 * kStep);
+      step(buf2, p + 2 * kStep);
+      if (p + 5 * kStep >= cb + 64) {
+        cb += 64;
+        ids_cur = ids_next;
+        ids_next = load_ids(cb + 64);
+      }
     }
   }
 

@@ -136,6 +136,13 @@ __device__ __forceinline__ void fwht_wave(float* v, int block, int lane) {
   }
 }
 
+// Raw buffer descriptor over [base, base + bytes): loads through it take a
+// 32-bit lane offset and return zero beyond `bytes` (word 3 = 32-bit data
+// format, the value raw loads expect on CDNA).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+
 // fp32 constant 1/sqrt(b) of a Hadamard block (the correctly rounded values
 // 0x3E800000, 0x3E3504F3, 0x3E000000, 0x3DB504F3 for b = 16, 32, 64, 128).
 __device__ __forceinline__ float block_norm(int b) {
