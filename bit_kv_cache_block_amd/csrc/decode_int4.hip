@@ -35,7 +35,7 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaves = 4;
 constexpr int kStep = 4;   // pages per step
-constexpr int kDepth = 2;  // steps in registers: 2 = one in flight, 3 = two in flight
+constexpr int kDepth = 1;  // steps in registers: 1 = none in flight while computing, 2 = one, 3 = two
 
 __device__ __forceinline__ float half_lo(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
@@ -439,7 +439,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
     else
       compute(sb, p, std::false_type{});
   };
-  if constexpr (kDepth == 2) {
+  if constexpr (kDepth == 1) {
+    for (int p = pw0; p < pw1; p += kStep) {
+      step(buf0, p);
+      if (p + kStep >= pw1) break;
+      if (p + kStep >= cb + 64) {   // the next step starts in the following 64 ids
+        cb += 64;
+        ids_cur = ids_next;
+        ids_next = load_ids(cb + 64);
+      }
+      load(buf0, p + kStep);
+    }
+  } else if constexpr (kDepth == 2) {
     for (int p = pw0; p < pw1; p += 2 * kStep) {
       if (p + kStep < pw1) load(buf1, p + kStep);
       step(buf0, p);
