@@ -205,14 +205,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
       const uint8_t* sl = pool_h + static_cast<int64_t>(sb.pv[i] ? id : 0) * page_stride;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, kSlab);
       if constexpr (D == 128) {
-        sb.kx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, k_off, 0, 0));
+        sb.kx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, k_off, 0, kStreamOnce));
       } else {
-        const u32x2 t2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, k_off, 0, 0));
+        const u32x2 t2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, k_off, 0, kStreamOnce));
         sb.kx[i] = u32x4{t2[0], t2[1], 0u, 0u};
       }
-      sb.vx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, 0, 0));
-      sb.km[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off, 0, 0);
-      sb.vm[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off + 4 * kPage, 0, 0);
+      sb.vx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, 0, kStreamOnce));
+      sb.km[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off, 0, kStreamOnce);
+      sb.vm[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off + 4 * kPage, 0, kStreamOnce);
     }
   };
   // the query is consumed before the first page loads are issued, so waiting
