@@ -24,7 +24,7 @@ constexpr int kHalfStride = kLaneElems * 2 + 16;  // LDS bytes per lane slot (+1
 template <int D>
 struct AppendShape {
   static constexpr int kLanesPerVec = D / kLaneElems;                   // 1 or 2
-  static constexpr int kRows = kAppendThreads / (2 * kLanesPerVec);     // (token, head) rows per block
+  static constexpr int kRows = kAppendThreads / (2 * kLanesPerVec);     // tokens per block
   static constexpr int kChunks = D / 8;                                 // 16-byte chunks per input row
   static constexpr int kSlab = kPage * (D + 8);                         // bytes per (page, head)
 };
@@ -44,32 +44,32 @@ __device__ __forceinline__ void widen8(u32x4 w, float* x) {
   }
 }
 
-// One block handles kRows consecutive (token, head) rows; lanes of waves 0-1
-// take the K vectors, waves 2-3 the V vectors; each lane owns 64 contiguous
-// channels of one vector (two lanes per vector at D = 128).
+// Block (x, h) handles kRows consecutive tokens of KV head h: lanes of waves
+// 0-1 take the K vectors, waves 2-3 the V vectors; each lane owns 64
+// contiguous channels of one vector (two lanes per vector at D = 128).
+// Consecutive lanes hold consecutive tokens, so tokens that fill a page in
+// order are written as whole contiguous runs of the page slab.
 template <int D, int BLK, bool BF16>
 __global__ __launch_bounds__(kAppendThreads) void append_int4_kernel(AppendArgs a) {
   using S = AppendShape<D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * S::kRows * S::kLanesPerVec * kHalfStride];
   const int tid = threadIdx.x;
-  const int hkv = a.num_kv_heads;
-  const int64_t total_rows = static_cast<int64_t>(a.num_tokens) * hkv;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * S::kRows;
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * S::kRows;
+  const int nrows = min(S::kRows, a.num_tokens - t0);
 
-  // 1. coalesced 16-byte loads of the block's K and V rows into LDS
+  // 1. coalesced 16-byte loads of the block's K and V rows into LDS (the
+  // inputs are read once: non-temporal)
 #pragma unroll
   for (int kind = 0; kind < 2; ++kind) {
-    const uint16_t* src = kind ? a.v : a.k;
+    const uint16_t* src = (kind ? a.v : a.k) + static_cast<int64_t>(t0) * a.token_stride + h * D;
 #pragma unroll
     for (int it = 0; it < S::kRows * S::kChunks / kAppendThreads; ++it) {
       const int c = tid + it * kAppendThreads;
       const int lr = c / S::kChunks, piece = c % S::kChunks;
-      const int64_t r = row0 + lr;
-      if (r < total_rows) {
-        const int64_t t = r / hkv;
-        const int h = static_cast<int>(r - t * hkv);
-        const u32x4 w = *reinterpret_cast<const u32x4*>(src + t * a.token_stride +
-                                                        static_cast<int64_t>(h) * D + piece * 8);
+      if (lr < nrows) {
+        const u32x4 w = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(lr) * a.token_stride + piece * 8));
         const int half = piece / 8, pp = piece % 8;
         *reinterpret_cast<u32x4*>(lds + ((kind * S::kRows + lr) * S::kLanesPerVec + half) * kHalfStride +
                                   pp * 16) = w;
@@ -83,7 +83,6 @@ __global__ __launch_bounds__(kAppendThreads) void append_int4_kernel(AppendArgs 
   const int j = tid % (kAppendThreads / 2);
   const int lr = j / S::kLanesPerVec;
   const int hf = j % S::kLanesPerVec;
-  const int64_t r = row0 + lr;
   float x[kLaneElems];
   {
     const uint8_t* base = lds + ((kind * S::kRows + lr) * S::kLanesPerVec + hf) * kHalfStride;
@@ -129,12 +128,20 @@ __global__ __launch_bounds__(kAppendThreads) void append_int4_kernel(AppendArgs 
     mn = fminf(mn, dpp_f<kDppXor1>(mn));
     mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
   }
+  // A power-of-two normalisation (b = 16, 64) is exact, so it is folded into
+  // the subtraction below: fma(x, s, -zero) rounds x*s - zero once, which is
+  // the rounding of (x*s) - zero.  (Only a product below 2^-126 can lose
+  // bits; that is far below half an ulp of any nonzero fp16 zero point, and
+  // with a zero zero point both forms are the rounded product.)
+  constexpr bool kExactNorm = BLK == 16 || BLK == 64;
+  const float sb = BLK > 0 ? block_norm(BLK) : 1.0f;
   if constexpr (BLK > 0) {
-    const float sb = block_norm(BLK);
     mn = mn * sb;
     mx = mx * sb;
+    if constexpr (!kExactNorm) {
 #pragma unroll
-    for (int k = 0; k < kLaneElems; ++k) x[k] = x[k] * sb;
+      for (int k = 0; k < kLaneElems; ++k) x[k] = x[k] * sb;
+    }
   }
 
   // 5. fp16 zero and scale, reciprocal (0 for a zero scale)
@@ -157,7 +164,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_int4_kernel(AppendArgs 
     uint32_t c[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float d = x[8 * m + i] - zf;
+      const float d = kExactNorm ? __builtin_fmaf(x[8 * m + i], sb, -zf) : x[8 * m + i] - zf;
       const float q = d * inv;
       const float t = __builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388623.0f);
       c[i] = f2u(t);
@@ -166,13 +173,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_int4_kernel(AppendArgs 
   }
 
   // 7. scatter into the slot's page
-  if (r >= total_rows) return;
-  const int64_t t = r / hkv;
-  const int h = static_cast<int>(r - t * hkv);
-  const int32_t slot = a.slot_mapping[t];
+  if (lr >= nrows) return;
+  const int32_t slot = a.slot_mapping[t0 + lr];
   if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(a.num_pages) * kPage) return;
   const int page = slot / kPage, off = slot % kPage;
-  uint8_t* slab = a.pool + (static_cast<int64_t>(page) * hkv + h) * S::kSlab;
+  uint8_t* slab = a.pool + (static_cast<int64_t>(page) * a.num_kv_heads + h) * S::kSlab;
   if (kind == 0) {
     u32x4* dst = reinterpret_cast<u32x4*>(slab + off * (D / 2) + hf * 32);
     dst[0] = u32x4{words[0], words[1], words[2], words[3]};
@@ -236,8 +241,7 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
 template <int D, int BLK>
 hipError_t launch_int4_d(const AppendArgs& a, hipStream_t s) {
   using S = AppendShape<D>;
-  const int64_t rows = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads;
-  const dim3 grid(static_cast<unsigned>((rows + S::kRows - 1) / S::kRows));
+  const dim3 grid(static_cast<unsigned>((a.num_tokens + S::kRows - 1) / S::kRows), static_cast<unsigned>(a.num_kv_heads));
   if (a.in_bf16)
     append_int4_kernel<D, BLK, true><<<grid, kAppendThreads, 0, s>>>(a);
   else
