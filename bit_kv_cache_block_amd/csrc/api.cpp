@@ -52,6 +52,8 @@ kvq_status check_append(const void* pool, const void* k, const void* v, kvq_dtyp
   if (token_stride < static_cast<int64_t>(hkv) * d)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "token_stride %lld < num_kv_heads*head_dim", (long long)token_stride);
   if (token_stride % 8 != 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "token_stride must be a multiple of 8 elements");
+  // the append kernel addresses a tile of 64 token rows with 32-bit offsets
+  if (token_stride > (int64_t{1} << 24)) return fail(KVQ_ERR_INVALID_ARGUMENT, "token_stride above 2^24 elements");
   return KVQ_OK;
 }
 

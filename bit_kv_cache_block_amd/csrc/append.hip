@@ -17,17 +17,12 @@
 namespace kvq {
 namespace {
 
-constexpr int kAppendThreads = 256;  // 4 waves
+constexpr int kAppendThreads = 256;  // 4 independent waves
 constexpr int kLaneElems = 64;       // elements of one vector owned by one lane
-constexpr int kHalfStride = kLaneElems * 2 + 16;  // LDS bytes per lane slot (+16 B pad)
-
-template <int D>
-struct AppendShape {
-  static constexpr int kLanesPerVec = D / kLaneElems;                   // 1 or 2
-  static constexpr int kRows = kAppendThreads / (2 * kLanesPerVec);     // tokens per block
-  static constexpr int kChunks = D / 8;                                 // 16-byte chunks per input row
-  static constexpr int kSlab = kPage * (D + 8);                         // bytes per (page, head)
-};
+// Waves stay resident and loop over work units: 768 workgroups of 4 waves
+// are 3 waves per SIMD on the 256 CUs of an MI355X (the kernel is held to
+// 168 VGPRs so that they all fit).
+constexpr int kResidentBlocks = 768;
 
 template <bool BF16>
 __device__ __forceinline__ void widen8(u32x4 w, float* x) {
@@ -44,153 +39,179 @@ __device__ __forceinline__ void widen8(u32x4 w, float* x) {
   }
 }
 
-// Block (x, h) handles kRows consecutive tokens of KV head h: lanes of waves
-// 0-1 take the K vectors, waves 2-3 the V vectors; each lane owns 64
-// contiguous channels of one vector (two lanes per vector at D = 128).
-// Consecutive lanes hold consecutive tokens, so tokens that fill a page in
-// order are written as whole contiguous runs of the page slab.
+// A work unit is (tile of kTok consecutive tokens, KV head, K or V) and
+// belongs to one wave.  The wave loads the tile's rows with coalesced 16-byte
+// loads (64 lanes cover 1 KiB of whole rows) and passes them through a
+// wave-private LDS region, from which lane (r, hf) takes channels
+// [64 hf, 64 hf + 64) of token t0 + r (two lanes per vector at D = 128, one
+// at D = 64).  The loads of the wave's next unit are issued before the
+// current one is computed.  Lanes of consecutive tokens write consecutive
+// words of a page slab, so tokens that fill a page in order are stored as
+// contiguous runs.
 template <int D, int BLK, bool BF16>
-__global__ __launch_bounds__(kAppendThreads) void append_int4_kernel(AppendArgs a) {
-  using S = AppendShape<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * S::kRows * S::kLanesPerVec * kHalfStride];
-  const int tid = threadIdx.x;
-  const int h = blockIdx.y;
-  const int t0 = blockIdx.x * S::kRows;
-  const int nrows = min(S::kRows, a.num_tokens - t0);
+__global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void append_int4_kernel(AppendArgs a) {
+  constexpr int kLPV = D / kLaneElems;   // lanes per vector
+  constexpr int kTok = 64 / kLPV;        // tokens per unit
+  constexpr int kChunks = D / 8;         // 16-byte pieces per row
+  constexpr int kSlab = kPage * (D + 8);
+  // a row is kLPV half slots of 128 B + 16 B pad: with this stride the
+  // 16-byte reads of any 8 consecutive lanes hit distinct LDS banks
+  constexpr int kHalf = 144, kRowBytes = kLPV * kHalf;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[kAppendThreads / 64][kTok * kRowBytes];
+  uint8_t* lds = lds_all[threadIdx.x >> 6];
+  const int lane = threadIdx.x & 63;
+  const int r = lane / kLPV, hf = lane % kLPV;
+  const uint32_t hkv = static_cast<uint32_t>(a.num_kv_heads);
+  const int64_t units = (static_cast<int64_t>(a.num_tokens) + kTok - 1) / kTok * hkv * 2;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * (kAppendThreads / 64);
+  int64_t u = static_cast<int64_t>(blockIdx.x) * (kAppendThreads / 64) + (threadIdx.x >> 6);
 
-  // 1. coalesced 16-byte loads of the block's K and V rows into LDS (the
-  // inputs are read once: non-temporal)
+  // unit -> (first token, head, kind); kind is the fastest index, so the K
+  // and V units of one (tile, head) run side by side
+  struct Unit { int t0, h, kind; };
+  auto unit = [&](int64_t uu) {
+    const int64_t rest = uu >> 1;
+    const int64_t tile = rest / hkv;
+    return Unit{static_cast<int>(tile * kTok), static_cast<int>(rest - tile * hkv), static_cast<int>(uu & 1)};
+  };
+  // Piece m of this lane is row lane / kChunks + m * kRowsPerLoad, chunk
+  // lane % kChunks.  One buffer descriptor spans the unit's rows that exist,
+  // so rows past the last token read as zeros.
+  constexpr int kRowsPerLoad = 64 / kChunks;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.token_stride) * 2u;
+  const uint32_t lane_off = static_cast<uint32_t>(lane / kChunks) * row_bytes + (lane % kChunks) * 16u;
+  auto load = [&](u32x4 (&pf)[8], int64_t uu) {
+    const Unit w = unit(uu);
+    const uint16_t* src = (w.kind ? a.v : a.k) + static_cast<int64_t>(w.t0) * a.token_stride + w.h * D;
+    const int rows = min(kTok, a.num_tokens - w.t0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, static_cast<int>(static_cast<uint32_t>(rows) * row_bytes));
 #pragma unroll
-  for (int kind = 0; kind < 2; ++kind) {
-    const uint16_t* src = (kind ? a.v : a.k) + static_cast<int64_t>(t0) * a.token_stride + h * D;
+    for (int m = 0; m < 8; ++m)
+      pf[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, lane_off, static_cast<int>(m * kRowsPerLoad * row_bytes), kStreamOnce));
+  };
+
+  u32x4 pf[8];
+  if (u < units) load(pf, u);
+  for (; u < units; u += stride) {
+    const Unit w = unit(u);
+    const int t = w.t0 + r;
 #pragma unroll
-    for (int it = 0; it < S::kRows * S::kChunks / kAppendThreads; ++it) {
-      const int c = tid + it * kAppendThreads;
-      const int lr = c / S::kChunks, piece = c % S::kChunks;
-      if (lr < nrows) {
-        const u32x4 w = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(lr) * a.token_stride + piece * 8));
-        const int half = piece / 8, pp = piece % 8;
-        *reinterpret_cast<u32x4*>(lds + ((kind * S::kRows + lr) * S::kLanesPerVec + half) * kHalfStride +
-                                  pp * 16) = w;
-      }
+    for (int m = 0; m < 8; ++m) {
+      const int c = lane + 64 * m, row = c / kChunks, chunk = c % kChunks;
+      *reinterpret_cast<u32x4*>(lds + row * kRowBytes + (chunk / 8) * kHalf + (chunk % 8) * 16) = pf[m];
     }
-  }
-  __syncthreads();
+    if (u + stride < units) load(pf, u + stride);
+    // the wave's LDS writes above complete before its reads below (LDS
+    // instructions of one wave execute in order)
+    float x[kLaneElems];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      widen8<BF16>(*reinterpret_cast<const u32x4*>(lds + r * kRowBytes + hf * kHalf + 16 * m), x + 8 * m);
 
-  // 2. each lane: 64 channels of one vector, widened to fp32
-  const int kind = tid / (kAppendThreads / 2);
-  const int j = tid % (kAppendThreads / 2);
-  const int lr = j / S::kLanesPerVec;
-  const int hf = j % S::kLanesPerVec;
-  float x[kLaneElems];
-  {
-    const uint8_t* base = lds + ((kind * S::kRows + lr) * S::kLanesPerVec + hf) * kHalfStride;
+    // block Hadamard butterfly, stages h = 1, 2, ..., BLK/2 ascending
+    if constexpr (BLK > 0) {
+      constexpr int kIn = BLK < kLaneElems ? BLK : kLaneElems;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) widen8<BF16>(*reinterpret_cast<const u32x4*>(base + 16 * m), x + 8 * m);
-  }
-
-  // 3. block Hadamard butterfly, stages h = 1, 2, ..., BLK/2 ascending
-  if constexpr (BLK > 0) {
-    constexpr int kIn = BLK < kLaneElems ? BLK : kLaneElems;
+      for (int hh = 1; hh < kIn; hh *= 2)
 #pragma unroll
-    for (int hh = 1; hh < kIn; hh *= 2)
+        for (int i = 0; i < kLaneElems; i += 2 * hh)
 #pragma unroll
-      for (int i = 0; i < kLaneElems; i += 2 * hh)
+          for (int k = i; k < i + hh; ++k) {
+            const float p = x[k], q = x[k + hh];
+            x[k] = p + q;
+            x[k + hh] = p - q;
+          }
+      if constexpr (BLK == 128) {
+        // last stage h = 64 pairs channel k (lane hf = 0) with k + 64 (hf = 1):
+        // lower half keeps own + partner, upper half partner - own; the
+        // product by +-1 is exact, so the fma rounds once like an add/sub.
+        const float sgn = hf ? -1.0f : 1.0f;
 #pragma unroll
-        for (int k = i; k < i + hh; ++k) {
-          const float u = x[k], w = x[k + hh];
-          x[k] = u + w;
-          x[k + hh] = u - w;
+        for (int k = 0; k < kLaneElems; ++k) {
+          const float p = dpp_f<kDppXor1>(x[k]);
+          x[k] = __builtin_fmaf(sgn, x[k], p);
         }
-    if constexpr (BLK == 128) {
-      // last stage h = 64 pairs channel k (lane hf = 0) with k + 64 (hf = 1):
-      // lower half keeps own + partner, upper half partner - own; the product
-      // by +-1 is exact, so the fma rounds exactly once like an add/sub.
-      const float sgn = hf ? -1.0f : 1.0f;
-#pragma unroll
-      for (int k = 0; k < kLaneElems; ++k) {
-        const float p = dpp_f<kDppXor1>(x[k]);
-        x[k] = __builtin_fmaf(sgn, x[k], p);
       }
     }
-  }
 
-  // 4. range.  Rounding is monotone, so min/max of the unscaled butterfly
-  // output, scaled once, equal min/max of the scaled elements.
-  float mn = x[0], mx = x[0];
+    // range.  Rounding is monotone, so min/max of the unscaled butterfly
+    // output, scaled once, equal min/max of the scaled elements.
+    float mn = x[0], mx = x[0];
 #pragma unroll
-  for (int k = 1; k < kLaneElems; ++k) {
-    mn = fminf(mn, x[k]);
-    mx = fmaxf(mx, x[k]);
-  }
-  if constexpr (S::kLanesPerVec == 2) {
-    mn = fminf(mn, dpp_f<kDppXor1>(mn));
-    mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
-  }
-  // A power-of-two normalisation (b = 16, 64) is exact, so it is folded into
-  // the subtraction below: fma(x, s, -zero) rounds x*s - zero once, which is
-  // the rounding of (x*s) - zero.  (Only a product below 2^-126 can lose
-  // bits; that is far below half an ulp of any nonzero fp16 zero point, and
-  // with a zero zero point both forms are the rounded product.)
-  constexpr bool kExactNorm = BLK == 16 || BLK == 64;
-  const float sb = BLK > 0 ? block_norm(BLK) : 1.0f;
-  if constexpr (BLK > 0) {
-    mn = mn * sb;
-    mx = mx * sb;
-    if constexpr (!kExactNorm) {
-#pragma unroll
-      for (int k = 0; k < kLaneElems; ++k) x[k] = x[k] * sb;
+    for (int k = 1; k < kLaneElems; ++k) {
+      mn = fminf(mn, x[k]);
+      mx = fmaxf(mx, x[k]);
     }
-  }
-
-  // 5. fp16 zero and scale, reciprocal (0 for a zero scale)
-  const float zero_f = mn + 0.0f;
-  const float range = (mx - mn) + 0.0f;
-  const float step = range / 15.0f;
-  const _Float16 sh = static_cast<_Float16>(step);
-  const _Float16 zh = static_cast<_Float16>(zero_f);
-  const float sf = static_cast<float>(sh);
-  const float zf = static_cast<float>(zh);
-  const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
-
-  // 6. codes: (y - zero) * inv, then round-half-even and clamp to [0, 15].
-  // Adding 2^23 rounds to an integer in the current (nearest-even) mode for
-  // any value in [0, 2^23); the clamp in that biased domain equals clamping
-  // the rounded value; the code is then the low 4 bits of the float.
-  uint32_t words[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float d = kExactNorm ? __builtin_fmaf(x[8 * m + i], sb, -zf) : x[8 * m + i] - zf;
-      const float q = d * inv;
-      const float t = __builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388623.0f);
-      c[i] = f2u(t);
+    if constexpr (kLPV == 2) {
+      mn = fminf(mn, dpp_f<kDppXor1>(mn));
+      mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
     }
-    words[m] = pack8_nibbles(c);
-  }
-
-  // 7. scatter into the slot's page
-  if (lr >= nrows) return;
-  const int32_t slot = a.slot_mapping[t0 + lr];
-  if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(a.num_pages) * kPage) return;
-  const int page = slot / kPage, off = slot % kPage;
-  uint8_t* slab = a.pool + (static_cast<int64_t>(page) * a.num_kv_heads + h) * S::kSlab;
-  if (kind == 0) {
-    u32x4* dst = reinterpret_cast<u32x4*>(slab + off * (D / 2) + hf * 32);
-    dst[0] = u32x4{words[0], words[1], words[2], words[3]};
-    dst[1] = u32x4{words[4], words[5], words[6], words[7]};
-  } else {
-    uint32_t* vw = reinterpret_cast<uint32_t*>(slab + kPage * D / 2);
+    // A power-of-two normalisation (b = 16, 64) is exact, so it is folded
+    // into the subtraction below: fma(x, s, -zero) rounds x*s - zero once,
+    // which is the rounding of (x*s) - zero.  (Only a product below 2^-126
+    // can lose bits; that is far below half an ulp of any nonzero fp16 zero
+    // point, and with a zero zero point both forms are the rounded product.)
+    constexpr bool kExactNorm = BLK == 16 || BLK == 64;
+    const float sb = BLK > 0 ? block_norm(BLK) : 1.0f;
+    if constexpr (BLK > 0) {
+      mn = mn * sb;
+      mx = mx * sb;
+      if constexpr (!kExactNorm) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) vw[(hf * 8 + m) * kPage + off] = words[m];
-  }
-  if (hf == 0) {
-    const uint32_t meta = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
-                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
-    *reinterpret_cast<uint32_t*>(slab + kPage * D + kind * 4 * kPage + off * 4) = meta;
+        for (int k = 0; k < kLaneElems; ++k) x[k] = x[k] * sb;
+      }
+    }
+
+    // fp16 zero and scale, reciprocal (0 for a zero scale)
+    const float zero_f = mn + 0.0f;
+    const float range = (mx - mn) + 0.0f;
+    const float step = range / 15.0f;
+    const _Float16 sh = static_cast<_Float16>(step);
+    const _Float16 zh = static_cast<_Float16>(zero_f);
+    const float sf = static_cast<float>(sh);
+    const float zf = static_cast<float>(zh);
+    const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+
+    // codes: (y - zero) * inv, then round-half-even and clamp to [0, 15].
+    // Adding 2^23 rounds to an integer in the current (nearest-even) mode for
+    // any value in [0, 2^23); the clamp in that biased domain equals clamping
+    // the rounded value; the code is then the low 4 bits of the float.
+    uint32_t words[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      uint32_t c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float d = kExactNorm ? __builtin_fmaf(x[8 * m + i], sb, -zf) : x[8 * m + i] - zf;
+        const float q = d * inv;
+        const float t = __builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388623.0f);
+        c[i] = f2u(t);
+      }
+      words[m] = pack8_nibbles(c);
+    }
+
+    // scatter into the slot's page
+    if (t >= a.num_tokens) continue;
+    const int32_t slot = a.slot_mapping[t];
+    if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(a.num_pages) * kPage) continue;
+    const int page = slot / kPage, off = slot % kPage;
+    uint8_t* slab = a.pool + (static_cast<int64_t>(page) * hkv + w.h) * kSlab;
+    if (w.kind == 0) {
+      u32x4* dst = reinterpret_cast<u32x4*>(slab + off * (D / 2) + hf * 32);
+      dst[0] = u32x4{words[0], words[1], words[2], words[3]};
+      dst[1] = u32x4{words[4], words[5], words[6], words[7]};
+    } else {
+      uint32_t* vw = reinterpret_cast<uint32_t*>(slab + kPage * D / 2);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) vw[(hf * 8 + m) * kPage + off] = words[m];
+    }
+    if (hf == 0) {
+      const uint32_t meta = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
+                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
+      *reinterpret_cast<uint32_t*>(slab + kPage * D + w.kind * 4 * kPage + off * 4) = meta;
+    }
   }
 }
 
@@ -240,8 +261,10 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
 
 template <int D, int BLK>
 hipError_t launch_int4_d(const AppendArgs& a, hipStream_t s) {
-  using S = AppendShape<D>;
-  const dim3 grid(static_cast<unsigned>((a.num_tokens + S::kRows - 1) / S::kRows), static_cast<unsigned>(a.num_kv_heads));
+  constexpr int kTok = D == 128 ? 32 : 64;
+  const int64_t units = (static_cast<int64_t>(a.num_tokens) + kTok - 1) / kTok * a.num_kv_heads * 2;
+  const int64_t blocks = (units + kAppendThreads / 64 - 1) / (kAppendThreads / 64);
+  const dim3 grid(static_cast<unsigned>(blocks < kResidentBlocks ? blocks : kResidentBlocks));
   if (a.in_bf16)
     append_int4_kernel<D, BLK, true><<<grid, kAppendThreads, 0, s>>>(a);
   else

@@ -115,7 +115,8 @@ size_t kvq_bf16_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head
  *
  * k, v:         device, [num_tokens][token_stride] elements of `dtype`, the
  *               first num_kv_heads*head_dim of each token used; 16-byte
- *               aligned, token_stride a multiple of 8 and >= num_kv_heads*D.
+ *               aligned, token_stride a multiple of 8, >= num_kv_heads*D and
+ *               <= 2^24 (else KVQ_ERR_INVALID_ARGUMENT).
  * slot_mapping: device int32 [num_tokens]; two tokens of one call must not
  *               share a slot.
  * num_tokens:   >= 0 (0 launches nothing).

@@ -66,6 +66,7 @@ def _append(desc, k=FAKE, v=FAKE, dtype=kvq.KVQ_BF16, stride=128, slots=FAKE, n=
     (_int4(), {"k": FAKE + 8}, kvq.KVQ_ERR_INVALID_ARGUMENT),
     (_int4(), {"stride": 64}, kvq.KVQ_ERR_INVALID_ARGUMENT),
     (_int4(), {"stride": 132}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    (_int4(), {"stride": (1 << 24) + 8}, kvq.KVQ_ERR_INVALID_ARGUMENT),
     (_int4(), {"dtype": 7}, kvq.KVQ_ERR_INVALID_ARGUMENT),
     (_int4(), {"n": -1}, kvq.KVQ_ERR_INVALID_ARGUMENT),
 ])
