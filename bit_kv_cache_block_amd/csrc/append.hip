@@ -63,28 +63,37 @@ void append_int4_kernel(AppendArgs a) {
   const int lane = threadIdx.x & 63;
   const int r = lane / kLPV, hf = lane % kLPV;
   const uint32_t hkv = static_cast<uint32_t>(a.num_kv_heads);
-  const int64_t units = (static_cast<int64_t>(a.num_tokens) + kTok - 1) / kTok * hkv * 2;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * (kAppendThreads / 64);
-  int64_t u = static_cast<int64_t>(blockIdx.x) * (kAppendThreads / 64) + (threadIdx.x >> 6);
-
-  // unit -> (first token, head, kind); kind is the fastest index, so the K
-  // and V units of one (tile, head) run side by side
-  struct Unit { int t0, h, kind; };
-  auto unit = [&](int64_t uu) {
-    const int64_t rest = uu >> 1;
-    const int64_t tile = rest / hkv;
-    return Unit{static_cast<int>(tile * kTok), static_cast<int>(rest - tile * hkv), static_cast<int>(uu & 1)};
+  const uint32_t tiles = (static_cast<uint32_t>(a.num_tokens) + kTok - 1) / kTok;
+  // Unit u = (tile * hkv + head) * 2 + kind; wave w takes u = w, w + S, ...
+  // with S = 4 * gridDim.x even, so its kind never changes and (tile, head)
+  // advance by a fixed step (all wave-uniform scalar arithmetic).
+  const uint32_t w0 = blockIdx.x * (kAppendThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kind = static_cast<int>(w0 & 1u);
+  const uint16_t* in = kind ? a.v : a.k;
+  const uint32_t half_stride = gridDim.x * (kAppendThreads / 128);
+  const uint32_t st_t = half_stride / hkv, st_h = half_stride - st_t * hkv;
+  struct Unit { uint32_t tile, h; };
+  Unit cur{(w0 >> 1) / hkv, (w0 >> 1) % hkv};
+  auto advance = [&](Unit x) {
+    x.h += st_h;
+    x.tile += st_t;
+    if (x.h >= hkv) {
+      x.h -= hkv;
+      ++x.tile;
+    }
+    return x;
   };
+
   // Piece m of this lane is row lane / kChunks + m * kRowsPerLoad, chunk
   // lane % kChunks.  One buffer descriptor spans the unit's rows that exist,
   // so rows past the last token read as zeros.
   constexpr int kRowsPerLoad = 64 / kChunks;
   const uint32_t row_bytes = static_cast<uint32_t>(a.token_stride) * 2u;
   const uint32_t lane_off = static_cast<uint32_t>(lane / kChunks) * row_bytes + (lane % kChunks) * 16u;
-  auto load = [&](u32x4 (&pf)[8], int64_t uu) {
-    const Unit w = unit(uu);
-    const uint16_t* src = (w.kind ? a.v : a.k) + static_cast<int64_t>(w.t0) * a.token_stride + w.h * D;
-    const int rows = min(kTok, a.num_tokens - w.t0);
+  auto load = [&](u32x4 (&pf)[8], Unit w) {
+    const int t0 = static_cast<int>(w.tile) * kTok;
+    const uint16_t* src = in + static_cast<int64_t>(t0) * a.token_stride + w.h * D;
+    const int rows = min(kTok, a.num_tokens - t0);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, static_cast<int>(static_cast<uint32_t>(rows) * row_bytes));
 #pragma unroll
     for (int m = 0; m < 8; ++m)
@@ -93,16 +102,16 @@ void append_int4_kernel(AppendArgs a) {
   };
 
   u32x4 pf[8];
-  if (u < units) load(pf, u);
-  for (; u < units; u += stride) {
-    const Unit w = unit(u);
-    const int t = w.t0 + r;
+  if (cur.tile < tiles) load(pf, cur);
+  for (; cur.tile < tiles; cur = advance(cur)) {
+    const int t = static_cast<int>(cur.tile) * kTok + r;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int c = lane + 64 * m, row = c / kChunks, chunk = c % kChunks;
       *reinterpret_cast<u32x4*>(lds + row * kRowBytes + (chunk / 8) * kHalf + (chunk % 8) * 16) = pf[m];
     }
-    if (u + stride < units) load(pf, u + stride);
+    const Unit nxt = advance(cur);
+    if (nxt.tile < tiles) load(pf, nxt);
     // the wave's LDS writes above complete before its reads below (LDS
     // instructions of one wave execute in order)
     float x[kLaneElems];
@@ -197,8 +206,8 @@ void append_int4_kernel(AppendArgs a) {
     const int32_t slot = a.slot_mapping[t];
     if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(a.num_pages) * kPage) continue;
     const int page = slot / kPage, off = slot % kPage;
-    uint8_t* slab = a.pool + (static_cast<int64_t>(page) * hkv + w.h) * kSlab;
-    if (w.kind == 0) {
+    uint8_t* slab = a.pool + (static_cast<int64_t>(page) * hkv + cur.h) * kSlab;
+    if (kind == 0) {
       u32x4* dst = reinterpret_cast<u32x4*>(slab + off * (D / 2) + hf * 32);
       dst[0] = u32x4{words[0], words[1], words[2], words[3]};
       dst[1] = u32x4{words[4], words[5], words[6], words[7]};
@@ -210,7 +219,7 @@ void append_int4_kernel(AppendArgs a) {
     if (hf == 0) {
       const uint32_t meta = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
                             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
-      *reinterpret_cast<uint32_t*>(slab + kPage * D + w.kind * 4 * kPage + off * 4) = meta;
+      *reinterpret_cast<uint32_t*>(slab + kPage * D + kind * 4 * kPage + off * 4) = meta;
     }
   }
 }
