@@ -250,7 +250,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=["full", "decode", "copy"], default="full")
+    ap.add_argument("--mode", choices=["full", "decode", "prefill", "copy"], default="full")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -272,6 +272,11 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+        return 0
+
+    if args.mode == "prefill":
+        r = prefill_rate(torch, kvq, workloads, 64, iters=args.steps)
+        print(json.dumps({"mode": "prefill", **r}))
         return 0
 
     db = DecodeBench(torch, kvq, workloads, block=64)

@@ -90,8 +90,10 @@ void append_int4_kernel(AppendArgs a) {
   constexpr int kRowsPerLoad = 64 / kChunks;
   const uint32_t row_bytes = static_cast<uint32_t>(a.token_stride) * 2u;
   const uint32_t lane_off = static_cast<uint32_t>(lane / kChunks) * row_bytes + (lane % kChunks) * 16u;
-  auto load = [&](u32x4 (&pf)[8], Unit w) {
+  // the unit's rows and this lane's slot are loaded together
+  auto load = [&](u32x4 (&pf)[8], int32_t& slot, Unit w) {
     const int t0 = static_cast<int>(w.tile) * kTok;
+    slot = t0 + r < a.num_tokens ? a.slot_mapping[t0 + r] : -1;
     const uint16_t* src = in + static_cast<int64_t>(t0) * a.token_stride + w.h * D;
     const int rows = min(kTok, a.num_tokens - t0);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, static_cast<int>(static_cast<uint32_t>(rows) * row_bytes));
@@ -102,16 +104,17 @@ void append_int4_kernel(AppendArgs a) {
   };
 
   u32x4 pf[8];
-  if (cur.tile < tiles) load(pf, cur);
+  int32_t slot_nxt = -1;
+  if (cur.tile < tiles) load(pf, slot_nxt, cur);
   for (; cur.tile < tiles; cur = advance(cur)) {
-    const int t = static_cast<int>(cur.tile) * kTok + r;
+    const int32_t slot = slot_nxt;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int c = lane + 64 * m, row = c / kChunks, chunk = c % kChunks;
       *reinterpret_cast<u32x4*>(lds + row * kRowBytes + (chunk / 8) * kHalf + (chunk % 8) * 16) = pf[m];
     }
     const Unit nxt = advance(cur);
-    if (nxt.tile < tiles) load(pf, nxt);
+    if (nxt.tile < tiles) load(pf, slot_nxt, nxt);
     // the wave's LDS writes above complete before its reads below (LDS
     // instructions of one wave execute in order)
     float x[kLaneElems];
@@ -201,9 +204,7 @@ void append_int4_kernel(AppendArgs a) {
       words[m] = pack8_nibbles(c);
     }
 
-    // scatter into the slot's page
-    if (t >= a.num_tokens) continue;
-    const int32_t slot = a.slot_mapping[t];
+    // scatter into the slot's page (tokens past the end have slot -1)
     if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(a.num_pages) * kPage) continue;
     const int page = slot / kPage, off = slot % kPage;
     uint8_t* slab = a.pool + (static_cast<int64_t>(page) * hkv + cur.h) * kSlab;

@@ -6,9 +6,9 @@
 // idea of "InnerQ", Figure 1).
 //
 // A workgroup of four waves owns one (sequence b, KV head, split s) and each
-// wave streams a quarter of its pages, four pages per step, with the next
-// step's loads in flight while the current step computes.  Per page and per
-// group of four query heads:
+// wave streams a quarter of its pages, four pages per step, with
+// non-temporal buffer loads (the cache is read once per call).  Per page and
+// per group of four query heads:
 //   QK:  C[(head, limb)][token] = sum_c qlimb[c] * code[token][c]   (int8 MFMA)
 //        The rotated query is a 23-bit fixed-point integer split into three
 //        signed 8-bit limbs (rows of the tile); codes are exact int8; products
@@ -35,7 +35,6 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaves = 4;
 constexpr int kStep = 4;   // pages per step
-constexpr int kDepth = 1;  // steps in registers: 1 = none in flight while computing, 2 = one, 3 = two
 
 __device__ __forceinline__ float half_lo(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
@@ -234,7 +233,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   for (int r = 0; r < NS; ++r)
 #pragma unroll
     for (int k = 0; k < kVL; ++k) asm volatile("" : : "v"(qv[r][k]) : "memory");
-  StepBuf buf0, buf1;
+  StepBuf buf0;
   if (pw0 < pw1) load(buf0, pw0);
   // ---- query: rotate in registers, fixed point, limbs ------------------------
   for (int e = tid; e < kWaves * NS * 4 * 4 * 16; e += 64 * kWaves)
@@ -432,57 +431,26 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
     }
   };
 
-  // ---- stream: compute step k while step k+1 loads --------------------------
+  // ---- stream the wave's pages ----------------------------------------------
   auto step = [&](const StepBuf& sb, int p) {
     if (!sb.all_ok || (p + kStep) * kPage > len)
       compute(sb, p, std::true_type{});
     else
       compute(sb, p, std::false_type{});
   };
-  if constexpr (kDepth == 1) {
-    for (int p = pw0; p < pw1; p += kStep) {
-      step(buf0, p);
-      if (p + kStep >= pw1) break;
-      if (p + kStep >= cb + 64) {   // the next step starts in the following 64 ids
-        cb += 64;
-        ids_cur = ids_next;
-        ids_next = load_ids(cb + 64);
-      }
-      load(buf0, p + kStep);
+  // One step at a time: its four pages are loaded, then computed.  While a
+  // wave computes, the other waves of its SIMD keep loads in flight (an
+  // in-register prefetch of the next step measured slower: more VGPRs and
+  // conservative waits).
+  for (int p = pw0; p < pw1; p += kStep) {
+    step(buf0, p);
+    if (p + kStep >= pw1) break;
+    if (p + kStep >= cb + 64) {   // the next step starts in the following 64 ids
+      cb += 64;
+      ids_cur = ids_next;
+      ids_next = load_ids(cb + 64);
     }
-  } else if constexpr (kDepth == 2) {
-    for (int p = pw0; p < pw1; p += 2 * kStep) {
-      if (p + kStep < pw1) load(buf1, p + kStep);
-      step(buf0, p);
-      if (p + kStep >= pw1) break;
-      if (p + 2 * kStep < pw1) load(buf0, p + 2 * kStep);
-      step(buf1, p + kStep);
-      if (p + 3 * kStep >= cb + 64) {
-        // the next step to load starts in the following 64 ids: slide the
-        // window (every later load stays below cb + 128)
-        cb += 64;
-        ids_cur = ids_next;
-        ids_next = load_ids(cb + 64);
-      }
-    }
-  } else {
-    StepBuf buf2;
-    if (pw0 + kStep < pw1) load(buf1, pw0 + kStep);
-    for (int p = pw0; p < pw1; p += 3 * kStep) {
-      if (p + 2 * kStep < pw1) load(buf2, p + 2 * kStep);
-      step(buf0, p);
-      if (p + kStep >= pw1) break;
-      if (p + 3 * kStep < pw1) load(buf0, p + 3 * kStep);
-      step(buf1, p + kStep);
-      if (p + 2 * kStep >= pw1) break;
-      if (p + 4 * kStep < pw1) load(buf1, p + 4 * kStep);
-      step(buf2, p + 2 * kStep);
-      if (p + 5 * kStep >= cb + 64) {
-        cb += 64;
-        ids_cur = ids_next;
-        ids_next = load_ids(cb + 64);
-      }
-    }
+    load(buf0, p + kStep);
   }
 
   // ---- merge the four waves --------------------------------------------------
