@@ -77,16 +77,20 @@ def _src_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel_file: str, alg_bytes: int):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current source of the kernel."""
+DECODE_SOURCES = ("decode_int4.hip", "dev_common.hpp", "kvq_internal.hpp")
+
+
+def _traffic(alg_bytes: int):
+    """HBM bytes per launch of the decode kernel from the committed counter
+    record (calibrated FETCH_SIZE + WRITE_SIZE), or None when the kernel's
+    sources changed after the counters were taken."""
     path = os.path.join(ROOT, "profiles", "counters_decode_int4_llama8b.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except OSError:
         return None
-    if rec.get("source_sha") != _src_hash(kernel_file):
+    if rec.get("source_sha") != _src_hash(*DECODE_SOURCES):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -341,7 +345,7 @@ def main(argv=None):
     prefill_plain = prefill_rate(torch, kvq, workloads, 0)
     torch.cuda.empty_cache()
 
-    traffic = _traffic("decode_int4.hip", dec_bytes)
+    traffic = _traffic(dec_bytes)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -382,7 +386,8 @@ def main(argv=None):
             "bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(value / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_int4_kernel + reduce_kernel (one kvq_decode_attn call)",
+            "kernel": "decode_int4_kernel (one kvq_decode_attn call; at this shape the split "
+                      "plan is one split per (sequence, KV head), so no reduce kernel runs)",
         },
     }
     line["cpu_baseline"] = None if cb is None else \
