@@ -284,3 +284,86 @@ def test_decode_ignores_stale_bytes_in_unwritten_slots():
     bwant = oracle.decode_bf16(bpool, w.hkv, w.d, bits(w.q), oracle.BF16, w.block_table,
                                w.seq_lens, w.sm_scale)
     assert_close(gpu_decode(bc, w, bf16=True), bwant, "bf16 stale")
+
+
+def test_append_prefill_full_size_bitexact():
+    """The benchmark's prefill append at full size (32768 ragged tokens, 8 KV
+    heads, head_dim 128, Student-t values, block 64): every byte of the pool."""
+    w = workloads.prefill_append(3, device=DEV, block=64)
+    print("append prefill full size", flush=True)
+    cache = kvq.Int4Cache(w.num_pages, w.hkv, w.d, 64, DEV)
+    kvq.kvq_append_paged(cache, w.k, w.v, w.slot_mapping)
+    torch.cuda.synchronize()
+    assert_pool_equal(cache.pool, oracle_int4_pool(w, 64), "prefill full")
+
+
+def _oracle_pool_for(w, sample, step=None):
+    """The oracle's pool holding only the tokens of the sequences in
+    ``sample`` (of the fill ``w``, then of the decode ``step`` if given)."""
+    sel = torch.from_numpy(np.isin(w.token_seq, sample)).to(w.k.device)
+    pool = oracle_int4_pool(w, w.block, sel=sel)
+    if step is not None:
+        ssel = np.isin(step.token_seq, sample)
+        tsel = torch.from_numpy(ssel).to(step.k.device)
+        oracle.append_int4(pool, step.num_pages, step.hkv, step.d, step.block, bits(step.k[tsel]),
+                           bits(step.v[tsel]), oracle.BF16, step.slot_mapping.cpu().numpy()[ssel])
+    return pool
+
+
+def test_long_context_full_size_sampled():
+    """Qwen3-4B-shaped long context at full size (8 x 131072 tokens, 65536
+    pages, per-channel scales in [0.1, 10], block 64) with the default split
+    plan: pages of two sampled sequences bit-exact, their attention within
+    tolerance."""
+    w = workloads.long_context_decode(4, device=DEV, batch=8, context=131072, block=64)
+    print("long context full size", flush=True)
+    cache = kvq.Int4Cache(w.num_pages, w.hkv, w.d, 64, DEV)
+    kvq.kvq_append_paged(cache, w.k, w.v, w.slot_mapping)
+    out = kvq.kvq_decode_attn(cache, w.q, torch.from_numpy(w.block_table).to(DEV),
+                              torch.from_numpy(w.seq_lens).to(DEV), w.max_seq_len, w.sm_scale)
+    torch.cuda.synchronize()
+    sample = [0, 5]
+    pool = _oracle_pool_for(w, sample)
+    slab = w.hkv * oracle.int4_slab_bytes(16, w.d)
+    gpool = cache.pool.cpu().numpy()
+    for b in sample:
+        pages = w.block_table[b][w.block_table[b] >= 0]
+        got = gpool[pages].reshape(-1)
+        want = np.concatenate([pool[pg * slab:(pg + 1) * slab] for pg in pages])
+        assert np.array_equal(got, want), f"seq {b} pages differ"
+    mask = np.zeros((w.batch, w.hq), np.uint8)
+    mask[sample] = 1
+    want = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table,
+                              w.seq_lens, w.sm_scale, mask=mask)
+    assert_close(out.cpu().numpy().astype(np.float64)[sample], want[sample], "long full sampled")
+
+
+def test_concurrency_full_size_sampled():
+    """70B-shaped layer (GQA 8) at the largest batch of the sweep: 256 ragged
+    lognormal contexts (median 2048, cap 32768), one appended token per
+    sequence, then decode.  Sampled sequences (the longest, the shortest and
+    two more): pages bit-exact, attention within tolerance."""
+    fill, steps = workloads.concurrency_step(5, device=DEV, batch=256, block=64, steps=1)
+    step = steps[0]
+    print(f"concurrency full size: {int(fill.seq_lens.sum())} tokens", flush=True)
+    cache = kvq.Int4Cache(fill.num_pages, fill.hkv, fill.d, 64, DEV)
+    kvq.kvq_append_paged(cache, fill.k, fill.v, fill.slot_mapping)
+    kvq.kvq_append_paged(cache, step.k, step.v, step.slot_mapping)
+    out = kvq.kvq_decode_attn(cache, step.q, torch.from_numpy(step.block_table).to(DEV),
+                              torch.from_numpy(step.seq_lens).to(DEV), step.max_seq_len,
+                              step.sm_scale)
+    torch.cuda.synchronize()
+    lens = fill.seq_lens
+    sample = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 17, 200})
+    pool = _oracle_pool_for(fill, sample, step=step)
+    slab = fill.hkv * oracle.int4_slab_bytes(16, fill.d)
+    gpool = cache.pool.cpu().numpy()
+    for b in sample:
+        for pg in step.block_table[b][step.block_table[b] >= 0]:
+            # pages past the sequence's end were never written on either side
+            assert np.array_equal(gpool[pg], pool[pg * slab:(pg + 1) * slab]), f"seq {b} page {pg}"
+    mask = np.zeros((step.batch, step.hq), np.uint8)
+    mask[sample] = 1
+    want = oracle.decode_int4(pool, step.hkv, step.d, 64, bits(step.q), oracle.BF16,
+                              step.block_table, step.seq_lens, step.sm_scale, mask=mask)
+    assert_close(out.cpu().numpy().astype(np.float64)[sample], want[sample], "concurrency sampled")
