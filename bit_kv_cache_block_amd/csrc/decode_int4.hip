@@ -34,7 +34,8 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaves = 4;
-constexpr int kStep = 4;   // pages per step
+constexpr int kQuads = 1;          // groups of 4 pages per step
+constexpr int kStep = 4 * kQuads;  // pages per step
 
 __device__ __forceinline__ float half_lo(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
@@ -71,6 +72,13 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp_f<kDppRowHalfMirror>(x);
   return x + dpp_f<kDppRowMirror>(x);
 }
+__device__ __forceinline__ int32_t row_sum16_i(int32_t x) {
+  uint32_t u = static_cast<uint32_t>(x);
+  u += dpp_u<kDppXor1>(u);
+  u += dpp_u<kDppXor2>(u);
+  u += dpp_u<kDppRowHalfMirror>(u);
+  return static_cast<int32_t>(u + dpp_u<kDppRowMirror>(u));
+}
 
 // channel of k-slot (dword i, byte k) of the QK operand `op` for lane group g
 template <int D>
@@ -87,7 +95,7 @@ __device__ __forceinline__ int pv_channel(int n, int tau) {
 }
 
 template <int D, int NS>
-struct Smem {
+struct alignas(16) Smem {
   static constexpr int kGP = 4 * NS;
   union {
     int32_t qi[kGP][D];
@@ -98,7 +106,7 @@ struct Smem {
     } merge;
   } u;
   float hA[kGP], hS[kGP];
-  uint32_t wl[kWaves][NS][4][4][16];   // [wave][set][limb][head][token] = 4 pages' bytes
+  uint32_t wl[kWaves][NS][kQuads][4][4][16];   // [wave][set][quad][limb][head][token] = 4 pages' bytes
 };
 
 // one step's loads: four pages of one KV head
@@ -116,7 +124,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   constexpr int kNT = D / 16;          // PV tiles = output channels per lane
   constexpr int kOps = D / 64;         // QK MFMAs per page and head group
   constexpr int kGP = 4 * NS;          // padded heads per KV head
-  constexpr int kVL = D / 64;          // channels per lane in the per-wave vector form
+  constexpr int kC = D / 16;           // channels per lane when a row of 16 lanes holds a vector
   __shared__ Smem<D, NS> sm;
 
   const int tid = threadIdx.x;
@@ -128,14 +136,26 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
 
   // ---- prologue: loads that do not depend on seq_lens go out first ----------
-  // query: per wave one head at a time (two consecutive channels per lane at
-  // D = 128); padding heads read head G-1 and are zeroed below
-  uint32_t qraw[NS];
+  // query: wave w < NS takes heads 4w .. 4w+3 of the group, one per row of 16
+  // lanes; lane (g, n) holds channels [kC n, kC n + kC) of head 4w + g.
+  // Padding heads read head G-1 and are zeroed below.
+  const bool qwave = wave < NS;
+  const int qhead = 4 * wave + g;
+  uint32_t qraw[kC / 2];
+  if (qwave) {
+    const uint16_t* qp = a.q + (hq0 + min(qhead, G - 1)) * D + kC * n;
+    if constexpr (kC == 8) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(qp);
 #pragma unroll
-  for (int r = 0; r < NS; ++r) {
-    const int j = min(wave + kWaves * r, G - 1);
-    const uint16_t* qp = a.q + (hq0 + j) * D + kVL * lane;
-    qraw[r] = (D == 128) ? *reinterpret_cast<const uint32_t*>(qp) : static_cast<uint32_t>(*qp);
+      for (int i = 0; i < 4; ++i) qraw[i] = t[i];
+    } else {
+      const u32x2 t = *reinterpret_cast<const u32x2*>(qp);
+      qraw[0] = t[0];
+      qraw[1] = t[1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kC / 2; ++i) qraw[i] = 0u;
   }
   // Page ids of this wave's range, 64 at a time: lane i of ids_cur holds the
   // id of page cb + i, ids_next the following 64.  A step pulls its four ids
@@ -216,59 +236,54 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   };
   // the query is consumed before the first page loads are issued, so waiting
   // for it never waits for them
-  float qv[NS][kVL];
+  float qv[kC];
 #pragma unroll
-  for (int r = 0; r < NS; ++r) {
-    const int j = wave + kWaves * r;
-#pragma unroll
-    for (int k = 0; k < kVL; ++k) {
-      const uint16_t u = static_cast<uint16_t>(qraw[r] >> (16 * k));
-      const float x = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
-      qv[r][k] = j < G ? x : 0.0f;
-    }
+  for (int k = 0; k < kC; ++k) {
+    const uint16_t u = static_cast<uint16_t>(qraw[k / 2] >> (16 * (k & 1)));
+    const float x = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
+    qv[k] = qhead < G ? x : 0.0f;
   }
   // materialise the query here (its wait drains only the query and the ids)
   // and keep the page loads below this point
 #pragma unroll
-  for (int r = 0; r < NS; ++r)
-#pragma unroll
-    for (int k = 0; k < kVL; ++k) asm volatile("" : : "v"(qv[r][k]) : "memory");
+  for (int k = 0; k < kC; ++k) asm volatile("" : : "v"(qv[k]) : "memory");
   StepBuf buf0;
   if (pw0 < pw1) load(buf0, pw0);
   // ---- query: rotate in registers, fixed point, limbs ------------------------
-  for (int e = tid; e < kWaves * NS * 4 * 4 * 16; e += 64 * kWaves)
-    (&sm.wl[0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
+  for (int e = tid; e < kWaves * NS * kQuads * 4 * 4 * 16; e += 64 * kWaves)
+    (&sm.wl[0][0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
+  if (qwave) {
+    float v[kC];
 #pragma unroll
-  for (int r = 0; r < NS; ++r) {
-    const int j = wave + kWaves * r;
-    float v[kVL];
-#pragma unroll
-    for (int k = 0; k < kVL; ++k) v[k] = qv[r][k];
+    for (int k = 0; k < kC; ++k) v[k] = qv[k];
     if (a.block > 0) {
-      fwht_wave<D>(v, a.block, lane);
+      fwht_row<kC>(v, a.block, n);
       const float sb = block_norm(a.block);
 #pragma unroll
-      for (int k = 0; k < kVL; ++k) v[k] *= sb;
+      for (int k = 0; k < kC; ++k) v[k] *= sb;
     }
     float am = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kVL; ++k) am = fmaxf(am, fabsf(v[k]));
-    for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+    for (int k = 0; k < kC; ++k) am = fmaxf(am, fabsf(v[k]));
+    am = row_max16(am);
     int ex = 0;
     frexpf(am, &ex);                    // am < 2^ex
     ex = ex < -100 ? -100 : ex;         // keeps 2^(22-ex) finite; smaller q is ~0
     const float sc = ldexpf(1.0f, 22 - ex);
+    int32_t qi[kC];
     int32_t sum = 0;
 #pragma unroll
-    for (int k = 0; k < kVL; ++k) {
-      const int32_t qv = static_cast<int32_t>(rintf(v[k] * sc));
-      sm.u.qi[j][kVL * lane + k] = qv;
-      sum += qv;
+    for (int k = 0; k < kC; ++k) {
+      qi[k] = static_cast<int32_t>(rintf(v[k] * sc));
+      sum += qi[k];
     }
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-    if (lane == 0) {
-      sm.hA[j] = a.sm_log2 * ldexpf(1.0f, ex - 22);
-      sm.hS[j] = static_cast<float>(sum);
+#pragma unroll
+    for (int k = 0; k < kC; k += 4)
+      *reinterpret_cast<v4i*>(&sm.u.qi[qhead][kC * n + k]) = v4i{qi[k], qi[k + 1], qi[k + 2], qi[k + 3]};
+    sum = row_sum16_i(sum);             // |sum| <= D * 2^22: exact in int32
+    if (n == 0) {
+      sm.hA[qhead] = a.sm_log2 * ldexpf(1.0f, ex - 22);
+      sm.hS[qhead] = static_cast<float>(sum);
     }
   }
   __syncthreads();
@@ -354,7 +369,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
     float alpha[NS], sw[NS];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      float mc = fmaxf(fmaxf(lg[st][0], lg[st][1]), fmaxf(lg[st][2], lg[st][3]));
+      float mc = lg[st][0];
+#pragma unroll
+      for (int i = 1; i < kStep; ++i) mc = fmaxf(mc, lg[st][i]);
       mc = row_max16(mc);
       const float mnew = fmaxf(m_run[st], mc);
       const float muse = mnew == kNegInf ? 0.0f : mnew;
@@ -387,43 +404,57 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
 #pragma unroll
       for (int i = 0; i < kStep; ++i)
         y[i] = static_cast<uint32_t>(static_cast<int32_t>(rintf(w[i] * wsc)) + 0x8080);
-      // limb bytes of the four pages, one word per limb: bytes 2 / 1 / 0 of y
-      const uint32_t l0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0602u),
-                                                __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0602u), 0x05040100u);
-      const uint32_t l1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0501u),
-                                                __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0501u), 0x05040100u) ^ 0x80808080u;
-      const uint32_t l2w = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0400u),
-                                                 __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0400u), 0x05040100u) ^ 0x80808080u;
-      uint32_t* wl = &sm.wl[wave][st][0][0][0];
-      wl[(0 * 4 + g) * 16 + n] = l0;
-      wl[(1 * 4 + g) * 16 + n] = l1;
-      wl[(2 * 4 + g) * 16 + n] = l2w;
+      // limb bytes of each four pages, one word per limb: bytes 2 / 1 / 0 of y
+#pragma unroll
+      for (int qd = 0; qd < kQuads; ++qd) {
+        const uint32_t* yq = y + 4 * qd;
+        const uint32_t l0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(yq[3], yq[2], 0x0c0c0602u),
+                                                  __builtin_amdgcn_perm(yq[1], yq[0], 0x0c0c0602u), 0x05040100u);
+        const uint32_t l1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(yq[3], yq[2], 0x0c0c0501u),
+                                                  __builtin_amdgcn_perm(yq[1], yq[0], 0x0c0c0501u), 0x05040100u) ^ 0x80808080u;
+        const uint32_t l2w = __builtin_amdgcn_perm(__builtin_amdgcn_perm(yq[3], yq[2], 0x0c0c0400u),
+                                                   __builtin_amdgcn_perm(yq[1], yq[0], 0x0c0c0400u), 0x05040100u) ^ 0x80808080u;
+        uint32_t* wl = &sm.wl[wave][st][qd][0][0][0];
+        wl[(0 * 4 + g) * 16 + n] = l0;
+        wl[(1 * 4 + g) * 16 + n] = l1;
+        wl[(2 * 4 + g) * 16 + n] = l2w;
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
-    v4i apv[NS];
+    v4i apv[NS][kQuads];
 #pragma unroll
     for (int st = 0; st < NS; ++st)
-      apv[st] = *reinterpret_cast<const v4i*>(&sm.wl[wave][st][0][0][0] + wl_row);
-
-    // V: per token r of the lane group, transpose across the four pages so a
-    // word holds the four pages' codes of one channel pair; nibbles split it.
-    uint32_t vt[4][4];   // [r][byte j]
 #pragma unroll
-    for (int r = 0; r < 4; ++r) transpose_bytes4(sb.vx[0][r], sb.vx[1][r], sb.vx[2][r], sb.vx[3][r], vt[r]);
+      for (int qd = 0; qd < kQuads; ++qd)
+        apv[st][qd] = *reinterpret_cast<const v4i*>(&sm.wl[wave][st][qd][0][0][0] + wl_row);
+
+    // V: per token r of the lane group, transpose across four pages so a
+    // word holds the four pages' codes of one channel pair; nibbles split it.
+    uint32_t vt[kQuads][4][4];   // [quad][r][byte j]
+#pragma unroll
+    for (int qd = 0; qd < kQuads; ++qd)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        transpose_bytes4(sb.vx[4 * qd][r], sb.vx[4 * qd + 1][r], sb.vx[4 * qd + 2][r], sb.vx[4 * qd + 3][r],
+                         vt[qd][r]);
 #pragma unroll
     for (int tau = 0; tau < kNT; ++tau) {
-      v4i bv;
+      v4i bv[kQuads];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t yv;
-        if constexpr (D == 128) yv = (tau & 1) ? (vt[r][tau >> 1] >> 4) : vt[r][tau >> 1];
-        else yv = vt[r][tau] >> (4 * (n >> 3));
-        bv[r] = static_cast<int32_t>(yv & kLowNibbles);
-      }
+      for (int qd = 0; qd < kQuads; ++qd)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t yv;
+          if constexpr (D == 128) yv = (tau & 1) ? (vt[qd][r][tau >> 1] >> 4) : vt[qd][r][tau >> 1];
+          else yv = vt[qd][r][tau] >> (4 * (n >> 3));
+          bv[qd][r] = static_cast<int32_t>(yv & kLowNibbles);
+        }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const v4i c = mfma_i8(apv[st], bv, zero4);
+        v4i c = mfma_i8(apv[st][0], bv[0], zero4);
+#pragma unroll
+        for (int qd = 1; qd < kQuads; ++qd) c = mfma_i8(apv[st][qd], bv[qd], c);
         const float f = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f,
                                        static_cast<float>(c[2]));
         acc[st][tau] = __builtin_fmaf(f, sw[st], acc[st][tau] * alpha[st]);
@@ -468,7 +499,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
     }
   }
   __syncthreads();
-  for (int j = wave; j < G; j += kWaves) {   // one wave per head
+  if (qwave) {   // wave w < NS finishes heads 4w .. 4w+3, one per row of 16 lanes
+    const int j = qhead;
     float mstar = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, sm.u.merge.m[w][j]);
@@ -479,29 +511,38 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
       f[w] = exp2f(sm.u.merge.m[w][j] - muse);
       lsum = __builtin_fmaf(sm.u.merge.l[w][j], f[w], lsum);
     }
-    float o[kVL];
+    float o[kC];
 #pragma unroll
-    for (int k = 0; k < kVL; ++k) {
-      o[k] = 0.0f;
+    for (int k = 0; k < kC; ++k) o[k] = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) o[k] = __builtin_fmaf(sm.u.merge.acc[w][j][kVL * lane + k], f[w], o[k]);
-    }
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int k = 0; k < kC; k += 4) {
+        const v4f x = *reinterpret_cast<const v4f*>(&sm.u.merge.acc[w][j][kC * n + k]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[k + i] = __builtin_fmaf(x[i], f[w], o[k + i]);
+      }
     if (a.nsplit == 1) {
       const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
-      for (int k = 0; k < kVL; ++k) o[k] *= inv;
+      for (int k = 0; k < kC; ++k) o[k] *= inv;
       float scale = 1.0f;
-      if (a.block > 0) {
-        fwht_wave<D>(o, a.block, lane);
+      if (a.block > 0) {   // every row takes part: the butterfly reads its neighbours
+        fwht_row<kC>(o, a.block, n);
         scale = block_norm(a.block);
       }
+      if (j < G) {
+        float* dst = a.out + (hq0 + j) * D + kC * n;
 #pragma unroll
-      for (int k = 0; k < kVL; ++k) a.out[(hq0 + j) * D + kVL * lane + k] = o[k] * scale;
-    } else {
+        for (int k = 0; k < kC; k += 4)
+          *reinterpret_cast<v4f*>(dst + k) = v4f{o[k] * scale, o[k + 1] * scale, o[k + 2] * scale, o[k + 3] * scale};
+      }
+    } else if (j < G) {
       const int64_t idx = (hq0 + j) * a.nsplit + s;
+      float* dst = a.part_acc + idx * D + kC * n;
 #pragma unroll
-      for (int k = 0; k < kVL; ++k) a.part_acc[idx * D + kVL * lane + k] = o[k];
-      if (lane == 0) {
+      for (int k = 0; k < kC; k += 4) *reinterpret_cast<v4f*>(dst + k) = v4f{o[k], o[k + 1], o[k + 2], o[k + 3]};
+      if (n == 0) {
         a.part_ml[idx * 2 + 0] = mstar;
         a.part_ml[idx * 2 + 1] = lsum;
       }

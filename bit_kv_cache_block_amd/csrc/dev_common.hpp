@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kvq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -23,6 +25,8 @@ __device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(flo
 constexpr int kDppXor1 = 0xB1;
 constexpr int kDppXor2 = 0x4E;
 constexpr int kDppBcast0 = 0x00;   // quad_perm [0,0,0,0]
+constexpr int kDppXor3 = 0x1B;            // quad_perm [3,2,1,0] (lane ^ 3)
+constexpr int kDppRowRor8 = 0x128;        // rotate a row of 16 by 8: lane i <- i ^ 8
 constexpr int kDppRowMirror = 0x140;      // lane i <- 15 - i within a row of 16
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <- 7 - i within each half row
 
@@ -107,33 +111,48 @@ __device__ __forceinline__ uint32_t pack8_nibbles(const uint32_t c[8]) {
   return lo | (hi << 16);
 }
 
-// Block Walsh-Hadamard butterfly over one vector spread across a wave:
-// D = 128: lane l holds channels 2l, 2l+1 in v[0], v[1]; D = 64: lane l holds
-// channel l in v[0].  Stages h = 1, 2, 4, ..., block/2 in ascending order; the
-// lower element of each pair becomes x + y, the upper x - y.  Unnormalised.
-template <int D>
-__device__ __forceinline__ void fwht_wave(float* v, int block, int lane) {
-  if constexpr (D == 128) {
-    if (block < 2) return;
-    const float a = v[0], b = v[1];
-    v[0] = a + b;
-    v[1] = a - b;
-    for (int h = 2; h < block; h *= 2) {
-      const int dl = h >> 1;
-      const bool upper = (lane & dl) != 0;
+// Value of lane i ^ M within a row of 16 lanes (M = 1, 2, 4, 8), all by DPP;
+// lane ^ 4 is lane ^ 3 followed by the half-row mirror (lane ^ 7).
+template <int M>
+__device__ __forceinline__ float dpp_xor(float x) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "row xor");
+  if constexpr (M == 1) return dpp_f<kDppXor1>(x);
+  else if constexpr (M == 2) return dpp_f<kDppXor2>(x);
+  else if constexpr (M == 4) return dpp_f<kDppRowHalfMirror>(dpp_f<kDppXor3>(x));
+  else return dpp_f<kDppRowRor8>(x);
+}
+
+// Block Walsh-Hadamard butterfly over one vector held by a row of 16 lanes:
+// lane n holds channels [C n, C n + C) in v[0 .. C).  Stages h = 1, 2, ...,
+// block/2 in ascending order, inside the lane while h < C, then with lane
+// n ^ (h / C) through DPP.  The lower element of each pair becomes x + y, the
+// upper x - y (the upper lane computes partner - own as an fma by -1, which
+// rounds once).  Unnormalised; block is a power of two up to 16 C.
+template <int C>
+__device__ __forceinline__ void fwht_row(float* v, int block, int n) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const float partner = __shfl_xor(v[k], dl);
-        v[k] = upper ? partner - v[k] : v[k] + partner;
-      }
-    }
-  } else {
-    for (int h = 1; h < block; h *= 2) {
-      const bool upper = (lane & h) != 0;
-      const float partner = __shfl_xor(v[0], h);
-      v[0] = upper ? partner - v[0] : v[0] + partner;
+  for (int h = 1; h < C; h *= 2) {
+    if (h < block) {
+#pragma unroll
+      for (int i = 0; i < C; i += 2 * h)
+#pragma unroll
+        for (int k = i; k < i + h; ++k) {
+          const float x = v[k], y = v[k + h];
+          v[k] = x + y;
+          v[k + h] = x - y;
+        }
     }
   }
+  auto cross = [&](auto m_tag) {
+    constexpr int M = decltype(m_tag)::value;
+    const float sgn = (n & M) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int k = 0; k < C; ++k) v[k] = __builtin_fmaf(sgn, v[k], dpp_xor<M>(v[k]));
+  };
+  if (C < block) cross(std::integral_constant<int, 1>{});
+  if (2 * C < block) cross(std::integral_constant<int, 2>{});
+  if (4 * C < block) cross(std::integral_constant<int, 4>{});
+  if (8 * C < block) cross(std::integral_constant<int, 8>{});
 }
 
 // Raw buffer descriptor over [base, base + bytes): loads through it take a
