@@ -19,10 +19,10 @@ namespace {
 
 constexpr int kAppendThreads = 256;  // 4 independent waves
 constexpr int kLaneElems = 64;       // elements of one vector owned by one lane
-// Waves stay resident and loop over work units: 768 workgroups of 4 waves
-// are 3 waves per SIMD on the 256 CUs of an MI355X (the kernel is held to
-// 168 VGPRs so that they all fit).
-constexpr int kResidentBlocks = 768;
+// Waves stay resident and loop over work units: 1024 workgroups of 4 waves
+// are 4 waves per SIMD on the 256 CUs of an MI355X (the kernel is held to
+// 128 VGPRs and 32 KiB of LDS per workgroup so that they all fit).
+constexpr int kResidentBlocks = 1024;
 
 template <bool BF16>
 __device__ __forceinline__ void widen8(u32x4 w, float* x) {
@@ -40,24 +40,23 @@ __device__ __forceinline__ void widen8(u32x4 w, float* x) {
 }
 
 // A work unit is (tile of kTok consecutive tokens, KV head, K or V) and
-// belongs to one wave.  The wave loads the tile's rows with coalesced 16-byte
-// loads (64 lanes cover 1 KiB of whole rows) and passes them through a
-// wave-private LDS region, from which lane (r, hf) takes channels
-// [64 hf, 64 hf + 64) of token t0 + r (two lanes per vector at D = 128, one
-// at D = 64).  The loads of the wave's next unit are issued before the
-// current one is computed.  Lanes of consecutive tokens write consecutive
+// belongs to one wave.  The unit's rows go straight from HBM into a
+// wave-private LDS image with direct-to-LDS buffer loads (16 bytes per lane,
+// 1 KiB of whole rows per instruction; no VGPRs held), from which lane
+// (r, hf) takes channels [64 hf, 64 hf + 64) of token t0 + r (two lanes per
+// vector at D = 128, one at D = 64).  The next unit's rows are requested as
+// soon as the current ones are in registers, so they stream in while the
+// current unit is computed.  Lanes of consecutive tokens write consecutive
 // words of a page slab, so tokens that fill a page in order are stored as
 // contiguous runs.
 template <int D, int BLK, bool BF16>
-__global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void append_int4_kernel(AppendArgs a) {
   constexpr int kLPV = D / kLaneElems;   // lanes per vector
   constexpr int kTok = 64 / kLPV;        // tokens per unit
   constexpr int kChunks = D / 8;         // 16-byte pieces per row
+  constexpr int kRowBytes = 2 * D;
   constexpr int kSlab = kPage * (D + 8);
-  // a row is kLPV half slots of 128 B + 16 B pad: with this stride the
-  // 16-byte reads of any 8 consecutive lanes hit distinct LDS banks
-  constexpr int kHalf = 144, kRowBytes = kLPV * kHalf;
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[kAppendThreads / 64][kTok * kRowBytes];
   uint8_t* lds = lds_all[threadIdx.x >> 6];
   const int lane = threadIdx.x & 63;
@@ -84,43 +83,91 @@ void append_int4_kernel(AppendArgs a) {
     return x;
   };
 
-  // Piece m of this lane is row lane / kChunks + m * kRowsPerLoad, chunk
-  // lane % kChunks.  One buffer descriptor spans the unit's rows that exist,
-  // so rows past the last token read as zeros.
+  // LDS image of a unit: row rr holds kChunks 16-byte slots; chunk c of the
+  // row sits in slot swz(rr, c), a permutation of the row chosen so that the
+  // reads below (any 16 consecutive lanes) fall in distinct banks.
+  auto swz = [](int rr, int c) {
+    if constexpr (kChunks == 16) return c ^ ((2 * rr) & 15) ^ (c >> 3);
+    else return c ^ ((rr ^ (rr >> 3)) & 7);
+  };
+  auto unswz = [](int rr, int sl) {   // the chunk held by slot sl of row rr
+    if constexpr (kChunks == 16) {
+      const int u = sl ^ ((2 * rr) & 15);
+      return u ^ (u >> 3);
+    } else {
+      return sl ^ ((rr ^ (rr >> 3)) & 7);
+    }
+  };
+  // Load m of lane L fills LDS bytes [1024 m + 16 L, +16): row
+  // rr = m * kRowsPerLoad + L / kChunks, slot L % kChunks.  One buffer
+  // descriptor spans the unit's rows that exist: rows past the last token
+  // read as zeros.
   constexpr int kRowsPerLoad = 64 / kChunks;
   const uint32_t row_bytes = static_cast<uint32_t>(a.token_stride) * 2u;
-  const uint32_t lane_off = static_cast<uint32_t>(lane / kChunks) * row_bytes + (lane % kChunks) * 16u;
-  // the unit's rows and this lane's slot are loaded together
-  auto load = [&](u32x4 (&pf)[8], int32_t& slot, Unit w) {
+  uint32_t voff[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int rr = m * kRowsPerLoad + lane / kChunks;
+    voff[m] = static_cast<uint32_t>(lane / kChunks) * row_bytes + unswz(rr, lane % kChunks) * 16u;
+  }
+  auto request = [&](Unit w) {
     const int t0 = static_cast<int>(w.tile) * kTok;
-    slot = t0 + r < a.num_tokens ? a.slot_mapping[t0 + r] : -1;
     const uint16_t* src = in + static_cast<int64_t>(t0) * a.token_stride + w.h * D;
     const int rows = min(kTok, a.num_tokens - t0);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, static_cast<int>(static_cast<uint32_t>(rows) * row_bytes));
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-      pf[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs, lane_off, static_cast<int>(m * kRowsPerLoad * row_bytes), kStreamOnce));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds + 1024 * m), 16, voff[m],
+          static_cast<int>(m * kRowsPerLoad * row_bytes), 0, kStreamOnce);
+    return t0 + r < a.num_tokens ? a.slot_mapping[t0 + r] : -1;
   };
 
-  u32x4 pf[8];
+  // Codes and sidecar of one unit, written into the slot's page (tokens past
+  // the end have slot -1).  A unit is stored one iteration after it is
+  // computed, so that the wait for the next rows never waits for fresh stores.
+  struct Pending { uint32_t words[8]; uint32_t meta; int32_t slot; uint32_t h; };
+  auto store = [&](const Pending& q) {
+    if (q.slot < 0 || static_cast<int64_t>(q.slot) >= static_cast<int64_t>(a.num_pages) * kPage) return;
+    const int page = q.slot / kPage, off = q.slot % kPage;
+    uint8_t* slab = a.pool + (static_cast<int64_t>(page) * hkv + q.h) * kSlab;
+    if (kind == 0) {
+      u32x4* dst = reinterpret_cast<u32x4*>(slab + off * (D / 2) + hf * 32);
+      dst[0] = u32x4{q.words[0], q.words[1], q.words[2], q.words[3]};
+      dst[1] = u32x4{q.words[4], q.words[5], q.words[6], q.words[7]};
+    } else {
+      uint32_t* vw = reinterpret_cast<uint32_t*>(slab + kPage * D / 2);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) vw[(hf * 8 + m) * kPage + off] = q.words[m];
+    }
+    if (hf == 0) *reinterpret_cast<uint32_t*>(slab + kPage * D + kind * 4 * kPage + off * 4) = q.meta;
+  };
+
   int32_t slot_nxt = -1;
-  if (cur.tile < tiles) load(pf, slot_nxt, cur);
+  if (cur.tile < tiles) slot_nxt = request(cur);
+  Pending pend;
+  bool have_pend = false;
   for (; cur.tile < tiles; cur = advance(cur)) {
     const int32_t slot = slot_nxt;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int c = lane + 64 * m, row = c / kChunks, chunk = c % kChunks;
-      *reinterpret_cast<u32x4*>(lds + row * kRowBytes + (chunk / 8) * kHalf + (chunk % 8) * 16) = pf[m];
-    }
-    const Unit nxt = advance(cur);
-    if (nxt.tile < tiles) load(pf, slot_nxt, nxt);
-    // the wave's LDS writes above complete before its reads below (LDS
-    // instructions of one wave execute in order)
+    // the unit's rows have landed in LDS (the direct loads count in vmcnt,
+    // which the compiler does not track for them); the stores waited for
+    // here were issued one whole unit earlier
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (have_pend) store(pend);
     float x[kLaneElems];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      widen8<BF16>(*reinterpret_cast<const u32x4*>(lds + r * kRowBytes + hf * kHalf + 16 * m), x + 8 * m);
+    for (int m = 0; m < 8; ++m) {
+      const int c = hf * 8 + m;
+      widen8<BF16>(*reinterpret_cast<const u32x4*>(lds + r * kRowBytes + swz(r, c) * 16), x + 8 * m);
+    }
+    // the reads above are complete before the next unit's rows overwrite them
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const Unit nxt = advance(cur);
+    if (nxt.tile < tiles) slot_nxt = request(nxt);
 
     // block Hadamard butterfly, stages h = 1, 2, ..., BLK/2 ascending
     if constexpr (BLK > 0) {
@@ -204,25 +251,16 @@ void append_int4_kernel(AppendArgs a) {
       words[m] = pack8_nibbles(c);
     }
 
-    // scatter into the slot's page (tokens past the end have slot -1)
-    if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(a.num_pages) * kPage) continue;
-    const int page = slot / kPage, off = slot % kPage;
-    uint8_t* slab = a.pool + (static_cast<int64_t>(page) * hkv + cur.h) * kSlab;
-    if (kind == 0) {
-      u32x4* dst = reinterpret_cast<u32x4*>(slab + off * (D / 2) + hf * 32);
-      dst[0] = u32x4{words[0], words[1], words[2], words[3]};
-      dst[1] = u32x4{words[4], words[5], words[6], words[7]};
-    } else {
-      uint32_t* vw = reinterpret_cast<uint32_t*>(slab + kPage * D / 2);
+    // the unit's results are stored at the start of the next iteration
 #pragma unroll
-      for (int m = 0; m < 8; ++m) vw[(hf * 8 + m) * kPage + off] = words[m];
-    }
-    if (hf == 0) {
-      const uint32_t meta = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
-                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
-      *reinterpret_cast<uint32_t*>(slab + kPage * D + kind * 4 * kPage + off * 4) = meta;
-    }
+    for (int m = 0; m < 8; ++m) pend.words[m] = words[m];
+    pend.meta = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
+    pend.slot = slot;
+    pend.h = cur.h;
+    have_pend = true;
   }
+  if (have_pend) store(pend);
 }
 
 // bf16 baseline: one thread per (token, head, 8-channel group).
