@@ -199,6 +199,89 @@ def prefill_rate(torch, kvq, workloads, block, iters=50):
             "us": mean_ms * 1e3, "bytes": nbytes, "tokens": tok}
 
 
+def long_context_rate(torch, kvq, workloads, iters=30):
+    """Qwen3-4B-shaped long-context decode (8 x 131072 tokens, 65536 pages):
+    split-K over pages plus the reduce, timed per call on two cache copies,
+    Hadamard block 64 and plain INT4."""
+    w = workloads.long_context_decode(4, device="cuda", batch=8, context=131072, block=64)
+    bt = torch.from_numpy(w.block_table).to("cuda")
+    sl = torch.from_numpy(w.seq_lens).to("cuda")
+    nbytes = decode_bytes(w.seq_lens, w.hkv, w.hq, w.d, int4_bytes_per_vector(w.d))
+    splits = kvq.kvq_decode_workspace_bytes(w.batch, w.hq, w.hkv, w.d, w.max_seq_len) // \
+        (w.batch * w.hq * (w.d + 2) * 4)
+    res = {"workload": "8 sequences x 131072 tokens, 32 q / 8 kv heads, head_dim 128, page 16, "
+                       "per-channel scales in [0.1, 10]", "splits": int(splits), "bytes": nbytes}
+    for blk in (64, 0):
+        caches = [kvq.Int4Cache(w.num_pages, w.hkv, w.d, blk, "cuda") for _ in range(2)]
+        for c in caches:
+            kvq.kvq_append_paged(c, w.k, w.v, w.slot_mapping)
+        out = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(16, kvq.kvq_decode_workspace_bytes(w.batch, w.hq, w.hkv, w.d, w.max_seq_len)),
+                         dtype=torch.uint8, device="cuda")
+
+        def run(i):
+            kvq.kvq_decode_attn(caches[i % 2], w.q, bt, sl, w.max_seq_len, w.sm_scale, out=out, workspace=ws)
+
+        for i in range(5):
+            run(i)
+        ms, _ = _time_events(torch, run, iters)
+        key = "int4_block64" if blk else "int4_plain"
+        res[key] = {"us": round(ms * 1e3, 2), "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        del caches
+        torch.cuda.empty_cache()
+    res["rotated_over_plain"] = round(res["int4_plain"]["us"] / res["int4_block64"]["us"], 4)
+    return res
+
+
+def concurrency_sweep(torch, kvq, workloads, steps=32, warm=8, batches=(1, 8, 32, 128, 256)):
+    """70B-shaped layer (64 q / 8 kv heads): per batch size, fill the ragged
+    lognormal contexts, run ``warm`` untimed decode steps, then time ``steps``
+    decode steps (append one token per sequence, then decode over it) for the
+    rotated INT4, plain INT4 and bf16 caches.  Tokens/s = batch * steps /
+    time.  Successive steps attend the same cache, as a serving loop does
+    (small batches stay in the Infinity Cache)."""
+    out = {"workload": "64 q / 8 kv heads, head_dim 128, lognormal contexts (median 2048, "
+                       "sigma 1, cap 32768), page 16, one new token per sequence per step",
+           "steps": steps}
+    for b in batches:
+        fill, st = workloads.concurrency_step(5, device="cuda", batch=b, block=64, steps=warm + steps)
+        bt = torch.from_numpy(st[0].block_table).to("cuda")
+        sls = [torch.from_numpy(x.seq_lens).to("cuda") for x in st]
+        maxlen = int(st[-1].max_seq_len)
+        ws = torch.empty(max(16, kvq.kvq_decode_workspace_bytes(b, fill.hq, fill.hkv, fill.d, maxlen)),
+                         dtype=torch.uint8, device="cuda")
+        o = torch.empty((b, fill.hq, fill.d), dtype=torch.float32, device="cuda")
+        row = {"context_tokens": int(fill.seq_lens.sum())}
+        for name in ("int4_block64", "int4_plain", "bf16"):
+            if name == "bf16":
+                cache = kvq.Bf16Cache(fill.num_pages, fill.hkv, fill.d, "cuda")
+                app, dec = kvq.kvq_append_paged_bf16, kvq.kvq_decode_attn_bf16
+            else:
+                cache = kvq.Int4Cache(fill.num_pages, fill.hkv, fill.d, 64 if name == "int4_block64" else 0,
+                                      "cuda")
+                app, dec = kvq.kvq_append_paged, kvq.kvq_decode_attn
+            app(cache, fill.k, fill.v, fill.slot_mapping)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            for i, x in enumerate(st):
+                if i == warm:
+                    torch.cuda.synchronize()
+                    e0.record()
+                app(cache, x.k, x.v, x.slot_mapping)
+                dec(cache, x.q, bt, sls[i], maxlen, x.sm_scale, out=o, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            row[name] = {"us_per_step": round(ms * 1e3 / steps, 2), "tokens_s": round(b * steps / (ms * 1e-3), 1)}
+            del cache
+        row["rotated_over_plain"] = round(row["int4_block64"]["tokens_s"] / row["int4_plain"]["tokens_s"], 4)
+        row["int4_over_bf16"] = round(row["int4_block64"]["tokens_s"] / row["bf16"]["tokens_s"], 3)
+        out[f"batch{b}"] = row
+        del fill, st
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The oracle (as it stands) on the host cores over a bounded sample of the
     same workload: host copies of whole sequences are appended (rotate +
@@ -349,6 +432,8 @@ def main(argv=None):
     prefill_rot = prefill_rate(torch, kvq, workloads, 64)
     prefill_plain = prefill_rate(torch, kvq, workloads, 0)
     torch.cuda.empty_cache()
+    long_ctx = long_context_rate(torch, kvq, workloads)
+    conc = concurrency_sweep(torch, kvq, workloads)
 
     traffic = _traffic(dec_bytes)
     line = {
@@ -384,6 +469,8 @@ def main(argv=None):
         },
         "decode_variants_gb_s": {k: round(v, 1) for k, v in sorted(variants.items())},
         "rotated_over_plain_decode": round(variants["int4_block64"] / variants["int4_plain"], 4),
+        "long_context_decode": long_ctx,
+        "concurrency_sweep": conc,
         "bf16_kv": {"gb_s": round(bf16_bytes / (ms_bf16 * 1e-3) / 1e9, 1),
                     "us": round(ms_bf16 * 1e3, 2), "bytes": bf16_bytes,
                     "int4_speedup": round(ms_bf16 / dec_mean, 3)},

@@ -522,15 +522,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[k + i] = __builtin_fmaf(x[i], f[w], o[k + i]);
       }
+    // back to the original basis; with several splits each partial is
+    // rotated here (the merge is a weighted sum, so it commutes)
+    float scale = 1.0f;
+    if (a.block > 0) {   // every row takes part: the butterfly reads its neighbours
+      fwht_row<kC>(o, a.block, n);
+      scale = block_norm(a.block);
+    }
     if (a.nsplit == 1) {
-      const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-#pragma unroll
-      for (int k = 0; k < kC; ++k) o[k] *= inv;
-      float scale = 1.0f;
-      if (a.block > 0) {   // every row takes part: the butterfly reads its neighbours
-        fwht_row<kC>(o, a.block, n);
-        scale = block_norm(a.block);
-      }
+      scale *= lsum > 0.0f ? 1.0f / lsum : 0.0f;
       if (j < G) {
         float* dst = a.out + (hq0 + j) * D + kC * n;
 #pragma unroll
@@ -541,7 +541,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
       const int64_t idx = (hq0 + j) * a.nsplit + s;
       float* dst = a.part_acc + idx * D + kC * n;
 #pragma unroll
-      for (int k = 0; k < kC; k += 4) *reinterpret_cast<v4f*>(dst + k) = v4f{o[k], o[k + 1], o[k + 2], o[k + 3]};
+      for (int k = 0; k < kC; k += 4)
+        *reinterpret_cast<v4f*>(dst + k) = v4f{o[k] * scale, o[k + 1] * scale, o[k + 2] * scale, o[k + 3] * scale};
       if (n == 0) {
         a.part_ml[idx * 2 + 0] = mstar;
         a.part_ml[idx * 2 + 1] = lsum;

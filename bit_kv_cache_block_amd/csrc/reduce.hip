@@ -1,78 +1,69 @@
-// Split-K merge: for each (sequence, query head) combine the partial
-// (max, sum, unnormalised output) of every split with the log-sum-exp rule,
-// normalise, and rotate the output back to the original basis with the same
-// block Hadamard (it is symmetric, so it is its own inverse up to the 1/sqrt(b)
-// normalisation already folded into each factor).
+// Split-K merge: for each (sequence, query head) combine the partials (max,
+// sum, unnormalised output) of its splits with the log-sum-exp rule and
+// normalise.  The decode kernels store each partial already rotated back to
+// the original basis (the rotation is linear and the merge is a weighted
+// sum), so nothing is rotated here.
+//
+// A wave merges four (sequence, query head) rows, one per row of 16 lanes;
+// lane n of a row owns channels [C n, C n + C) with C = D / 16, read as
+// 16-byte vectors from every split.
 #include "dev_common.hpp"
 #include "kvq_internal.hpp"
 
 namespace kvq {
 namespace {
 
-__global__ __launch_bounds__(64) void reduce_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.num_q_heads;
-  const int d = a.head_dim;
-  const int lane = threadIdx.x;
-  __shared__ float o[128];
-  __shared__ float wsplit[64];
-  float* dst = a.out + static_cast<int64_t>(bh) * d;
+constexpr int kReduceThreads = 256;   // 16 (sequence, query head) rows per workgroup
+
+template <int D>
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
+  constexpr int kC = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
+  const int64_t bh = static_cast<int64_t>(blockIdx.x) * (kReduceThreads / 16) + (threadIdx.x >> 4);
+  if (bh >= rows) return;
+  const int b = static_cast<int>(bh / a.num_q_heads);
+  float* dst = a.out + bh * D + kC * n;
 
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
   const int npg = (len + kPage - 1) / kPage;
-  const int nsp = (npg + a.split_pages - 1) / a.split_pages;
-  const float* ml = a.part_ml + static_cast<int64_t>(bh) * a.nsplit * 2;
-  const float* pa = a.part_acc + static_cast<int64_t>(bh) * a.nsplit * d;
+  const int nsp = (npg + a.split_pages - 1) / a.split_pages;   // splits that hold pages
+  const float* ml = a.part_ml + bh * a.nsplit * 2;
+  const float* pa = a.part_acc + bh * a.nsplit * D + kC * n;
 
   float mstar = -__builtin_inff();
-  for (int s = lane; s < nsp; s += 64) mstar = fmaxf(mstar, ml[2 * s]);
-  for (int off = 32; off > 0; off >>= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, off));
+  for (int s = 0; s < nsp; ++s) mstar = fmaxf(mstar, ml[2 * s]);
   float lsum = 0.0f;
-  for (int s = lane; s < nsp; s += 64) lsum += ml[2 * s + 1] * exp2f(ml[2 * s] - mstar);
-  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
-
-  if (nsp == 0 || !(lsum > 0.0f)) {
-    for (int c = lane; c < d; c += 64) dst[c] = 0.0f;
-    return;
-  }
-  const float inv_l = 1.0f / lsum;
-  float accv[2] = {0.0f, 0.0f};
-  for (int s0 = 0; s0 < nsp; s0 += 64) {
-    const int cnt = min(64, nsp - s0);
-    __syncthreads();
-    if (lane < cnt) wsplit[lane] = exp2f(ml[2 * (s0 + lane)] - mstar);
-    __syncthreads();
-    for (int s = 0; s < cnt; ++s) {
-      const float w = wsplit[s];
-      const float* row = pa + static_cast<int64_t>(s0 + s) * d;
-      for (int k = 0, c = lane; c < d; ++k, c += 64) accv[k] = __builtin_fmaf(row[c], w, accv[k]);
+  float o[kC];
+#pragma unroll
+  for (int k = 0; k < kC; ++k) o[k] = 0.0f;
+  for (int s = 0; s < nsp; ++s) {
+    const float w = exp2f(ml[2 * s] - mstar);
+    lsum = __builtin_fmaf(ml[2 * s + 1], w, lsum);
+#pragma unroll
+    for (int k = 0; k < kC; k += 4) {
+      const v4f x = *reinterpret_cast<const v4f*>(pa + static_cast<int64_t>(s) * D + k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[k + i] = __builtin_fmaf(x[i], w, o[k + i]);
     }
   }
-  for (int k = 0, c = lane; c < d; ++k, c += 64) o[c] = accv[k] * inv_l;
-  __syncthreads();
-  if (a.block > 0) {
-    for (int hh = 1; hh < a.block; hh *= 2) {
-      for (int q = lane; q < d / 2; q += 64) {
-        const int i = (q / hh) * (2 * hh) + (q % hh);
-        const float u = o[i], w = o[i + hh];
-        o[i] = u + w;
-        o[i + hh] = u - w;
-      }
-      __syncthreads();
-    }
-    const float sb = block_norm(a.block);
-    for (int c = lane; c < d; c += 64) dst[c] = o[c] * sb;
-  } else {
-    for (int c = lane; c < d; c += 64) dst[c] = o[c];
-  }
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;   // an empty sequence stores zeros
+#pragma unroll
+  for (int k = 0; k < kC; k += 4)
+    *reinterpret_cast<v4f*>(dst + k) = v4f{o[k] * inv, o[k + 1] * inv, o[k + 2] * inv, o[k + 3] * inv};
 }
 
 }  // namespace
 
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.batch * a.num_q_heads));
-  reduce_kernel<<<grid, 64, 0, s>>>(a);
+  const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
+  const dim3 grid(static_cast<unsigned>((rows + kReduceThreads / 16 - 1) / (kReduceThreads / 16)));
+  if (a.head_dim == 128)
+    reduce_kernel<128><<<grid, kReduceThreads, 0, s>>>(a);
+  else
+    reduce_kernel<64><<<grid, kReduceThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
