@@ -177,26 +177,40 @@ class DecodeBench:
         self.torch.cuda.empty_cache()
 
 
-def prefill_rate(torch, kvq, workloads, block, iters=50):
+def prefill_rates(torch, kvq, workloads, blocks=(64, 0), iters=50, chunk=10):
     """Rotate+quantize append of 32768 ragged tokens (8 KV heads, d 128) into a
-    page-16 pool: Mtokens/s and GB/s, RING input/cache sets."""
-    sets = []
-    for r in range(RING):
-        w = workloads.prefill_append(3 + 10 * r, device="cuda", block=block)
-        sets.append((w, kvq.Int4Cache(w.num_pages, w.hkv, w.d, block, "cuda")))
+    page-16 pool, for each Hadamard block in ``blocks``: Mtokens/s and GB/s
+    over RING input/cache sets.  The blocks are timed in alternating runs of
+    ``chunk`` calls so that they see the same clocks."""
+    sets = {}
+    for blk in blocks:
+        sets[blk] = []
+        for r in range(RING):
+            w = workloads.prefill_append(3 + 10 * r, device="cuda", block=blk)
+            sets[blk].append((w, kvq.Int4Cache(w.num_pages, w.hkv, w.d, blk, "cuda")))
 
-    def run(i):
-        w, c = sets[i % RING]
+    def run(blk, i):
+        w, c = sets[blk][i % RING]
         kvq.kvq_append_paged(c, w.k, w.v, w.slot_mapping)
 
-    for i in range(10):
-        run(i)
-    mean_ms, med_ms = _time_events(torch, run, iters)
-    w = sets[0][0]
-    tok = w.num_tokens
-    nbytes = append_bytes(tok, w.hkv, w.d, int4_bytes_per_vector(w.d))
-    return {"mtok_s": tok / (mean_ms * 1e-3) / 1e6, "gb_s": nbytes / (mean_ms * 1e-3) / 1e9,
-            "us": mean_ms * 1e3, "bytes": nbytes, "tokens": tok}
+    for blk in blocks:
+        for i in range(10):
+            run(blk, i)
+    tot = {blk: [] for blk in blocks}
+    for i0 in range(0, iters, chunk):
+        for blk in blocks:
+            n = min(chunk, iters - i0)
+            mean_ms, _ = _time_events(torch, lambda i: run(blk, i0 + i), n)
+            tot[blk].append((mean_ms, n))
+    res = {}
+    for blk in blocks:
+        mean_ms = sum(m * n for m, n in tot[blk]) / sum(n for _, n in tot[blk])
+        w = sets[blk][0][0]
+        tok = w.num_tokens
+        nbytes = append_bytes(tok, w.hkv, w.d, int4_bytes_per_vector(w.d))
+        res[blk] = {"mtok_s": tok / (mean_ms * 1e-3) / 1e6, "gb_s": nbytes / (mean_ms * 1e-3) / 1e9,
+                    "us": mean_ms * 1e3, "bytes": nbytes, "tokens": tok}
+    return res
 
 
 def long_context_rate(torch, kvq, workloads, iters=30):
@@ -233,16 +247,20 @@ def long_context_rate(torch, kvq, workloads, iters=30):
     return res
 
 
-def concurrency_sweep(torch, kvq, workloads, steps=32, warm=8, batches=(1, 8, 32, 128, 256)):
+def concurrency_sweep(torch, kvq, workloads, steps=32, warm=8, block_steps=8,
+                      batches=(1, 8, 32, 128, 256)):
     """70B-shaped layer (64 q / 8 kv heads): per batch size, fill the ragged
-    lognormal contexts, run ``warm`` untimed decode steps, then time ``steps``
-    decode steps (append one token per sequence, then decode over it) for the
-    rotated INT4, plain INT4 and bf16 caches.  Tokens/s = batch * steps /
-    time.  Successive steps attend the same cache, as a serving loop does
-    (small batches stay in the Infinity Cache)."""
+    lognormal contexts into a rotated INT4, a plain INT4 and a bf16 cache, run
+    ``warm`` untimed decode steps on each (append one token per sequence, then
+    decode over it), then time ``steps`` more per cache in runs of
+    ``block_steps`` that alternate between the caches, so that all three see
+    the same clocks.  Tokens/s = batch * steps / time.  Successive steps
+    attend the same cache, as a serving loop does (small batches stay in the
+    Infinity Cache)."""
     out = {"workload": "64 q / 8 kv heads, head_dim 128, lognormal contexts (median 2048, "
                        "sigma 1, cap 32768), page 16, one new token per sequence per step",
            "steps": steps}
+    names = ("int4_block64", "int4_plain", "bf16")
     for b in batches:
         fill, st = workloads.concurrency_step(5, device="cuda", batch=b, block=64, steps=warm + steps)
         bt = torch.from_numpy(st[0].block_table).to("cuda")
@@ -251,33 +269,46 @@ def concurrency_sweep(torch, kvq, workloads, steps=32, warm=8, batches=(1, 8, 32
         ws = torch.empty(max(16, kvq.kvq_decode_workspace_bytes(b, fill.hq, fill.hkv, fill.d, maxlen)),
                          dtype=torch.uint8, device="cuda")
         o = torch.empty((b, fill.hq, fill.d), dtype=torch.float32, device="cuda")
-        row = {"context_tokens": int(fill.seq_lens.sum())}
-        for name in ("int4_block64", "int4_plain", "bf16"):
+        caches, fns = {}, {}
+        for name in names:
             if name == "bf16":
-                cache = kvq.Bf16Cache(fill.num_pages, fill.hkv, fill.d, "cuda")
-                app, dec = kvq.kvq_append_paged_bf16, kvq.kvq_decode_attn_bf16
+                caches[name] = kvq.Bf16Cache(fill.num_pages, fill.hkv, fill.d, "cuda")
+                fns[name] = (kvq.kvq_append_paged_bf16, kvq.kvq_decode_attn_bf16)
             else:
-                cache = kvq.Int4Cache(fill.num_pages, fill.hkv, fill.d, 64 if name == "int4_block64" else 0,
-                                      "cuda")
-                app, dec = kvq.kvq_append_paged, kvq.kvq_decode_attn
-            app(cache, fill.k, fill.v, fill.slot_mapping)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            for i, x in enumerate(st):
-                if i == warm:
-                    torch.cuda.synchronize()
-                    e0.record()
-                app(cache, x.k, x.v, x.slot_mapping)
-                dec(cache, x.q, bt, sls[i], maxlen, x.sm_scale, out=o, workspace=ws)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1)
-            row[name] = {"us_per_step": round(ms * 1e3 / steps, 2), "tokens_s": round(b * steps / (ms * 1e-3), 1)}
-            del cache
+                caches[name] = kvq.Int4Cache(fill.num_pages, fill.hkv, fill.d,
+                                             64 if name == "int4_block64" else 0, "cuda")
+                fns[name] = (kvq.kvq_append_paged, kvq.kvq_decode_attn)
+            fns[name][0](caches[name], fill.k, fill.v, fill.slot_mapping)
+
+        def run(name, i):
+            app, dec = fns[name]
+            x = st[i]
+            app(caches[name], x.k, x.v, x.slot_mapping)
+            dec(caches[name], x.q, bt, sls[i], maxlen, x.sm_scale, out=o, workspace=ws)
+
+        for name in names:
+            for i in range(warm):
+                run(name, i)
+        ms = {name: 0.0 for name in names}
+        for i0 in range(warm, warm + steps, block_steps):
+            for name in names:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for i in range(i0, min(i0 + block_steps, warm + steps)):
+                    run(name, i)
+                e1.record()
+                torch.cuda.synchronize()
+                ms[name] += e0.elapsed_time(e1)
+        row = {"context_tokens": int(fill.seq_lens.sum())}
+        for name in names:
+            row[name] = {"us_per_step": round(ms[name] * 1e3 / steps, 2),
+                         "tokens_s": round(b * steps / (ms[name] * 1e-3), 1)}
         row["rotated_over_plain"] = round(row["int4_block64"]["tokens_s"] / row["int4_plain"]["tokens_s"], 4)
         row["int4_over_bf16"] = round(row["int4_block64"]["tokens_s"] / row["bf16"]["tokens_s"], 3)
         out[f"batch{b}"] = row
-        del fill, st
+        del fill, st, caches
         torch.cuda.empty_cache()
     return out
 
@@ -367,7 +398,7 @@ def main(argv=None):
         return 0
 
     if args.mode == "prefill":
-        r = prefill_rate(torch, kvq, workloads, 64, iters=args.steps)
+        r = prefill_rates(torch, kvq, workloads, blocks=(64,), iters=args.steps)[64]
         print(json.dumps({"mode": "prefill", **r}))
         return 0
 
@@ -429,8 +460,9 @@ def main(argv=None):
     db.free()
     del db
 
-    prefill_rot = prefill_rate(torch, kvq, workloads, 64)
-    prefill_plain = prefill_rate(torch, kvq, workloads, 0)
+    pre = prefill_rates(torch, kvq, workloads)
+    prefill_rot, prefill_plain = pre[64], pre[0]
+    del pre
     torch.cuda.empty_cache()
     long_ctx = long_context_rate(torch, kvq, workloads)
     conc = concurrency_sweep(torch, kvq, workloads)

@@ -131,7 +131,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63;
   const int g = lane >> 4, n = lane & 15, hs = n >> 2, lam = n & 3;
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // Work item (split s, sequence b, KV head), KV head fastest and split
+  // slowest, last split first.  Each split is one contiguous run of
+  // workgroups that the round-robin dispatch spreads over every XCD and CU
+  // (with the split fastest, a period of 2, 4 or 8 left most CUs with the
+  // empty splits of short sequences only), and the later splits, busy only
+  // for the longest sequences, start first instead of last.
+  const uint32_t wid = blockIdx.x;
+  const int kvh = static_cast<int>(wid % a.num_kv_heads);
+  const int b = static_cast<int>((wid / a.num_kv_heads) % a.batch);
+  const int s = a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
 
@@ -553,7 +562,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
 
 template <int D, int NS>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.nsplit, a.num_kv_heads, a.batch);
+  const dim3 grid(static_cast<unsigned>(a.nsplit) * a.num_kv_heads * a.batch);
   if (a.in_bf16)
     decode_int4_kernel<D, NS, true><<<grid, 64 * kWaves, 0, s>>>(a);
   else
