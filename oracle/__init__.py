@@ -89,6 +89,9 @@ def _declare(L):
     L.kvq_oracle_decode_int4_bruteforce.argtypes = [_p, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p,
                                                     _i32, _p, _i32, C.c_double, _p]
     L.kvq_oracle_decode_int4_bruteforce.restype = _i32
+    L.kvq_oracle_decode_windowed.argtypes = [_p, _p, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p, _i32,
+                                             _p, _i32, _p, _i32, _i32, _i32, C.c_double, _p, _p]
+    L.kvq_oracle_decode_windowed.restype = _i32
     L.kvq_oracle_num_threads.argtypes = []
     L.kvq_oracle_num_threads.restype = _i32
 
@@ -238,6 +241,25 @@ def decode_bf16(pool, num_kv_heads, head_dim, q, dtype, block_table, seq_lens, s
                                       float(sm_scale), None if mk is None else _ptr(mk), _ptr(out))
     if rc != 0:
         raise ValueError("oracle decode_bf16 rejected its arguments")
+    return out
+
+
+def decode_windowed(int4_pool, win_pool, num_kv_heads, head_dim, block, q, dtype, block_table,
+                    win_block_table, seq_lens, w_sink, w_recent, sm_scale, page_size=16, mask=None):
+    q = _c(q, np.uint16)
+    bt = _c(block_table, np.int32)
+    wbt = _c(win_block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    batch, hq, d = q.shape
+    out = np.zeros((batch, hq, d), np.float64)
+    mk = None if mask is None else _c(mask, np.uint8)
+    rc = lib().kvq_oracle_decode_windowed(_ptr(int4_pool), _ptr(win_pool), page_size, num_kv_heads,
+                                          head_dim, int(block), _ptr(q), int(dtype), hq, _ptr(bt),
+                                          bt.shape[1], _ptr(wbt), wbt.shape[1], _ptr(sl), batch,
+                                          int(w_sink), int(w_recent), float(sm_scale),
+                                          None if mk is None else _ptr(mk), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle decode_windowed rejected its arguments")
     return out
 
 

@@ -355,6 +355,77 @@ int32_t kvq_oracle_decode_bf16(const uint8_t* pool, int32_t page_size, int32_t n
                       block_table, max_pages_per_seq, seq_lens, batch, sm_scale, mask, out);
 }
 
+int32_t kvq_oracle_decode_windowed(const uint8_t* int4_pool, const uint8_t* win_pool,
+                                   int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block, const uint16_t* q, int32_t dtype,
+                                   int32_t num_q_heads, const int32_t* block_table,
+                                   int32_t max_pages_per_seq, const int32_t* win_block_table,
+                                   int32_t max_win_pages, const int32_t* seq_lens, int32_t batch,
+                                   int32_t w_sink, int32_t w_recent, double sm_scale,
+                                   const uint8_t* mask, double* out) {
+  const int d = head_dim, hq = num_q_heads, p = page_size;
+  if (!valid_block(block, d) || num_kv_heads <= 0 || hq % num_kv_heads != 0) return 1;
+  if (w_sink < 0 || w_recent < 0) return 1;
+  const int group = hq / num_kv_heads;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < batch; ++b)
+    for (int h = 0; h < hq; ++h) {
+      double* o = out + (static_cast<size_t>(b) * hq + h) * d;
+      for (int c = 0; c < d; ++c) o[c] = 0.0;
+      if (mask && !mask[static_cast<size_t>(b) * hq + h]) continue;
+      const int len = seq_lens[b];
+      if (len <= 0) continue;
+      const int kvh = h / group;
+      std::vector<double> qv(d), qr(d), s(len), o_int4(d, 0.0), o_win(d, 0.0), tmp(d);
+      for (int c = 0; c < d; ++c) qv[c] = widen(q[(static_cast<size_t>(b) * hq + h) * d + c], dtype);
+      rotate_f64(qv.data(), qr.data(), d, block);
+      /* token t lives in the bf16 window when it is one of the first w_sink
+         or of the last w_recent tokens; window position: sinks in order, then
+         a ring of w_recent slots indexed by (t - w_sink) mod w_recent */
+      auto in_window = [&](int t) { return t < w_sink || t >= len - w_recent; };
+      auto win_page_off = [&](int t, int* page, int* off) {
+        const int pos = t < w_sink ? t : w_sink + (t - w_sink) % w_recent;
+        *page = win_block_table[static_cast<size_t>(b) * max_win_pages + pos / p];
+        *off = pos % p;
+      };
+      double mx = -INFINITY;
+      for (int t = 0; t < len; ++t) {
+        double dot = 0.0;
+        if (in_window(t)) {   /* original basis, un-rotated query */
+          int page, off;
+          win_page_off(t, &page, &off);
+          for (int c = 0; c < d; ++c)
+            dot += qv[c] * kvq_oracle_bf16_read(win_pool, p, num_kv_heads, d, page, kvh, off, 0, c);
+        } else {              /* rotated basis, rotated query */
+          const int page = block_table[static_cast<size_t>(b) * max_pages_per_seq + t / p];
+          for (int c = 0; c < d; ++c)
+            dot += qr[c] * kvq_oracle_int4_read(int4_pool, p, num_kv_heads, d, page, kvh, t % p, 0, c,
+                                                nullptr, nullptr, nullptr);
+        }
+        s[t] = sm_scale * dot;
+        if (s[t] > mx) mx = s[t];
+      }
+      double l = 0.0;
+      for (int t = 0; t < len; ++t) { s[t] = std::exp(s[t] - mx); l += s[t]; }
+      for (int t = 0; t < len; ++t) {
+        if (in_window(t)) {
+          int page, off;
+          win_page_off(t, &page, &off);
+          for (int c = 0; c < d; ++c)
+            o_win[c] += s[t] * kvq_oracle_bf16_read(win_pool, p, num_kv_heads, d, page, kvh, off, 1, c);
+        } else {
+          const int page = block_table[static_cast<size_t>(b) * max_pages_per_seq + t / p];
+          for (int c = 0; c < d; ++c)
+            o_int4[c] += s[t] * kvq_oracle_int4_read(int4_pool, p, num_kv_heads, d, page, kvh, t % p, 1, c,
+                                                     nullptr, nullptr, nullptr);
+        }
+      }
+      rotate_f64(o_int4.data(), tmp.data(), d, block);   /* back to the original basis */
+      for (int c = 0; c < d; ++c) o[c] = (tmp[c] + o_win[c]) / l;
+    }
+  return 0;
+}
+
 int32_t kvq_oracle_decode_int4_bruteforce(const uint8_t* pool, int32_t page_size,
                                           int32_t num_kv_heads, int32_t head_dim, int32_t block,
                                           const uint16_t* q, int32_t dtype, int32_t num_q_heads,

@@ -141,6 +141,26 @@ int32_t kvq_oracle_decode_bf16(const uint8_t* pool, int32_t page_size,
                                const int32_t* seq_lens, int32_t batch, double sm_scale,
                                const uint8_t* mask, double* out);
 
+/* Attention with high-precision windows ("InnerQ", Abstract and Figure 2):
+ * for a sequence of length L the first w_sink tokens and the last w_recent
+ * tokens are read as bf16 from `win_pool` (a bf16 pool in the layout above)
+ * in the original basis with the un-rotated query; every other token is read
+ * from the INT4 pool in the rotated basis with the rotated query.  One exact
+ * fp64 softmax over all L tokens; the INT4 tokens' share of the output is
+ * rotated back before the two shares are added.  Window position of token t:
+ * t when t < w_sink, else w_sink + (t - w_sink) mod w_recent (a ring of the
+ * recent tokens), found through `win_block_table` [batch][max_win_pages].
+ * Reading R8: the windows hold unrotated bf16 copies (the rotation only
+ * serves the 4-bit codes). */
+int32_t kvq_oracle_decode_windowed(const uint8_t* int4_pool, const uint8_t* win_pool,
+                                   int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block, const uint16_t* q, int32_t dtype,
+                                   int32_t num_q_heads, const int32_t* block_table,
+                                   int32_t max_pages_per_seq, const int32_t* win_block_table,
+                                   int32_t max_win_pages, const int32_t* seq_lens, int32_t batch,
+                                   int32_t w_sink, int32_t w_recent, double sm_scale,
+                                   const uint8_t* mask, double* out);
+
 /* Brute-force twin of kvq_oracle_decode_int4: gathers each sequence's keys and
  * values into contiguous fp64 rows, rotates every decoded row back with the
  * explicit matrix (H_b/sqrt(b))^T, and attends with the un-rotated query.  A

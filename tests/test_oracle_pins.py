@@ -510,3 +510,98 @@ def test_large_logits_stay_finite():
         vv = _dequant_seq(w, pool, b, 0, 1) @ rinv.T
         p = scipy.special.softmax(w.sm_scale * kk @ qf[b, 0])
         assert np.abs(out[b, 0] - p @ vv).max() <= 1e-9 * np.abs(vv).max()
+
+
+# ---------------------------------------------------------------- high-precision windows
+
+def _window_pool(w, w_sink, w_recent, seed=5, final_len=None):
+    """The bf16 window pool holding, for each sequence, the tokens that are in
+    its windows at length final_len (default: the workload's lengths)."""
+    rng = np.random.default_rng(seed)
+    wbt, npages = workloads.window_layout(w.batch, w_sink, w_recent, rng)
+    flen = w.seq_lens if final_len is None else np.asarray(final_len)
+    slots = workloads.window_slots(wbt, w.token_seq, w.token_pos, flen, w_sink, w_recent)
+    pool = oracle.new_bf16_pool(npages, w.hkv, w.d)
+    oracle.append_bf16(pool, npages, w.hkv, w.d, workloads.bits(w.k), workloads.bits(w.v),
+                       oracle.F16 if w.k.dtype == torch.float16 else oracle.BF16, slots)
+    return wbt, pool
+
+
+def test_windowed_without_windows_is_int4_attention():
+    w, pool = _tiny_case(seed=6, block=64, lens=[45, 16, 3])
+    wbt, wpool = _window_pool(w, 0, 0)
+    q = workloads.bits(w.q)
+    a = oracle.decode_int4(pool, w.hkv, w.d, 64, q, oracle.F16, w.block_table, w.seq_lens, w.sm_scale)
+    b = oracle.decode_windowed(pool, wpool, w.hkv, w.d, 64, q, oracle.F16, w.block_table, wbt,
+                               w.seq_lens, 0, 0, w.sm_scale)
+    assert np.abs(a - b).max() <= 1e-12 * max(1.0, np.abs(a).max())
+
+
+@pytest.mark.parametrize("w_sink,w_recent", [(64, 0), (0, 64), (20, 44)])
+def test_windowed_covering_everything_is_bf16_attention(w_sink, w_recent):
+    """Windows at least as long as every sequence: every token is read as
+    bf16, which is plain bf16 attention over the window pool."""
+    w, pool = _tiny_case(seed=7, block=32, lens=[40, 64, 9])
+    wbt, wpool = _window_pool(w, w_sink, w_recent)
+    q = workloads.bits(w.q)
+    want = oracle.decode_bf16(wpool, w.hkv, w.d, q, oracle.F16, wbt, w.seq_lens, w.sm_scale)
+    got = oracle.decode_windowed(pool, wpool, w.hkv, w.d, 32, q, oracle.F16, w.block_table, wbt,
+                                 w.seq_lens, w_sink, w_recent, w.sm_scale)
+    assert np.abs(got - want).max() <= 1e-12 * max(1.0, np.abs(want).max())
+
+
+@pytest.mark.parametrize("block,w_sink,w_recent", [(64, 4, 12), (16, 0, 20), (0, 7, 0)])
+def test_windowed_matches_explicit_rows(block, w_sink, w_recent):
+    """Brute force: each token's key and value assembled by hand (window
+    tokens from the inputs rounded to bf16 by torch, the others decoded from
+    the INT4 pool and rotated back with scipy's Hadamard), one scipy softmax."""
+    w, pool = _tiny_case(seed=8, block=block, lens=[53, 21, 6])
+    wbt, wpool = _window_pool(w, w_sink, w_recent)
+    q = workloads.bits(w.q)
+    out = oracle.decode_windowed(pool, wpool, w.hkv, w.d, block, q, oracle.F16, w.block_table, wbt,
+                                 w.seq_lens, w_sink, w_recent, w.sm_scale)
+    g = w.hq // w.hkv
+    rinv = np.eye(w.d) if block == 0 else np.kron(np.eye(w.d // block), scipy.linalg.hadamard(block)) / np.sqrt(block)
+    qf = w.q.float().numpy().astype(np.float64)
+    kin = w.k.to(torch.bfloat16).float().numpy().astype(np.float64)
+    vin = w.v.to(torch.bfloat16).float().numpy().astype(np.float64)
+    for b in range(w.batch):
+        n = int(w.seq_lens[b])
+        idx = np.nonzero(w.token_seq == b)[0]
+        idx = idx[np.argsort(w.token_pos[idx])]
+        for h in range(w.hq):
+            kvh = h // g
+            kk = _dequant_seq(w, pool, b, kvh, 0) @ rinv.T
+            vv = _dequant_seq(w, pool, b, kvh, 1) @ rinv.T
+            for t in range(n):
+                if t < w_sink or t >= n - w_recent:
+                    kk[t] = kin[idx[t], kvh]
+                    vv[t] = vin[idx[t], kvh]
+            p = scipy.special.softmax(w.sm_scale * kk @ qf[b, h])
+            assert np.abs(out[b, h] - p @ vv).max() <= 1e-12 * max(1.0, np.abs(vv).max())
+
+
+def test_windowed_ring_after_decode_steps():
+    """Appending one token at a time into the ring keeps exactly the last
+    w_recent tokens: the oracle then equals the brute force over the final
+    length, though every ring slot was overwritten."""
+    lens = np.array([30, 19])
+    w, pool = _tiny_case(seed=9, block=16, lens=lens)
+    w_sink, w_recent = 3, 5
+    rng = np.random.default_rng(4)
+    wbt, npages = workloads.window_layout(w.batch, w_sink, w_recent, rng)
+    wpool = oracle.new_bf16_pool(npages, w.hkv, w.d)
+    kb, vb = workloads.bits(w.k), workloads.bits(w.v)
+    order = np.lexsort((w.token_seq, w.token_pos))      # by position, as decode steps append
+    for i in order:
+        # the sequence has token_pos + 1 tokens right after this append
+        s = workloads.window_slots(wbt, w.token_seq[i:i + 1], w.token_pos[i:i + 1],
+                                   np.full(w.batch, w.token_pos[i] + 1), w_sink, w_recent)
+        oracle.append_bf16(wpool, npages, w.hkv, w.d, kb[i:i + 1], vb[i:i + 1], oracle.F16, s)
+    ref_wbt, ref_pool = _window_pool(w, w_sink, w_recent, seed=4)
+    q = workloads.bits(w.q)
+    got = oracle.decode_windowed(pool, wpool, w.hkv, w.d, 16, q, oracle.F16, w.block_table, wbt,
+                                 w.seq_lens, w_sink, w_recent, w.sm_scale)
+    want = oracle.decode_windowed(pool, ref_pool, w.hkv, w.d, 16, q, oracle.F16, w.block_table, ref_wbt,
+                                  w.seq_lens, w_sink, w_recent, w.sm_scale)
+    assert np.array_equal(got, want)

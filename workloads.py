@@ -267,6 +267,36 @@ def random_decode(seed: int, device="cpu", batch: int = 3, hq: int = 8, hkv: int
     return _make("random_decode", hq, hkv, d, block, dtype, seq_lens, k, v, q, rng, device)
 
 
+# ---------------------------------------------------------------------------
+# High-precision windows: the first w_sink tokens and the last w_recent tokens
+# of each sequence also live as bf16 in a separate window pool.  Window
+# position of token t: t for t < w_sink, else w_sink + (t - w_sink) % w_recent
+# (a ring, so a new token overwrites the one that leaves the window).
+
+
+def window_layout(batch: int, w_sink: int, w_recent: int, rng: np.random.Generator):
+    """Window block table [batch][pages per window] over a seeded permutation
+    of the window pool; returns (table, pool pages)."""
+    per = max(1, (w_sink + w_recent + PAGE - 1) // PAGE)
+    perm = rng.permutation(batch * per).astype(np.int32)
+    return perm.reshape(batch, per), batch * per
+
+
+def window_slots(win_bt: np.ndarray, seq: np.ndarray, pos: np.ndarray, final_len: np.ndarray,
+                 w_sink: int, w_recent: int) -> np.ndarray:
+    """Window-pool slot of each token (seq[i], pos[i]) that is still inside
+    its sequence's windows once the sequence has final_len[seq] tokens; -1 for
+    the others (so one append call never writes a ring slot twice)."""
+    seq = np.asarray(seq)
+    pos = np.asarray(pos).astype(np.int64)
+    flen = np.asarray(final_len)[seq].astype(np.int64)
+    keep = (pos < w_sink) | (pos >= flen - w_recent)
+    wpos = np.where(pos < w_sink, pos, w_sink + (pos - w_sink) % max(w_recent, 1))
+    pages = win_bt[seq, wpos // PAGE]
+    slots = pages.astype(np.int64) * PAGE + wpos % PAGE
+    return np.where(keep, slots, -1).astype(np.int32)
+
+
 def bits(x: torch.Tensor) -> np.ndarray:
     """16-bit float tensor -> numpy uint16 bit patterns (host copy)."""
     return x.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
