@@ -29,6 +29,7 @@ PAGE_SIZE = 16
 EXPORTED = (
     "kvq_int4_page_bytes", "kvq_bf16_page_bytes", "kvq_append_paged", "kvq_decode_attn",
     "kvq_decode_workspace_bytes", "kvq_append_paged_bf16", "kvq_decode_attn_bf16",
+    "kvq_decode_attn_windowed", "kvq_decode_windowed_workspace_bytes",
     "kvq_status_string", "kvq_last_error", "kvq_abi_version",
 )
 
@@ -78,6 +79,12 @@ def lib() -> C.CDLL:
         L.kvq_decode_attn_bf16.restype = i32
         L.kvq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.kvq_decode_workspace_bytes.restype = sz
+        L.kvq_decode_attn_windowed.argtypes = [C.POINTER(_Int4Desc), C.POINTER(_Bf16Desc), p, i32, i32,
+                                               p, i32, p, i32, p, i32, i32, i32, i32, C.c_float, i32,
+                                               p, p, sz, p]
+        L.kvq_decode_attn_windowed.restype = i32
+        L.kvq_decode_windowed_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.kvq_decode_windowed_workspace_bytes.restype = sz
         L.kvq_status_string.argtypes = [i32]
         L.kvq_status_string.restype = C.c_char_p
         L.kvq_last_error.argtypes = []
@@ -238,6 +245,45 @@ def kvq_decode_attn_bf16(cache: Bf16Cache, q: torch.Tensor, block_table: torch.T
     return _decode(lib().kvq_decode_attn_bf16, cache.desc(), cache.num_kv_heads, cache.head_dim,
                    q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace, num_splits,
                    stream)
+
+
+def kvq_decode_windowed_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int,
+                                        head_dim: int, max_seq_len: int, num_splits: int = 0) -> int:
+    return int(lib().kvq_decode_windowed_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                         max_seq_len, num_splits))
+
+
+def kvq_decode_attn_windowed(cache: Int4Cache, window: Bf16Cache, q: torch.Tensor,
+                             block_table: torch.Tensor, window_table: torch.Tensor,
+                             seq_lens: torch.Tensor, max_seq_len: int, w_sink: int, w_recent: int,
+                             sm_scale: float | None = None, out: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None, num_splits: int = 0,
+                             stream=None) -> torch.Tensor:
+    """Decode attention with bf16 windows for the first w_sink and the last
+    w_recent tokens of each sequence; returns fp32 [B][Hq][D]."""
+    d = cache.head_dim
+    if q.dim() != 3 or q.shape[2] != d or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][Hq][D] tensor")
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    for name, t in (("block_table", block_table), ("window_table", window_table), ("seq_lens", seq_lens)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor")
+    need = kvq_decode_windowed_workspace_bytes(batch, hq, cache.num_kv_heads, d, max_seq_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().kvq_decode_attn_windowed(
+        C.byref(cache.desc()), C.byref(window.desc()), _ptr(q), _dtype_code(q), hq, _ptr(block_table),
+        int(block_table.shape[1]), _ptr(window_table), int(window_table.shape[1]), _ptr(seq_lens),
+        batch, int(max_seq_len), int(w_sink), int(w_recent), float(sm_scale), int(num_splits),
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream, q.device)))
+    return out
 
 
 def abi_version() -> int:

@@ -156,6 +156,8 @@ kvq_status launch_decode(bool int4, const void* pool, int32_t num_pages, int32_t
   a.nsplit = plan.nsplit;
   a.sm_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
   a.in_bf16 = dtype == KVQ_BF16;
+  a.part_stride = plan.nsplit;
+  a.window_slot = -1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = int4 ? launch_decode_int4(a, s) : launch_decode_bf16(a, s);
   if (e == hipSuccess && plan.nsplit > 1) e = launch_reduce(a, s);
@@ -263,6 +265,110 @@ kvq_status kvq_decode_attn_bf16(const kvq_bf16_cache* cache, const void* q, kvq_
                        q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens, batch,
                        max_seq_len, sm_scale, num_splits, out, workspace, workspace_bytes_given,
                        stream);
+}
+
+kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_cache* window,
+                                    const void* q, kvq_dtype dtype, int32_t num_q_heads,
+                                    const int32_t* block_table, int32_t max_pages_per_seq,
+                                    const int32_t* window_table, int32_t max_window_pages,
+                                    const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                    int32_t w_sink, int32_t w_recent, float sm_scale,
+                                    int32_t num_splits, float* out, void* workspace,
+                                    size_t workspace_bytes_given, void* stream) {
+  if (cache == nullptr || window == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
+  kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
+  if (st != KVQ_OK) return st;
+  st = check_geometry(window->num_pages, window->page_size, window->num_kv_heads, window->head_dim);
+  if (st != KVQ_OK) return st;
+  if (window->num_kv_heads != cache->num_kv_heads || window->head_dim != cache->head_dim)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "window pool geometry differs from the INT4 cache");
+  const int blk = cache->hadamard_block;
+  if (!(blk == 0 || blk == 16 || blk == 32 || blk == 64 || blk == 128) || blk > cache->head_dim)
+    return fail(KVQ_ERR_UNSUPPORTED, "hadamard_block %d unsupported for head_dim %d", blk, cache->head_dim);
+  const int32_t hkv = cache->num_kv_heads, d = cache->head_dim, hq = num_q_heads;
+  st = check_decode(cache->pool, q, dtype, hq, hkv, block_table, max_pages_per_seq, seq_lens, batch,
+                    max_seq_len, sm_scale, num_splits, out);
+  if (st != KVQ_OK) return st;
+  if (w_sink < 0 || w_recent < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "window sizes must be >= 0");
+  const int64_t wlen = static_cast<int64_t>(w_sink) + w_recent;
+  if (wlen > INT32_MAX / 2) return fail(KVQ_ERR_INVALID_ARGUMENT, "window sizes too large");
+  if (wlen > 0) {
+    if (window->pool == nullptr || !aligned16(window->pool))
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "window pool null or not 16-byte aligned");
+    if (batch > 0 && (window_table == nullptr || !aligned4(window_table)))
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "window_table null or misaligned");
+    if (static_cast<int64_t>(max_window_pages) * 16 < wlen)
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "max_window_pages*16 < w_sink + w_recent");
+  }
+  if (batch == 0) return KVQ_OK;
+  const SplitPlan plan = plan_splits(batch, hkv, max_seq_len, num_splits);
+  const int32_t stride = plan.nsplit + 1;   // the INT4 splits, then the window pass
+  if (static_cast<int64_t>(plan.nsplit) * hkv * batch > INT32_MAX)
+    return fail(KVQ_ERR_UNSUPPORTED, "batch * num_kv_heads * splits above 2^31 workgroups");
+  const size_t need = static_cast<size_t>(batch) * hq * stride * (d + 2) * sizeof(float);
+  if (workspace_bytes_given < need)
+    return fail(KVQ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes_given, need);
+  if (workspace == nullptr || !aligned16(workspace))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "workspace null or not 16-byte aligned");
+
+  DecodeArgs a{};   // the INT4 pass over the tokens between the windows
+  a.pool = static_cast<const uint8_t*>(cache->pool);
+  a.q = static_cast<const uint16_t*>(q);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.part_acc = static_cast<float*>(workspace);
+  a.part_ml = static_cast<float*>(workspace) + static_cast<size_t>(batch) * hq * stride * d;
+  a.num_pages = cache->num_pages;
+  a.num_kv_heads = hkv;
+  a.num_q_heads = hq;
+  a.head_dim = d;
+  a.block = blk;
+  a.bt_stride = max_pages_per_seq;
+  a.batch = batch;
+  a.max_seq_len = max_seq_len;
+  a.split_pages = plan.split_pages;
+  a.nsplit = plan.nsplit;
+  a.sm_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  a.in_bf16 = dtype == KVQ_BF16;
+  a.skip_first = w_sink;
+  a.skip_last = w_recent;
+  a.part_stride = stride;
+  a.force_partial = 1;
+  a.window_slot = -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_decode_int4(a, s);
+  if (e == hipSuccess && wlen > 0) {   // the bf16 pass over each sequence's window
+    DecodeArgs w = a;
+    w.pool = static_cast<const uint8_t*>(window->pool);
+    w.block_table = window_table;
+    w.bt_stride = max_window_pages;
+    w.num_pages = window->num_pages;
+    w.block = 0;
+    w.skip_first = w.skip_last = 0;
+    w.len_cap = static_cast<int32_t>(wlen);
+    w.split_pages = static_cast<int32_t>((wlen + 15) / 16 + 3) / 4 * 4;
+    w.nsplit = 1;
+    w.part_slot0 = plan.nsplit;
+    e = launch_decode_bf16(w, s);
+  }
+  if (e == hipSuccess) {
+    DecodeArgs r = a;
+    r.len_cap = static_cast<int32_t>(wlen);
+    r.window_slot = wlen > 0 ? plan.nsplit : -1;
+    e = launch_reduce(r, s);
+  }
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+size_t kvq_decode_windowed_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t max_seq_len, int32_t num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
+      num_splits < 0)
+    return 0;
+  const SplitPlan plan = plan_splits(batch, num_kv_heads, max_seq_len, num_splits);
+  return static_cast<size_t>(batch) * num_q_heads * (plan.nsplit + 1) * (head_dim + 2) * sizeof(float);
 }
 
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -90,11 +90,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) 
 
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+  if (a.len_cap > 0 && len > a.len_cap) len = a.len_cap;   // window pass: the window's tokens
   const int npg = (len + kPage - 1) / kPage;
   const int p0 = s * a.split_pages;
   const int p1 = min(npg, p0 + a.split_pages);
   if (p0 >= p1) {
-    if (a.nsplit == 1) {
+    if (a.nsplit == 1 && !a.force_partial) {
       for (int e = tid; e < G * D; e += 64 * kWaves)
         a.out[(static_cast<int64_t>(b) * a.num_q_heads + kvh * G + e / D) * D + e % D] = 0.0f;
     }
@@ -287,10 +288,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) 
       lsum = __builtin_fmaf(sm.u.merge.l[w][j], f, lsum);
       osum = __builtin_fmaf(sm.u.merge.acc[w][j][c], f, osum);
     }
-    if (a.nsplit == 1) {
+    if (a.nsplit == 1 && !a.force_partial) {
       a.out[(hq0 + j) * D + c] = lsum > 0.0f ? osum / lsum : 0.0f;
     } else {
-      const int64_t idx = (hq0 + j) * a.nsplit + s;
+      const int64_t idx = (hq0 + j) * a.part_stride + a.part_slot0 + s;
       a.part_acc[idx * D + c] = osum;
       if (c == 0) {
         a.part_ml[idx * 2 + 0] = mstar;

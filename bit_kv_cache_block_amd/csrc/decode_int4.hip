@@ -185,19 +185,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
 
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-  const int npg = (len + kPage - 1) / kPage;
+  int lo, hi;   // the tokens this pass reads (all of them unless windows take some)
+  int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
+  const int npg = (hi + kPage - 1) / kPage;
+  const int q0 = max(p0, lo / kPage);
   const int p1 = min(npg, p0 + a.split_pages);
-  if (p0 >= p1) {
-    if (a.nsplit == 1) {   // empty sequence: zero output rows
+  if (q0 >= p1 || hi <= lo) {
+    if (a.nsplit == 1 && !a.force_partial) {   // empty sequence: zero output rows
       for (int e = tid; e < G * D; e += 64 * kWaves) a.out[hq0 * D + e] = 0.0f;
     }
     return;
   }
 
   // ---- this wave's share of the split's pages ---------------------------------
-  const int span = p1 - p0;
+  const int span = p1 - q0;
   const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
-  const int pw0 = p0 + wave * per_wave;
+  const int pw0 = q0 + wave * per_wave;
   const int pw1 = min(p1, pw0 + per_wave);
   const uint8_t* pool_h = a.pool + static_cast<int64_t>(kvh) * kSlab;
   const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kSlab;
@@ -361,7 +364,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
                  static_cast<int32_t>((sb.kx[i][0] >> 4) & kLowNibbles),
                  static_cast<int32_t>((sb.kx[i][1] >> 4) & kLowNibbles)};
       }
-      const bool ok = !tail || (sb.pv[i] && (p + i) * kPage + n < len);
+      const int tok = (p + i) * kPage + n;
+      const bool ok = !tail || (sb.pv[i] && tok >= lo && tok < hi);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         v4i c = mfma_i8(aq[st][0], b0, zero4);
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
 
   // ---- stream the wave's pages ----------------------------------------------
   auto step = [&](const StepBuf& sb, int p) {
-    if (!sb.all_ok || (p + kStep) * kPage > len)
+    if (!sb.all_ok || (p + kStep) * kPage > hi || p * kPage < lo)
       compute(sb, p, std::true_type{});
     else
       compute(sb, p, std::false_type{});
@@ -538,7 +542,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
       fwht_row<kC>(o, a.block, n);
       scale = block_norm(a.block);
     }
-    if (a.nsplit == 1) {
+    if (a.nsplit == 1 && !a.force_partial) {
       scale *= lsum > 0.0f ? 1.0f / lsum : 0.0f;
       if (j < G) {
         float* dst = a.out + (hq0 + j) * D + kC * n;
@@ -547,7 +551,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
           *reinterpret_cast<v4f*>(dst + k) = v4f{o[k] * scale, o[k + 1] * scale, o[k + 2] * scale, o[k + 3] * scale};
       }
     } else if (j < G) {
-      const int64_t idx = (hq0 + j) * a.nsplit + s;
+      const int64_t idx = (hq0 + j) * a.part_stride + a.part_slot0 + s;
       float* dst = a.part_acc + idx * D + kC * n;
 #pragma unroll
       for (int k = 0; k < kC; k += 4)

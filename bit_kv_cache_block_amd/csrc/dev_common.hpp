@@ -155,6 +155,14 @@ __device__ __forceinline__ void fwht_row(float* v, int block, int n) {
   if (8 * C < block) cross(std::integral_constant<int, 8>{});
 }
 
+// Tokens [lo, hi) of a sequence of `len` tokens that an INT4 pass reads
+// when the first skip_first and the last skip_last tokens are left to the
+// high-precision windows (both zero: all of them).
+__device__ __forceinline__ void int4_token_range(int len, int skip_first, int skip_last, int& lo, int& hi) {
+  lo = skip_first < len ? skip_first : len;
+  hi = len - skip_last > lo ? len - skip_last : lo;
+}
+
 // Raw buffer descriptor over [base, base + bytes): loads through it take a
 // 32-bit lane offset and return zero beyond `bytes` (word 3 = 32-bit data
 // format, the value raw loads expect on CDNA).

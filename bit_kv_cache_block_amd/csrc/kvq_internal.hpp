@@ -42,6 +42,20 @@ struct DecodeArgs {
   int32_t nsplit;            // partitions of the longest sequence
   float sm_log2;             // sm_scale * log2(e)
   int32_t in_bf16;
+  // High-precision windows (zero for plain decode): the INT4 pass skips the
+  // first skip_first and the last skip_last tokens of each sequence; the bf16
+  // window pass attends at most len_cap tokens.
+  int32_t skip_first;
+  int32_t skip_last;
+  int32_t len_cap;
+  // Partials of (sequence b, query head h, split s) go to slot
+  // (b * hq + h) * part_stride + part_slot0 + s; force_partial stores them
+  // even with one split.  window_slot: the slot the reduce reads the window
+  // pass from (-1 = none).
+  int32_t part_stride;
+  int32_t part_slot0;
+  int32_t force_partial;
+  int32_t window_slot;
 };
 
 // Split-K plan shared by the launch and the workspace query.

@@ -1,5 +1,6 @@
 // Split-K merge: for each (sequence, query head) combine the partials (max,
-// sum, unnormalised output) of its splits with the log-sum-exp rule and
+// sum, unnormalised output) of its splits, and of the bf16 window pass when
+// high-precision windows are in use, with the log-sum-exp rule and
 // normalise.  The decode kernels store each partial already rotated back to
 // the original basis (the rotation is linear and the merge is a weighted
 // sum), so nothing is rotated here.
@@ -28,19 +29,30 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
 
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-  const int npg = (len + kPage - 1) / kPage;
-  const int nsp = (npg + a.split_pages - 1) / a.split_pages;   // splits that hold pages
-  const float* ml = a.part_ml + bh * a.nsplit * 2;
-  const float* pa = a.part_acc + bh * a.nsplit * D + kC * n;
+  // the INT4 splits that held pages of this sequence, and the window pass
+  int lo, hi;
+  int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
+  const int npg = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
+  const int win_len = a.len_cap < len ? a.len_cap : len;
+  auto valid = [&](int slot) {
+    if (slot == a.window_slot) return win_len > 0;
+    const int q0 = max(slot * a.split_pages, pfirst);
+    return hi > lo && q0 < min(npg, (slot + 1) * a.split_pages);
+  };
+  const float* ml = a.part_ml + bh * a.part_stride * 2;
+  const float* pa = a.part_acc + bh * a.part_stride * D + kC * n;
 
   float mstar = -__builtin_inff();
-  for (int s = 0; s < nsp; ++s) mstar = fmaxf(mstar, ml[2 * s]);
+  for (int s = 0; s < a.part_stride; ++s)
+    if (valid(s)) mstar = fmaxf(mstar, ml[2 * s]);
+  const float muse = mstar == -__builtin_inff() ? 0.0f : mstar;
   float lsum = 0.0f;
   float o[kC];
 #pragma unroll
   for (int k = 0; k < kC; ++k) o[k] = 0.0f;
-  for (int s = 0; s < nsp; ++s) {
-    const float w = exp2f(ml[2 * s] - mstar);
+  for (int s = 0; s < a.part_stride; ++s) {
+    if (!valid(s)) continue;
+    const float w = exp2f(ml[2 * s] - muse);
     lsum = __builtin_fmaf(ml[2 * s + 1], w, lsum);
 #pragma unroll
     for (int k = 0; k < kC; k += 4) {

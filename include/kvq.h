@@ -162,6 +162,47 @@ kvq_status kvq_decode_attn(const kvq_int4_cache* cache, const void* q, kvq_dtype
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_seq_len, int32_t num_splits);
 
+/*
+ * kvq_decode_attn_windowed -- kvq_decode_attn with high-precision windows
+ * ("InnerQ", Abstract and Figure 2: a small window of sink tokens and of
+ * recent tokens is kept in high precision next to the quantized cache; the
+ * two parts of the attention output are computed separately and merged).
+ *
+ * For a sequence of L tokens the first w_sink and the last w_recent tokens
+ * are read from `window`, a bf16 pool holding unrotated copies of them, and
+ * attended with the unrotated query; the tokens in between are read from the
+ * INT4 cache as in kvq_decode_attn.  The result is the one softmax over all
+ * L tokens (the INT4 share rotated back), obtained by the log-sum-exp merge
+ * of the INT4 split partials and the window pass.
+ *
+ * Window layout: window position of token t is t when t < w_sink, else
+ * w_sink + (t - w_sink) mod w_recent (a ring of the recent tokens: a new
+ * token overwrites the one leaving the window); position i lives in page
+ * window_table[b * max_window_pages + i / 16] at offset i % 16 of `window`.
+ * The caller writes the window with kvq_append_paged_bf16 (and every token,
+ * windowed or not, with kvq_append_paged).  Only the positions
+ * [0, min(L, w_sink + w_recent)) are read.
+ *
+ * window_table: device int32 [batch][max_window_pages], max_window_pages*16
+ *               >= w_sink + w_recent (may be null when both are 0).
+ * w_sink, w_recent: >= 0.
+ * workspace:    at least kvq_decode_windowed_workspace_bytes(...) (never 0).
+ * Other arguments as kvq_decode_attn; the window pool must have the cache's
+ * num_kv_heads and head_dim.
+ */
+kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_cache* window,
+                                    const void* q, kvq_dtype dtype, int32_t num_q_heads,
+                                    const int32_t* block_table, int32_t max_pages_per_seq,
+                                    const int32_t* window_table, int32_t max_window_pages,
+                                    const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                    int32_t w_sink, int32_t w_recent, float sm_scale,
+                                    int32_t num_splits, float* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kvq_decode_attn_windowed needs (always > 0 for batch > 0). */
+size_t kvq_decode_windowed_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t max_seq_len, int32_t num_splits);
+
 /* bf16 baseline of kvq_append_paged: copies K and V (fp16 input is rounded
  * to bf16, nearest even) into the bf16 pool.  Same argument rules. */
 kvq_status kvq_append_paged_bf16(const kvq_bf16_cache* cache, const void* k, const void* v,

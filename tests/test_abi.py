@@ -22,7 +22,7 @@ def _header_functions():
 
 def test_exports_every_declared_symbol():
     names = _header_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     assert sorted(kvq.EXPORTED) == names
     L = kvq.lib()
     for name in names:
@@ -146,3 +146,34 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kvq, "_lib_handle", None)
     with pytest.raises(RuntimeError, match="libkvq.so not found"):
         kvq.kvq_int4_page_bytes(16, 8, 128)
+
+
+def _windowed(desc, win, ws_bytes=0, w_sink=4, w_recent=12, wmaxp=1, maxlen=4096, wt=FAKE):
+    L = kvq.lib()
+    return L.kvq_decode_attn_windowed(C.byref(desc), C.byref(win), FAKE, kvq.KVQ_BF16, 8, FAKE, 256, wt,
+                                      wmaxp, FAKE, 4, maxlen, w_sink, w_recent, 0.125, 0, FAKE, FAKE,
+                                      ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"w_sink": -1}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    ({"w_recent": -3}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    ({"wmaxp": 0}, kvq.KVQ_ERR_INVALID_ARGUMENT),        # 0 pages < 16 window tokens
+    ({"wt": 0}, kvq.KVQ_ERR_INVALID_ARGUMENT),
+    ({"ws_bytes": 0}, kvq.KVQ_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_windowed_decode_validation(kw, status):
+    assert _windowed(_int4(), kvq._Bf16Desc(FAKE, 4, 16, 2, 64), **kw) == status
+
+
+def test_windowed_decode_rejects_mismatched_window_pool():
+    assert _windowed(_int4(), kvq._Bf16Desc(FAKE, 4, 16, 4, 64)) == kvq.KVQ_ERR_INVALID_ARGUMENT
+    assert _windowed(_int4(), kvq._Bf16Desc(FAKE, 4, 16, 2, 128)) == kvq.KVQ_ERR_INVALID_ARGUMENT
+
+
+def test_windowed_workspace_has_a_slot_for_the_window():
+    for maxlen in (16, 4096, 131072):
+        plain = kvq.kvq_decode_workspace_bytes(4, 8, 2, 64, maxlen, 0)
+        win = kvq.kvq_decode_windowed_workspace_bytes(4, 8, 2, 64, maxlen, 0)
+        row = 4 * 8 * (64 + 2) * 4
+        assert win == max(plain, row) + row if plain else win == 2 * row

@@ -367,3 +367,96 @@ def test_concurrency_full_size_sampled():
     want = oracle.decode_int4(pool, step.hkv, step.d, 64, bits(step.q), oracle.BF16,
                               step.block_table, step.seq_lens, step.sm_scale, mask=mask)
     assert_close(out.cpu().numpy().astype(np.float64)[sample], want[sample], "concurrency sampled")
+
+
+# ---------------------------------------------------------------- high-precision windows
+
+def _gpu_window(w, w_sink, w_recent, seed=21, final_len=None):
+    """bf16 window pools (GPU and oracle) holding each sequence's window
+    tokens at final_len (default: the workload's lengths)."""
+    rng = np.random.default_rng(seed)
+    wbt, npages = workloads.window_layout(w.batch, w_sink, w_recent, rng)
+    flen = w.seq_lens if final_len is None else np.asarray(final_len)
+    slots = workloads.window_slots(wbt, w.token_seq, w.token_pos, flen, w_sink, w_recent)
+    win = kvq.Bf16Cache(npages, w.hkv, w.d, DEV)
+    kvq.kvq_append_paged_bf16(win, w.k.to(DEV), w.v.to(DEV), torch.from_numpy(slots).to(DEV))
+    pool = oracle.new_bf16_pool(npages, w.hkv, w.d)
+    oracle.append_bf16(pool, npages, w.hkv, w.d, bits(w.k), bits(w.v), _odt(w.k), slots)
+    return win, pool, wbt
+
+
+def _windowed(cache, win, w, wbt, w_sink, w_recent, num_splits=0):
+    out = kvq.kvq_decode_attn_windowed(cache, win, w.q.to(DEV), torch.from_numpy(w.block_table).to(DEV),
+                                       torch.from_numpy(wbt).to(DEV), torch.from_numpy(w.seq_lens).to(DEV),
+                                       w.max_seq_len, w_sink, w_recent, w.sm_scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("w_sink,w_recent", [(4, 12), (0, 20), (7, 0), (0, 0)])
+def test_windowed_decode_tiny(w_sink, w_recent):
+    w = workloads.tiny_decode(1, block=64)
+    cache = gpu_int4_cache(w, 64)
+    pool = oracle_int4_pool(w, 64)
+    win, wpool, wbt = _gpu_window(w, w_sink, w_recent)
+    want = oracle.decode_windowed(pool, wpool, w.hkv, w.d, 64, bits(w.q), oracle.F16, w.block_table, wbt,
+                                  w.seq_lens, w_sink, w_recent, w.sm_scale)
+    for splits in (0, 1, 3):
+        assert_close(_windowed(cache, win, w, wbt, w_sink, w_recent, splits), want,
+                     f"windowed tiny {w_sink}/{w_recent} S{splits}")
+
+
+def test_windowed_decode_llama_shape():
+    """Sink 4 + recent 124 tokens (128 in all, as in InnerQ Figure 5) over
+    4096-token contexts, Hadamard block 64."""
+    w = workloads.llama8b_decode(2, batch=3, context=4096, block=64)
+    cache = gpu_int4_cache(w, 64)
+    pool = oracle_int4_pool(w, 64)
+    win, wpool, wbt = _gpu_window(w, 4, 124)
+    want = oracle.decode_windowed(pool, wpool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table, wbt,
+                                  w.seq_lens, 4, 124, w.sm_scale)
+    assert_close(_windowed(cache, win, w, wbt, 4, 124), want, "windowed llama")
+
+
+@pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float16)])
+def test_windowed_decode_edge_lengths(d, dtype):
+    lens = [0, 1, 3, 4, 5, 16, 100, 128, 129, 300]
+    w = workloads.random_decode(31, batch=len(lens), hq=8, hkv=2, d=d, block=d // 2, dtype=dtype,
+                                seq_lens=lens)
+    cache = gpu_int4_cache(w, w.block)
+    pool = oracle_int4_pool(w, w.block)
+    win, wpool, wbt = _gpu_window(w, 4, 124)
+    want = oracle.decode_windowed(pool, wpool, w.hkv, w.d, w.block, bits(w.q), _odt(w.q), w.block_table,
+                                  wbt, w.seq_lens, 4, 124, w.sm_scale)
+    for splits in (0, 1, 2, 5):
+        got = _windowed(cache, win, w, wbt, 4, 124, splits)
+        assert not got[0].any()                      # empty sequence -> zeros
+        assert_close(got, want, f"windowed edges d{d} S{splits}")
+
+
+def test_windowed_decode_ring_after_steps():
+    """70B-shaped layer: fill, then decode steps that append one token per
+    sequence to the INT4 cache and to the window ring, which overwrites the
+    token leaving the window."""
+    w_sink, w_recent = 4, 60
+    fill, steps = workloads.concurrency_step(5, batch=6, block=64, steps=20, cap=2048)
+    last = steps[-1]
+    cache = gpu_int4_cache(fill, 64)
+    rng = np.random.default_rng(22)
+    wbt, npages = workloads.window_layout(fill.batch, w_sink, w_recent, rng)
+    win = kvq.Bf16Cache(npages, fill.hkv, fill.d, DEV)
+    wpool = oracle.new_bf16_pool(npages, fill.hkv, fill.d)
+    pool = oracle_int4_pool(fill, 64)
+    slots = workloads.window_slots(wbt, fill.token_seq, fill.token_pos, fill.seq_lens, w_sink, w_recent)
+    kvq.kvq_append_paged_bf16(win, fill.k.to(DEV), fill.v.to(DEV), torch.from_numpy(slots).to(DEV))
+    oracle.append_bf16(wpool, npages, fill.hkv, fill.d, bits(fill.k), bits(fill.v), oracle.BF16, slots)
+    for st in steps:
+        kvq.kvq_append_paged(cache, st.k.to(DEV), st.v.to(DEV), st.slot_mapping.to(DEV))
+        oracle.append_int4(pool, st.num_pages, st.hkv, st.d, 64, bits(st.k), bits(st.v), oracle.BF16,
+                           st.slot_mapping.numpy())
+        s = workloads.window_slots(wbt, st.token_seq, st.token_pos, st.seq_lens, w_sink, w_recent)
+        kvq.kvq_append_paged_bf16(win, st.k.to(DEV), st.v.to(DEV), torch.from_numpy(s).to(DEV))
+        oracle.append_bf16(wpool, npages, st.hkv, st.d, bits(st.k), bits(st.v), oracle.BF16, s)
+    want = oracle.decode_windowed(pool, wpool, last.hkv, last.d, 64, bits(last.q), oracle.BF16,
+                                  last.block_table, wbt, last.seq_lens, w_sink, w_recent, last.sm_scale)
+    assert_close(_windowed(cache, win, last, wbt, w_sink, w_recent), want, "windowed ring")
