@@ -213,6 +213,53 @@ def prefill_rates(torch, kvq, workloads, blocks=(64, 0), iters=50, chunk=10):
     return res
 
 
+def windowed_bytes(seq_lens, hkv, hq, d, w_total, page=16) -> int:
+    """Algorithmic bytes of a decode with high-precision windows of w_total
+    tokens: INT4 tokens outside the windows, bf16 tokens inside, the query,
+    the fp32 output, both page tables and seq_lens."""
+    b = len(seq_lens)
+    win = sum(min(int(x), w_total) for x in seq_lens)
+    toks = sum(int(x) for x in seq_lens)
+    pages = sum((int(x) + page - 1) // page for x in seq_lens)
+    wpages = b * ((w_total + page - 1) // page)
+    return ((toks - win) * hkv * 2 * int4_bytes_per_vector(d) + win * hkv * 2 * d * 2
+            + b * hq * d * (2 + 4) + (pages + wpages) * 4 + b * 4)
+
+
+def windowed_rate(torch, kvq, workloads, db, iters, plain_gb_s, plain_bytes, w_sink=4, w_recent=124):
+    """The headline workload decoded with bf16 windows of the first 4 and the
+    last 124 tokens (128 in all, as in InnerQ Figure 5) next to the INT4 cache
+    (Hadamard block 64), decode-only loop over the cache ring."""
+    w = db.w
+    rng = __import__("numpy").random.default_rng(9)
+    wbt, npages = workloads.window_layout(w.batch, w_sink, w_recent, rng)
+    slots = workloads.window_slots(wbt, w.token_seq, w.token_pos, w.seq_lens, w_sink, w_recent)
+    sl_dev = torch.from_numpy(slots).to("cuda")
+    wins = []
+    for _ in range(RING):
+        c = kvq.Bf16Cache(npages, w.hkv, w.d, "cuda")
+        kvq.kvq_append_paged_bf16(c, w.k, w.v, sl_dev)
+        wins.append(c)
+    wbt_dev = torch.from_numpy(wbt).to("cuda")
+    ws = torch.empty(kvq.kvq_decode_windowed_workspace_bytes(w.batch, w.hq, w.hkv, w.d, w.max_seq_len),
+                     dtype=torch.uint8, device="cuda")
+
+    def run(i):
+        kvq.kvq_decode_attn_windowed(db.int4[i % RING], wins[i % RING], db.qs[i % RING], db.bt, wbt_dev,
+                                     db.sl, w.max_seq_len, w_sink, w_recent, w.sm_scale, out=db.out,
+                                     workspace=ws)
+
+    for i in range(10):
+        run(i)
+    ms, _ = _time_events(torch, run, iters)
+    nbytes = windowed_bytes(w.seq_lens, w.hkv, w.hq, w.d, w_sink + w_recent)
+    plain_us = plain_bytes / (plain_gb_s * 1e9) * 1e6
+    del wins
+    return {"w_sink": w_sink, "w_recent": w_recent, "us": round(ms * 1e3, 2), "bytes": nbytes,
+            "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "time_over_int4_block64": round(ms * 1e3 / plain_us, 4)}
+
+
 def long_context_rate(torch, kvq, workloads, iters=30):
     """Qwen3-4B-shaped long-context decode (8 x 131072 tokens, 65536 pages):
     split-K over pages plus the reduce, timed per call on two cache copies,
@@ -446,6 +493,7 @@ def main(argv=None):
         ms, _ = _time_events(torch, db.decode, args.steps)
         variants[f"int4_block{blk}" if blk else "int4_plain"] = dec_bytes / (ms * 1e-3) / 1e9
     db.refill(64)
+    windowed = windowed_rate(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes)
     db.int4 = db.int4[:1]
     torch.cuda.empty_cache()
     db.make_bf16()
@@ -501,6 +549,7 @@ def main(argv=None):
         },
         "decode_variants_gb_s": {k: round(v, 1) for k, v in sorted(variants.items())},
         "rotated_over_plain_decode": round(variants["int4_block64"] / variants["int4_plain"], 4),
+        "windowed_decode": windowed,
         "long_context_decode": long_ctx,
         "concurrency_sweep": conc,
         "bf16_kv": {"gb_s": round(bf16_bytes / (ms_bf16 * 1e-3) / 1e9, 1),
