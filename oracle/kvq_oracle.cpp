@@ -112,6 +112,7 @@ void rotate_f64(const double* x, double* y, int d, int b) {
 }
 
 size_t int4_slab(int p, int d) { return static_cast<size_t>(p) * (d + 8); }
+size_t int8_slab(int p, int d) { return static_cast<size_t>(p) * (2 * d + 8); }
 size_t bf16_slab(int p, int d) { return static_cast<size_t>(2) * p * d * 2; }
 
 /* Byte address helpers of the INT4 slab (layout text in the header). */
@@ -122,6 +123,15 @@ size_t v_code_byte(int p, int d, int t, int c) {
 }
 size_t meta_byte(int p, int d, int kind, int t) {
   return static_cast<size_t>(p) * d + static_cast<size_t>(kind) * 4 * p + static_cast<size_t>(t) * 4;
+}
+/* Byte address helpers of the INT8 slab (layout text in the header). */
+size_t k8_code_byte(int p, int d, int t, int c) { (void)p; return static_cast<size_t>(t) * d + c; }
+size_t v8_code_byte(int p, int d, int t, int c) {
+  int n = c / 8, h = (c % 8) / 4, j = c % 4;
+  return static_cast<size_t>(p) * d + ((static_cast<size_t>(n) * p + t) * 2 + h) * 4 + j;
+}
+size_t meta8_byte(int p, int d, int kind, int t) {
+  return static_cast<size_t>(2) * p * d + static_cast<size_t>(kind) * 4 * p + static_cast<size_t>(t) * 4;
 }
 size_t bf16_elem(int p, int d, int kind, int t, int c) {
   if (kind == 0) return static_cast<size_t>(t) * d + c;
@@ -207,9 +217,16 @@ void kvq_oracle_rotate(const float* x, float* y, int32_t d, int32_t b) {
   for (int i = 0; i < d; ++i) y[i] = a[i];
 }
 
-void kvq_oracle_quantize(const float* y, int32_t d, uint8_t* codes, uint16_t* scale,
-                         uint16_t* zero) {
+}  // extern "C"
+
+namespace {
+
+/* Token-wise asymmetric quantization of one vector to `levels` + 1 codes
+ * 0..levels (15 for INT4, 255 for INT8): the steps of R2, R4 and R5. */
+void quantize_levels(const float* y, int32_t d, int levels, uint8_t* codes, uint16_t* scale,
+                     uint16_t* zero) {
   std::fesetround(FE_TONEAREST);
+  const float top = static_cast<float>(levels);
   float mn = y[0], mx = y[0];
   for (int i = 1; i < d; ++i) {
     if (y[i] < mn) mn = y[i];
@@ -217,7 +234,7 @@ void kvq_oracle_quantize(const float* y, int32_t d, uint8_t* codes, uint16_t* sc
   }
   float zero_f = mn + 0.0f;
   float range = (mx - mn) + 0.0f;
-  float step = range / 15.0f;
+  float step = range / top;
   uint16_t sh = f32_to_f16(step);
   uint16_t zh = f32_to_f16(zero_f);
   float sf = f16_to_f32(sh);
@@ -228,15 +245,30 @@ void kvq_oracle_quantize(const float* y, int32_t d, uint8_t* codes, uint16_t* sc
     float r = diff * inv;
     float c = std::nearbyint(r);
     if (c < 0.0f) c = 0.0f;
-    if (c > 15.0f) c = 15.0f;
+    if (c > top) c = top;
     codes[i] = static_cast<uint8_t>(c);
   }
   *scale = sh;
   *zero = zh;
 }
 
+}  // namespace
+
+extern "C" {
+
+void kvq_oracle_quantize(const float* y, int32_t d, uint8_t* codes, uint16_t* scale,
+                         uint16_t* zero) {
+  quantize_levels(y, d, 15, codes, scale, zero);
+}
+
+void kvq_oracle_quantize_int8(const float* y, int32_t d, uint8_t* codes, uint16_t* scale,
+                              uint16_t* zero) {
+  quantize_levels(y, d, 255, codes, scale, zero);
+}
+
 size_t kvq_oracle_int4_slab_bytes(int32_t page_size, int32_t head_dim) { return int4_slab(page_size, head_dim); }
 size_t kvq_oracle_bf16_slab_bytes(int32_t page_size, int32_t head_dim) { return bf16_slab(page_size, head_dim); }
+size_t kvq_oracle_int8_slab_bytes(int32_t page_size, int32_t head_dim) { return int8_slab(page_size, head_dim); }
 
 int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_size,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
@@ -269,6 +301,40 @@ int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_si
         }
         put_u16(s + meta_byte(p, d, kind, off), sh);
         put_u16(s + meta_byte(p, d, kind, off) + 2, zh);
+      }
+    }
+  }
+  return 0;
+}
+
+int32_t kvq_oracle_append_int8(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                               const uint16_t* k, const uint16_t* v, int32_t dtype,
+                               int64_t token_stride, const int32_t* slot_mapping,
+                               int32_t num_tokens) {
+  const int p = page_size, d = head_dim, hkv = num_kv_heads;
+  if (!valid_block(block, d) || p % 4 != 0 || d % 8 != 0) return 1;
+  const size_t slab = int8_slab(p, d);
+  const int64_t capacity = static_cast<int64_t>(num_pages) * p;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int t = 0; t < num_tokens; ++t) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= capacity) continue;
+    const int page = static_cast<int>(slot / p), off = static_cast<int>(slot % p);
+    std::vector<float> x(d), y(d);
+    std::vector<uint8_t> codes(d);
+    for (int h = 0; h < hkv; ++h) {
+      uint8_t* s = pool + (static_cast<size_t>(page) * hkv + h) * slab;
+      for (int kind = 0; kind < 2; ++kind) {
+        const uint16_t* src = (kind == 0 ? k : v) + t * token_stride + static_cast<int64_t>(h) * d;
+        for (int c = 0; c < d; ++c) x[c] = widen(src[c], dtype);
+        kvq_oracle_rotate(x.data(), y.data(), d, block);
+        uint16_t sh, zh;
+        kvq_oracle_quantize_int8(y.data(), d, codes.data(), &sh, &zh);
+        for (int c = 0; c < d; ++c)
+          s[kind == 0 ? k8_code_byte(p, d, off, c) : v8_code_byte(p, d, off, c)] = codes[c];
+        put_u16(s + meta8_byte(p, d, kind, off), sh);
+        put_u16(s + meta8_byte(p, d, kind, off) + 2, zh);
       }
     }
   }
@@ -320,6 +386,22 @@ double kvq_oracle_int4_read(const uint8_t* pool, int32_t page_size, int32_t num_
          static_cast<double>(f16_to_f32(zh));
 }
 
+double kvq_oracle_int8_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t page, int32_t head, int32_t off,
+                            int32_t kind, int32_t channel, int32_t* code, uint16_t* scale,
+                            uint16_t* zero) {
+  const int p = page_size, d = head_dim;
+  const uint8_t* s = pool + (static_cast<size_t>(page) * num_kv_heads + head) * int8_slab(p, d);
+  int c = s[kind == 0 ? k8_code_byte(p, d, off, channel) : v8_code_byte(p, d, off, channel)];
+  uint16_t sh = get_u16(s + meta8_byte(p, d, kind, off));
+  uint16_t zh = get_u16(s + meta8_byte(p, d, kind, off) + 2);
+  if (code) *code = c;
+  if (scale) *scale = sh;
+  if (zero) *zero = zh;
+  return static_cast<double>(c) * static_cast<double>(f16_to_f32(sh)) +
+         static_cast<double>(f16_to_f32(zh));
+}
+
 double kvq_oracle_bf16_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
                             int32_t head_dim, int32_t page, int32_t head, int32_t off,
                             int32_t kind, int32_t channel) {
@@ -337,6 +419,20 @@ int32_t kvq_oracle_decode_int4(const uint8_t* pool, int32_t page_size, int32_t n
   if (!valid_block(block, head_dim)) return 1;
   auto read = [&](int page, int head, int off, int kind, int c) {
     return kvq_oracle_int4_read(pool, page_size, num_kv_heads, head_dim, page, head, off, kind, c,
+                                nullptr, nullptr, nullptr);
+  };
+  return decode_paged(read, page_size, num_kv_heads, head_dim, block, q, dtype, num_q_heads,
+                      block_table, max_pages_per_seq, seq_lens, batch, sm_scale, mask, out);
+}
+
+int32_t kvq_oracle_decode_int8(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block, const uint16_t* q, int32_t dtype,
+                               int32_t num_q_heads, const int32_t* block_table,
+                               int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                               double sm_scale, const uint8_t* mask, double* out) {
+  if (!valid_block(block, head_dim)) return 1;
+  auto read = [&](int page, int head, int off, int kind, int c) {
+    return kvq_oracle_int8_read(pool, page_size, num_kv_heads, head_dim, page, head, off, kind, c,
                                 nullptr, nullptr, nullptr);
   };
   return decode_paged(read, page_size, num_kv_heads, head_dim, block, q, dtype, num_q_heads,

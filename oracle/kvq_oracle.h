@@ -36,6 +36,10 @@
  *   R5  the signed zero of min and of (max - min) is made +0 by adding +0.0f.
  *   R6  the query is rotated by the same block Hadamard so q.k is preserved;
  *       the attention output is returned in the original (un-rotated) basis.
+ *   R9  INT8 variant ("GPU-Accelerated INT8 Quantization for KV Cache
+ *       Compression in Large Language Models", Abstract, which gives no
+ *       formula): the same token-wise asymmetric quantizer with 8-bit codes,
+ *       codes 0..255, scale = (max - min) / 255, everything else as R2-R5.
  *   R7  softmax scale is a parameter (normally 1/sqrt(head_dim)); grouped
  *       query attention maps query head h to KV head h / (Hq / Hkv); an empty
  *       sequence gives a zero output; slot < 0 means "do not store".
@@ -52,6 +56,14 @@
  *     bytes [P*D, P*D+4P)     K sidecar: token t -> fp16 scale at 4t, fp16 zero
  *                             at 4t+2 (little endian).
  *     bytes [P*D+4P, P*D+8P)  V sidecar, same form.
+ *   INT8 pool (token-wise INT8 variant, reading R9): [num_pages][num_kv_heads]
+ *   [slab], slab = P * (2*D + 8) bytes:
+ *     bytes [0, P*D)          K codes, token-major: byte t*D + c = channel c.
+ *     bytes [P*D, 2*P*D)      V codes: the 4-byte word index (n*P + t)*2 + h
+ *                             (n = 0 .. D/8-1, h = 0, 1) holds channels
+ *                             8n+4h .. 8n+4h+3 of token t, byte j = channel
+ *                             8n+4h+j.
+ *     bytes [2*P*D, +4P)      K sidecar as in the INT4 pool; then V sidecar.
  *   bf16 pool: [num_pages][num_kv_heads][slab], slab = 2 * P * D * 2 bytes:
  *     K: bf16 element index t*D + c (token-major);
  *     V: bf16 element index P*D + ((n*(P/4) + g)*8 + j)*4 + i for channel
@@ -90,14 +102,26 @@ void kvq_oracle_rotate(const float* x, float* y, int32_t d, int32_t b);
 void kvq_oracle_quantize(const float* y, int32_t d, uint8_t* codes,
                          uint16_t* scale, uint16_t* zero);
 
+/* The same with 8-bit codes 0..255 and scale (max - min) / 255 (R9). */
+void kvq_oracle_quantize_int8(const float* y, int32_t d, uint8_t* codes,
+                              uint16_t* scale, uint16_t* zero);
+
 /* ---- cache steps ----------------------------------------------------- */
 size_t kvq_oracle_int4_slab_bytes(int32_t page_size, int32_t head_dim);
 size_t kvq_oracle_bf16_slab_bytes(int32_t page_size, int32_t head_dim);
+size_t kvq_oracle_int8_slab_bytes(int32_t page_size, int32_t head_dim);
 
 /* Rotate + quantize + scatter num_tokens tokens into the INT4 pool.
  * k, v: [num_tokens][token_stride] 16-bit elements of type dtype, the first
  * num_kv_heads*head_dim of each token used as [num_kv_heads][head_dim]. */
 int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                               const uint16_t* k, const uint16_t* v, int32_t dtype,
+                               int64_t token_stride, const int32_t* slot_mapping,
+                               int32_t num_tokens);
+
+/* The same into the INT8 pool (R9). */
+int32_t kvq_oracle_append_int8(uint8_t* pool, int32_t num_pages, int32_t page_size,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
                                const uint16_t* k, const uint16_t* v, int32_t dtype,
                                int64_t token_stride, const int32_t* slot_mapping,
@@ -117,6 +141,10 @@ double kvq_oracle_int4_read(const uint8_t* pool, int32_t page_size, int32_t num_
                             int32_t head_dim, int32_t page, int32_t head, int32_t off,
                             int32_t kind, int32_t channel, int32_t* code,
                             uint16_t* scale, uint16_t* zero);
+double kvq_oracle_int8_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t page, int32_t head, int32_t off,
+                            int32_t kind, int32_t channel, int32_t* code,
+                            uint16_t* scale, uint16_t* zero);
 double kvq_oracle_bf16_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
                             int32_t head_dim, int32_t page, int32_t head, int32_t off,
                             int32_t kind, int32_t channel);
@@ -127,6 +155,14 @@ double kvq_oracle_bf16_read(const uint8_t* pool, int32_t page_size, int32_t num_
  * [batch][num_q_heads][head_dim].  Only the (b, h) pairs with
  * mask == NULL or mask[b*num_q_heads + h] != 0 are computed (others are 0). */
 int32_t kvq_oracle_decode_int4(const uint8_t* pool, int32_t page_size,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                               const uint16_t* q, int32_t dtype, int32_t num_q_heads,
+                               const int32_t* block_table, int32_t max_pages_per_seq,
+                               const int32_t* seq_lens, int32_t batch, double sm_scale,
+                               const uint8_t* mask, double* out);
+
+/* The same over the INT8 pool. */
+int32_t kvq_oracle_decode_int8(const uint8_t* pool, int32_t page_size,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
                                const uint16_t* q, int32_t dtype, int32_t num_q_heads,
                                const int32_t* block_table, int32_t max_pages_per_seq,
