@@ -260,6 +260,50 @@ def windowed_rate(torch, kvq, workloads, db, iters, plain_gb_s, plain_bytes, w_s
             "time_over_int4_block64": round(ms * 1e3 / plain_us, 4)}
 
 
+def int8_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes):
+    """Token-wise INT8 variant (twice the code bytes of INT4) on the headline
+    workload: decode-only loop over two cache copies (Hadamard block 64), and
+    the prefill append of 32768 ragged tokens over two input/cache sets."""
+    w = db.w
+    caches = [kvq.Int8Cache(w.num_pages, w.hkv, w.d, 64, "cuda") for _ in range(2)]
+    for c in caches:
+        kvq.kvq_append_paged_int8(c, w.k, w.v, w.slot_mapping)
+
+    def dec(i):
+        kvq.kvq_decode_attn_int8(caches[i % 2], db.qs[i % RING], db.bt, db.sl, w.max_seq_len,
+                                 w.sm_scale, out=db.out, workspace=db.ws)
+
+    for i in range(10):
+        dec(i)
+    ms, _ = _time_events(torch, dec, iters)
+    nbytes = decode_bytes(w.seq_lens, w.hkv, w.hq, w.d, w.d + 4)   # D codes + fp16 scale, zero
+    res = {"decode": {"us": round(ms * 1e3, 2), "bytes": nbytes,
+                      "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                      "pct_of_peak": round(100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                      "time_over_int4": round(ms * 1e3 / (int4_bytes / (int4_gb_s * 1e9) * 1e6), 4)}}
+    del caches
+    torch.cuda.empty_cache()
+    sets = []
+    for r in range(2):
+        pw = workloads.prefill_append(3 + 10 * r, device="cuda", block=64)
+        sets.append((pw, kvq.Int8Cache(pw.num_pages, pw.hkv, pw.d, 64, "cuda")))
+
+    def app(i):
+        pw, c = sets[i % 2]
+        kvq.kvq_append_paged_int8(c, pw.k, pw.v, pw.slot_mapping)
+
+    for i in range(10):
+        app(i)
+    ms, _ = _time_events(torch, app, iters)
+    pw = sets[0][0]
+    abytes = append_bytes(pw.num_tokens, pw.hkv, pw.d, pw.d + 4)
+    res["prefill_append"] = {"us": round(ms * 1e3, 2), "mtok_s": round(pw.num_tokens / (ms * 1e-3) / 1e6, 1),
+                             "gb_s": round(abytes / (ms * 1e-3) / 1e9, 1), "bytes": abytes}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def long_context_rate(torch, kvq, workloads, iters=30):
     """Qwen3-4B-shaped long-context decode (8 x 131072 tokens, 65536 pages):
     split-K over pages plus the reduce, timed per call on two cache copies,
@@ -494,6 +538,7 @@ def main(argv=None):
         variants[f"int4_block{blk}" if blk else "int4_plain"] = dec_bytes / (ms * 1e-3) / 1e9
     db.refill(64)
     windowed = windowed_rate(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes)
+    int8 = int8_rates(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes)
     db.int4 = db.int4[:1]
     torch.cuda.empty_cache()
     db.make_bf16()
@@ -550,6 +595,7 @@ def main(argv=None):
         "decode_variants_gb_s": {k: round(v, 1) for k, v in sorted(variants.items())},
         "rotated_over_plain_decode": round(variants["int4_block64"] / variants["int4_plain"], 4),
         "windowed_decode": windowed,
+        "int8_kv": int8,
         "long_context_decode": long_ctx,
         "concurrency_sweep": conc,
         "bf16_kv": {"gb_s": round(bf16_bytes / (ms_bf16 * 1e-3) / 1e9, 1),

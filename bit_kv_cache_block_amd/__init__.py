@@ -7,8 +7,9 @@ kernels of libkvq.so.  There is no fallback: if the library is missing, every
 call raises.
 
 Entry points carry the C names: ``kvq_append_paged``, ``kvq_decode_attn``,
-``kvq_append_paged_bf16``, ``kvq_decode_attn_bf16``,
-``kvq_decode_workspace_bytes``, ``kvq_int4_page_bytes``, ``kvq_bf16_page_bytes``.
+``kvq_decode_attn_windowed``, ``kvq_append_paged_int8``, ``kvq_decode_attn_int8``,
+``kvq_append_paged_bf16``, ``kvq_decode_attn_bf16``, the workspace and page
+size queries.
 """
 from __future__ import annotations
 
@@ -27,7 +28,8 @@ PAGE_SIZE = 16
 
 # every symbol include/kvq.h declares
 EXPORTED = (
-    "kvq_int4_page_bytes", "kvq_bf16_page_bytes", "kvq_append_paged", "kvq_decode_attn",
+    "kvq_int4_page_bytes", "kvq_int8_page_bytes", "kvq_bf16_page_bytes",
+    "kvq_append_paged", "kvq_decode_attn", "kvq_append_paged_int8", "kvq_decode_attn_int8",
     "kvq_decode_workspace_bytes", "kvq_append_paged_bf16", "kvq_decode_attn_bf16",
     "kvq_decode_attn_windowed", "kvq_decode_windowed_workspace_bytes",
     "kvq_status_string", "kvq_last_error", "kvq_abi_version",
@@ -40,7 +42,7 @@ class KvqError(RuntimeError):
         self.status = status
 
 
-class _Int4Desc(C.Structure):
+class _QuantDesc(C.Structure):   # kvq_int4_cache and kvq_int8_cache
     _fields_ = [("pool", C.c_void_p), ("num_pages", C.c_int32), ("page_size", C.c_int32),
                 ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("hadamard_block", C.c_int32)]
@@ -66,20 +68,26 @@ def lib() -> C.CDLL:
         p, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
         L.kvq_int4_page_bytes.argtypes = [i32, i32, i32]
         L.kvq_int4_page_bytes.restype = sz
+        L.kvq_int8_page_bytes.argtypes = [i32, i32, i32]
+        L.kvq_int8_page_bytes.restype = sz
         L.kvq_bf16_page_bytes.argtypes = [i32, i32, i32]
         L.kvq_bf16_page_bytes.restype = sz
-        L.kvq_append_paged.argtypes = [C.POINTER(_Int4Desc), p, p, i32, i64, p, i32, p]
+        L.kvq_append_paged.argtypes = [C.POINTER(_QuantDesc), p, p, i32, i64, p, i32, p]
         L.kvq_append_paged.restype = i32
+        L.kvq_append_paged_int8.argtypes = [C.POINTER(_QuantDesc), p, p, i32, i64, p, i32, p]
+        L.kvq_append_paged_int8.restype = i32
         L.kvq_append_paged_bf16.argtypes = [C.POINTER(_Bf16Desc), p, p, i32, i64, p, i32, p]
         L.kvq_append_paged_bf16.restype = i32
         dec = [p, i32, i32, p, i32, p, i32, i32, C.c_float, i32, p, p, sz, p]
-        L.kvq_decode_attn.argtypes = [C.POINTER(_Int4Desc), *dec]
+        L.kvq_decode_attn.argtypes = [C.POINTER(_QuantDesc), *dec]
         L.kvq_decode_attn.restype = i32
+        L.kvq_decode_attn_int8.argtypes = [C.POINTER(_QuantDesc), *dec]
+        L.kvq_decode_attn_int8.restype = i32
         L.kvq_decode_attn_bf16.argtypes = [C.POINTER(_Bf16Desc), *dec]
         L.kvq_decode_attn_bf16.restype = i32
         L.kvq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.kvq_decode_workspace_bytes.restype = sz
-        L.kvq_decode_attn_windowed.argtypes = [C.POINTER(_Int4Desc), C.POINTER(_Bf16Desc), p, i32, i32,
+        L.kvq_decode_attn_windowed.argtypes = [C.POINTER(_QuantDesc), C.POINTER(_Bf16Desc), p, i32, i32,
                                                p, i32, p, i32, p, i32, i32, i32, i32, C.c_float, i32,
                                                p, p, sz, p]
         L.kvq_decode_attn_windowed.restype = i32
@@ -124,27 +132,49 @@ def kvq_int4_page_bytes(page_size: int, num_kv_heads: int, head_dim: int) -> int
     return int(lib().kvq_int4_page_bytes(page_size, num_kv_heads, head_dim))
 
 
+def kvq_int8_page_bytes(page_size: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(lib().kvq_int8_page_bytes(page_size, num_kv_heads, head_dim))
+
+
 def kvq_bf16_page_bytes(page_size: int, num_kv_heads: int, head_dim: int) -> int:
     return int(lib().kvq_bf16_page_bytes(page_size, num_kv_heads, head_dim))
 
 
-class Int4Cache:
-    """Caller-owned INT4 page pool (uint8 tensor [num_pages][page bytes])."""
+class _QuantCache:
+    """Caller-owned quantized page pool (uint8 tensor [num_pages][page bytes])."""
+
+    _page_bytes = None
 
     def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int, hadamard_block: int,
                  device="cuda", page_size: int = PAGE_SIZE, pool: torch.Tensor | None = None):
         self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
         self.hadamard_block, self.page_size = hadamard_block, page_size
-        nbytes = kvq_int4_page_bytes(page_size, num_kv_heads, head_dim)
+        nbytes = type(self)._page_bytes(page_size, num_kv_heads, head_dim)
         if pool is None:
             pool = torch.zeros((num_pages, nbytes), dtype=torch.uint8, device=device)
         if pool.numel() < num_pages * nbytes or pool.dtype != torch.uint8 or not pool.is_contiguous():
             raise ValueError("pool must be a contiguous uint8 tensor of num_pages * page bytes")
         self.pool = pool
 
-    def desc(self) -> _Int4Desc:
-        return _Int4Desc(self.pool.data_ptr(), self.num_pages, self.page_size, self.num_kv_heads,
-                         self.head_dim, self.hadamard_block)
+    def desc(self) -> _QuantDesc:
+        return _QuantDesc(self.pool.data_ptr(), self.num_pages, self.page_size, self.num_kv_heads,
+                          self.head_dim, self.hadamard_block)
+
+
+class Int4Cache(_QuantCache):
+    """INT4 page pool (kvq_int4_cache)."""
+    _page_bytes = staticmethod(kvq_int4_page_bytes)
+
+
+class Int8Cache(_QuantCache):
+    """INT8 page pool (kvq_int8_cache)."""
+    _page_bytes = staticmethod(kvq_int8_page_bytes)
+
+
+def _need(cache, cls):
+    if not isinstance(cache, cls):
+        raise TypeError(f"expected {cls.__name__}, got {type(cache).__name__}")
+    return cache
 
 
 class Bf16Cache:
@@ -188,8 +218,15 @@ def _append(fn, desc, hkv, d, k, v, slot_mapping, stream):
 def kvq_append_paged(cache: Int4Cache, k: torch.Tensor, v: torch.Tensor,
                      slot_mapping: torch.Tensor, stream=None) -> None:
     """Rotate + quantize + scatter new tokens (k, v: [T][Hkv][D] fp16/bf16)."""
-    _append(lib().kvq_append_paged, cache.desc(), cache.num_kv_heads, cache.head_dim, k, v,
-            slot_mapping, stream)
+    _append(lib().kvq_append_paged, _need(cache, Int4Cache).desc(), cache.num_kv_heads,
+            cache.head_dim, k, v, slot_mapping, stream)
+
+
+def kvq_append_paged_int8(cache: Int8Cache, k: torch.Tensor, v: torch.Tensor,
+                          slot_mapping: torch.Tensor, stream=None) -> None:
+    """Rotate + quantize to 8 bits + scatter new tokens into the INT8 pool."""
+    _append(lib().kvq_append_paged_int8, _need(cache, Int8Cache).desc(), cache.num_kv_heads,
+            cache.head_dim, k, v, slot_mapping, stream)
 
 
 def kvq_append_paged_bf16(cache: Bf16Cache, k: torch.Tensor, v: torch.Tensor,
@@ -233,9 +270,19 @@ def kvq_decode_attn(cache: Int4Cache, q: torch.Tensor, block_table: torch.Tensor
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                     num_splits: int = 0, stream=None) -> torch.Tensor:
     """Paged decode attention over the INT4 cache; returns fp32 [B][Hq][D]."""
-    return _decode(lib().kvq_decode_attn, cache.desc(), cache.num_kv_heads, cache.head_dim, q,
-                   block_table, seq_lens, max_seq_len, sm_scale, out, workspace, num_splits,
-                   stream)
+    return _decode(lib().kvq_decode_attn, _need(cache, Int4Cache).desc(), cache.num_kv_heads,
+                   cache.head_dim, q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace,
+                   num_splits, stream)
+
+
+def kvq_decode_attn_int8(cache: Int8Cache, q: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float | None = None,
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         num_splits: int = 0, stream=None) -> torch.Tensor:
+    """Paged decode attention over the INT8 cache; returns fp32 [B][Hq][D]."""
+    return _decode(lib().kvq_decode_attn_int8, _need(cache, Int8Cache).desc(), cache.num_kv_heads,
+                   cache.head_dim, q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace,
+                   num_splits, stream)
 
 
 def kvq_decode_attn_bf16(cache: Bf16Cache, q: torch.Tensor, block_table: torch.Tensor,
@@ -278,7 +325,8 @@ def kvq_decode_attn_windowed(cache: Int4Cache, window: Bf16Cache, q: torch.Tenso
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check(lib().kvq_decode_attn_windowed(
-        C.byref(cache.desc()), C.byref(window.desc()), _ptr(q), _dtype_code(q), hq, _ptr(block_table),
+        C.byref(_need(cache, Int4Cache).desc()), C.byref(window.desc()), _ptr(q), _dtype_code(q), hq,
+        _ptr(block_table),
         int(block_table.shape[1]), _ptr(window_table), int(window_table.shape[1]), _ptr(seq_lens),
         batch, int(max_seq_len), int(w_sink), int(w_recent), float(sm_scale), int(num_splits),
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),

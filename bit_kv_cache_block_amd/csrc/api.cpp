@@ -119,7 +119,15 @@ size_t workspace_bytes(int32_t batch, int32_t hq, int32_t d, const SplitPlan& p)
 
 namespace {
 
-kvq_status launch_decode(bool int4, const void* pool, int32_t num_pages, int32_t hkv, int32_t d,
+enum class Pool { kInt4, kInt8, kBf16 };
+
+kvq_status check_block(int32_t b, int32_t d) {
+  if (!(b == 0 || b == 16 || b == 32 || b == 64 || b == 128) || b > d)
+    return fail(KVQ_ERR_UNSUPPORTED, "hadamard_block %d unsupported for head_dim %d", b, d);
+  return KVQ_OK;
+}
+
+kvq_status launch_decode(Pool kind, const void* pool, int32_t num_pages, int32_t hkv, int32_t d,
                          int32_t block, const void* q, kvq_dtype dtype, int32_t hq,
                          const int32_t* block_table, int32_t max_pages_per_seq,
                          const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
@@ -159,7 +167,9 @@ kvq_status launch_decode(bool int4, const void* pool, int32_t num_pages, int32_t
   a.part_stride = plan.nsplit;
   a.window_slot = -1;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = int4 ? launch_decode_int4(a, s) : launch_decode_bf16(a, s);
+  hipError_t e = kind == Pool::kInt4   ? launch_decode_int4(a, s)
+                 : kind == Pool::kInt8 ? launch_decode_int8(a, s)
+                                       : launch_decode_bf16(a, s);
   if (e == hipSuccess && plan.nsplit > 1) e = launch_reduce(a, s);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;
@@ -182,15 +192,27 @@ size_t kvq_bf16_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head
   return static_cast<size_t>(num_kv_heads) * page_size * head_dim * 4;
 }
 
-kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const void* v,
-                            kvq_dtype dtype, int64_t token_stride, const int32_t* slot_mapping,
-                            int32_t num_tokens, void* stream) {
+size_t kvq_int8_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim) {
+  if (page_size <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  return static_cast<size_t>(num_kv_heads) * page_size * (2 * head_dim + 8);
+}
+
+}  // extern "C"
+
+namespace kvq {
+namespace {
+
+// The quantizing append shared by the INT4 and INT8 pools (same descriptor
+// fields, different code width).
+template <class Cache>
+kvq_status append_quant(const Cache* cache, bool int8, const void* k, const void* v, kvq_dtype dtype,
+                        int64_t token_stride, const int32_t* slot_mapping, int32_t num_tokens,
+                        void* stream) {
   if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
   kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
   if (st != KVQ_OK) return st;
-  const int b = cache->hadamard_block;
-  if (!(b == 0 || b == 16 || b == 32 || b == 64 || b == 128) || b > cache->head_dim)
-    return fail(KVQ_ERR_UNSUPPORTED, "hadamard_block %d unsupported for head_dim %d", b, cache->head_dim);
+  st = check_block(cache->hadamard_block, cache->head_dim);
+  if (st != KVQ_OK) return st;
   st = check_append(cache->pool, k, v, dtype, token_stride, slot_mapping, num_tokens,
                     cache->num_kv_heads, cache->head_dim);
   if (st != KVQ_OK || num_tokens == 0) return st;
@@ -204,11 +226,46 @@ kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const vo
   a.num_pages = cache->num_pages;
   a.num_kv_heads = cache->num_kv_heads;
   a.head_dim = cache->head_dim;
-  a.block = b;
+  a.block = cache->hadamard_block;
   a.in_bf16 = dtype == KVQ_BF16;
-  const hipError_t e = launch_append_int4(a, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = int8 ? launch_append_int8(a, s) : launch_append_int4(a, s);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;
+}
+
+template <class Cache>
+kvq_status decode_quant(const Cache* cache, bool int8, const void* q, kvq_dtype dtype,
+                        int32_t num_q_heads, const int32_t* block_table, int32_t max_pages_per_seq,
+                        const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
+                        int32_t num_splits, float* out, void* workspace,
+                        size_t workspace_bytes_given, void* stream) {
+  if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
+  kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
+  if (st != KVQ_OK) return st;
+  st = check_block(cache->hadamard_block, cache->head_dim);
+  if (st != KVQ_OK) return st;
+  return launch_decode(int8 ? Pool::kInt8 : Pool::kInt4, cache->pool, cache->num_pages,
+                       cache->num_kv_heads, cache->head_dim, cache->hadamard_block, q, dtype,
+                       num_q_heads, block_table, max_pages_per_seq, seq_lens, batch, max_seq_len,
+                       sm_scale, num_splits, out, workspace, workspace_bytes_given, stream);
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" {
+
+kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const void* v,
+                            kvq_dtype dtype, int64_t token_stride, const int32_t* slot_mapping,
+                            int32_t num_tokens, void* stream) {
+  return append_quant(cache, false, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
+}
+
+kvq_status kvq_append_paged_int8(const kvq_int8_cache* cache, const void* k, const void* v,
+                                 kvq_dtype dtype, int64_t token_stride,
+                                 const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
+  return append_quant(cache, true, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
 }
 
 kvq_status kvq_append_paged_bf16(const kvq_bf16_cache* cache, const void* k, const void* v,
@@ -241,16 +298,19 @@ kvq_status kvq_decode_attn(const kvq_int4_cache* cache, const void* q, kvq_dtype
                            int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
                            int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
                            void* workspace, size_t workspace_bytes_given, void* stream) {
-  if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
-  kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
-  if (st != KVQ_OK) return st;
-  const int b = cache->hadamard_block;
-  if (!(b == 0 || b == 16 || b == 32 || b == 64 || b == 128) || b > cache->head_dim)
-    return fail(KVQ_ERR_UNSUPPORTED, "hadamard_block %d unsupported for head_dim %d", b, cache->head_dim);
-  return launch_decode(true, cache->pool, cache->num_pages, cache->num_kv_heads, cache->head_dim, b,
-                       q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens, batch,
-                       max_seq_len, sm_scale, num_splits, out, workspace, workspace_bytes_given,
-                       stream);
+  return decode_quant(cache, false, q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                      batch, max_seq_len, sm_scale, num_splits, out, workspace,
+                      workspace_bytes_given, stream);
+}
+
+kvq_status kvq_decode_attn_int8(const kvq_int8_cache* cache, const void* q, kvq_dtype dtype,
+                                int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                                void* workspace, size_t workspace_bytes_given, void* stream) {
+  return decode_quant(cache, true, q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                      batch, max_seq_len, sm_scale, num_splits, out, workspace,
+                      workspace_bytes_given, stream);
 }
 
 kvq_status kvq_decode_attn_bf16(const kvq_bf16_cache* cache, const void* q, kvq_dtype dtype,
@@ -261,7 +321,7 @@ kvq_status kvq_decode_attn_bf16(const kvq_bf16_cache* cache, const void* q, kvq_
   if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
   kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
   if (st != KVQ_OK) return st;
-  return launch_decode(false, cache->pool, cache->num_pages, cache->num_kv_heads, cache->head_dim, 0,
+  return launch_decode(Pool::kBf16, cache->pool, cache->num_pages, cache->num_kv_heads, cache->head_dim, 0,
                        q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens, batch,
                        max_seq_len, sm_scale, num_splits, out, workspace, workspace_bytes_given,
                        stream);
@@ -283,8 +343,8 @@ kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_
   if (window->num_kv_heads != cache->num_kv_heads || window->head_dim != cache->head_dim)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "window pool geometry differs from the INT4 cache");
   const int blk = cache->hadamard_block;
-  if (!(blk == 0 || blk == 16 || blk == 32 || blk == 64 || blk == 128) || blk > cache->head_dim)
-    return fail(KVQ_ERR_UNSUPPORTED, "hadamard_block %d unsupported for head_dim %d", blk, cache->head_dim);
+  st = check_block(blk, cache->head_dim);
+  if (st != KVQ_OK) return st;
   const int32_t hkv = cache->num_kv_heads, d = cache->head_dim, hq = num_q_heads;
   st = check_decode(cache->pool, q, dtype, hq, hkv, block_table, max_pages_per_seq, seq_lens, batch,
                     max_seq_len, sm_scale, num_splits, out);

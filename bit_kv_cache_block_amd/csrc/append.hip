@@ -3,8 +3,10 @@
 // Quantization for Real-World LLM Serving", summary page, Research Findings:
 // token-wise INT4 after a block-diagonal Hadamard rotation, with a fused
 // rotation-quantization kernel writing into the paged KV-cache layout; scale
-// and zero point kept as FP16 as in "InnerQ", Table 3).  Also the bf16-cache
-// baseline copy.
+// and zero point kept as FP16 as in "InnerQ", Table 3).  The same kernel with
+// 8-bit codes (255 levels) writes the INT8 variant ("GPU-Accelerated INT8
+// Quantization for KV Cache Compression in Large Language Models",
+// Abstract).  Also the bf16-cache baseline copy.
 //
 // Bit-exactness: the quantizer's fp32 steps are done one rounding at a time
 // in the order the header of kvq.h states (this file is built with
@@ -49,14 +51,18 @@ __device__ __forceinline__ void widen8(u32x4 w, float* x) {
 // current unit is computed.  Lanes of consecutive tokens write consecutive
 // words of a page slab, so tokens that fill a page in order are stored as
 // contiguous runs.
-template <int D, int BLK, bool BF16>
+template <int D, int BLK, bool BF16, int BITS>
 __global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void append_int4_kernel(AppendArgs a) {
+void append_quant_kernel(AppendArgs a) {
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
   constexpr int kLPV = D / kLaneElems;   // lanes per vector
   constexpr int kTok = 64 / kLPV;        // tokens per unit
   constexpr int kChunks = D / 8;         // 16-byte pieces per row
   constexpr int kRowBytes = 2 * D;
-  constexpr int kSlab = kPage * (D + 8);
+  constexpr int kCodeBytes = D * BITS / 8;             // one vector's codes
+  constexpr int kSlab = kPage * (2 * kCodeBytes + 8);
+  constexpr int kWords = kLaneElems * BITS / 32;       // code words per lane
+  constexpr float kTop = BITS == 4 ? 15.0f : 255.0f;   // largest code
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[kAppendThreads / 64][kTok * kRowBytes];
   uint8_t* lds = lds_all[threadIdx.x >> 6];
   const int lane = threadIdx.x & 63;
@@ -126,21 +132,26 @@ void append_int4_kernel(AppendArgs a) {
   // Codes and sidecar of one unit, written into the slot's page (tokens past
   // the end have slot -1).  A unit is stored one iteration after it is
   // computed, so that the wait for the next rows never waits for fresh stores.
-  struct Pending { uint32_t words[8]; uint32_t meta; int32_t slot; uint32_t h; };
+  struct Pending { uint32_t words[kWords]; uint32_t meta; int32_t slot; uint32_t h; };
   auto store = [&](const Pending& q) {
     if (q.slot < 0 || static_cast<int64_t>(q.slot) >= static_cast<int64_t>(a.num_pages) * kPage) return;
     const int page = q.slot / kPage, off = q.slot % kPage;
     uint8_t* slab = a.pool + (static_cast<int64_t>(page) * hkv + q.h) * kSlab;
-    if (kind == 0) {
-      u32x4* dst = reinterpret_cast<u32x4*>(slab + off * (D / 2) + hf * 32);
-      dst[0] = u32x4{q.words[0], q.words[1], q.words[2], q.words[3]};
-      dst[1] = u32x4{q.words[4], q.words[5], q.words[6], q.words[7]};
-    } else {
-      uint32_t* vw = reinterpret_cast<uint32_t*>(slab + kPage * D / 2);
+    if (kind == 0) {   // K: token-major, the lane's 64 channels contiguous
+      u32x4* dst = reinterpret_cast<u32x4*>(slab + off * kCodeBytes + hf * (kWords * 4));
+#pragma unroll
+      for (int i = 0; i < kWords / 4; ++i)
+        dst[i] = u32x4{q.words[4 * i], q.words[4 * i + 1], q.words[4 * i + 2], q.words[4 * i + 3]};
+    } else if constexpr (BITS == 4) {   // V: word n*P + t = channels 8n..8n+7 of token t
+      uint32_t* vw = reinterpret_cast<uint32_t*>(slab + kPage * kCodeBytes);
 #pragma unroll
       for (int m = 0; m < 8; ++m) vw[(hf * 8 + m) * kPage + off] = q.words[m];
+    } else {           // V: words (n*P + t)*2 + {0, 1} = channels 8n..8n+7 of token t
+      u32x2* vw = reinterpret_cast<u32x2*>(slab + kPage * kCodeBytes);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) vw[(hf * 8 + m) * kPage + off] = u32x2{q.words[2 * m], q.words[2 * m + 1]};
     }
-    if (hf == 0) *reinterpret_cast<uint32_t*>(slab + kPage * D + kind * 4 * kPage + off * 4) = q.meta;
+    if (hf == 0) *reinterpret_cast<uint32_t*>(slab + 2 * kPage * kCodeBytes + kind * 4 * kPage + off * 4) = q.meta;
   };
 
   int32_t slot_nxt = -1;
@@ -226,34 +237,37 @@ void append_int4_kernel(AppendArgs a) {
     // fp16 zero and scale, reciprocal (0 for a zero scale)
     const float zero_f = mn + 0.0f;
     const float range = (mx - mn) + 0.0f;
-    const float step = range / 15.0f;
+    const float step = range / kTop;
     const _Float16 sh = static_cast<_Float16>(step);
     const _Float16 zh = static_cast<_Float16>(zero_f);
     const float sf = static_cast<float>(sh);
     const float zf = static_cast<float>(zh);
     const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
 
-    // codes: (y - zero) * inv, then round-half-even and clamp to [0, 15].
+    // codes: (y - zero) * inv, then round-half-even and clamp to [0, top].
     // Adding 2^23 rounds to an integer in the current (nearest-even) mode for
     // any value in [0, 2^23); the clamp in that biased domain equals clamping
-    // the rounded value; the code is then the low 4 bits of the float.
-    uint32_t words[8];
+    // the rounded value; the code is then the low 4 (8) bits of the float.
+    constexpr int kPer = 32 / BITS;   // codes per word
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      uint32_t c[8];
+    for (int m = 0; m < kWords; ++m) {
+      uint32_t c[kPer];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float d = kExactNorm ? __builtin_fmaf(x[8 * m + i], sb, -zf) : x[8 * m + i] - zf;
+      for (int i = 0; i < kPer; ++i) {
+        const float d = kExactNorm ? __builtin_fmaf(x[kPer * m + i], sb, -zf) : x[kPer * m + i] - zf;
         const float q = d * inv;
-        const float t = __builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388623.0f);
+        const float t = __builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388608.0f + kTop);
         c[i] = f2u(t);
       }
-      words[m] = pack8_nibbles(c);
+      // the unit's results are stored at the start of the next iteration
+      if constexpr (BITS == 4) {
+        pend.words[m] = pack8_nibbles(c);
+      } else {
+        const uint32_t lo = __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u);   // c0.byte0, c1.byte0
+        const uint32_t hi = __builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u);
+        pend.words[m] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      }
     }
-
-    // the unit's results are stored at the start of the next iteration
-#pragma unroll
-    for (int m = 0; m < 8; ++m) pend.words[m] = words[m];
     pend.meta = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
     pend.slot = slot;
@@ -307,28 +321,28 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
   }
 }
 
-template <int D, int BLK>
-hipError_t launch_int4_d(const AppendArgs& a, hipStream_t s) {
+template <int D, int BLK, int BITS>
+hipError_t launch_quant_d(const AppendArgs& a, hipStream_t s) {
   constexpr int kTok = D == 128 ? 32 : 64;
   const int64_t units = (static_cast<int64_t>(a.num_tokens) + kTok - 1) / kTok * a.num_kv_heads * 2;
   const int64_t blocks = (units + kAppendThreads / 64 - 1) / (kAppendThreads / 64);
   const dim3 grid(static_cast<unsigned>(blocks < kResidentBlocks ? blocks : kResidentBlocks));
   if (a.in_bf16)
-    append_int4_kernel<D, BLK, true><<<grid, kAppendThreads, 0, s>>>(a);
+    append_quant_kernel<D, BLK, true, BITS><<<grid, kAppendThreads, 0, s>>>(a);
   else
-    append_int4_kernel<D, BLK, false><<<grid, kAppendThreads, 0, s>>>(a);
+    append_quant_kernel<D, BLK, false, BITS><<<grid, kAppendThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_int4_block(const AppendArgs& a, hipStream_t s) {
+template <int D, int BITS>
+hipError_t launch_quant_block(const AppendArgs& a, hipStream_t s) {
   switch (a.block) {
-    case 0: return launch_int4_d<D, 0>(a, s);
-    case 16: return launch_int4_d<D, 16>(a, s);
-    case 32: return launch_int4_d<D, 32>(a, s);
-    case 64: return launch_int4_d<D, 64>(a, s);
+    case 0: return launch_quant_d<D, 0, BITS>(a, s);
+    case 16: return launch_quant_d<D, 16, BITS>(a, s);
+    case 32: return launch_quant_d<D, 32, BITS>(a, s);
+    case 64: return launch_quant_d<D, 64, BITS>(a, s);
     case 128:
-      if constexpr (D == 128) return launch_int4_d<D, 128>(a, s);
+      if constexpr (D == 128) return launch_quant_d<D, 128, BITS>(a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -338,7 +352,12 @@ hipError_t launch_int4_block(const AppendArgs& a, hipStream_t s) {
 
 hipError_t launch_append_int4(const AppendArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  return a.head_dim == 128 ? launch_int4_block<128>(a, s) : launch_int4_block<64>(a, s);
+  return a.head_dim == 128 ? launch_quant_block<128, 4>(a, s) : launch_quant_block<64, 4>(a, s);
+}
+
+hipError_t launch_append_int8(const AppendArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  return a.head_dim == 128 ? launch_quant_block<128, 8>(a, s) : launch_quant_block<64, 8>(a, s);
 }
 
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s) {

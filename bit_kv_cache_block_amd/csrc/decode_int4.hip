@@ -24,6 +24,11 @@
 // The four waves merge in LDS.  With one split each wave finishes heads of the
 // group (normalise, rotate back, store); otherwise it stores a partial (max,
 // sum, unnormalised output) for the reduce kernel.
+//
+// The same kernel reads the token-wise INT8 variant ("GPU-Accelerated INT8
+// Quantization for KV Cache Compression in Large Language Models",
+// Abstract): codes 0..255 enter the int8 MFMA as code - 128 (one xor per
+// byte) and the 128 * scale they lose is added to the zero point.
 #include "dev_common.hpp"
 #include "kvq_internal.hpp"
 
@@ -80,10 +85,12 @@ __device__ __forceinline__ int32_t row_sum16_i(int32_t x) {
   return static_cast<int32_t>(u + dpp_u<kDppRowMirror>(u));
 }
 
-// channel of k-slot (dword i, byte k) of the QK operand `op` for lane group g
-template <int D>
+// channel of k-slot (dword i, byte k) of the QK operand `op` for lane group g:
+// 4-bit codes split into low and high nibbles, 8-bit codes in byte order
+template <int D, int BITS>
 __device__ __forceinline__ int qk_channel(int g, int op, int i, int k) {
-  if constexpr (D == 128) return 32 * g + 8 * i + 2 * k + op;
+  if constexpr (BITS == 8) return (D / 4) * g + 16 * op + 4 * i + k;
+  else if constexpr (D == 128) return 32 * g + 8 * i + 2 * k + op;
   else return 16 * g + 8 * (i & 1) + 2 * k + (i >> 1);
 }
 
@@ -109,18 +116,25 @@ struct alignas(16) Smem {
   uint32_t wl[kWaves][NS][kQuads][4][4][16];   // [wave][set][quad][limb][head][token] = 4 pages' bytes
 };
 
-// one step's loads: four pages of one KV head
+// one step's loads: four pages of one KV head, KX (VX) 16-byte pieces of
+// K (V) codes per lane and page
+template <int KX, int VX>
 struct StepBuf {
-  u32x4 kx[kStep];
-  u32x4 vx[kStep];
+  u32x4 kx[kStep][KX];
+  u32x4 vx[kStep][VX];
   uint32_t km[kStep], vm[kStep];
   bool pv[kStep];
   bool all_ok;
 };
 
-template <int D, int NS, bool QBF16>
-__global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) {
-  constexpr int kSlab = kPage * (D + 8);
+template <int D, int NS, bool QBF16, int BITS>
+__global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a) {
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
+  constexpr int kCodeBytes = D * BITS / 8;           // one vector's codes
+  constexpr int kSlab = kPage * (2 * kCodeBytes + 8);
+  constexpr int kKX = BITS == 8 && D == 128 ? 2 : 1;  // 16-byte K pieces per lane and page
+  constexpr int kVX = BITS == 8 ? 2 : 1;              // 16-byte V pieces per lane and page
+  using Buf = StepBuf<kKX, kVX>;
   constexpr int kNT = D / 16;          // PV tiles = output channels per lane
   constexpr int kOps = D / 64;         // QK MFMAs per page and head group
   constexpr int kGP = 4 * NS;          // padded heads per KV head
@@ -206,10 +220,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kSlab;
   const int vn = n & (D / 8 - 1);
   // lane offsets within a page slab, unsigned so that each load is a uniform
-  // 64-bit base plus a 32-bit lane offset
-  const uint32_t k_off = (D == 128) ? n * (D / 2) + g * 16 : n * (D / 2) + g * 8;
-  const uint32_t v_off = kPage * D / 2 + (vn * kPage + 4 * g) * 4;
-  const uint32_t km_off = kPage * D + 4 * n;
+  // 64-bit base plus a 32-bit lane offset: lane (g, n) reads K codes of token
+  // n (channels [D/4 g, D/4 (g+1))) and V codes of tokens 4g..4g+3 (channel
+  // group vn)
+  const uint32_t k_off = n * kCodeBytes + g * (kCodeBytes / 4);
+  const uint32_t v_off = kPage * kCodeBytes + (vn * kPage + 4 * g) * (BITS == 8 ? 8 : 4);
+  const uint32_t km_off = 2 * kPage * kCodeBytes + 4 * n;
   auto load_ids = [&](int first) {
     const int pg = first + lane;
     return pg < pw1 ? bt[pg] : -1;
@@ -223,7 +239,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
     const int rel = pg - cb;
     return rel < 64 ? __builtin_amdgcn_readlane(ids_cur, rel) : __builtin_amdgcn_readlane(ids_next, rel - 64);
   };
-  auto load = [&](StepBuf& sb, int p) {
+  auto load = [&](Buf& sb, int p) {
     sb.all_ok = true;
 #pragma unroll
     for (int i = 0; i < kStep; ++i) {
@@ -235,13 +251,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
       // that base plus the lane's 32-bit offset; nothing can reach past the slab
       const uint8_t* sl = pool_h + static_cast<int64_t>(sb.pv[i] ? id : 0) * page_stride;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, kSlab);
-      if constexpr (D == 128) {
-        sb.kx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, k_off, 0, kStreamOnce));
+      if constexpr (kCodeBytes / 4 >= 16) {
+#pragma unroll
+        for (int j = 0; j < kKX; ++j)
+          sb.kx[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, k_off + 16 * j, 0, kStreamOnce));
       } else {
         const u32x2 t2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, k_off, 0, kStreamOnce));
-        sb.kx[i] = u32x4{t2[0], t2[1], 0u, 0u};
+        sb.kx[i][0] = u32x4{t2[0], t2[1], 0u, 0u};
       }
-      sb.vx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, 0, kStreamOnce));
+#pragma unroll
+      for (int j = 0; j < kVX; ++j)
+        sb.vx[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_off + 16 * j, 0, kStreamOnce));
       sb.km[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off, 0, kStreamOnce);
       sb.vm[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off + 4 * kPage, 0, kStreamOnce);
     }
@@ -259,7 +279,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   // and keep the page loads below this point
 #pragma unroll
   for (int k = 0; k < kC; ++k) asm volatile("" : : "v"(qv[k]) : "memory");
-  StepBuf buf0;
+  Buf buf0;
   if (pw0 < pw1) load(buf0, pw0);
   // ---- query: rotate in registers, fixed point, limbs ------------------------
   for (int e = tid; e < kWaves * NS * kQuads * 4 * 4 * 16; e += 64 * kWaves)
@@ -327,7 +347,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
         uint32_t w = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          w |= limb.byte(qc[qk_channel<D>(0, op, i, k)]) << (8 * k);
+          w |= limb.byte(qc[qk_channel<D, BITS>(0, op, i, k)]) << (8 * k);
         vv[i] = static_cast<int32_t>(w);
       }
       aq[st][op] = vv;
@@ -346,24 +366,32 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   const v4i zero4 = {0, 0, 0, 0};
   const int wl_row = (lam * 4 + hs) * 16 + 4 * g;   // reader offset within a set, dwords
 
-  auto compute = [&](const StepBuf& sb, int p, auto mask_tag) {
+  auto compute = [&](const Buf& sb, int p, auto mask_tag) {
     constexpr bool tail = decltype(mask_tag)::value;
     // QK: lane (g, n) gets the four limb rows of head g (per set), token n
     float lg[NS][kStep];
 #pragma unroll
     for (int i = 0; i < kStep; ++i) {
       v4i b0, b1;
-      if constexpr (D == 128) {
+      if constexpr (BITS == 8) {   // code - 128 as a signed byte
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          b0[w] = static_cast<int32_t>(sb.kx[i][w] & kLowNibbles);
-          b1[w] = static_cast<int32_t>((sb.kx[i][w] >> 4) & kLowNibbles);
+          b0[w] = static_cast<int32_t>(sb.kx[i][0][w] ^ 0x80808080u);
+          if constexpr (kKX == 2) b1[w] = static_cast<int32_t>(sb.kx[i][1][w] ^ 0x80808080u);
+        }
+      } else if constexpr (D == 128) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          b0[w] = static_cast<int32_t>(sb.kx[i][0][w] & kLowNibbles);
+          b1[w] = static_cast<int32_t>((sb.kx[i][0][w] >> 4) & kLowNibbles);
         }
       } else {
-        b0 = v4i{static_cast<int32_t>(sb.kx[i][0] & kLowNibbles), static_cast<int32_t>(sb.kx[i][1] & kLowNibbles),
-                 static_cast<int32_t>((sb.kx[i][0] >> 4) & kLowNibbles),
-                 static_cast<int32_t>((sb.kx[i][1] >> 4) & kLowNibbles)};
+        b0 = v4i{static_cast<int32_t>(sb.kx[i][0][0] & kLowNibbles), static_cast<int32_t>(sb.kx[i][0][1] & kLowNibbles),
+                 static_cast<int32_t>((sb.kx[i][0][0] >> 4) & kLowNibbles),
+                 static_cast<int32_t>((sb.kx[i][0][1] >> 4) & kLowNibbles)};
       }
+      // zero point of the codes as the MFMA sees them
+      const float kzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(sb.km[i]), half_hi(sb.km[i])) : half_hi(sb.km[i]);
       const int tok = (p + i) * kPage + n;
       const bool ok = !tail || (sb.pv[i] && tok >= lo && tok < hi);
 #pragma unroll
@@ -373,7 +401,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
         // limbs: c0 * 2^16 + c1 * 2^8 + c2 (c0 * 2^8 + c1 is exact in int32)
         const float tq = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f,
                                         static_cast<float>(c[2]));
-        const float l2 = qA[st] * __builtin_fmaf(half_hi(sb.km[i]), qS[st], half_lo(sb.km[i]) * tq);
+        const float l2 = qA[st] * __builtin_fmaf(kzero, qS[st], half_lo(sb.km[i]) * tq);
         lg[st][i] = ok ? l2 : kNegInf;
       }
     }
@@ -395,12 +423,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
       for (int i = 0; i < kStep; ++i) {
         const float pp = exp2f(lg[st][i] - muse);
         psum += pp;
+        const float vzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(sb.vm[i]), half_hi(sb.vm[i])) : half_hi(sb.vm[i]);
         if (tail) {
           const bool ok = lg[st][i] != kNegInf;
-          zsum += ok ? pp * half_hi(sb.vm[i]) : 0.0f;
+          zsum += ok ? pp * vzero : 0.0f;
           w[i] = ok ? pp * half_lo(sb.vm[i]) : 0.0f;
         } else {
-          zsum = __builtin_fmaf(pp, half_hi(sb.vm[i]), zsum);
+          zsum = __builtin_fmaf(pp, vzero, zsum);
           w[i] = pp * half_lo(sb.vm[i]);
         }
         wmax = fmaxf(wmax, w[i]);
@@ -443,14 +472,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
         apv[st][qd] = *reinterpret_cast<const v4i*>(&sm.wl[wave][st][qd][0][0][0] + wl_row);
 
     // V: per token r of the lane group, transpose across four pages so a
-    // word holds the four pages' codes of one channel pair; nibbles split it.
-    uint32_t vt[kQuads][4][4];   // [quad][r][byte j]
+    // word holds the four pages' codes of one channel pair (4-bit: nibbles
+    // split it) or of one channel (8-bit, then made signed).
+    uint32_t vt[kQuads][4][kVX][4];   // [quad][r][half][byte j]
 #pragma unroll
     for (int qd = 0; qd < kQuads; ++qd)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        transpose_bytes4(sb.vx[4 * qd][r], sb.vx[4 * qd + 1][r], sb.vx[4 * qd + 2][r], sb.vx[4 * qd + 3][r],
-                         vt[qd][r]);
+#pragma unroll
+        for (int hh = 0; hh < kVX; ++hh) {
+          // 4-bit: dword r of the piece is token 4g+r; 8-bit: dwords
+          // 2(r&1)+hh of piece r>>1 are token 4g+r, channels 4hh..4hh+3
+          auto src = [&](int pg) {
+            return BITS == 8 ? sb.vx[4 * qd + pg][r >> 1][2 * (r & 1) + hh] : sb.vx[4 * qd + pg][0][r];
+          };
+          transpose_bytes4(src(0), src(1), src(2), src(3), vt[qd][r][hh]);
+        }
 #pragma unroll
     for (int tau = 0; tau < kNT; ++tau) {
       v4i bv[kQuads];
@@ -459,9 +496,20 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           uint32_t yv;
-          if constexpr (D == 128) yv = (tau & 1) ? (vt[qd][r][tau >> 1] >> 4) : vt[qd][r][tau >> 1];
-          else yv = vt[qd][r][tau] >> (4 * (n >> 3));
-          bv[qd][r] = static_cast<int32_t>(yv & kLowNibbles);
+          if constexpr (BITS == 8) {
+            if constexpr (D == 128) {   // channel 8n + tau
+              yv = vt[qd][r][tau >> 2][tau & 3];
+            } else {                    // channel 8(n&7) + 2tau + (n>>3)
+              const uint32_t* h4 = vt[qd][r][tau >> 1];
+              yv = (n >> 3) ? h4[2 * (tau & 1) + 1] : h4[2 * (tau & 1)];
+            }
+            yv ^= 0x80808080u;
+          } else {
+            if constexpr (D == 128) yv = (tau & 1) ? (vt[qd][r][0][tau >> 1] >> 4) : vt[qd][r][0][tau >> 1];
+            else yv = vt[qd][r][0][tau] >> (4 * (n >> 3));
+            yv &= kLowNibbles;
+          }
+          bv[qd][r] = static_cast<int32_t>(yv);
         }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
@@ -476,7 +524,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   };
 
   // ---- stream the wave's pages ----------------------------------------------
-  auto step = [&](const StepBuf& sb, int p) {
+  auto step = [&](const Buf& sb, int p) {
     if (!sb.all_ok || (p + kStep) * kPage > hi || p * kPage < lo)
       compute(sb, p, std::true_type{});
     else
@@ -564,28 +612,32 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int4_kernel(DecodeArgs a) 
   }
 }
 
-template <int D, int NS>
+template <int D, int NS, int BITS>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.nsplit) * a.num_kv_heads * a.batch);
   if (a.in_bf16)
-    decode_int4_kernel<D, NS, true><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_quant_kernel<D, NS, true, BITS><<<grid, 64 * kWaves, 0, s>>>(a);
   else
-    decode_int4_kernel<D, NS, false><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_quant_kernel<D, NS, false, BITS><<<grid, 64 * kWaves, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int BITS>
 hipError_t launch_ns(const DecodeArgs& a, hipStream_t s) {
   const int g = a.num_q_heads / a.num_kv_heads;
-  if (g <= 4) return launch_d<D, 1>(a, s);
-  if (g <= 8) return launch_d<D, 2>(a, s);
-  return launch_d<D, 4>(a, s);
+  if (g <= 4) return launch_d<D, 1, BITS>(a, s);
+  if (g <= 8) return launch_d<D, 2, BITS>(a, s);
+  return launch_d<D, 4, BITS>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_int4(const DecodeArgs& a, hipStream_t s) {
-  return a.head_dim == 128 ? launch_ns<128>(a, s) : launch_ns<64>(a, s);
+  return a.head_dim == 128 ? launch_ns<128, 4>(a, s) : launch_ns<64, 4>(a, s);
+}
+
+hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t s) {
+  return a.head_dim == 128 ? launch_ns<128, 8>(a, s) : launch_ns<64, 8>(a, s);
 }
 
 }  // namespace kvq

@@ -39,6 +39,14 @@
  *     [P*D + 4P, P*D+8P) V sidecar, same form.
  *   A decoded element is code * scale + zero, in the rotated basis.
  *
+ * INT8 page pool layout (token-wise INT8 variant): [num_pages][num_kv_heads]
+ *   [slab] bytes with slab = P * (2*D + 8) bytes (4224 at D = 128):
+ *     [0, P*D)           K codes, token-major: byte t*D + c = channel c.
+ *     [P*D, 2*P*D)       V codes: 32-bit word (n*P + t)*2 + h (n < D/8,
+ *                        h < 2) holds channels 8n+4h .. 8n+4h+3 of token t,
+ *                        byte j = channel 8n+4h+j.
+ *     [2*P*D, +4P)       K sidecar as in the INT4 pool; then the V sidecar.
+ *
  * bf16 page pool layout: [num_pages][num_kv_heads][slab], slab = 4*P*D bytes:
  *     K: bf16 element t*D + c (token-major);
  *     V: bf16 element P*D + ((n*(P/4) + g)*8 + j)*4 + i for channel c = 8n + j
@@ -83,6 +91,17 @@ typedef struct {
   int32_t hadamard_block;   /* 16, 32, 64 or 128 (dividing head_dim); 0 = plain INT4 */
 } kvq_int4_cache;
 
+/* INT8 cache descriptor: the same fields as the INT4 one; `pool` holds
+ * kvq_int8_page_bytes(page_size, num_kv_heads, head_dim) * num_pages bytes. */
+typedef struct {
+  void*   pool;
+  int32_t num_pages;
+  int32_t page_size;        /* must be 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t hadamard_block;   /* 16, 32, 64 or 128 (dividing head_dim); 0 = no rotation */
+} kvq_int8_cache;
+
 /* bf16 cache descriptor (baseline).  `pool` 16-byte aligned,
  * kvq_bf16_page_bytes(...) * num_pages bytes. */
 typedef struct {
@@ -95,6 +114,7 @@ typedef struct {
 
 /* Bytes of one page (all KV heads) of each pool. */
 size_t kvq_int4_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
+size_t kvq_int8_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
 size_t kvq_bf16_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
 
 /*
@@ -202,6 +222,27 @@ kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_
 /* Workspace bytes kvq_decode_attn_windowed needs (always > 0 for batch > 0). */
 size_t kvq_decode_windowed_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t max_seq_len, int32_t num_splits);
+
+/*
+ * Token-wise INT8 variant ("GPU-Accelerated INT8 Quantization for KV Cache
+ * Compression in Large Language Models", Abstract: 8-bit KV codes), twice
+ * the bytes of INT4 per token.  The quantizer is kvq_append_paged's with 255
+ * levels:
+ *   zero = fp16(min y + 0), scale = fp16(((max y - min y) + 0) / 255)
+ *   code_d = clamp(round_half_even((y_d - zero) * (1/scale)), 0, 255)
+ * after the same optional block Hadamard rotation; codes and sidecars are
+ * bit-exact functions of the input.  kvq_decode_attn_int8 is kvq_decode_attn
+ * over the INT8 pool (same arguments, accuracy and workspace size, from
+ * kvq_decode_workspace_bytes).
+ */
+kvq_status kvq_append_paged_int8(const kvq_int8_cache* cache, const void* k, const void* v,
+                                 kvq_dtype dtype, int64_t token_stride,
+                                 const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+kvq_status kvq_decode_attn_int8(const kvq_int8_cache* cache, const void* q, kvq_dtype dtype,
+                                int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* bf16 baseline of kvq_append_paged: copies K and V (fp16 input is rounded
  * to bf16, nearest even) into the bf16 pool.  Same argument rules. */

@@ -22,7 +22,7 @@ def _header_functions():
 
 def test_exports_every_declared_symbol():
     names = _header_functions()
-    assert len(names) == 12
+    assert len(names) == 15
     assert sorted(kvq.EXPORTED) == names
     L = kvq.lib()
     for name in names:
@@ -40,16 +40,18 @@ def test_page_bytes():
     assert kvq.kvq_int4_page_bytes(16, 8, 128) == 8 * 2176
     assert kvq.kvq_int4_page_bytes(16, 2, 64) == 2 * 1152
     assert kvq.kvq_bf16_page_bytes(16, 8, 128) == 8 * 8192
+    assert kvq.kvq_int8_page_bytes(16, 8, 128) == 8 * 4224
+    assert kvq.kvq_int8_page_bytes(16, 2, 64) == 2 * 2176
 
 
 def _int4(num_pages=64, page=16, hkv=2, d=64, block=64, pool=FAKE):
-    return kvq._Int4Desc(pool, num_pages, page, hkv, d, block)
+    return kvq._QuantDesc(pool, num_pages, page, hkv, d, block)
 
 
-def _append(desc, k=FAKE, v=FAKE, dtype=kvq.KVQ_BF16, stride=128, slots=FAKE, n=4):
+def _append(desc, k=FAKE, v=FAKE, dtype=kvq.KVQ_BF16, stride=128, slots=FAKE, n=4, fn="kvq_append_paged"):
     L = kvq.lib()
-    return L.kvq_append_paged(C.byref(desc) if desc is not None else None, k, v, dtype, stride,
-                              slots, n, None)
+    return getattr(L, fn)(C.byref(desc) if desc is not None else None, k, v, dtype, stride,
+                          slots, n, None)
 
 
 @pytest.mark.parametrize("desc,kw,status", [
@@ -70,22 +72,24 @@ def _append(desc, k=FAKE, v=FAKE, dtype=kvq.KVQ_BF16, stride=128, slots=FAKE, n=
     (_int4(), {"dtype": 7}, kvq.KVQ_ERR_INVALID_ARGUMENT),
     (_int4(), {"n": -1}, kvq.KVQ_ERR_INVALID_ARGUMENT),
 ])
-def test_append_validation(desc, kw, status):
-    assert _append(desc, **kw) == status
+@pytest.mark.parametrize("fn", ["kvq_append_paged", "kvq_append_paged_int8"])
+def test_append_validation(desc, kw, status, fn):
+    assert _append(desc, fn=fn, **kw) == status
     assert kvq.lib().kvq_last_error() != b""
 
 
 def test_append_zero_tokens_is_a_noop():
     assert _append(_int4(), k=0, v=0, slots=0, n=0) == kvq.KVQ_OK
+    assert _append(_int4(), k=0, v=0, slots=0, n=0, fn="kvq_append_paged_int8") == kvq.KVQ_OK
 
 
 def _decode(desc, q=FAKE, dtype=kvq.KVQ_BF16, hq=8, bt=FAKE, maxp=256, sl=FAKE, batch=4,
-            maxlen=4096, sm=0.125, splits=0, out=FAKE, ws=FAKE, wsb=0):
+            maxlen=4096, sm=0.125, splits=0, out=FAKE, ws=FAKE, wsb=0, fn="kvq_decode_attn"):
     # the defaults need a split-K workspace (4 x 4096 tokens over 2 KV heads),
     # so with wsb = 0 every call here is rejected before anything is launched
     L = kvq.lib()
-    return L.kvq_decode_attn(C.byref(desc), q, dtype, hq, bt, maxp, sl, batch, maxlen, sm, splits,
-                             out, ws, wsb, None)
+    return getattr(L, fn)(C.byref(desc), q, dtype, hq, bt, maxp, sl, batch, maxlen, sm, splits,
+                          out, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -100,14 +104,33 @@ def _decode(desc, q=FAKE, dtype=kvq.KVQ_BF16, hq=8, bt=FAKE, maxp=256, sl=FAKE, 
     ({"splits": -2}, kvq.KVQ_ERR_INVALID_ARGUMENT),
     ({"wsb": 0}, kvq.KVQ_ERR_WORKSPACE_TOO_SMALL),
 ])
-def test_decode_validation(kw, status):
-    assert _decode(_int4(), **kw) == status
+@pytest.mark.parametrize("fn", ["kvq_decode_attn", "kvq_decode_attn_int8"])
+def test_decode_validation(kw, status, fn):
+    assert _decode(_int4(), fn=fn, **kw) == status
+
+
+@pytest.mark.parametrize("fn", ["kvq_decode_attn", "kvq_decode_attn_int8"])
+def test_decode_rejects_bad_block(fn):
+    assert _decode(_int4(block=8), fn=fn, wsb=1 << 30) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _decode(_int4(d=96), fn=fn, wsb=1 << 30) == kvq.KVQ_ERR_UNSUPPORTED
 
 
 def test_decode_workspace_too_small_by_one():
     need = kvq.kvq_decode_workspace_bytes(4, 8, 2, 64, 4096, 0)
     assert need > 0
     assert _decode(_int4(), wsb=need - 1) == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
+    assert _decode(_int4(), wsb=need - 1, fn="kvq_decode_attn_int8") == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_binding_keeps_int4_and_int8_pools_apart():
+    c8 = kvq.Int8Cache(2, 2, 64, 64, device="cpu")
+    c4 = kvq.Int4Cache(2, 2, 64, 64, device="cpu")
+    assert c8.pool.shape[1] == kvq.kvq_int8_page_bytes(16, 2, 64)
+    assert c4.pool.shape[1] == kvq.kvq_int4_page_bytes(16, 2, 64)
+    with pytest.raises(TypeError):
+        kvq.kvq_append_paged(c8, None, None, None)
+    with pytest.raises(TypeError):
+        kvq.kvq_decode_attn_int8(c4, None, None, None, 0)
 
 
 def test_decode_zero_batch_is_a_noop():
