@@ -79,6 +79,17 @@ def _declare(L):
     L.kvq_oracle_decode_int8.argtypes = [_p, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p, _i32, _p,
                                          _i32, C.c_double, _p, _p]
     L.kvq_oracle_decode_int8.restype = _i32
+    L.kvq_oracle_int4g_slab_bytes.argtypes = [_i32, _i32, _i32]
+    L.kvq_oracle_int4g_slab_bytes.restype = C.c_size_t
+    L.kvq_oracle_append_int4g.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _i32, _i64,
+                                          _p, _i32]
+    L.kvq_oracle_append_int4g.restype = _i32
+    L.kvq_oracle_int4g_read.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        _p, _p, _p]
+    L.kvq_oracle_int4g_read.restype = C.c_double
+    L.kvq_oracle_decode_int4g.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p, _i32,
+                                          _p, _i32, C.c_double, _p, _p]
+    L.kvq_oracle_decode_int4g.restype = _i32
     L.kvq_oracle_int4_slab_bytes.argtypes = [_i32, _i32]
     L.kvq_oracle_int4_slab_bytes.restype = C.c_size_t
     L.kvq_oracle_bf16_slab_bytes.argtypes = [_i32, _i32]
@@ -167,6 +178,15 @@ def int8_slab_bytes(page_size: int, head_dim: int) -> int:
     return int(lib().kvq_oracle_int8_slab_bytes(page_size, head_dim))
 
 
+def int4g_slab_bytes(page_size: int, head_dim: int, group: int) -> int:
+    return int(lib().kvq_oracle_int4g_slab_bytes(page_size, head_dim, group))
+
+
+def new_int4g_pool(num_pages, num_kv_heads, head_dim, group, page_size=16, fill=0):
+    n = num_pages * num_kv_heads * int4g_slab_bytes(page_size, head_dim, group)
+    return np.full(n, fill, np.uint8)
+
+
 def bf16_slab_bytes(page_size: int, head_dim: int) -> int:
     return int(lib().kvq_oracle_bf16_slab_bytes(page_size, head_dim))
 
@@ -219,6 +239,22 @@ def append_int8(pool, num_pages, num_kv_heads, head_dim, block, k, v, dtype, slo
     return pool
 
 
+def append_int4g(pool, num_pages, num_kv_heads, head_dim, block, group, k, v, dtype,
+                 slot_mapping, page_size=16, token_stride=None):
+    """Per-group INT4 into the grouped pool."""
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    sm = _c(slot_mapping, np.int32)
+    if token_stride is None:
+        token_stride = num_kv_heads * head_dim
+    rc = lib().kvq_oracle_append_int4g(_ptr(pool), num_pages, page_size, num_kv_heads, head_dim,
+                                       int(block), int(group), _ptr(k), _ptr(v),
+                                       int(dtype), int(token_stride), _ptr(sm), sm.shape[0])
+    if rc != 0:
+        raise ValueError("oracle append_int4g rejected its arguments")
+    return pool
+
+
 def append_bf16(pool, num_pages, num_kv_heads, head_dim, k, v, dtype, slot_mapping,
                 page_size=16, token_stride=None):
     k = _c(k, np.uint16)
@@ -249,6 +285,15 @@ def int8_read(pool, num_kv_heads, head_dim, page, head, off, kind, channel, page
     z = np.zeros(1, np.uint16)
     val = lib().kvq_oracle_int8_read(_ptr(pool), page_size, num_kv_heads, head_dim, page, head,
                                      off, kind, channel, _ptr(code), _ptr(s), _ptr(z))
+    return float(val), int(code[0]), int(s[0]), int(z[0])
+
+
+def int4g_read(pool, num_kv_heads, head_dim, group, page, head, off, kind, channel, page_size=16):
+    code = np.zeros(1, np.int32)
+    s = np.zeros(1, np.uint16)
+    z = np.zeros(1, np.uint16)
+    val = lib().kvq_oracle_int4g_read(_ptr(pool), page_size, num_kv_heads, head_dim, group, page,
+                                      head, off, kind, channel, _ptr(code), _ptr(s), _ptr(z))
     return float(val), int(code[0]), int(s[0]), int(z[0])
 
 
@@ -288,6 +333,23 @@ def decode_int8(pool, num_kv_heads, head_dim, block, q, dtype, block_table, seq_
                                       _ptr(out))
     if rc != 0:
         raise ValueError("oracle decode_int8 rejected its arguments")
+    return out
+
+
+def decode_int4g(pool, num_kv_heads, head_dim, block, group, q, dtype, block_table, seq_lens,
+                 sm_scale, page_size=16, mask=None):
+    q = _c(q, np.uint16)
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    batch, hq, d = q.shape
+    out = np.zeros((batch, hq, d), np.float64)
+    mk = None if mask is None else _c(mask, np.uint8)
+    rc = lib().kvq_oracle_decode_int4g(_ptr(pool), page_size, num_kv_heads, head_dim, int(block),
+                                       int(group), _ptr(q), int(dtype), hq, _ptr(bt), bt.shape[1],
+                                       _ptr(sl), batch, float(sm_scale),
+                                       None if mk is None else _ptr(mk), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle decode_int4g rejected its arguments")
     return out
 
 

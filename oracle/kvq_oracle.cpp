@@ -124,6 +124,18 @@ size_t v_code_byte(int p, int d, int t, int c) {
 size_t meta_byte(int p, int d, int kind, int t) {
   return static_cast<size_t>(p) * d + static_cast<size_t>(kind) * 4 * p + static_cast<size_t>(t) * 4;
 }
+/* Byte address helpers of the grouped INT4 slab (layout text in the header). */
+size_t int4g_slab(int p, int d, int group) { return static_cast<size_t>(p) * (d + 8 * (d / group)); }
+size_t vg_code_byte(int p, int d, int t, int c) {
+  int n = c % (d / 8), j = c / (d / 8);  /* word n*P + t, nibble j */
+  return static_cast<size_t>(p) * d / 2 + (static_cast<size_t>(n) * p + t) * 4 + j / 2;
+}
+size_t metag_byte(int p, int d, int group, int kind, int t, int gi) {
+  const int ng = d / group;
+  return static_cast<size_t>(p) * d + static_cast<size_t>(kind) * 4 * p * ng +
+         (static_cast<size_t>(t) * ng + gi) * 4;
+}
+
 /* Byte address helpers of the INT8 slab (layout text in the header). */
 size_t k8_code_byte(int p, int d, int t, int c) { (void)p; return static_cast<size_t>(t) * d + c; }
 size_t v8_code_byte(int p, int d, int t, int c) {
@@ -269,6 +281,9 @@ void kvq_oracle_quantize_int8(const float* y, int32_t d, uint8_t* codes, uint16_
 size_t kvq_oracle_int4_slab_bytes(int32_t page_size, int32_t head_dim) { return int4_slab(page_size, head_dim); }
 size_t kvq_oracle_bf16_slab_bytes(int32_t page_size, int32_t head_dim) { return bf16_slab(page_size, head_dim); }
 size_t kvq_oracle_int8_slab_bytes(int32_t page_size, int32_t head_dim) { return int8_slab(page_size, head_dim); }
+size_t kvq_oracle_int4g_slab_bytes(int32_t page_size, int32_t head_dim, int32_t group) {
+  return int4g_slab(page_size, head_dim, group);
+}
 
 int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_size,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
@@ -341,6 +356,46 @@ int32_t kvq_oracle_append_int8(uint8_t* pool, int32_t num_pages, int32_t page_si
   return 0;
 }
 
+int32_t kvq_oracle_append_int4g(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                                int32_t group, const uint16_t* k, const uint16_t* v,
+                                int32_t dtype, int64_t token_stride, const int32_t* slot_mapping,
+                                int32_t num_tokens) {
+  const int p = page_size, d = head_dim, hkv = num_kv_heads;
+  if (!valid_block(block, d) || p % 4 != 0 || d % 16 != 0) return 1;
+  if (group < 16 || d % group != 0) return 1;
+  const size_t slab = int4g_slab(p, d, group);
+  const int64_t capacity = static_cast<int64_t>(num_pages) * p;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int t = 0; t < num_tokens; ++t) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= capacity) continue;
+    const int page = static_cast<int>(slot / p), off = static_cast<int>(slot % p);
+    std::vector<float> x(d), y(d);
+    std::vector<uint8_t> codes(d);
+    for (int h = 0; h < hkv; ++h) {
+      uint8_t* s = pool + (static_cast<size_t>(page) * hkv + h) * slab;
+      for (int kind = 0; kind < 2; ++kind) {
+        const uint16_t* src = (kind == 0 ? k : v) + t * token_stride + static_cast<int64_t>(h) * d;
+        for (int c = 0; c < d; ++c) x[c] = widen(src[c], dtype);
+        kvq_oracle_rotate(x.data(), y.data(), d, block);
+        for (int gi = 0; gi < d / group; ++gi) {
+          uint16_t sh, zh;
+          kvq_oracle_quantize(&y[gi * group], group, &codes[gi * group], &sh, &zh);   /* R10 */
+          put_u16(s + metag_byte(p, d, group, kind, off, gi), sh);
+          put_u16(s + metag_byte(p, d, group, kind, off, gi) + 2, zh);
+        }
+        for (int c = 0; c < d; ++c) {
+          size_t at = kind == 0 ? k_code_byte(p, d, off, c) : vg_code_byte(p, d, off, c);
+          bool high = kind == 0 ? (c % 2 == 1) : ((c / (d / 8)) % 2 == 1);
+          s[at] = static_cast<uint8_t>(high ? ((s[at] & 0x0f) | (codes[c] << 4)) : ((s[at] & 0xf0) | codes[c]));
+        }
+      }
+    }
+  }
+  return 0;
+}
+
 int32_t kvq_oracle_append_bf16(uint8_t* pool, int32_t num_pages, int32_t page_size,
                                int32_t num_kv_heads, int32_t head_dim,
                                const uint16_t* k, const uint16_t* v, int32_t dtype,
@@ -402,6 +457,24 @@ double kvq_oracle_int8_read(const uint8_t* pool, int32_t page_size, int32_t num_
          static_cast<double>(f16_to_f32(zh));
 }
 
+double kvq_oracle_int4g_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t group, int32_t page, int32_t head,
+                             int32_t off, int32_t kind, int32_t channel, int32_t* code,
+                             uint16_t* scale, uint16_t* zero) {
+  const int p = page_size, d = head_dim;
+  const uint8_t* s = pool + (static_cast<size_t>(page) * num_kv_heads + head) * int4g_slab(p, d, group);
+  int c;
+  if (kind == 0) c = (channel % 2 == 0) ? (s[k_code_byte(p, d, off, channel)] & 0xf) : (s[k_code_byte(p, d, off, channel)] >> 4);
+  else c = ((channel / (d / 8)) % 2 == 0) ? (s[vg_code_byte(p, d, off, channel)] & 0xf) : (s[vg_code_byte(p, d, off, channel)] >> 4);
+  const size_t m = metag_byte(p, d, group, kind, off, channel / group);
+  uint16_t sh = get_u16(s + m), zh = get_u16(s + m + 2);
+  if (code) *code = c;
+  if (scale) *scale = sh;
+  if (zero) *zero = zh;
+  return static_cast<double>(c) * static_cast<double>(f16_to_f32(sh)) +
+         static_cast<double>(f16_to_f32(zh));
+}
+
 double kvq_oracle_bf16_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
                             int32_t head_dim, int32_t page, int32_t head, int32_t off,
                             int32_t kind, int32_t channel) {
@@ -434,6 +507,20 @@ int32_t kvq_oracle_decode_int8(const uint8_t* pool, int32_t page_size, int32_t n
   auto read = [&](int page, int head, int off, int kind, int c) {
     return kvq_oracle_int8_read(pool, page_size, num_kv_heads, head_dim, page, head, off, kind, c,
                                 nullptr, nullptr, nullptr);
+  };
+  return decode_paged(read, page_size, num_kv_heads, head_dim, block, q, dtype, num_q_heads,
+                      block_table, max_pages_per_seq, seq_lens, batch, sm_scale, mask, out);
+}
+
+int32_t kvq_oracle_decode_int4g(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block, int32_t group, const uint16_t* q,
+                                int32_t dtype, int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                double sm_scale, const uint8_t* mask, double* out) {
+  if (!valid_block(block, head_dim) || group < 16 || head_dim % group != 0) return 1;
+  auto read = [&](int page, int head, int off, int kind, int c) {
+    return kvq_oracle_int4g_read(pool, page_size, num_kv_heads, head_dim, group, page, head, off,
+                                 kind, c, nullptr, nullptr, nullptr);
   };
   return decode_paged(read, page_size, num_kv_heads, head_dim, block, q, dtype, num_q_heads,
                       block_table, max_pages_per_seq, seq_lens, batch, sm_scale, mask, out);

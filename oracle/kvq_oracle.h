@@ -40,6 +40,10 @@
  *       Compression in Large Language Models", Abstract, which gives no
  *       formula): the same token-wise asymmetric quantizer with 8-bit codes,
  *       codes 0..255, scale = (max - min) / 255, everything else as R2-R5.
+ *   R10 per-block groups (a variant of R1; "InnerQ" Abstract
+ *       and Figure 1 group along the inner dimension): one group per
+ *       `group` consecutive channels of the rotated vector (normally the
+ *       Hadamard block), each with its own fp16 scale and zero as in R2.
  *   R7  softmax scale is a parameter (normally 1/sqrt(head_dim)); grouped
  *       query attention maps query head h to KV head h / (Hq / Hkv); an empty
  *       sequence gives a zero output; slot < 0 means "do not store".
@@ -64,6 +68,15 @@
  *                             8n+4h .. 8n+4h+3 of token t, byte j = channel
  *                             8n+4h+j.
  *     bytes [2*P*D, +4P)      K sidecar as in the INT4 pool; then V sidecar.
+ *   Grouped INT4 pool (R10, group size g dividing D, at least 16):
+ *   [num_pages][num_kv_heads][slab], slab = P * (D + 8 * (D/g)) bytes:
+ *     bytes [0, P*D/2)        K codes as in the INT4 pool.
+ *     bytes [P*D/2, P*D)      V codes: the 4-byte word index n*P + t (n < D/8)
+ *                             holds channels n + (D/8) j, j = 0..7, of token t
+ *                             (nibble j: byte j/2, bits 4(j%2)..+3).
+ *     bytes [P*D, +4P*D/g)    K sidecar: token t, group i -> fp16 scale at
+ *                             4(t*(D/g) + i), fp16 zero 2 bytes later.
+ *     then the V sidecar in the same form.
  *   bf16 pool: [num_pages][num_kv_heads][slab], slab = 2 * P * D * 2 bytes:
  *     K: bf16 element index t*D + c (token-major);
  *     V: bf16 element index P*D + ((n*(P/4) + g)*8 + j)*4 + i for channel
@@ -110,6 +123,7 @@ void kvq_oracle_quantize_int8(const float* y, int32_t d, uint8_t* codes,
 size_t kvq_oracle_int4_slab_bytes(int32_t page_size, int32_t head_dim);
 size_t kvq_oracle_bf16_slab_bytes(int32_t page_size, int32_t head_dim);
 size_t kvq_oracle_int8_slab_bytes(int32_t page_size, int32_t head_dim);
+size_t kvq_oracle_int4g_slab_bytes(int32_t page_size, int32_t head_dim, int32_t group);
 
 /* Rotate + quantize + scatter num_tokens tokens into the INT4 pool.
  * k, v: [num_tokens][token_stride] 16-bit elements of type dtype, the first
@@ -126,6 +140,13 @@ int32_t kvq_oracle_append_int8(uint8_t* pool, int32_t num_pages, int32_t page_si
                                const uint16_t* k, const uint16_t* v, int32_t dtype,
                                int64_t token_stride, const int32_t* slot_mapping,
                                int32_t num_tokens);
+
+/* Rotate + per-group quantize (R10) + scatter into the grouped INT4 pool. */
+int32_t kvq_oracle_append_int4g(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                                int32_t group, const uint16_t* k, const uint16_t* v,
+                                int32_t dtype, int64_t token_stride, const int32_t* slot_mapping,
+                                int32_t num_tokens);
 
 /* Copy num_tokens tokens into the bf16 pool (fp16 input is rounded to bf16). */
 int32_t kvq_oracle_append_bf16(uint8_t* pool, int32_t num_pages, int32_t page_size,
@@ -145,6 +166,10 @@ double kvq_oracle_int8_read(const uint8_t* pool, int32_t page_size, int32_t num_
                             int32_t head_dim, int32_t page, int32_t head, int32_t off,
                             int32_t kind, int32_t channel, int32_t* code,
                             uint16_t* scale, uint16_t* zero);
+double kvq_oracle_int4g_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t group, int32_t page, int32_t head,
+                             int32_t off, int32_t kind, int32_t channel, int32_t* code,
+                             uint16_t* scale, uint16_t* zero);
 double kvq_oracle_bf16_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
                             int32_t head_dim, int32_t page, int32_t head, int32_t off,
                             int32_t kind, int32_t channel);
@@ -168,6 +193,13 @@ int32_t kvq_oracle_decode_int8(const uint8_t* pool, int32_t page_size,
                                const int32_t* block_table, int32_t max_pages_per_seq,
                                const int32_t* seq_lens, int32_t batch, double sm_scale,
                                const uint8_t* mask, double* out);
+
+/* The same over the grouped INT4 pool. */
+int32_t kvq_oracle_decode_int4g(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block, int32_t group, const uint16_t* q,
+                                int32_t dtype, int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                double sm_scale, const uint8_t* mask, double* out);
 
 /* The same over the bf16 pool (no rotation). */
 int32_t kvq_oracle_decode_bf16(const uint8_t* pool, int32_t page_size,
