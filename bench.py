@@ -260,23 +260,31 @@ def windowed_rate(torch, kvq, workloads, db, iters, plain_gb_s, plain_bytes, w_s
             "time_over_int4_block64": round(ms * 1e3 / plain_us, 4)}
 
 
-def int8_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes):
-    """Token-wise INT8 variant (twice the code bytes of INT4) on the headline
-    workload: decode-only loop over two cache copies (Hadamard block 64), and
-    the prefill append of 32768 ragged tokens over two input/cache sets."""
+def variant_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes, kind):
+    """A cache variant on the headline workload (Hadamard block 64):
+    decode-only loop over two cache copies, and the prefill append of 32768
+    ragged tokens over two input/cache sets.  kind "int8": token-wise INT8
+    (D code bytes + 4 sidecar bytes per vector); "int4g64": INT4 with one
+    scale/zero per 64 channels (D/2 + 4 D/64 bytes)."""
     w = db.w
-    caches = [kvq.Int8Cache(w.num_pages, w.hkv, w.d, 64, "cuda") for _ in range(2)]
+    if kind == "int8":
+        make = lambda nb: kvq.Int8Cache(nb, w.hkv, w.d, 64, "cuda")
+        app_fn, dec_fn, vec_bytes = kvq.kvq_append_paged_int8, kvq.kvq_decode_attn_int8, w.d + 4
+    else:
+        make = lambda nb: kvq.Int4GroupedCache(nb, w.hkv, w.d, 64, 64, "cuda")
+        app_fn, dec_fn, vec_bytes = kvq.kvq_append_paged_int4g, kvq.kvq_decode_attn_int4g, w.d // 2 + 4 * (w.d // 64)
+    caches = [make(w.num_pages) for _ in range(2)]
     for c in caches:
-        kvq.kvq_append_paged_int8(c, w.k, w.v, w.slot_mapping)
+        app_fn(c, w.k, w.v, w.slot_mapping)
 
     def dec(i):
-        kvq.kvq_decode_attn_int8(caches[i % 2], db.qs[i % RING], db.bt, db.sl, w.max_seq_len,
-                                 w.sm_scale, out=db.out, workspace=db.ws)
+        dec_fn(caches[i % 2], db.qs[i % RING], db.bt, db.sl, w.max_seq_len, w.sm_scale, out=db.out,
+               workspace=db.ws)
 
     for i in range(10):
         dec(i)
     ms, _ = _time_events(torch, dec, iters)
-    nbytes = decode_bytes(w.seq_lens, w.hkv, w.hq, w.d, w.d + 4)   # D codes + fp16 scale, zero
+    nbytes = decode_bytes(w.seq_lens, w.hkv, w.hq, w.d, vec_bytes)
     res = {"decode": {"us": round(ms * 1e3, 2), "bytes": nbytes,
                       "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                       "pct_of_peak": round(100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
@@ -286,17 +294,17 @@ def int8_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes):
     sets = []
     for r in range(2):
         pw = workloads.prefill_append(3 + 10 * r, device="cuda", block=64)
-        sets.append((pw, kvq.Int8Cache(pw.num_pages, pw.hkv, pw.d, 64, "cuda")))
+        sets.append((pw, make(pw.num_pages)))
 
     def app(i):
         pw, c = sets[i % 2]
-        kvq.kvq_append_paged_int8(c, pw.k, pw.v, pw.slot_mapping)
+        app_fn(c, pw.k, pw.v, pw.slot_mapping)
 
     for i in range(10):
         app(i)
     ms, _ = _time_events(torch, app, iters)
     pw = sets[0][0]
-    abytes = append_bytes(pw.num_tokens, pw.hkv, pw.d, pw.d + 4)
+    abytes = append_bytes(pw.num_tokens, pw.hkv, pw.d, vec_bytes)
     res["prefill_append"] = {"us": round(ms * 1e3, 2), "mtok_s": round(pw.num_tokens / (ms * 1e-3) / 1e6, 1),
                              "gb_s": round(abytes / (ms * 1e-3) / 1e9, 1), "bytes": abytes}
     del sets
@@ -538,7 +546,8 @@ def main(argv=None):
         variants[f"int4_block{blk}" if blk else "int4_plain"] = dec_bytes / (ms * 1e-3) / 1e9
     db.refill(64)
     windowed = windowed_rate(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes)
-    int8 = int8_rates(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes)
+    int8 = variant_rates(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes, "int8")
+    int4g = variant_rates(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes, "int4g64")
     db.int4 = db.int4[:1]
     torch.cuda.empty_cache()
     db.make_bf16()
@@ -596,6 +605,7 @@ def main(argv=None):
         "rotated_over_plain_decode": round(variants["int4_block64"] / variants["int4_plain"], 4),
         "windowed_decode": windowed,
         "int8_kv": int8,
+        "int4_groups64": int4g,
         "long_context_decode": long_ctx,
         "concurrency_sweep": conc,
         "bf16_kv": {"gb_s": round(bf16_bytes / (ms_bf16 * 1e-3) / 1e9, 1),

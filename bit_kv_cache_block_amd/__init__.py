@@ -8,6 +8,7 @@ call raises.
 
 Entry points carry the C names: ``kvq_append_paged``, ``kvq_decode_attn``,
 ``kvq_decode_attn_windowed``, ``kvq_append_paged_int8``, ``kvq_decode_attn_int8``,
+``kvq_append_paged_int4g``, ``kvq_decode_attn_int4g``,
 ``kvq_append_paged_bf16``, ``kvq_decode_attn_bf16``, the workspace and page
 size queries.
 """
@@ -28,8 +29,9 @@ PAGE_SIZE = 16
 
 # every symbol include/kvq.h declares
 EXPORTED = (
-    "kvq_int4_page_bytes", "kvq_int8_page_bytes", "kvq_bf16_page_bytes",
+    "kvq_int4_page_bytes", "kvq_int8_page_bytes", "kvq_int4g_page_bytes", "kvq_bf16_page_bytes",
     "kvq_append_paged", "kvq_decode_attn", "kvq_append_paged_int8", "kvq_decode_attn_int8",
+    "kvq_append_paged_int4g", "kvq_decode_attn_int4g",
     "kvq_decode_workspace_bytes", "kvq_append_paged_bf16", "kvq_decode_attn_bf16",
     "kvq_decode_attn_windowed", "kvq_decode_windowed_workspace_bytes",
     "kvq_status_string", "kvq_last_error", "kvq_abi_version",
@@ -46,6 +48,12 @@ class _QuantDesc(C.Structure):   # kvq_int4_cache and kvq_int8_cache
     _fields_ = [("pool", C.c_void_p), ("num_pages", C.c_int32), ("page_size", C.c_int32),
                 ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("hadamard_block", C.c_int32)]
+
+
+class _GroupedDesc(C.Structure):   # kvq_int4g_cache
+    _fields_ = [("pool", C.c_void_p), ("num_pages", C.c_int32), ("page_size", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("hadamard_block", C.c_int32), ("group_size", C.c_int32)]
 
 
 class _Bf16Desc(C.Structure):
@@ -70,12 +78,16 @@ def lib() -> C.CDLL:
         L.kvq_int4_page_bytes.restype = sz
         L.kvq_int8_page_bytes.argtypes = [i32, i32, i32]
         L.kvq_int8_page_bytes.restype = sz
+        L.kvq_int4g_page_bytes.argtypes = [i32, i32, i32, i32]
+        L.kvq_int4g_page_bytes.restype = sz
         L.kvq_bf16_page_bytes.argtypes = [i32, i32, i32]
         L.kvq_bf16_page_bytes.restype = sz
         L.kvq_append_paged.argtypes = [C.POINTER(_QuantDesc), p, p, i32, i64, p, i32, p]
         L.kvq_append_paged.restype = i32
         L.kvq_append_paged_int8.argtypes = [C.POINTER(_QuantDesc), p, p, i32, i64, p, i32, p]
         L.kvq_append_paged_int8.restype = i32
+        L.kvq_append_paged_int4g.argtypes = [C.POINTER(_GroupedDesc), p, p, i32, i64, p, i32, p]
+        L.kvq_append_paged_int4g.restype = i32
         L.kvq_append_paged_bf16.argtypes = [C.POINTER(_Bf16Desc), p, p, i32, i64, p, i32, p]
         L.kvq_append_paged_bf16.restype = i32
         dec = [p, i32, i32, p, i32, p, i32, i32, C.c_float, i32, p, p, sz, p]
@@ -83,6 +95,8 @@ def lib() -> C.CDLL:
         L.kvq_decode_attn.restype = i32
         L.kvq_decode_attn_int8.argtypes = [C.POINTER(_QuantDesc), *dec]
         L.kvq_decode_attn_int8.restype = i32
+        L.kvq_decode_attn_int4g.argtypes = [C.POINTER(_GroupedDesc), *dec]
+        L.kvq_decode_attn_int4g.restype = i32
         L.kvq_decode_attn_bf16.argtypes = [C.POINTER(_Bf16Desc), *dec]
         L.kvq_decode_attn_bf16.restype = i32
         L.kvq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -136,6 +150,10 @@ def kvq_int8_page_bytes(page_size: int, num_kv_heads: int, head_dim: int) -> int
     return int(lib().kvq_int8_page_bytes(page_size, num_kv_heads, head_dim))
 
 
+def kvq_int4g_page_bytes(page_size: int, num_kv_heads: int, head_dim: int, group_size: int) -> int:
+    return int(lib().kvq_int4g_page_bytes(page_size, num_kv_heads, head_dim, group_size))
+
+
 def kvq_bf16_page_bytes(page_size: int, num_kv_heads: int, head_dim: int) -> int:
     return int(lib().kvq_bf16_page_bytes(page_size, num_kv_heads, head_dim))
 
@@ -169,6 +187,28 @@ class Int4Cache(_QuantCache):
 class Int8Cache(_QuantCache):
     """INT8 page pool (kvq_int8_cache)."""
     _page_bytes = staticmethod(kvq_int8_page_bytes)
+
+
+class Int4GroupedCache:
+    """Caller-owned grouped INT4 page pool (kvq_int4g_cache)."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int, hadamard_block: int,
+                 group_size: int, device="cuda", page_size: int = PAGE_SIZE,
+                 pool: torch.Tensor | None = None):
+        self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
+        self.hadamard_block, self.group_size, self.page_size = hadamard_block, group_size, page_size
+        nbytes = kvq_int4g_page_bytes(page_size, num_kv_heads, head_dim, group_size)
+        if nbytes == 0:
+            raise ValueError("group_size must divide head_dim")
+        if pool is None:
+            pool = torch.zeros((num_pages, nbytes), dtype=torch.uint8, device=device)
+        if pool.numel() < num_pages * nbytes or pool.dtype != torch.uint8 or not pool.is_contiguous():
+            raise ValueError("pool must be a contiguous uint8 tensor of num_pages * page bytes")
+        self.pool = pool
+
+    def desc(self) -> _GroupedDesc:
+        return _GroupedDesc(self.pool.data_ptr(), self.num_pages, self.page_size, self.num_kv_heads,
+                            self.head_dim, self.hadamard_block, self.group_size)
 
 
 def _need(cache, cls):
@@ -229,6 +269,13 @@ def kvq_append_paged_int8(cache: Int8Cache, k: torch.Tensor, v: torch.Tensor,
             cache.head_dim, k, v, slot_mapping, stream)
 
 
+def kvq_append_paged_int4g(cache: Int4GroupedCache, k: torch.Tensor, v: torch.Tensor,
+                           slot_mapping: torch.Tensor, stream=None) -> None:
+    """Rotate + per-group quantize + scatter new tokens into the grouped pool."""
+    _append(lib().kvq_append_paged_int4g, _need(cache, Int4GroupedCache).desc(), cache.num_kv_heads,
+            cache.head_dim, k, v, slot_mapping, stream)
+
+
 def kvq_append_paged_bf16(cache: Bf16Cache, k: torch.Tensor, v: torch.Tensor,
                           slot_mapping: torch.Tensor, stream=None) -> None:
     _append(lib().kvq_append_paged_bf16, cache.desc(), cache.num_kv_heads, cache.head_dim, k, v,
@@ -283,6 +330,16 @@ def kvq_decode_attn_int8(cache: Int8Cache, q: torch.Tensor, block_table: torch.T
     return _decode(lib().kvq_decode_attn_int8, _need(cache, Int8Cache).desc(), cache.num_kv_heads,
                    cache.head_dim, q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace,
                    num_splits, stream)
+
+
+def kvq_decode_attn_int4g(cache: Int4GroupedCache, q: torch.Tensor, block_table: torch.Tensor,
+                          seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float | None = None,
+                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                          num_splits: int = 0, stream=None) -> torch.Tensor:
+    """Paged decode attention over the grouped INT4 cache; returns fp32 [B][Hq][D]."""
+    return _decode(lib().kvq_decode_attn_int4g, _need(cache, Int4GroupedCache).desc(),
+                   cache.num_kv_heads, cache.head_dim, q, block_table, seq_lens, max_seq_len,
+                   sm_scale, out, workspace, num_splits, stream)
 
 
 def kvq_decode_attn_bf16(cache: Bf16Cache, q: torch.Tensor, block_table: torch.Tensor,

@@ -119,7 +119,7 @@ size_t workspace_bytes(int32_t batch, int32_t hq, int32_t d, const SplitPlan& p)
 
 namespace {
 
-enum class Pool { kInt4, kInt8, kBf16 };
+enum class Pool { kInt4, kInt8, kInt4g, kBf16 };
 
 kvq_status check_block(int32_t b, int32_t d) {
   if (!(b == 0 || b == 16 || b == 32 || b == 64 || b == 128) || b > d)
@@ -128,7 +128,7 @@ kvq_status check_block(int32_t b, int32_t d) {
 }
 
 kvq_status launch_decode(Pool kind, const void* pool, int32_t num_pages, int32_t hkv, int32_t d,
-                         int32_t block, const void* q, kvq_dtype dtype, int32_t hq,
+                         int32_t block, int32_t group, const void* q, kvq_dtype dtype, int32_t hq,
                          const int32_t* block_table, int32_t max_pages_per_seq,
                          const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                          float sm_scale, int32_t num_splits, float* out, void* workspace,
@@ -166,10 +166,12 @@ kvq_status launch_decode(Pool kind, const void* pool, int32_t num_pages, int32_t
   a.in_bf16 = dtype == KVQ_BF16;
   a.part_stride = plan.nsplit;
   a.window_slot = -1;
+  a.group = group;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = kind == Pool::kInt4   ? launch_decode_int4(a, s)
-                 : kind == Pool::kInt8 ? launch_decode_int8(a, s)
-                                       : launch_decode_bf16(a, s);
+  hipError_t e = kind == Pool::kInt4    ? launch_decode_int4(a, s)
+                 : kind == Pool::kInt8  ? launch_decode_int8(a, s)
+                 : kind == Pool::kInt4g ? launch_decode_int4g(a, s)
+                                        : launch_decode_bf16(a, s);
   if (e == hipSuccess && plan.nsplit > 1) e = launch_reduce(a, s);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;
@@ -197,6 +199,14 @@ size_t kvq_int8_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head
   return static_cast<size_t>(num_kv_heads) * page_size * (2 * head_dim + 8);
 }
 
+size_t kvq_int4g_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t group_size) {
+  if (page_size <= 0 || num_kv_heads <= 0 || head_dim <= 0 || group_size <= 0 ||
+      head_dim % group_size != 0)
+    return 0;
+  return static_cast<size_t>(num_kv_heads) * page_size * (head_dim + 8 * (head_dim / group_size));
+}
+
 }  // extern "C"
 
 namespace kvq {
@@ -204,14 +214,31 @@ namespace {
 
 // The quantizing append shared by the INT4 and INT8 pools (same descriptor
 // fields, different code width).
+int32_t group_of(const kvq_int4_cache*) { return 0; }
+int32_t group_of(const kvq_int8_cache*) { return 0; }
+int32_t group_of(const kvq_int4g_cache* c) { return c->group_size; }
+
 template <class Cache>
-kvq_status append_quant(const Cache* cache, bool int8, const void* k, const void* v, kvq_dtype dtype,
-                        int64_t token_stride, const int32_t* slot_mapping, int32_t num_tokens,
-                        void* stream) {
+kvq_status check_quant_cache(const Cache* cache, Pool kind) {
   if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
   kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
   if (st != KVQ_OK) return st;
   st = check_block(cache->hadamard_block, cache->head_dim);
+  if (st != KVQ_OK) return st;
+  if (kind == Pool::kInt4g) {
+    const int32_t gs = group_of(cache);
+    if (!(gs == 32 || gs == 64) || gs > cache->head_dim)
+      return fail(KVQ_ERR_UNSUPPORTED, "group_size %d unsupported for head_dim %d (32 or 64)", gs,
+                  cache->head_dim);
+  }
+  return KVQ_OK;
+}
+
+template <class Cache>
+kvq_status append_quant(const Cache* cache, Pool kind, const void* k, const void* v, kvq_dtype dtype,
+                        int64_t token_stride, const int32_t* slot_mapping, int32_t num_tokens,
+                        void* stream) {
+  kvq_status st = check_quant_cache(cache, kind);
   if (st != KVQ_OK) return st;
   st = check_append(cache->pool, k, v, dtype, token_stride, slot_mapping, num_tokens,
                     cache->num_kv_heads, cache->head_dim);
@@ -228,25 +255,25 @@ kvq_status append_quant(const Cache* cache, bool int8, const void* k, const void
   a.head_dim = cache->head_dim;
   a.block = cache->hadamard_block;
   a.in_bf16 = dtype == KVQ_BF16;
+  a.group = group_of(cache);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = int8 ? launch_append_int8(a, s) : launch_append_int4(a, s);
+  const hipError_t e = kind == Pool::kInt8    ? launch_append_int8(a, s)
+                       : kind == Pool::kInt4g ? launch_append_int4g(a, s)
+                                              : launch_append_int4(a, s);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;
 }
 
 template <class Cache>
-kvq_status decode_quant(const Cache* cache, bool int8, const void* q, kvq_dtype dtype,
+kvq_status decode_quant(const Cache* cache, Pool kind, const void* q, kvq_dtype dtype,
                         int32_t num_q_heads, const int32_t* block_table, int32_t max_pages_per_seq,
                         const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
                         int32_t num_splits, float* out, void* workspace,
                         size_t workspace_bytes_given, void* stream) {
-  if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
-  kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
+  kvq_status st = check_quant_cache(cache, kind);
   if (st != KVQ_OK) return st;
-  st = check_block(cache->hadamard_block, cache->head_dim);
-  if (st != KVQ_OK) return st;
-  return launch_decode(int8 ? Pool::kInt8 : Pool::kInt4, cache->pool, cache->num_pages,
-                       cache->num_kv_heads, cache->head_dim, cache->hadamard_block, q, dtype,
+  return launch_decode(kind, cache->pool, cache->num_pages, cache->num_kv_heads, cache->head_dim,
+                       cache->hadamard_block, group_of(cache), q, dtype,
                        num_q_heads, block_table, max_pages_per_seq, seq_lens, batch, max_seq_len,
                        sm_scale, num_splits, out, workspace, workspace_bytes_given, stream);
 }
@@ -259,13 +286,19 @@ extern "C" {
 kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const void* v,
                             kvq_dtype dtype, int64_t token_stride, const int32_t* slot_mapping,
                             int32_t num_tokens, void* stream) {
-  return append_quant(cache, false, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
+  return append_quant(cache, Pool::kInt4, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
 }
 
 kvq_status kvq_append_paged_int8(const kvq_int8_cache* cache, const void* k, const void* v,
                                  kvq_dtype dtype, int64_t token_stride,
                                  const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
-  return append_quant(cache, true, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
+  return append_quant(cache, Pool::kInt8, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
+}
+
+kvq_status kvq_append_paged_int4g(const kvq_int4g_cache* cache, const void* k, const void* v,
+                                  kvq_dtype dtype, int64_t token_stride,
+                                  const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
+  return append_quant(cache, Pool::kInt4g, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
 }
 
 kvq_status kvq_append_paged_bf16(const kvq_bf16_cache* cache, const void* k, const void* v,
@@ -298,7 +331,7 @@ kvq_status kvq_decode_attn(const kvq_int4_cache* cache, const void* q, kvq_dtype
                            int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
                            int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
                            void* workspace, size_t workspace_bytes_given, void* stream) {
-  return decode_quant(cache, false, q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+  return decode_quant(cache, Pool::kInt4, q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                       batch, max_seq_len, sm_scale, num_splits, out, workspace,
                       workspace_bytes_given, stream);
 }
@@ -308,8 +341,18 @@ kvq_status kvq_decode_attn_int8(const kvq_int8_cache* cache, const void* q, kvq_
                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
                                 int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
                                 void* workspace, size_t workspace_bytes_given, void* stream) {
-  return decode_quant(cache, true, q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+  return decode_quant(cache, Pool::kInt8, q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                       batch, max_seq_len, sm_scale, num_splits, out, workspace,
+                      workspace_bytes_given, stream);
+}
+
+kvq_status kvq_decode_attn_int4g(const kvq_int4g_cache* cache, const void* q, kvq_dtype dtype,
+                                 int32_t num_q_heads, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                 int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                                 void* workspace, size_t workspace_bytes_given, void* stream) {
+  return decode_quant(cache, Pool::kInt4g, q, dtype, num_q_heads, block_table, max_pages_per_seq,
+                      seq_lens, batch, max_seq_len, sm_scale, num_splits, out, workspace,
                       workspace_bytes_given, stream);
 }
 
@@ -321,7 +364,7 @@ kvq_status kvq_decode_attn_bf16(const kvq_bf16_cache* cache, const void* q, kvq_
   if (cache == nullptr) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache descriptor is null");
   kvq_status st = check_geometry(cache->num_pages, cache->page_size, cache->num_kv_heads, cache->head_dim);
   if (st != KVQ_OK) return st;
-  return launch_decode(Pool::kBf16, cache->pool, cache->num_pages, cache->num_kv_heads, cache->head_dim, 0,
+  return launch_decode(Pool::kBf16, cache->pool, cache->num_pages, cache->num_kv_heads, cache->head_dim, 0, 0,
                        q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens, batch,
                        max_seq_len, sm_scale, num_splits, out, workspace, workspace_bytes_given,
                        stream);

@@ -6,7 +6,9 @@
 // and zero point kept as FP16 as in "InnerQ", Table 3).  The same kernel with
 // 8-bit codes (255 levels) writes the INT8 variant ("GPU-Accelerated INT8
 // Quantization for KV Cache Compression in Large Language Models",
-// Abstract).  Also the bf16-cache baseline copy.
+// Abstract), and with one scale and zero per group of channels the grouped
+// INT4 variant (grouping along the inner dimension as in "InnerQ", Abstract
+// and Figure 1).  Also the bf16-cache baseline copy.
 //
 // Bit-exactness: the quantizer's fp32 steps are done one rounding at a time
 // in the order the header of kvq.h states (this file is built with
@@ -51,16 +53,20 @@ __device__ __forceinline__ void widen8(u32x4 w, float* x) {
 // current unit is computed.  Lanes of consecutive tokens write consecutive
 // words of a page slab, so tokens that fill a page in order are stored as
 // contiguous runs.
-template <int D, int BLK, bool BF16, int BITS>
+template <int D, int BLK, bool BF16, int BITS, int GS>
 __global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void append_quant_kernel(AppendArgs a) {
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
+  static_assert(GS == 0 || (BITS == 4 && (GS == 32 || GS == 64) && GS <= D), "groups of 32 or 64 channels, 4-bit");
   constexpr int kLPV = D / kLaneElems;   // lanes per vector
   constexpr int kTok = 64 / kLPV;        // tokens per unit
   constexpr int kChunks = D / 8;         // 16-byte pieces per row
   constexpr int kRowBytes = 2 * D;
   constexpr int kCodeBytes = D * BITS / 8;             // one vector's codes
-  constexpr int kSlab = kPage * (2 * kCodeBytes + 8);
+  constexpr int kNG = GS ? D / GS : 1;                 // scale/zero pairs per vector
+  constexpr int kGL = GS ? kLaneElems / GS : 1;        // of them held by one lane
+  constexpr int kGE = kLaneElems / kGL;                // elements of a lane's group
+  constexpr int kSlab = kPage * (2 * kCodeBytes + 8 * kNG);
   constexpr int kWords = kLaneElems * BITS / 32;       // code words per lane
   constexpr float kTop = BITS == 4 ? 15.0f : 255.0f;   // largest code
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[kAppendThreads / 64][kTok * kRowBytes];
@@ -132,7 +138,7 @@ void append_quant_kernel(AppendArgs a) {
   // Codes and sidecar of one unit, written into the slot's page (tokens past
   // the end have slot -1).  A unit is stored one iteration after it is
   // computed, so that the wait for the next rows never waits for fresh stores.
-  struct Pending { uint32_t words[kWords]; uint32_t meta; int32_t slot; uint32_t h; };
+  struct Pending { uint32_t words[kWords]; uint32_t meta[kGL]; int32_t slot; uint32_t h; };
   auto store = [&](const Pending& q) {
     if (q.slot < 0 || static_cast<int64_t>(q.slot) >= static_cast<int64_t>(a.num_pages) * kPage) return;
     const int page = q.slot / kPage, off = q.slot % kPage;
@@ -142,7 +148,7 @@ void append_quant_kernel(AppendArgs a) {
 #pragma unroll
       for (int i = 0; i < kWords / 4; ++i)
         dst[i] = u32x4{q.words[4 * i], q.words[4 * i + 1], q.words[4 * i + 2], q.words[4 * i + 3]};
-    } else if constexpr (BITS == 4) {   // V: word n*P + t = channels 8n..8n+7 of token t
+    } else if constexpr (BITS == 4) {   // V: word n*P + t of token t (8 channels)
       uint32_t* vw = reinterpret_cast<uint32_t*>(slab + kPage * kCodeBytes);
 #pragma unroll
       for (int m = 0; m < 8; ++m) vw[(hf * 8 + m) * kPage + off] = q.words[m];
@@ -151,7 +157,14 @@ void append_quant_kernel(AppendArgs a) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) vw[(hf * 8 + m) * kPage + off] = u32x2{q.words[2 * m], q.words[2 * m + 1]};
     }
-    if (hf == 0) *reinterpret_cast<uint32_t*>(slab + 2 * kPage * kCodeBytes + kind * 4 * kPage + off * 4) = q.meta;
+    uint8_t* meta = slab + 2 * kPage * kCodeBytes + kind * 4 * kPage * kNG;
+    if constexpr (GS == 0) {
+      if (hf == 0) *reinterpret_cast<uint32_t*>(meta + off * 4) = q.meta[0];
+    } else if constexpr (kGL == 1) {   // group hf of token off
+      *reinterpret_cast<uint32_t*>(meta + (off * kNG + hf) * 4) = q.meta[0];
+    } else {                           // groups 2hf, 2hf+1
+      *reinterpret_cast<u32x2*>(meta + (off * kNG + hf * kGL) * 4) = u32x2{q.meta[0], q.meta[1]};
+    }
   };
 
   int32_t slot_nxt = -1;
@@ -206,17 +219,22 @@ void append_quant_kernel(AppendArgs a) {
       }
     }
 
-    // range.  Rounding is monotone, so min/max of the unscaled butterfly
-    // output, scaled once, equal min/max of the scaled elements.
-    float mn = x[0], mx = x[0];
+    // range of each group (the whole vector when GS = 0).  Rounding is
+    // monotone, so min/max of the unscaled butterfly output, scaled once,
+    // equal min/max of the scaled elements.
+    float mn[kGL], mx[kGL];
 #pragma unroll
-    for (int k = 1; k < kLaneElems; ++k) {
-      mn = fminf(mn, x[k]);
-      mx = fmaxf(mx, x[k]);
+    for (int gl = 0; gl < kGL; ++gl) {
+      mn[gl] = mx[gl] = x[gl * kGE];
+#pragma unroll
+      for (int k = gl * kGE + 1; k < (gl + 1) * kGE; ++k) {
+        mn[gl] = fminf(mn[gl], x[k]);
+        mx[gl] = fmaxf(mx[gl], x[k]);
+      }
     }
-    if constexpr (kLPV == 2) {
-      mn = fminf(mn, dpp_f<kDppXor1>(mn));
-      mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
+    if constexpr (GS == 0 && kLPV == 2) {
+      mn[0] = fminf(mn[0], dpp_f<kDppXor1>(mn[0]));
+      mx[0] = fmaxf(mx[0], dpp_f<kDppXor1>(mx[0]));
     }
     // A power-of-two normalisation (b = 16, 64) is exact, so it is folded
     // into the subtraction below: fma(x, s, -zero) rounds x*s - zero once,
@@ -226,50 +244,95 @@ void append_quant_kernel(AppendArgs a) {
     constexpr bool kExactNorm = BLK == 16 || BLK == 64;
     const float sb = BLK > 0 ? block_norm(BLK) : 1.0f;
     if constexpr (BLK > 0) {
-      mn = mn * sb;
-      mx = mx * sb;
+#pragma unroll
+      for (int gl = 0; gl < kGL; ++gl) {
+        mn[gl] = mn[gl] * sb;
+        mx[gl] = mx[gl] * sb;
+      }
       if constexpr (!kExactNorm) {
 #pragma unroll
         for (int k = 0; k < kLaneElems; ++k) x[k] = x[k] * sb;
       }
     }
 
-    // fp16 zero and scale, reciprocal (0 for a zero scale)
-    const float zero_f = mn + 0.0f;
-    const float range = (mx - mn) + 0.0f;
-    const float step = range / kTop;
-    const _Float16 sh = static_cast<_Float16>(step);
-    const _Float16 zh = static_cast<_Float16>(zero_f);
-    const float sf = static_cast<float>(sh);
-    const float zf = static_cast<float>(zh);
-    const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+    // fp16 zero and scale, reciprocal (0 for a zero scale), per group
+    float zf[kGL], inv[kGL];
+#pragma unroll
+    for (int gl = 0; gl < kGL; ++gl) {
+      const float zero_f = mn[gl] + 0.0f;
+      const float range = (mx[gl] - mn[gl]) + 0.0f;
+      const float step = range / kTop;
+      const _Float16 sh = static_cast<_Float16>(step);
+      const _Float16 zh = static_cast<_Float16>(zero_f);
+      const float sf = static_cast<float>(sh);
+      zf[gl] = static_cast<float>(zh);
+      inv[gl] = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+      pend.meta[gl] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
+                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
+    }
 
     // codes: (y - zero) * inv, then round-half-even and clamp to [0, top].
     // Adding 2^23 rounds to an integer in the current (nearest-even) mode for
     // any value in [0, 2^23); the clamp in that biased domain equals clamping
     // the rounded value; the code is then the low 4 (8) bits of the float.
     constexpr int kPer = 32 / BITS;   // codes per word
+    auto code = [&](int k) {
+      constexpr int gl_div = kGE;
+      const int gl = k / gl_div;
+      const float d = kExactNorm ? __builtin_fmaf(x[k], sb, -zf[gl]) : x[k] - zf[gl];
+      const float q = d * inv[gl];
+      return f2u(__builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388608.0f + kTop));
+    };
+    // the unit's results are stored at the start of the next iteration
+    if (GS == 0 || kind == 0) {   // consecutive channels: K, or V of the token-wise pools
 #pragma unroll
-    for (int m = 0; m < kWords; ++m) {
-      uint32_t c[kPer];
+      for (int m = 0; m < kWords; ++m) {
+        uint32_t c[kPer];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const float d = kExactNorm ? __builtin_fmaf(x[kPer * m + i], sb, -zf) : x[kPer * m + i] - zf;
-        const float q = d * inv;
-        const float t = __builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388608.0f + kTop);
-        c[i] = f2u(t);
+        for (int i = 0; i < kPer; ++i) c[i] = code(kPer * m + i);
+        if constexpr (BITS == 4) {
+          pend.words[m] = pack8_nibbles(c);
+        } else {
+          const uint32_t lo = __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u);   // c0.byte0, c1.byte0
+          const uint32_t hi = __builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u);
+          pend.words[m] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
       }
-      // the unit's results are stored at the start of the next iteration
-      if constexpr (BITS == 4) {
+    } else if constexpr (GS != 0 && kLPV == 1) {
+      // grouped V, D = 64: word n holds channels n + 8j, j = 0..7
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        uint32_t c[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = code(m + 8 * j);
         pend.words[m] = pack8_nibbles(c);
-      } else {
-        const uint32_t lo = __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u);   // c0.byte0, c1.byte0
-        const uint32_t hi = __builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u);
-        pend.words[m] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      }
+    } else if constexpr (GS != 0) {
+      // grouped V, D = 128: word n holds channels n + 16j, j = 0..7; this
+      // lane has j = 4hf .. 4hf+3 (its channels n + 16j'), i.e. 16 bits of
+      // every word, and stores words 8hf .. 8hf+7 after swapping the other
+      // half-words with its partner lane
+      uint32_t hw[16];
+#pragma unroll
+      for (int n2 = 0; n2 < 16; ++n2) {
+        const uint32_t t0 = __builtin_amdgcn_perm(code(n2 + 16), code(n2), 0x0c0c0400u);        // c0 | c1 << 8
+        const uint32_t t1 = __builtin_amdgcn_perm(code(n2 + 48), code(n2 + 32), 0x0c0c0400u);
+        const uint32_t b0 = (t0 | (t0 >> 4)) & 0xFFu;                                           // c0 | c1 << 4
+        const uint32_t b1 = (t1 | (t1 >> 4)) & 0xFFu;
+        hw[n2] = b0 | (b1 << 8);
+      }
+      uint32_t send[4], recv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        send[i] = hf ? (hw[2 * i] | (hw[2 * i + 1] << 16)) : (hw[8 + 2 * i] | (hw[9 + 2 * i] << 16));
+        recv[i] = dpp_u<kDppXor1>(send[i]);
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const uint32_t other = (m & 1) ? (recv[m >> 1] >> 16) : (recv[m >> 1] & 0xFFFFu);
+        pend.words[m] = hf ? (other | (hw[8 + m] << 16)) : (hw[m] | (other << 16));
       }
     }
-    pend.meta = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
-                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
     pend.slot = slot;
     pend.h = cur.h;
     have_pend = true;
@@ -321,28 +384,28 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
   }
 }
 
-template <int D, int BLK, int BITS>
+template <int D, int BLK, int BITS, int GS>
 hipError_t launch_quant_d(const AppendArgs& a, hipStream_t s) {
   constexpr int kTok = D == 128 ? 32 : 64;
   const int64_t units = (static_cast<int64_t>(a.num_tokens) + kTok - 1) / kTok * a.num_kv_heads * 2;
   const int64_t blocks = (units + kAppendThreads / 64 - 1) / (kAppendThreads / 64);
   const dim3 grid(static_cast<unsigned>(blocks < kResidentBlocks ? blocks : kResidentBlocks));
   if (a.in_bf16)
-    append_quant_kernel<D, BLK, true, BITS><<<grid, kAppendThreads, 0, s>>>(a);
+    append_quant_kernel<D, BLK, true, BITS, GS><<<grid, kAppendThreads, 0, s>>>(a);
   else
-    append_quant_kernel<D, BLK, false, BITS><<<grid, kAppendThreads, 0, s>>>(a);
+    append_quant_kernel<D, BLK, false, BITS, GS><<<grid, kAppendThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int GS>
 hipError_t launch_quant_block(const AppendArgs& a, hipStream_t s) {
   switch (a.block) {
-    case 0: return launch_quant_d<D, 0, BITS>(a, s);
-    case 16: return launch_quant_d<D, 16, BITS>(a, s);
-    case 32: return launch_quant_d<D, 32, BITS>(a, s);
-    case 64: return launch_quant_d<D, 64, BITS>(a, s);
+    case 0: return launch_quant_d<D, 0, BITS, GS>(a, s);
+    case 16: return launch_quant_d<D, 16, BITS, GS>(a, s);
+    case 32: return launch_quant_d<D, 32, BITS, GS>(a, s);
+    case 64: return launch_quant_d<D, 64, BITS, GS>(a, s);
     case 128:
-      if constexpr (D == 128) return launch_quant_d<D, 128, BITS>(a, s);
+      if constexpr (D == 128) return launch_quant_d<D, 128, BITS, GS>(a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -352,12 +415,19 @@ hipError_t launch_quant_block(const AppendArgs& a, hipStream_t s) {
 
 hipError_t launch_append_int4(const AppendArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  return a.head_dim == 128 ? launch_quant_block<128, 4>(a, s) : launch_quant_block<64, 4>(a, s);
+  return a.head_dim == 128 ? launch_quant_block<128, 4, 0>(a, s) : launch_quant_block<64, 4, 0>(a, s);
+}
+
+hipError_t launch_append_int4g(const AppendArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  if (a.head_dim == 128)
+    return a.group == 32 ? launch_quant_block<128, 4, 32>(a, s) : launch_quant_block<128, 4, 64>(a, s);
+  return a.group == 32 ? launch_quant_block<64, 4, 32>(a, s) : launch_quant_block<64, 4, 64>(a, s);
 }
 
 hipError_t launch_append_int8(const AppendArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  return a.head_dim == 128 ? launch_quant_block<128, 8>(a, s) : launch_quant_block<64, 8>(a, s);
+  return a.head_dim == 128 ? launch_quant_block<128, 8, 0>(a, s) : launch_quant_block<64, 8, 0>(a, s);
 }
 
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s) {

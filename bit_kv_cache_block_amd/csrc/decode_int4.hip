@@ -29,6 +29,13 @@
 // Quantization for KV Cache Compression in Large Language Models",
 // Abstract): codes 0..255 enter the int8 MFMA as code - 128 (one xor per
 // byte) and the 128 * scale they lose is added to the zero point.
+//
+// And the grouped INT4 variant (one scale and zero per group of GS channels,
+// grouping along the inner dimension as "InnerQ", Abstract and Figure 1): QK
+// runs one product per group with the query operand masked to the group's
+// channels; V is stored so that each PV tile of 16 output channels lies in
+// one group, so PV keeps one product per tile, with the softmax weights of
+// that group (w = p * v_scale of the group) as its operand.
 #include "dev_common.hpp"
 #include "kvq_internal.hpp"
 
@@ -39,8 +46,7 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaves = 4;
-constexpr int kQuads = 1;          // groups of 4 pages per step
-constexpr int kStep = 4 * kQuads;  // pages per step
+constexpr int kStep = 4;   // pages per step
 
 __device__ __forceinline__ float half_lo(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
@@ -94,14 +100,21 @@ __device__ __forceinline__ int qk_channel(int g, int op, int i, int k) {
   else return 16 * g + 8 * (i & 1) + 2 * k + (i >> 1);
 }
 
-// output channel of PV tile tau for lane column n
-template <int D>
+// output channel of PV tile tau for lane column n (the V layout of the
+// token-wise pools puts 8 consecutive channels in a word, the grouped pool
+// channels n + (D/8) j)
+template <int D, int GS>
 __device__ __forceinline__ int pv_channel(int n, int tau) {
-  if constexpr (D == 128) return 8 * n + tau;
-  else return 8 * (n & 7) + 2 * tau + (n >> 3);
+  if constexpr (GS != 0) {
+    if constexpr (D == 128) return n + 16 * tau;
+    else return (n & 7) + 8 * (2 * tau + (n >> 3));
+  } else {
+    if constexpr (D == 128) return 8 * n + tau;
+    else return 8 * (n & 7) + 2 * tau + (n >> 3);
+  }
 }
 
-template <int D, int NS>
+template <int D, int NS, int NG>
 struct alignas(16) Smem {
   static constexpr int kGP = 4 * NS;
   union {
@@ -112,34 +125,36 @@ struct alignas(16) Smem {
       float l[kWaves][kGP];
     } merge;
   } u;
-  float hA[kGP], hS[kGP];
-  uint32_t wl[kWaves][NS][kQuads][4][4][16];   // [wave][set][quad][limb][head][token] = 4 pages' bytes
+  float hA[kGP], hS[kGP][NG];
+  uint32_t wl[kWaves][NS][NG][4][4][16];   // [wave][set][group][limb][head][token] = 4 pages' bytes
 };
 
 // one step's loads: four pages of one KV head, KX (VX) 16-byte pieces of
 // K (V) codes per lane and page
-template <int KX, int VX>
+template <int KX, int VX, int NG>
 struct StepBuf {
   u32x4 kx[kStep][KX];
   u32x4 vx[kStep][VX];
-  uint32_t km[kStep], vm[kStep];
+  uint32_t km[kStep][NG], vm[kStep][NG];   // (scale, zero) per group
   bool pv[kStep];
   bool all_ok;
 };
 
-template <int D, int NS, bool QBF16, int BITS>
+template <int D, int NS, bool QBF16, int BITS, int GS>
 __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a) {
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
+  static_assert(GS == 0 || (BITS == 4 && (GS == 32 || GS == 64) && GS <= D), "groups of 32 or 64 channels, 4-bit");
   constexpr int kCodeBytes = D * BITS / 8;           // one vector's codes
-  constexpr int kSlab = kPage * (2 * kCodeBytes + 8);
+  constexpr int kNG = GS ? D / GS : 1;               // (scale, zero) pairs per vector
+  constexpr int kSlab = kPage * (2 * kCodeBytes + 8 * kNG);
   constexpr int kKX = BITS == 8 && D == 128 ? 2 : 1;  // 16-byte K pieces per lane and page
   constexpr int kVX = BITS == 8 ? 2 : 1;              // 16-byte V pieces per lane and page
-  using Buf = StepBuf<kKX, kVX>;
+  using Buf = StepBuf<kKX, kVX, kNG>;
   constexpr int kNT = D / 16;          // PV tiles = output channels per lane
   constexpr int kOps = D / 64;         // QK MFMAs per page and head group
   constexpr int kGP = 4 * NS;          // padded heads per KV head
   constexpr int kC = D / 16;           // channels per lane when a row of 16 lanes holds a vector
-  __shared__ Smem<D, NS> sm;
+  __shared__ Smem<D, NS, kNG> sm;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -225,7 +240,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
   // group vn)
   const uint32_t k_off = n * kCodeBytes + g * (kCodeBytes / 4);
   const uint32_t v_off = kPage * kCodeBytes + (vn * kPage + 4 * g) * (BITS == 8 ? 8 : 4);
-  const uint32_t km_off = 2 * kPage * kCodeBytes + 4 * n;
+  const uint32_t km_off = 2 * kPage * kCodeBytes + 4 * kNG * n;
   auto load_ids = [&](int first) {
     const int pg = first + lane;
     return pg < pw1 ? bt[pg] : -1;
@@ -262,8 +277,25 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
 #pragma unroll
       for (int j = 0; j < kVX; ++j)
         sb.vx[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_off + 16 * j, 0, kStreamOnce));
-      sb.km[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off, 0, kStreamOnce);
-      sb.vm[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off + 4 * kPage, 0, kStreamOnce);
+      if constexpr (kNG == 1) {
+        sb.km[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off, 0, kStreamOnce);
+        sb.vm[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off + 4 * kPage, 0, kStreamOnce);
+      } else if constexpr (kNG == 2) {
+        const u32x2 k2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, km_off, 0, kStreamOnce));
+        const u32x2 v2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, km_off + 8 * kPage, 0, kStreamOnce));
+        sb.km[i][0] = k2[0];
+        sb.km[i][1] = k2[1];
+        sb.vm[i][0] = v2[0];
+        sb.vm[i][1] = v2[1];
+      } else {
+        const u32x4 k4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, km_off, 0, kStreamOnce));
+        const u32x4 v4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, km_off + 16 * kPage, 0, kStreamOnce));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sb.km[i][j] = k4[j];
+          sb.vm[i][j] = v4[j];
+        }
+      }
     }
   };
   // the query is consumed before the first page loads are issued, so waiting
@@ -282,7 +314,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
   Buf buf0;
   if (pw0 < pw1) load(buf0, pw0);
   // ---- query: rotate in registers, fixed point, limbs ------------------------
-  for (int e = tid; e < kWaves * NS * kQuads * 4 * 4 * 16; e += 64 * kWaves)
+  for (int e = tid; e < kWaves * NS * kNG * 4 * 4 * 16; e += 64 * kWaves)
     (&sm.wl[0][0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
   if (qwave) {
     float v[kC];
@@ -312,10 +344,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
 #pragma unroll
     for (int k = 0; k < kC; k += 4)
       *reinterpret_cast<v4i*>(&sm.u.qi[qhead][kC * n + k]) = v4i{qi[k], qi[k + 1], qi[k + 2], qi[k + 3]};
-    sum = row_sum16_i(sum);             // |sum| <= D * 2^22: exact in int32
+    // sum of the query over each group (|sum| <= D * 2^22: exact in int32);
+    // a lane's kC channels lie in group kC n / GS
+    int32_t gsum[kNG];
+#pragma unroll
+    for (int gi = 0; gi < kNG; ++gi) gsum[gi] = row_sum16_i(kNG == 1 || (kC * n) / (GS ? GS : D) == gi ? sum : 0);
     if (n == 0) {
       sm.hA[qhead] = a.sm_log2 * ldexpf(1.0f, ex - 22);
-      sm.hS[qhead] = static_cast<float>(sum);
+#pragma unroll
+      for (int gi = 0; gi < kNG; ++gi) sm.hS[qhead][gi] = static_cast<float>(gsum[gi]);
     }
   }
   __syncthreads();
@@ -323,12 +360,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
   // A operand of QK: row (head hs, limb lam), k-slots of lane group g: the
   // lane's D/4 consecutive channels, read from LDS as whole vectors
   const LimbSel limb(lam);
-  v4i aq[NS][kOps];
-  float qA[NS], qS[NS];
+  v4i aq[NS][kNG][kOps];   // per group: the operand with other groups' channels zeroed
+  float qA[NS], qS[NS][kNG];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     qA[st] = sm.hA[4 * st + g];          // C-layout head of this lane: row group g
-    qS[st] = sm.hS[4 * st + g];
+#pragma unroll
+    for (int gi = 0; gi < kNG; ++gi) qS[st][gi] = sm.hS[4 * st + g][gi];
     int32_t qc[D / 4];
     const v4i* src = reinterpret_cast<const v4i*>(&sm.u.qi[4 * st + hs][(D / 4) * g]);
 #pragma unroll
@@ -350,16 +388,19 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
           w |= limb.byte(qc[qk_channel<D, BITS>(0, op, i, k)]) << (8 * k);
         vv[i] = static_cast<int32_t>(w);
       }
-      aq[st][op] = vv;
+      // lane group g holds channels [D/4 g, D/4 (g+1)): one group's
+#pragma unroll
+      for (int gi = 0; gi < kNG; ++gi) aq[st][gi][op] = (kNG == 1 || (D / 4) * g / (GS ? GS : D) == gi) ? vv : v4i{0, 0, 0, 0};
     }
   }
 
-  float m_run[NS], l_run[NS], z_run[NS], acc[NS][kNT];
+  float m_run[NS], l_run[NS], z_run[NS][kNG], acc[NS][kNT];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     m_run[st] = kNegInf;
     l_run[st] = 0.0f;
-    z_run[st] = 0.0f;
+#pragma unroll
+    for (int gi = 0; gi < kNG; ++gi) z_run[st][gi] = 0.0f;
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[st][t] = 0.0f;
   }
@@ -390,24 +431,30 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
                  static_cast<int32_t>((sb.kx[i][0][0] >> 4) & kLowNibbles),
                  static_cast<int32_t>((sb.kx[i][0][1] >> 4) & kLowNibbles)};
       }
-      // zero point of the codes as the MFMA sees them
-      const float kzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(sb.km[i]), half_hi(sb.km[i])) : half_hi(sb.km[i]);
       const int tok = (p + i) * kPage + n;
       const bool ok = !tail || (sb.pv[i] && tok >= lo && tok < hi);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        v4i c = mfma_i8(aq[st][0], b0, zero4);
-        if constexpr (kOps == 2) c = mfma_i8(aq[st][1], b1, c);
-        // limbs: c0 * 2^16 + c1 * 2^8 + c2 (c0 * 2^8 + c1 is exact in int32)
-        const float tq = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f,
-                                        static_cast<float>(c[2]));
-        const float l2 = qA[st] * __builtin_fmaf(kzero, qS[st], half_lo(sb.km[i]) * tq);
-        lg[st][i] = ok ? l2 : kNegInf;
+        float dot = 0.0f;
+#pragma unroll
+        for (int gi = 0; gi < kNG; ++gi) {
+          v4i c = mfma_i8(aq[st][gi][0], b0, zero4);
+          if constexpr (kOps == 2) c = mfma_i8(aq[st][gi][1], b1, c);
+          // limbs: c0 * 2^16 + c1 * 2^8 + c2 (c0 * 2^8 + c1 is exact in int32)
+          const float tq = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f,
+                                          static_cast<float>(c[2]));
+          // zero point of the codes as the MFMA sees them
+          const uint32_t km = sb.km[i][gi];
+          const float kzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(km), half_hi(km)) : half_hi(km);
+          dot = gi == 0 ? __builtin_fmaf(kzero, qS[st][0], half_lo(km) * tq)
+                        : dot + __builtin_fmaf(kzero, qS[st][gi], half_lo(km) * tq);
+        }
+        lg[st][i] = ok ? qA[st] * dot : kNegInf;
       }
     }
 
     // online softmax (row = head) and the limbs of w = p * v_scale through LDS
-    float alpha[NS], sw[NS];
+    float alpha[NS], sw[NS][kNG];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       float mc = lg[st][0];
@@ -418,45 +465,49 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
       const float muse = mnew == kNegInf ? 0.0f : mnew;
       alpha[st] = exp2f(m_run[st] - muse);
       m_run[st] = mnew;
-      float psum = 0.0f, zsum = 0.0f, wmax = 0.0f, w[kStep];
+      float pp[kStep], psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < kStep; ++i) {
-        const float pp = exp2f(lg[st][i] - muse);
-        psum += pp;
-        const float vzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(sb.vm[i]), half_hi(sb.vm[i])) : half_hi(sb.vm[i]);
-        if (tail) {
-          const bool ok = lg[st][i] != kNegInf;
-          zsum += ok ? pp * vzero : 0.0f;
-          w[i] = ok ? pp * half_lo(sb.vm[i]) : 0.0f;
-        } else {
-          zsum = __builtin_fmaf(pp, vzero, zsum);
-          w[i] = pp * half_lo(sb.vm[i]);
-        }
-        wmax = fmaxf(wmax, w[i]);
+        pp[i] = exp2f(lg[st][i] - muse);
+        psum += pp[i];
       }
       l_run[st] = __builtin_fmaf(l_run[st], alpha[st], psum);
-      z_run[st] = __builtin_fmaf(z_run[st], alpha[st], zsum);
-      wmax = row_max16(wmax);
-      int ew = 0;
-      frexpf(wmax, &ew);                 // wmax < 2^ew
-      ew = ew < -100 ? -100 : ew;        // such a step weighs < 2^-76 of the max
-      const float wsc = ldexpf(1.0f, 22 - ew);
-      sw[st] = ldexpf(1.0f, ew - 22);
-      uint32_t y[kStep];
 #pragma unroll
-      for (int i = 0; i < kStep; ++i)
-        y[i] = static_cast<uint32_t>(static_cast<int32_t>(rintf(w[i] * wsc)) + 0x8080);
-      // limb bytes of each four pages, one word per limb: bytes 2 / 1 / 0 of y
+      for (int gi = 0; gi < kNG; ++gi) {
+        float zsum = 0.0f, wmax = 0.0f, w[kStep];
 #pragma unroll
-      for (int qd = 0; qd < kQuads; ++qd) {
-        const uint32_t* yq = y + 4 * qd;
-        const uint32_t l0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(yq[3], yq[2], 0x0c0c0602u),
-                                                  __builtin_amdgcn_perm(yq[1], yq[0], 0x0c0c0602u), 0x05040100u);
-        const uint32_t l1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(yq[3], yq[2], 0x0c0c0501u),
-                                                  __builtin_amdgcn_perm(yq[1], yq[0], 0x0c0c0501u), 0x05040100u) ^ 0x80808080u;
-        const uint32_t l2w = __builtin_amdgcn_perm(__builtin_amdgcn_perm(yq[3], yq[2], 0x0c0c0400u),
-                                                   __builtin_amdgcn_perm(yq[1], yq[0], 0x0c0c0400u), 0x05040100u) ^ 0x80808080u;
-        uint32_t* wl = &sm.wl[wave][st][qd][0][0][0];
+        for (int i = 0; i < kStep; ++i) {
+          const uint32_t vm = sb.vm[i][gi];
+          const float vzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(vm), half_hi(vm)) : half_hi(vm);
+          if (tail) {
+            const bool ok = lg[st][i] != kNegInf;
+            zsum += ok ? pp[i] * vzero : 0.0f;
+            w[i] = ok ? pp[i] * half_lo(vm) : 0.0f;
+          } else {
+            zsum = __builtin_fmaf(pp[i], vzero, zsum);
+            w[i] = pp[i] * half_lo(vm);
+          }
+          wmax = fmaxf(wmax, w[i]);
+        }
+        z_run[st][gi] = __builtin_fmaf(z_run[st][gi], alpha[st], zsum);
+        wmax = row_max16(wmax);
+        int ew = 0;
+        frexpf(wmax, &ew);                 // wmax < 2^ew
+        ew = ew < -100 ? -100 : ew;        // such a step weighs < 2^-76 of the max
+        const float wsc = ldexpf(1.0f, 22 - ew);
+        sw[st][gi] = ldexpf(1.0f, ew - 22);
+        uint32_t y[kStep];
+#pragma unroll
+        for (int i = 0; i < kStep; ++i)
+          y[i] = static_cast<uint32_t>(static_cast<int32_t>(rintf(w[i] * wsc)) + 0x8080);
+        // limb bytes of the four pages, one word per limb: bytes 2 / 1 / 0 of y
+        const uint32_t l0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0602u),
+                                                  __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0602u), 0x05040100u);
+        const uint32_t l1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0501u),
+                                                  __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0501u), 0x05040100u) ^ 0x80808080u;
+        const uint32_t l2w = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0400u),
+                                                   __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0400u), 0x05040100u) ^ 0x80808080u;
+        uint32_t* wl = &sm.wl[wave][st][gi][0][0][0];
         wl[(0 * 4 + g) * 16 + n] = l0;
         wl[(1 * 4 + g) * 16 + n] = l1;
         wl[(2 * 4 + g) * 16 + n] = l2w;
@@ -464,61 +515,59 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
-    v4i apv[NS][kQuads];
+    v4i apv[NS][kNG];
 #pragma unroll
     for (int st = 0; st < NS; ++st)
 #pragma unroll
-      for (int qd = 0; qd < kQuads; ++qd)
-        apv[st][qd] = *reinterpret_cast<const v4i*>(&sm.wl[wave][st][qd][0][0][0] + wl_row);
+      for (int gi = 0; gi < kNG; ++gi)
+        apv[st][gi] = *reinterpret_cast<const v4i*>(&sm.wl[wave][st][gi][0][0][0] + wl_row);
 
     // V: per token r of the lane group, transpose across four pages so a
     // word holds the four pages' codes of one channel pair (4-bit: nibbles
     // split it) or of one channel (8-bit, then made signed).
-    uint32_t vt[kQuads][4][kVX][4];   // [quad][r][half][byte j]
+    uint32_t vt[4][kVX][4];   // [r][half][byte j]
 #pragma unroll
-    for (int qd = 0; qd < kQuads; ++qd)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int hh = 0; hh < kVX; ++hh) {
-          // 4-bit: dword r of the piece is token 4g+r; 8-bit: dwords
-          // 2(r&1)+hh of piece r>>1 are token 4g+r, channels 4hh..4hh+3
-          auto src = [&](int pg) {
-            return BITS == 8 ? sb.vx[4 * qd + pg][r >> 1][2 * (r & 1) + hh] : sb.vx[4 * qd + pg][0][r];
-          };
-          transpose_bytes4(src(0), src(1), src(2), src(3), vt[qd][r][hh]);
-        }
+      for (int hh = 0; hh < kVX; ++hh) {
+        // 4-bit: dword r of the piece is token 4g+r; 8-bit: dwords
+        // 2(r&1)+hh of piece r>>1 are token 4g+r, channels 4hh..4hh+3
+        auto src = [&](int pg) {
+          return BITS == 8 ? sb.vx[pg][r >> 1][2 * (r & 1) + hh] : sb.vx[pg][0][r];
+        };
+        transpose_bytes4(src(0), src(1), src(2), src(3), vt[r][hh]);
+      }
 #pragma unroll
     for (int tau = 0; tau < kNT; ++tau) {
-      v4i bv[kQuads];
+      v4i bv;
 #pragma unroll
-      for (int qd = 0; qd < kQuads; ++qd)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint32_t yv;
-          if constexpr (BITS == 8) {
-            if constexpr (D == 128) {   // channel 8n + tau
-              yv = vt[qd][r][tau >> 2][tau & 3];
-            } else {                    // channel 8(n&7) + 2tau + (n>>3)
-              const uint32_t* h4 = vt[qd][r][tau >> 1];
-              yv = (n >> 3) ? h4[2 * (tau & 1) + 1] : h4[2 * (tau & 1)];
-            }
-            yv ^= 0x80808080u;
-          } else {
-            if constexpr (D == 128) yv = (tau & 1) ? (vt[qd][r][0][tau >> 1] >> 4) : vt[qd][r][0][tau >> 1];
-            else yv = vt[qd][r][0][tau] >> (4 * (n >> 3));
-            yv &= kLowNibbles;
+      for (int r = 0; r < 4; ++r) {
+        uint32_t yv;
+        if constexpr (BITS == 8) {
+          if constexpr (D == 128) {   // channel 8n + tau
+            yv = vt[r][tau >> 2][tau & 3];
+          } else {                    // channel 8(n&7) + 2tau + (n>>3)
+            const uint32_t* h4 = vt[r][tau >> 1];
+            yv = (n >> 3) ? h4[2 * (tau & 1) + 1] : h4[2 * (tau & 1)];
           }
-          bv[qd][r] = static_cast<int32_t>(yv);
+          yv ^= 0x80808080u;
+        } else {   // nibble tau (D = 128) or 2tau + (n>>3) (D = 64) of the word
+          if constexpr (D == 128) yv = (tau & 1) ? (vt[r][0][tau >> 1] >> 4) : vt[r][0][tau >> 1];
+          else yv = vt[r][0][tau] >> (4 * (n >> 3));
+          yv &= kLowNibbles;
         }
+        bv[r] = static_cast<int32_t>(yv);
+      }
+      // the tile's group: its channels n + 16 tau (D = 128) or
+      // (n&7) + 16 tau + 8 (n>>3) (D = 64) all lie in group 16 tau / GS
+      constexpr int kTileGroupDiv = GS ? GS : 16 * kNT;
+      const int gi = 16 * tau / kTileGroupDiv;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        v4i c = mfma_i8(apv[st][0], bv[0], zero4);
-#pragma unroll
-        for (int qd = 1; qd < kQuads; ++qd) c = mfma_i8(apv[st][qd], bv[qd], c);
+        const v4i c = mfma_i8(apv[st][gi], bv, zero4);
         const float f = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f,
                                        static_cast<float>(c[2]));
-        acc[st][tau] = __builtin_fmaf(f, sw[st], acc[st][tau] * alpha[st]);
+        acc[st][tau] = __builtin_fmaf(f, sw[st][gi], acc[st][tau] * alpha[st]);
       }
     }
   };
@@ -550,10 +599,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     const float lt = row_sum16(l_run[st]);
-    const float zt = row_sum16(z_run[st]);
+    float zt[kNG];
+#pragma unroll
+    for (int gi = 0; gi < kNG; ++gi) zt[gi] = row_sum16(z_run[st][gi]);
     const int j = 4 * st + g;            // PV-layout head = row group
 #pragma unroll
-    for (int tau = 0; tau < kNT; ++tau) sm.u.merge.acc[wave][j][pv_channel<D>(n, tau)] = acc[st][tau] + zt;
+    for (int tau = 0; tau < kNT; ++tau)
+      sm.u.merge.acc[wave][j][pv_channel<D, GS>(n, tau)] = acc[st][tau] + zt[16 * tau / (GS ? GS : 16 * kNT)];
     if (n == 0) {
       sm.u.merge.m[wave][j] = m_run[st];
       sm.u.merge.l[wave][j] = lt;
@@ -612,32 +664,38 @@ __global__ __launch_bounds__(64 * kWaves) void decode_quant_kernel(DecodeArgs a)
   }
 }
 
-template <int D, int NS, int BITS>
+template <int D, int NS, int BITS, int GS>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.nsplit) * a.num_kv_heads * a.batch);
   if (a.in_bf16)
-    decode_quant_kernel<D, NS, true, BITS><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_quant_kernel<D, NS, true, BITS, GS><<<grid, 64 * kWaves, 0, s>>>(a);
   else
-    decode_quant_kernel<D, NS, false, BITS><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_quant_kernel<D, NS, false, BITS, GS><<<grid, 64 * kWaves, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int GS>
 hipError_t launch_ns(const DecodeArgs& a, hipStream_t s) {
   const int g = a.num_q_heads / a.num_kv_heads;
-  if (g <= 4) return launch_d<D, 1, BITS>(a, s);
-  if (g <= 8) return launch_d<D, 2, BITS>(a, s);
-  return launch_d<D, 4, BITS>(a, s);
+  if (g <= 4) return launch_d<D, 1, BITS, GS>(a, s);
+  if (g <= 8) return launch_d<D, 2, BITS, GS>(a, s);
+  return launch_d<D, 4, BITS, GS>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_int4(const DecodeArgs& a, hipStream_t s) {
-  return a.head_dim == 128 ? launch_ns<128, 4>(a, s) : launch_ns<64, 4>(a, s);
+  return a.head_dim == 128 ? launch_ns<128, 4, 0>(a, s) : launch_ns<64, 4, 0>(a, s);
 }
 
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t s) {
-  return a.head_dim == 128 ? launch_ns<128, 8>(a, s) : launch_ns<64, 8>(a, s);
+  return a.head_dim == 128 ? launch_ns<128, 8, 0>(a, s) : launch_ns<64, 8, 0>(a, s);
+}
+
+hipError_t launch_decode_int4g(const DecodeArgs& a, hipStream_t s) {
+  if (a.head_dim == 128)
+    return a.group == 32 ? launch_ns<128, 4, 32>(a, s) : launch_ns<128, 4, 64>(a, s);
+  return a.group == 32 ? launch_ns<64, 4, 32>(a, s) : launch_ns<64, 4, 64>(a, s);
 }
 
 }  // namespace kvq

@@ -20,6 +20,7 @@ struct AppendArgs {
   int32_t head_dim;
   int32_t block;             // Hadamard block (0 = none); unused by the bf16 pool
   int32_t in_bf16;           // 1: inputs are bf16, 0: fp16
+  int32_t group;             // channels per scale/zero pair (grouped INT4 pool only)
 };
 
 struct DecodeArgs {
@@ -56,6 +57,7 @@ struct DecodeArgs {
   int32_t part_slot0;
   int32_t force_partial;
   int32_t window_slot;
+  int32_t group;             // channels per scale/zero pair (grouped INT4 pool only)
 };
 
 // Split-K plan shared by the launch and the workspace query.
@@ -68,9 +70,11 @@ size_t workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, con
 
 hipError_t launch_append_int4(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_int8(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_int4g(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_int4(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_int4g(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t s);
 

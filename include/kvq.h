@@ -47,6 +47,16 @@
  *                        byte j = channel 8n+4h+j.
  *     [2*P*D, +4P)       K sidecar as in the INT4 pool; then the V sidecar.
  *
+ * Grouped INT4 page pool layout (one scale/zero per g channels, g = 32 or
+ *   64): [num_pages][num_kv_heads][slab], slab = P * (D + 8 * (D/g)) bytes:
+ *     [0, P*D/2)         K codes as in the INT4 pool.
+ *     [P*D/2, P*D)       V codes: 32-bit word n*P + t (n < D/8) holds channels
+ *                        n + (D/8) j, j = 0..7, of token t; byte j/2 holds
+ *                        nibble j (j even: bits 0..3).
+ *     [P*D, +4P*D/g)     K sidecar: token t, group i -> fp16 scale at byte
+ *                        4 (t*(D/g) + i), fp16 zero 2 bytes later.
+ *     then the V sidecar in the same form.
+ *
  * bf16 page pool layout: [num_pages][num_kv_heads][slab], slab = 4*P*D bytes:
  *     K: bf16 element t*D + c (token-major);
  *     V: bf16 element P*D + ((n*(P/4) + g)*8 + j)*4 + i for channel c = 8n + j
@@ -102,6 +112,19 @@ typedef struct {
   int32_t hadamard_block;   /* 16, 32, 64 or 128 (dividing head_dim); 0 = no rotation */
 } kvq_int8_cache;
 
+/* Grouped INT4 cache descriptor: the INT4 fields plus the group size; `pool`
+ * holds kvq_int4g_page_bytes(page_size, num_kv_heads, head_dim, group_size)
+ * * num_pages bytes. */
+typedef struct {
+  void*   pool;
+  int32_t num_pages;
+  int32_t page_size;        /* must be 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t hadamard_block;   /* 16, 32, 64 or 128 (dividing head_dim); 0 = no rotation */
+  int32_t group_size;       /* channels per scale/zero pair: 32 or 64 (<= head_dim) */
+} kvq_int4g_cache;
+
 /* bf16 cache descriptor (baseline).  `pool` 16-byte aligned,
  * kvq_bf16_page_bytes(...) * num_pages bytes. */
 typedef struct {
@@ -115,6 +138,8 @@ typedef struct {
 /* Bytes of one page (all KV heads) of each pool. */
 size_t kvq_int4_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
 size_t kvq_int8_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
+size_t kvq_int4g_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t group_size);
 size_t kvq_bf16_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
 
 /*
@@ -243,6 +268,25 @@ kvq_status kvq_decode_attn_int8(const kvq_int8_cache* cache, const void* q, kvq_
                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
                                 int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped INT4 variant: the quantizer of kvq_append_paged applied to each
+ * group of group_size consecutive channels of the rotated vector on its own
+ * (one fp16 scale and zero per group: the grouping along the inner dimension
+ * of "InnerQ", Abstract and Figure 1; with group_size = hadamard_block, one
+ * group per Hadamard block).  An outlier channel then only widens its own
+ * group's scale.  kvq_decode_attn_int4g is kvq_decode_attn over this pool
+ * (same arguments, accuracy and workspace size).  Codes and sidecars are
+ * bit-exact functions of the input.
+ */
+kvq_status kvq_append_paged_int4g(const kvq_int4g_cache* cache, const void* k, const void* v,
+                                  kvq_dtype dtype, int64_t token_stride,
+                                  const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+kvq_status kvq_decode_attn_int4g(const kvq_int4g_cache* cache, const void* q, kvq_dtype dtype,
+                                 int32_t num_q_heads, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                 int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* bf16 baseline of kvq_append_paged: copies K and V (fp16 input is rounded
  * to bf16, nearest even) into the bf16 pool.  Same argument rules. */

@@ -22,7 +22,7 @@ def _header_functions():
 
 def test_exports_every_declared_symbol():
     names = _header_functions()
-    assert len(names) == 15
+    assert len(names) == 18
     assert sorted(kvq.EXPORTED) == names
     L = kvq.lib()
     for name in names:
@@ -42,6 +42,9 @@ def test_page_bytes():
     assert kvq.kvq_bf16_page_bytes(16, 8, 128) == 8 * 8192
     assert kvq.kvq_int8_page_bytes(16, 8, 128) == 8 * 4224
     assert kvq.kvq_int8_page_bytes(16, 2, 64) == 2 * 2176
+    assert kvq.kvq_int4g_page_bytes(16, 8, 128, 64) == 8 * 16 * (128 + 16)
+    assert kvq.kvq_int4g_page_bytes(16, 8, 128, 32) == 8 * 16 * (128 + 32)
+    assert kvq.kvq_int4g_page_bytes(16, 8, 128, 48) == 0
 
 
 def _int4(num_pages=64, page=16, hkv=2, d=64, block=64, pool=FAKE):
@@ -122,6 +125,27 @@ def test_decode_workspace_too_small_by_one():
     assert _decode(_int4(), wsb=need - 1, fn="kvq_decode_attn_int8") == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
 
 
+def _grouped(group=64, d=128, block=64):
+    return kvq._GroupedDesc(FAKE, 64, 16, 2, d, block, group)
+
+
+@pytest.mark.parametrize("desc,status", [
+    (_grouped(group=16), kvq.KVQ_ERR_UNSUPPORTED),
+    (_grouped(group=128), kvq.KVQ_ERR_UNSUPPORTED),
+    (_grouped(group=64, d=64, block=128), kvq.KVQ_ERR_UNSUPPORTED),
+    (_grouped(group=0), kvq.KVQ_ERR_UNSUPPORTED),
+])
+def test_grouped_entry_points_validate(desc, status):
+    L = kvq.lib()
+    assert L.kvq_append_paged_int4g(C.byref(desc), FAKE, FAKE, 1, 256, FAKE, 4, None) == status
+    assert L.kvq_decode_attn_int4g(C.byref(desc), FAKE, 1, 8, FAKE, 256, FAKE, 4, 4096, 0.1, 0,
+                                   FAKE, FAKE, 1 << 30, None) == status
+    ok = _grouped()
+    assert L.kvq_append_paged_int4g(C.byref(ok), FAKE, FAKE, 1, 64, FAKE, 4, None) == kvq.KVQ_ERR_INVALID_ARGUMENT
+    assert L.kvq_decode_attn_int4g(C.byref(ok), FAKE, 1, 8, FAKE, 256, FAKE, 4, 4096, 0.1, 0,
+                                   FAKE, FAKE, 0, None) == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_binding_keeps_int4_and_int8_pools_apart():
     c8 = kvq.Int8Cache(2, 2, 64, 64, device="cpu")
     c4 = kvq.Int4Cache(2, 2, 64, 64, device="cpu")
@@ -131,6 +155,10 @@ def test_binding_keeps_int4_and_int8_pools_apart():
         kvq.kvq_append_paged(c8, None, None, None)
     with pytest.raises(TypeError):
         kvq.kvq_decode_attn_int8(c4, None, None, None, 0)
+    cg = kvq.Int4GroupedCache(2, 2, 128, 64, 32, device="cpu")
+    assert cg.pool.shape[1] == kvq.kvq_int4g_page_bytes(16, 2, 128, 32)
+    with pytest.raises(TypeError):
+        kvq.kvq_decode_attn(cg, None, None, None, 0)
 
 
 def test_decode_zero_batch_is_a_noop():
