@@ -90,6 +90,21 @@ def _declare(L):
     L.kvq_oracle_decode_int4g.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p, _i32,
                                           _p, _i32, C.c_double, _p, _p]
     L.kvq_oracle_decode_int4g.restype = _i32
+    L.kvq_oracle_e2m1_encode.argtypes = [C.c_float]
+    L.kvq_oracle_e2m1_encode.restype = C.c_uint8
+    L.kvq_oracle_e2m1_decode.argtypes = [C.c_uint8]
+    L.kvq_oracle_e2m1_decode.restype = C.c_double
+    L.kvq_oracle_quantize_mx.argtypes = [_p, _i32, _p, _p]
+    L.kvq_oracle_quantize_mx.restype = None
+    L.kvq_oracle_mxfp4_slab_bytes.argtypes = [_i32, _i32]
+    L.kvq_oracle_mxfp4_slab_bytes.restype = C.c_size_t
+    L.kvq_oracle_append_mxfp4.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _i32, _i64, _p, _i32]
+    L.kvq_oracle_append_mxfp4.restype = _i32
+    L.kvq_oracle_mxfp4_read.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]
+    L.kvq_oracle_mxfp4_read.restype = C.c_double
+    L.kvq_oracle_decode_mxfp4.argtypes = [_p, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p, _i32, _p,
+                                          _i32, C.c_double, _p, _p]
+    L.kvq_oracle_decode_mxfp4.restype = _i32
     L.kvq_oracle_int4_slab_bytes.argtypes = [_i32, _i32]
     L.kvq_oracle_int4_slab_bytes.restype = C.c_size_t
     L.kvq_oracle_bf16_slab_bytes.argtypes = [_i32, _i32]
@@ -168,6 +183,23 @@ def quantize(y: np.ndarray, bits: int = 4):
     return codes, int(s[0]), int(z[0])
 
 
+def e2m1_encode(v: float) -> int:
+    return int(lib().kvq_oracle_e2m1_encode(float(v)))
+
+
+def e2m1_decode(code: int) -> float:
+    return float(lib().kvq_oracle_e2m1_decode(int(code)))
+
+
+def quantize_mx(y: np.ndarray):
+    """One MXFP4 block: (codes uint8[n], E8M0 scale byte)."""
+    y = _c(y, np.float32)
+    codes = np.empty(y.shape[-1], np.uint8)
+    e = np.zeros(1, np.uint8)
+    lib().kvq_oracle_quantize_mx(_ptr(y), y.shape[-1], _ptr(codes), _ptr(e))
+    return codes, int(e[0])
+
+
 # ---- cache -----------------------------------------------------------------
 
 def int4_slab_bytes(page_size: int, head_dim: int) -> int:
@@ -184,6 +216,15 @@ def int4g_slab_bytes(page_size: int, head_dim: int, group: int) -> int:
 
 def new_int4g_pool(num_pages, num_kv_heads, head_dim, group, page_size=16, fill=0):
     n = num_pages * num_kv_heads * int4g_slab_bytes(page_size, head_dim, group)
+    return np.full(n, fill, np.uint8)
+
+
+def mxfp4_slab_bytes(page_size: int, head_dim: int) -> int:
+    return int(lib().kvq_oracle_mxfp4_slab_bytes(page_size, head_dim))
+
+
+def new_mxfp4_pool(num_pages, num_kv_heads, head_dim, page_size=16, fill=0):
+    n = num_pages * num_kv_heads * mxfp4_slab_bytes(page_size, head_dim)
     return np.full(n, fill, np.uint8)
 
 
@@ -255,6 +296,21 @@ def append_int4g(pool, num_pages, num_kv_heads, head_dim, block, group, k, v, dt
     return pool
 
 
+def append_mxfp4(pool, num_pages, num_kv_heads, head_dim, block, k, v, dtype, slot_mapping,
+                 page_size=16, token_stride=None):
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    sm = _c(slot_mapping, np.int32)
+    if token_stride is None:
+        token_stride = num_kv_heads * head_dim
+    rc = lib().kvq_oracle_append_mxfp4(_ptr(pool), num_pages, page_size, num_kv_heads, head_dim,
+                                       int(block), _ptr(k), _ptr(v), int(dtype), int(token_stride),
+                                       _ptr(sm), sm.shape[0])
+    if rc != 0:
+        raise ValueError("oracle append_mxfp4 rejected its arguments")
+    return pool
+
+
 def append_bf16(pool, num_pages, num_kv_heads, head_dim, k, v, dtype, slot_mapping,
                 page_size=16, token_stride=None):
     k = _c(k, np.uint16)
@@ -295,6 +351,14 @@ def int4g_read(pool, num_kv_heads, head_dim, group, page, head, off, kind, chann
     val = lib().kvq_oracle_int4g_read(_ptr(pool), page_size, num_kv_heads, head_dim, group, page,
                                       head, off, kind, channel, _ptr(code), _ptr(s), _ptr(z))
     return float(val), int(code[0]), int(s[0]), int(z[0])
+
+
+def mxfp4_read(pool, num_kv_heads, head_dim, page, head, off, kind, channel, page_size=16):
+    code = np.zeros(1, np.int32)
+    e = np.zeros(1, np.uint8)
+    val = lib().kvq_oracle_mxfp4_read(_ptr(pool), page_size, num_kv_heads, head_dim, page, head,
+                                      off, kind, channel, _ptr(code), _ptr(e))
+    return float(val), int(code[0]), int(e[0])
 
 
 def bf16_read(pool, num_kv_heads, head_dim, page, head, off, kind, channel, page_size=16):
@@ -350,6 +414,23 @@ def decode_int4g(pool, num_kv_heads, head_dim, block, group, q, dtype, block_tab
                                        None if mk is None else _ptr(mk), _ptr(out))
     if rc != 0:
         raise ValueError("oracle decode_int4g rejected its arguments")
+    return out
+
+
+def decode_mxfp4(pool, num_kv_heads, head_dim, block, q, dtype, block_table, seq_lens, sm_scale,
+                 page_size=16, mask=None):
+    q = _c(q, np.uint16)
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    batch, hq, d = q.shape
+    out = np.zeros((batch, hq, d), np.float64)
+    mk = None if mask is None else _c(mask, np.uint8)
+    rc = lib().kvq_oracle_decode_mxfp4(_ptr(pool), page_size, num_kv_heads, head_dim, int(block),
+                                       _ptr(q), int(dtype), hq, _ptr(bt), bt.shape[1], _ptr(sl),
+                                       batch, float(sm_scale), None if mk is None else _ptr(mk),
+                                       _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle decode_mxfp4 rejected its arguments")
     return out
 
 

@@ -136,6 +136,14 @@ size_t metag_byte(int p, int d, int group, int kind, int t, int gi) {
          (static_cast<size_t>(t) * ng + gi) * 4;
 }
 
+/* Byte address helpers of the MXFP4 slab (layout text in the header): codes
+ * as in the grouped INT4 slab, then one E8M0 byte per 32-channel block. */
+size_t mx_slab(int p, int d) { return static_cast<size_t>(p) * (d + d / 16); }
+size_t mx_scale_byte(int p, int d, int kind, int t, int blk) {
+  return static_cast<size_t>(p) * d + static_cast<size_t>(kind) * p * (d / 32) +
+         static_cast<size_t>(t) * (d / 32) + blk;
+}
+
 /* Byte address helpers of the INT8 slab (layout text in the header). */
 size_t k8_code_byte(int p, int d, int t, int c) { (void)p; return static_cast<size_t>(t) * d + c; }
 size_t v8_code_byte(int p, int d, int t, int c) {
@@ -264,9 +272,51 @@ void quantize_levels(const float* y, int32_t d, int levels, uint8_t* codes, uint
   *zero = zh;
 }
 
+/* The eight E2M1 magnitudes, in code order. */
+const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
 }  // namespace
 
 extern "C" {
+
+uint8_t kvq_oracle_e2m1_encode(float v) {
+  /* round |v| to the nearest E2M1 magnitude, ties to the even code (the one
+     with mantissa bit 0), saturating at 6; the sign bit only on nonzero codes */
+  const double a = std::fabs(static_cast<double>(v));
+  int best = 7;
+  if (a < 6.0) {
+    best = 0;
+    for (int c = 1; c < 8; ++c) {
+      const double dc = std::fabs(a - kE2M1[c]), db = std::fabs(a - kE2M1[best]);
+      if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+  }
+  return static_cast<uint8_t>(best == 0 ? 0 : ((v < 0.0f ? 8 : 0) | best));
+}
+
+double kvq_oracle_e2m1_decode(uint8_t code) {
+  const double m = kE2M1[code & 7];
+  return (code & 8) ? -m : m;
+}
+
+void kvq_oracle_quantize_mx(const float* y, int32_t n, uint8_t* codes, uint8_t* scale_e8m0) {
+  /* reading R12: shared exponent X = floor(log2(max|y|)) - 2 (2 = the largest
+     E2M1 exponent), 2^X stored as the E8M0 byte X + 127; elements y / 2^X
+     rounded to E2M1 */
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) amax = std::fmax(amax, std::fabs(y[i]));
+  int x = -127;
+  if (amax > 0.0f) {
+    int e = 0;
+    std::frexp(static_cast<double>(amax), &e);   /* amax in [2^(e-1), 2^e) */
+    x = (e - 1) - 2;
+    if (x < -127) x = -127;
+    if (x > 127) x = 127;
+  }
+  *scale_e8m0 = static_cast<uint8_t>(x + 127);
+  for (int i = 0; i < n; ++i)
+    codes[i] = kvq_oracle_e2m1_encode(static_cast<float>(std::ldexp(static_cast<double>(y[i]), -x)));
+}
 
 void kvq_oracle_quantize(const float* y, int32_t d, uint8_t* codes, uint16_t* scale,
                          uint16_t* zero) {
@@ -281,6 +331,7 @@ void kvq_oracle_quantize_int8(const float* y, int32_t d, uint8_t* codes, uint16_
 size_t kvq_oracle_int4_slab_bytes(int32_t page_size, int32_t head_dim) { return int4_slab(page_size, head_dim); }
 size_t kvq_oracle_bf16_slab_bytes(int32_t page_size, int32_t head_dim) { return bf16_slab(page_size, head_dim); }
 size_t kvq_oracle_int8_slab_bytes(int32_t page_size, int32_t head_dim) { return int8_slab(page_size, head_dim); }
+size_t kvq_oracle_mxfp4_slab_bytes(int32_t page_size, int32_t head_dim) { return mx_slab(page_size, head_dim); }
 size_t kvq_oracle_int4g_slab_bytes(int32_t page_size, int32_t head_dim, int32_t group) {
   return int4g_slab(page_size, head_dim, group);
 }
@@ -396,6 +447,41 @@ int32_t kvq_oracle_append_int4g(uint8_t* pool, int32_t num_pages, int32_t page_s
   return 0;
 }
 
+int32_t kvq_oracle_append_mxfp4(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                                const uint16_t* k, const uint16_t* v, int32_t dtype,
+                                int64_t token_stride, const int32_t* slot_mapping,
+                                int32_t num_tokens) {
+  const int p = page_size, d = head_dim, hkv = num_kv_heads;
+  if (!valid_block(block, d) || p % 4 != 0 || d % 32 != 0) return 1;
+  const size_t slab = mx_slab(p, d);
+  const int64_t capacity = static_cast<int64_t>(num_pages) * p;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int t = 0; t < num_tokens; ++t) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= capacity) continue;
+    const int page = static_cast<int>(slot / p), off = static_cast<int>(slot % p);
+    std::vector<float> x(d), y(d);
+    std::vector<uint8_t> codes(d);
+    for (int h = 0; h < hkv; ++h) {
+      uint8_t* s = pool + (static_cast<size_t>(page) * hkv + h) * slab;
+      for (int kind = 0; kind < 2; ++kind) {
+        const uint16_t* src = (kind == 0 ? k : v) + t * token_stride + static_cast<int64_t>(h) * d;
+        for (int c = 0; c < d; ++c) x[c] = widen(src[c], dtype);
+        kvq_oracle_rotate(x.data(), y.data(), d, block);
+        for (int b = 0; b < d / 32; ++b)
+          kvq_oracle_quantize_mx(&y[32 * b], 32, &codes[32 * b], &s[mx_scale_byte(p, d, kind, off, b)]);
+        for (int c = 0; c < d; ++c) {
+          size_t at = kind == 0 ? k_code_byte(p, d, off, c) : vg_code_byte(p, d, off, c);
+          bool high = kind == 0 ? (c % 2 == 1) : ((c / (d / 8)) % 2 == 1);
+          s[at] = static_cast<uint8_t>(high ? ((s[at] & 0x0f) | (codes[c] << 4)) : ((s[at] & 0xf0) | codes[c]));
+        }
+      }
+    }
+  }
+  return 0;
+}
+
 int32_t kvq_oracle_append_bf16(uint8_t* pool, int32_t num_pages, int32_t page_size,
                                int32_t num_kv_heads, int32_t head_dim,
                                const uint16_t* k, const uint16_t* v, int32_t dtype,
@@ -475,6 +561,20 @@ double kvq_oracle_int4g_read(const uint8_t* pool, int32_t page_size, int32_t num
          static_cast<double>(f16_to_f32(zh));
 }
 
+double kvq_oracle_mxfp4_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page, int32_t head, int32_t off, int32_t kind,
+                             int32_t channel, int32_t* code, uint8_t* scale_e8m0) {
+  const int p = page_size, d = head_dim;
+  const uint8_t* s = pool + (static_cast<size_t>(page) * num_kv_heads + head) * mx_slab(p, d);
+  int c;
+  if (kind == 0) c = (channel % 2 == 0) ? (s[k_code_byte(p, d, off, channel)] & 0xf) : (s[k_code_byte(p, d, off, channel)] >> 4);
+  else c = ((channel / (d / 8)) % 2 == 0) ? (s[vg_code_byte(p, d, off, channel)] & 0xf) : (s[vg_code_byte(p, d, off, channel)] >> 4);
+  const uint8_t e = s[mx_scale_byte(p, d, kind, off, channel / 32)];
+  if (code) *code = c;
+  if (scale_e8m0) *scale_e8m0 = e;
+  return std::ldexp(kvq_oracle_e2m1_decode(static_cast<uint8_t>(c)), static_cast<int>(e) - 127);
+}
+
 double kvq_oracle_bf16_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
                             int32_t head_dim, int32_t page, int32_t head, int32_t off,
                             int32_t kind, int32_t channel) {
@@ -521,6 +621,20 @@ int32_t kvq_oracle_decode_int4g(const uint8_t* pool, int32_t page_size, int32_t 
   auto read = [&](int page, int head, int off, int kind, int c) {
     return kvq_oracle_int4g_read(pool, page_size, num_kv_heads, head_dim, group, page, head, off,
                                  kind, c, nullptr, nullptr, nullptr);
+  };
+  return decode_paged(read, page_size, num_kv_heads, head_dim, block, q, dtype, num_q_heads,
+                      block_table, max_pages_per_seq, seq_lens, batch, sm_scale, mask, out);
+}
+
+int32_t kvq_oracle_decode_mxfp4(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block, const uint16_t* q, int32_t dtype,
+                                int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                double sm_scale, const uint8_t* mask, double* out) {
+  if (!valid_block(block, head_dim) || head_dim % 32 != 0) return 1;
+  auto read = [&](int page, int head, int off, int kind, int c) {
+    return kvq_oracle_mxfp4_read(pool, page_size, num_kv_heads, head_dim, page, head, off, kind, c,
+                                 nullptr, nullptr);
   };
   return decode_paged(read, page_size, num_kv_heads, head_dim, block, q, dtype, num_q_heads,
                       block_table, max_pages_per_seq, seq_lens, batch, sm_scale, mask, out);

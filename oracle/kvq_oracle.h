@@ -44,6 +44,14 @@
  *       and Figure 1 group along the inner dimension): one group per
  *       `group` consecutive channels of the rotated vector (normally the
  *       Hadamard block), each with its own fp16 scale and zero as in R2.
+ *   R12 MXFP4 variant ("BitDecoding-FP4", Abstract: native FP4 KV cache with
+ *       Hadamard rotation under token-wise scaling; the block format is the
+ *       OCP microscaling MXFP4 one): each 32 consecutive channels of the
+ *       rotated vector share an E8M0 scale 2^X with X = floor(log2 max|y|)
+ *       - 2 (-127 for an all-zero block), and each element is y / 2^X
+ *       rounded to the nearest E2M1 value {0, 0.5, 1, 1.5, 2, 3, 4, 6}
+ *       (ties to the code with mantissa bit 0, saturating at 6, sign only
+ *       on nonzero codes).  Decoded value = E2M1 value * 2^X.
  *   R7  softmax scale is a parameter (normally 1/sqrt(head_dim)); grouped
  *       query attention maps query head h to KV head h / (Hq / Hkv); an empty
  *       sequence gives a zero output; slot < 0 means "do not store".
@@ -77,6 +85,14 @@
  *     bytes [P*D, +4P*D/g)    K sidecar: token t, group i -> fp16 scale at
  *                             4(t*(D/g) + i), fp16 zero 2 bytes later.
  *     then the V sidecar in the same form.
+ *   MXFP4 pool (R12): [num_pages][num_kv_heads][slab], slab = P * (D + D/16)
+ *   bytes:
+ *     bytes [0, P*D)          K and V E2M1 codes, placed as the grouped INT4
+ *                             pool places its codes (nibble = sign << 3 |
+ *                             magnitude code).
+ *     bytes [P*D, +P*D/32)    K scales: byte t*(D/32) + i = E8M0 of token t,
+ *                             channels 32i .. 32i+31.
+ *     then the V scales in the same form.
  *   bf16 pool: [num_pages][num_kv_heads][slab], slab = 2 * P * D * 2 bytes:
  *     K: bf16 element index t*D + c (token-major);
  *     V: bf16 element index P*D + ((n*(P/4) + g)*8 + j)*4 + i for channel
@@ -119,11 +135,19 @@ void kvq_oracle_quantize(const float* y, int32_t d, uint8_t* codes,
 void kvq_oracle_quantize_int8(const float* y, int32_t d, uint8_t* codes,
                               uint16_t* scale, uint16_t* zero);
 
+/* E2M1 code of one value (R12) and the value of a code. */
+uint8_t kvq_oracle_e2m1_encode(float v);
+double  kvq_oracle_e2m1_decode(uint8_t code);
+
+/* One MXFP4 block of n values (R12): codes and the E8M0 scale byte. */
+void kvq_oracle_quantize_mx(const float* y, int32_t n, uint8_t* codes, uint8_t* scale_e8m0);
+
 /* ---- cache steps ----------------------------------------------------- */
 size_t kvq_oracle_int4_slab_bytes(int32_t page_size, int32_t head_dim);
 size_t kvq_oracle_bf16_slab_bytes(int32_t page_size, int32_t head_dim);
 size_t kvq_oracle_int8_slab_bytes(int32_t page_size, int32_t head_dim);
 size_t kvq_oracle_int4g_slab_bytes(int32_t page_size, int32_t head_dim, int32_t group);
+size_t kvq_oracle_mxfp4_slab_bytes(int32_t page_size, int32_t head_dim);
 
 /* Rotate + quantize + scatter num_tokens tokens into the INT4 pool.
  * k, v: [num_tokens][token_stride] 16-bit elements of type dtype, the first
@@ -148,6 +172,13 @@ int32_t kvq_oracle_append_int4g(uint8_t* pool, int32_t num_pages, int32_t page_s
                                 int32_t dtype, int64_t token_stride, const int32_t* slot_mapping,
                                 int32_t num_tokens);
 
+/* Rotate + MXFP4-quantize (R12) + scatter into the MXFP4 pool. */
+int32_t kvq_oracle_append_mxfp4(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                                const uint16_t* k, const uint16_t* v, int32_t dtype,
+                                int64_t token_stride, const int32_t* slot_mapping,
+                                int32_t num_tokens);
+
 /* Copy num_tokens tokens into the bf16 pool (fp16 input is rounded to bf16). */
 int32_t kvq_oracle_append_bf16(uint8_t* pool, int32_t num_pages, int32_t page_size,
                                int32_t num_kv_heads, int32_t head_dim,
@@ -170,6 +201,9 @@ double kvq_oracle_int4g_read(const uint8_t* pool, int32_t page_size, int32_t num
                              int32_t head_dim, int32_t group, int32_t page, int32_t head,
                              int32_t off, int32_t kind, int32_t channel, int32_t* code,
                              uint16_t* scale, uint16_t* zero);
+double kvq_oracle_mxfp4_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page, int32_t head, int32_t off,
+                             int32_t kind, int32_t channel, int32_t* code, uint8_t* scale_e8m0);
 double kvq_oracle_bf16_read(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
                             int32_t head_dim, int32_t page, int32_t head, int32_t off,
                             int32_t kind, int32_t channel);
@@ -198,6 +232,13 @@ int32_t kvq_oracle_decode_int8(const uint8_t* pool, int32_t page_size,
 int32_t kvq_oracle_decode_int4g(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block, int32_t group, const uint16_t* q,
                                 int32_t dtype, int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                double sm_scale, const uint8_t* mask, double* out);
+
+/* The same over the MXFP4 pool. */
+int32_t kvq_oracle_decode_mxfp4(const uint8_t* pool, int32_t page_size, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block, const uint16_t* q, int32_t dtype,
+                                int32_t num_q_heads, const int32_t* block_table,
                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
                                 double sm_scale, const uint8_t* mask, double* out);
 
