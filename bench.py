@@ -265,11 +265,15 @@ def variant_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes, kind)
     decode-only loop over two cache copies, and the prefill append of 32768
     ragged tokens over two input/cache sets.  kind "int8": token-wise INT8
     (D code bytes + 4 sidecar bytes per vector); "int4g64": INT4 with one
-    scale/zero per 64 channels (D/2 + 4 D/64 bytes)."""
+    scale/zero per 64 channels (D/2 + 4 D/64 bytes); "mxfp4": E2M1 codes with
+    one E8M0 byte per 32 channels (D/2 + D/32 bytes)."""
     w = db.w
     if kind == "int8":
         make = lambda nb: kvq.Int8Cache(nb, w.hkv, w.d, 64, "cuda")
         app_fn, dec_fn, vec_bytes = kvq.kvq_append_paged_int8, kvq.kvq_decode_attn_int8, w.d + 4
+    elif kind == "mxfp4":
+        make = lambda nb: kvq.MxFp4Cache(nb, w.hkv, w.d, 64, "cuda")
+        app_fn, dec_fn, vec_bytes = kvq.kvq_append_paged_mxfp4, kvq.kvq_decode_attn_mxfp4, w.d // 2 + w.d // 32
     else:
         make = lambda nb: kvq.Int4GroupedCache(nb, w.hkv, w.d, 64, 64, "cuda")
         app_fn, dec_fn, vec_bytes = kvq.kvq_append_paged_int4g, kvq.kvq_decode_attn_int4g, w.d // 2 + 4 * (w.d // 64)
@@ -548,6 +552,7 @@ def main(argv=None):
     windowed = windowed_rate(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes)
     int8 = variant_rates(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes, "int8")
     int4g = variant_rates(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes, "int4g64")
+    mxfp4 = variant_rates(torch, kvq, workloads, db, args.steps, variants["int4_block64"], dec_bytes, "mxfp4")
     db.int4 = db.int4[:1]
     torch.cuda.empty_cache()
     db.make_bf16()
@@ -606,6 +611,7 @@ def main(argv=None):
         "windowed_decode": windowed,
         "int8_kv": int8,
         "int4_groups64": int4g,
+        "mxfp4": mxfp4,
         "long_context_decode": long_ctx,
         "concurrency_sweep": conc,
         "bf16_kv": {"gb_s": round(bf16_bytes / (ms_bf16 * 1e-3) / 1e9, 1),

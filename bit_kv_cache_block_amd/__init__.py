@@ -8,7 +8,8 @@ call raises.
 
 Entry points carry the C names: ``kvq_append_paged``, ``kvq_decode_attn``,
 ``kvq_decode_attn_windowed``, ``kvq_append_paged_int8``, ``kvq_decode_attn_int8``,
-``kvq_append_paged_int4g``, ``kvq_decode_attn_int4g``,
+``kvq_append_paged_int4g``, ``kvq_decode_attn_int4g``, ``kvq_append_paged_mxfp4``,
+``kvq_decode_attn_mxfp4``,
 ``kvq_append_paged_bf16``, ``kvq_decode_attn_bf16``, the workspace and page
 size queries.
 """
@@ -31,7 +32,8 @@ PAGE_SIZE = 16
 EXPORTED = (
     "kvq_int4_page_bytes", "kvq_int8_page_bytes", "kvq_int4g_page_bytes", "kvq_bf16_page_bytes",
     "kvq_append_paged", "kvq_decode_attn", "kvq_append_paged_int8", "kvq_decode_attn_int8",
-    "kvq_append_paged_int4g", "kvq_decode_attn_int4g",
+    "kvq_append_paged_int4g", "kvq_decode_attn_int4g", "kvq_mxfp4_page_bytes",
+    "kvq_append_paged_mxfp4", "kvq_decode_attn_mxfp4",
     "kvq_decode_workspace_bytes", "kvq_append_paged_bf16", "kvq_decode_attn_bf16",
     "kvq_decode_attn_windowed", "kvq_decode_windowed_workspace_bytes",
     "kvq_status_string", "kvq_last_error", "kvq_abi_version",
@@ -44,7 +46,7 @@ class KvqError(RuntimeError):
         self.status = status
 
 
-class _QuantDesc(C.Structure):   # kvq_int4_cache and kvq_int8_cache
+class _QuantDesc(C.Structure):   # kvq_int4_cache, kvq_int8_cache and kvq_mxfp4_cache
     _fields_ = [("pool", C.c_void_p), ("num_pages", C.c_int32), ("page_size", C.c_int32),
                 ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("hadamard_block", C.c_int32)]
@@ -78,6 +80,8 @@ def lib() -> C.CDLL:
         L.kvq_int4_page_bytes.restype = sz
         L.kvq_int8_page_bytes.argtypes = [i32, i32, i32]
         L.kvq_int8_page_bytes.restype = sz
+        L.kvq_mxfp4_page_bytes.argtypes = [i32, i32, i32]
+        L.kvq_mxfp4_page_bytes.restype = sz
         L.kvq_int4g_page_bytes.argtypes = [i32, i32, i32, i32]
         L.kvq_int4g_page_bytes.restype = sz
         L.kvq_bf16_page_bytes.argtypes = [i32, i32, i32]
@@ -86,6 +90,8 @@ def lib() -> C.CDLL:
         L.kvq_append_paged.restype = i32
         L.kvq_append_paged_int8.argtypes = [C.POINTER(_QuantDesc), p, p, i32, i64, p, i32, p]
         L.kvq_append_paged_int8.restype = i32
+        L.kvq_append_paged_mxfp4.argtypes = [C.POINTER(_QuantDesc), p, p, i32, i64, p, i32, p]
+        L.kvq_append_paged_mxfp4.restype = i32
         L.kvq_append_paged_int4g.argtypes = [C.POINTER(_GroupedDesc), p, p, i32, i64, p, i32, p]
         L.kvq_append_paged_int4g.restype = i32
         L.kvq_append_paged_bf16.argtypes = [C.POINTER(_Bf16Desc), p, p, i32, i64, p, i32, p]
@@ -95,6 +101,8 @@ def lib() -> C.CDLL:
         L.kvq_decode_attn.restype = i32
         L.kvq_decode_attn_int8.argtypes = [C.POINTER(_QuantDesc), *dec]
         L.kvq_decode_attn_int8.restype = i32
+        L.kvq_decode_attn_mxfp4.argtypes = [C.POINTER(_QuantDesc), *dec]
+        L.kvq_decode_attn_mxfp4.restype = i32
         L.kvq_decode_attn_int4g.argtypes = [C.POINTER(_GroupedDesc), *dec]
         L.kvq_decode_attn_int4g.restype = i32
         L.kvq_decode_attn_bf16.argtypes = [C.POINTER(_Bf16Desc), *dec]
@@ -150,6 +158,10 @@ def kvq_int8_page_bytes(page_size: int, num_kv_heads: int, head_dim: int) -> int
     return int(lib().kvq_int8_page_bytes(page_size, num_kv_heads, head_dim))
 
 
+def kvq_mxfp4_page_bytes(page_size: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(lib().kvq_mxfp4_page_bytes(page_size, num_kv_heads, head_dim))
+
+
 def kvq_int4g_page_bytes(page_size: int, num_kv_heads: int, head_dim: int, group_size: int) -> int:
     return int(lib().kvq_int4g_page_bytes(page_size, num_kv_heads, head_dim, group_size))
 
@@ -187,6 +199,11 @@ class Int4Cache(_QuantCache):
 class Int8Cache(_QuantCache):
     """INT8 page pool (kvq_int8_cache)."""
     _page_bytes = staticmethod(kvq_int8_page_bytes)
+
+
+class MxFp4Cache(_QuantCache):
+    """MXFP4 page pool (kvq_mxfp4_cache)."""
+    _page_bytes = staticmethod(kvq_mxfp4_page_bytes)
 
 
 class Int4GroupedCache:
@@ -276,6 +293,13 @@ def kvq_append_paged_int4g(cache: Int4GroupedCache, k: torch.Tensor, v: torch.Te
             cache.head_dim, k, v, slot_mapping, stream)
 
 
+def kvq_append_paged_mxfp4(cache: MxFp4Cache, k: torch.Tensor, v: torch.Tensor,
+                           slot_mapping: torch.Tensor, stream=None) -> None:
+    """Rotate + MXFP4-quantize + scatter new tokens into the MXFP4 pool."""
+    _append(lib().kvq_append_paged_mxfp4, _need(cache, MxFp4Cache).desc(), cache.num_kv_heads,
+            cache.head_dim, k, v, slot_mapping, stream)
+
+
 def kvq_append_paged_bf16(cache: Bf16Cache, k: torch.Tensor, v: torch.Tensor,
                           slot_mapping: torch.Tensor, stream=None) -> None:
     _append(lib().kvq_append_paged_bf16, cache.desc(), cache.num_kv_heads, cache.head_dim, k, v,
@@ -340,6 +364,16 @@ def kvq_decode_attn_int4g(cache: Int4GroupedCache, q: torch.Tensor, block_table:
     return _decode(lib().kvq_decode_attn_int4g, _need(cache, Int4GroupedCache).desc(),
                    cache.num_kv_heads, cache.head_dim, q, block_table, seq_lens, max_seq_len,
                    sm_scale, out, workspace, num_splits, stream)
+
+
+def kvq_decode_attn_mxfp4(cache: MxFp4Cache, q: torch.Tensor, block_table: torch.Tensor,
+                          seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float | None = None,
+                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                          num_splits: int = 0, stream=None) -> torch.Tensor:
+    """Paged decode attention over the MXFP4 cache; returns fp32 [B][Hq][D]."""
+    return _decode(lib().kvq_decode_attn_mxfp4, _need(cache, MxFp4Cache).desc(), cache.num_kv_heads,
+                   cache.head_dim, q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace,
+                   num_splits, stream)
 
 
 def kvq_decode_attn_bf16(cache: Bf16Cache, q: torch.Tensor, block_table: torch.Tensor,

@@ -119,7 +119,7 @@ size_t workspace_bytes(int32_t batch, int32_t hq, int32_t d, const SplitPlan& p)
 
 namespace {
 
-enum class Pool { kInt4, kInt8, kInt4g, kBf16 };
+enum class Pool { kInt4, kInt8, kInt4g, kMxfp4, kBf16 };
 
 kvq_status check_block(int32_t b, int32_t d) {
   if (!(b == 0 || b == 16 || b == 32 || b == 64 || b == 128) || b > d)
@@ -171,6 +171,7 @@ kvq_status launch_decode(Pool kind, const void* pool, int32_t num_pages, int32_t
   hipError_t e = kind == Pool::kInt4    ? launch_decode_int4(a, s)
                  : kind == Pool::kInt8  ? launch_decode_int8(a, s)
                  : kind == Pool::kInt4g ? launch_decode_int4g(a, s)
+                 : kind == Pool::kMxfp4 ? launch_decode_mxfp4(a, s)
                                         : launch_decode_bf16(a, s);
   if (e == hipSuccess && plan.nsplit > 1) e = launch_reduce(a, s);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
@@ -199,6 +200,11 @@ size_t kvq_int8_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head
   return static_cast<size_t>(num_kv_heads) * page_size * (2 * head_dim + 8);
 }
 
+size_t kvq_mxfp4_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim) {
+  if (page_size <= 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 32 != 0) return 0;
+  return static_cast<size_t>(num_kv_heads) * page_size * (head_dim + head_dim / 16);
+}
+
 size_t kvq_int4g_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
                             int32_t group_size) {
   if (page_size <= 0 || num_kv_heads <= 0 || head_dim <= 0 || group_size <= 0 ||
@@ -217,6 +223,7 @@ namespace {
 int32_t group_of(const kvq_int4_cache*) { return 0; }
 int32_t group_of(const kvq_int8_cache*) { return 0; }
 int32_t group_of(const kvq_int4g_cache* c) { return c->group_size; }
+int32_t group_of(const kvq_mxfp4_cache*) { return 32; }
 
 template <class Cache>
 kvq_status check_quant_cache(const Cache* cache, Pool kind) {
@@ -259,6 +266,7 @@ kvq_status append_quant(const Cache* cache, Pool kind, const void* k, const void
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = kind == Pool::kInt8    ? launch_append_int8(a, s)
                        : kind == Pool::kInt4g ? launch_append_int4g(a, s)
+                       : kind == Pool::kMxfp4 ? launch_append_mxfp4(a, s)
                                               : launch_append_int4(a, s);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;
@@ -272,6 +280,8 @@ kvq_status decode_quant(const Cache* cache, Pool kind, const void* q, kvq_dtype 
                         size_t workspace_bytes_given, void* stream) {
   kvq_status st = check_quant_cache(cache, kind);
   if (st != KVQ_OK) return st;
+  if (kind == Pool::kMxfp4 && cache->head_dim != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "MXFP4 decode is built for head_dim 128 only");
   return launch_decode(kind, cache->pool, cache->num_pages, cache->num_kv_heads, cache->head_dim,
                        cache->hadamard_block, group_of(cache), q, dtype,
                        num_q_heads, block_table, max_pages_per_seq, seq_lens, batch, max_seq_len,
@@ -293,6 +303,12 @@ kvq_status kvq_append_paged_int8(const kvq_int8_cache* cache, const void* k, con
                                  kvq_dtype dtype, int64_t token_stride,
                                  const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
   return append_quant(cache, Pool::kInt8, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
+}
+
+kvq_status kvq_append_paged_mxfp4(const kvq_mxfp4_cache* cache, const void* k, const void* v,
+                                  kvq_dtype dtype, int64_t token_stride,
+                                  const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
+  return append_quant(cache, Pool::kMxfp4, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
 }
 
 kvq_status kvq_append_paged_int4g(const kvq_int4g_cache* cache, const void* k, const void* v,
@@ -343,6 +359,16 @@ kvq_status kvq_decode_attn_int8(const kvq_int8_cache* cache, const void* q, kvq_
                                 void* workspace, size_t workspace_bytes_given, void* stream) {
   return decode_quant(cache, Pool::kInt8, q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                       batch, max_seq_len, sm_scale, num_splits, out, workspace,
+                      workspace_bytes_given, stream);
+}
+
+kvq_status kvq_decode_attn_mxfp4(const kvq_mxfp4_cache* cache, const void* q, kvq_dtype dtype,
+                                 int32_t num_q_heads, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                 int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                                 void* workspace, size_t workspace_bytes_given, void* stream) {
+  return decode_quant(cache, Pool::kMxfp4, q, dtype, num_q_heads, block_table, max_pages_per_seq,
+                      seq_lens, batch, max_seq_len, sm_scale, num_splits, out, workspace,
                       workspace_bytes_given, stream);
 }
 

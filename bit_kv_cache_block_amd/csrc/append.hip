@@ -8,7 +8,10 @@
 // Quantization for KV Cache Compression in Large Language Models",
 // Abstract), and with one scale and zero per group of channels the grouped
 // INT4 variant (grouping along the inner dimension as in "InnerQ", Abstract
-// and Figure 1).  Also the bf16-cache baseline copy.
+// and Figure 1), and with E2M1 codes under one E8M0 power-of-two scale per 32
+// channels the MXFP4 variant ("BitDecoding-FP4", Abstract: an FP4 KV cache
+// with Hadamard rotation under token-wise scaling).  Also the bf16-cache
+// baseline copy.
 //
 // Bit-exactness: the quantizer's fp32 steps are done one rounding at a time
 // in the order the header of kvq.h states (this file is built with
@@ -53,11 +56,23 @@ __device__ __forceinline__ void widen8(u32x4 w, float* x) {
 // current unit is computed.  Lanes of consecutive tokens write consecutive
 // words of a page slab, so tokens that fill a page in order are stored as
 // contiguous runs.
-template <int D, int BLK, bool BF16, int BITS, int GS>
+// E2M1 code of v (nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 by magnitude; a tie
+// goes to the code with mantissa bit 0; 6 and above saturate; the sign bit
+// only on nonzero codes).  Each comparison is exact, and the strict / non-
+// strict choice at each midpoint is the tie rule.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                     (a >= 3.5f) + (a > 5.0f);
+  return m | ((v < 0.0f && m != 0u) ? 8u : 0u);
+}
+
+template <int D, int BLK, bool BF16, int BITS, int GS, bool MX>
 __global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void append_quant_kernel(AppendArgs a) {
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
   static_assert(GS == 0 || (BITS == 4 && (GS == 32 || GS == 64) && GS <= D), "groups of 32 or 64 channels, 4-bit");
+  static_assert(!MX || (BITS == 4 && GS == 32), "MXFP4: 4-bit codes in blocks of 32");
   constexpr int kLPV = D / kLaneElems;   // lanes per vector
   constexpr int kTok = 64 / kLPV;        // tokens per unit
   constexpr int kChunks = D / 8;         // 16-byte pieces per row
@@ -66,7 +81,8 @@ void append_quant_kernel(AppendArgs a) {
   constexpr int kNG = GS ? D / GS : 1;                 // scale/zero pairs per vector
   constexpr int kGL = GS ? kLaneElems / GS : 1;        // of them held by one lane
   constexpr int kGE = kLaneElems / kGL;                // elements of a lane's group
-  constexpr int kSlab = kPage * (2 * kCodeBytes + 8 * kNG);
+  constexpr int kSideBytes = MX ? kNG : 4 * kNG;       // sidecar bytes per vector
+  constexpr int kSlab = kPage * (2 * kCodeBytes + 2 * kSideBytes);
   constexpr int kWords = kLaneElems * BITS / 32;       // code words per lane
   constexpr float kTop = BITS == 4 ? 15.0f : 255.0f;   // largest code
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[kAppendThreads / 64][kTok * kRowBytes];
@@ -157,8 +173,11 @@ void append_quant_kernel(AppendArgs a) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) vw[(hf * 8 + m) * kPage + off] = u32x2{q.words[2 * m], q.words[2 * m + 1]};
     }
-    uint8_t* meta = slab + 2 * kPage * kCodeBytes + kind * 4 * kPage * kNG;
-    if constexpr (GS == 0) {
+    uint8_t* meta = slab + 2 * kPage * kCodeBytes + kind * kPage * kSideBytes;
+    if constexpr (MX) {   // E8M0 bytes of this lane's blocks (2hf, 2hf+1)
+      *reinterpret_cast<uint16_t*>(meta + off * kSideBytes + hf * kGL) =
+          static_cast<uint16_t>(q.meta[0] | (q.meta[1] << 8));
+    } else if constexpr (GS == 0) {
       if (hf == 0) *reinterpret_cast<uint32_t*>(meta + off * 4) = q.meta[0];
     } else if constexpr (kGL == 1) {   // group hf of token off
       *reinterpret_cast<uint32_t*>(meta + (off * kNG + hf) * 4) = q.meta[0];
@@ -255,10 +274,23 @@ void append_quant_kernel(AppendArgs a) {
       }
     }
 
-    // fp16 zero and scale, reciprocal (0 for a zero scale), per group
+    // fp16 zero and scale, reciprocal (0 for a zero scale), per group; for
+    // MXFP4 the shared exponent X = floor(log2 max|y|) - 2 of each block
     float zf[kGL], inv[kGL];
+    int xe[kGL];
 #pragma unroll
     for (int gl = 0; gl < kGL; ++gl) {
+      if constexpr (MX) {
+        const float amax = fmaxf(fabsf(mn[gl]), fabsf(mx[gl]));
+        int e = 0;
+        frexpf(amax, &e);                      // amax in [2^(e-1), 2^e)
+        int x = amax > 0.0f ? e - 3 : -127;
+        x = x < -127 ? -127 : (x > 127 ? 127 : x);
+        xe[gl] = x;
+        pend.meta[gl] = static_cast<uint32_t>(x + 127);
+        zf[gl] = inv[gl] = 0.0f;
+        continue;
+      }
       const float zero_f = mn[gl] + 0.0f;
       const float range = (mx[gl] - mn[gl]) + 0.0f;
       const float step = range / kTop;
@@ -276,9 +308,14 @@ void append_quant_kernel(AppendArgs a) {
     // any value in [0, 2^23); the clamp in that biased domain equals clamping
     // the rounded value; the code is then the low 4 (8) bits of the float.
     constexpr int kPer = 32 / BITS;   // codes per word
-    auto code = [&](int k) {
+    auto code = [&](int k) -> uint32_t {
       constexpr int gl_div = kGE;
       const int gl = k / gl_div;
+      if constexpr (MX) {   // y / 2^X (exact scaling), then E2M1
+        // (b = 32, 128 scaled x in place above; b = 16, 64 scale exactly here)
+        const float y = kExactNorm ? x[k] * sb : x[k];
+        return e2m1_code(ldexpf(y, -xe[gl]));
+      }
       const float d = kExactNorm ? __builtin_fmaf(x[k], sb, -zf[gl]) : x[k] - zf[gl];
       const float q = d * inv[gl];
       return f2u(__builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388608.0f + kTop));
@@ -384,28 +421,28 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
   }
 }
 
-template <int D, int BLK, int BITS, int GS>
+template <int D, int BLK, int BITS, int GS, bool MX = false>
 hipError_t launch_quant_d(const AppendArgs& a, hipStream_t s) {
   constexpr int kTok = D == 128 ? 32 : 64;
   const int64_t units = (static_cast<int64_t>(a.num_tokens) + kTok - 1) / kTok * a.num_kv_heads * 2;
   const int64_t blocks = (units + kAppendThreads / 64 - 1) / (kAppendThreads / 64);
   const dim3 grid(static_cast<unsigned>(blocks < kResidentBlocks ? blocks : kResidentBlocks));
   if (a.in_bf16)
-    append_quant_kernel<D, BLK, true, BITS, GS><<<grid, kAppendThreads, 0, s>>>(a);
+    append_quant_kernel<D, BLK, true, BITS, GS, MX><<<grid, kAppendThreads, 0, s>>>(a);
   else
-    append_quant_kernel<D, BLK, false, BITS, GS><<<grid, kAppendThreads, 0, s>>>(a);
+    append_quant_kernel<D, BLK, false, BITS, GS, MX><<<grid, kAppendThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int D, int BITS, int GS>
+template <int D, int BITS, int GS, bool MX = false>
 hipError_t launch_quant_block(const AppendArgs& a, hipStream_t s) {
   switch (a.block) {
-    case 0: return launch_quant_d<D, 0, BITS, GS>(a, s);
-    case 16: return launch_quant_d<D, 16, BITS, GS>(a, s);
-    case 32: return launch_quant_d<D, 32, BITS, GS>(a, s);
-    case 64: return launch_quant_d<D, 64, BITS, GS>(a, s);
+    case 0: return launch_quant_d<D, 0, BITS, GS, MX>(a, s);
+    case 16: return launch_quant_d<D, 16, BITS, GS, MX>(a, s);
+    case 32: return launch_quant_d<D, 32, BITS, GS, MX>(a, s);
+    case 64: return launch_quant_d<D, 64, BITS, GS, MX>(a, s);
     case 128:
-      if constexpr (D == 128) return launch_quant_d<D, 128, BITS, GS>(a, s);
+      if constexpr (D == 128) return launch_quant_d<D, 128, BITS, GS, MX>(a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -423,6 +460,11 @@ hipError_t launch_append_int4g(const AppendArgs& a, hipStream_t s) {
   if (a.head_dim == 128)
     return a.group == 32 ? launch_quant_block<128, 4, 32>(a, s) : launch_quant_block<128, 4, 64>(a, s);
   return a.group == 32 ? launch_quant_block<64, 4, 32>(a, s) : launch_quant_block<64, 4, 64>(a, s);
+}
+
+hipError_t launch_append_mxfp4(const AppendArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  return a.head_dim == 128 ? launch_quant_block<128, 4, 32, true>(a, s) : launch_quant_block<64, 4, 32, true>(a, s);
 }
 
 hipError_t launch_append_int8(const AppendArgs& a, hipStream_t s) {

@@ -48,49 +48,6 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaves = 4;
 constexpr int kStep = 4;   // pages per step
 
-__device__ __forceinline__ float half_lo(uint32_t w) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
-}
-__device__ __forceinline__ float half_hi(uint32_t w) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
-}
-
-// Limbs of the balanced base-256 split v = l0*2^16 + l1*2^8 + l2 with l1, l2
-// in [-128, 127] (|v| <= 2^22): with y = v + 0x8080, limb 0 is byte 2 of y,
-// limbs 1 and 2 are bytes 1 and 0 of y with the top bit flipped.  A lane
-// extracts its own limb `lam` (3 = the zero pad row) branch-free with the
-// per-lane shift / flip / keep constants below.
-struct LimbSel {
-  uint32_t shift, flip, keep;
-  __device__ explicit LimbSel(int lam)
-      : shift(lam < 3 ? 16u - 8u * lam : 0u), flip(lam == 1 || lam == 2 ? 0x80u : 0u),
-        keep(lam < 3 ? 0xFFu : 0u) {}
-  __device__ __forceinline__ uint32_t byte(int32_t v) const {
-    return ((static_cast<uint32_t>(v + 0x8080) >> shift) ^ flip) & keep;
-  }
-};
-
-// max / sum over the 16 lanes of a row, result in every lane of the row
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, dpp_f<kDppXor1>(x));
-  x = fmaxf(x, dpp_f<kDppXor2>(x));
-  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
-  return fmaxf(x, dpp_f<kDppRowMirror>(x));
-}
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp_f<kDppXor1>(x);
-  x += dpp_f<kDppXor2>(x);
-  x += dpp_f<kDppRowHalfMirror>(x);
-  return x + dpp_f<kDppRowMirror>(x);
-}
-__device__ __forceinline__ int32_t row_sum16_i(int32_t x) {
-  uint32_t u = static_cast<uint32_t>(x);
-  u += dpp_u<kDppXor1>(u);
-  u += dpp_u<kDppXor2>(u);
-  u += dpp_u<kDppRowHalfMirror>(u);
-  return static_cast<int32_t>(u + dpp_u<kDppRowMirror>(u));
-}
-
 // channel of k-slot (dword i, byte k) of the QK operand `op` for lane group g:
 // 4-bit codes split into low and high nibbles, 8-bit codes in byte order
 template <int D, int BITS>

@@ -1,0 +1,441 @@
+// Read path over the MXFP4 cache: split-K paged decode attention whose QK
+// product runs on gfx950's block-scaled FP4 matrix instruction
+// ("BitDecoding-FP4", Abstract: native FP4 KV decoding, the query heads of a
+// GQA group stacked into one product per page; the cache holds E2M1 codes
+// with one E8M0 power-of-two scale per 32 channels, the OCP microscaling
+// block format).
+//
+// Work split, page streaming, online softmax and merge follow the INT4
+// decode kernel.  Per page and per group of four query heads:
+//   QK:  v_mfma_scale_f32_16x16x128_f8f6f4 with B = the page's K codes as
+//        they are stored (E2M1, 32 channels per lane) and their E8M0 block
+//        scales applied by the hardware, and A = the rotated query as eight
+//        FP8 (E4M3) limbs: limb L of each element is the E4M3 rounding of
+//        what limbs 0..L-1 left, at 2^-4L of the block's scale, so the eight
+//        rows of a head sum to the query within 2^-32 of its block maximum.
+//        Limbs 0-3 and 4-7 are the rows of two products that accumulate into
+//        the same tile; each lane then adds its head's four rows.
+//   PV:  the V scales run along channels (one per token and 32 channels), a
+//        direction the instruction's per-column scales cannot carry, so PV
+//        stays on the int8 MFMA: E2M1 codes become exact int8 values (twice
+//        the E2M1 value, by table lookup), the weights w = p * 2^(E-128) of
+//        each 32-channel block go through LDS as 23-bit fixed-point limbs, and
+//        the V codes are laid out so that each 16-channel output tile lies in
+//        one block.
+#include "dev_common.hpp"
+#include "kvq_internal.hpp"
+
+#include <type_traits>
+
+namespace kvq {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kWaves = 4;
+constexpr int kStep = 4;       // pages per step
+constexpr int kD = 128;        // head_dim
+constexpr int kBlocks = kD / 32;
+constexpr int kLimbs = 8;      // FP8 limbs of the query
+
+template <int NS>
+struct alignas(16) MxSmem {
+  static constexpr int kGP = 4 * NS;
+  union {
+    uint8_t qb[kGP][kLimbs][kD];   // FP8 limbs of the rotated query, by channel
+    struct {
+      float acc[kWaves][kGP][kD];
+      float m[kWaves][kGP];
+      float l[kWaves][kGP];
+    } merge;
+  } u;
+  int32_t qexp[kGP][kBlocks];       // block exponent s0 of limb 0
+  uint32_t wl[kWaves][NS][kBlocks][4][4][16];   // [wave][set][block][limb][head][token]
+};
+
+struct MxStep {
+  u32x4 kx[kStep];
+  u32x4 vx[kStep];
+  uint32_t ks[kStep], vs[kStep];   // E8M0 bytes of the token's four blocks
+  bool pv[kStep];
+  bool all_ok;
+};
+
+// E2M1 codes (a nibble per byte) -> int8 twice their value: sign-magnitude
+// through two byte lookups and a per-byte select.
+__device__ __forceinline__ uint32_t e2m1x2_to_i8(uint32_t codes) {
+  const uint32_t mag = codes & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, mag);   // 0 1 2 3 4 6 8 12
+  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, mag);   // their negatives
+  const uint32_t sel = ((codes >> 3) & 0x01010101u) * 0xFFu;
+  return (neg & sel) | (pos & ~sel);
+}
+
+template <int NS, bool QBF16>
+__global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a) {
+  constexpr int D = kD;
+  constexpr int kSlab = kPage * (D + D / 16);
+  constexpr int kNT = D / 16;          // PV tiles
+  constexpr int kC = D / 16;           // channels per lane in a row of 16 lanes
+  __shared__ MxSmem<NS> sm;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4, n = lane & 15, hs = n >> 2, lam = n & 3;
+  // work item (split s, sequence b, KV head): KV head fastest, split slowest,
+  // last split first (as the INT4 decode)
+  const uint32_t wid = blockIdx.x;
+  const int kvh = static_cast<int>(wid % a.num_kv_heads);
+  const int b = static_cast<int>((wid / a.num_kv_heads) % a.batch);
+  const int s = a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
+
+  // ---- query: wave w < NS rotates heads 4w..4w+3, one per row of 16 lanes ----
+  const bool qwave = wave < NS;
+  const int qhead = 4 * wave + g;
+  uint32_t qraw[kC / 2];
+  if (qwave) {
+    const u32x4 t = *reinterpret_cast<const u32x4*>(a.q + (hq0 + min(qhead, G - 1)) * D + kC * n);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qraw[i] = t[i];
+  }
+  const int p0 = s * a.split_pages;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  int len = a.seq_lens[b];
+  len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+  const int npg = (len + kPage - 1) / kPage;
+  const int p1 = min(npg, p0 + a.split_pages);
+  if (p0 >= p1) {
+    if (a.nsplit == 1) {
+      for (int e = tid; e < G * D; e += 64 * kWaves) a.out[hq0 * D + e] = 0.0f;
+    }
+    return;
+  }
+  const int span = p1 - p0;
+  const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
+  const int pw0 = p0 + wave * per_wave;
+  const int pw1 = min(p1, pw0 + per_wave);
+  const uint8_t* pool_h = a.pool + static_cast<int64_t>(kvh) * kSlab;
+  const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kSlab;
+  // lane offsets in a page slab: K codes of token n, channels [32g, 32g+32);
+  // V codes of tokens 4g..4g+3, word n; the token's E8M0 bytes
+  const uint32_t k_off = n * (D / 2) + g * 16;
+  const uint32_t v_off = kPage * D / 2 + (n * kPage + 4 * g) * 4;
+  const uint32_t ks_off = kPage * D + n * kBlocks;
+  const uint32_t vs_off = ks_off + kPage * kBlocks;
+  int cb = pw0;
+  auto load_ids = [&](int first) {
+    const int pg = first + lane;
+    return pg < pw1 ? bt[pg] : -1;
+  };
+  int ids_cur = load_ids(cb), ids_next = load_ids(cb + 64);
+  auto page_id = [&](int pg) {
+    const int rel = pg - cb;
+    return rel < 64 ? __builtin_amdgcn_readlane(ids_cur, rel) : __builtin_amdgcn_readlane(ids_next, rel - 64);
+  };
+  auto load = [&](MxStep& sb, int p) {
+    sb.all_ok = true;
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) {
+      const int pg = p + i;
+      const int id = pg < pw1 ? page_id(pg) : -1;
+      sb.pv[i] = id >= 0 && id < a.num_pages;
+      sb.all_ok = sb.all_ok && sb.pv[i];
+      const uint8_t* sl = pool_h + static_cast<int64_t>(sb.pv[i] ? id : 0) * page_stride;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, kSlab);
+      sb.kx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, k_off, 0, kStreamOnce));
+      sb.vx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, 0, kStreamOnce));
+      sb.ks[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, ks_off, 0, kStreamOnce);
+      sb.vs[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs_off, 0, kStreamOnce);
+    }
+  };
+  float qv[kC];
+#pragma unroll
+  for (int k = 0; k < kC; ++k) {
+    const uint16_t u = qwave ? static_cast<uint16_t>(qraw[k / 2] >> (16 * (k & 1))) : 0;
+    const float x = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
+    qv[k] = (qwave && qhead < G) ? x : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < kC; ++k) asm volatile("" : : "v"(qv[k]) : "memory");
+  MxStep buf0;
+  if (pw0 < pw1) load(buf0, pw0);
+
+  for (int e = tid; e < kWaves * NS * kBlocks * 4 * 4 * 16; e += 64 * kWaves)
+    (&sm.wl[0][0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
+  if (qwave) {
+    float v[kC];
+#pragma unroll
+    for (int k = 0; k < kC; ++k) v[k] = qv[k];
+    if (a.block > 0) {
+      fwht_row<kC>(v, a.block, n);
+      const float sbn = block_norm(a.block);
+#pragma unroll
+      for (int k = 0; k < kC; ++k) v[k] *= sbn;
+    }
+    // block exponent: lanes 4i..4i+3 hold the 32 channels of block i
+    float am = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kC; ++k) am = fmaxf(am, fabsf(v[k]));
+    am = fmaxf(am, dpp_f<kDppXor1>(am));
+    am = fmaxf(am, dpp_f<kDppXor2>(am));
+    int ex = 0;
+    frexpf(am, &ex);                                  // am < 2^ex
+    int s0 = am > 0.0f ? ex - 8 : -99;                // limb 0 below 2^8 (E4M3 max 448)
+    s0 = s0 < -99 ? -99 : (s0 > 120 ? 120 : s0);      // limb 7's scale stays a valid E8M0
+    if ((n & 3) == 0) sm.qexp[qhead][n >> 2] = s0;
+    // FP8 limbs: t = q * 2^-s0; limb L = E4M3(t), t <- (t - limb L) * 16
+    float t[kC];
+#pragma unroll
+    for (int k = 0; k < kC; ++k) t[k] = ldexpf(v[k], -s0);
+#pragma unroll
+    for (int L = 0; L < kLimbs; ++L) {
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(t[4], t[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(t[6], t[7], hi, true);
+      *reinterpret_cast<u32x2*>(&sm.u.qb[qhead][L][kC * n]) = u32x2{static_cast<uint32_t>(lo), static_cast<uint32_t>(hi)};
+      const float back[kC] = {__builtin_amdgcn_cvt_f32_fp8(lo, 0), __builtin_amdgcn_cvt_f32_fp8(lo, 1),
+                              __builtin_amdgcn_cvt_f32_fp8(lo, 2), __builtin_amdgcn_cvt_f32_fp8(lo, 3),
+                              __builtin_amdgcn_cvt_f32_fp8(hi, 0), __builtin_amdgcn_cvt_f32_fp8(hi, 1),
+                              __builtin_amdgcn_cvt_f32_fp8(hi, 2), __builtin_amdgcn_cvt_f32_fp8(hi, 3)};
+#pragma unroll
+      for (int k = 0; k < kC; ++k) t[k] = (t[k] - back[k]) * 16.0f;
+    }
+  }
+  __syncthreads();
+
+  // A operands of QK: lane (g, r) is row r = (head r/4, limb 4ls + r%4) and
+  // holds channels 16g..16g+15 and 64+16g..64+16g+15; its scale byte is that
+  // row's E8M0 for channel block g
+  v8i aq[NS][2];
+  int sa[NS][2];
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int ls = 0; ls < 2; ++ls) {
+      const int head = 4 * st + hs, L = 4 * ls + lam;
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(&sm.u.qb[head][L][16 * g]);
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(&sm.u.qb[head][L][64 + 16 * g]);
+      aq[st][ls] = v8i{static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x0[2]), static_cast<int>(x0[3]),
+                       static_cast<int>(x1[0]), static_cast<int>(x1[1]), static_cast<int>(x1[2]), static_cast<int>(x1[3])};
+      sa[st][ls] = sm.qexp[head][g] - 4 * L + 127;
+    }
+
+  float m_run[NS], l_run[NS], acc[NS][kNT];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    m_run[st] = kNegInf;
+    l_run[st] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) acc[st][t] = 0.0f;
+  }
+  const v4i zero4 = {0, 0, 0, 0};
+  const v4f zero4f = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int wl_row = (lam * 4 + hs) * 16 + 4 * g;
+
+  auto compute = [&](const MxStep& sb, int p, auto mask_tag) {
+    constexpr bool tail = decltype(mask_tag)::value;
+    float lg[NS][kStep];
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) {
+      const v8i bk = v8i{static_cast<int>(sb.kx[i][0]), static_cast<int>(sb.kx[i][1]),
+                         static_cast<int>(sb.kx[i][2]), static_cast<int>(sb.kx[i][3]), 0, 0, 0, 0};
+      const int sbk = static_cast<int>((sb.ks[i] >> (8 * g)) & 0xFFu);   // token n, block g
+      const int tok = (p + i) * kPage + n;
+      const bool ok = !tail || (sb.pv[i] && tok < len);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[st][0], bk, zero4f, 0, 4, 0, sa[st][0], 0, sbk);
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[st][1], bk, c, 0, 4, 0, sa[st][1], 0, sbk);
+        const float dot = (c[0] + c[1]) + (c[2] + c[3]);
+        lg[st][i] = ok ? a.sm_log2 * dot : kNegInf;
+      }
+    }
+
+    float alpha[NS], sw[NS][kBlocks];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      float mc = lg[st][0];
+#pragma unroll
+      for (int i = 1; i < kStep; ++i) mc = fmaxf(mc, lg[st][i]);
+      mc = row_max16(mc);
+      const float mnew = fmaxf(m_run[st], mc);
+      const float muse = mnew == kNegInf ? 0.0f : mnew;
+      alpha[st] = exp2f(m_run[st] - muse);
+      m_run[st] = mnew;
+      float pp[kStep], psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kStep; ++i) {
+        pp[i] = tail && lg[st][i] == kNegInf ? 0.0f : exp2f(lg[st][i] - muse);
+        psum += pp[i];
+      }
+      l_run[st] = __builtin_fmaf(l_run[st], alpha[st], psum);
+#pragma unroll
+      for (int gi = 0; gi < kBlocks; ++gi) {
+        // w = p * 2^(E - 128): the int8 V operand is twice the E2M1 value
+        float w[kStep], wmax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kStep; ++i) {
+          const int e = static_cast<int>((sb.vs[i] >> (8 * gi)) & 0xFFu);
+          w[i] = ldexpf(pp[i], e - 128);
+          wmax = fmaxf(wmax, w[i]);
+        }
+        wmax = row_max16(wmax);
+        int ew = 0;
+        frexpf(wmax, &ew);
+        ew = ew < -100 ? -100 : ew;
+        const float wsc = ldexpf(1.0f, 22 - ew);
+        sw[st][gi] = ldexpf(1.0f, ew - 22);
+        uint32_t y[kStep];
+#pragma unroll
+        for (int i = 0; i < kStep; ++i)
+          y[i] = static_cast<uint32_t>(static_cast<int32_t>(rintf(w[i] * wsc)) + 0x8080);
+        const uint32_t l0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0602u),
+                                                  __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0602u), 0x05040100u);
+        const uint32_t l1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0501u),
+                                                  __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0501u), 0x05040100u) ^ 0x80808080u;
+        const uint32_t l2w = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0400u),
+                                                   __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0400u), 0x05040100u) ^ 0x80808080u;
+        uint32_t* wl = &sm.wl[wave][st][gi][0][0][0];
+        wl[(0 * 4 + g) * 16 + n] = l0;
+        wl[(1 * 4 + g) * 16 + n] = l1;
+        wl[(2 * 4 + g) * 16 + n] = l2w;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    v4i apv[NS][kBlocks];
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int gi = 0; gi < kBlocks; ++gi)
+        apv[st][gi] = *reinterpret_cast<const v4i*>(&sm.wl[wave][st][gi][0][0][0] + wl_row);
+
+    // V: per token r of the lane group, the four pages' codes of one channel
+    // pair in a word (nibble tau is channel n + 16 tau)
+    uint32_t vt[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) transpose_bytes4(sb.vx[0][r], sb.vx[1][r], sb.vx[2][r], sb.vx[3][r], vt[r]);
+#pragma unroll
+    for (int tau = 0; tau < kNT; ++tau) {
+      v4i bv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t nib = ((tau & 1) ? (vt[r][tau >> 1] >> 4) : vt[r][tau >> 1]) & kLowNibbles;
+        bv[r] = static_cast<int32_t>(e2m1x2_to_i8(nib));
+      }
+      const int gi = tau >> 1;   // channels n + 16 tau lie in block tau / 2
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const v4i c = mfma_i8(apv[st][gi], bv, zero4);
+        const float f = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f, static_cast<float>(c[2]));
+        acc[st][tau] = __builtin_fmaf(f, sw[st][gi], acc[st][tau] * alpha[st]);
+      }
+    }
+  };
+
+  auto step = [&](const MxStep& sb, int p) {
+    if (!sb.all_ok || (p + kStep) * kPage > len)
+      compute(sb, p, std::true_type{});
+    else
+      compute(sb, p, std::false_type{});
+  };
+  for (int p = pw0; p < pw1; p += kStep) {
+    step(buf0, p);
+    if (p + kStep >= pw1) break;
+    if (p + kStep >= cb + 64) {
+      cb += 64;
+      ids_cur = ids_next;
+      ids_next = load_ids(cb + 64);
+    }
+    load(buf0, p + kStep);
+  }
+
+  // ---- merge the four waves, rotate back, store ------------------------------
+  __syncthreads();   // the query limbs are reused below
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const float lt = row_sum16(l_run[st]);
+    const int j = 4 * st + g;
+#pragma unroll
+    for (int tau = 0; tau < kNT; ++tau) sm.u.merge.acc[wave][j][n + 16 * tau] = acc[st][tau];
+    if (n == 0) {
+      sm.u.merge.m[wave][j] = m_run[st];
+      sm.u.merge.l[wave][j] = lt;
+    }
+  }
+  __syncthreads();
+  if (qwave) {
+    const int j = qhead;
+    float mstar = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, sm.u.merge.m[w][j]);
+    const float muse = mstar == kNegInf ? 0.0f : mstar;
+    float f[kWaves], lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      f[w] = exp2f(sm.u.merge.m[w][j] - muse);
+      lsum = __builtin_fmaf(sm.u.merge.l[w][j], f[w], lsum);
+    }
+    float o[kC];
+#pragma unroll
+    for (int k = 0; k < kC; ++k) o[k] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int k = 0; k < kC; k += 4) {
+        const v4f x = *reinterpret_cast<const v4f*>(&sm.u.merge.acc[w][j][kC * n + k]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[k + i] = __builtin_fmaf(x[i], f[w], o[k + i]);
+      }
+    float scale = 1.0f;
+    if (a.block > 0) {
+      fwht_row<kC>(o, a.block, n);
+      scale = block_norm(a.block);
+    }
+    if (a.nsplit == 1) {
+      scale *= lsum > 0.0f ? 1.0f / lsum : 0.0f;
+      if (j < G) {
+        float* dst = a.out + (hq0 + j) * D + kC * n;
+#pragma unroll
+        for (int k = 0; k < kC; k += 4)
+          *reinterpret_cast<v4f*>(dst + k) = v4f{o[k] * scale, o[k + 1] * scale, o[k + 2] * scale, o[k + 3] * scale};
+      }
+    } else if (j < G) {
+      const int64_t idx = (hq0 + j) * a.part_stride + a.part_slot0 + s;
+      float* dst = a.part_acc + idx * D + kC * n;
+#pragma unroll
+      for (int k = 0; k < kC; k += 4)
+        *reinterpret_cast<v4f*>(dst + k) = v4f{o[k] * scale, o[k + 1] * scale, o[k + 2] * scale, o[k + 3] * scale};
+      if (n == 0) {
+        a.part_ml[idx * 2 + 0] = mstar;
+        a.part_ml[idx * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+template <int NS>
+hipError_t launch_mx(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.nsplit) * a.num_kv_heads * a.batch);
+  if (a.in_bf16)
+    decode_mxfp4_kernel<NS, true><<<grid, 64 * kWaves, 0, s>>>(a);
+  else
+    decode_mxfp4_kernel<NS, false><<<grid, 64 * kWaves, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mxfp4(const DecodeArgs& a, hipStream_t s) {
+  const int g = a.num_q_heads / a.num_kv_heads;
+  if (g <= 4) return launch_mx<1>(a, s);
+  if (g <= 8) return launch_mx<2>(a, s);
+  return launch_mx<4>(a, s);
+}
+
+}  // namespace kvq

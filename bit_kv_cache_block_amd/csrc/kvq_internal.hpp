@@ -71,10 +71,12 @@ size_t workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, con
 hipError_t launch_append_int4(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_int8(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_int4g(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_mxfp4(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_int4(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_int4g(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_mxfp4(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t s);
 

@@ -57,6 +57,16 @@
  *                        4 (t*(D/g) + i), fp16 zero 2 bytes later.
  *     then the V sidecar in the same form.
  *
+ * MXFP4 page pool layout: [num_pages][num_kv_heads][slab], slab = P * (D + D/16)
+ *   bytes (2176 at D = 128):
+ *     [0, P*D)           K and V E2M1 codes placed as in the grouped INT4 pool
+ *                        (nibble = sign << 3 | magnitude code 0..7 for
+ *                        0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ *     [P*D, +P*D/32)     K scales: byte t*(D/32) + i is the E8M0 exponent
+ *                        (2^(byte-127)) of token t, channels 32i .. 32i+31.
+ *     then the V scales in the same form.
+ *   A decoded element is E2M1 value * 2^(byte-127), in the rotated basis.
+ *
  * bf16 page pool layout: [num_pages][num_kv_heads][slab], slab = 4*P*D bytes:
  *     K: bf16 element t*D + c (token-major);
  *     V: bf16 element P*D + ((n*(P/4) + g)*8 + j)*4 + i for channel c = 8n + j
@@ -125,6 +135,17 @@ typedef struct {
   int32_t group_size;       /* channels per scale/zero pair: 32 or 64 (<= head_dim) */
 } kvq_int4g_cache;
 
+/* MXFP4 cache descriptor: the INT4 fields; `pool` holds
+ * kvq_mxfp4_page_bytes(page_size, num_kv_heads, head_dim) * num_pages bytes. */
+typedef struct {
+  void*   pool;
+  int32_t num_pages;
+  int32_t page_size;        /* must be 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;         /* 64 or 128 (decode: 128) */
+  int32_t hadamard_block;   /* 16, 32, 64 or 128 (dividing head_dim); 0 = no rotation */
+} kvq_mxfp4_cache;
+
 /* bf16 cache descriptor (baseline).  `pool` 16-byte aligned,
  * kvq_bf16_page_bytes(...) * num_pages bytes. */
 typedef struct {
@@ -140,6 +161,7 @@ size_t kvq_int4_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head
 size_t kvq_int8_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
 size_t kvq_int4g_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
                             int32_t group_size);
+size_t kvq_mxfp4_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
 size_t kvq_bf16_page_bytes(int32_t page_size, int32_t num_kv_heads, int32_t head_dim);
 
 /*
@@ -283,6 +305,28 @@ kvq_status kvq_append_paged_int4g(const kvq_int4g_cache* cache, const void* k, c
                                   kvq_dtype dtype, int64_t token_stride,
                                   const int32_t* slot_mapping, int32_t num_tokens, void* stream);
 kvq_status kvq_decode_attn_int4g(const kvq_int4g_cache* cache, const void* q, kvq_dtype dtype,
+                                 int32_t num_q_heads, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                 int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * MXFP4 variant ("BitDecoding-FP4", Abstract: an FP4 KV cache with Hadamard
+ * rotation under token-wise scaling; OCP microscaling block format): after the
+ * optional block Hadamard rotation, each 32 channels of a vector share the
+ * E8M0 scale 2^X with X = floor(log2(max |y|)) - 2 (-127 for a zero block),
+ * and each element is y / 2^X rounded to the nearest E2M1 value (a tie goes
+ * to the code with mantissa bit 0; 6 and above saturate to 6; the sign bit
+ * only on nonzero codes).  Same bytes per token as INT4.  Codes and scales
+ * are bit-exact functions of the input.  kvq_decode_attn_mxfp4 is
+ * kvq_decode_attn over this pool (head_dim 128; same arguments, accuracy and
+ * workspace size); its QK product runs on the block-scaled FP4 matrix
+ * instruction of gfx950.
+ */
+kvq_status kvq_append_paged_mxfp4(const kvq_mxfp4_cache* cache, const void* k, const void* v,
+                                  kvq_dtype dtype, int64_t token_stride,
+                                  const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+kvq_status kvq_decode_attn_mxfp4(const kvq_mxfp4_cache* cache, const void* q, kvq_dtype dtype,
                                  int32_t num_q_heads, const int32_t* block_table,
                                  int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
                                  int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,

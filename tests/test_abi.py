@@ -22,7 +22,7 @@ def _header_functions():
 
 def test_exports_every_declared_symbol():
     names = _header_functions()
-    assert len(names) == 18
+    assert len(names) == 21
     assert sorted(kvq.EXPORTED) == names
     L = kvq.lib()
     for name in names:
@@ -45,6 +45,8 @@ def test_page_bytes():
     assert kvq.kvq_int4g_page_bytes(16, 8, 128, 64) == 8 * 16 * (128 + 16)
     assert kvq.kvq_int4g_page_bytes(16, 8, 128, 32) == 8 * 16 * (128 + 32)
     assert kvq.kvq_int4g_page_bytes(16, 8, 128, 48) == 0
+    assert kvq.kvq_mxfp4_page_bytes(16, 8, 128) == 8 * 2176
+    assert kvq.kvq_mxfp4_page_bytes(16, 2, 64) == 2 * 16 * 68
 
 
 def _int4(num_pages=64, page=16, hkv=2, d=64, block=64, pool=FAKE):
@@ -146,6 +148,20 @@ def test_grouped_entry_points_validate(desc, status):
                                    FAKE, FAKE, 0, None) == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_mxfp4_entry_points_validate():
+    L = kvq.lib()
+    d64 = kvq._QuantDesc(FAKE, 64, 16, 2, 64, 64)
+    assert L.kvq_decode_attn_mxfp4(C.byref(d64), FAKE, 1, 8, FAKE, 256, FAKE, 4, 4096, 0.1, 0,
+                                   FAKE, FAKE, 1 << 30, None) == kvq.KVQ_ERR_UNSUPPORTED
+    bad = kvq._QuantDesc(FAKE, 64, 16, 2, 128, 8)
+    assert L.kvq_append_paged_mxfp4(C.byref(bad), FAKE, FAKE, 1, 256, FAKE, 4, None) == kvq.KVQ_ERR_UNSUPPORTED
+    ok = kvq._QuantDesc(FAKE, 64, 16, 2, 128, 64)
+    assert L.kvq_append_paged_mxfp4(C.byref(ok), FAKE, FAKE, 1, 128, FAKE, 4, None) == kvq.KVQ_ERR_INVALID_ARGUMENT
+    assert L.kvq_decode_attn_mxfp4(C.byref(ok), FAKE, 1, 8, FAKE, 256, FAKE, 4, 4096, 0.1, 0,
+                                   FAKE, FAKE, 0, None) == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
+    assert L.kvq_append_paged_mxfp4(C.byref(ok), 0, 0, 1, 256, 0, 0, None) == kvq.KVQ_OK
+
+
 def test_binding_keeps_int4_and_int8_pools_apart():
     c8 = kvq.Int8Cache(2, 2, 64, 64, device="cpu")
     c4 = kvq.Int4Cache(2, 2, 64, 64, device="cpu")
@@ -159,6 +175,10 @@ def test_binding_keeps_int4_and_int8_pools_apart():
     assert cg.pool.shape[1] == kvq.kvq_int4g_page_bytes(16, 2, 128, 32)
     with pytest.raises(TypeError):
         kvq.kvq_decode_attn(cg, None, None, None, 0)
+    cm = kvq.MxFp4Cache(2, 2, 128, 64, device="cpu")
+    assert cm.pool.shape[1] == kvq.kvq_mxfp4_page_bytes(16, 2, 128)
+    with pytest.raises(TypeError):
+        kvq.kvq_append_paged(cm, None, None, None)
 
 
 def test_decode_zero_batch_is_a_noop():
