@@ -261,6 +261,12 @@ def test_full_size_llama_layer_sampled():
     want = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table,
                               w.seq_lens, w.sm_scale, mask=mask)
     assert_close(out.cpu().numpy().astype(np.float64)[sample], want[sample], "full llama sampled")
+    # two splits: 1024 workgroups, the large-grid build of the kernel
+    out2 = kvq.kvq_decode_attn(cache, w.q, torch.from_numpy(w.block_table).to(DEV),
+                               torch.from_numpy(w.seq_lens).to(DEV), w.max_seq_len, w.sm_scale,
+                               num_splits=2)
+    torch.cuda.synchronize()
+    assert_close(out2.cpu().numpy().astype(np.float64)[sample], want[sample], "full llama sampled S2")
 
 
 def test_decode_ignores_stale_bytes_in_unwritten_slots():
