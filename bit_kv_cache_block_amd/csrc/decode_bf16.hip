@@ -90,6 +90,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) 
 
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+  const int len_full = len;
   if (a.len_cap > 0 && len > a.len_cap) len = a.len_cap;   // window pass: the window's tokens
   const int npg = (len + kPage - 1) / kPage;
   const int p0 = s * a.split_pages;
@@ -288,7 +289,30 @@ __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) 
       lsum = __builtin_fmaf(sm.u.merge.l[w][j], f, lsum);
       osum = __builtin_fmaf(sm.u.merge.acc[w][j][c], f, osum);
     }
-    if (a.nsplit == 1 && !a.force_partial) {
+    if (a.fin_splits > 0) {
+      // finish the windowed call: merge the INT4 passes' partials (already in
+      // the original basis) of this row with the window's share
+      int lo, hi;
+      int4_token_range(len_full, a.fin_skip_first, a.fin_skip_last, lo, hi);
+      const int npg4 = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
+      const int64_t row = (hq0 + j) * a.part_stride;
+      float mall = mstar;
+      for (int sp = 0; sp < a.fin_splits; ++sp) {
+        const bool ok = hi > lo && max(sp * a.fin_split_pages, pfirst) < min(npg4, (sp + 1) * a.fin_split_pages);
+        if (ok) mall = fmaxf(mall, a.part_ml[(row + sp) * 2]);
+      }
+      const float mu = mall == kNegInf ? 0.0f : mall;
+      const float fw = exp2f(mstar - mu);
+      float lt = lsum * fw, ot = osum * fw;
+      for (int sp = 0; sp < a.fin_splits; ++sp) {
+        const bool ok = hi > lo && max(sp * a.fin_split_pages, pfirst) < min(npg4, (sp + 1) * a.fin_split_pages);
+        if (!ok) continue;
+        const float f = exp2f(a.part_ml[(row + sp) * 2] - mu);
+        lt = __builtin_fmaf(a.part_ml[(row + sp) * 2 + 1], f, lt);
+        ot = __builtin_fmaf(a.part_acc[(row + sp) * D + c], f, ot);
+      }
+      a.out[(hq0 + j) * D + c] = lt > 0.0f ? ot / lt : 0.0f;
+    } else if (a.nsplit == 1 && !a.force_partial) {
       a.out[(hq0 + j) * D + c] = lsum > 0.0f ? osum / lsum : 0.0f;
     } else {
       const int64_t idx = (hq0 + j) * a.part_stride + a.part_slot0 + s;

@@ -21,6 +21,14 @@ struct AppendArgs {
   int32_t block;             // Hadamard block (0 = none); unused by the bf16 pool
   int32_t in_bf16;           // 1: inputs are bf16, 0: fp16
   int32_t group;             // channels per scale/zero pair (grouped INT4 pool only)
+  // Window pass that also finishes the call (fin_splits > 0): after its own
+  // share it merges the fin_splits INT4 partials of each (sequence, query
+  // head), whose pass skipped fin_skip_first / fin_skip_last tokens in splits
+  // of fin_split_pages pages, and writes the normalised output.
+  int32_t fin_splits;
+  int32_t fin_split_pages;
+  int32_t fin_skip_first;
+  int32_t fin_skip_last;
 };
 
 struct DecodeArgs {
@@ -51,13 +59,19 @@ struct DecodeArgs {
   int32_t len_cap;
   // Partials of (sequence b, query head h, split s) go to slot
   // (b * hq + h) * part_stride + part_slot0 + s; force_partial stores them
-  // even with one split.  window_slot: the slot the reduce reads the window
-  // pass from (-1 = none).
+  // even with one split.
   int32_t part_stride;
   int32_t part_slot0;
   int32_t force_partial;
-  int32_t window_slot;
   int32_t group;             // channels per scale/zero pair (grouped INT4 pool only)
+  // Window pass that also finishes the call (fin_splits > 0): after its own
+  // share it merges the fin_splits INT4 partials of each (sequence, query
+  // head), whose pass skipped fin_skip_first / fin_skip_last tokens in splits
+  // of fin_split_pages pages, and writes the normalised output.
+  int32_t fin_splits;
+  int32_t fin_split_pages;
+  int32_t fin_skip_first;
+  int32_t fin_skip_last;
 };
 
 // Split-K plan shared by the launch and the workspace query.

@@ -1,6 +1,5 @@
 // Split-K merge: for each (sequence, query head) combine the partials (max,
-// sum, unnormalised output) of its splits, and of the bf16 window pass when
-// high-precision windows are in use, with the log-sum-exp rule and
+// sum, unnormalised output) of its splits with the log-sum-exp rule and
 // normalise.  The decode kernels store each partial already rotated back to
 // the original basis (the rotation is linear and the merge is a weighted
 // sum), so nothing is rotated here.
@@ -29,13 +28,11 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
 
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-  // the INT4 splits that held pages of this sequence, and the window pass
+  // the splits that held pages of this sequence
   int lo, hi;
   int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
   const int npg = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
-  const int win_len = a.len_cap < len ? a.len_cap : len;
   auto valid = [&](int slot) {
-    if (slot == a.window_slot) return win_len > 0;
     const int q0 = max(slot * a.split_pages, pfirst);
     return hi > lo && q0 < min(npg, (slot + 1) * a.split_pages);
   };

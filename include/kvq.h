@@ -231,16 +231,18 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
 
 /*
  * kvq_decode_attn_windowed -- kvq_decode_attn with high-precision windows
- * ("InnerQ", Abstract and Figure 2: a small window of sink tokens and of
- * recent tokens is kept in high precision next to the quantized cache; the
- * two parts of the attention output are computed separately and merged).
+ * ("InnerQ", Abstract and Figure 2: sink tokens and the most recent tokens
+ * stay in high precision beside the quantized cache, and the output shares of
+ * the two are formed apart and then combined).
  *
  * For a sequence of L tokens the first w_sink and the last w_recent tokens
  * are read from `window`, a bf16 pool holding unrotated copies of them, and
  * attended with the unrotated query; the tokens in between are read from the
  * INT4 cache as in kvq_decode_attn.  The result is the one softmax over all
  * L tokens (the INT4 share rotated back), obtained by the log-sum-exp merge
- * of the INT4 split partials and the window pass.
+ * of the INT4 split partials and the window pass.  Two launches: the INT4
+ * pass stores its split partials in the workspace; the window pass, after it
+ * on the stream, merges them with its own share and writes `out`.
  *
  * Window layout: window position of token t is t when t < w_sink, else
  * w_sink + (t - w_sink) mod w_recent (a ring of the recent tokens: a new
@@ -266,7 +268,9 @@ kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_
                                     int32_t num_splits, float* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
-/* Workspace bytes kvq_decode_attn_windowed needs (always > 0 for batch > 0). */
+/* Workspace bytes kvq_decode_attn_windowed needs: one partial per INT4
+ * split, batch * num_q_heads * splits * (head_dim + 2) floats (always > 0 for
+ * batch > 0). */
 size_t kvq_decode_windowed_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t max_seq_len, int32_t num_splits);
 

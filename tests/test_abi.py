@@ -242,9 +242,11 @@ def test_windowed_decode_rejects_mismatched_window_pool():
     assert _windowed(_int4(), kvq._Bf16Desc(FAKE, 4, 16, 2, 128)) == kvq.KVQ_ERR_INVALID_ARGUMENT
 
 
-def test_windowed_workspace_has_a_slot_for_the_window():
+def test_windowed_workspace_holds_a_partial_per_split():
+    """The INT4 pass always stores partials (the window pass merges them), so
+    even one split needs a slot; split counts match kvq_decode_attn's."""
     for maxlen in (16, 4096, 131072):
         plain = kvq.kvq_decode_workspace_bytes(4, 8, 2, 64, maxlen, 0)
         win = kvq.kvq_decode_windowed_workspace_bytes(4, 8, 2, 64, maxlen, 0)
         row = 4 * 8 * (64 + 2) * 4
-        assert win == max(plain, row) + row if plain else win == 2 * row
+        assert win == (plain if plain else row)
