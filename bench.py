@@ -350,16 +350,17 @@ def long_context_rate(torch, kvq, workloads, iters=30):
     return res
 
 
-def concurrency_sweep(torch, kvq, workloads, steps=32, warm=8, block_steps=8,
+def concurrency_sweep(torch, kvq, workloads, steps=48, warm=8, block_steps=8,
                       batches=(1, 8, 32, 128, 256)):
     """70B-shaped layer (64 q / 8 kv heads): per batch size, fill the ragged
     lognormal contexts into a rotated INT4, a plain INT4 and a bf16 cache, run
     ``warm`` untimed decode steps on each (append one token per sequence, then
     decode over it), then time ``steps`` more per cache in runs of
-    ``block_steps`` that alternate between the caches, so that all three see
-    the same clocks.  Tokens/s = batch * steps / time.  Successive steps
-    attend the same cache, as a serving loop does (small batches stay in the
-    Infinity Cache)."""
+    ``block_steps`` that alternate between the caches, the first of each round
+    rotating (6 rounds: each cache first twice), so that all three see the
+    same clocks.  Tokens/s = batch * steps / time.  Successive steps attend
+    the same cache, as a serving loop does (small batches stay in the Infinity
+    Cache)."""
     out = {"workload": "64 q / 8 kv heads, head_dim 128, lognormal contexts (median 2048, "
                        "sigma 1, cap 32768), page 16, one new token per sequence per step",
            "steps": steps}
@@ -393,8 +394,11 @@ def concurrency_sweep(torch, kvq, workloads, steps=32, warm=8, block_steps=8,
             for i in range(warm):
                 run(name, i)
         ms = {name: 0.0 for name in names}
-        for i0 in range(warm, warm + steps, block_steps):
-            for name in names:
+        for rnd, i0 in enumerate(range(warm, warm + steps, block_steps)):
+            # the variant that runs first after the synchronisation changes
+            # from round to round, so none is always first
+            order = names[rnd % len(names):] + names[:rnd % len(names)]
+            for name in order:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 torch.cuda.synchronize()
