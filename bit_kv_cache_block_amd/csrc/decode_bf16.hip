@@ -296,20 +296,28 @@ __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) 
       int4_token_range(len_full, a.fin_skip_first, a.fin_skip_last, lo, hi);
       const int npg4 = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
       const int64_t row = (hq0 + j) * a.part_stride;
+      // (loads of several splits in flight; invalid splits' stale bytes are
+      // never used, by selection)
       float mall = mstar;
+#pragma unroll 8
       for (int sp = 0; sp < a.fin_splits; ++sp) {
         const bool ok = hi > lo && max(sp * a.fin_split_pages, pfirst) < min(npg4, (sp + 1) * a.fin_split_pages);
-        if (ok) mall = fmaxf(mall, a.part_ml[(row + sp) * 2]);
+        const float m = a.part_ml[(row + sp) * 2];
+        mall = ok ? fmaxf(mall, m) : mall;
       }
       const float mu = mall == kNegInf ? 0.0f : mall;
       const float fw = exp2f(mstar - mu);
       float lt = lsum * fw, ot = osum * fw;
+#pragma unroll 4
       for (int sp = 0; sp < a.fin_splits; ++sp) {
         const bool ok = hi > lo && max(sp * a.fin_split_pages, pfirst) < min(npg4, (sp + 1) * a.fin_split_pages);
-        if (!ok) continue;
-        const float f = exp2f(a.part_ml[(row + sp) * 2] - mu);
-        lt = __builtin_fmaf(a.part_ml[(row + sp) * 2 + 1], f, lt);
-        ot = __builtin_fmaf(a.part_acc[(row + sp) * D + c], f, ot);
+        const float m = a.part_ml[(row + sp) * 2], l = a.part_ml[(row + sp) * 2 + 1];
+        const float x = a.part_acc[(row + sp) * D + c];
+        if (ok) {
+          const float f = exp2f(m - mu);
+          lt = __builtin_fmaf(l, f, lt);
+          ot = __builtin_fmaf(x, f, ot);
+        }
       }
       a.out[(hq0 + j) * D + c] = lt > 0.0f ? ot / lt : 0.0f;
     } else if (a.nsplit == 1 && !a.force_partial) {

@@ -39,23 +39,35 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
   const float* ml = a.part_ml + bh * a.part_stride * 2;
   const float* pa = a.part_acc + bh * a.part_stride * D + kC * n;
 
+  // Every slot's loads are issued (the workspace holds part_stride slots per
+  // row) and only the valid slots are taken, by selection rather than by a
+  // zero weight, so the stale bytes of unused slots never enter the sums; the
+  // unrolled loops keep several slots' loads in flight instead of one round
+  // trip per split.
   float mstar = -__builtin_inff();
-  for (int s = 0; s < a.part_stride; ++s)
-    if (valid(s)) mstar = fmaxf(mstar, ml[2 * s]);
+#pragma unroll 8
+  for (int s = 0; s < a.part_stride; ++s) {
+    const float m = ml[2 * s];
+    mstar = valid(s) ? fmaxf(mstar, m) : mstar;
+  }
   const float muse = mstar == -__builtin_inff() ? 0.0f : mstar;
   float lsum = 0.0f;
   float o[kC];
 #pragma unroll
   for (int k = 0; k < kC; ++k) o[k] = 0.0f;
+#pragma unroll 4
   for (int s = 0; s < a.part_stride; ++s) {
-    if (!valid(s)) continue;
-    const float w = exp2f(ml[2 * s] - muse);
-    lsum = __builtin_fmaf(ml[2 * s + 1], w, lsum);
+    const float m = ml[2 * s], l = ml[2 * s + 1];
+    v4f x[kC / 4];
 #pragma unroll
-    for (int k = 0; k < kC; k += 4) {
-      const v4f x = *reinterpret_cast<const v4f*>(pa + static_cast<int64_t>(s) * D + k);
+    for (int k = 0; k < kC / 4; ++k) x[k] = *reinterpret_cast<const v4f*>(pa + static_cast<int64_t>(s) * D + 4 * k);
+    if (valid(s)) {
+      const float w = exp2f(m - muse);
+      lsum = __builtin_fmaf(l, w, lsum);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[k + i] = __builtin_fmaf(x[i], w, o[k + i]);
+      for (int k = 0; k < kC / 4; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[4 * k + i] = __builtin_fmaf(x[k][i], w, o[4 * k + i]);
     }
   }
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;   // an empty sequence stores zeros
