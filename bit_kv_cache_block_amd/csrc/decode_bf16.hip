@@ -296,28 +296,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) 
       int4_token_range(len_full, a.fin_skip_first, a.fin_skip_last, lo, hi);
       const int npg4 = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
       const int64_t row = (hq0 + j) * a.part_stride;
-      // (loads of several splits in flight; invalid splits' stale bytes are
-      // never used, by selection)
-      float mall = mstar;
-#pragma unroll 8
-      for (int sp = 0; sp < a.fin_splits; ++sp) {
-        const bool ok = hi > lo && max(sp * a.fin_split_pages, pfirst) < min(npg4, (sp + 1) * a.fin_split_pages);
-        const float m = a.part_ml[(row + sp) * 2];
-        mall = ok ? fmaxf(mall, m) : mall;
-      }
-      const float mu = mall == kNegInf ? 0.0f : mall;
-      const float fw = exp2f(mstar - mu);
-      float lt = lsum * fw, ot = osum * fw;
+      // The window's share opens the running (max, sum, output) and the
+      // splits fold in with the online form of the rule.  Invalid splits'
+      // stale bytes are dropped by selection, and with no branch in the loop
+      // the unrolled splits' loads are in flight together.
+      float mr = mstar, lt = lsum, ot = osum;
 #pragma unroll 4
       for (int sp = 0; sp < a.fin_splits; ++sp) {
         const bool ok = hi > lo && max(sp * a.fin_split_pages, pfirst) < min(npg4, (sp + 1) * a.fin_split_pages);
         const float m = a.part_ml[(row + sp) * 2], l = a.part_ml[(row + sp) * 2 + 1];
         const float x = a.part_acc[(row + sp) * D + c];
-        if (ok) {
-          const float f = exp2f(m - mu);
-          lt = __builtin_fmaf(l, f, lt);
-          ot = __builtin_fmaf(x, f, ot);
-        }
+        const float mn = ok ? fmaxf(mr, m) : mr;
+        const float mu = mn == kNegInf ? 0.0f : mn;
+        const float fo = exp2f(mr - mu), fs = exp2f(m - mu);
+        lt = ok ? __builtin_fmaf(lt, fo, l * fs) : lt;
+        ot = ok ? __builtin_fmaf(ot, fo, x * fs) : ot;
+        mr = mn;
       }
       a.out[(hq0 + j) * D + c] = lt > 0.0f ? ot / lt : 0.0f;
     } else if (a.nsplit == 1 && !a.force_partial) {

@@ -4,88 +4,134 @@
 // the original basis (the rotation is linear and the merge is a weighted
 // sum), so nothing is rotated here.
 //
-// A wave merges four (sequence, query head) rows, one per row of 16 lanes;
-// lane n of a row owns channels [C n, C n + C) with C = D / 16, read as
-// 16-byte vectors from every split.
+// A row's splits are dealt round-robin to G groups of D/4 lanes; lane c of a
+// group owns channels [4c, 4c + 4), read as one 16-byte vector per split.
+// Each group folds its splits in with the online form of the rule (running
+// maximum, rescaled sum and output), so the loads of all its splits can be in
+// flight at once and no separate pass over the maxima is needed; the G group
+// results of a row then meet in LDS.  The host picks G so that a lane reads
+// at most about four splits: a merge of few rows and many splits (small
+// batches cut finely) is a couple of memory round trips rather than one per
+// split.
 #include "dev_common.hpp"
 #include "kvq_internal.hpp"
 
 namespace kvq {
 namespace {
 
-constexpr int kReduceThreads = 256;   // 16 (sequence, query head) rows per workgroup
+constexpr int kReduceThreads = 256;
 
-template <int D>
+template <int D, int G>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
-  constexpr int kC = D / 16;
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15;
+  constexpr int kL = D / 4;                          // lanes per split group
+  constexpr int kRows = kReduceThreads / (kL * G);   // rows per workgroup
+  static_assert(kRows >= 1 && kRows * kL * G == kReduceThreads, "group shape");
+  __shared__ float sm_o[kRows][G][D];
+  __shared__ float sm_m[kRows][G];
+  __shared__ float sm_l[kRows][G];
+
+  const int t = threadIdx.x;
+  const int r = t / (kL * G);
+  const int g = (t / kL) % G;
+  const int c = t % kL;
   const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
-  const int64_t bh = static_cast<int64_t>(blockIdx.x) * (kReduceThreads / 16) + (threadIdx.x >> 4);
-  if (bh >= rows) return;
-  const int b = static_cast<int>(bh / a.num_q_heads);
-  float* dst = a.out + bh * D + kC * n;
+  const int64_t bh = static_cast<int64_t>(blockIdx.x) * kRows + r;
+  const bool live = bh < rows;
 
-  int len = a.seq_lens[b];
-  len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-  // the splits that held pages of this sequence
-  int lo, hi;
-  int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
-  const int npg = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
-  auto valid = [&](int slot) {
-    const int q0 = max(slot * a.split_pages, pfirst);
-    return hi > lo && q0 < min(npg, (slot + 1) * a.split_pages);
-  };
-  const float* ml = a.part_ml + bh * a.part_stride * 2;
-  const float* pa = a.part_acc + bh * a.part_stride * D + kC * n;
-
-  // Every slot's loads are issued (the workspace holds part_stride slots per
-  // row) and only the valid slots are taken, by selection rather than by a
-  // zero weight, so the stale bytes of unused slots never enter the sums; the
-  // unrolled loops keep several slots' loads in flight instead of one round
-  // trip per split.
-  float mstar = -__builtin_inff();
-#pragma unroll 8
-  for (int s = 0; s < a.part_stride; ++s) {
-    const float m = ml[2 * s];
-    mstar = valid(s) ? fmaxf(mstar, m) : mstar;
-  }
-  const float muse = mstar == -__builtin_inff() ? 0.0f : mstar;
-  float lsum = 0.0f;
-  float o[kC];
-#pragma unroll
-  for (int k = 0; k < kC; ++k) o[k] = 0.0f;
+  float m = -__builtin_inff(), l = 0.0f;
+  v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (live) {
+    const int b = static_cast<int>(bh / a.num_q_heads);
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+    // the splits that held pages of this sequence
+    int lo, hi;
+    int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
+    const int npg = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
+    const float* ml = a.part_ml + bh * a.part_stride * 2;
+    const float* pa = a.part_acc + bh * a.part_stride * D + 4 * c;
+    // Every slot's loads are issued (the workspace holds part_stride slots
+    // per row) and only valid slots are folded in, by selection rather than
+    // a zero weight, so stale bytes never enter the sums; without a branch in
+    // the loop the unrolled iterations' loads are all in flight together.
 #pragma unroll 4
-  for (int s = 0; s < a.part_stride; ++s) {
-    const float m = ml[2 * s], l = ml[2 * s + 1];
-    v4f x[kC / 4];
+    for (int s = g; s < a.part_stride; s += G) {
+      const float ms = ml[2 * s], ls = ml[2 * s + 1];
+      const v4f x = *reinterpret_cast<const v4f*>(pa + static_cast<int64_t>(s) * D);
+      const bool ok = hi > lo && max(s * a.split_pages, pfirst) < min(npg, (s + 1) * a.split_pages);
+      const float mn = ok ? fmaxf(m, ms) : m;
+      const float mu = mn == -__builtin_inff() ? 0.0f : mn;
+      const float fo = exp2f(m - mu), fs = exp2f(ms - mu);
+      l = ok ? __builtin_fmaf(l, fo, ls * fs) : l;
 #pragma unroll
-    for (int k = 0; k < kC / 4; ++k) x[k] = *reinterpret_cast<const v4f*>(pa + static_cast<int64_t>(s) * D + 4 * k);
-    if (valid(s)) {
-      const float w = exp2f(m - muse);
-      lsum = __builtin_fmaf(l, w, lsum);
-#pragma unroll
-      for (int k = 0; k < kC / 4; ++k)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[4 * k + i] = __builtin_fmaf(x[k][i], w, o[4 * k + i]);
+      for (int i = 0; i < 4; ++i) o[i] = ok ? __builtin_fmaf(o[i], fo, x[i] * fs) : o[i];
+      m = mn;
     }
   }
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;   // an empty sequence stores zeros
+  float* dst = a.out + bh * D + 4 * c;
+  if constexpr (G == 1) {
+    if (!live) return;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;   // an empty sequence stores zeros
+    *reinterpret_cast<v4f*>(dst) = v4f{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+  } else {
+    *reinterpret_cast<v4f*>(&sm_o[r][g][4 * c]) = o;
+    if (c == 0) {
+      sm_m[r][g] = m;
+      sm_l[r][g] = l;
+    }
+    __syncthreads();
+    if (!live || g != 0) return;
+    float mstar = sm_m[r][0];
 #pragma unroll
-  for (int k = 0; k < kC; k += 4)
-    *reinterpret_cast<v4f*>(dst + k) = v4f{o[k] * inv, o[k + 1] * inv, o[k + 2] * inv, o[k + 3] * inv};
+    for (int k = 1; k < G; ++k) mstar = fmaxf(mstar, sm_m[r][k]);
+    const float mu = mstar == -__builtin_inff() ? 0.0f : mstar;
+    float lsum = 0.0f;
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const float f = exp2f(sm_m[r][k] - mu);
+      lsum = __builtin_fmaf(sm_l[r][k], f, lsum);
+      const v4f y = *reinterpret_cast<const v4f*>(&sm_o[r][k][4 * c]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(y[i], f, acc[i]);
+    }
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    *reinterpret_cast<v4f*>(dst) = v4f{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  }
+}
+
+template <int D, int G>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
+  constexpr int kRows = kReduceThreads / (D / 4 * G);
+  const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
+  const dim3 grid(static_cast<unsigned>((rows + kRows - 1) / kRows));
+  reduce_kernel<D, G><<<grid, kReduceThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dim(const DecodeArgs& a, hipStream_t s) {
+  // about four splits per lane: G = the power of two >= part_stride / 4,
+  // at most one row per workgroup
+  constexpr int kMaxG = kReduceThreads / (D / 4);
+  int g = 1;
+  while (g < kMaxG && 4 * g < a.part_stride) g *= 2;
+  switch (g) {
+    case 1: return launch_g<D, 1>(a, s);
+    case 2: return launch_g<D, 2>(a, s);
+    case 4: return launch_g<D, 4>(a, s);
+    case 8: return launch_g<D, 8>(a, s);
+    default:
+      if constexpr (kMaxG >= 16) return launch_g<D, 16>(a, s);
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t s) {
-  const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
-  const dim3 grid(static_cast<unsigned>((rows + kReduceThreads / 16 - 1) / (kReduceThreads / 16)));
-  if (a.head_dim == 128)
-    reduce_kernel<128><<<grid, kReduceThreads, 0, s>>>(a);
-  else
-    reduce_kernel<64><<<grid, kReduceThreads, 0, s>>>(a);
-  return hipGetLastError();
+  if (a.head_dim == 128) return launch_dim<128>(a, s);
+  return launch_dim<64>(a, s);
 }
 
 }  // namespace kvq

@@ -195,6 +195,32 @@ def test_decode_edge_lengths(d, dtype):
         assert_close(got, want, f"edges d{d} S{splits}")
 
 
+@pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float16)])
+def test_decode_many_splits_stale_workspace(d, dtype):
+    """Few rows cut into many splits (the merge then deals a row's splits to
+    several lane groups), with a workspace pre-filled with 0xFF bytes (NaN as
+    fp32): slots no split of a short sequence wrote must not leak in."""
+    lens = [0, 1, 40, 1000, 4000, 9000]
+    w = workloads.random_decode(17, batch=len(lens), hq=4, hkv=1, d=d, block=d // 2, dtype=dtype,
+                                seq_lens=lens)
+    cache = gpu_int4_cache(w, w.block)
+    pool = oracle_int4_pool(w, w.block)
+    want = oracle.decode_int4(pool, w.hkv, w.d, w.block, bits(w.q), _odt(w.q), w.block_table,
+                              w.seq_lens, w.sm_scale)
+    q = w.q.to(DEV)
+    bt = torch.from_numpy(w.block_table).to(DEV)
+    sl = torch.from_numpy(w.seq_lens).to(DEV)
+    for splits in (4, 9, 17, 33, 64, 140):
+        nb = kvq.kvq_decode_workspace_bytes(w.batch, w.hq, w.hkv, w.d, w.max_seq_len, splits)
+        ws = torch.full((max(nb, 16),), 0xFF, dtype=torch.uint8, device=DEV)
+        out = kvq.kvq_decode_attn(cache, q, bt, sl, w.max_seq_len, w.sm_scale, workspace=ws,
+                                  num_splits=splits)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert not got[0].any()
+        assert_close(got, want, f"many splits d{d} S{splits} ({nb} workspace bytes)")
+
+
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (16, 1)])
 def test_decode_group_sizes(hq, hkv):
     w = workloads.random_decode(12, batch=3, hq=hq, hkv=hkv, d=128, block=64,
