@@ -113,6 +113,9 @@ void decode_quant_kernel(DecodeArgs a) {
   // the step (fewest instructions); otherwise the per-group form, whose
   // shorter live ranges also fit the 128-VGPR build
   constexpr bool kOnePass = kNG == 1 && WPE == 1;
+  // two step buffers (see the streaming loop): the two-set INT4 kernel, whose
+  // registers allow two waves per SIMD with or without the second buffer
+  constexpr bool kPrefetch = NS == 2 && BITS == 4 && GS == 0;
   constexpr int kNT = D / 16;          // PV tiles = output channels per lane
   constexpr int kOps = D / 64;         // QK MFMAs per page and head group
   constexpr int kGP = 4 * NS;          // padded heads per KV head
@@ -217,18 +220,20 @@ void decode_quant_kernel(DecodeArgs a) {
     const int rel = pg - cb;
     return rel < 64 ? __builtin_amdgcn_readlane(ids_cur, rel) : __builtin_amdgcn_readlane(ids_next, rel - 64);
   };
-  auto load = [&](Buf& sb, int p) {
+  // id_of(i) is the id of page p + i (-1 when the page is past the range)
+  auto load_with = [&](Buf& sb, int p, auto id_of) {
     sb.all_ok = true;
 #pragma unroll
     for (int i = 0; i < kStep; ++i) {
-      const int pg = p + i;
-      const int id = pg < pw1 ? page_id(pg) : -1;
+      const int id = id_of(i);
       sb.pv[i] = id >= 0 && id < a.num_pages;
       sb.all_ok = sb.all_ok && sb.pv[i];
       // one buffer descriptor per page slab (scalar registers): each load is
-      // that base plus the lane's 32-bit offset; nothing can reach past the slab
+      // that base plus the lane's 32-bit offset; nothing can reach past the
+      // slab, and a page that is not there gets an empty descriptor, whose
+      // loads return zeros without touching memory
       const uint8_t* sl = pool_h + static_cast<int64_t>(sb.pv[i] ? id : 0) * page_stride;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, kSlab);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, sb.pv[i] ? kSlab : 0);
       if constexpr (kCodeBytes / 4 >= 16) {
 #pragma unroll
         for (int j = 0; j < kKX; ++j)
@@ -261,6 +266,20 @@ void decode_quant_kernel(DecodeArgs a) {
       }
     }
   };
+  auto load = [&](Buf& sb, int p) {
+    load_with(sb, p, [&](int i) { return p + i < pw1 ? page_id(p + i) : -1; });
+  };
+  // With two step buffers the page ids come by scalar loads (wave-uniform
+  // addresses, always inside the row: pages past pw1 read a clamped entry
+  // and are dropped where the ids are used, so that nothing waits for these
+  // loads before the step that needs them).
+  using ConstI32 = const __attribute__((address_space(4))) int32_t;
+  ConstI32* bt_s = (ConstI32*)bt;   // generic to constant address space
+  auto ids4 = [&](int p, int32_t (&id)[kStep]) {
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) id[i] = bt_s[min(p + i, pw1 - 1)];
+  };
+  int32_t idA[kStep], idB[kStep];
   // the query is consumed before the first page loads are issued, so waiting
   // for it never waits for them
   float qv[kC];
@@ -275,7 +294,13 @@ void decode_quant_kernel(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < kC; ++k) asm volatile("" : : "v"(qv[k]) : "memory");
   Buf buf0;
-  if (pw0 < pw1) load(buf0, pw0);
+  if constexpr (kPrefetch) {
+    ids4(pw0, idA);
+    load_with(buf0, pw0, [&](int i) { return pw0 + i < pw1 ? idA[i] : -1; });
+    ids4(pw0 + kStep, idB);
+  } else {
+    if (pw0 < pw1) load(buf0, pw0);
+  }
   // ---- query: rotate in registers, fixed point, limbs ------------------------
   for (int e = tid; e < kWaves * NS * kNG * 4 * 4 * 16; e += 64 * kWaves)
     (&sm.wl[0][0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
@@ -587,19 +612,39 @@ void decode_quant_kernel(DecodeArgs a) {
     else
       compute(sb, p, std::false_type{});
   };
-  // One step at a time: its four pages are loaded, then computed.  While a
-  // wave computes, the other waves of its SIMD keep loads in flight (an
-  // in-register prefetch of the next step measured slower: more VGPRs and
-  // conservative waits).
-  for (int p = pw0; p < pw1; p += kStep) {
-    step(buf0, p);
-    if (p + kStep >= pw1) break;
-    if (p + kStep >= cb + 64) {   // the next step starts in the following 64 ids
-      cb += 64;
-      ids_cur = ids_next;
-      ids_next = load_ids(cb + 64);
+  if constexpr (kPrefetch) {
+    // The next step's loads go out before this step is computed, so a wave
+    // keeps a step in flight while it computes, and the ids of the step after
+    // that are fetched meanwhile.  With two sets of heads a step computes long
+    // enough that the two waves per SIMD would otherwise leave the SIMD's
+    // loads idle much of the time.  The loads are issued whether or not their
+    // step exists (its pages then have empty descriptors), so each wait for a
+    // step's data leaves the following step's loads in flight.
+    Buf buf1;
+    for (int p = pw0; p < pw1; p += 2 * kStep) {
+      load_with(buf1, p + kStep, [&](int i) { return p + kStep + i < pw1 ? idB[i] : -1; });
+      ids4(p + 2 * kStep, idA);
+      step(buf0, p);
+      if (p + kStep >= pw1) break;
+      load_with(buf0, p + 2 * kStep, [&](int i) { return p + 2 * kStep + i < pw1 ? idA[i] : -1; });
+      ids4(p + 3 * kStep, idB);
+      step(buf1, p + kStep);
     }
-    load(buf0, p + kStep);
+  } else {
+    // One step at a time: its four pages are loaded, then computed.  While a
+    // wave computes, the other waves of its SIMD keep loads in flight (with
+    // one set of heads an in-register prefetch of the next step measured
+    // slower: more VGPRs, fewer waves).
+    for (int p = pw0; p < pw1; p += kStep) {
+      step(buf0, p);
+      if (p + kStep >= pw1) break;
+      if (p + kStep >= cb + 64) {   // the next step starts in the following 64 ids
+        cb += 64;
+        ids_cur = ids_next;
+        ids_next = load_ids(cb + 64);
+      }
+      load(buf0, p + kStep);
+    }
   }
 
   // ---- merge the four waves --------------------------------------------------

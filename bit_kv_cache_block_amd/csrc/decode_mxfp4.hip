@@ -144,8 +144,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
       const int id = pg < pw1 ? page_id(pg) : -1;
       sb.pv[i] = id >= 0 && id < a.num_pages;
       sb.all_ok = sb.all_ok && sb.pv[i];
+      // a page that is not there gets an empty descriptor (its loads return
+      // zeros without touching memory)
       const uint8_t* sl = pool_h + static_cast<int64_t>(sb.pv[i] ? id : 0) * page_stride;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, kSlab);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, sb.pv[i] ? kSlab : 0);
       sb.kx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, k_off, 0, kStreamOnce));
       sb.vx[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, 0, kStreamOnce));
       sb.ks[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, ks_off, 0, kStreamOnce);

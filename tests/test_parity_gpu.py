@@ -180,10 +180,11 @@ def test_decode_ragged_group8_with_appended_token():
     assert_close(gpu_decode(cache, step), want, "concurrency")
 
 
+@pytest.mark.parametrize("hq", [8, 16])
 @pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float16)])
-def test_decode_edge_lengths(d, dtype):
+def test_decode_edge_lengths(d, dtype, hq):
     lens = [0, 1, 15, 16, 17, 63, 64, 65, 100, 300]
-    w = workloads.random_decode(11, batch=len(lens), hq=8, hkv=2, d=d, block=d // 2, dtype=dtype,
+    w = workloads.random_decode(11, batch=len(lens), hq=hq, hkv=2, d=d, block=d // 2, dtype=dtype,
                                 seq_lens=lens)
     cache = gpu_int4_cache(w, w.block)
     pool = oracle_int4_pool(w, w.block)
@@ -192,16 +193,17 @@ def test_decode_edge_lengths(d, dtype):
     for splits in (0, 1, 2, 3, 100):
         got = gpu_decode(cache, w, splits)
         assert not got[0].any()                     # empty sequence -> zeros
-        assert_close(got, want, f"edges d{d} S{splits}")
+        assert_close(got, want, f"edges d{d} hq{hq} S{splits}")
 
 
+@pytest.mark.parametrize("hq", [4, 8])
 @pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float16)])
-def test_decode_many_splits_stale_workspace(d, dtype):
+def test_decode_many_splits_stale_workspace(d, dtype, hq):
     """Few rows cut into many splits (the merge then deals a row's splits to
     several lane groups), with a workspace pre-filled with 0xFF bytes (NaN as
     fp32): slots no split of a short sequence wrote must not leak in."""
     lens = [0, 1, 40, 1000, 4000, 9000]
-    w = workloads.random_decode(17, batch=len(lens), hq=4, hkv=1, d=d, block=d // 2, dtype=dtype,
+    w = workloads.random_decode(17, batch=len(lens), hq=hq, hkv=1, d=d, block=d // 2, dtype=dtype,
                                 seq_lens=lens)
     cache = gpu_int4_cache(w, w.block)
     pool = oracle_int4_pool(w, w.block)
@@ -218,7 +220,7 @@ def test_decode_many_splits_stale_workspace(d, dtype):
         torch.cuda.synchronize()
         got = out.cpu().numpy().astype(np.float64)
         assert not got[0].any()
-        assert_close(got, want, f"many splits d{d} S{splits} ({nb} workspace bytes)")
+        assert_close(got, want, f"many splits d{d} hq{hq} S{splits} ({nb} workspace bytes)")
 
 
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (16, 1)])
