@@ -21,9 +21,9 @@ alone in a decode-only loop, and ``rotated_over_plain_decode`` compares block
 64 with plain INT4 under that same loop.
 
 Other modes (for rocprofv3 runs): ``--mode decode`` times only the headline
-decode; ``--mode prefill`` only the prefill append; ``--mode copy`` runs a
-plain 1 GiB device copy used to calibrate the FETCH_SIZE / WRITE_SIZE
-counters.
+decode; ``--mode prefill`` only the prefill append; ``--mode concurrency``
+only the concurrency sweep; ``--mode copy`` runs a plain 1 GiB device copy
+used to calibrate the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
 
@@ -360,7 +360,9 @@ def concurrency_sweep(torch, kvq, workloads, steps=48, warm=8, block_steps=8,
     rotating (6 rounds: each cache first twice), so that all three see the
     same clocks.  Tokens/s = batch * steps / time.  Successive steps attend
     the same cache, as a serving loop does (small batches stay in the Infinity
-    Cache)."""
+    Cache).  The steps are timed twice: called one by one from Python (the
+    host's per-call cost included; it bounds the small batches), and captured
+    in HIP graphs and replayed."""
     out = {"workload": "64 q / 8 kv heads, head_dim 128, lognormal contexts (median 2048, "
                        "sigma 1, cap 32768), page 16, one new token per sequence per step",
            "steps": steps}
@@ -408,12 +410,47 @@ def concurrency_sweep(torch, kvq, workloads, steps=48, warm=8, block_steps=8,
                 e1.record()
                 torch.cuda.synchronize()
                 ms[name] += e0.elapsed_time(e1)
+        # The same steps captured in HIP graphs (one per run of block_steps)
+        # and replayed in the same rotating order: the GPU time of a step
+        # without the host's per-call cost, as a serving loop that replays
+        # captured decode steps sees it.  Replays write the same tokens into
+        # the same slots, so the caches stay as the eager steps left them.
+        graphs = {name: [] for name in names}
+        for name in names:
+            for i0 in range(warm, warm + steps, block_steps):
+                g = torch.cuda.CUDAGraph()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g):
+                    for i in range(i0, min(i0 + block_steps, warm + steps)):
+                        run(name, i)
+                graphs[name].append(g)
+        for name in names:
+            graphs[name][0].replay()
+        gms = {name: 0.0 for name in names}
+        for rnd in range(len(graphs[names[0]])):
+            order = names[rnd % len(names):] + names[:rnd % len(names)]
+            for name in order:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                graphs[name][rnd].replay()
+                e1.record()
+                torch.cuda.synchronize()
+                gms[name] += e0.elapsed_time(e1)
         row = {"context_tokens": int(fill.seq_lens.sum())}
         for name in names:
             row[name] = {"us_per_step": round(ms[name] * 1e3 / steps, 2),
-                         "tokens_s": round(b * steps / (ms[name] * 1e-3), 1)}
+                         "tokens_s": round(b * steps / (ms[name] * 1e-3), 1),
+                         "graph_us_per_step": round(gms[name] * 1e3 / steps, 2),
+                         "graph_tokens_s": round(b * steps / (gms[name] * 1e-3), 1)}
         row["rotated_over_plain"] = round(row["int4_block64"]["tokens_s"] / row["int4_plain"]["tokens_s"], 4)
         row["int4_over_bf16"] = round(row["int4_block64"]["tokens_s"] / row["bf16"]["tokens_s"], 3)
+        row["graph_rotated_over_plain"] = round(row["int4_block64"]["graph_tokens_s"]
+                                                / row["int4_plain"]["graph_tokens_s"], 4)
+        row["graph_int4_over_bf16"] = round(row["int4_block64"]["graph_tokens_s"]
+                                            / row["bf16"]["graph_tokens_s"], 3)
+        del graphs
         out[f"batch{b}"] = row
         del fill, st, caches
         torch.cuda.empty_cache()
@@ -480,7 +517,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=["full", "decode", "prefill", "copy"], default="full")
+    ap.add_argument("--mode", choices=["full", "decode", "prefill", "copy", "concurrency"], default="full")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -502,6 +539,10 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+        return 0
+
+    if args.mode == "concurrency":
+        print(json.dumps({"mode": "concurrency", **concurrency_sweep(torch, kvq, workloads)}))
         return 0
 
     if args.mode == "prefill":

@@ -140,10 +140,17 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
 
 
+# torch's current stream as a raw handle without building a Stream object
+# (the per-call host cost matters for decode steps of a few sequences)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream, device) -> C.c_void_p:
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return C.c_void_p(stream.cuda_stream)
+    if stream is not None:
+        return C.c_void_p(stream.cuda_stream)
+    if _raw_stream is not None and device.index is not None:
+        return C.c_void_p(_raw_stream(device.index))
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
 def _ptr(t: torch.Tensor | None) -> C.c_void_p:
@@ -254,14 +261,16 @@ class Bf16Cache:
 
 
 def _token_stride(k: torch.Tensor, v: torch.Tensor, hkv: int, d: int) -> int:
-    for t in (k, v):
+    ks, kst = k.shape, k.stride()
+    if (len(ks) == 3 and ks[1] == hkv and ks[2] == d and kst[1] == d and kst[2] == 1
+            and v.shape == ks and v.stride() == kst and v.dtype == k.dtype):
+        return int(kst[0])
+    for t in (k, v):   # say what is wrong
         if t.dim() != 3 or t.shape[1] != hkv or t.shape[2] != d:
             raise ValueError(f"k/v must be [T][{hkv}][{d}], got {tuple(t.shape)}")
         if t.stride(2) != 1 or t.stride(1) != d:
             raise ValueError("each token's [Hkv][D] block of k/v must be contiguous")
-    if k.stride(0) != v.stride(0) or k.dtype != v.dtype or k.shape[0] != v.shape[0]:
-        raise ValueError("k and v must share shape, dtype and token stride")
-    return int(k.stride(0))
+    raise ValueError("k and v must share shape, dtype and token stride")
 
 
 def _append(fn, desc, hkv, d, k, v, slot_mapping, stream):
@@ -326,8 +335,8 @@ def _decode(fn, desc, hkv, d, q, block_table, seq_lens, max_seq_len, sm_scale, o
         out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
     if out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 tensor")
-    need = kvq_decode_workspace_bytes(batch, hq, hkv, d, max_seq_len, num_splits)
-    if workspace is None:
+    if workspace is None:   # (a caller's workspace is checked by the library)
+        need = kvq_decode_workspace_bytes(batch, hq, hkv, d, max_seq_len, num_splits)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check(fn(C.byref(desc), _ptr(q), _dtype_code(q), hq, _ptr(block_table),
               int(block_table.shape[1]), _ptr(seq_lens), batch, int(max_seq_len),
@@ -412,8 +421,9 @@ def kvq_decode_attn_windowed(cache: Int4Cache, window: Bf16Cache, q: torch.Tenso
         out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
     if out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 tensor")
-    need = kvq_decode_windowed_workspace_bytes(batch, hq, cache.num_kv_heads, d, max_seq_len, num_splits)
-    if workspace is None:
+    if workspace is None:   # (a caller's workspace is checked by the library)
+        need = kvq_decode_windowed_workspace_bytes(batch, hq, cache.num_kv_heads, d, max_seq_len,
+                                                   num_splits)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check(lib().kvq_decode_attn_windowed(
         C.byref(_need(cache, Int4Cache).desc()), C.byref(window.desc()), _ptr(q), _dtype_code(q), hq,

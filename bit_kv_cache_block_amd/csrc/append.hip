@@ -67,6 +67,51 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
   return m | ((v < 0.0f && m != 0u) ? 8u : 0u);
 }
 
+// The asymmetric quantizer of one vector (or group), shared by both append
+// kernels so that their codes and sidecars agree bit for bit.  From the range
+// [mn, mx] of the (normalised) elements: zero point mn and scale
+// (mx - mn) / top, both rounded to fp16, and the reciprocal of the rounded
+// scale (0 for a zero scale).  meta packs the fp16 scale (low half) and zero
+// point (high half).
+struct QParams {
+  float zf, inv;
+  uint32_t meta;
+};
+template <int BITS>
+__device__ __forceinline__ QParams tok_params(float mn, float mx) {
+  constexpr float kTop = BITS == 4 ? 15.0f : 255.0f;
+  const float zero_f = mn + 0.0f;
+  const float range = (mx - mn) + 0.0f;
+  const float step = range / kTop;
+  const _Float16 sh = static_cast<_Float16>(step);
+  const _Float16 zh = static_cast<_Float16>(zero_f);
+  const float sf = static_cast<float>(sh);
+  QParams q;
+  q.zf = static_cast<float>(zh);
+  q.inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+  q.meta = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
+  return q;
+}
+
+// Code of one element: (y - zero) * inv, then round-half-even and clamp to
+// [0, top].  Adding 2^23 rounds to an integer in the current (nearest-even)
+// mode for any value in [0, 2^23); the clamp in that biased domain equals
+// clamping the rounded value; the code is then the low 4 (8) bits of the
+// float.  A power-of-two normalisation (b = 16, 64) is exact, so it is folded
+// into the subtraction: fma(x, s, -zero) rounds x*s - zero once, which is the
+// rounding of (x*s) - zero.  (Only a product below 2^-126 can lose bits; that
+// is far below half an ulp of any nonzero fp16 zero point, and with a zero
+// zero point both forms are the rounded product.)  Otherwise x is already the
+// normalised y.
+template <int BITS, bool EXACT_NORM>
+__device__ __forceinline__ uint32_t tok_code(float x, float sb, float zf, float inv) {
+  constexpr float kTop = BITS == 4 ? 15.0f : 255.0f;
+  const float d = EXACT_NORM ? __builtin_fmaf(x, sb, -zf) : x - zf;
+  const float q = d * inv;
+  return f2u(__builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388608.0f + kTop));
+}
+
 template <int D, int BLK, bool BF16, int BITS, int GS, bool MX>
 __global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void append_quant_kernel(AppendArgs a) {
@@ -84,7 +129,6 @@ void append_quant_kernel(AppendArgs a) {
   constexpr int kSideBytes = MX ? kNG : 4 * kNG;       // sidecar bytes per vector
   constexpr int kSlab = kPage * (2 * kCodeBytes + 2 * kSideBytes);
   constexpr int kWords = kLaneElems * BITS / 32;       // code words per lane
-  constexpr float kTop = BITS == 4 ? 15.0f : 255.0f;   // largest code
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[kAppendThreads / 64][kTok * kRowBytes];
   uint8_t* lds = lds_all[threadIdx.x >> 6];
   const int lane = threadIdx.x & 63;
@@ -255,11 +299,8 @@ void append_quant_kernel(AppendArgs a) {
       mn[0] = fminf(mn[0], dpp_f<kDppXor1>(mn[0]));
       mx[0] = fmaxf(mx[0], dpp_f<kDppXor1>(mx[0]));
     }
-    // A power-of-two normalisation (b = 16, 64) is exact, so it is folded
-    // into the subtraction below: fma(x, s, -zero) rounds x*s - zero once,
-    // which is the rounding of (x*s) - zero.  (Only a product below 2^-126
-    // can lose bits; that is far below half an ulp of any nonzero fp16 zero
-    // point, and with a zero zero point both forms are the rounded product.)
+    // A power-of-two normalisation (b = 16, 64) is exact and folded into the
+    // code's subtraction (tok_code); b = 32, 128 scale the elements here.
     constexpr bool kExactNorm = BLK == 16 || BLK == 64;
     const float sb = BLK > 0 ? block_norm(BLK) : 1.0f;
     if constexpr (BLK > 0) {
@@ -291,22 +332,13 @@ void append_quant_kernel(AppendArgs a) {
         zf[gl] = inv[gl] = 0.0f;
         continue;
       }
-      const float zero_f = mn[gl] + 0.0f;
-      const float range = (mx[gl] - mn[gl]) + 0.0f;
-      const float step = range / kTop;
-      const _Float16 sh = static_cast<_Float16>(step);
-      const _Float16 zh = static_cast<_Float16>(zero_f);
-      const float sf = static_cast<float>(sh);
-      zf[gl] = static_cast<float>(zh);
-      inv[gl] = (sf == 0.0f) ? 0.0f : 1.0f / sf;
-      pend.meta[gl] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh)) |
-                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zh)) << 16);
+      const QParams qp = tok_params<BITS>(mn[gl], mx[gl]);
+      zf[gl] = qp.zf;
+      inv[gl] = qp.inv;
+      pend.meta[gl] = qp.meta;
     }
 
-    // codes: (y - zero) * inv, then round-half-even and clamp to [0, top].
-    // Adding 2^23 rounds to an integer in the current (nearest-even) mode for
-    // any value in [0, 2^23); the clamp in that biased domain equals clamping
-    // the rounded value; the code is then the low 4 (8) bits of the float.
+    // codes (tok_code; MXFP4: E2M1 of y / 2^X)
     constexpr int kPer = 32 / BITS;   // codes per word
     auto code = [&](int k) -> uint32_t {
       constexpr int gl_div = kGE;
@@ -316,9 +348,7 @@ void append_quant_kernel(AppendArgs a) {
         const float y = kExactNorm ? x[k] * sb : x[k];
         return e2m1_code(ldexpf(y, -xe[gl]));
       }
-      const float d = kExactNorm ? __builtin_fmaf(x[k], sb, -zf[gl]) : x[k] - zf[gl];
-      const float q = d * inv[gl];
-      return f2u(__builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388608.0f + kTop));
+      return tok_code<BITS, kExactNorm>(x[k], sb, zf[gl], inv[gl]);
     };
     // the unit's results are stored at the start of the next iteration
     if (GS == 0 || kind == 0) {   // consecutive channels: K, or V of the token-wise pools
@@ -377,6 +407,85 @@ void append_quant_kernel(AppendArgs a) {
   if (have_pend) store(pend);
 }
 
+// Few tokens (appends of one token per sequence at decode time): a vector
+// is spread over D/8 lanes, eight consecutive channels per lane, loaded
+// straight from memory.  The butterfly's first three stages run inside the
+// lane and the rest across lanes (DPP), and the range is a reduction across
+// the vector's lanes, so each lane's serial work is that of 8 elements
+// instead of 64: such an append is bound by that latency, not by memory.
+// The butterfly order and the quantizer steps are the tile kernel's, so the
+// codes and sidecars are the same bit for bit.  Token-wise INT4 and INT8.
+template <int D, int BLK, bool BF16, int BITS>
+__global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
+  constexpr int kLPV = D / 8;          // lanes per vector
+  constexpr int kVPW = 64 / kLPV;      // vectors per wave
+  constexpr int kCodeBytes = D * BITS / 8;
+  constexpr int kSlab = kPage * (2 * kCodeBytes + 8);
+  const int lane = threadIdx.x & 63;
+  const int c = lane % kLPV;           // channels [8c, 8c + 8)
+  // vector (token, KV head, K or V), K/V fastest; the kLPV lanes of a vector
+  // are all live or all not, so the cross-lane steps read live lanes only
+  const int64_t vec = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kVPW + lane / kLPV;
+  if (vec >= static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * 2) return;
+  const int kind = static_cast<int>(vec & 1);
+  const int64_t th = vec >> 1;
+  const int h = static_cast<int>(th % a.num_kv_heads);
+  const int64_t t = th / a.num_kv_heads;
+  const uint16_t* src = (kind ? a.v : a.k) + t * a.token_stride + static_cast<int64_t>(h) * D + 8 * c;
+  const int32_t slot = a.slot_mapping[t];
+  float x[8];
+  widen8<BF16>(*reinterpret_cast<const u32x4*>(src), x);
+  if constexpr (BLK > 0) fwht_row<8>(x, BLK, c);   // stages 1, 2, ..., BLK/2
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) {
+    mn = fminf(mn, x[k]);
+    mx = fmaxf(mx, x[k]);
+  }
+  mn = fminf(mn, dpp_xor<1>(mn));
+  mx = fmaxf(mx, dpp_xor<1>(mx));
+  mn = fminf(mn, dpp_xor<2>(mn));
+  mx = fmaxf(mx, dpp_xor<2>(mx));
+  mn = fminf(mn, dpp_xor<4>(mn));
+  mx = fmaxf(mx, dpp_xor<4>(mx));
+  if constexpr (kLPV == 16) {
+    mn = fminf(mn, dpp_xor<8>(mn));
+    mx = fmaxf(mx, dpp_xor<8>(mx));
+  }
+  constexpr bool kExactNorm = BLK == 16 || BLK == 64;
+  const float sb = BLK > 0 ? block_norm(BLK) : 1.0f;
+  if constexpr (BLK > 0) {
+    mn = mn * sb;
+    mx = mx * sb;
+    if constexpr (!kExactNorm) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = x[k] * sb;
+    }
+  }
+  const QParams qp = tok_params<BITS>(mn, mx);
+  uint32_t cd[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) cd[k] = tok_code<BITS, kExactNorm>(x[k], sb, qp.zf, qp.inv);
+
+  if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(a.num_pages) * kPage) return;
+  const int page = slot / kPage, off = slot % kPage;
+  uint8_t* slab = a.pool + (static_cast<int64_t>(page) * a.num_kv_heads + h) * kSlab;
+  if constexpr (BITS == 4) {   // K: token-major; V: word c*P + t holds channels 8c .. 8c+7
+    const uint32_t w = pack8_nibbles(cd);
+    if (kind == 0) *reinterpret_cast<uint32_t*>(slab + off * kCodeBytes + 4 * c) = w;
+    else reinterpret_cast<uint32_t*>(slab + kPage * kCodeBytes)[c * kPage + off] = w;
+  } else {                     // the same with two words (8 bytes) per 8 channels
+    const uint32_t w0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(cd[3], cd[2], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(cd[1], cd[0], 0x0c0c0400u), 0x05040100u);
+    const uint32_t w1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(cd[7], cd[6], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(cd[5], cd[4], 0x0c0c0400u), 0x05040100u);
+    if (kind == 0) *reinterpret_cast<u32x2*>(slab + off * kCodeBytes + 8 * c) = u32x2{w0, w1};
+    else reinterpret_cast<u32x2*>(slab + kPage * kCodeBytes)[c * kPage + off] = u32x2{w0, w1};
+  }
+  if (c == 0) *reinterpret_cast<uint32_t*>(slab + 2 * kPage * kCodeBytes + kind * kPage * 4 + off * 4) = qp.meta;
+}
+
 // bf16 baseline: one thread per (token, head, 8-channel group).
 template <bool BF16>
 __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
@@ -421,8 +530,23 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
   }
 }
 
+// Appends of at most this many tokens (decode steps) use the few-token kernel.
+constexpr int kSmallTokens = 1024;
+
 template <int D, int BLK, int BITS, int GS, bool MX = false>
 hipError_t launch_quant_d(const AppendArgs& a, hipStream_t s) {
+  if constexpr (GS == 0 && !MX) {
+    if (a.num_tokens <= kSmallTokens) {
+      constexpr int kVecPerBlock = 4 * (64 / (D / 8));
+      const int64_t nvec = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * 2;
+      const dim3 grid(static_cast<unsigned>((nvec + kVecPerBlock - 1) / kVecPerBlock));
+      if (a.in_bf16)
+        append_small_kernel<D, BLK, true, BITS><<<grid, 256, 0, s>>>(a);
+      else
+        append_small_kernel<D, BLK, false, BITS><<<grid, 256, 0, s>>>(a);
+      return hipGetLastError();
+    }
+  }
   constexpr int kTok = D == 128 ? 32 : 64;
   const int64_t units = (static_cast<int64_t>(a.num_tokens) + kTok - 1) / kTok * a.num_kv_heads * 2;
   const int64_t blocks = (units + kAppendThreads / 64 - 1) / (kAppendThreads / 64);

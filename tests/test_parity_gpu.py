@@ -121,6 +121,46 @@ def test_append_strided_tokens_skip_slots_and_degenerate_vectors():
         assert_pool_equal(cache.pool, pool, f"edge b{block}")
 
 
+@pytest.mark.parametrize("bits_", [4, 8])
+@pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float16)])
+def test_append_few_token_and_tile_kernels_bitexact(d, dtype, bits_):
+    """Appends of at most 1024 tokens take the few-token kernel (a vector over
+    D/8 lanes), larger ones the tile kernel: both match the oracle bit for
+    bit, on strided rows with constant, signed-zero, tiny and large vectors,
+    skipped and out-of-pool slots, for every block size."""
+    torch.manual_seed(3)
+    hkv = 2
+    t_all = 1100
+    wide = torch.randn(t_all, hkv * d + 32, dtype=torch.float32)
+    wide[5, :hkv * d] = 0.75
+    wide[6, :hkv * d] = -0.0
+    wide[7, :hkv * d] *= 1e-7
+    wide[8, :d] = 3.0e4 * torch.sign(wide[8, :d])
+    wide[9, d:2 * d] = 1e-30
+    wide = wide.to(dtype)
+    k = wide[:, :hkv * d].view(t_all, hkv, d)
+    v = wide.flip(0)[:, :hkv * d].view(t_all, hkv, d)
+    pages = (t_all + 15) // 16 + 8
+    rng = np.random.default_rng(4)
+    slots = rng.permutation(pages * 16)[:t_all].astype(np.int32)
+    slots[3] = -1
+    slots[11] = pages * 16 + 5
+    odt = oracle.BF16 if dtype == torch.bfloat16 else oracle.F16
+    cls = kvq.Int4Cache if bits_ == 4 else kvq.Int8Cache
+    app = kvq.kvq_append_paged if bits_ == 4 else kvq.kvq_append_paged_int8
+    new_pool = oracle.new_int4_pool if bits_ == 4 else oracle.new_int8_pool
+    oapp = oracle.append_int4 if bits_ == 4 else oracle.append_int8
+    for block in [b for b in (0, 16, 32, 64, 128) if b <= d]:
+        for t in (1, 7, 1024, t_all):   # t <= 1024: few-token kernel
+            cache = cls(pages, hkv, d, block, DEV)
+            app(cache, k[:t].to(DEV), v[:t].to(DEV), torch.from_numpy(slots[:t]).to(DEV))
+            torch.cuda.synchronize()
+            pool = new_pool(pages, hkv, d)
+            oapp(pool, pages, hkv, d, block, bits(k[:t].contiguous()), bits(v[:t].contiguous()), odt,
+                 slots[:t])
+            assert_pool_equal(cache.pool, pool, f"int{bits_} d{d} b{block} t{t}")
+
+
 def test_append_bf16_cache_matches_oracle():
     for w in (workloads.tiny_decode(1, block=0), workloads.llama8b_decode(2, batch=2, context=256)):
         cache = kvq.Bf16Cache(w.num_pages, w.hkv, w.d, DEV)
