@@ -161,22 +161,25 @@ void decode_quant_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < kC / 2; ++i) qraw[i] = 0u;
   }
-  // Page ids of this wave's range, 64 at a time: lane i of ids_cur holds the
-  // id of page cb + i, ids_next the following 64.  A step pulls its four ids
-  // out with readlane (wave-uniform, no memory round trip).  They are fetched
-  // first for the range a full-length split gives this wave, and again only if
-  // the sequence is shorter and its balanced range starts elsewhere.  An id
-  // outside the pool reads page 0 and is masked out of the softmax.
+  // Page ids come by scalar loads (wave-uniform addresses, always inside the
+  // row), a step ahead of the page loads that use them, so they never wait
+  // behind vector loads.  The first step's ids are fetched at once for the
+  // range a full-length split gives this wave, and again only if the
+  // sequence is shorter and its balanced range starts elsewhere.
   const int p0 = s * a.split_pages;
   const int per_wave_full = ((a.split_pages + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  int cb = p0 + wave * per_wave_full;
-  int ids_cur, ids_next;
-  {
-    const int pg = cb + lane, lim = min(p0 + a.split_pages, a.bt_stride);
-    ids_cur = pg < lim ? bt[pg] : -1;
-    ids_next = pg + 64 < lim ? bt[pg + 64] : -1;
-  }
+  using ConstI32 = const __attribute__((address_space(4))) int32_t;
+  ConstI32* bt_s = (ConstI32*)bt;   // generic to constant address space
+  // raw entries of pages p .. p+3, indexes clamped below lim (pages at or
+  // past the range are dropped where the ids are used)
+  auto ids4 = [&](int p, int lim, int32_t (&id)[kStep]) {
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) id[i] = bt_s[min(p + i, lim - 1)];
+  };
+  const int cb = p0 + wave * per_wave_full;
+  int32_t idA[kStep], idB[kStep];
+  ids4(cb, min(p0 + a.split_pages, a.bt_stride), idA);
 
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
@@ -207,19 +210,7 @@ void decode_quant_kernel(DecodeArgs a) {
   const uint32_t k_off = n * kCodeBytes + g * (kCodeBytes / 4);
   const uint32_t v_off = kPage * kCodeBytes + (vn * kPage + 4 * g) * (BITS == 8 ? 8 : 4);
   const uint32_t km_off = 2 * kPage * kCodeBytes + 4 * kNG * n;
-  auto load_ids = [&](int first) {
-    const int pg = first + lane;
-    return pg < pw1 ? bt[pg] : -1;
-  };
-  if (cb != pw0) {   // shorter sequence: its balanced range starts elsewhere
-    cb = pw0;
-    ids_cur = load_ids(pw0);
-    ids_next = load_ids(pw0 + 64);
-  }
-  auto page_id = [&](int pg) {
-    const int rel = pg - cb;
-    return rel < 64 ? __builtin_amdgcn_readlane(ids_cur, rel) : __builtin_amdgcn_readlane(ids_next, rel - 64);
-  };
+  if (cb != pw0) ids4(pw0, pw1, idA);   // shorter sequence: its range starts elsewhere
   // id_of(i) is the id of page p + i (-1 when the page is past the range)
   auto load_with = [&](Buf& sb, int p, auto id_of) {
     sb.all_ok = true;
@@ -266,40 +257,19 @@ void decode_quant_kernel(DecodeArgs a) {
       }
     }
   };
-  auto load = [&](Buf& sb, int p) {
-    load_with(sb, p, [&](int i) { return p + i < pw1 ? page_id(p + i) : -1; });
-  };
-  // With two step buffers the page ids come by scalar loads (wave-uniform
-  // addresses, always inside the row: pages past pw1 read a clamped entry
-  // and are dropped where the ids are used, so that nothing waits for these
-  // loads before the step that needs them).
-  using ConstI32 = const __attribute__((address_space(4))) int32_t;
-  ConstI32* bt_s = (ConstI32*)bt;   // generic to constant address space
-  auto ids4 = [&](int p, int32_t (&id)[kStep]) {
-#pragma unroll
-    for (int i = 0; i < kStep; ++i) id[i] = bt_s[min(p + i, pw1 - 1)];
-  };
-  int32_t idA[kStep], idB[kStep];
-  // the query is consumed before the first page loads are issued, so waiting
-  // for it never waits for them
+  // The first step's page loads go out before the query is waited for: the
+  // query was requested first, so its wait leaves the pages in flight, and
+  // its rotation and limbs are computed while they arrive.
+  Buf buf0;
+  load_with(buf0, pw0, [&](int i) { return pw0 + i < pw1 ? idA[i] : -1; });
+  ids4(pw0 + kStep, pw1, idB);
+  __builtin_amdgcn_sched_barrier(0);
   float qv[kC];
 #pragma unroll
   for (int k = 0; k < kC; ++k) {
     const uint16_t u = static_cast<uint16_t>(qraw[k / 2] >> (16 * (k & 1)));
     const float x = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
     qv[k] = qhead < G ? x : 0.0f;
-  }
-  // materialise the query here (its wait drains only the query and the ids)
-  // and keep the page loads below this point
-#pragma unroll
-  for (int k = 0; k < kC; ++k) asm volatile("" : : "v"(qv[k]) : "memory");
-  Buf buf0;
-  if constexpr (kPrefetch) {
-    ids4(pw0, idA);
-    load_with(buf0, pw0, [&](int i) { return pw0 + i < pw1 ? idA[i] : -1; });
-    ids4(pw0 + kStep, idB);
-  } else {
-    if (pw0 < pw1) load(buf0, pw0);
   }
   // ---- query: rotate in registers, fixed point, limbs ------------------------
   for (int e = tid; e < kWaves * NS * kNG * 4 * 4 * 16; e += 64 * kWaves)
@@ -623,11 +593,11 @@ void decode_quant_kernel(DecodeArgs a) {
     Buf buf1;
     for (int p = pw0; p < pw1; p += 2 * kStep) {
       load_with(buf1, p + kStep, [&](int i) { return p + kStep + i < pw1 ? idB[i] : -1; });
-      ids4(p + 2 * kStep, idA);
+      ids4(p + 2 * kStep, pw1, idA);
       step(buf0, p);
       if (p + kStep >= pw1) break;
       load_with(buf0, p + 2 * kStep, [&](int i) { return p + 2 * kStep + i < pw1 ? idA[i] : -1; });
-      ids4(p + 3 * kStep, idB);
+      ids4(p + 3 * kStep, pw1, idB);
       step(buf1, p + kStep);
     }
   } else {
@@ -638,12 +608,8 @@ void decode_quant_kernel(DecodeArgs a) {
     for (int p = pw0; p < pw1; p += kStep) {
       step(buf0, p);
       if (p + kStep >= pw1) break;
-      if (p + kStep >= cb + 64) {   // the next step starts in the following 64 ids
-        cb += 64;
-        ids_cur = ids_next;
-        ids_next = load_ids(cb + 64);
-      }
-      load(buf0, p + kStep);
+      load_with(buf0, p + kStep, [&](int i) { return p + kStep + i < pw1 ? idB[i] : -1; });
+      ids4(p + 2 * kStep, pw1, idB);
     }
   }
 
