@@ -126,22 +126,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
   const uint32_t v_off = kPage * D / 2 + (n * kPage + 4 * g) * 4;
   const uint32_t ks_off = kPage * D + n * kBlocks;
   const uint32_t vs_off = ks_off + kPage * kBlocks;
-  int cb = pw0;
-  auto load_ids = [&](int first) {
-    const int pg = first + lane;
-    return pg < pw1 ? bt[pg] : -1;
+  // page ids by scalar loads (wave-uniform, inside the row; pages at or past
+  // pw1 are dropped where the ids are used), a step ahead of their loads
+  using ConstI32 = const __attribute__((address_space(4))) int32_t;
+  ConstI32* bt_s = (ConstI32*)bt;   // generic to constant address space
+  auto ids4 = [&](int p, int32_t (&id)[kStep]) {
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) id[i] = bt_s[min(p + i, pw1 - 1)];
   };
-  int ids_cur = load_ids(cb), ids_next = load_ids(cb + 64);
-  auto page_id = [&](int pg) {
-    const int rel = pg - cb;
-    return rel < 64 ? __builtin_amdgcn_readlane(ids_cur, rel) : __builtin_amdgcn_readlane(ids_next, rel - 64);
-  };
-  auto load = [&](MxStep& sb, int p) {
+  int32_t idA[kStep], idB[kStep];
+  ids4(pw0, idA);
+  auto load = [&](MxStep& sb, int p, const int32_t (&ids)[kStep]) {
     sb.all_ok = true;
 #pragma unroll
     for (int i = 0; i < kStep; ++i) {
-      const int pg = p + i;
-      const int id = pg < pw1 ? page_id(pg) : -1;
+      const int id = p + i < pw1 ? ids[i] : -1;
       sb.pv[i] = id >= 0 && id < a.num_pages;
       sb.all_ok = sb.all_ok && sb.pv[i];
       // a page that is not there gets an empty descriptor (its loads return
@@ -154,6 +153,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
       sb.vs[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs_off, 0, kStreamOnce);
     }
   };
+  // the first step's page loads go out before the query is waited for (the
+  // query was requested first, so its wait leaves them in flight)
+  MxStep buf0;
+  load(buf0, pw0, idA);
+  ids4(pw0 + kStep, idB);
+  __builtin_amdgcn_sched_barrier(0);
   float qv[kC];
 #pragma unroll
   for (int k = 0; k < kC; ++k) {
@@ -161,10 +166,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
     const float x = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
     qv[k] = (qwave && qhead < G) ? x : 0.0f;
   }
-#pragma unroll
-  for (int k = 0; k < kC; ++k) asm volatile("" : : "v"(qv[k]) : "memory");
-  MxStep buf0;
-  if (pw0 < pw1) load(buf0, pw0);
 
   for (int e = tid; e < kWaves * NS * kBlocks * 4 * 4 * 16; e += 64 * kWaves)
     (&sm.wl[0][0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
@@ -346,15 +347,29 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
     else
       compute(sb, p, std::false_type{});
   };
-  for (int p = pw0; p < pw1; p += kStep) {
-    step(buf0, p);
-    if (p + kStep >= pw1) break;
-    if (p + kStep >= cb + 64) {
-      cb += 64;
-      ids_cur = ids_next;
-      ids_next = load_ids(cb + 64);
+  if constexpr (NS == 1) {
+    // Two step buffers: the next step's loads go out before this step is
+    // computed (the E2M1 conversions and per-block limbs make a step long
+    // enough that two waves per SIMD leave the loads idle otherwise; the
+    // registers still allow two waves).  Loads of a step past the range
+    // have empty descriptors, so each wait leaves the next step in flight.
+    MxStep buf1;
+    for (int p = pw0; p < pw1; p += 2 * kStep) {
+      load(buf1, p + kStep, idB);
+      ids4(p + 2 * kStep, idA);
+      step(buf0, p);
+      if (p + kStep >= pw1) break;
+      load(buf0, p + 2 * kStep, idA);
+      ids4(p + 3 * kStep, idB);
+      step(buf1, p + kStep);
     }
-    load(buf0, p + kStep);
+  } else {
+    for (int p = pw0; p < pw1; p += kStep) {
+      step(buf0, p);
+      if (p + kStep >= pw1) break;
+      load(buf0, p + kStep, idB);
+      ids4(p + 2 * kStep, idB);
+    }
   }
 
   // ---- merge the four waves, rotate back, store ------------------------------
