@@ -279,7 +279,7 @@ void decode_quant_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < kC; ++k) v[k] = qv[k];
     if (a.block > 0) {
-      fwht_row<kC>(v, a.block, n);
+      fwht_row_any<kC>(v, a.block, n);
       const float sb = block_norm(a.block);
 #pragma unroll
       for (int k = 0; k < kC; ++k) v[k] *= sb;
@@ -658,7 +658,7 @@ void decode_quant_kernel(DecodeArgs a) {
     // rotated here (the merge is a weighted sum, so it commutes)
     float scale = 1.0f;
     if (a.block > 0) {   // every row takes part: the butterfly reads its neighbours
-      fwht_row<kC>(o, a.block, n);
+      fwht_row_any<kC>(o, a.block, n);
       scale = block_norm(a.block);
     }
     if (a.nsplit == 1 && !a.force_partial) {

@@ -174,7 +174,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
 #pragma unroll
     for (int k = 0; k < kC; ++k) v[k] = qv[k];
     if (a.block > 0) {
-      fwht_row<kC>(v, a.block, n);
+      fwht_row_any<kC>(v, a.block, n);
       const float sbn = block_norm(a.block);
 #pragma unroll
       for (int k = 0; k < kC; ++k) v[k] *= sbn;
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
       }
     float scale = 1.0f;
     if (a.block > 0) {
-      fwht_row<kC>(o, a.block, n);
+      fwht_row_any<kC>(o, a.block, n);
       scale = block_norm(a.block);
     }
     if (a.nsplit == 1) {

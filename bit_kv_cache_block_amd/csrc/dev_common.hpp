@@ -155,6 +155,24 @@ __device__ __forceinline__ void fwht_row(float* v, int block, int n) {
   if (8 * C < block) cross(std::integral_constant<int, 8>{});
 }
 
+// The same butterfly for a block size known only at run time: one
+// straight-line copy per block size (a uniform branch picks it), so that no
+// stage is guarded by a run-time test (such guards cost register copies on
+// the latency-bound paths that rotate one vector per row).  Block 0: no
+// rotation.
+template <int C>
+__device__ __forceinline__ void fwht_row_any(float* v, int block, int n) {
+  switch (block) {
+    case 16: fwht_row<C>(v, 16, n); break;
+    case 32: fwht_row<C>(v, 32, n); break;
+    case 64: fwht_row<C>(v, 64, n); break;
+    case 128:
+      if constexpr (16 * C >= 128) fwht_row<C>(v, 128, n);
+      break;
+    default: break;
+  }
+}
+
 // Tokens [lo, hi) of a sequence of `len` tokens that an INT4 pass reads
 // when the first skip_first and the last skip_last tokens are left to the
 // high-precision windows (both zero: all of them).
