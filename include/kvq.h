@@ -207,7 +207,10 @@ kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const vo
  * 1e-3 of exact fp64 attention over the same decoded cache.
  *
  * q:            device, [batch][num_q_heads][head_dim] of `dtype`, 16-byte aligned.
- * block_table:  device int32 [batch][max_pages_per_seq].
+ * block_table:  device int32 [batch][max_pages_per_seq].  An entry of a
+ *               sequence's range outside [0, num_pages) is a page that is
+ *               not there: it is not read and its tokens are left out of the
+ *               softmax (a row with no token left is zero).
  * seq_lens:     device int32 [batch], each <= max_seq_len.
  * max_seq_len:  host bound on seq_lens (sizes the split-K grid);
  *               max_pages_per_seq*16 >= max_seq_len.

@@ -366,10 +366,19 @@ def bf16_read(pool, num_kv_heads, head_dim, page, head, off, kind, channel, page
                                             head, off, kind, channel))
 
 
+def _pages_in_pool(block_table, pool, num_kv_heads, slab_bytes):
+    """The block table with every id outside [0, num_pages) (num_pages from
+    the pool's size) set to -1, which the decode reads as a page that is not
+    there."""
+    num_pages = np.asarray(pool).size // (num_kv_heads * slab_bytes)
+    bt = np.asarray(block_table, dtype=np.int32)
+    return np.where((bt >= 0) & (bt < num_pages), bt, -1).astype(np.int32)
+
+
 def decode_int4(pool, num_kv_heads, head_dim, block, q, dtype, block_table, seq_lens, sm_scale,
                 page_size=16, mask=None):
     q = _c(q, np.uint16)
-    bt = _c(block_table, np.int32)
+    bt = _c(_pages_in_pool(block_table, pool, num_kv_heads, int4_slab_bytes(page_size, head_dim)), np.int32)
     sl = _c(seq_lens, np.int32)
     batch, hq, d = q.shape
     out = np.zeros((batch, hq, d), np.float64)
@@ -386,7 +395,7 @@ def decode_int4(pool, num_kv_heads, head_dim, block, q, dtype, block_table, seq_
 def decode_int8(pool, num_kv_heads, head_dim, block, q, dtype, block_table, seq_lens, sm_scale,
                 page_size=16, mask=None):
     q = _c(q, np.uint16)
-    bt = _c(block_table, np.int32)
+    bt = _c(_pages_in_pool(block_table, pool, num_kv_heads, int8_slab_bytes(page_size, head_dim)), np.int32)
     sl = _c(seq_lens, np.int32)
     batch, hq, d = q.shape
     out = np.zeros((batch, hq, d), np.float64)
@@ -403,7 +412,7 @@ def decode_int8(pool, num_kv_heads, head_dim, block, q, dtype, block_table, seq_
 def decode_int4g(pool, num_kv_heads, head_dim, block, group, q, dtype, block_table, seq_lens,
                  sm_scale, page_size=16, mask=None):
     q = _c(q, np.uint16)
-    bt = _c(block_table, np.int32)
+    bt = _c(_pages_in_pool(block_table, pool, num_kv_heads, int4g_slab_bytes(page_size, head_dim, group)), np.int32)
     sl = _c(seq_lens, np.int32)
     batch, hq, d = q.shape
     out = np.zeros((batch, hq, d), np.float64)
@@ -420,7 +429,7 @@ def decode_int4g(pool, num_kv_heads, head_dim, block, group, q, dtype, block_tab
 def decode_mxfp4(pool, num_kv_heads, head_dim, block, q, dtype, block_table, seq_lens, sm_scale,
                  page_size=16, mask=None):
     q = _c(q, np.uint16)
-    bt = _c(block_table, np.int32)
+    bt = _c(_pages_in_pool(block_table, pool, num_kv_heads, mxfp4_slab_bytes(page_size, head_dim)), np.int32)
     sl = _c(seq_lens, np.int32)
     batch, hq, d = q.shape
     out = np.zeros((batch, hq, d), np.float64)
@@ -437,7 +446,7 @@ def decode_mxfp4(pool, num_kv_heads, head_dim, block, q, dtype, block_table, seq
 def decode_bf16(pool, num_kv_heads, head_dim, q, dtype, block_table, seq_lens, sm_scale,
                 page_size=16, mask=None):
     q = _c(q, np.uint16)
-    bt = _c(block_table, np.int32)
+    bt = _c(_pages_in_pool(block_table, pool, num_kv_heads, bf16_slab_bytes(page_size, head_dim)), np.int32)
     sl = _c(seq_lens, np.int32)
     batch, hq, d = q.shape
     out = np.zeros((batch, hq, d), np.float64)

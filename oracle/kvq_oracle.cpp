@@ -192,18 +192,26 @@ int32_t decode_paged(Read read, int32_t page_size, int32_t num_kv_heads, int32_t
       std::vector<double> qv(d), qr(d), s(len), orot(d, 0.0);
       for (int c = 0; c < d; ++c) qv[c] = widen(q[(static_cast<size_t>(b) * hq + h) * d + c], dtype);
       rotate_f64(qv.data(), qr.data(), d, rot);
+      // a negative page id marks a page that is not there: its tokens are
+      // left out of the softmax, and a row with no token left is zero
       double mx = -INFINITY;
       for (int t = 0; t < len; ++t) {
         const int page = block_table[static_cast<size_t>(b) * max_pages_per_seq + t / p];
+        if (page < 0) {
+          s[t] = -INFINITY;
+          continue;
+        }
         double dot = 0.0;
         for (int c = 0; c < d; ++c) dot += qr[c] * read(page, kvh, t % p, 0, c);
         s[t] = sm_scale * dot;
         if (s[t] > mx) mx = s[t];
       }
+      if (mx == -INFINITY) continue;
       double l = 0.0;
-      for (int t = 0; t < len; ++t) { s[t] = std::exp(s[t] - mx); l += s[t]; }
+      for (int t = 0; t < len; ++t) { s[t] = s[t] == -INFINITY ? 0.0 : std::exp(s[t] - mx); l += s[t]; }
       for (int t = 0; t < len; ++t) {
         const int page = block_table[static_cast<size_t>(b) * max_pages_per_seq + t / p];
+        if (page < 0) continue;
         for (int c = 0; c < d; ++c) orot[c] += s[t] * read(page, kvh, t % p, 1, c);
       }
       for (int c = 0; c < d; ++c) orot[c] /= l;

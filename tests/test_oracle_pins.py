@@ -381,6 +381,30 @@ def test_empty_sequence_gives_zeros():
     assert not out[0].any() and np.abs(out[1]).max() > 0
 
 
+def test_absent_pages_leave_their_tokens_out():
+    """A block-table entry outside [0, num_pages) (negative or past the pool)
+    is a page that is not there: the row equals attention over the other
+    tokens (rebuilt as a shorter sequence over the remaining pages), and a row
+    whose pages are all absent is zero."""
+    w, pool = _tiny_case(seed=6, block=64, lens=[40, 40, 33])
+    q = workloads.bits(w.q)
+    args = (w.hkv, w.d, 64, q, oracle.F16)
+    bt = w.block_table.copy()
+    p0, p1, p2 = (int(x) for x in bt[0][:3])
+    bt[0][1] = -1                                  # the middle page of sequence 0 (tokens 16..31)
+    bt[1][2] = w.num_pages + 3                     # the last page of sequence 1 (tokens 32..39)
+    bt[2][:3] = [-1, -5, w.num_pages]              # every page of sequence 2
+    out = oracle.decode_int4(pool, *args, bt, w.seq_lens, w.sm_scale)
+    ref_bt = w.block_table.copy()
+    ref_bt[0][:2] = [p0, p2]                       # tokens 0..15 then 32..39: 24 tokens
+    ref_lens = np.array([24, 32, 0], np.int32)
+    ref = oracle.decode_int4(pool, *args, ref_bt, ref_lens, w.sm_scale)
+    assert np.allclose(out[0], ref[0], rtol=1e-12, atol=1e-14)
+    assert np.array_equal(out[1], ref[1])          # the same tokens in the same order
+    assert not out[2].any()
+    assert np.abs(out[0] - oracle.decode_int4(pool, *args, w.block_table, w.seq_lens, w.sm_scale)[0]).max() > 1e-6
+
+
 def test_page_permutation_invariance():
     """Moving pages and their table entries together leaves the output bit-identical."""
     w, pool = _tiny_case(seed=5, block=64, lens=[70, 33, 16])
