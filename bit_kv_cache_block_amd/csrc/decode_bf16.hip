@@ -103,14 +103,63 @@ __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) 
     return;
   }
 
-  for (int e = tid; e < kGP * D; e += 64 * kWaves) {
-    const int j = e / D, c = e % D;
-    float v = 0.0f;
-    if (j < G) {
-      const uint16_t u = a.q[(static_cast<int64_t>(b) * a.num_q_heads + kvh * G + j) * D + c];
-      v = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
+  const int span = p1 - p0;
+  const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
+  const int pw0 = p0 + wave * per_wave;
+  const int pw1 = min(p1, pw0 + per_wave);
+  const uint8_t* pool_h = a.pool + static_cast<int64_t>(kvh) * kSlab;
+  const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kSlab;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const int vn = n & (D / 8 - 1);
+  const int k_off = (n * D + 8 * g) * 2;
+  const int v_off = (kPage * D + (vn * (kPage / 4) + g) * 32) * 2;
+
+  // The query is requested first; then the page ids (scalar loads, always
+  // inside the row: pages at or past pw1 read a clamped entry and are
+  // dropped) and the first step's pages, so that the query's wait leaves
+  // the pages in flight while the query is staged into limbs.
+  constexpr int kQPer = kGP * D / (64 * kWaves);   // query elements per thread
+  uint16_t qraw[kQPer];
+#pragma unroll
+  for (int r = 0; r < kQPer; ++r) {
+    const int e = tid + r * 64 * kWaves, j = e / D, c = e % D;
+    qraw[r] = j < G ? a.q[(static_cast<int64_t>(b) * a.num_q_heads + kvh * G + j) * D + c] : 0;
+  }
+  using ConstI32 = const __attribute__((address_space(4))) int32_t;
+  ConstI32* bt_s = (ConstI32*)bt;   // generic to constant address space
+  auto ids = [&](int p, int32_t (&id)[kStep]) {
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) id[i] = bt_s[min(p + i, pw1 - 1)];
+  };
+  u32x4 kx[kStep][kNK], vx[kStep][4];
+  bool pv[kStep];
+  bool all_ok = true;
+  auto load_step = [&](int p, const int32_t (&id)[kStep]) {
+    all_ok = true;
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) {
+      pv[i] = p + i < pw1 && id[i] >= 0 && id[i] < a.num_pages;
+      all_ok = all_ok && pv[i];
+      const uint8_t* sl = pool_h + static_cast<int64_t>(pv[i] ? id[i] : 0) * page_stride;
+#pragma unroll
+      for (int mu = 0; mu < kNK; ++mu) kx[i][mu] = *reinterpret_cast<const u32x4*>(sl + k_off + 64 * mu);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) vx[i][qq] = *reinterpret_cast<const u32x4*>(sl + v_off + 16 * qq);
     }
-    sm.u.qs[j][c] = v;
+  };
+  int32_t idc[kStep];
+  if constexpr (NS <= 2) {   // (with four sets the step buffer held here would cost a wave per SIMD)
+    ids(pw0, idc);
+    load_step(pw0, idc);
+    ids(pw0 + kStep, idc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+#pragma unroll
+  for (int r = 0; r < kQPer; ++r) {
+    const int e = tid + r * 64 * kWaves, j = e / D, c = e % D;
+    const uint16_t u = qraw[r];
+    sm.u.qs[j][c] = j < G ? (QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u))) : 0.0f;
   }
   for (int e = tid; e < kWaves * NS * 4 * 4 * kStep * 16; e += 64 * kWaves)
     (&sm.pl[0][0][0][0][0][0])[e] = 0;   // limb-3 rows stay zero
@@ -132,11 +181,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) 
       aq[st][mu] = w;
     }
 
-  const int span = p1 - p0;
-  const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
-  const int pw0 = p0 + wave * per_wave;
-  const int pw1 = min(p1, pw0 + per_wave);
-
   float m_run[NS], l_run[NS], acc[NS][kNT];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
@@ -145,36 +189,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) 
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[st][t] = 0.0f;
   }
-  const uint8_t* pool_h = a.pool + static_cast<int64_t>(kvh) * kSlab;
-  const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kSlab;
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  const int vn = n & (D / 8 - 1);
   const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int k_off = (n * D + 8 * g) * 2;
-  const int v_off = (kPage * D + (vn * (kPage / 4) + g) * 32) * 2;
   for (int p = pw0; p < pw1; p += kStep) {
-    int pid[kStep];
-    bool pv[kStep];
-    bool all_ok = true;
-#pragma unroll
-    for (int i = 0; i < kStep; ++i) {
-      const int pg = p + i;
-      const int id = pg < pw1 ? bt[pg] : -1;
-      pv[i] = id >= 0 && id < a.num_pages;
-      pid[i] = pv[i] ? id : 0;
-      all_ok = all_ok && pv[i];
+    if constexpr (NS > 2) {   // loads at the top of the step
+      ids(p, idc);
+      load_step(p, idc);
     }
     const bool tail = !all_ok || (p + kStep) * kPage > len;
-    u32x4 kx[kStep][kNK], vx[kStep][4];
-#pragma unroll
-    for (int i = 0; i < kStep; ++i) {
-      const uint8_t* sl = pool_h + static_cast<int64_t>(pid[i]) * page_stride;
-#pragma unroll
-      for (int mu = 0; mu < kNK; ++mu) kx[i][mu] = *reinterpret_cast<const u32x4*>(sl + k_off + 64 * mu);
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) vx[i][qq] = *reinterpret_cast<const u32x4*>(sl + v_off + 16 * qq);
-    }
     if (tail) {
       // zero the values of tokens past the end (or of unusable pages) so that
       // stale bits there never meet the zero weights as NaN or Inf
@@ -259,6 +281,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) 
         const v4f c = mfma_bf16(as_bf(apv[st]), as_bf(bv), zero4);
         acc[st][tau] = __builtin_fmaf(acc[st][tau], alpha[st], (c[0] + c[1]) + c[2]);
       }
+    }
+    if constexpr (NS <= 2) {   // the next step's loads, then the ids of the step after it
+      if (p + kStep >= pw1) break;
+      load_step(p + kStep, idc);
+      ids(p + 2 * kStep, idc);
     }
   }
 
