@@ -430,8 +430,9 @@ kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_
   }
   if (batch == 0) return KVQ_OK;
   const SplitPlan plan = plan_splits(batch, hkv, max_seq_len, num_splits);
-  const int32_t stride = plan.nsplit;   // one partial per INT4 split
-  if (static_cast<int64_t>(plan.nsplit) * hkv * batch > INT32_MAX)
+  // one partial per INT4 split, and one for the window pass
+  const int32_t stride = plan.nsplit + (wlen > 0 ? 1 : 0);
+  if (static_cast<int64_t>(plan.nsplit + 1) * hkv * batch > INT32_MAX)
     return fail(KVQ_ERR_UNSUPPORTED, "batch * num_kv_heads * splits above 2^31 workgroups");
   const size_t need = static_cast<size_t>(batch) * hq * stride * (d + 2) * sizeof(float);
   if (workspace_bytes_given < need)
@@ -464,10 +465,10 @@ kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_
   a.part_stride = stride;
   a.force_partial = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_decode_int4(a, s);
-  if (e == hipSuccess && wlen > 0) {
-    // the bf16 pass over each sequence's window; it runs after the INT4
-    // partials on the same stream and finishes the call by merging them
+  hipError_t e;
+  if (wlen > 0) {
+    // the bf16 pass over each sequence's window, in the same grid as the
+    // INT4 pass, into the last slot of each row
     DecodeArgs w = a;
     w.pool = static_cast<const uint8_t*>(window->pool);
     w.block_table = window_table;
@@ -478,15 +479,14 @@ kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_
     w.len_cap = static_cast<int32_t>(wlen);
     w.split_pages = static_cast<int32_t>((wlen + 15) / 16 + 3) / 4 * 4;
     w.nsplit = 1;
-    w.force_partial = 0;
-    w.fin_splits = plan.nsplit;
-    w.fin_split_pages = plan.split_pages;
-    w.fin_skip_first = w_sink;
-    w.fin_skip_last = w_recent;
-    e = launch_decode_bf16(w, s);
-  } else if (e == hipSuccess) {   // no windows: the INT4 partials alone
-    e = launch_reduce(a, s);
+    w.part_slot0 = plan.nsplit;
+    e = launch_decode_windowed(a, w, s);
+    a.has_window = 1;
+    a.win_len = static_cast<int32_t>(wlen);
+  } else {
+    e = launch_decode_int4(a, s);
   }
+  if (e == hipSuccess) e = launch_reduce(a, s);   // merge and normalise
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;
 }
@@ -497,7 +497,7 @@ size_t kvq_decode_windowed_workspace_bytes(int32_t batch, int32_t num_q_heads, i
       num_splits < 0)
     return 0;
   const SplitPlan plan = plan_splits(batch, num_kv_heads, max_seq_len, num_splits);
-  return static_cast<size_t>(batch) * num_q_heads * plan.nsplit * (head_dim + 2) * sizeof(float);
+  return static_cast<size_t>(batch) * num_q_heads * (plan.nsplit + 1) * (head_dim + 2) * sizeof(float);
 }
 
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -36,651 +36,17 @@
 // channels; V is stored so that each PV tile of 16 output channels lies in
 // one group, so PV keeps one product per tile, with the softmax weights of
 // that group (w = p * v_scale of the group) as its operand.
-#include "dev_common.hpp"
-#include "kvq_internal.hpp"
-
-#include <type_traits>
+#include "decode_int4_body.hpp"
 
 namespace kvq {
 namespace {
 
-constexpr float kNegInf = -__builtin_inff();
-constexpr int kWaves = 4;
-constexpr int kStep = 4;   // pages per step
+using q4::kWaves;
 
-// channel of k-slot (dword i, byte k) of the QK operand `op` for lane group g:
-// 4-bit codes split into low and high nibbles, 8-bit codes in byte order
-template <int D, int BITS>
-__device__ __forceinline__ int qk_channel(int g, int op, int i, int k) {
-  if constexpr (BITS == 8) return (D / 4) * g + 16 * op + 4 * i + k;
-  else if constexpr (D == 128) return 32 * g + 8 * i + 2 * k + op;
-  else return 16 * g + 8 * (i & 1) + 2 * k + (i >> 1);
-}
-
-// output channel of PV tile tau for lane column n (the V layout of the
-// token-wise pools puts 8 consecutive channels in a word, the grouped pool
-// channels n + (D/8) j)
-template <int D, int GS>
-__device__ __forceinline__ int pv_channel(int n, int tau) {
-  if constexpr (GS != 0) {
-    if constexpr (D == 128) return n + 16 * tau;
-    else return (n & 7) + 8 * (2 * tau + (n >> 3));
-  } else {
-    if constexpr (D == 128) return 8 * n + tau;
-    else return 8 * (n & 7) + 2 * tau + (n >> 3);
-  }
-}
-
-template <int D, int NS, int NG>
-struct alignas(16) Smem {
-  static constexpr int kGP = 4 * NS;
-  union {
-    int32_t qi[kGP][D];
-    struct {
-      float acc[kWaves][kGP][D];
-      float m[kWaves][kGP];
-      float l[kWaves][kGP];
-    } merge;
-  } u;
-  float hA[kGP], hS[kGP][NG];
-  uint32_t wl[kWaves][NS][NG][4][4][16];   // [wave][set][group][limb][head][token] = 4 pages' bytes
-};
-
-// one step's loads: four pages of one KV head, KX (VX) 16-byte pieces of
-// K (V) codes per lane and page
-template <int KX, int VX, int NG>
-struct StepBuf {
-  u32x4 kx[kStep][KX];
-  u32x4 vx[kStep][VX];
-  uint32_t km[kStep][NG], vm[kStep][NG];   // (scale, zero) per group
-  bool pv[kStep];
-  bool all_ok;
-};
-
-// WPE: waves per SIMD the register allocation must allow (1 = no limit)
 template <int D, int NS, bool QBF16, int BITS, int GS, int WPE>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(WPE)))
 void decode_quant_kernel(DecodeArgs a) {
-  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
-  static_assert(GS == 0 || (BITS == 4 && (GS == 32 || GS == 64) && GS <= D), "groups of 32 or 64 channels, 4-bit");
-  constexpr int kCodeBytes = D * BITS / 8;           // one vector's codes
-  constexpr int kNG = GS ? D / GS : 1;               // (scale, zero) pairs per vector
-  constexpr int kSlab = kPage * (2 * kCodeBytes + 8 * kNG);
-  constexpr int kKX = BITS == 8 && D == 128 ? 2 : 1;  // 16-byte K pieces per lane and page
-  constexpr int kVX = BITS == 8 ? 2 : 1;              // 16-byte V pieces per lane and page
-  using Buf = StepBuf<kKX, kVX, kNG>;
-  // one scale/zero per vector and no register cap: the single-pass form of
-  // the step (fewest instructions); otherwise the per-group form, whose
-  // shorter live ranges also fit the 128-VGPR build
-  constexpr bool kOnePass = kNG == 1 && WPE == 1;
-  // two step buffers (see the streaming loop): the two-set INT4 kernel, whose
-  // registers allow two waves per SIMD with or without the second buffer
-  constexpr bool kPrefetch = NS == 2 && BITS == 4 && GS == 0;
-  constexpr int kNT = D / 16;          // PV tiles = output channels per lane
-  constexpr int kOps = D / 64;         // QK MFMAs per page and head group
-  constexpr int kGP = 4 * NS;          // padded heads per KV head
-  constexpr int kC = D / 16;           // channels per lane when a row of 16 lanes holds a vector
-  __shared__ Smem<D, NS, kNG> sm;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int lane = tid & 63;
-  const int g = lane >> 4, n = lane & 15, hs = n >> 2, lam = n & 3;
-  // Work item (split s, sequence b, KV head), KV head fastest and split
-  // slowest, last split first.  Each split is one contiguous run of
-  // workgroups that the round-robin dispatch spreads over every XCD and CU
-  // (with the split fastest, a period of 2, 4 or 8 left most CUs with the
-  // empty splits of short sequences only), and the later splits, busy only
-  // for the longest sequences, start first instead of last.
-  const uint32_t wid = blockIdx.x;
-  const int kvh = static_cast<int>(wid % a.num_kv_heads);
-  const int b = static_cast<int>((wid / a.num_kv_heads) % a.batch);
-  const int s = a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
-
-  // ---- prologue: loads that do not depend on seq_lens go out first ----------
-  // query: wave w < NS takes heads 4w .. 4w+3 of the group, one per row of 16
-  // lanes; lane (g, n) holds channels [kC n, kC n + kC) of head 4w + g.
-  // Padding heads read head G-1 and are zeroed below.
-  const bool qwave = wave < NS;
-  const int qhead = 4 * wave + g;
-  uint32_t qraw[kC / 2];
-  if (qwave) {
-    const uint16_t* qp = a.q + (hq0 + min(qhead, G - 1)) * D + kC * n;
-    if constexpr (kC == 8) {
-      const u32x4 t = *reinterpret_cast<const u32x4*>(qp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qraw[i] = t[i];
-    } else {
-      const u32x2 t = *reinterpret_cast<const u32x2*>(qp);
-      qraw[0] = t[0];
-      qraw[1] = t[1];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kC / 2; ++i) qraw[i] = 0u;
-  }
-  // Page ids come by scalar loads (wave-uniform addresses, always inside the
-  // row), a step ahead of the page loads that use them, so they never wait
-  // behind vector loads.  The first step's ids are fetched at once for the
-  // range a full-length split gives this wave, and again only if the
-  // sequence is shorter and its balanced range starts elsewhere.
-  const int p0 = s * a.split_pages;
-  const int per_wave_full = ((a.split_pages + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  using ConstI32 = const __attribute__((address_space(4))) int32_t;
-  ConstI32* bt_s = (ConstI32*)bt;   // generic to constant address space
-  // raw entries of pages p .. p+3, indexes clamped below lim (pages at or
-  // past the range are dropped where the ids are used)
-  auto ids4 = [&](int p, int lim, int32_t (&id)[kStep]) {
-#pragma unroll
-    for (int i = 0; i < kStep; ++i) id[i] = bt_s[min(p + i, lim - 1)];
-  };
-  const int cb = p0 + wave * per_wave_full;
-  int32_t idA[kStep], idB[kStep];
-  ids4(cb, min(p0 + a.split_pages, a.bt_stride), idA);
-
-  int len = a.seq_lens[b];
-  len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-  int lo, hi;   // the tokens this pass reads (all of them unless windows take some)
-  int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
-  const int npg = (hi + kPage - 1) / kPage;
-  const int q0 = max(p0, lo / kPage);
-  const int p1 = min(npg, p0 + a.split_pages);
-  if (q0 >= p1 || hi <= lo) {
-    if (a.nsplit == 1 && !a.force_partial) {   // empty sequence: zero output rows
-      for (int e = tid; e < G * D; e += 64 * kWaves) a.out[hq0 * D + e] = 0.0f;
-    }
-    return;
-  }
-
-  // ---- this wave's share of the split's pages ---------------------------------
-  const int span = p1 - q0;
-  const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
-  const int pw0 = q0 + wave * per_wave;
-  const int pw1 = min(p1, pw0 + per_wave);
-  const uint8_t* pool_h = a.pool + static_cast<int64_t>(kvh) * kSlab;
-  const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kSlab;
-  const int vn = n & (D / 8 - 1);
-  // lane offsets within a page slab, unsigned so that each load is a uniform
-  // 64-bit base plus a 32-bit lane offset: lane (g, n) reads K codes of token
-  // n (channels [D/4 g, D/4 (g+1))) and V codes of tokens 4g..4g+3 (channel
-  // group vn)
-  const uint32_t k_off = n * kCodeBytes + g * (kCodeBytes / 4);
-  const uint32_t v_off = kPage * kCodeBytes + (vn * kPage + 4 * g) * (BITS == 8 ? 8 : 4);
-  const uint32_t km_off = 2 * kPage * kCodeBytes + 4 * kNG * n;
-  if (cb != pw0) ids4(pw0, pw1, idA);   // shorter sequence: its range starts elsewhere
-  // id_of(i) is the id of page p + i (-1 when the page is past the range)
-  auto load_with = [&](Buf& sb, int p, auto id_of) {
-    sb.all_ok = true;
-#pragma unroll
-    for (int i = 0; i < kStep; ++i) {
-      const int id = id_of(i);
-      sb.pv[i] = id >= 0 && id < a.num_pages;
-      sb.all_ok = sb.all_ok && sb.pv[i];
-      // one buffer descriptor per page slab (scalar registers): each load is
-      // that base plus the lane's 32-bit offset; nothing can reach past the
-      // slab, and a page that is not there gets an empty descriptor, whose
-      // loads return zeros without touching memory
-      const uint8_t* sl = pool_h + static_cast<int64_t>(sb.pv[i] ? id : 0) * page_stride;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, sb.pv[i] ? kSlab : 0);
-      if constexpr (kCodeBytes / 4 >= 16) {
-#pragma unroll
-        for (int j = 0; j < kKX; ++j)
-          sb.kx[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, k_off + 16 * j, 0, kStreamOnce));
-      } else {
-        const u32x2 t2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, k_off, 0, kStreamOnce));
-        sb.kx[i][0] = u32x4{t2[0], t2[1], 0u, 0u};
-      }
-#pragma unroll
-      for (int j = 0; j < kVX; ++j)
-        sb.vx[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_off + 16 * j, 0, kStreamOnce));
-      if constexpr (kNG == 1) {
-        sb.km[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off, 0, kStreamOnce);
-        sb.vm[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, km_off + 4 * kPage, 0, kStreamOnce);
-      } else if constexpr (kNG == 2) {
-        const u32x2 k2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, km_off, 0, kStreamOnce));
-        const u32x2 v2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, km_off + 8 * kPage, 0, kStreamOnce));
-        sb.km[i][0] = k2[0];
-        sb.km[i][1] = k2[1];
-        sb.vm[i][0] = v2[0];
-        sb.vm[i][1] = v2[1];
-      } else {
-        const u32x4 k4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, km_off, 0, kStreamOnce));
-        const u32x4 v4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, km_off + 16 * kPage, 0, kStreamOnce));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sb.km[i][j] = k4[j];
-          sb.vm[i][j] = v4[j];
-        }
-      }
-    }
-  };
-  // The first step's page loads go out before the query is waited for: the
-  // query was requested first, so its wait leaves the pages in flight, and
-  // its rotation and limbs are computed while they arrive.
-  Buf buf0;
-  load_with(buf0, pw0, [&](int i) { return pw0 + i < pw1 ? idA[i] : -1; });
-  ids4(pw0 + kStep, pw1, idB);
-  __builtin_amdgcn_sched_barrier(0);
-  float qv[kC];
-#pragma unroll
-  for (int k = 0; k < kC; ++k) {
-    const uint16_t u = static_cast<uint16_t>(qraw[k / 2] >> (16 * (k & 1)));
-    const float x = QBF16 ? u2f(static_cast<uint32_t>(u) << 16) : static_cast<float>(__builtin_bit_cast(_Float16, u));
-    qv[k] = qhead < G ? x : 0.0f;
-  }
-  // ---- query: rotate in registers, fixed point, limbs ------------------------
-  for (int e = tid; e < kWaves * NS * kNG * 4 * 4 * 16; e += 64 * kWaves)
-    (&sm.wl[0][0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
-  if (qwave) {
-    float v[kC];
-#pragma unroll
-    for (int k = 0; k < kC; ++k) v[k] = qv[k];
-    if (a.block > 0) {
-      fwht_row_any<kC>(v, a.block, n);
-      const float sb = block_norm(a.block);
-#pragma unroll
-      for (int k = 0; k < kC; ++k) v[k] *= sb;
-    }
-    float am = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kC; ++k) am = fmaxf(am, fabsf(v[k]));
-    am = row_max16(am);
-    int ex = 0;
-    frexpf(am, &ex);                    // am < 2^ex
-    ex = ex < -100 ? -100 : ex;         // keeps 2^(22-ex) finite; smaller q is ~0
-    const float sc = ldexpf(1.0f, 22 - ex);
-    int32_t qi[kC];
-    int32_t sum = 0;
-#pragma unroll
-    for (int k = 0; k < kC; ++k) {
-      qi[k] = static_cast<int32_t>(rintf(v[k] * sc));
-      sum += qi[k];
-    }
-#pragma unroll
-    for (int k = 0; k < kC; k += 4)
-      *reinterpret_cast<v4i*>(&sm.u.qi[qhead][kC * n + k]) = v4i{qi[k], qi[k + 1], qi[k + 2], qi[k + 3]};
-    // sum of the query over each group (|sum| <= D * 2^22: exact in int32);
-    // a lane's kC channels lie in group kC n / GS
-    int32_t gsum[kNG];
-#pragma unroll
-    for (int gi = 0; gi < kNG; ++gi) gsum[gi] = row_sum16_i(kNG == 1 || (kC * n) / (GS ? GS : D) == gi ? sum : 0);
-    if (n == 0) {
-      sm.hA[qhead] = a.sm_log2 * ldexpf(1.0f, ex - 22);
-#pragma unroll
-      for (int gi = 0; gi < kNG; ++gi) sm.hS[qhead][gi] = static_cast<float>(gsum[gi]);
-    }
-  }
-  __syncthreads();
-
-  // A operand of QK: row (head hs, limb lam), k-slots of lane group g: the
-  // lane's D/4 consecutive channels, read from LDS as whole vectors
-  const LimbSel limb(lam);
-  v4i aq[NS][kNG][kOps];   // per group: the operand with other groups' channels zeroed
-  float qA[NS], qS[NS][kNG];
-#pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    qA[st] = sm.hA[4 * st + g];          // C-layout head of this lane: row group g
-#pragma unroll
-    for (int gi = 0; gi < kNG; ++gi) qS[st][gi] = sm.hS[4 * st + g][gi];
-    int32_t qc[D / 4];
-    const v4i* src = reinterpret_cast<const v4i*>(&sm.u.qi[4 * st + hs][(D / 4) * g]);
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      const v4i x = src[t];
-      qc[4 * t] = x[0];
-      qc[4 * t + 1] = x[1];
-      qc[4 * t + 2] = x[2];
-      qc[4 * t + 3] = x[3];
-    }
-#pragma unroll
-    for (int op = 0; op < kOps; ++op) {
-      v4i vv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          w |= limb.byte(qc[qk_channel<D, BITS>(0, op, i, k)]) << (8 * k);
-        vv[i] = static_cast<int32_t>(w);
-      }
-      // lane group g holds channels [D/4 g, D/4 (g+1)): one group's
-#pragma unroll
-      for (int gi = 0; gi < kNG; ++gi) aq[st][gi][op] = (kNG == 1 || (D / 4) * g / (GS ? GS : D) == gi) ? vv : v4i{0, 0, 0, 0};
-    }
-  }
-
-  float m_run[NS], l_run[NS], z_run[NS][kNG], acc[NS][kNT];
-#pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    m_run[st] = kNegInf;
-    l_run[st] = 0.0f;
-#pragma unroll
-    for (int gi = 0; gi < kNG; ++gi) z_run[st][gi] = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kNT; ++t) acc[st][t] = 0.0f;
-  }
-  const v4i zero4 = {0, 0, 0, 0};
-  const int wl_row = (lam * 4 + hs) * 16 + 4 * g;   // reader offset within a set, dwords
-
-  auto compute = [&](const Buf& sb, int p, auto mask_tag) {
-    constexpr bool tail = decltype(mask_tag)::value;
-    // QK: lane (g, n) gets the four limb rows of head g (per set), token n
-    float lg[NS][kStep];
-#pragma unroll
-    for (int i = 0; i < kStep; ++i) {
-      v4i b0, b1;
-      if constexpr (BITS == 8) {   // code - 128 as a signed byte
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          b0[w] = static_cast<int32_t>(sb.kx[i][0][w] ^ 0x80808080u);
-          if constexpr (kKX == 2) b1[w] = static_cast<int32_t>(sb.kx[i][1][w] ^ 0x80808080u);
-        }
-      } else if constexpr (D == 128) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          b0[w] = static_cast<int32_t>(sb.kx[i][0][w] & kLowNibbles);
-          b1[w] = static_cast<int32_t>((sb.kx[i][0][w] >> 4) & kLowNibbles);
-        }
-      } else {
-        b0 = v4i{static_cast<int32_t>(sb.kx[i][0][0] & kLowNibbles), static_cast<int32_t>(sb.kx[i][0][1] & kLowNibbles),
-                 static_cast<int32_t>((sb.kx[i][0][0] >> 4) & kLowNibbles),
-                 static_cast<int32_t>((sb.kx[i][0][1] >> 4) & kLowNibbles)};
-      }
-      const int tok = (p + i) * kPage + n;
-      const bool ok = !tail || (sb.pv[i] && tok >= lo && tok < hi);
-      if constexpr (kOnePass) {
-        // zero point of the codes as the MFMA sees them
-        const uint32_t km = sb.km[i][0];
-        const float kzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(km), half_hi(km)) : half_hi(km);
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          v4i c = mfma_i8(aq[st][0][0], b0, zero4);
-          if constexpr (kOps == 2) c = mfma_i8(aq[st][0][1], b1, c);
-          // limbs: c0 * 2^16 + c1 * 2^8 + c2 (c0 * 2^8 + c1 is exact in int32)
-          const float tq = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f,
-                                          static_cast<float>(c[2]));
-          const float l2 = qA[st] * __builtin_fmaf(kzero, qS[st][0], half_lo(km) * tq);
-          lg[st][i] = ok ? l2 : kNegInf;
-        }
-        continue;
-      }
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        float dot = 0.0f;
-#pragma unroll
-        for (int gi = 0; gi < kNG; ++gi) {
-          v4i c = mfma_i8(aq[st][gi][0], b0, zero4);
-          if constexpr (kOps == 2) c = mfma_i8(aq[st][gi][1], b1, c);
-          // limbs: c0 * 2^16 + c1 * 2^8 + c2 (c0 * 2^8 + c1 is exact in int32)
-          const float tq = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f,
-                                          static_cast<float>(c[2]));
-          // zero point of the codes as the MFMA sees them
-          const uint32_t km = sb.km[i][gi];
-          const float kzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(km), half_hi(km)) : half_hi(km);
-          dot = gi == 0 ? __builtin_fmaf(kzero, qS[st][0], half_lo(km) * tq)
-                        : dot + __builtin_fmaf(kzero, qS[st][gi], half_lo(km) * tq);
-        }
-        lg[st][i] = ok ? qA[st] * dot : kNegInf;
-      }
-    }
-
-    // online softmax (row = head) and the limbs of w = p * v_scale through LDS
-    float alpha[NS], sw[NS][kNG];
-    // w = p * v_scale as a 23-bit fixed-point integer relative to the step's
-    // largest w of the head (power-of-two scale sw), three int8 limbs of it
-    // into the LDS tile of (set st, group gi)
-    auto store_limbs = [&](int st, int gi, const float* w, float wmax) {
-      wmax = row_max16(wmax);
-      int ew = 0;
-      frexpf(wmax, &ew);                 // wmax < 2^ew
-      ew = ew < -100 ? -100 : ew;        // such a step weighs < 2^-76 of the max
-      const float wsc = ldexpf(1.0f, 22 - ew);
-      sw[st][gi] = ldexpf(1.0f, ew - 22);
-      uint32_t y[kStep];
-#pragma unroll
-      for (int i = 0; i < kStep; ++i)
-        y[i] = static_cast<uint32_t>(static_cast<int32_t>(rintf(w[i] * wsc)) + 0x8080);
-      // limb bytes of the four pages, one word per limb: bytes 2 / 1 / 0 of y
-      const uint32_t l0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0602u),
-                                                __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0602u), 0x05040100u);
-      const uint32_t l1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0501u),
-                                                __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0501u), 0x05040100u) ^ 0x80808080u;
-      const uint32_t l2w = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0400u),
-                                                 __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0400u), 0x05040100u) ^ 0x80808080u;
-      uint32_t* wl = &sm.wl[wave][st][gi][0][0][0];
-      wl[(0 * 4 + g) * 16 + n] = l0;
-      wl[(1 * 4 + g) * 16 + n] = l1;
-      wl[(2 * 4 + g) * 16 + n] = l2w;
-    };
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      float mc = lg[st][0];
-#pragma unroll
-      for (int i = 1; i < kStep; ++i) mc = fmaxf(mc, lg[st][i]);
-      mc = row_max16(mc);
-      const float mnew = fmaxf(m_run[st], mc);
-      const float muse = mnew == kNegInf ? 0.0f : mnew;
-      alpha[st] = exp2f(m_run[st] - muse);
-      m_run[st] = mnew;
-      if constexpr (kOnePass) {   // one scale/zero per vector: a single pass over the step
-        float psum = 0.0f, zsum = 0.0f, wmax = 0.0f, w[kStep];
-#pragma unroll
-        for (int i = 0; i < kStep; ++i) {
-          const float pp = exp2f(lg[st][i] - muse);
-          psum += pp;
-          const uint32_t vm = sb.vm[i][0];
-          const float vzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(vm), half_hi(vm)) : half_hi(vm);
-          if (tail) {
-            const bool ok = lg[st][i] != kNegInf;
-            zsum += ok ? pp * vzero : 0.0f;
-            w[i] = ok ? pp * half_lo(vm) : 0.0f;
-          } else {
-            zsum = __builtin_fmaf(pp, vzero, zsum);
-            w[i] = pp * half_lo(vm);
-          }
-          wmax = fmaxf(wmax, w[i]);
-        }
-        l_run[st] = __builtin_fmaf(l_run[st], alpha[st], psum);
-        z_run[st][0] = __builtin_fmaf(z_run[st][0], alpha[st], zsum);
-        store_limbs(st, 0, w, wmax);
-        continue;
-      }
-      float pp[kStep], psum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kStep; ++i) {
-        pp[i] = exp2f(lg[st][i] - muse);
-        psum += pp[i];
-      }
-      l_run[st] = __builtin_fmaf(l_run[st], alpha[st], psum);
-#pragma unroll
-      for (int gi = 0; gi < kNG; ++gi) {
-        float zsum = 0.0f, wmax = 0.0f, w[kStep];
-#pragma unroll
-        for (int i = 0; i < kStep; ++i) {
-          const uint32_t vm = sb.vm[i][gi];
-          const float vzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(vm), half_hi(vm)) : half_hi(vm);
-          if (tail) {
-            const bool ok = lg[st][i] != kNegInf;
-            zsum += ok ? pp[i] * vzero : 0.0f;
-            w[i] = ok ? pp[i] * half_lo(vm) : 0.0f;
-          } else {
-            zsum = __builtin_fmaf(pp[i], vzero, zsum);
-            w[i] = pp[i] * half_lo(vm);
-          }
-          wmax = fmaxf(wmax, w[i]);
-        }
-        z_run[st][gi] = __builtin_fmaf(z_run[st][gi], alpha[st], zsum);
-        store_limbs(st, gi, w, wmax);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
-    __builtin_amdgcn_wave_barrier();
-    v4i apv[NS][kNG];
-#pragma unroll
-    for (int st = 0; st < NS; ++st)
-#pragma unroll
-      for (int gi = 0; gi < kNG; ++gi)
-        apv[st][gi] = *reinterpret_cast<const v4i*>(&sm.wl[wave][st][gi][0][0][0] + wl_row);
-
-    // V: per token r of the lane group, transpose across four pages so a
-    // word holds the four pages' codes of one channel pair (4-bit: nibbles
-    // split it) or of one channel (8-bit, then made signed).
-    uint32_t vt[4][kVX][4];   // [r][half][byte j]
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int hh = 0; hh < kVX; ++hh) {
-        // 4-bit: dword r of the piece is token 4g+r; 8-bit: dwords
-        // 2(r&1)+hh of piece r>>1 are token 4g+r, channels 4hh..4hh+3
-        auto src = [&](int pg) {
-          return BITS == 8 ? sb.vx[pg][r >> 1][2 * (r & 1) + hh] : sb.vx[pg][0][r];
-        };
-        transpose_bytes4(src(0), src(1), src(2), src(3), vt[r][hh]);
-      }
-#pragma unroll
-    for (int tau = 0; tau < kNT; ++tau) {
-      v4i bv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t yv;
-        if constexpr (BITS == 8) {
-          if constexpr (D == 128) {   // channel 8n + tau
-            yv = vt[r][tau >> 2][tau & 3];
-          } else {                    // channel 8(n&7) + 2tau + (n>>3)
-            const uint32_t* h4 = vt[r][tau >> 1];
-            yv = (n >> 3) ? h4[2 * (tau & 1) + 1] : h4[2 * (tau & 1)];
-          }
-          yv ^= 0x80808080u;
-        } else {   // nibble tau (D = 128) or 2tau + (n>>3) (D = 64) of the word
-          if constexpr (D == 128) yv = (tau & 1) ? (vt[r][0][tau >> 1] >> 4) : vt[r][0][tau >> 1];
-          else yv = vt[r][0][tau] >> (4 * (n >> 3));
-          yv &= kLowNibbles;
-        }
-        bv[r] = static_cast<int32_t>(yv);
-      }
-      // the tile's group: its channels n + 16 tau (D = 128) or
-      // (n&7) + 16 tau + 8 (n>>3) (D = 64) all lie in group 16 tau / GS
-      constexpr int kTileGroupDiv = GS ? GS : 16 * kNT;
-      const int gi = 16 * tau / kTileGroupDiv;
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const v4i c = mfma_i8(apv[st][gi], bv, zero4);
-        const float f = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f,
-                                       static_cast<float>(c[2]));
-        acc[st][tau] = __builtin_fmaf(f, sw[st][gi], acc[st][tau] * alpha[st]);
-      }
-    }
-  };
-
-  // ---- stream the wave's pages ----------------------------------------------
-  auto step = [&](const Buf& sb, int p) {
-    if (!sb.all_ok || (p + kStep) * kPage > hi || p * kPage < lo)
-      compute(sb, p, std::true_type{});
-    else
-      compute(sb, p, std::false_type{});
-  };
-  if constexpr (kPrefetch) {
-    // The next step's loads go out before this step is computed, so a wave
-    // keeps a step in flight while it computes, and the ids of the step after
-    // that are fetched meanwhile.  With two sets of heads a step computes long
-    // enough that the two waves per SIMD would otherwise leave the SIMD's
-    // loads idle much of the time.  The loads are issued whether or not their
-    // step exists (its pages then have empty descriptors), so each wait for a
-    // step's data leaves the following step's loads in flight.
-    Buf buf1;
-    for (int p = pw0; p < pw1; p += 2 * kStep) {
-      load_with(buf1, p + kStep, [&](int i) { return p + kStep + i < pw1 ? idB[i] : -1; });
-      ids4(p + 2 * kStep, pw1, idA);
-      step(buf0, p);
-      if (p + kStep >= pw1) break;
-      load_with(buf0, p + 2 * kStep, [&](int i) { return p + 2 * kStep + i < pw1 ? idA[i] : -1; });
-      ids4(p + 3 * kStep, pw1, idB);
-      step(buf1, p + kStep);
-    }
-  } else {
-    // One step at a time: its four pages are loaded, then computed.  While a
-    // wave computes, the other waves of its SIMD keep loads in flight (with
-    // one set of heads an in-register prefetch of the next step measured
-    // slower: more VGPRs, fewer waves).
-    for (int p = pw0; p < pw1; p += kStep) {
-      step(buf0, p);
-      if (p + kStep >= pw1) break;
-      load_with(buf0, p + kStep, [&](int i) { return p + kStep + i < pw1 ? idB[i] : -1; });
-      ids4(p + 2 * kStep, pw1, idB);
-    }
-  }
-
-  // ---- merge the four waves --------------------------------------------------
-  __syncthreads();   // the query scratch is reused below
-#pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    const float lt = row_sum16(l_run[st]);
-    float zt[kNG];
-#pragma unroll
-    for (int gi = 0; gi < kNG; ++gi) zt[gi] = row_sum16(z_run[st][gi]);
-    const int j = 4 * st + g;            // PV-layout head = row group
-#pragma unroll
-    for (int tau = 0; tau < kNT; ++tau)
-      sm.u.merge.acc[wave][j][pv_channel<D, GS>(n, tau)] = acc[st][tau] + zt[16 * tau / (GS ? GS : 16 * kNT)];
-    if (n == 0) {
-      sm.u.merge.m[wave][j] = m_run[st];
-      sm.u.merge.l[wave][j] = lt;
-    }
-  }
-  __syncthreads();
-  if (qwave) {   // wave w < NS finishes heads 4w .. 4w+3, one per row of 16 lanes
-    const int j = qhead;
-    float mstar = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, sm.u.merge.m[w][j]);
-    const float muse = mstar == kNegInf ? 0.0f : mstar;
-    float f[kWaves], lsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      f[w] = exp2f(sm.u.merge.m[w][j] - muse);
-      lsum = __builtin_fmaf(sm.u.merge.l[w][j], f[w], lsum);
-    }
-    float o[kC];
-#pragma unroll
-    for (int k = 0; k < kC; ++k) o[k] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-      for (int k = 0; k < kC; k += 4) {
-        const v4f x = *reinterpret_cast<const v4f*>(&sm.u.merge.acc[w][j][kC * n + k]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[k + i] = __builtin_fmaf(x[i], f[w], o[k + i]);
-      }
-    // back to the original basis; with several splits each partial is
-    // rotated here (the merge is a weighted sum, so it commutes)
-    float scale = 1.0f;
-    if (a.block > 0) {   // every row takes part: the butterfly reads its neighbours
-      fwht_row_any<kC>(o, a.block, n);
-      scale = block_norm(a.block);
-    }
-    if (a.nsplit == 1 && !a.force_partial) {
-      scale *= lsum > 0.0f ? 1.0f / lsum : 0.0f;
-      if (j < G) {
-        float* dst = a.out + (hq0 + j) * D + kC * n;
-#pragma unroll
-        for (int k = 0; k < kC; k += 4)
-          *reinterpret_cast<v4f*>(dst + k) = v4f{o[k] * scale, o[k + 1] * scale, o[k + 2] * scale, o[k + 3] * scale};
-      }
-    } else if (j < G) {
-      const int64_t idx = (hq0 + j) * a.part_stride + a.part_slot0 + s;
-      float* dst = a.part_acc + idx * D + kC * n;
-#pragma unroll
-      for (int k = 0; k < kC; k += 4)
-        *reinterpret_cast<v4f*>(dst + k) = v4f{o[k] * scale, o[k + 1] * scale, o[k + 2] * scale, o[k + 3] * scale};
-      if (n == 0) {
-        a.part_ml[idx * 2 + 0] = mstar;
-        a.part_ml[idx * 2 + 1] = lsum;
-      }
-    }
-  }
+  q4::decode_quant_body<D, NS, QBF16, BITS, GS, WPE>(a, blockIdx.x);
 }
 
 template <int D, int NS, int BITS, int GS, int WPE>

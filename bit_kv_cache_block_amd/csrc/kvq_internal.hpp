@@ -21,14 +21,6 @@ struct AppendArgs {
   int32_t block;             // Hadamard block (0 = none); unused by the bf16 pool
   int32_t in_bf16;           // 1: inputs are bf16, 0: fp16
   int32_t group;             // channels per scale/zero pair (grouped INT4 pool only)
-  // Window pass that also finishes the call (fin_splits > 0): after its own
-  // share it merges the fin_splits INT4 partials of each (sequence, query
-  // head), whose pass skipped fin_skip_first / fin_skip_last tokens in splits
-  // of fin_split_pages pages, and writes the normalised output.
-  int32_t fin_splits;
-  int32_t fin_split_pages;
-  int32_t fin_skip_first;
-  int32_t fin_skip_last;
 };
 
 struct DecodeArgs {
@@ -64,14 +56,11 @@ struct DecodeArgs {
   int32_t part_slot0;
   int32_t force_partial;
   int32_t group;             // channels per scale/zero pair (grouped INT4 pool only)
-  // Window pass that also finishes the call (fin_splits > 0): after its own
-  // share it merges the fin_splits INT4 partials of each (sequence, query
-  // head), whose pass skipped fin_skip_first / fin_skip_last tokens in splits
-  // of fin_split_pages pages, and writes the normalised output.
-  int32_t fin_splits;
-  int32_t fin_split_pages;
-  int32_t fin_skip_first;
-  int32_t fin_skip_last;
+  // Split merge of a windowed call (has_window = 1): the last slot of each
+  // row holds the bf16 window pass's partial, which exists when the sequence
+  // has a token among its first win_len positions.
+  int32_t has_window;
+  int32_t win_len;
 };
 
 // Split-K plan shared by the launch and the workspace query.
@@ -93,5 +82,8 @@ hipError_t launch_decode_int4g(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mxfp4(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t s);
+// One grid of the bf16 window workgroups (aw, one split) and the INT4
+// workgroups (a4), both storing partials.
+hipError_t launch_decode_windowed(const DecodeArgs& a4, const DecodeArgs& aw, hipStream_t s);
 
 }  // namespace kvq

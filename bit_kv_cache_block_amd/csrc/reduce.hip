@@ -1,6 +1,7 @@
 // Split-K merge: for each (sequence, query head) combine the partials (max,
 // sum, unnormalised output) of its splits with the log-sum-exp rule and
-// normalise.  The decode kernels store each partial already rotated back to
+// normalise.  In a windowed call the last slot of each row is the bf16 window
+// pass's partial.  The decode kernels store each partial already rotated back to
 // the original basis (the rotation is linear and the merge is a weighted
 // sum), so nothing is rotated here.
 //
@@ -58,7 +59,10 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     for (int s = g; s < a.part_stride; s += G) {
       const float ms = ml[2 * s], ls = ml[2 * s + 1];
       const v4f x = *reinterpret_cast<const v4f*>(pa + static_cast<int64_t>(s) * D);
-      const bool ok = hi > lo && max(s * a.split_pages, pfirst) < min(npg, (s + 1) * a.split_pages);
+      // INT4 split s, or (windowed calls) the window pass's slot, the last
+      const bool ok = (a.has_window && s == a.part_stride - 1)
+                          ? min(len, a.win_len) > 0
+                          : hi > lo && max(s * a.split_pages, pfirst) < min(npg, (s + 1) * a.split_pages);
       const float mn = ok ? fmaxf(m, ms) : m;
       const float mu = mn == -__builtin_inff() ? 0.0f : mn;
       const float fo = exp2f(m - mu), fs = exp2f(ms - mu);

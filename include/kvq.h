@@ -243,9 +243,10 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  * attended with the unrotated query; the tokens in between are read from the
  * INT4 cache as in kvq_decode_attn.  The result is the one softmax over all
  * L tokens (the INT4 share rotated back), obtained by the log-sum-exp merge
- * of the INT4 split partials and the window pass.  Two launches: the INT4
- * pass stores its split partials in the workspace; the window pass, after it
- * on the stream, merges them with its own share and writes `out`.
+ * of the INT4 split partials and the window pass.  Two launches: one grid
+ * of the window and INT4 workgroups stores every partial in the workspace
+ * (the window's in the last slot of each row); the split merge then writes
+ * `out`.
  *
  * Window layout: window position of token t is t when t < w_sink, else
  * w_sink + (t - w_sink) mod w_recent (a ring of the recent tokens: a new
@@ -272,8 +273,8 @@ kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_
                                     size_t workspace_bytes, void* stream);
 
 /* Workspace bytes kvq_decode_attn_windowed needs: one partial per INT4
- * split, batch * num_q_heads * splits * (head_dim + 2) floats (always > 0 for
- * batch > 0). */
+ * split and one for the window pass, batch * num_q_heads * (splits + 1) *
+ * (head_dim + 2) floats (always > 0 for batch > 0). */
 size_t kvq_decode_windowed_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t max_seq_len, int32_t num_splits);
 

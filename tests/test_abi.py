@@ -242,11 +242,12 @@ def test_windowed_decode_rejects_mismatched_window_pool():
     assert _windowed(_int4(), kvq._Bf16Desc(FAKE, 4, 16, 2, 128)) == kvq.KVQ_ERR_INVALID_ARGUMENT
 
 
-def test_windowed_workspace_holds_a_partial_per_split():
-    """The INT4 pass always stores partials (the window pass merges them), so
-    even one split needs a slot; split counts match kvq_decode_attn's."""
+def test_windowed_workspace_holds_a_partial_per_split_and_the_window():
+    """The INT4 pass always stores partials and the window pass stores one
+    more per row (the split merge finishes the call), so even one split needs
+    two slots; split counts match kvq_decode_attn's."""
     for maxlen in (16, 4096, 131072):
         plain = kvq.kvq_decode_workspace_bytes(4, 8, 2, 64, maxlen, 0)
         win = kvq.kvq_decode_windowed_workspace_bytes(4, 8, 2, 64, maxlen, 0)
         row = 4 * 8 * (64 + 2) * 4
-        assert win == (plain if plain else row)
+        assert win == (plain if plain else row) + row
