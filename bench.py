@@ -82,7 +82,7 @@ def _src_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-DECODE_SOURCES = ("decode_int4.hip", "decode_int4_body.hpp", "dev_common.hpp", "kvq_internal.hpp")
+DECODE_SOURCES = ("decode_int4.hip", "decode_int4_launch.hpp", "decode_int4_body.hpp", "dev_common.hpp", "kvq_internal.hpp")
 
 
 def _traffic(alg_bytes: int):

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "kvq")
 LIB = os.path.join(PKG, "libkvq.so")
 
-SOURCES = ["api.cpp", "append.hip", "decode_int4.hip", "decode_mxfp4.hip", "decode_bf16.hip", "decode_windowed.hip", "reduce.hip"]
+SOURCES = ["api.cpp", "append.hip", "decode_int4.hip", "decode_int4_bal.hip", "decode_mxfp4.hip", "decode_bf16.hip", "decode_windowed.hip", "reduce.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

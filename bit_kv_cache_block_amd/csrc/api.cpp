@@ -112,6 +112,16 @@ SplitPlan plan_splits(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t n
   return SplitPlan{static_cast<int32_t>(sp), static_cast<int32_t>(s)};
 }
 
+// The device may grow the splits (balanced_split_pages) for a small batch cut
+// into many splits (16 or more: long contexts) whose whole work could exceed
+// about 512 workgroups of the planned size; otherwise the plan stands and the
+// kernels skip the scan of the lengths.
+bool may_balance(int32_t batch, int32_t hkv, int32_t max_seq_len, const SplitPlan& p) {
+  if (p.nsplit < 16 || batch > kBalanceMaxBatch) return false;
+  const int64_t pages_max = (static_cast<int64_t>(max_seq_len) + 15) / 16;
+  return pages_max * batch * hkv > static_cast<int64_t>(p.split_pages) * 512;
+}
+
 size_t workspace_bytes(int32_t batch, int32_t hq, int32_t d, const SplitPlan& p) {
   if (p.nsplit <= 1) return 0;   // unsplit work writes the output directly
   return static_cast<size_t>(batch) * hq * p.nsplit * (d + 2) * sizeof(float);
@@ -166,6 +176,7 @@ kvq_status launch_decode(Pool kind, const void* pool, int32_t num_pages, int32_t
   a.in_bf16 = dtype == KVQ_BF16;
   a.part_stride = plan.nsplit;
   a.group = group;
+  a.balance = may_balance(batch, hkv, max_seq_len, plan);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = kind == Pool::kInt4    ? launch_decode_int4(a, s)
                  : kind == Pool::kInt8  ? launch_decode_int8(a, s)
@@ -464,6 +475,7 @@ kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_
   a.skip_last = w_recent;
   a.part_stride = stride;
   a.force_partial = 1;
+  a.balance = may_balance(batch, hkv, max_seq_len, plan);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (wlen > 0) {
@@ -479,6 +491,7 @@ kvq_status kvq_decode_attn_windowed(const kvq_int4_cache* cache, const kvq_bf16_
     w.len_cap = static_cast<int32_t>(wlen);
     w.split_pages = static_cast<int32_t>((wlen + 15) / 16 + 3) / 4 * 4;
     w.nsplit = 1;
+    w.balance = 0;
     w.part_slot0 = plan.nsplit;
     e = launch_decode_windowed(a, w, s);
     a.has_window = 1;

@@ -11,19 +11,24 @@ namespace {
 
 using b16::kWaves;
 
-template <int D, int NS, bool QBF16>
+template <int D, int NS, bool QBF16, bool BAL>
 __global__ __launch_bounds__(64 * kWaves) void decode_bf16_kernel(DecodeArgs a) {
-  b16::decode_bf16_body<D, NS, QBF16>(a, blockIdx.x);
+  b16::decode_bf16_body<D, NS, QBF16, BAL>(a, blockIdx.x);
+}
+
+template <int D, int NS, bool BAL>
+hipError_t launch_b(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.nsplit) * a.num_kv_heads * a.batch);
+  if (a.in_bf16)
+    decode_bf16_kernel<D, NS, true, BAL><<<grid, 64 * kWaves, 0, s>>>(a);
+  else
+    decode_bf16_kernel<D, NS, false, BAL><<<grid, 64 * kWaves, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int D, int NS>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.nsplit) * a.num_kv_heads * a.batch);
-  if (a.in_bf16)
-    decode_bf16_kernel<D, NS, true><<<grid, 64 * kWaves, 0, s>>>(a);
-  else
-    decode_bf16_kernel<D, NS, false><<<grid, 64 * kWaves, 0, s>>>(a);
-  return hipGetLastError();
+  return a.balance ? launch_b<D, NS, true>(a, s) : launch_b<D, NS, false>(a, s);
 }
 
 template <int D>

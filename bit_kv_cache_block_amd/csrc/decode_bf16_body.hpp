@@ -62,7 +62,9 @@ struct SmemB {
   uint16_t pl[kWaves][NS][4][4][kStep][16];   // [wave][set][limb][head][page][token]
 };
 
-template <int D, int NS, bool QBF16>
+// BAL: a balanced call (balanced_split_pages), built apart so that the
+// planned calls carry none of its code
+template <int D, int NS, bool QBF16, bool BAL>
 __device__ __forceinline__ void decode_bf16_body(const DecodeArgs& a, uint32_t wid) {
   constexpr int kSlab = 4 * kPage * D;   // bytes
   constexpr int kNT = D / 16;
@@ -82,15 +84,23 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeArgs& a, uint32_t w
   // for the longest sequences, start first instead of last.
   const int kvh = static_cast<int>(wid % a.num_kv_heads);
   const int b = static_cast<int>((wid / a.num_kv_heads) % a.batch);
-  const int s = a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
+  // pages per split, and the split: last first, unless the device grew the
+  // splits (then the later ones are empty, and first-split-first keeps them
+  // from holding the machine before the work starts)
+  const int sp = BAL ? balanced_split_pages(a.split_pages, a.seq_lens, a.batch, a.max_seq_len,
+                                            a.num_kv_heads)
+                     : a.split_pages;
+  const int s = BAL && sp != a.split_pages
+                    ? static_cast<int>(wid / a.num_kv_heads / a.batch)
+                    : a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
   const int G = a.num_q_heads / a.num_kv_heads;
 
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
   if (a.len_cap > 0 && len > a.len_cap) len = a.len_cap;   // window pass: the window's tokens
   const int npg = (len + kPage - 1) / kPage;
-  const int p0 = s * a.split_pages;
-  const int p1 = min(npg, p0 + a.split_pages);
+  const int p0 = s * sp;
+  const int p1 = min(npg, p0 + sp);
   if (p0 >= p1) {
     if (a.nsplit == 1 && !a.force_partial) {
       for (int e = tid; e < G * D; e += 64 * kWaves)

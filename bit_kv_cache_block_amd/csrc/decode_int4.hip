@@ -36,63 +36,20 @@
 // channels; V is stored so that each PV tile of 16 output channels lies in
 // one group, so PV keeps one product per tile, with the softmax weights of
 // that group (w = p * v_scale of the group) as its operand.
-#include "decode_int4_body.hpp"
+#include "decode_int4_launch.hpp"
 
 namespace kvq {
-namespace {
-
-using q4::kWaves;
-
-template <int D, int NS, bool QBF16, int BITS, int GS, int WPE>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(WPE)))
-void decode_quant_kernel(DecodeArgs a) {
-  q4::decode_quant_body<D, NS, QBF16, BITS, GS, WPE>(a, blockIdx.x);
-}
-
-template <int D, int NS, int BITS, int GS, int WPE>
-hipError_t launch_w(const DecodeArgs& a, hipStream_t s, unsigned wgs) {
-  if (a.in_bf16)
-    decode_quant_kernel<D, NS, true, BITS, GS, WPE><<<dim3(wgs), 64 * kWaves, 0, s>>>(a);
-  else
-    decode_quant_kernel<D, NS, false, BITS, GS, WPE><<<dim3(wgs), 64 * kWaves, 0, s>>>(a);
-  return hipGetLastError();
-}
-
-template <int D, int NS, int BITS, int GS>
-hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
-  const unsigned wgs = static_cast<unsigned>(a.nsplit) * a.num_kv_heads * a.batch;
-  // The 4-byte-sidecar INT4 kernel for one set of heads needs a few VGPRs more
-  // than 128.  When the grid is larger than 512 workgroups (two per CU), a
-  // build held to 128 VGPRs (4 waves per SIMD) keeps more of it resident:
-  // measured 7% faster at 1024 workgroups, 2% slower at 512.
-  if constexpr (NS == 1 && BITS == 4 && GS == 0) {
-    if (wgs > 512) return launch_w<D, NS, BITS, GS, 4>(a, s, wgs);
-  }
-  return launch_w<D, NS, BITS, GS, 1>(a, s, wgs);
-}
-
-template <int D, int BITS, int GS>
-hipError_t launch_ns(const DecodeArgs& a, hipStream_t s) {
-  const int g = a.num_q_heads / a.num_kv_heads;
-  if (g <= 4) return launch_d<D, 1, BITS, GS>(a, s);
-  if (g <= 8) return launch_d<D, 2, BITS, GS>(a, s);
-  return launch_d<D, 4, BITS, GS>(a, s);
-}
-
-}  // namespace
 
 hipError_t launch_decode_int4(const DecodeArgs& a, hipStream_t s) {
-  return a.head_dim == 128 ? launch_ns<128, 4, 0>(a, s) : launch_ns<64, 4, 0>(a, s);
+  return a.balance ? launch_decode_quant_balanced(a, 4, 0, s) : launch_format<false>(a, 4, 0, s);
 }
 
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t s) {
-  return a.head_dim == 128 ? launch_ns<128, 8, 0>(a, s) : launch_ns<64, 8, 0>(a, s);
+  return a.balance ? launch_decode_quant_balanced(a, 8, 0, s) : launch_format<false>(a, 8, 0, s);
 }
 
 hipError_t launch_decode_int4g(const DecodeArgs& a, hipStream_t s) {
-  if (a.head_dim == 128)
-    return a.group == 32 ? launch_ns<128, 4, 32>(a, s) : launch_ns<128, 4, 64>(a, s);
-  return a.group == 32 ? launch_ns<64, 4, 32>(a, s) : launch_ns<64, 4, 64>(a, s);
+  return a.balance ? launch_decode_quant_balanced(a, 4, a.group, s) : launch_format<false>(a, 4, a.group, s);
 }
 
 }  // namespace kvq

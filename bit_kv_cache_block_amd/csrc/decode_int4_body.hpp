@@ -62,8 +62,10 @@ struct StepBuf {
   bool all_ok;
 };
 
-// WPE: waves per SIMD the register allocation must allow (1 = no limit)
-template <int D, int NS, bool QBF16, int BITS, int GS, int WPE>
+// WPE: waves per SIMD the register allocation must allow (1 = no limit);
+// BAL: a balanced call (balanced_split_pages), built apart so that the
+// planned calls carry none of its code
+template <int D, int NS, bool QBF16, int BITS, int GS, int WPE, bool BAL>
 __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t wid) {
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
   static_assert(GS == 0 || (BITS == 4 && (GS == 32 || GS == 64) && GS <= D), "groups of 32 or 64 channels, 4-bit");
@@ -98,7 +100,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   // for the longest sequences, start first instead of last.
   const int kvh = static_cast<int>(wid % a.num_kv_heads);
   const int b = static_cast<int>((wid / a.num_kv_heads) % a.batch);
-  const int s = a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
+  const int s_plan = a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
 
@@ -127,10 +129,11 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   // Page ids come by scalar loads (wave-uniform addresses, always inside the
   // row), a step ahead of the page loads that use them, so they never wait
   // behind vector loads.  The first step's ids are fetched at once for the
-  // range a full-length split gives this wave, and again only if the
-  // sequence is shorter and its balanced range starts elsewhere.
-  const int p0 = s * a.split_pages;
-  const int per_wave_full = ((a.split_pages + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
+  // range a full-length split of the host's plan gives this wave, and again
+  // only if the sequence is shorter (its balanced range starts elsewhere) or
+  // the split grew.
+  const int p0_plan = s_plan * a.split_pages;
+  const int per_wave_plan = ((a.split_pages + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
   using ConstI32 = const __attribute__((address_space(4))) int32_t;
   ConstI32* bt_s = (ConstI32*)bt;   // generic to constant address space
@@ -140,9 +143,18 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
 #pragma unroll
     for (int i = 0; i < kStep; ++i) id[i] = bt_s[min(p + i, lim - 1)];
   };
-  const int cb = p0 + wave * per_wave_full;
+  const int cb = p0_plan + wave * per_wave_plan;
   int32_t idA[kStep], idB[kStep];
-  ids4(cb, min(p0 + a.split_pages, a.bt_stride), idA);
+  ids4(cb, min(p0_plan + a.split_pages, a.bt_stride), idA);
+  // pages per split, and the split: last first, unless the device grew the
+  // splits (then the later ones are empty, and first-split-first keeps them
+  // from holding the machine before the work starts)
+  const int sp = BAL ? balanced_split_pages(a.split_pages, a.seq_lens, a.batch, a.max_seq_len,
+                                            a.num_kv_heads)
+                     : a.split_pages;
+  const bool grown = BAL && sp != a.split_pages;
+  const int s = grown ? static_cast<int>(wid / a.num_kv_heads / a.batch) : s_plan;
+  const int p0 = s * sp;
 
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
@@ -150,7 +162,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
   const int npg = (hi + kPage - 1) / kPage;
   const int q0 = max(p0, lo / kPage);
-  const int p1 = min(npg, p0 + a.split_pages);
+  const int p1 = min(npg, p0 + sp);
   if (q0 >= p1 || hi <= lo) {
     if (a.nsplit == 1 && !a.force_partial) {   // empty sequence: zero output rows
       for (int e = tid; e < G * D; e += 64 * kWaves) a.out[hq0 * D + e] = 0.0f;
@@ -173,7 +185,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   const uint32_t k_off = n * kCodeBytes + g * (kCodeBytes / 4);
   const uint32_t v_off = kPage * kCodeBytes + (vn * kPage + 4 * g) * (BITS == 8 ? 8 : 4);
   const uint32_t km_off = 2 * kPage * kCodeBytes + 4 * kNG * n;
-  if (cb != pw0) ids4(pw0, pw1, idA);   // shorter sequence: its range starts elsewhere
+  if (cb != pw0 || grown) ids4(pw0, pw1, idA);   // the range starts elsewhere
   // id_of(i) is the id of page p + i (-1 when the page is past the range)
   auto load_with = [&](Buf& sb, int p, auto id_of) {
     sb.all_ok = true;

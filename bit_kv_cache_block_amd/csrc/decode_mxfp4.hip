@@ -72,7 +72,9 @@ __device__ __forceinline__ uint32_t e2m1x2_to_i8(uint32_t codes) {
   return (neg & sel) | (pos & ~sel);
 }
 
-template <int NS, bool QBF16>
+// BAL: a balanced call (balanced_split_pages), built apart so that the
+// planned calls carry none of its code
+template <int NS, bool QBF16, bool BAL>
 __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a) {
   constexpr int D = kD;
   constexpr int kSlab = kPage * (D + D / 16);
@@ -89,7 +91,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
   const uint32_t wid = blockIdx.x;
   const int kvh = static_cast<int>(wid % a.num_kv_heads);
   const int b = static_cast<int>((wid / a.num_kv_heads) % a.batch);
-  const int s = a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
+  // pages per split, and the split: last first, unless the device grew the
+  // splits (then the later ones are empty, and first-split-first keeps them
+  // from holding the machine before the work starts)
+  const int sp = BAL ? balanced_split_pages(a.split_pages, a.seq_lens, a.batch, a.max_seq_len,
+                                            a.num_kv_heads)
+                     : a.split_pages;
+  const int s = BAL && sp != a.split_pages
+                    ? static_cast<int>(wid / a.num_kv_heads / a.batch)
+                    : a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
 
@@ -102,12 +112,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) qraw[i] = t[i];
   }
-  const int p0 = s * a.split_pages;
+  const int p0 = s * sp;
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
   const int npg = (len + kPage - 1) / kPage;
-  const int p1 = min(npg, p0 + a.split_pages);
+  const int p1 = min(npg, p0 + sp);
   if (p0 >= p1) {
     if (a.nsplit == 1) {
       for (int e = tid; e < G * D; e += 64 * kWaves) a.out[hq0 * D + e] = 0.0f;
@@ -436,14 +446,19 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
   }
 }
 
-template <int NS>
-hipError_t launch_mx(const DecodeArgs& a, hipStream_t s) {
+template <int NS, bool BAL>
+hipError_t launch_b(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.nsplit) * a.num_kv_heads * a.batch);
   if (a.in_bf16)
-    decode_mxfp4_kernel<NS, true><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_mxfp4_kernel<NS, true, BAL><<<grid, 64 * kWaves, 0, s>>>(a);
   else
-    decode_mxfp4_kernel<NS, false><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_mxfp4_kernel<NS, false, BAL><<<grid, 64 * kWaves, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int NS>
+hipError_t launch_mx(const DecodeArgs& a, hipStream_t s) {
+  return a.balance ? launch_b<NS, true>(a, s) : launch_b<NS, false>(a, s);
 }
 
 }  // namespace

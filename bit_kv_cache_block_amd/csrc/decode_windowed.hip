@@ -14,25 +14,32 @@ namespace {
 
 static_assert(b16::kWaves == q4::kWaves, "one workgroup shape");
 
-template <int D, int NS, bool QBF16>
+// BAL: the INT4 pass is a balanced call (balanced_split_pages; the window
+// pass never is)
+template <int D, int NS, bool QBF16, bool BAL>
 __global__ __launch_bounds__(64 * q4::kWaves) void decode_windowed_kernel(DecodeArgs a4, DecodeArgs aw,
                                                                          uint32_t n4) {
   if (blockIdx.x < n4)
-    q4::decode_quant_body<D, NS, QBF16, 4, 0, 1>(a4, blockIdx.x);
+    q4::decode_quant_body<D, NS, QBF16, 4, 0, 1, BAL>(a4, blockIdx.x);
   else
-    b16::decode_bf16_body<D, NS, QBF16>(aw, blockIdx.x - n4);
+    b16::decode_bf16_body<D, NS, QBF16, false>(aw, blockIdx.x - n4);
 }
 
-template <int D, int NS>
-hipError_t launch_d(const DecodeArgs& a4, const DecodeArgs& aw, hipStream_t s) {
+template <int D, int NS, bool BAL>
+hipError_t launch_b(const DecodeArgs& a4, const DecodeArgs& aw, hipStream_t s) {
   const uint32_t n_win = static_cast<uint32_t>(aw.nsplit) * aw.num_kv_heads * aw.batch;
   const uint32_t n4 = static_cast<uint32_t>(a4.nsplit) * a4.num_kv_heads * a4.batch;
   const dim3 grid(n_win + n4);
   if (a4.in_bf16)
-    decode_windowed_kernel<D, NS, true><<<grid, 64 * q4::kWaves, 0, s>>>(a4, aw, n4);
+    decode_windowed_kernel<D, NS, true, BAL><<<grid, 64 * q4::kWaves, 0, s>>>(a4, aw, n4);
   else
-    decode_windowed_kernel<D, NS, false><<<grid, 64 * q4::kWaves, 0, s>>>(a4, aw, n4);
+    decode_windowed_kernel<D, NS, false, BAL><<<grid, 64 * q4::kWaves, 0, s>>>(a4, aw, n4);
   return hipGetLastError();
+}
+
+template <int D, int NS>
+hipError_t launch_d(const DecodeArgs& a4, const DecodeArgs& aw, hipStream_t s) {
+  return a4.balance ? launch_b<D, NS, true>(a4, aw, s) : launch_b<D, NS, false>(a4, aw, s);
 }
 
 template <int D>

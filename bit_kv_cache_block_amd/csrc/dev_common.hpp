@@ -173,6 +173,30 @@ __device__ __forceinline__ void fwht_row_any(float* v, int block, int n) {
   }
 }
 
+// Pages per split of a decode call.  The host plans splits of at most sp
+// pages from the longest length alone (a ragged batch's longest sequence must
+// be cut finely).  Balanced calls (the host asks for them only for small
+// batches cut into many splits; at most 64 sequences, whose lengths one wave
+// reads with one load) grow the split to about total_pages * hkv / 512 pages
+// when the batch's whole work is large, so that long uniform contexts run as
+// about 512 workgroups of long streams instead of many short ones (the grid
+// keeps the planned count; the extra splits are empty).  Every workgroup and
+// the merge of a balanced call compute the same value.  All 64 lanes of the
+// wave must be active.
+__device__ __forceinline__ int balanced_split_pages(int sp, const int32_t* seq_lens, int batch,
+                                                    int max_seq_len, int hkv) {
+  const int lane = threadIdx.x & 63;
+  int len = lane < batch ? seq_lens[lane] : 0;
+  len = len < 0 ? 0 : (len > max_seq_len ? max_seq_len : len);
+  int total = (len + kPage - 1) / kPage;
+#pragma unroll
+  for (int m = 1; m < 64; m *= 2) total += __shfl_xor(total, m);
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int64_t want = (static_cast<int64_t>(total) * hkv + 511) / 512;
+  const int64_t even = (want + 3) / 4 * 4;
+  return even > sp ? static_cast<int>(even) : sp;
+}
+
 // Tokens [lo, hi) of a sequence of `len` tokens that an INT4 pass reads
 // when the first skip_first and the last skip_last tokens are left to the
 // high-precision windows (both zero: all of them).

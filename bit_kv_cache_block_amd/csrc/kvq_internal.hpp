@@ -8,6 +8,11 @@
 
 namespace kvq {
 
+// Decode calls of at most this many sequences may grow their splits on the
+// device from the batch's whole work (DecodeArgs::balance; one wave reads the
+// lengths, so at most 64).
+constexpr int kBalanceMaxBatch = 32;
+
 struct AppendArgs {
   uint8_t* pool;
   const uint16_t* k;
@@ -61,6 +66,8 @@ struct DecodeArgs {
   // has a token among its first win_len positions.
   int32_t has_window;
   int32_t win_len;
+  // The splits may grow with the batch's whole work (balanced_split_pages).
+  int32_t balance;
 };
 
 // Split-K plan shared by the launch and the workspace query.
@@ -70,6 +77,7 @@ struct SplitPlan {
 };
 SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len, int32_t num_splits);
 size_t workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, const SplitPlan& p);
+bool may_balance(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len, const SplitPlan& p);
 
 hipError_t launch_append_int4(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_int8(const AppendArgs& a, hipStream_t s);
@@ -79,6 +87,9 @@ hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_int4(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_int4g(const DecodeArgs& a, hipStream_t s);
+// The balanced build (a.balance set) of the three above: codes of `bits` bits
+// with one scale and zero per `gs` channels (0: per token).
+hipError_t launch_decode_quant_balanced(const DecodeArgs& a, int bits, int gs, hipStream_t s);
 hipError_t launch_decode_mxfp4(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t s);

@@ -39,6 +39,10 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * kRows + r;
   const bool live = bh < rows;
 
+  // (every lane of the wave takes part in reading the lengths)
+  const int sp = a.balance ? balanced_split_pages(a.split_pages, a.seq_lens, a.batch, a.max_seq_len,
+                                                  a.num_kv_heads)
+                           : a.split_pages;
   float m = -__builtin_inff(), l = 0.0f;
   v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
   if (live) {
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
       // INT4 split s, or (windowed calls) the window pass's slot, the last
       const bool ok = (a.has_window && s == a.part_stride - 1)
                           ? min(len, a.win_len) > 0
-                          : hi > lo && max(s * a.split_pages, pfirst) < min(npg, (s + 1) * a.split_pages);
+                          : hi > lo && max(s * sp, pfirst) < min(npg, (s + 1) * sp);
       const float mn = ok ? fmaxf(m, ms) : m;
       const float mu = mn == -__builtin_inff() ? 0.0f : mn;
       const float fo = exp2f(m - mu), fs = exp2f(ms - mu);
