@@ -677,7 +677,7 @@ def main(argv=None):
             "bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(value / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_quant_kernel<128, 1, true, 4> (one kvq_decode_attn call; at this shape the split "
+            "kernel": "decode_quant_kernel<128, 1, true, 4, 0, 1, false> (one kvq_decode_attn call; at this shape the split "
                       "plan is one split per (sequence, KV head), so no reduce kernel runs)",
         },
     }
