@@ -593,6 +593,11 @@ def main(argv=None):
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
     dec_mean = sum(dec_ms) / len(dec_ms)
     app_mean = sum(app_ms) / len(app_ms)
+
+    def pct(xs):
+        s = sorted(xs)
+        at = lambda f: s[min(len(s) - 1, int(f * (len(s) - 1) + 0.5))]
+        return {"p10": round(at(0.1) * 1e3, 2), "p50": round(at(0.5) * 1e3, 2), "p90": round(at(0.9) * 1e3, 2)}
     value = dec_bytes / (dec_mean * 1e-3) / 1e9
 
     # ---- variants on the same workload, all timed alone (decode only) ---------
@@ -652,7 +657,9 @@ def main(argv=None):
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "decode_us": round(dec_mean * 1e3, 2),
+        "decode_us_per_step": pct(dec_ms),
         "append_us": round(app_mean * 1e3, 2),
+        "append_us_per_step": pct(app_ms),
         "decode_bytes": dec_bytes,
         "rotate_quant_mtok_s": round(prefill_rot["mtok_s"], 1),
         "prefill_append": {

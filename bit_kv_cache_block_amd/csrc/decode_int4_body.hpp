@@ -81,7 +81,8 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   constexpr bool kOnePass = kNG == 1 && WPE == 1;
   // two step buffers (see the streaming loop): the two-set INT4 kernel, whose
   // registers allow two waves per SIMD with or without the second buffer
-  constexpr bool kPrefetch = NS == 2 && BITS == 4 && GS == 0;
+  // (the build held to three waves per SIMD keeps one)
+  constexpr bool kPrefetch = NS == 2 && BITS == 4 && GS == 0 && WPE == 1;
   constexpr int kNT = D / 16;          // PV tiles = output channels per lane
   constexpr int kOps = D / 64;         // QK MFMAs per page and head group
   constexpr int kGP = 4 * NS;          // padded heads per KV head

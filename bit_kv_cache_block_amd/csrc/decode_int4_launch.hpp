@@ -37,6 +37,17 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   if constexpr (NS == 1 && BITS == 4 && GS == 0) {
     if (wgs > 512) return launch_w<BAL, D, NS, BITS, GS, 4>(a, s, wgs);
   }
+  // The two-set INT4 kernel (205 VGPRs with its second step buffer: 2 waves
+  // per SIMD) is bound by its instruction latencies when the grid is large;
+  // without the second buffer it fits 168 VGPRs (3 waves per SIMD).  Above
+  // 4096 workgroups the extra wave wins (GQA-8 serving step at batch 256:
+  // 230 -> 221 us); at 1536 it loses badly (48 -> 62 us), since there the
+  // chain of the longest sequence's split, which the second buffer shortens,
+  // sets the time.  (Head_dim 64 fits 3 waves with both buffers; balanced
+  // calls are bound by their few long splits.)
+  if constexpr (!BAL && D == 128 && NS == 2 && BITS == 4 && GS == 0) {
+    if (wgs > 4096) return launch_w<BAL, D, NS, BITS, GS, 3>(a, s, wgs);
+  }
   return launch_w<BAL, D, NS, BITS, GS, 1>(a, s, wgs);
 }
 

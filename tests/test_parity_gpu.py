@@ -236,6 +236,25 @@ def test_decode_edge_lengths(d, dtype, hq):
         assert_close(got, want, f"edges d{d} hq{hq} S{splits}")
 
 
+@pytest.mark.parametrize("block", [64, 0])
+def test_decode_gqa8_large_grid(block):
+    """GQA 8 with more than 4096 workgroups (64 ragged sequences, 8 KV heads,
+    10 splits of 8 pages: 5120), the grid size at which the two-set kernel runs its build
+    held to three waves per SIMD (one step buffer)."""
+    lens = [int(x) for x in np.random.default_rng(3).integers(1, 1200, 64)]
+    lens[5], lens[17], lens[40] = 0, 1199, 16
+    w = workloads.random_decode(61, batch=64, hq=64, hkv=8, d=128, block=block, seq_lens=lens)
+    cache = gpu_int4_cache(w, block)
+    pool = oracle_int4_pool(w, block)
+    want = oracle.decode_int4(pool, w.hkv, w.d, block, bits(w.q), _odt(w.q), w.block_table,
+                              w.seq_lens, w.sm_scale)
+    nb = kvq.kvq_decode_workspace_bytes(w.batch, w.hq, w.hkv, w.d, w.max_seq_len, 10)
+    assert nb // (w.batch * w.hq * (w.d + 2) * 4) * w.hkv * w.batch > 4096
+    got = gpu_decode(cache, w, 10)
+    assert not got[5].any()
+    assert_close(got, want, f"gqa8 large grid block{block}")
+
+
 @pytest.mark.parametrize("hq", [4, 8])
 @pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float16)])
 def test_decode_many_splits_stale_workspace(d, dtype, hq):
