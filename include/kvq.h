@@ -216,7 +216,13 @@ kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const vo
  *               max_pages_per_seq*16 >= max_seq_len.
  * sm_scale:     softmax scale (normally 1/sqrt(head_dim)), finite.
  * num_splits:   0 = choose automatically; otherwise the number of split-K
- *               partitions of the longest sequence (clamped to what fits).
+ *               partitions of the longest sequence (clamped to what fits;
+ *               each partition holds a multiple of 4 pages, so the count
+ *               used can be smaller).  A batch of at most 32 sequences cut
+ *               into 16 or more partitions may have them grown on the
+ *               device from the batch's total length, so that the busy
+ *               ones stay about 512 workgroups' worth.  The partitioning
+ *               changes only the rounding of the result.
  * out:          device fp32 [batch][num_q_heads][head_dim], 16-byte aligned.
  * workspace:    device scratch of at least kvq_decode_workspace_bytes(...)
  *               for the same arguments, 16-byte aligned; its contents are
