@@ -492,13 +492,35 @@ def cpu_baseline(w, budget_s=15.0):
     lens = [int(w.seq_lens[b]) for b in done]
     dbytes = decode_bytes(lens, w.hkv, w.hq, w.d, int4_bytes_per_vector(w.d))
     tokens = sum(lens)
+    cores = oracle.num_threads()
+    # the first sampled sequence again on one thread (same codes, same output)
+    b = done[0]
+    sel = torch.from_numpy(w.token_seq == b).to(w.k.device)
+    kh, vh = bits(w.k[sel]), bits(w.v[sel])
+    sm = w.slot_mapping[sel].cpu().numpy()
+    mask = np.zeros((w.batch, w.hq), np.uint8)
+    mask[b] = 1
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.append_int4(pool, w.num_pages, w.hkv, w.d, w.block, kh, vh, oracle.BF16, sm)
+        t1 = time.perf_counter()
+        oracle.decode_int4(pool, w.hkv, w.d, w.block, qh, oracle.BF16, w.block_table, w.seq_lens,
+                           w.sm_scale, mask=mask)
+        t2 = time.perf_counter()
+    finally:
+        oracle.set_num_threads(cores)
+    one_bytes = decode_bytes([lens[0]], w.hkv, w.hq, w.d, int4_bytes_per_vector(w.d))
     return {
-        "value": dbytes / t_dec / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+        "value": dbytes / t_dec / 1e9, "unit": "GB/s", "cores": cores,
         "kind": "oracle",
         "sample": f"{len(done)} of {w.batch} sequences x {lens[0]} tokens, all {w.hq} q heads, "
                   f"block {w.block}: oracle append then fp64 decode; decode {t_dec:.2f} s, "
                   f"append {t_app:.2f} s",
         "append_mtok_s": tokens / t_app / 1e6,
+        "one_thread": {"value": round(one_bytes / (t2 - t1) / 1e9, 5),
+                       "append_mtok_s": round(lens[0] / (t1 - t0) / 1e6, 5),
+                       "sample": f"sequence {b} ({lens[0]} tokens) on one thread"},
     }
 
 

@@ -131,6 +131,8 @@ def _declare(L):
     L.kvq_oracle_decode_windowed.restype = _i32
     L.kvq_oracle_num_threads.argtypes = []
     L.kvq_oracle_num_threads.restype = _i32
+    L.kvq_oracle_set_num_threads.argtypes = [_i32]
+    L.kvq_oracle_set_num_threads.restype = None
 
 
 def _ptr(a: np.ndarray):
@@ -496,3 +498,8 @@ def decode_int4_bruteforce(pool, num_kv_heads, head_dim, block, q, dtype, block_
 
 def num_threads() -> int:
     return int(lib().kvq_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the following calls (timing only: the results are the same)."""
+    lib().kvq_oracle_set_num_threads(int(n))

@@ -804,4 +804,12 @@ int32_t kvq_oracle_num_threads(void) {
 #endif
 }
 
+void kvq_oracle_set_num_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 }  // extern "C"

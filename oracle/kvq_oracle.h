@@ -283,6 +283,8 @@ int32_t kvq_oracle_decode_int4_bruteforce(const uint8_t* pool, int32_t page_size
 
 /* Number of OpenMP threads the oracle uses (for the CPU-baseline report). */
 int32_t kvq_oracle_num_threads(void);
+/* Threads the following calls use (n > 0; timing only, results do not change). */
+void kvq_oracle_set_num_threads(int32_t n);
 
 #ifdef __cplusplus
 }

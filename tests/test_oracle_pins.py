@@ -629,3 +629,24 @@ def test_windowed_ring_after_decode_steps():
     want = oracle.decode_windowed(pool, ref_pool, w.hkv, w.d, 16, q, oracle.F16, w.block_table, ref_wbt,
                                   w.seq_lens, w_sink, w_recent, w.sm_scale)
     assert np.array_equal(got, want)
+
+
+def test_thread_count_does_not_change_results():
+    """The oracle's threads split independent vectors and rows, so one thread
+    and all of them give the same bytes and the same attention."""
+    w = workloads.random_decode(71, batch=3, hq=8, hkv=2, d=64, block=32, seq_lens=[50, 1, 33])
+    outs = []
+    n = oracle.num_threads()
+    try:
+        for t in (1, n):
+            oracle.set_num_threads(t)
+            pool = oracle.new_int4_pool(w.num_pages, w.hkv, w.d)
+            oracle.append_int4(pool, w.num_pages, w.hkv, w.d, 32, workloads.bits(w.k),
+                               workloads.bits(w.v), oracle.BF16, w.slot_mapping.numpy())
+            att = oracle.decode_int4(pool, w.hkv, w.d, 32, workloads.bits(w.q), oracle.BF16,
+                                     w.block_table, w.seq_lens, w.sm_scale)
+            outs.append((pool.copy(), att))
+    finally:
+        oracle.set_num_threads(n)
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
