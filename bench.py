@@ -43,6 +43,8 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 METRIC = "INT4-KV decode attn HBM GB/s (% of peak); rotate+quant Mtokens/s"
 RING = 4
+PREFILL_RING = 8   # prefill input/cache sets: 8 x 170 MB, well past the Infinity Cache
+PREFILL_SEEDS = (3, 13, 23, 33, 43, 63, 93, 103)   # seeds whose length draws stay in [512, 4096]
 
 
 # ---------------------------------------------------------------- accounting
@@ -180,17 +182,17 @@ class DecodeBench:
 def prefill_rates(torch, kvq, workloads, blocks=(64, 0), iters=50, chunk=10):
     """Rotate+quantize append of 32768 ragged tokens (8 KV heads, d 128) into a
     page-16 pool, for each Hadamard block in ``blocks``: Mtokens/s and GB/s
-    over RING input/cache sets.  The blocks are timed in alternating runs of
+    over PREFILL_RING input/cache sets.  The blocks are timed in alternating runs of
     ``chunk`` calls so that they see the same clocks."""
     sets = {}
     for blk in blocks:
         sets[blk] = []
-        for r in range(RING):
-            w = workloads.prefill_append(3 + 10 * r, device="cuda", block=blk)
+        for r in range(PREFILL_RING):
+            w = workloads.prefill_append(PREFILL_SEEDS[r], device="cuda", block=blk)
             sets[blk].append((w, kvq.Int4Cache(w.num_pages, w.hkv, w.d, blk, "cuda")))
 
     def run(blk, i):
-        w, c = sets[blk][i % RING]
+        w, c = sets[blk][i % PREFILL_RING]
         kvq.kvq_append_paged(c, w.k, w.v, w.slot_mapping)
 
     for blk in blocks:
@@ -296,12 +298,12 @@ def variant_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes, kind)
     del caches
     torch.cuda.empty_cache()
     sets = []
-    for r in range(2):
-        pw = workloads.prefill_append(3 + 10 * r, device="cuda", block=64)
+    for r in range(PREFILL_RING):
+        pw = workloads.prefill_append(PREFILL_SEEDS[r], device="cuda", block=64)
         sets.append((pw, make(pw.num_pages)))
 
     def app(i):
-        pw, c = sets[i % 2]
+        pw, c = sets[i % PREFILL_RING]
         app_fn(c, pw.k, pw.v, pw.slot_mapping)
 
     for i in range(10):
