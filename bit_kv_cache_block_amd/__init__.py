@@ -157,6 +157,18 @@ def _ptr(t: torch.Tensor | None) -> C.c_void_p:
     return C.c_void_p(0 if t is None else t.data_ptr())
 
 
+def _same_gpu(pool: torch.Tensor, **tensors) -> None:
+    """Every tensor handed to the library must live on the GPU that holds the
+    cache pool: a host pointer or another device's pointer would reach a
+    kernel as an address it cannot use."""
+    dev = pool.get_device()
+    if dev < 0 or not pool.is_cuda:
+        raise ValueError("the cache pool must be a GPU tensor")
+    for name, t in tensors.items():
+        if t is not None and t.get_device() != dev:
+            raise ValueError(f"{name} must be on the cache's GPU (cuda:{dev})")
+
+
 def kvq_int4_page_bytes(page_size: int, num_kv_heads: int, head_dim: int) -> int:
     return int(lib().kvq_int4_page_bytes(page_size, num_kv_heads, head_dim))
 
@@ -273,46 +285,44 @@ def _token_stride(k: torch.Tensor, v: torch.Tensor, hkv: int, d: int) -> int:
     raise ValueError("k and v must share shape, dtype and token stride")
 
 
-def _append(fn, desc, hkv, d, k, v, slot_mapping, stream):
-    stride = _token_stride(k, v, hkv, d)
+def _append(fn, cache, k, v, slot_mapping, stream):
+    stride = _token_stride(k, v, cache.num_kv_heads, cache.head_dim)
     if slot_mapping.dtype != torch.int32 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be a contiguous int32 tensor")
-    _check(fn(C.byref(desc), _ptr(k), _ptr(v), _dtype_code(k), stride, _ptr(slot_mapping),
+    if slot_mapping.numel() != k.shape[0]:
+        raise ValueError(f"slot_mapping has {slot_mapping.numel()} entries for {k.shape[0]} tokens")
+    _same_gpu(cache.pool, k=k, v=v, slot_mapping=slot_mapping)
+    _check(fn(C.byref(cache.desc()), _ptr(k), _ptr(v), _dtype_code(k), stride, _ptr(slot_mapping),
               int(k.shape[0]), _stream(stream, k.device)))
 
 
 def kvq_append_paged(cache: Int4Cache, k: torch.Tensor, v: torch.Tensor,
                      slot_mapping: torch.Tensor, stream=None) -> None:
     """Rotate + quantize + scatter new tokens (k, v: [T][Hkv][D] fp16/bf16)."""
-    _append(lib().kvq_append_paged, _need(cache, Int4Cache).desc(), cache.num_kv_heads,
-            cache.head_dim, k, v, slot_mapping, stream)
+    _append(lib().kvq_append_paged, _need(cache, Int4Cache), k, v, slot_mapping, stream)
 
 
 def kvq_append_paged_int8(cache: Int8Cache, k: torch.Tensor, v: torch.Tensor,
                           slot_mapping: torch.Tensor, stream=None) -> None:
     """Rotate + quantize to 8 bits + scatter new tokens into the INT8 pool."""
-    _append(lib().kvq_append_paged_int8, _need(cache, Int8Cache).desc(), cache.num_kv_heads,
-            cache.head_dim, k, v, slot_mapping, stream)
+    _append(lib().kvq_append_paged_int8, _need(cache, Int8Cache), k, v, slot_mapping, stream)
 
 
 def kvq_append_paged_int4g(cache: Int4GroupedCache, k: torch.Tensor, v: torch.Tensor,
                            slot_mapping: torch.Tensor, stream=None) -> None:
     """Rotate + per-group quantize + scatter new tokens into the grouped pool."""
-    _append(lib().kvq_append_paged_int4g, _need(cache, Int4GroupedCache).desc(), cache.num_kv_heads,
-            cache.head_dim, k, v, slot_mapping, stream)
+    _append(lib().kvq_append_paged_int4g, _need(cache, Int4GroupedCache), k, v, slot_mapping, stream)
 
 
 def kvq_append_paged_mxfp4(cache: MxFp4Cache, k: torch.Tensor, v: torch.Tensor,
                            slot_mapping: torch.Tensor, stream=None) -> None:
     """Rotate + MXFP4-quantize + scatter new tokens into the MXFP4 pool."""
-    _append(lib().kvq_append_paged_mxfp4, _need(cache, MxFp4Cache).desc(), cache.num_kv_heads,
-            cache.head_dim, k, v, slot_mapping, stream)
+    _append(lib().kvq_append_paged_mxfp4, _need(cache, MxFp4Cache), k, v, slot_mapping, stream)
 
 
 def kvq_append_paged_bf16(cache: Bf16Cache, k: torch.Tensor, v: torch.Tensor,
                           slot_mapping: torch.Tensor, stream=None) -> None:
-    _append(lib().kvq_append_paged_bf16, cache.desc(), cache.num_kv_heads, cache.head_dim, k, v,
-            slot_mapping, stream)
+    _append(lib().kvq_append_paged_bf16, _need(cache, Bf16Cache), k, v, slot_mapping, stream)
 
 
 def kvq_decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -321,24 +331,47 @@ def kvq_decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, 
                                                 max_seq_len, num_splits))
 
 
-def _decode(fn, desc, hkv, d, q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace,
-            num_splits, stream):
+def _decode_args(cache, q, block_table, seq_lens, out, **more):
+    """Shape, dtype and device checks shared by the decode calls, made before
+    anything is handed to the library; returns (batch, num_q_heads)."""
+    d = cache.head_dim
     if q.dim() != 3 or q.shape[2] != d or not q.is_contiguous():
         raise ValueError("q must be a contiguous [B][Hq][D] tensor")
     batch, hq = int(q.shape[0]), int(q.shape[1])
-    for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+    tables = (("block_table", block_table), ("seq_lens", seq_lens), *more.items())
+    for name, t in tables:
         if t.dtype != torch.int32 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 tensor")
+    if block_table.dim() != 2 or block_table.shape[0] != batch:
+        raise ValueError(f"block_table must be [{batch}][max_pages_per_seq]")
+    if seq_lens.numel() != batch:
+        raise ValueError(f"seq_lens must hold {batch} lengths")
+    for name, t in more.items():
+        if t.dim() != 2 or t.shape[0] != batch:
+            raise ValueError(f"{name} must be [{batch}][pages]")
+    if out is not None:
+        if out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 tensor")
+        if tuple(out.shape) != (batch, hq, d):
+            raise ValueError(f"out must be [{batch}][{hq}][{d}], got {tuple(out.shape)}")
+    _same_gpu(cache.pool, q=q, block_table=block_table, seq_lens=seq_lens, out=out, **more)
+    return batch, hq
+
+
+def _decode(fn, cache, q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace,
+            num_splits, stream):
+    hkv, d = cache.num_kv_heads, cache.head_dim
+    batch, hq = _decode_args(cache, q, block_table, seq_lens, out)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 tensor")
-    if workspace is None:   # (a caller's workspace is checked by the library)
+    if workspace is None:   # (a caller's workspace size is checked by the library)
         need = kvq_decode_workspace_bytes(batch, hq, hkv, d, max_seq_len, num_splits)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _check(fn(C.byref(desc), _ptr(q), _dtype_code(q), hq, _ptr(block_table),
+    else:
+        _same_gpu(cache.pool, workspace=workspace)
+    _check(fn(C.byref(cache.desc()), _ptr(q), _dtype_code(q), hq, _ptr(block_table),
               int(block_table.shape[1]), _ptr(seq_lens), batch, int(max_seq_len),
               float(sm_scale), int(num_splits), _ptr(out), _ptr(workspace),
               workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
@@ -350,9 +383,8 @@ def kvq_decode_attn(cache: Int4Cache, q: torch.Tensor, block_table: torch.Tensor
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                     num_splits: int = 0, stream=None) -> torch.Tensor:
     """Paged decode attention over the INT4 cache; returns fp32 [B][Hq][D]."""
-    return _decode(lib().kvq_decode_attn, _need(cache, Int4Cache).desc(), cache.num_kv_heads,
-                   cache.head_dim, q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace,
-                   num_splits, stream)
+    return _decode(lib().kvq_decode_attn, _need(cache, Int4Cache), q, block_table, seq_lens, max_seq_len,
+                   sm_scale, out, workspace, num_splits, stream)
 
 
 def kvq_decode_attn_int8(cache: Int8Cache, q: torch.Tensor, block_table: torch.Tensor,
@@ -360,9 +392,8 @@ def kvq_decode_attn_int8(cache: Int8Cache, q: torch.Tensor, block_table: torch.T
                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                          num_splits: int = 0, stream=None) -> torch.Tensor:
     """Paged decode attention over the INT8 cache; returns fp32 [B][Hq][D]."""
-    return _decode(lib().kvq_decode_attn_int8, _need(cache, Int8Cache).desc(), cache.num_kv_heads,
-                   cache.head_dim, q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace,
-                   num_splits, stream)
+    return _decode(lib().kvq_decode_attn_int8, _need(cache, Int8Cache), q, block_table, seq_lens, max_seq_len,
+                   sm_scale, out, workspace, num_splits, stream)
 
 
 def kvq_decode_attn_int4g(cache: Int4GroupedCache, q: torch.Tensor, block_table: torch.Tensor,
@@ -370,9 +401,8 @@ def kvq_decode_attn_int4g(cache: Int4GroupedCache, q: torch.Tensor, block_table:
                           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                           num_splits: int = 0, stream=None) -> torch.Tensor:
     """Paged decode attention over the grouped INT4 cache; returns fp32 [B][Hq][D]."""
-    return _decode(lib().kvq_decode_attn_int4g, _need(cache, Int4GroupedCache).desc(),
-                   cache.num_kv_heads, cache.head_dim, q, block_table, seq_lens, max_seq_len,
-                   sm_scale, out, workspace, num_splits, stream)
+    return _decode(lib().kvq_decode_attn_int4g, _need(cache, Int4GroupedCache), q, block_table,
+                   seq_lens, max_seq_len, sm_scale, out, workspace, num_splits, stream)
 
 
 def kvq_decode_attn_mxfp4(cache: MxFp4Cache, q: torch.Tensor, block_table: torch.Tensor,
@@ -380,18 +410,16 @@ def kvq_decode_attn_mxfp4(cache: MxFp4Cache, q: torch.Tensor, block_table: torch
                           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                           num_splits: int = 0, stream=None) -> torch.Tensor:
     """Paged decode attention over the MXFP4 cache; returns fp32 [B][Hq][D]."""
-    return _decode(lib().kvq_decode_attn_mxfp4, _need(cache, MxFp4Cache).desc(), cache.num_kv_heads,
-                   cache.head_dim, q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace,
-                   num_splits, stream)
+    return _decode(lib().kvq_decode_attn_mxfp4, _need(cache, MxFp4Cache), q, block_table, seq_lens, max_seq_len,
+                   sm_scale, out, workspace, num_splits, stream)
 
 
 def kvq_decode_attn_bf16(cache: Bf16Cache, q: torch.Tensor, block_table: torch.Tensor,
                          seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float | None = None,
                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                          num_splits: int = 0, stream=None) -> torch.Tensor:
-    return _decode(lib().kvq_decode_attn_bf16, cache.desc(), cache.num_kv_heads, cache.head_dim,
-                   q, block_table, seq_lens, max_seq_len, sm_scale, out, workspace, num_splits,
-                   stream)
+    return _decode(lib().kvq_decode_attn_bf16, _need(cache, Bf16Cache), q, block_table, seq_lens,
+                   max_seq_len, sm_scale, out, workspace, num_splits, stream)
 
 
 def kvq_decode_windowed_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int,
@@ -408,25 +436,21 @@ def kvq_decode_attn_windowed(cache: Int4Cache, window: Bf16Cache, q: torch.Tenso
                              stream=None) -> torch.Tensor:
     """Decode attention with bf16 windows for the first w_sink and the last
     w_recent tokens of each sequence; returns fp32 [B][Hq][D]."""
-    d = cache.head_dim
-    if q.dim() != 3 or q.shape[2] != d or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [B][Hq][D] tensor")
-    batch, hq = int(q.shape[0]), int(q.shape[1])
-    for name, t in (("block_table", block_table), ("window_table", window_table), ("seq_lens", seq_lens)):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    d = _need(cache, Int4Cache).head_dim
+    batch, hq = _decode_args(cache, q, block_table, seq_lens, out, window_table=window_table)
+    _same_gpu(cache.pool, window_pool=_need(window, Bf16Cache).pool)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 tensor")
-    if workspace is None:   # (a caller's workspace is checked by the library)
+    if workspace is None:   # (a caller's workspace size is checked by the library)
         need = kvq_decode_windowed_workspace_bytes(batch, hq, cache.num_kv_heads, d, max_seq_len,
                                                    num_splits)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _same_gpu(cache.pool, workspace=workspace)
     _check(lib().kvq_decode_attn_windowed(
-        C.byref(_need(cache, Int4Cache).desc()), C.byref(window.desc()), _ptr(q), _dtype_code(q), hq,
+        C.byref(cache.desc()), C.byref(window.desc()), _ptr(q), _dtype_code(q), hq,
         _ptr(block_table),
         int(block_table.shape[1]), _ptr(window_table), int(window_table.shape[1]), _ptr(seq_lens),
         batch, int(max_seq_len), int(w_sink), int(w_recent), float(sm_scale), int(num_splits),

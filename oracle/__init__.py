@@ -464,8 +464,8 @@ def decode_bf16(pool, num_kv_heads, head_dim, q, dtype, block_table, seq_lens, s
 def decode_windowed(int4_pool, win_pool, num_kv_heads, head_dim, block, q, dtype, block_table,
                     win_block_table, seq_lens, w_sink, w_recent, sm_scale, page_size=16, mask=None):
     q = _c(q, np.uint16)
-    bt = _c(block_table, np.int32)
-    wbt = _c(win_block_table, np.int32)
+    bt = _c(_pages_in_pool(block_table, int4_pool, num_kv_heads, int4_slab_bytes(page_size, head_dim)), np.int32)
+    wbt = _c(_pages_in_pool(win_block_table, win_pool, num_kv_heads, bf16_slab_bytes(page_size, head_dim)), np.int32)
     sl = _c(seq_lens, np.int32)
     batch, hq, d = q.shape
     out = np.zeros((batch, hq, d), np.float64)

@@ -693,35 +693,50 @@ int32_t kvq_oracle_decode_windowed(const uint8_t* int4_pool, const uint8_t* win_
         *page = win_block_table[static_cast<size_t>(b) * max_win_pages + pos / p];
         *off = pos % p;
       };
+      /* page of token t in the table that holds it (window or INT4) and its
+         offset there; a negative id is a page that is not there, whose
+         tokens are left out of the softmax (a row with none left is zero) */
+      auto where = [&](int t, int* page, int* off) {
+        if (in_window(t)) {
+          win_page_off(t, page, off);
+        } else {
+          *page = block_table[static_cast<size_t>(b) * max_pages_per_seq + t / p];
+          *off = t % p;
+        }
+      };
       double mx = -INFINITY;
       for (int t = 0; t < len; ++t) {
+        int page, off;
+        where(t, &page, &off);
+        if (page < 0) {
+          s[t] = -INFINITY;
+          continue;
+        }
         double dot = 0.0;
         if (in_window(t)) {   /* original basis, un-rotated query */
-          int page, off;
-          win_page_off(t, &page, &off);
           for (int c = 0; c < d; ++c)
             dot += qv[c] * kvq_oracle_bf16_read(win_pool, p, num_kv_heads, d, page, kvh, off, 0, c);
         } else {              /* rotated basis, rotated query */
-          const int page = block_table[static_cast<size_t>(b) * max_pages_per_seq + t / p];
           for (int c = 0; c < d; ++c)
-            dot += qr[c] * kvq_oracle_int4_read(int4_pool, p, num_kv_heads, d, page, kvh, t % p, 0, c,
+            dot += qr[c] * kvq_oracle_int4_read(int4_pool, p, num_kv_heads, d, page, kvh, off, 0, c,
                                                 nullptr, nullptr, nullptr);
         }
         s[t] = sm_scale * dot;
         if (s[t] > mx) mx = s[t];
       }
+      if (mx == -INFINITY) continue;
       double l = 0.0;
-      for (int t = 0; t < len; ++t) { s[t] = std::exp(s[t] - mx); l += s[t]; }
+      for (int t = 0; t < len; ++t) { s[t] = s[t] == -INFINITY ? 0.0 : std::exp(s[t] - mx); l += s[t]; }
       for (int t = 0; t < len; ++t) {
+        int page, off;
+        where(t, &page, &off);
+        if (page < 0) continue;
         if (in_window(t)) {
-          int page, off;
-          win_page_off(t, &page, &off);
           for (int c = 0; c < d; ++c)
             o_win[c] += s[t] * kvq_oracle_bf16_read(win_pool, p, num_kv_heads, d, page, kvh, off, 1, c);
         } else {
-          const int page = block_table[static_cast<size_t>(b) * max_pages_per_seq + t / p];
           for (int c = 0; c < d; ++c)
-            o_int4[c] += s[t] * kvq_oracle_int4_read(int4_pool, p, num_kv_heads, d, page, kvh, t % p, 1, c,
+            o_int4[c] += s[t] * kvq_oracle_int4_read(int4_pool, p, num_kv_heads, d, page, kvh, off, 1, c,
                                                      nullptr, nullptr, nullptr);
         }
       }

@@ -260,7 +260,9 @@ int32_t kvq_oracle_decode_bf16(const uint8_t* pool, int32_t page_size,
  * t when t < w_sink, else w_sink + (t - w_sink) mod w_recent (a ring of the
  * recent tokens), found through `win_block_table` [batch][max_win_pages].
  * Reading R8: the windows hold unrotated bf16 copies (the rotation only
- * serves the 4-bit codes). */
+ * serves the 4-bit codes).  A negative id in either table is a page that is
+ * not there: its tokens are left out of the softmax, as in the plain decode
+ * (a row with no token left is zero). */
 int32_t kvq_oracle_decode_windowed(const uint8_t* int4_pool, const uint8_t* win_pool,
                                    int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t block, const uint16_t* q, int32_t dtype,

@@ -251,3 +251,68 @@ def test_windowed_workspace_holds_a_partial_per_split_and_the_window():
         win = kvq.kvq_decode_windowed_workspace_bytes(4, 8, 2, 64, maxlen, 0)
         row = 4 * 8 * (64 + 2) * 4
         assert win == (plain if plain else row) + row
+
+
+# ---------------------------------------------------------------- binding checks
+# The Python binding checks shapes and devices before it hands anything to the
+# library; every call below raises ValueError on the host, so nothing is
+# launched (all tensors are host tensors and no GPU is needed).
+
+def _host_decode_args(batch=3, hq=8, hkv=2, d=64, pages=4):
+    import torch
+    cache = kvq.Int4Cache(16, hkv, d, 64, device="cpu")
+    q = torch.zeros((batch, hq, d), dtype=torch.bfloat16)
+    bt = torch.zeros((batch, pages), dtype=torch.int32)
+    sl = torch.full((batch,), 16, dtype=torch.int32)
+    return cache, q, bt, sl
+
+
+@pytest.mark.parametrize("fault,match", [
+    ("short_table", "block_table must be"),
+    ("flat_table", "block_table must be"),
+    ("short_lens", "seq_lens must hold"),
+    ("bad_out", "out must be"),
+    ("host_pool", "cache pool must be a GPU tensor"),
+])
+def test_binding_decode_rejects_bad_shapes_and_devices(fault, match):
+    import torch
+    cache, q, bt, sl = _host_decode_args()
+    out = None
+    if fault == "short_table":
+        bt = bt[:2].contiguous()
+    elif fault == "flat_table":
+        bt = bt.reshape(-1).contiguous()
+    elif fault == "short_lens":
+        sl = sl[:2].contiguous()
+    elif fault == "bad_out":
+        out = torch.zeros((3, 8, 32), dtype=torch.float32)
+    with pytest.raises(ValueError, match=match):
+        kvq.kvq_decode_attn(cache, q, bt, sl, 64, out=out)
+    with pytest.raises(ValueError, match=match):
+        kvq.kvq_decode_attn_bf16(kvq.Bf16Cache(16, 2, 64, device="cpu"), q, bt, sl, 64, out=out)
+
+
+def test_binding_windowed_rejects_bad_window_table():
+    import torch
+    cache, q, bt, sl = _host_decode_args()
+    win = kvq.Bf16Cache(8, 2, 64, device="cpu")
+    with pytest.raises(ValueError, match="window_table must be"):
+        kvq.kvq_decode_attn_windowed(cache, win, q, bt, torch.zeros((2, 1), dtype=torch.int32), sl,
+                                     64, 4, 12)
+    with pytest.raises(ValueError, match="cache pool must be a GPU tensor"):
+        kvq.kvq_decode_attn_windowed(cache, win, q, bt, torch.zeros((3, 1), dtype=torch.int32), sl,
+                                     64, 4, 12)
+
+
+@pytest.mark.parametrize("fn,cache_fn", [
+    ("kvq_append_paged", lambda: kvq.Int4Cache(4, 2, 64, 64, device="cpu")),
+    ("kvq_append_paged_int8", lambda: kvq.Int8Cache(4, 2, 64, 64, device="cpu")),
+    ("kvq_append_paged_bf16", lambda: kvq.Bf16Cache(4, 2, 64, device="cpu")),
+])
+def test_binding_append_rejects_bad_slots_and_devices(fn, cache_fn):
+    import torch
+    k = torch.zeros((5, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="slot_mapping has 4 entries for 5 tokens"):
+        getattr(kvq, fn)(cache_fn(), k, k.clone(), torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="cache pool must be a GPU tensor"):
+        getattr(kvq, fn)(cache_fn(), k, k.clone(), torch.zeros(5, dtype=torch.int32))

@@ -123,6 +123,25 @@ def test_rotated_dot_product_preserved(b):
         assert abs(np.linalg.norm(qr) - np.linalg.norm(q)) <= 1e-6 * np.linalg.norm(q)
 
 
+def test_butterfly_stage_order_worked_example():
+    """The fp32 butterfly runs its stages in ascending order: a 16-element
+    vector whose result differs between the two stage orders, with the
+    expected bits derived by hand in the fixture (tests/golden/
+    fwht_stage_order.txt)."""
+    import os
+    rows = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "fwht_stage_order.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        key, *vals = line.split()
+        rows[key] = vals
+    b = int(rows["block"][0])
+    x = np.array([int(h, 16) for h in rows["input"]], np.uint32).view(np.float32)
+    want = np.array([int(h, 16) for h in rows["output"]], np.uint32)
+    got = oracle.rotate(x, b).view(np.uint32)
+    assert np.array_equal(got, want), [hex(v) for v in got]
+
+
 def test_block_one_is_identity_of_plain_int4():
     rng = np.random.default_rng(7)
     for _ in range(100):
@@ -499,17 +518,24 @@ def _table3():
     return rows
 
 
-def test_sidecar_accounting_matches_innerq_table3():
-    """FP16 scale / zero bits averaged over the group (Table 3: group 32 ->
-    0.5 bit each; FP32 norms over head dim 128 -> 0.25) -- the same accounting
-    gives 4 + 32/D bits per element for token-wise INT4 with FP16 scale+zero."""
-    import bench
+def test_pool_bit_widths_match_innerq_table3_accounting():
+    """The oracle's page slabs hold, per stored number, the integer bits plus
+    the FP16 scale and zero bits averaged over the numbers of their group --
+    the accounting of InnerQ Table 3 (group 32: 0.5 bit each for scale and
+    zero point, KIVI's key row).  Token-wise INT4 over head_dim 128 is then 4 +
+    0.25 bits, grouped INT4 with groups of 32 is 4 + 0.5 + 0.5, and INT8 is 8 +
+    0.25."""
     t3 = _table3()
-    assert bench.overhead_bits(16, 32) == t3[("KIVI", "key", "scale")]
-    assert bench.overhead_bits(16, 32) == t3[("KIVI", "key", "zero_point")]
-    assert bench.overhead_bits(32, 128) == t3[("TurboQuant", "key", "channel_norm")]
-    assert bench.int4_bytes_per_vector(128) * 8 / 128 == 4 + 2 * bench.overhead_bits(16, 128)
-    assert bench.int4_bytes_per_vector(128) == 68
+    numbers = 16 * 2 * 128          # tokens of a page x (K, V) x channels
+    bits_of = lambda slab: slab * 8 / numbers
+    fp16_over = lambda group: 16 / group
+    assert fp16_over(32) == t3[("KIVI", "key", "scale")] == t3[("KIVI", "key", "zero_point")]
+    assert bits_of(oracle.int4g_slab_bytes(16, 128, 32)) == 4 + t3[("KIVI", "key", "scale")] + t3[("KIVI", "key", "zero_point")]
+    assert bits_of(oracle.int4_slab_bytes(16, 128)) == 4 + 2 * fp16_over(128)
+    assert bits_of(oracle.int4g_slab_bytes(16, 128, 64)) == 4 + 2 * fp16_over(64)
+    assert bits_of(oracle.int8_slab_bytes(16, 128)) == 8 + 2 * fp16_over(128)
+    # the same averaging gives the table's FP32 channel norm over head dim 128
+    assert 32 / 128 == t3[("TurboQuant", "key", "channel_norm")]
 
 
 def test_prefill_lengths_ragged_and_exact():
@@ -603,6 +629,57 @@ def test_windowed_matches_explicit_rows(block, w_sink, w_recent):
                     vv[t] = vin[idx[t], kvh]
             p = scipy.special.softmax(w.sm_scale * kk @ qf[b, h])
             assert np.abs(out[b, h] - p @ vv).max() <= 1e-12 * max(1.0, np.abs(vv).max())
+
+
+def test_windowed_absent_pages_leave_their_tokens_out():
+    """Absent pages in either table (ids outside the INT4 pool or outside the
+    window pool) drop their tokens: the row equals one scipy softmax over the
+    hand-assembled keys and values of the remaining tokens, and a row whose
+    every page is absent is zero."""
+    block, w_sink, w_recent = 64, 4, 12
+    w, pool = _tiny_case(seed=11, block=block, lens=[53, 40, 6])
+    wbt, wpool = _window_pool(w, w_sink, w_recent)
+    q = workloads.bits(w.q)
+    bt = w.block_table.copy()
+    wt = wbt.copy()
+    n_win_pages = wpool.size // (w.hkv * oracle.bf16_slab_bytes(16, w.d))
+    bt[0][1] = -1                      # INT4 tokens 16..31 of sequence 0
+    wt[0][0] = n_win_pages + 2         # window positions 0..15: every window token of sequence 0
+    bt[1][1] = w.num_pages             # INT4 tokens 16..27 of sequence 1 (28..39 are recent)
+    bt[2][0] = -3                      # sequence 2 (6 tokens) lies in the window only ...
+    wt[2][:] = -1                      # ... and its window pages are absent too
+    out = oracle.decode_windowed(pool, wpool, w.hkv, w.d, block, q, oracle.F16, bt, wt,
+                                 w.seq_lens, w_sink, w_recent, w.sm_scale)
+    g = w.hq // w.hkv
+    rinv = np.kron(np.eye(w.d // block), scipy.linalg.hadamard(block)) / np.sqrt(block)
+    qf = w.q.float().numpy().astype(np.float64)
+    kin = w.k.to(torch.bfloat16).float().numpy().astype(np.float64)
+    vin = w.v.to(torch.bfloat16).float().numpy().astype(np.float64)
+    for b in range(2):
+        n = int(w.seq_lens[b])
+        idx = np.nonzero(w.token_seq == b)[0]
+        idx = idx[np.argsort(w.token_pos[idx])]
+        for h in range(w.hq):
+            kvh = h // g
+            kk = _dequant_seq(w, pool, b, kvh, 0) @ rinv.T
+            vv = _dequant_seq(w, pool, b, kvh, 1) @ rinv.T
+            keep = []
+            for t in range(n):
+                windowed = t < w_sink or t >= n - w_recent
+                if windowed:
+                    kk[t] = kin[idx[t], kvh]
+                    vv[t] = vin[idx[t], kvh]
+                    pos = t if t < w_sink else w_sink + (t - w_sink) % w_recent
+                    present = 0 <= wt[b][pos // 16] < n_win_pages
+                else:
+                    present = 0 <= bt[b][t // 16] < w.num_pages
+                if present:
+                    keep.append(t)
+            keep = np.array(keep)
+            assert 0 < len(keep) < n
+            p = scipy.special.softmax(w.sm_scale * kk[keep] @ qf[b, h])
+            assert np.abs(out[b, h] - p @ vv[keep]).max() <= 1e-12 * max(1.0, np.abs(vv).max())
+    assert not out[2].any()
 
 
 def test_windowed_ring_after_decode_steps():

@@ -390,76 +390,116 @@ def test_append_prefill_full_size_bitexact():
     assert_pool_equal(cache.pool, oracle_int4_pool(w, 64), "prefill full")
 
 
-def _oracle_pool_for(w, sample, step=None):
-    """The oracle's pool holding only the tokens of the sequences in
-    ``sample`` (of the fill ``w``, then of the decode ``step`` if given)."""
-    sel = torch.from_numpy(np.isin(w.token_seq, sample)).to(w.k.device)
-    pool = oracle_int4_pool(w, w.block, sel=sel)
+def _oracle_pool_for(w, sample, step=None, kind="int4"):
+    """The oracle's pool (INT4 with the workload's block, or bf16) holding
+    only the tokens of the sequences in ``sample`` (of the fill ``w``, then of
+    the decode ``step`` if given)."""
+    def append(pool, x, sel):
+        sm = x.slot_mapping.cpu().numpy()[sel]
+        tsel = torch.from_numpy(sel).to(x.k.device)
+        if kind == "bf16":
+            oracle.append_bf16(pool, x.num_pages, x.hkv, x.d, bits(x.k[tsel]), bits(x.v[tsel]),
+                               _odt(x.k), sm)
+        else:
+            oracle.append_int4(pool, x.num_pages, x.hkv, x.d, x.block, bits(x.k[tsel]),
+                               bits(x.v[tsel]), _odt(x.k), sm)
+
+    pool = (oracle.new_bf16_pool if kind == "bf16" else oracle.new_int4_pool)(w.num_pages, w.hkv, w.d)
+    append(pool, w, np.isin(w.token_seq, sample))
     if step is not None:
-        ssel = np.isin(step.token_seq, sample)
-        tsel = torch.from_numpy(ssel).to(step.k.device)
-        oracle.append_int4(pool, step.num_pages, step.hkv, step.d, step.block, bits(step.k[tsel]),
-                           bits(step.v[tsel]), oracle.BF16, step.slot_mapping.cpu().numpy()[ssel])
+        append(pool, step, np.isin(step.token_seq, sample))
     return pool
 
 
-def test_long_context_full_size_sampled():
-    """Qwen3-4B-shaped long context at full size (8 x 131072 tokens, 65536
-    pages, per-channel scales in [0.1, 10], block 64) with the default split
-    plan: pages of two sampled sequences bit-exact, their attention within
-    tolerance."""
-    w = workloads.long_context_decode(4, device=DEV, batch=8, context=131072, block=64)
-    print("long context full size", flush=True)
-    cache = kvq.Int4Cache(w.num_pages, w.hkv, w.d, 64, DEV)
-    kvq.kvq_append_paged(cache, w.k, w.v, w.slot_mapping)
-    out = kvq.kvq_decode_attn(cache, w.q, torch.from_numpy(w.block_table).to(DEV),
-                              torch.from_numpy(w.seq_lens).to(DEV), w.max_seq_len, w.sm_scale)
-    torch.cuda.synchronize()
-    sample = [0, 5]
-    pool = _oracle_pool_for(w, sample)
-    slab = w.hkv * oracle.int4_slab_bytes(16, w.d)
-    gpool = cache.pool.cpu().numpy()
+# (cache kind, Hadamard block) of the full-size sampled cases: the rotated
+# and plain INT4 caches and the bf16 baseline, as the benchmark times them
+FULL_KINDS = {"int4_b64": 64, "int4_plain": 0, "bf16": 0}
+
+
+def _full_size_cache(kind, w, *more):
+    """GPU cache of ``kind`` filled with the workload ``w`` and then the
+    appends in ``more``."""
+    if kind == "bf16":
+        cache = kvq.Bf16Cache(w.num_pages, w.hkv, w.d, DEV)
+        app = kvq.kvq_append_paged_bf16
+    else:
+        cache = kvq.Int4Cache(w.num_pages, w.hkv, w.d, FULL_KINDS[kind], DEV)
+        app = kvq.kvq_append_paged
+    for x in (w, *more):
+        app(cache, x.k, x.v, x.slot_mapping)
+    return cache
+
+
+def _check_sampled(kind, cache, out, w, pool, sample, block_table, label):
+    """Pages of the sampled sequences bit-exact (every page in their rows of
+    the table: pages past a sequence's end were never written on either
+    side), their attention within tolerance of the oracle's."""
+    slab = w.hkv * (oracle.bf16_slab_bytes(16, w.d) if kind == "bf16" else oracle.int4_slab_bytes(16, w.d))
     for b in sample:
-        pages = w.block_table[b][w.block_table[b] >= 0]
-        got = gpool[pages].reshape(-1)
+        pages = block_table[b][block_table[b] >= 0]
+        got = cache.pool[torch.from_numpy(pages.astype(np.int64)).to(DEV)].cpu().numpy().reshape(-1)
         want = np.concatenate([pool[pg * slab:(pg + 1) * slab] for pg in pages])
-        assert np.array_equal(got, want), f"seq {b} pages differ"
+        assert np.array_equal(got, want), f"{label}: seq {b} pages differ"
     mask = np.zeros((w.batch, w.hq), np.uint8)
     mask[sample] = 1
-    want = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table,
-                              w.seq_lens, w.sm_scale, mask=mask)
-    assert_close(out.cpu().numpy().astype(np.float64)[sample], want[sample], "long full sampled")
+    return out.cpu().numpy().astype(np.float64)[sample], mask
 
 
-def test_concurrency_full_size_sampled():
+@pytest.mark.parametrize("kind", list(FULL_KINDS))
+def test_long_context_full_size_sampled(kind):
+    """Qwen3-4B-shaped long context at full size (8 x 131072 tokens, 65536
+    pages, per-channel scales in [0.1, 10]) with the default split plan, for
+    the rotated (block 64) and plain INT4 caches and the bf16 baseline: pages
+    of two sampled sequences bit-exact, their attention within tolerance."""
+    blk = FULL_KINDS[kind]
+    w = workloads.long_context_decode(4, device=DEV, batch=8, context=131072, block=blk)
+    print(f"long context full size {kind}", flush=True)
+    cache = _full_size_cache(kind, w)
+    dec = kvq.kvq_decode_attn_bf16 if kind == "bf16" else kvq.kvq_decode_attn
+    out = dec(cache, w.q, torch.from_numpy(w.block_table).to(DEV), torch.from_numpy(w.seq_lens).to(DEV),
+              w.max_seq_len, w.sm_scale)
+    torch.cuda.synchronize()
+    sample = [0, 5]
+    pool = _oracle_pool_for(w, sample, kind="bf16" if kind == "bf16" else "int4")
+    got, mask = _check_sampled(kind, cache, out, w, pool, sample, w.block_table, f"long {kind}")
+    del cache
+    if kind == "bf16":
+        want = oracle.decode_bf16(pool, w.hkv, w.d, bits(w.q), oracle.BF16, w.block_table,
+                                  w.seq_lens, w.sm_scale, mask=mask)
+    else:
+        want = oracle.decode_int4(pool, w.hkv, w.d, blk, bits(w.q), oracle.BF16, w.block_table,
+                                  w.seq_lens, w.sm_scale, mask=mask)
+    assert_close(got, want[sample], f"long full sampled {kind}")
+
+
+@pytest.mark.parametrize("kind", list(FULL_KINDS))
+def test_concurrency_full_size_sampled(kind):
     """70B-shaped layer (GQA 8) at the largest batch of the sweep: 256 ragged
     lognormal contexts (median 2048, cap 32768), one appended token per
-    sequence, then decode.  Sampled sequences (the longest, the shortest and
+    sequence, then decode, for the rotated (block 64) and plain INT4 caches
+    and the bf16 baseline.  Sampled sequences (the longest, the shortest and
     two more): pages bit-exact, attention within tolerance."""
-    fill, steps = workloads.concurrency_step(5, device=DEV, batch=256, block=64, steps=1)
+    blk = FULL_KINDS[kind]
+    fill, steps = workloads.concurrency_step(5, device=DEV, batch=256, block=blk, steps=1)
     step = steps[0]
-    print(f"concurrency full size: {int(fill.seq_lens.sum())} tokens", flush=True)
-    cache = kvq.Int4Cache(fill.num_pages, fill.hkv, fill.d, 64, DEV)
-    kvq.kvq_append_paged(cache, fill.k, fill.v, fill.slot_mapping)
-    kvq.kvq_append_paged(cache, step.k, step.v, step.slot_mapping)
-    out = kvq.kvq_decode_attn(cache, step.q, torch.from_numpy(step.block_table).to(DEV),
-                              torch.from_numpy(step.seq_lens).to(DEV), step.max_seq_len,
-                              step.sm_scale)
+    print(f"concurrency full size {kind}: {int(fill.seq_lens.sum())} tokens", flush=True)
+    cache = _full_size_cache(kind, fill, step)
+    dec = kvq.kvq_decode_attn_bf16 if kind == "bf16" else kvq.kvq_decode_attn
+    out = dec(cache, step.q, torch.from_numpy(step.block_table).to(DEV),
+              torch.from_numpy(step.seq_lens).to(DEV), step.max_seq_len, step.sm_scale)
     torch.cuda.synchronize()
     lens = fill.seq_lens
     sample = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 17, 200})
-    pool = _oracle_pool_for(fill, sample, step=step)
-    slab = fill.hkv * oracle.int4_slab_bytes(16, fill.d)
-    gpool = cache.pool.cpu().numpy()
-    for b in sample:
-        for pg in step.block_table[b][step.block_table[b] >= 0]:
-            # pages past the sequence's end were never written on either side
-            assert np.array_equal(gpool[pg], pool[pg * slab:(pg + 1) * slab]), f"seq {b} page {pg}"
-    mask = np.zeros((step.batch, step.hq), np.uint8)
-    mask[sample] = 1
-    want = oracle.decode_int4(pool, step.hkv, step.d, 64, bits(step.q), oracle.BF16,
-                              step.block_table, step.seq_lens, step.sm_scale, mask=mask)
-    assert_close(out.cpu().numpy().astype(np.float64)[sample], want[sample], "concurrency sampled")
+    pool = _oracle_pool_for(fill, sample, step=step, kind="bf16" if kind == "bf16" else "int4")
+    got, mask = _check_sampled(kind, cache, out, step, pool, sample, step.block_table, f"conc {kind}")
+    del cache
+    if kind == "bf16":
+        want = oracle.decode_bf16(pool, step.hkv, step.d, bits(step.q), oracle.BF16, step.block_table,
+                                  step.seq_lens, step.sm_scale, mask=mask)
+    else:
+        want = oracle.decode_int4(pool, step.hkv, step.d, blk, bits(step.q), oracle.BF16,
+                                  step.block_table, step.seq_lens, step.sm_scale, mask=mask)
+    assert_close(got, want[sample], f"concurrency sampled {kind}")
 
 
 # ---------------------------------------------------------------- high-precision windows

@@ -106,3 +106,43 @@ def test_absent_pages_are_left_out(kind):
         got = out.cpu().numpy().astype(np.float64)
         assert not got[2].any() and not got[3].any(), f"{kind} S{splits}: rows without tokens"
         _close(got, want, f"absent pages {kind} S{splits}")
+
+
+def test_absent_pages_windowed():
+    """The windowed call: absent pages in the INT4 block table and in the
+    window table both leave their tokens out, as in the oracle."""
+    w_sink, w_recent = 4, 12
+    w = workloads.random_decode(33, batch=5, hq=8, hkv=2, d=128, block=64,
+                                seq_lens=[70, 100, 9, 0, 40])
+    rng = np.random.default_rng(12)
+    wbt, npages = workloads.window_layout(w.batch, w_sink, w_recent, rng)
+    slots = workloads.window_slots(wbt, w.token_seq, w.token_pos, w.seq_lens, w_sink, w_recent)
+    win = kvq.Bf16Cache(npages, w.hkv, w.d, DEV)
+    kvq.kvq_append_paged_bf16(win, w.k.to(DEV), w.v.to(DEV), torch.from_numpy(slots).to(DEV))
+    wpool = oracle.new_bf16_pool(npages, w.hkv, w.d)
+    oracle.append_bf16(wpool, npages, w.hkv, w.d, bits(w.k), bits(w.v), oracle.BF16, slots)
+    cache = kvq.Int4Cache(w.num_pages, w.hkv, w.d, 64, DEV)
+    kvq.kvq_append_paged(cache, w.k.to(DEV), w.v.to(DEV), w.slot_mapping.to(DEV))
+    pool = oracle.new_int4_pool(w.num_pages, w.hkv, w.d)
+    oracle.append_int4(pool, w.num_pages, w.hkv, w.d, 64, bits(w.k), bits(w.v), oracle.BF16,
+                       w.slot_mapping.numpy())
+    bt, wt = w.block_table.copy(), wbt.copy()
+    bt[0][1] = -1                    # INT4 tokens 16..31 of sequence 0
+    wt[0][0] = npages + 5            # every window token of sequence 0 (past the window pool)
+    bt[1][3] = w.num_pages + 7       # INT4 tokens 48..63 of sequence 1
+    bt[2][0] = -2                    # sequence 2 lies in its window only, ...
+    wt[2][:] = -1                    # ... whose pages are absent too: a zero row
+    bt[4][2] = -1                    # the last, partial page of sequence 4: in its recent window
+    want = oracle.decode_windowed(pool, wpool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, bt, wt,
+                                  w.seq_lens, w_sink, w_recent, w.sm_scale)
+    assert not want[2].any() and not want[3].any()
+    torch.cuda.synchronize()
+    for splits in (0, 1, 3):
+        out = kvq.kvq_decode_attn_windowed(cache, win, w.q.to(DEV), torch.from_numpy(bt).to(DEV),
+                                           torch.from_numpy(wt).to(DEV),
+                                           torch.from_numpy(w.seq_lens).to(DEV), w.max_seq_len,
+                                           w_sink, w_recent, w.sm_scale, num_splits=splits)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert not got[2].any() and not got[3].any(), f"windowed S{splits}: rows without tokens"
+        _close(got, want, f"absent pages windowed S{splits}")
