@@ -70,6 +70,20 @@ def _declare(L):
     L.kvq_oracle_quantize.restype = None
     L.kvq_oracle_quantize_int8.argtypes = [_p, _i32, _p, _p, _p]
     L.kvq_oracle_quantize_int8.restype = None
+    L.kvq_oracle_grid_sse.argtypes = [_p, _i32, _p, C.c_uint16, C.c_uint16, _i32]
+    L.kvq_oracle_grid_sse.restype = C.c_int64
+    L.kvq_oracle_grid_exponent.argtypes = [C.c_float]
+    L.kvq_oracle_grid_exponent.restype = _i32
+    L.kvq_oracle_quantize_search.argtypes = [_p, _i32, _p, _p, _p]
+    L.kvq_oracle_quantize_search.restype = _i32
+    L.kvq_oracle_quantize_hybrid.argtypes = [_p, _i32, _p, _p, _p]
+    L.kvq_oracle_quantize_hybrid.restype = _i32
+    L.kvq_oracle_append_int4_search.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _i32, _i64,
+                                                _p, _i32]
+    L.kvq_oracle_append_int4_search.restype = _i32
+    L.kvq_oracle_append_int4g_hybrid.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _i32,
+                                                 _i64, _p, _i32]
+    L.kvq_oracle_append_int4g_hybrid.restype = _i32
     L.kvq_oracle_int8_slab_bytes.argtypes = [_i32, _i32]
     L.kvq_oracle_int8_slab_bytes.restype = C.c_size_t
     L.kvq_oracle_append_int8.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _i32, _i64, _p, _i32]
@@ -185,6 +199,37 @@ def quantize(y: np.ndarray, bits: int = 4):
     return codes, int(s[0]), int(z[0])
 
 
+def grid_sse(y: np.ndarray, codes: np.ndarray, scale: int, zero: int, k: int) -> int:
+    """Grid SSE of the scale search and the hybrid mode (integer)."""
+    y = _c(y, np.float32)
+    codes = _c(codes, np.uint8)
+    return int(lib().kvq_oracle_grid_sse(_ptr(y), y.shape[-1], _ptr(codes), int(scale), int(zero), int(k)))
+
+
+def grid_exponent(amax: float) -> int:
+    return int(lib().kvq_oracle_grid_exponent(float(amax)))
+
+
+def quantize_search(y: np.ndarray):
+    """Scale-searched INT4 of one key vector: (codes, scale bits, zero bits, j)."""
+    y = _c(y, np.float32)
+    codes = np.empty(y.shape[-1], np.uint8)
+    s = np.zeros(1, np.uint16)
+    z = np.zeros(1, np.uint16)
+    j = lib().kvq_oracle_quantize_search(_ptr(y), y.shape[-1], _ptr(codes), _ptr(s), _ptr(z))
+    return codes, int(s[0]), int(z[0]), int(j)
+
+
+def quantize_hybrid(y: np.ndarray):
+    """Hybrid INT4 of one group: (codes, scale bits, zero bits, symmetric?)."""
+    y = _c(y, np.float32)
+    codes = np.empty(y.shape[-1], np.uint8)
+    s = np.zeros(1, np.uint16)
+    z = np.zeros(1, np.uint16)
+    sym = lib().kvq_oracle_quantize_hybrid(_ptr(y), y.shape[-1], _ptr(codes), _ptr(s), _ptr(z))
+    return codes, int(s[0]), int(z[0]), bool(sym)
+
+
 def e2m1_encode(v: float) -> int:
     return int(lib().kvq_oracle_e2m1_encode(float(v)))
 
@@ -266,6 +311,22 @@ def append_int4(pool, num_pages, num_kv_heads, head_dim, block, k, v, dtype, slo
     return pool
 
 
+def append_int4_search(pool, num_pages, num_kv_heads, head_dim, block, k, v, dtype, slot_mapping,
+                       page_size=16, token_stride=None):
+    """As append_int4, with the keys quantized by the scale search."""
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    sm = _c(slot_mapping, np.int32)
+    if token_stride is None:
+        token_stride = num_kv_heads * head_dim
+    rc = lib().kvq_oracle_append_int4_search(_ptr(pool), num_pages, page_size, num_kv_heads, head_dim,
+                                             int(block), _ptr(k), _ptr(v), int(dtype), int(token_stride),
+                                             _ptr(sm), sm.shape[0])
+    if rc != 0:
+        raise ValueError("oracle append_int4_search rejected its arguments")
+    return pool
+
+
 def append_int8(pool, num_pages, num_kv_heads, head_dim, block, k, v, dtype, slot_mapping,
                 page_size=16, token_stride=None):
     """As append_int4, into the INT8 pool."""
@@ -295,6 +356,22 @@ def append_int4g(pool, num_pages, num_kv_heads, head_dim, block, group, k, v, dt
                                        int(dtype), int(token_stride), _ptr(sm), sm.shape[0])
     if rc != 0:
         raise ValueError("oracle append_int4g rejected its arguments")
+    return pool
+
+
+def append_int4g_hybrid(pool, num_pages, num_kv_heads, head_dim, block, group, k, v, dtype,
+                        slot_mapping, page_size=16, token_stride=None):
+    """Hybrid per-group INT4 into the grouped pool."""
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    sm = _c(slot_mapping, np.int32)
+    if token_stride is None:
+        token_stride = num_kv_heads * head_dim
+    rc = lib().kvq_oracle_append_int4g_hybrid(_ptr(pool), num_pages, page_size, num_kv_heads, head_dim,
+                                              int(block), int(group), _ptr(k), _ptr(v),
+                                              int(dtype), int(token_stride), _ptr(sm), sm.shape[0])
+    if rc != 0:
+        raise ValueError("oracle append_int4g_hybrid rejected its arguments")
     return pool
 
 

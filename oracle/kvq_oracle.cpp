@@ -249,23 +249,14 @@ void kvq_oracle_rotate(const float* x, float* y, int32_t d, int32_t b) {
 
 namespace {
 
-/* Token-wise asymmetric quantization of one vector to `levels` + 1 codes
- * 0..levels (15 for INT4, 255 for INT8): the steps of R2, R4 and R5. */
-void quantize_levels(const float* y, int32_t d, int levels, uint8_t* codes, uint16_t* scale,
-                     uint16_t* zero) {
+/* Codes of R4 under a given fp16 scale and zero point: (y - zero) * (1 /
+ * scale), each fp32 operation rounded once, round half to even, clamped to
+ * [0, levels]; a zero scale gives 1/scale = 0.  The scale's sign bit is not
+ * part of its value (R14 keeps a mode flag there). */
+void encode_codes(const float* y, int32_t d, int levels, uint16_t sh, uint16_t zh, uint8_t* codes) {
   std::fesetround(FE_TONEAREST);
   const float top = static_cast<float>(levels);
-  float mn = y[0], mx = y[0];
-  for (int i = 1; i < d; ++i) {
-    if (y[i] < mn) mn = y[i];
-    if (y[i] > mx) mx = y[i];
-  }
-  float zero_f = mn + 0.0f;
-  float range = (mx - mn) + 0.0f;
-  float step = range / top;
-  uint16_t sh = f32_to_f16(step);
-  uint16_t zh = f32_to_f16(zero_f);
-  float sf = f16_to_f32(sh);
+  float sf = f16_to_f32(static_cast<uint16_t>(sh & 0x7fffu));
   float zf = f16_to_f32(zh);
   float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
   for (int i = 0; i < d; ++i) {
@@ -276,8 +267,62 @@ void quantize_levels(const float* y, int32_t d, int levels, uint8_t* codes, uint
     if (c > top) c = top;
     codes[i] = static_cast<uint8_t>(c);
   }
-  *scale = sh;
-  *zero = zh;
+}
+
+/* The asymmetric quantizer of R2, R4, R5 from a given range [lo, hi]:
+ * zero = fp16(lo + 0), scale = fp16(((hi - lo) + 0) / levels), then the
+ * codes of R4. */
+void quantize_range(const float* y, int32_t d, int levels, float lo, float hi, uint8_t* codes,
+                    uint16_t* scale, uint16_t* zero) {
+  float zero_f = lo + 0.0f;
+  float range = (hi - lo) + 0.0f;
+  float step = range / static_cast<float>(levels);
+  *scale = f32_to_f16(step);
+  *zero = f32_to_f16(zero_f);
+  encode_codes(y, d, levels, *scale, *zero, codes);
+}
+
+/* Token-wise asymmetric quantization of one vector to `levels` + 1 codes
+ * 0..levels (15 for INT4, 255 for INT8): the steps of R2, R4 and R5 over the
+ * vector's own range. */
+void quantize_levels(const float* y, int32_t d, int levels, uint8_t* codes, uint16_t* scale,
+                     uint16_t* zero) {
+  float mn = y[0], mx = y[0];
+  for (int i = 1; i < d; ++i) {
+    if (y[i] < mn) mn = y[i];
+    if (y[i] > mx) mx = y[i];
+  }
+  quantize_range(y, d, levels, mn, mx, codes, scale, zero);
+}
+
+/* Criterion of R13 and R14: the sum of squared reconstruction errors of y
+ * under (codes, scale, zero), measured on the integer grid 2^-k.  Each
+ * element is decoded as code * |scale| + zero (the product is exact, the sum
+ * rounded once in fp32), its error y - decoded rounded once in fp32, scaled
+ * by 2^k and rounded to the nearest integer (ties to even); the squares are
+ * summed exactly in 64-bit integers, so the order of the sum does not
+ * matter. */
+int64_t grid_sse(const float* y, int32_t d, const uint8_t* codes, uint16_t sh, uint16_t zh, int k) {
+  std::fesetround(FE_TONEAREST);
+  const float sf = f16_to_f32(static_cast<uint16_t>(sh & 0x7fffu));
+  const float zf = f16_to_f32(zh);
+  int64_t sse = 0;
+  for (int i = 0; i < d; ++i) {
+    float decoded = static_cast<float>(codes[i]) * sf;
+    decoded = decoded + zf;
+    const float err = y[i] - decoded;
+    const int64_t e = static_cast<int64_t>(std::nearbyint(std::ldexp(err, k)));
+    sse += e * e;
+  }
+  return sse;
+}
+
+/* The grid of R13 and R14 for elements of magnitude at most amax: 2^-k with
+ * k = 20 - ex, amax < 2^ex (so every error is below 2^21 grid steps). */
+int grid_exponent(float amax) {
+  int ex = 0;
+  std::frexp(amax, &ex);
+  return 20 - ex;
 }
 
 /* The eight E2M1 magnitudes, in code order. */
@@ -336,6 +381,84 @@ void kvq_oracle_quantize_int8(const float* y, int32_t d, uint8_t* codes, uint16_
   quantize_levels(y, d, 255, codes, scale, zero);
 }
 
+int64_t kvq_oracle_grid_sse(const float* y, int32_t d, const uint8_t* codes, uint16_t scale,
+                            uint16_t zero, int32_t k) {
+  return grid_sse(y, d, codes, scale, zero, k);
+}
+
+int32_t kvq_oracle_grid_exponent(float amax) { return grid_exponent(amax); }
+
+int32_t kvq_oracle_quantize_search(const float* y, int32_t d, uint8_t* codes, uint16_t* scale,
+                                   uint16_t* zero) {
+  /* R13: the token-wise INT4 quantizer over the range [mn, mx] shrunk toward
+     zero by each factor alpha_j = (16 - j) / 16, j = 0 .. 7 (mn * alpha_j and
+     mx * alpha_j, one fp32 rounding each; elements outside are clamped by the
+     codes' clamp); the candidate with the smallest grid_sse wins, the
+     smaller j on a tie.  j = 0 is the plain quantizer. */
+  float mn = y[0], mx = y[0];
+  for (int i = 1; i < d; ++i) {
+    if (y[i] < mn) mn = y[i];
+    if (y[i] > mx) mx = y[i];
+  }
+  const float amax = std::fmax(std::fabs(mn), std::fabs(mx));
+  const int k = grid_exponent(amax);
+  std::vector<uint8_t> cand(d);
+  int64_t best = 0;
+  int best_j = -1;
+  for (int j = 0; j < 8; ++j) {
+    const float alpha = static_cast<float>(16 - j) / 16.0f;
+    uint16_t sh, zh;
+    quantize_range(y, d, 15, mn * alpha, mx * alpha, cand.data(), &sh, &zh);
+    const int64_t e = grid_sse(y, d, cand.data(), sh, zh, k);
+    if (best_j < 0 || e < best) {
+      best = e;
+      best_j = j;
+      std::memcpy(codes, cand.data(), static_cast<size_t>(d));
+      *scale = sh;
+      *zero = zh;
+    }
+  }
+  return best_j;
+}
+
+int32_t kvq_oracle_quantize_hybrid(const float* y, int32_t g, uint8_t* codes, uint16_t* scale,
+                                   uint16_t* zero) {
+  /* R14: two candidates for the group -- asymmetric (R2) and symmetric:
+     scale = fp16(amax / 7) with amax = max |y|, zero = -8 * scale (exact in
+     fp16 when finite), so that 0 is the level of code 8 and the levels run
+     from -8 scale to 7 scale -- each with the codes of R4; the symmetric one
+     wins when its grid_sse is not larger (it needs no zero point of its
+     own), and is then marked by the sign bit of the stored scale.  A group
+     of zeros, or one whose symmetric scale is 0 or whose -8 * scale is not
+     finite in fp16, stays asymmetric. */
+  uint16_t sa, za;
+  quantize_levels(y, g, 15, codes, &sa, &za);
+  *scale = sa;
+  *zero = za;
+  float mn = y[0], mx = y[0];
+  for (int i = 1; i < g; ++i) {
+    if (y[i] < mn) mn = y[i];
+    if (y[i] > mx) mx = y[i];
+  }
+  const float amax = std::fmax(std::fabs(mn), std::fabs(mx));
+  if (amax == 0.0f) return 0;
+  const uint16_t ss = f32_to_f16(amax / 7.0f);
+  const float sf = f16_to_f32(ss);
+  const float zs_f = -8.0f * sf;
+  if (sf == 0.0f || !(std::fabs(zs_f) <= 65504.0f)) return 0;
+  const uint16_t zs = f32_to_f16(zs_f);   /* exact: a power-of-two multiple */
+  std::vector<uint8_t> cs(g);
+  encode_codes(y, g, 15, ss, zs, cs.data());
+  const int k = grid_exponent(amax);
+  if (grid_sse(y, g, cs.data(), ss, zs, k) <= grid_sse(y, g, codes, sa, za, k)) {
+    std::memcpy(codes, cs.data(), static_cast<size_t>(g));
+    *scale = static_cast<uint16_t>(ss | 0x8000u);
+    *zero = zs;
+    return 1;
+  }
+  return 0;
+}
+
 size_t kvq_oracle_int4_slab_bytes(int32_t page_size, int32_t head_dim) { return int4_slab(page_size, head_dim); }
 size_t kvq_oracle_bf16_slab_bytes(int32_t page_size, int32_t head_dim) { return bf16_slab(page_size, head_dim); }
 size_t kvq_oracle_int8_slab_bytes(int32_t page_size, int32_t head_dim) { return int8_slab(page_size, head_dim); }
@@ -344,11 +467,17 @@ size_t kvq_oracle_int4g_slab_bytes(int32_t page_size, int32_t head_dim, int32_t 
   return int4g_slab(page_size, head_dim, group);
 }
 
-int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_size,
-                               int32_t num_kv_heads, int32_t head_dim, int32_t block,
-                               const uint16_t* k, const uint16_t* v, int32_t dtype,
-                               int64_t token_stride, const int32_t* slot_mapping,
-                               int32_t num_tokens) {
+}  // extern "C"
+
+namespace {
+
+/* The INT4 append with the key quantizer `kq` (the plain R2 quantizer, or
+ * R13's scale search); values always take the plain one. */
+template <class KeyQuant>
+int32_t append_int4_with(KeyQuant kq, uint8_t* pool, int32_t num_pages, int32_t page_size,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                         const uint16_t* k, const uint16_t* v, int32_t dtype,
+                         int64_t token_stride, const int32_t* slot_mapping, int32_t num_tokens) {
   const int p = page_size, d = head_dim, hkv = num_kv_heads;
   if (!valid_block(block, d) || p % 4 != 0 || d % 8 != 0) return 1;
   const size_t slab = int4_slab(p, d);
@@ -367,7 +496,8 @@ int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_si
         for (int c = 0; c < d; ++c) x[c] = widen(src[c], dtype);
         kvq_oracle_rotate(x.data(), y.data(), d, block);
         uint16_t sh, zh;
-        kvq_oracle_quantize(y.data(), d, codes.data(), &sh, &zh);
+        if (kind == 0) kq(y.data(), d, codes.data(), &sh, &zh);
+        else kvq_oracle_quantize(y.data(), d, codes.data(), &sh, &zh);
         for (int c = 0; c < d; c += 2) {
           uint8_t byte = static_cast<uint8_t>(codes[c] | (codes[c + 1] << 4));
           size_t at = kind == 0 ? k_code_byte(p, d, off, c) : v_code_byte(p, d, off, c);
@@ -379,6 +509,31 @@ int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_si
     }
   }
   return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                               const uint16_t* k, const uint16_t* v, int32_t dtype,
+                               int64_t token_stride, const int32_t* slot_mapping,
+                               int32_t num_tokens) {
+  return append_int4_with(kvq_oracle_quantize, pool, num_pages, page_size, num_kv_heads, head_dim,
+                          block, k, v, dtype, token_stride, slot_mapping, num_tokens);
+}
+
+int32_t kvq_oracle_append_int4_search(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                                      const uint16_t* k, const uint16_t* v, int32_t dtype,
+                                      int64_t token_stride, const int32_t* slot_mapping,
+                                      int32_t num_tokens) {
+  auto search = [](const float* y, int32_t d, uint8_t* codes, uint16_t* scale, uint16_t* zero) {
+    kvq_oracle_quantize_search(y, d, codes, scale, zero);
+  };
+  return append_int4_with(search, pool, num_pages, page_size, num_kv_heads, head_dim, block, k, v,
+                          dtype, token_stride, slot_mapping, num_tokens);
 }
 
 int32_t kvq_oracle_append_int8(uint8_t* pool, int32_t num_pages, int32_t page_size,
@@ -415,11 +570,17 @@ int32_t kvq_oracle_append_int8(uint8_t* pool, int32_t num_pages, int32_t page_si
   return 0;
 }
 
-int32_t kvq_oracle_append_int4g(uint8_t* pool, int32_t num_pages, int32_t page_size,
-                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
-                                int32_t group, const uint16_t* k, const uint16_t* v,
-                                int32_t dtype, int64_t token_stride, const int32_t* slot_mapping,
-                                int32_t num_tokens) {
+}  // extern "C"
+
+namespace {
+
+/* The grouped INT4 append with the group quantizer `gq` (R10's, or R14's
+ * hybrid one). */
+template <class GroupQuant>
+int32_t append_int4g_with(GroupQuant gq, uint8_t* pool, int32_t num_pages, int32_t page_size,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block, int32_t group,
+                          const uint16_t* k, const uint16_t* v, int32_t dtype,
+                          int64_t token_stride, const int32_t* slot_mapping, int32_t num_tokens) {
   const int p = page_size, d = head_dim, hkv = num_kv_heads;
   if (!valid_block(block, d) || p % 4 != 0 || d % 16 != 0) return 1;
   if (group < 16 || d % group != 0) return 1;
@@ -440,7 +601,7 @@ int32_t kvq_oracle_append_int4g(uint8_t* pool, int32_t num_pages, int32_t page_s
         kvq_oracle_rotate(x.data(), y.data(), d, block);
         for (int gi = 0; gi < d / group; ++gi) {
           uint16_t sh, zh;
-          kvq_oracle_quantize(&y[gi * group], group, &codes[gi * group], &sh, &zh);   /* R10 */
+          gq(&y[gi * group], group, &codes[gi * group], &sh, &zh);   /* R10 / R14 */
           put_u16(s + metag_byte(p, d, group, kind, off, gi), sh);
           put_u16(s + metag_byte(p, d, group, kind, off, gi) + 2, zh);
         }
@@ -453,6 +614,31 @@ int32_t kvq_oracle_append_int4g(uint8_t* pool, int32_t num_pages, int32_t page_s
     }
   }
   return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_oracle_append_int4g(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                                int32_t group, const uint16_t* k, const uint16_t* v,
+                                int32_t dtype, int64_t token_stride, const int32_t* slot_mapping,
+                                int32_t num_tokens) {
+  return append_int4g_with(kvq_oracle_quantize, pool, num_pages, page_size, num_kv_heads, head_dim,
+                           block, group, k, v, dtype, token_stride, slot_mapping, num_tokens);
+}
+
+int32_t kvq_oracle_append_int4g_hybrid(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                                       int32_t group, const uint16_t* k, const uint16_t* v,
+                                       int32_t dtype, int64_t token_stride,
+                                       const int32_t* slot_mapping, int32_t num_tokens) {
+  auto hybrid = [](const float* y, int32_t g, uint8_t* codes, uint16_t* scale, uint16_t* zero) {
+    kvq_oracle_quantize_hybrid(y, g, codes, scale, zero);
+  };
+  return append_int4g_with(hybrid, pool, num_pages, page_size, num_kv_heads, head_dim, block, group,
+                           k, v, dtype, token_stride, slot_mapping, num_tokens);
 }
 
 int32_t kvq_oracle_append_mxfp4(uint8_t* pool, int32_t num_pages, int32_t page_size,
@@ -565,7 +751,8 @@ double kvq_oracle_int4g_read(const uint8_t* pool, int32_t page_size, int32_t num
   if (code) *code = c;
   if (scale) *scale = sh;
   if (zero) *zero = zh;
-  return static_cast<double>(c) * static_cast<double>(f16_to_f32(sh)) +
+  /* the scale's sign bit is the hybrid mode flag (R14), not part of it */
+  return static_cast<double>(c) * static_cast<double>(f16_to_f32(static_cast<uint16_t>(sh & 0x7fffu))) +
          static_cast<double>(f16_to_f32(zh));
 }
 

@@ -52,6 +52,32 @@
  *       rounded to the nearest E2M1 value {0, 0.5, 1, 1.5, 2, 3, 4, 6}
  *       (ties to the code with mantissa bit 0, saturating at 6, sign only
  *       on nonzero codes).  Decoded value = E2M1 value * 2^X.
+ *   R13 scale search for keys ("BitDecoding-FP4", Abstract: outlier-aware
+ *       key quantization combines Hadamard rotation with a scale search under
+ *       token-wise scaling; the pages give neither the grid nor the
+ *       criterion): the token-wise INT4 quantizer of R2 is tried over the key
+ *       vector's range [mn, mx] shrunk toward zero by alpha_j = (16 - j)/16,
+ *       j = 0 .. 7 (mn * alpha_j and mx * alpha_j in fp32; elements outside
+ *       the range are clamped by the codes' clamp), and the candidate with the
+ *       smallest grid SSE wins (the smaller j on a tie; j = 0 is the plain
+ *       quantizer).  Grid SSE: each element decoded as code * scale + zero
+ *       (fp32, the product exact, the sum rounded once), its error rounded
+ *       once in fp32, scaled by 2^k with k = 20 - ex where max |y| < 2^ex
+ *       (frexp), rounded to an integer (ties to even), squared and summed in
+ *       64-bit integers: exact, so the sum's order does not matter.  Values
+ *       keep the plain quantizer.
+ *   R14 hybrid symmetric/asymmetric per group ("InnerQ", Abstract and
+ *       Figure 3: symmetric or asymmetric quantization chosen per group from
+ *       the group's own statistics; the rule is not given): the asymmetric
+ *       candidate is R2 over the group; the symmetric one has scale =
+ *       fp16(amax / 7), amax = max |y|, and zero = -8 * scale (exact in
+ *       fp16), so the levels (code - 8) * scale hold 0 and reach 7 * scale =
+ *       amax; both take the codes of R4.  The symmetric one is kept when its
+ *       grid SSE (as in R13) is not larger, and is then marked by setting the
+ *       sign bit of the stored fp16 scale; a decoded element is code *
+ *       |scale| + zero in both modes.  A group of zeros, or one whose
+ *       symmetric scale is 0 or whose -8 * scale overflows fp16, stays
+ *       asymmetric.
  *   R7  softmax scale is a parameter (normally 1/sqrt(head_dim)); grouped
  *       query attention maps query head h to KV head h / (Hq / Hkv); an empty
  *       sequence gives a zero output; slot < 0 means "do not store".
@@ -84,7 +110,9 @@
  *                             (nibble j: byte j/2, bits 4(j%2)..+3).
  *     bytes [P*D, +4P*D/g)    K sidecar: token t, group i -> fp16 scale at
  *                             4(t*(D/g) + i), fp16 zero 2 bytes later.
- *     then the V sidecar in the same form.
+ *     then the V sidecar in the same form.  The scale's sign bit marks a
+ *     symmetric group of the hybrid quantizer (R14); a decoded element is
+ *     code * |scale| + zero.
  *   MXFP4 pool (R12): [num_pages][num_kv_heads][slab], slab = P * (D + D/16)
  *   bytes:
  *     bytes [0, P*D)          K and V E2M1 codes, placed as the grouped INT4
@@ -135,6 +163,23 @@ void kvq_oracle_quantize(const float* y, int32_t d, uint8_t* codes,
 void kvq_oracle_quantize_int8(const float* y, int32_t d, uint8_t* codes,
                               uint16_t* scale, uint16_t* zero);
 
+/* Grid SSE of R13/R14 for n elements under (codes, fp16 scale, fp16 zero),
+ * on the grid 2^-k; and the k of R13/R14 for elements of magnitude at most
+ * amax. */
+int64_t kvq_oracle_grid_sse(const float* y, int32_t d, const uint8_t* codes, uint16_t scale,
+                            uint16_t zero, int32_t k);
+int32_t kvq_oracle_grid_exponent(float amax);
+
+/* Token-wise INT4 of one key vector with the scale search of R13; returns
+ * the chosen j (alpha = (16 - j) / 16). */
+int32_t kvq_oracle_quantize_search(const float* y, int32_t d, uint8_t* codes,
+                                   uint16_t* scale, uint16_t* zero);
+
+/* Hybrid INT4 of one group of g values (R14); returns 1 for the symmetric
+ * mode (its scale then carries the sign bit), 0 for the asymmetric one. */
+int32_t kvq_oracle_quantize_hybrid(const float* y, int32_t g, uint8_t* codes,
+                                   uint16_t* scale, uint16_t* zero);
+
 /* E2M1 code of one value (R12) and the value of a code. */
 uint8_t kvq_oracle_e2m1_encode(float v);
 double  kvq_oracle_e2m1_decode(uint8_t code);
@@ -158,6 +203,14 @@ int32_t kvq_oracle_append_int4(uint8_t* pool, int32_t num_pages, int32_t page_si
                                int64_t token_stride, const int32_t* slot_mapping,
                                int32_t num_tokens);
 
+/* kvq_oracle_append_int4 with the keys quantized by the scale search of R13
+ * (values by the plain quantizer); the same INT4 pool. */
+int32_t kvq_oracle_append_int4_search(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                                      const uint16_t* k, const uint16_t* v, int32_t dtype,
+                                      int64_t token_stride, const int32_t* slot_mapping,
+                                      int32_t num_tokens);
+
 /* The same into the INT8 pool (R9). */
 int32_t kvq_oracle_append_int8(uint8_t* pool, int32_t num_pages, int32_t page_size,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block,
@@ -171,6 +224,14 @@ int32_t kvq_oracle_append_int4g(uint8_t* pool, int32_t num_pages, int32_t page_s
                                 int32_t group, const uint16_t* k, const uint16_t* v,
                                 int32_t dtype, int64_t token_stride, const int32_t* slot_mapping,
                                 int32_t num_tokens);
+
+/* kvq_oracle_append_int4g with the hybrid per-group quantizer of R14 (K and
+ * V); the same grouped pool, read with |scale|. */
+int32_t kvq_oracle_append_int4g_hybrid(uint8_t* pool, int32_t num_pages, int32_t page_size,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block,
+                                       int32_t group, const uint16_t* k, const uint16_t* v,
+                                       int32_t dtype, int64_t token_stride,
+                                       const int32_t* slot_mapping, int32_t num_tokens);
 
 /* Rotate + MXFP4-quantize (R12) + scatter into the MXFP4 pool. */
 int32_t kvq_oracle_append_mxfp4(uint8_t* pool, int32_t num_pages, int32_t page_size,
