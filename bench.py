@@ -22,8 +22,12 @@ alone in a decode-only loop, and ``rotated_over_plain_decode`` compares block
 
 Other modes (for rocprofv3 runs): ``--mode decode`` times only the headline
 decode; ``--mode prefill`` only the prefill append; ``--mode concurrency``
-only the concurrency sweep; ``--mode copy`` runs a plain 1 GiB device copy
-used to calibrate the FETCH_SIZE / WRITE_SIZE counters.
+only the concurrency sweep; ``--mode serving --batch B --cache C`` the
+70B-shaped serving step of one batch size and cache kind; ``--mode variant
+--cache C`` one decode variant (int8, int4g64, mxfp4, windowed, bf16) on the
+headline workload; ``--mode ceiling`` what the memory system gives the
+path's access patterns (probe kernels); ``--mode copy`` runs a plain 1 GiB
+device copy used to calibrate the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
 
@@ -318,6 +322,43 @@ def variant_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes, kind)
     return res
 
 
+def variant_decode(torch, kvq, workloads, db, kind, iters, warm):
+    """One decode variant alone on the headline workload (block 64), two
+    cache copies alternating, timed per call: the kernels for profiles."""
+    w = db.w
+    if kind == "windowed":
+        res = windowed_rate(torch, kvq, workloads, db, iters, 1.0, 1)
+        res.pop("time_over_int4_block64")
+        return res
+    if kind == "bf16":
+        db.int4 = db.int4[:1]
+        db.make_bf16()
+        fn, caches = kvq.kvq_decode_attn_bf16, db.bf16
+        vec = 2 * w.d
+    else:
+        make, app_fn, fn, vec = {
+            "int8": (lambda: kvq.Int8Cache(w.num_pages, w.hkv, w.d, 64, "cuda"), kvq.kvq_append_paged_int8,
+                     kvq.kvq_decode_attn_int8, w.d + 4),
+            "int4g64": (lambda: kvq.Int4GroupedCache(w.num_pages, w.hkv, w.d, 64, 64, "cuda"),
+                        kvq.kvq_append_paged_int4g, kvq.kvq_decode_attn_int4g, w.d // 2 + 4 * (w.d // 64)),
+            "mxfp4": (lambda: kvq.MxFp4Cache(w.num_pages, w.hkv, w.d, 64, "cuda"), kvq.kvq_append_paged_mxfp4,
+                      kvq.kvq_decode_attn_mxfp4, w.d // 2 + w.d // 32),
+        }[kind]
+        caches = [make() for _ in range(2)]
+        for c in caches:
+            app_fn(c, w.k, w.v, w.slot_mapping)
+
+    def dec(i):
+        fn(caches[i % 2], db.qs[i % RING], db.bt, db.sl, w.max_seq_len, w.sm_scale, out=db.out,
+           workspace=db.ws)
+
+    for i in range(warm):
+        dec(i)
+    ms, _ = _time_events(torch, dec, iters)
+    nbytes = decode_bytes(w.seq_lens, w.hkv, w.hq, w.d, vec)
+    return {"us": round(ms * 1e3, 2), "bytes": nbytes, "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def long_context_rate(torch, kvq, workloads, iters=30):
     """Qwen3-4B-shaped long-context decode (8 x 131072 tokens, 65536 pages):
     split-K over pages plus the reduce, timed per call on two cache copies,
@@ -352,47 +393,75 @@ def long_context_rate(torch, kvq, workloads, iters=30):
     return res
 
 
+RING_BYTES = 1 << 30   # each concurrency-sweep ring of layer caches holds at least 1 GiB
+
+
+class ServingRing:
+    """The 70B-shaped serving step at one batch size for one cache kind
+    ("int4_block64", "int4_plain" or "bf16"): a ring of layer caches of at
+    least RING_BYTES in all (successive layers of one decode step, so the
+    256 MB Infinity Cache cannot hold what a step reads), each filled with the
+    whole context and every step's token (a timed step rewrites its token's
+    slot with the same bytes, so every layer holds valid data for every
+    step).  Step i appends its token to layer i mod R and decodes it."""
+
+    def __init__(self, torch, kvq, fill, steps, name, ws, out):
+        self.kvq, self.st, self.ws, self.out = kvq, steps, ws, out
+        self.bt = torch.from_numpy(steps[0].block_table).to("cuda")
+        self.sls = [torch.from_numpy(x.seq_lens).to("cuda") for x in steps]
+        self.maxlen = int(steps[-1].max_seq_len)
+        if name == "bf16":
+            make = lambda: kvq.Bf16Cache(fill.num_pages, fill.hkv, fill.d, "cuda")
+            self.app, self.dec = kvq.kvq_append_paged_bf16, kvq.kvq_decode_attn_bf16
+            vec = 2 * fill.d
+        else:
+            blk = 64 if name == "int4_block64" else 0
+            make = lambda: kvq.Int4Cache(fill.num_pages, fill.hkv, fill.d, blk, "cuda")
+            self.app, self.dec = kvq.kvq_append_paged, kvq.kvq_decode_attn
+            vec = int4_bytes_per_vector(fill.d)
+        layer = decode_bytes(steps[-1].seq_lens, fill.hkv, fill.hq, fill.d, vec)
+        self.ring = max(2, -(-RING_BYTES // layer))
+        self.caches = []
+        for _ in range(self.ring):
+            c = make()
+            self.app(c, fill.k, fill.v, fill.slot_mapping)
+            for x in steps:
+                self.app(c, x.k, x.v, x.slot_mapping)
+            self.caches.append(c)
+
+    def run(self, i):
+        c, x = self.caches[i % self.ring], self.st[i]
+        self.app(c, x.k, x.v, x.slot_mapping)
+        self.dec(c, x.q, self.bt, self.sls[i], self.maxlen, x.sm_scale, out=self.out, workspace=self.ws)
+
+
 def concurrency_sweep(torch, kvq, workloads, steps=48, warm=8, block_steps=8,
                       batches=(1, 8, 32, 128, 256)):
-    """70B-shaped layer (64 q / 8 kv heads): per batch size, fill the ragged
-    lognormal contexts into a rotated INT4, a plain INT4 and a bf16 cache, run
-    ``warm`` untimed decode steps on each (append one token per sequence, then
-    decode over it), then time ``steps`` more per cache in runs of
-    ``block_steps`` that alternate between the caches, the first of each round
-    rotating (6 rounds: each cache first twice), so that all three see the
-    same clocks.  Tokens/s = batch * steps / time.  Successive steps attend
-    the same cache, as a serving loop does (small batches stay in the Infinity
-    Cache).  The steps are timed twice: called one by one from Python (the
-    host's per-call cost included; it bounds the small batches), and captured
-    in HIP graphs and replayed."""
+    """70B-shaped layer (64 q / 8 kv heads): per batch size and cache kind
+    (rotated INT4, plain INT4, bf16), a ServingRing of layer caches; ``warm``
+    untimed steps on each, then ``steps`` more per kind in runs of
+    ``block_steps`` that alternate between the kinds, the first of each round
+    rotating (6 rounds: each kind first twice), so that all three see the
+    same clocks.  Tokens/s = batch / time per step (one layer).  The steps are
+    timed twice: called one by one from Python (the host's per-call cost
+    included; it bounds the small batches), and captured in HIP graphs and
+    replayed."""
     out = {"workload": "64 q / 8 kv heads, head_dim 128, lognormal contexts (median 2048, "
-                       "sigma 1, cap 32768), page 16, one new token per sequence per step",
+                       "sigma 1, cap 32768), page 16, one new token per sequence per step; "
+                       "successive steps on successive layers of a ring of >= 1 GiB per cache kind",
            "steps": steps}
     names = ("int4_block64", "int4_plain", "bf16")
     for b in batches:
         fill, st = workloads.concurrency_step(5, device="cuda", batch=b, block=64, steps=warm + steps)
-        bt = torch.from_numpy(st[0].block_table).to("cuda")
-        sls = [torch.from_numpy(x.seq_lens).to("cuda") for x in st]
         maxlen = int(st[-1].max_seq_len)
         ws = torch.empty(max(16, kvq.kvq_decode_workspace_bytes(b, fill.hq, fill.hkv, fill.d, maxlen)),
                          dtype=torch.uint8, device="cuda")
         o = torch.empty((b, fill.hq, fill.d), dtype=torch.float32, device="cuda")
-        caches, fns = {}, {}
-        for name in names:
-            if name == "bf16":
-                caches[name] = kvq.Bf16Cache(fill.num_pages, fill.hkv, fill.d, "cuda")
-                fns[name] = (kvq.kvq_append_paged_bf16, kvq.kvq_decode_attn_bf16)
-            else:
-                caches[name] = kvq.Int4Cache(fill.num_pages, fill.hkv, fill.d,
-                                             64 if name == "int4_block64" else 0, "cuda")
-                fns[name] = (kvq.kvq_append_paged, kvq.kvq_decode_attn)
-            fns[name][0](caches[name], fill.k, fill.v, fill.slot_mapping)
+        rings = {name: ServingRing(torch, kvq, fill, st, name, ws, o) for name in names}
+        torch.cuda.synchronize()
 
         def run(name, i):
-            app, dec = fns[name]
-            x = st[i]
-            app(caches[name], x.k, x.v, x.slot_mapping)
-            dec(caches[name], x.q, bt, sls[i], maxlen, x.sm_scale, out=o, workspace=ws)
+            rings[name].run(i)
 
         for name in names:
             for i in range(warm):
@@ -440,7 +509,8 @@ def concurrency_sweep(torch, kvq, workloads, steps=48, warm=8, block_steps=8,
                 e1.record()
                 torch.cuda.synchronize()
                 gms[name] += e0.elapsed_time(e1)
-        row = {"context_tokens": int(fill.seq_lens.sum())}
+        row = {"context_tokens": int(fill.seq_lens.sum()),
+               "ring_layers": {name: rings[name].ring for name in names}}
         for name in names:
             row[name] = {"us_per_step": round(ms[name] * 1e3 / steps, 2),
                          "tokens_s": round(b * steps / (ms[name] * 1e-3), 1),
@@ -452,11 +522,84 @@ def concurrency_sweep(torch, kvq, workloads, steps=48, warm=8, block_steps=8,
                                                 / row["int4_plain"]["graph_tokens_s"], 4)
         row["graph_int4_over_bf16"] = round(row["int4_block64"]["graph_tokens_s"]
                                             / row["bf16"]["graph_tokens_s"], 3)
-        del graphs
+        del graphs, rings
         out[f"batch{b}"] = row
-        del fill, st, caches
+        del fill, st
         torch.cuda.empty_cache()
     return out
+
+
+def serving_mode(torch, kvq, workloads, batch, name, steps, warm):
+    """One cache kind's serving steps at one batch size (ServingRing), timed
+    back to back: the kernels of the 70B-shaped step alone, for profiles."""
+    fill, st = workloads.concurrency_step(5, device="cuda", batch=batch, block=64, steps=warm + steps)
+    maxlen = int(st[-1].max_seq_len)
+    ws = torch.empty(max(16, kvq.kvq_decode_workspace_bytes(batch, fill.hq, fill.hkv, fill.d, maxlen)),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty((batch, fill.hq, fill.d), dtype=torch.float32, device="cuda")
+    ring = ServingRing(torch, kvq, fill, st, name, ws, o)
+    for i in range(warm):
+        ring.run(i)
+    ms, _ = _time_events(torch, lambda i: ring.run(warm + i), steps)
+    return {"batch": batch, "cache": name, "ring_layers": ring.ring, "us_per_step": round(ms * 1e3, 2),
+            "tokens_s": round(batch / (ms * 1e-3), 1)}
+
+
+def ceiling_mode(torch, iters=20):
+    """What the memory system gives the hot path's access patterns on this
+    GPU, from the probe kernels of libkvq_probe.so: the decode's gather of
+    2176-byte page slabs in a seeded random order (1.14 GB, four layers'
+    worth of the headline cache), a streaming read of 4 GiB, and streaming
+    reads with a 4:1 and a 1:1 read:write mix (the append moves about 4 bytes
+    in per byte out).  TB/s of the bytes each probe moves."""
+    import ctypes as C
+    import numpy as np
+    import bit_kv_cache_block_amd as kvq_pkg
+
+    L = C.CDLL(os.path.join(os.path.dirname(kvq_pkg.__file__), "libkvq_probe.so"))
+    p, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+    L.kvq_probe_gather.argtypes = [p, i32, p, i32, i32, p, p]
+    L.kvq_probe_stream.argtypes = [p, i64, i32, p, i32, p, p]
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    grid = 2048
+    sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    res = {}
+
+    def timed(fn, nbytes):
+        for _ in range(3):
+            fn()
+        ms, _ = _time_events(torch, lambda i: fn(), iters)
+        return round(nbytes / (ms * 1e-3) / 1e12, 3)
+
+    slab, nslab = 2176, 4 * 16384 * 8
+    pool = torch.empty(nslab * slab, dtype=torch.uint8, device="cuda").fill_(3)
+    rng = np.random.default_rng(7)
+    ids = torch.from_numpy(rng.permutation(nslab).astype(np.int32)).to("cuda")
+
+    def gather():
+        assert L.kvq_probe_gather(p(pool.data_ptr()), slab, p(ids.data_ptr()), nslab, grid,
+                                  p(sink.data_ptr()), stream) == 0
+
+    res["gather_2176B_slabs_tb_s"] = timed(gather, nslab * slab)
+    del pool, ids
+    src = torch.empty(1 << 32, dtype=torch.uint8, device="cuda").fill_(5)
+
+    def read():
+        assert L.kvq_probe_stream(p(src.data_ptr()), (1 << 32) // 16, 1, None, grid,
+                                  p(sink.data_ptr()), stream) == 0
+
+    res["stream_read_tb_s"] = timed(read, 1 << 32)
+    for ratio in (4, 1):
+        items = (1 << 32) // 16 // ratio
+        dst = torch.empty(items * 16, dtype=torch.uint8, device="cuda")
+
+        def mix():
+            assert L.kvq_probe_stream(p(src.data_ptr()), items, ratio, p(dst.data_ptr()), grid,
+                                      None, stream) == 0
+
+        res[f"stream_{ratio}to1_read_write_tb_s"] = timed(mix, items * 16 * (ratio + 1))
+        del dst
+    return res
 
 
 def cpu_baseline(w, budget_s=15.0):
@@ -541,7 +684,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=["full", "decode", "prefill", "copy", "concurrency"], default="full")
+    ap.add_argument("--mode", choices=["full", "decode", "prefill", "copy", "concurrency", "serving",
+                                       "variant", "ceiling"], default="full")
+    ap.add_argument("--batch", type=int, default=256, help="serving mode: batch size")
+    ap.add_argument("--cache", default="int4_block64",
+                    help="serving mode: int4_block64, int4_plain or bf16; variant mode: int8, "
+                         "int4g64, mxfp4, windowed or bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -565,6 +713,15 @@ def main(argv=None):
         print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
         return 0
 
+    if args.mode == "ceiling":
+        print(json.dumps({"mode": "ceiling", **ceiling_mode(torch)}))
+        return 0
+
+    if args.mode == "serving":
+        print(json.dumps({"mode": "serving", **serving_mode(torch, kvq, workloads, args.batch, args.cache,
+                                                            args.steps, args.warmup)}))
+        return 0
+
     if args.mode == "concurrency":
         print(json.dumps({"mode": "concurrency", **concurrency_sweep(torch, kvq, workloads)}))
         return 0
@@ -585,6 +742,11 @@ def main(argv=None):
             db.decode(i)
         ms, _ = _time_events(torch, db.decode, args.steps)
         print(json.dumps({"mode": "decode", "us": ms * 1e3, "gb_s": dec_bytes / (ms * 1e-3) / 1e9}))
+        return 0
+
+    if args.mode == "variant":
+        print(json.dumps({"mode": "variant", "cache": args.cache,
+                          **variant_decode(torch, kvq, workloads, db, args.cache, args.steps, args.warmup)}))
         return 0
 
     # ---- headline: K steps of append + decode ------------------------------
@@ -623,6 +785,18 @@ def main(argv=None):
         at = lambda f: s[min(len(s) - 1, int(f * (len(s) - 1) + 0.5))]
         return {"p10": round(at(0.1) * 1e3, 2), "p50": round(at(0.5) * 1e3, 2), "p90": round(at(0.9) * 1e3, 2)}
     value = dec_bytes / (dec_mean * 1e-3) / 1e9
+    # the same decode launched back to back (one event pair around the whole
+    # run): the kernel's own duration without the per-call event gap
+    for i in range(10):
+        db.decode(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        db.decode(i)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_b2b_ms = e0.elapsed_time(e1) / args.steps
 
     # ---- variants on the same workload, all timed alone (decode only) ---------
     variants = {}
@@ -707,6 +881,8 @@ def main(argv=None):
         "roofline": {
             "bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(value / PEAK_HBM_GBS, 4),
+            "kernel_us_back_to_back": round(dec_b2b_ms * 1e3, 2),
+            "frac_kernel": round(dec_bytes / (dec_b2b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "kernel": "decode_quant_kernel<128, 1, true, 4, 0, 1, false> (one kvq_decode_attn call; at this shape the split "
                       "plan is one split per (sequence, KV head), so no reduce kernel runs)",

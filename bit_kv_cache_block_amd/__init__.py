@@ -7,6 +7,7 @@ kernels of libkvq.so.  There is no fallback: if the library is missing, every
 call raises.
 
 Entry points carry the C names: ``kvq_append_paged``, ``kvq_decode_attn``,
+``kvq_append_paged_int4_search``, ``kvq_append_paged_int4g_hybrid``,
 ``kvq_decode_attn_windowed``, ``kvq_append_paged_int8``, ``kvq_decode_attn_int8``,
 ``kvq_append_paged_int4g``, ``kvq_decode_attn_int4g``, ``kvq_append_paged_mxfp4``,
 ``kvq_decode_attn_mxfp4``,
@@ -32,6 +33,7 @@ PAGE_SIZE = 16
 EXPORTED = (
     "kvq_int4_page_bytes", "kvq_int8_page_bytes", "kvq_int4g_page_bytes", "kvq_bf16_page_bytes",
     "kvq_append_paged", "kvq_decode_attn", "kvq_append_paged_int8", "kvq_decode_attn_int8",
+    "kvq_append_paged_int4_search", "kvq_append_paged_int4g_hybrid",
     "kvq_append_paged_int4g", "kvq_decode_attn_int4g", "kvq_mxfp4_page_bytes",
     "kvq_append_paged_mxfp4", "kvq_decode_attn_mxfp4",
     "kvq_decode_workspace_bytes", "kvq_append_paged_bf16", "kvq_decode_attn_bf16",
@@ -88,6 +90,10 @@ def lib() -> C.CDLL:
         L.kvq_bf16_page_bytes.restype = sz
         L.kvq_append_paged.argtypes = [C.POINTER(_QuantDesc), p, p, i32, i64, p, i32, p]
         L.kvq_append_paged.restype = i32
+        L.kvq_append_paged_int4_search.argtypes = [C.POINTER(_QuantDesc), p, p, i32, i64, p, i32, p]
+        L.kvq_append_paged_int4_search.restype = i32
+        L.kvq_append_paged_int4g_hybrid.argtypes = [C.POINTER(_GroupedDesc), p, p, i32, i64, p, i32, p]
+        L.kvq_append_paged_int4g_hybrid.restype = i32
         L.kvq_append_paged_int8.argtypes = [C.POINTER(_QuantDesc), p, p, i32, i64, p, i32, p]
         L.kvq_append_paged_int8.restype = i32
         L.kvq_append_paged_mxfp4.argtypes = [C.POINTER(_QuantDesc), p, p, i32, i64, p, i32, p]
@@ -300,6 +306,19 @@ def kvq_append_paged(cache: Int4Cache, k: torch.Tensor, v: torch.Tensor,
                      slot_mapping: torch.Tensor, stream=None) -> None:
     """Rotate + quantize + scatter new tokens (k, v: [T][Hkv][D] fp16/bf16)."""
     _append(lib().kvq_append_paged, _need(cache, Int4Cache), k, v, slot_mapping, stream)
+
+
+def kvq_append_paged_int4_search(cache: Int4Cache, k: torch.Tensor, v: torch.Tensor,
+                                 slot_mapping: torch.Tensor, stream=None) -> None:
+    """kvq_append_paged with the scale search for the keys."""
+    _append(lib().kvq_append_paged_int4_search, _need(cache, Int4Cache), k, v, slot_mapping, stream)
+
+
+def kvq_append_paged_int4g_hybrid(cache: Int4GroupedCache, k: torch.Tensor, v: torch.Tensor,
+                                  slot_mapping: torch.Tensor, stream=None) -> None:
+    """Per-group hybrid (symmetric or asymmetric) quantize + scatter into the grouped pool."""
+    _append(lib().kvq_append_paged_int4g_hybrid, _need(cache, Int4GroupedCache), k, v, slot_mapping,
+            stream)
 
 
 def kvq_append_paged_int8(cache: Int8Cache, k: torch.Tensor, v: torch.Tensor,

@@ -254,7 +254,7 @@ kvq_status check_quant_cache(const Cache* cache, Pool kind) {
 template <class Cache>
 kvq_status append_quant(const Cache* cache, Pool kind, const void* k, const void* v, kvq_dtype dtype,
                         int64_t token_stride, const int32_t* slot_mapping, int32_t num_tokens,
-                        void* stream) {
+                        void* stream, int32_t mode = kQuantPlain) {
   kvq_status st = check_quant_cache(cache, kind);
   if (st != KVQ_OK) return st;
   st = check_append(cache->pool, k, v, dtype, token_stride, slot_mapping, num_tokens,
@@ -273,6 +273,7 @@ kvq_status append_quant(const Cache* cache, Pool kind, const void* k, const void
   a.block = cache->hadamard_block;
   a.in_bf16 = dtype == KVQ_BF16;
   a.group = group_of(cache);
+  a.mode = mode;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = kind == Pool::kInt8    ? launch_append_int8(a, s)
                        : kind == Pool::kInt4g ? launch_append_int4g(a, s)
@@ -309,6 +310,13 @@ kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const vo
   return append_quant(cache, Pool::kInt4, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
 }
 
+kvq_status kvq_append_paged_int4_search(const kvq_int4_cache* cache, const void* k, const void* v,
+                                        kvq_dtype dtype, int64_t token_stride,
+                                        const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
+  return append_quant(cache, Pool::kInt4, k, v, dtype, token_stride, slot_mapping, num_tokens, stream,
+                      kQuantKeySearch);
+}
+
 kvq_status kvq_append_paged_int8(const kvq_int8_cache* cache, const void* k, const void* v,
                                  kvq_dtype dtype, int64_t token_stride,
                                  const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
@@ -325,6 +333,13 @@ kvq_status kvq_append_paged_int4g(const kvq_int4g_cache* cache, const void* k, c
                                   kvq_dtype dtype, int64_t token_stride,
                                   const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
   return append_quant(cache, Pool::kInt4g, k, v, dtype, token_stride, slot_mapping, num_tokens, stream);
+}
+
+kvq_status kvq_append_paged_int4g_hybrid(const kvq_int4g_cache* cache, const void* k, const void* v,
+                                         kvq_dtype dtype, int64_t token_stride,
+                                         const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
+  return append_quant(cache, Pool::kInt4g, k, v, dtype, token_stride, slot_mapping, num_tokens, stream,
+                      kQuantHybrid);
 }
 
 kvq_status kvq_append_paged_bf16(const kvq_bf16_cache* cache, const void* k, const void* v,

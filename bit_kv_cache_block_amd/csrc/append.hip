@@ -112,12 +112,54 @@ __device__ __forceinline__ uint32_t tok_code(float x, float sb, float zf, float 
   return f2u(__builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388608.0f + kTop));
 }
 
-template <int D, int BLK, bool BF16, int BITS, int GS, bool MX>
-__global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(4)))
+// Squared reconstruction error of elements x[k0 .. k0 + n) under the 4-bit
+// quantizer (zf, inv) with scale sf (as a positive fp32), measured on the
+// integer grid 2^-ks: the code of tok_code, decoded as code * sf + zf (the
+// product is exact, so one fma rounds like the add), the error y - decoded
+// rounded once (with a power-of-two normalisation folded in, fma(x, sb, -dec)
+// is exact(x * sb) - dec rounded once: equal to rounding y - dec, since a
+// nonzero decoded value is a multiple of 2^-24 and a product that could lose
+// bits is below 2^-126), scaled by 2^ks, rounded to an integer and squared;
+// the squares are summed exactly in 64 bits, so the lanes' partial sums
+// combine in any order.  The criterion of the scale search and of the hybrid
+// mode.
+template <bool EXACT_NORM>
+__device__ __forceinline__ int64_t grid_sse(const float* x, int k0, int n, float sb, float zf, float inv,
+                                            float sf, int ks) {
+  int64_t acc = 0;
+  for (int k = k0; k < k0 + n; ++k) {
+    const float cf = u2f(tok_code<4, EXACT_NORM>(x[k], sb, zf, inv)) - 8388608.0f;   // the code, exact
+    const float dec = __builtin_fmaf(cf, sf, zf);
+    const float err = EXACT_NORM ? __builtin_fmaf(x[k], sb, -dec) : x[k] - dec;
+    const int32_t e = static_cast<int32_t>(__builtin_rintf(ldexpf(err, ks)));
+    acc += static_cast<int64_t>(e) * e;
+  }
+  return acc;
+}
+
+// The grid exponent ks = 20 - ex with amax < 2^ex: every error stays below
+// 2^21 grid steps.
+__device__ __forceinline__ int grid_exponent(float amax) {
+  int ex = 0;
+  frexpf(amax, &ex);
+  return 20 - ex;
+}
+
+// QM: the quantizer mode (kQuantPlain, kQuantKeySearch: the key vectors of
+// the token-wise INT4 pool take the scale search; kQuantHybrid: every group
+// of the grouped INT4 pool picks its symmetric or asymmetric form).  The two
+// searching modes hold their candidates' error sums beside the unit's 64
+// elements per lane, so they are built for 2 waves per SIMD (256 VGPRs)
+// rather than 4.
+template <int D, int BLK, bool BF16, int BITS, int GS, bool MX, int QM = kQuantPlain>
+__global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(QM == kQuantPlain ? 4 : 2)))
 void append_quant_kernel(AppendArgs a) {
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
   static_assert(GS == 0 || (BITS == 4 && (GS == 32 || GS == 64) && GS <= D), "groups of 32 or 64 channels, 4-bit");
   static_assert(!MX || (BITS == 4 && GS == 32), "MXFP4: 4-bit codes in blocks of 32");
+  static_assert(QM == kQuantPlain || (QM == kQuantKeySearch && BITS == 4 && GS == 0 && !MX) ||
+                    (QM == kQuantHybrid && BITS == 4 && GS != 0 && !MX),
+                "scale search: token-wise INT4; hybrid: grouped INT4");
   constexpr int kLPV = D / kLaneElems;   // lanes per vector
   constexpr int kTok = 64 / kLPV;        // tokens per unit
   constexpr int kChunks = D / 8;         // 16-byte pieces per row
@@ -336,6 +378,58 @@ void append_quant_kernel(AppendArgs a) {
       zf[gl] = qp.zf;
       inv[gl] = qp.inv;
       pend.meta[gl] = qp.meta;
+      if constexpr (QM == kQuantHybrid) {
+        // The symmetric candidate: scale fp16(amax / 7), zero -8 * scale
+        // (exact in fp16), so that 0 is the level of code 8; it is kept when
+        // its grid error is not larger than the asymmetric one's (a group of
+        // zeros, a zero symmetric scale or a zero point beyond fp16 stay
+        // asymmetric), and marked by the sign bit of the stored scale.
+        const float amax = fmaxf(fabsf(mn[gl]), fabsf(mx[gl]));
+        const _Float16 ss = static_cast<_Float16>(amax / 7.0f);
+        const float sfs = static_cast<float>(ss);
+        const float zs = -8.0f * sfs;
+        if (amax > 0.0f && sfs != 0.0f && fabsf(zs) <= 65504.0f) {
+          const float inv_s = 1.0f / sfs;
+          const int ks = grid_exponent(amax);
+          const float sf_a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(qp.meta & 0xFFFFu)));
+          const int64_t e_s = grid_sse<kExactNorm>(x, gl * kGE, kGE, sb, zs, inv_s, sfs, ks);
+          const int64_t e_a = grid_sse<kExactNorm>(x, gl * kGE, kGE, sb, qp.zf, qp.inv, sf_a, ks);
+          if (e_s <= e_a) {
+            zf[gl] = zs;
+            inv[gl] = inv_s;
+            pend.meta[gl] = (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ss)) | 0x8000u) |
+                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(zs))) << 16);
+          }
+        }
+      }
+    }
+    if constexpr (QM == kQuantKeySearch) {
+      if (kind == 0) {
+        // Keys: the range [mn, mx] shrunk toward zero by alpha_j = (16 - j)
+        // / 16, j = 0 .. 7; the candidate with the smallest grid error over
+        // the whole vector (the two lanes' partial sums added) wins, the
+        // smaller j on a tie.  Candidate 0 is the plain quantizer.
+        const float amax = fmaxf(fabsf(mn[0]), fabsf(mx[0]));
+        const int ks = grid_exponent(amax);
+        int64_t best = 0;
+#pragma unroll 1
+        for (int j = 0; j < 8; ++j) {
+          const float alpha = static_cast<float>(16 - j) / 16.0f;
+          const QParams qc = tok_params<4>(mn[0] * alpha, mx[0] * alpha);
+          const float sfc = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(qc.meta & 0xFFFFu)));
+          int64_t e = grid_sse<kExactNorm>(x, 0, kLaneElems, sb, qc.zf, qc.inv, sfc, ks);
+          if constexpr (kLPV == 2) {
+            const uint32_t lo = static_cast<uint32_t>(e), hi = static_cast<uint32_t>(e >> 32);
+            e += static_cast<int64_t>((static_cast<uint64_t>(dpp_u<kDppXor1>(hi)) << 32) | dpp_u<kDppXor1>(lo));
+          }
+          if (j == 0 || e < best) {
+            best = e;
+            zf[0] = qc.zf;
+            inv[0] = qc.inv;
+            pend.meta[0] = qc.meta;
+          }
+        }
+      }
     }
 
     // codes (tok_code; MXFP4: E2M1 of y / 2^X)
@@ -533,9 +627,9 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
 // Appends of at most this many tokens (decode steps) use the few-token kernel.
 constexpr int kSmallTokens = 1024;
 
-template <int D, int BLK, int BITS, int GS, bool MX = false>
+template <int D, int BLK, int BITS, int GS, bool MX = false, int QM = kQuantPlain>
 hipError_t launch_quant_d(const AppendArgs& a, hipStream_t s) {
-  if constexpr (GS == 0 && !MX) {
+  if constexpr (GS == 0 && !MX && QM == kQuantPlain) {
     if (a.num_tokens <= kSmallTokens) {
       constexpr int kVecPerBlock = 4 * (64 / (D / 8));
       const int64_t nvec = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * 2;
@@ -552,21 +646,21 @@ hipError_t launch_quant_d(const AppendArgs& a, hipStream_t s) {
   const int64_t blocks = (units + kAppendThreads / 64 - 1) / (kAppendThreads / 64);
   const dim3 grid(static_cast<unsigned>(blocks < kResidentBlocks ? blocks : kResidentBlocks));
   if (a.in_bf16)
-    append_quant_kernel<D, BLK, true, BITS, GS, MX><<<grid, kAppendThreads, 0, s>>>(a);
+    append_quant_kernel<D, BLK, true, BITS, GS, MX, QM><<<grid, kAppendThreads, 0, s>>>(a);
   else
-    append_quant_kernel<D, BLK, false, BITS, GS, MX><<<grid, kAppendThreads, 0, s>>>(a);
+    append_quant_kernel<D, BLK, false, BITS, GS, MX, QM><<<grid, kAppendThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int D, int BITS, int GS, bool MX = false>
+template <int D, int BITS, int GS, bool MX = false, int QM = kQuantPlain>
 hipError_t launch_quant_block(const AppendArgs& a, hipStream_t s) {
   switch (a.block) {
-    case 0: return launch_quant_d<D, 0, BITS, GS, MX>(a, s);
-    case 16: return launch_quant_d<D, 16, BITS, GS, MX>(a, s);
-    case 32: return launch_quant_d<D, 32, BITS, GS, MX>(a, s);
-    case 64: return launch_quant_d<D, 64, BITS, GS, MX>(a, s);
+    case 0: return launch_quant_d<D, 0, BITS, GS, MX, QM>(a, s);
+    case 16: return launch_quant_d<D, 16, BITS, GS, MX, QM>(a, s);
+    case 32: return launch_quant_d<D, 32, BITS, GS, MX, QM>(a, s);
+    case 64: return launch_quant_d<D, 64, BITS, GS, MX, QM>(a, s);
     case 128:
-      if constexpr (D == 128) return launch_quant_d<D, 128, BITS, GS, MX>(a, s);
+      if constexpr (D == 128) return launch_quant_d<D, 128, BITS, GS, MX, QM>(a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -576,11 +670,21 @@ hipError_t launch_quant_block(const AppendArgs& a, hipStream_t s) {
 
 hipError_t launch_append_int4(const AppendArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
+  if (a.mode == kQuantKeySearch)
+    return a.head_dim == 128 ? launch_quant_block<128, 4, 0, false, kQuantKeySearch>(a, s)
+                             : launch_quant_block<64, 4, 0, false, kQuantKeySearch>(a, s);
   return a.head_dim == 128 ? launch_quant_block<128, 4, 0>(a, s) : launch_quant_block<64, 4, 0>(a, s);
 }
 
 hipError_t launch_append_int4g(const AppendArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
+  if (a.mode == kQuantHybrid) {
+    if (a.head_dim == 128)
+      return a.group == 32 ? launch_quant_block<128, 4, 32, false, kQuantHybrid>(a, s)
+                           : launch_quant_block<128, 4, 64, false, kQuantHybrid>(a, s);
+    return a.group == 32 ? launch_quant_block<64, 4, 32, false, kQuantHybrid>(a, s)
+                         : launch_quant_block<64, 4, 64, false, kQuantHybrid>(a, s);
+  }
   if (a.head_dim == 128)
     return a.group == 32 ? launch_quant_block<128, 4, 32>(a, s) : launch_quant_block<128, 4, 64>(a, s);
   return a.group == 32 ? launch_quant_block<64, 4, 32>(a, s) : launch_quant_block<64, 4, 64>(a, s);

@@ -36,6 +36,14 @@ __device__ __forceinline__ int pv_channel(int n, int tau) {
   }
 }
 
+// Scale of a sidecar word (the low fp16).  In the grouped pool the sign bit
+// marks a group of the hybrid quantizer's symmetric form, so the magnitude is
+// taken there (for free: an input modifier of the instruction that uses it).
+template <int GS>
+__device__ __forceinline__ float side_scale(uint32_t w) {
+  return GS ? fabsf(half_lo(w)) : half_lo(w);
+}
+
 template <int D, int NS, int NG>
 struct alignas(16) Smem {
   static constexpr int kGP = 4 * NS;
@@ -378,7 +386,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
           // limbs: c0 * 2^16 + c1 * 2^8 + c2 (c0 * 2^8 + c1 is exact in int32)
           const float tq = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f,
                                           static_cast<float>(c[2]));
-          const float l2 = qA[st] * __builtin_fmaf(kzero, qS[st][0], half_lo(km) * tq);
+          const float l2 = qA[st] * __builtin_fmaf(kzero, qS[st][0], side_scale<GS>(km) * tq);
           lg[st][i] = ok ? l2 : kNegInf;
         }
         continue;
@@ -396,8 +404,8 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
           // zero point of the codes as the MFMA sees them
           const uint32_t km = sb.km[i][gi];
           const float kzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(km), half_hi(km)) : half_hi(km);
-          dot = gi == 0 ? __builtin_fmaf(kzero, qS[st][0], half_lo(km) * tq)
-                        : dot + __builtin_fmaf(kzero, qS[st][gi], half_lo(km) * tq);
+          dot = gi == 0 ? __builtin_fmaf(kzero, qS[st][0], side_scale<GS>(km) * tq)
+                        : dot + __builtin_fmaf(kzero, qS[st][gi], side_scale<GS>(km) * tq);
         }
         lg[st][i] = ok ? qA[st] * dot : kNegInf;
       }
@@ -452,10 +460,10 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
           if (tail) {
             const bool ok = lg[st][i] != kNegInf;
             zsum += ok ? pp * vzero : 0.0f;
-            w[i] = ok ? pp * half_lo(vm) : 0.0f;
+            w[i] = ok ? pp * side_scale<GS>(vm) : 0.0f;
           } else {
             zsum = __builtin_fmaf(pp, vzero, zsum);
-            w[i] = pp * half_lo(vm);
+            w[i] = pp * side_scale<GS>(vm);
           }
           wmax = fmaxf(wmax, w[i]);
         }
@@ -481,10 +489,10 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
           if (tail) {
             const bool ok = lg[st][i] != kNegInf;
             zsum += ok ? pp[i] * vzero : 0.0f;
-            w[i] = ok ? pp[i] * half_lo(vm) : 0.0f;
+            w[i] = ok ? pp[i] * side_scale<GS>(vm) : 0.0f;
           } else {
             zsum = __builtin_fmaf(pp[i], vzero, zsum);
-            w[i] = pp[i] * half_lo(vm);
+            w[i] = pp[i] * side_scale<GS>(vm);
           }
           wmax = fmaxf(wmax, w[i]);
         }

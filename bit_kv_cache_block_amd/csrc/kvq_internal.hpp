@@ -26,7 +26,15 @@ struct AppendArgs {
   int32_t block;             // Hadamard block (0 = none); unused by the bf16 pool
   int32_t in_bf16;           // 1: inputs are bf16, 0: fp16
   int32_t group;             // channels per scale/zero pair (grouped INT4 pool only)
+  int32_t mode;              // quantizer: kQuantPlain, kQuantKeySearch or kQuantHybrid
 };
+
+// Quantizer modes of the 4-bit appends: the plain token-wise (or per-group)
+// asymmetric quantizer; the scale search for keys (token-wise pool); the
+// hybrid symmetric/asymmetric choice per group (grouped pool).
+constexpr int kQuantPlain = 0;
+constexpr int kQuantKeySearch = 1;
+constexpr int kQuantHybrid = 2;
 
 struct DecodeArgs {
   const uint8_t* pool;

@@ -55,7 +55,9 @@
  *                        nibble j (j even: bits 0..3).
  *     [P*D, +4P*D/g)     K sidecar: token t, group i -> fp16 scale at byte
  *                        4 (t*(D/g) + i), fp16 zero 2 bytes later.
- *     then the V sidecar in the same form.
+ *     then the V sidecar in the same form.  A set sign bit of a scale marks a
+ *     group written in the symmetric form (kvq_append_paged_int4g_hybrid); a
+ *     decoded element is code * |scale| + zero in either form.
  *
  * MXFP4 page pool layout: [num_pages][num_kv_heads][slab], slab = P * (D + D/16)
  *   bytes (2176 at D = 128):
@@ -285,6 +287,29 @@ size_t kvq_decode_windowed_workspace_bytes(int32_t batch, int32_t num_q_heads, i
                                            int32_t head_dim, int32_t max_seq_len, int32_t num_splits);
 
 /*
+ * kvq_append_paged_int4_search -- kvq_append_paged with a scale search for
+ * the keys ("BitDecoding-FP4", Abstract: outlier-aware key quantization
+ * combines Hadamard rotation with a scale search under token-wise scaling).
+ * After the rotation, each key vector's range [min y, max y] is shrunk
+ * toward zero by alpha_j = (16 - j) / 16, j = 0 .. 7 (each end multiplied by
+ * alpha_j in fp32), the token-wise quantizer of kvq_append_paged is applied
+ * with each candidate range (elements outside it are clamped by the codes'
+ * clamp), and the candidate with the smallest squared reconstruction error
+ * is stored, the smaller j on a tie (j = 0 is kvq_append_paged's result).
+ * The error is measured exactly on an integer grid: each element decoded as
+ * code * scale + zero in fp32 (product exact, sum rounded once), its error
+ * y - decoded rounded once, scaled by 2^(20 - ex) with max |y| < 2^ex,
+ * rounded to an integer (ties to even), squared and summed in 64 bits.
+ * Values are quantized as in kvq_append_paged.  The pool is the INT4 pool,
+ * read by kvq_decode_attn; codes and sidecars are bit-exact functions of
+ * the input.  Same arguments and rules as kvq_append_paged (about eight
+ * quantizer passes per key vector: for caches whose keys carry outliers).
+ */
+kvq_status kvq_append_paged_int4_search(const kvq_int4_cache* cache, const void* k, const void* v,
+                                        kvq_dtype dtype, int64_t token_stride,
+                                        const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/*
  * Token-wise INT8 variant ("GPU-Accelerated INT8 Quantization for KV Cache
  * Compression in Large Language Models", Abstract: 8-bit KV codes), twice
  * the bytes of INT4 per token.  The quantizer is kvq_append_paged's with 255
@@ -323,6 +348,25 @@ kvq_status kvq_decode_attn_int4g(const kvq_int4g_cache* cache, const void* q, kv
                                  int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
                                  int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_append_paged_int4g_hybrid -- kvq_append_paged_int4g with the hybrid
+ * quantizer ("InnerQ", Abstract and Figure 3: symmetric or asymmetric
+ * quantization chosen for each group from the group's own statistics).  For
+ * each group two candidates: the asymmetric one of kvq_append_paged_int4g,
+ * and the symmetric one with scale = fp16(max |y| / 7) and zero = -8 * scale
+ * (exact in fp16), whose levels (code - 8) * scale hold 0.  The symmetric one
+ * is kept when its squared reconstruction error, measured on the integer
+ * grid of kvq_append_paged_int4_search, is not larger; its scale is then
+ * stored with the sign bit set.  A group of zeros, or one whose symmetric
+ * scale is 0 in fp16 or whose -8 * scale is beyond fp16, stays asymmetric.
+ * Read by kvq_decode_attn_int4g (which takes |scale|); codes and sidecars are
+ * bit-exact functions of the input.  Same arguments and rules as
+ * kvq_append_paged_int4g.
+ */
+kvq_status kvq_append_paged_int4g_hybrid(const kvq_int4g_cache* cache, const void* k, const void* v,
+                                         kvq_dtype dtype, int64_t token_stride,
+                                         const int32_t* slot_mapping, int32_t num_tokens, void* stream);
 
 /*
  * MXFP4 variant ("BitDecoding-FP4", Abstract: an FP4 KV cache with Hadamard

@@ -342,7 +342,7 @@ def test_full_size_llama_layer_sampled():
     gpool = cache.pool.cpu().numpy()
     for b in sample:
         for pg in w.block_table[b][w.block_table[b] >= 0]:
-            assert np.array_equal(gpool[pg], pool[pg * slab:(pg + 1) * slab]), f"page {pg}"
+            assert np.array_equal(gpool[pg], pool[int(pg) * slab:(int(pg) + 1) * slab]), f"page {pg}"
     mask = np.zeros((w.batch, w.hq), np.uint8)
     mask[sample] = 1
     want = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table,
@@ -438,7 +438,9 @@ def _check_sampled(kind, cache, out, w, pool, sample, block_table, label):
     for b in sample:
         pages = block_table[b][block_table[b] >= 0]
         got = cache.pool[torch.from_numpy(pages.astype(np.int64)).to(DEV)].cpu().numpy().reshape(-1)
-        want = np.concatenate([pool[pg * slab:(pg + 1) * slab] for pg in pages])
+        # (page ids as Python ints: a numpy int32 id times the slab size
+        # overflows for the bf16 pools)
+        want = np.concatenate([pool[int(pg) * slab:(int(pg) + 1) * slab] for pg in pages])
         assert np.array_equal(got, want), f"{label}: seq {b} pages differ"
     mask = np.zeros((w.batch, w.hq), np.uint8)
     mask[sample] = 1

@@ -185,7 +185,7 @@ def test_int8_full_size_llama_layer_sampled():
     gpool = cache.pool.cpu().numpy()
     for b in sample:
         for pg in w.block_table[b][w.block_table[b] >= 0]:
-            assert np.array_equal(gpool[pg], pool[pg * slab:(pg + 1) * slab]), f"page {pg}"
+            assert np.array_equal(gpool[pg], pool[int(pg) * slab:(int(pg) + 1) * slab]), f"page {pg}"
     mask = np.zeros((w.batch, w.hq), np.uint8)
     mask[sample] = 1
     want = oracle_attn(pool, w, 64, mask=mask)
