@@ -33,7 +33,7 @@ PAGE_SIZE = 16
 EXPORTED = (
     "kvq_int4_page_bytes", "kvq_int8_page_bytes", "kvq_int4g_page_bytes", "kvq_bf16_page_bytes",
     "kvq_append_paged", "kvq_decode_attn", "kvq_append_paged_int8", "kvq_decode_attn_int8",
-    "kvq_append_paged_int4_search", "kvq_append_paged_int4g_hybrid",
+    "kvq_append_paged_int4_search", "kvq_append_paged_int4g_hybrid", "kvq_decode_attn_noalloc",
     "kvq_append_paged_int4g", "kvq_decode_attn_int4g", "kvq_mxfp4_page_bytes",
     "kvq_append_paged_mxfp4", "kvq_decode_attn_mxfp4",
     "kvq_decode_workspace_bytes", "kvq_append_paged_bf16", "kvq_decode_attn_bf16",
@@ -105,6 +105,8 @@ def lib() -> C.CDLL:
         dec = [p, i32, i32, p, i32, p, i32, i32, C.c_float, i32, p, p, sz, p]
         L.kvq_decode_attn.argtypes = [C.POINTER(_QuantDesc), *dec]
         L.kvq_decode_attn.restype = i32
+        L.kvq_decode_attn_noalloc.argtypes = [C.POINTER(_QuantDesc), *dec[:11], p]
+        L.kvq_decode_attn_noalloc.restype = i32
         L.kvq_decode_attn_int8.argtypes = [C.POINTER(_QuantDesc), *dec]
         L.kvq_decode_attn_int8.restype = i32
         L.kvq_decode_attn_mxfp4.argtypes = [C.POINTER(_QuantDesc), *dec]
@@ -404,6 +406,29 @@ def kvq_decode_attn(cache: Int4Cache, q: torch.Tensor, block_table: torch.Tensor
     """Paged decode attention over the INT4 cache; returns fp32 [B][Hq][D]."""
     return _decode(lib().kvq_decode_attn, _need(cache, Int4Cache), q, block_table, seq_lens, max_seq_len,
                    sm_scale, out, workspace, num_splits, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
+
+
+def kvq_decode_attn_noalloc(cache: Int4Cache, q: torch.Tensor, block_table: torch.Tensor,
+                            seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float | None = None,
+                            out: torch.Tensor | None = None, num_splits: int = 0,
+                            stream=None) -> torch.Tensor:
+    """kvq_decode_attn with the split-K partials in the library's static
+    device scratch (no workspace); pass ``out`` and nothing is allocated."""
+    cache = _need(cache, Int4Cache)
+    batch, hq = _decode_args(cache, q, block_table, seq_lens, out)
+    d = cache.head_dim
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().kvq_decode_attn_noalloc(
+        C.byref(cache.desc()), _ptr(q), _dtype_code(q), hq, _ptr(block_table), int(block_table.shape[1]),
+        _ptr(seq_lens), batch, int(max_seq_len), float(sm_scale), int(num_splits), _ptr(out),
+        _stream(stream, q.device)))
+    return out
 
 
 def kvq_decode_attn_int8(cache: Int8Cache, q: torch.Tensor, block_table: torch.Tensor,

@@ -9,9 +9,16 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kvq_internal.hpp"
+
+// Split-K scratch of kvq_decode_attn_noalloc: a static device array, one copy
+// on each GPU the library runs on, held until the process ends.  Host code
+// never passes this name as an address (on the host it is only a stand-in);
+// each device's address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
 
 namespace kvq {
 
@@ -186,6 +193,27 @@ kvq_status launch_decode(Pool kind, const void* pool, int32_t num_pages, int32_t
   if (e == hipSuccess && plan.nsplit > 1) e = launch_reduce(a, s);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;
+}
+
+// The address of this device's copy of `scratch`, looked up once per device
+// with that device current (the caller's), then kept.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+hipError_t scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
 }
 
 }  // namespace
@@ -375,6 +403,32 @@ kvq_status kvq_decode_attn(const kvq_int4_cache* cache, const void* q, kvq_dtype
   return decode_quant(cache, Pool::kInt4, q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                       batch, max_seq_len, sm_scale, num_splits, out, workspace,
                       workspace_bytes_given, stream);
+}
+
+kvq_status kvq_decode_attn_noalloc(const kvq_int4_cache* cache, const void* q, kvq_dtype dtype,
+                                   int32_t num_q_heads, const int32_t* block_table,
+                                   int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                   int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                                   void* stream) {
+  kvq_status st = check_quant_cache(cache, Pool::kInt4);
+  if (st != KVQ_OK) return st;
+  st = check_decode(cache->pool, q, dtype, num_q_heads, cache->num_kv_heads, block_table,
+                    max_pages_per_seq, seq_lens, batch, max_seq_len, sm_scale, num_splits, out);
+  if (st != KVQ_OK || batch == 0) return st;
+  const SplitPlan plan = plan_splits(batch, cache->num_kv_heads, max_seq_len, num_splits);
+  const size_t need = workspace_bytes(batch, num_q_heads, cache->head_dim, plan);
+  if (need > KVQ_NOALLOC_SCRATCH_BYTES)
+    return fail(KVQ_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of split-K scratch; the static scratch holds %zu "
+                "(use kvq_decode_attn with a workspace, or fewer splits)",
+                need, static_cast<size_t>(KVQ_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_of_current_device(&ws);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(e));
+  }
+  return decode_quant(cache, Pool::kInt4, q, dtype, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                      batch, max_seq_len, sm_scale, num_splits, out, ws, need, stream);
 }
 
 kvq_status kvq_decode_attn_int8(const kvq_int8_cache* cache, const void* q, kvq_dtype dtype,

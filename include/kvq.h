@@ -92,6 +92,9 @@ extern "C" {
 
 #define KVQ_ABI_VERSION 1
 
+/* Bytes of the static device scratch of kvq_decode_attn_noalloc (64 MiB). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
 typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad size, misalignment       */
@@ -235,6 +238,27 @@ kvq_status kvq_decode_attn(const kvq_int4_cache* cache, const void* q, kvq_dtype
                            int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
                            int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_decode_attn_noalloc -- kvq_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and accuracy
+ * as kvq_decode_attn without the workspace: the split-K partials go to a
+ * static device array of KVQ_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends (its address is looked up on
+ * the first call on each device, with that device current).  The call
+ * allocates nothing.  A call whose split plan needs more scratch than that
+ * (kvq_decode_workspace_bytes of the same arguments) returns
+ * KVQ_ERR_WORKSPACE_TOO_SMALL before anything is launched.  Every call on a
+ * GPU shares that GPU's scratch and the partials of one call are read only
+ * by that call, so nothing needs clearing between calls; calls that overlap
+ * on one GPU (other streams, other threads) race on it.
+ */
+kvq_status kvq_decode_attn_noalloc(const kvq_int4_cache* cache, const void* q, kvq_dtype dtype,
+                                   int32_t num_q_heads, const int32_t* block_table,
+                                   int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                   int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
+                                   void* stream);
 
 /* Workspace bytes kvq_decode_attn / kvq_decode_attn_bf16 need (0 allowed). */
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
