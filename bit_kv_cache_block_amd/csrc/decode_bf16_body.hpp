@@ -243,13 +243,13 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeArgs& a, uint32_t w
       mc = row_max16(mc);
       const float mnew = fmaxf(m_run[st], mc);
       const float muse = mnew == kNegInf ? 0.0f : mnew;
-      alpha[st] = exp2f(m_run[st] - muse);
+      alpha[st] = fast_exp2(m_run[st] - muse);
       m_run[st] = mnew;
       float psum = 0.0f;
       uint16_t* pl = &sm.pl[wave][st][0][0][0][0];
 #pragma unroll
       for (int i = 0; i < kStep; ++i) {
-        const float pp = exp2f(lg[st][i] - muse);
+        const float pp = fast_exp2(lg[st][i] - muse);
         psum += pp;
         const uint16_t h = bf16_bits(pp);
         const float r1 = pp - bf16_val(h);
@@ -318,7 +318,7 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeArgs& a, uint32_t w
     float lsum = 0.0f, osum = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = exp2f(sm.u.merge.m[w][j] - muse);
+      const float f = fast_exp2(sm.u.merge.m[w][j] - muse);
       lsum = __builtin_fmaf(sm.u.merge.l[w][j], f, lsum);
       osum = __builtin_fmaf(sm.u.merge.acc[w][j][c], f, osum);
     }

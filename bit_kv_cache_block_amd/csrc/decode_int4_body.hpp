@@ -95,6 +95,11 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   constexpr int kOps = D / 64;         // QK MFMAs per page and head group
   constexpr int kGP = 4 * NS;          // padded heads per KV head
   constexpr int kC = D / 16;           // channels per lane when a row of 16 lanes holds a vector
+  // head_dim 128: the QK operand is built once, by the query waves, into an
+  // LDS image of NS * kOps * 64 lanes * 16 bytes (the size of the query
+  // scratch it replaces) that every wave then reads
+  constexpr bool kOpImage = D == 128;
+  static_assert(!kOpImage || NS * kOps * 64 * 16 == sizeof(int32_t) * 4 * NS * D, "operand image size");
   __shared__ Smem<D, NS, kNG> sm;
 
   const int tid = threadIdx.x;
@@ -283,9 +288,40 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
       qi[k] = static_cast<int32_t>(rintf(v[k] * sc));
       sum += qi[k];
     }
+    if constexpr (kOpImage) {
+      // This lane's words of the QK operand image (see below): limb L of a
+      // channel is byte 2 (L = 0), or byte 1 / 0 with the top bit flipped
+      // (L = 1, 2), of qi + 0x8080 (the balanced limbs of LimbSel); a word
+      // holds one limb of four channels; limb 3 is the zero pad row.
+      uint32_t y[kC];
 #pragma unroll
-    for (int k = 0; k < kC; k += 4)
-      *reinterpret_cast<v4i*>(&sm.u.qi[qhead][kC * n + k]) = v4i{qi[k], qi[k + 1], qi[k + 2], qi[k + 3]};
+      for (int k = 0; k < kC; ++k) y[k] = static_cast<uint32_t>(qi[k] + 0x8080);
+      auto word = [&](int c0, int c1, int c2, int c3, int L) -> uint32_t {
+        if (L == 3) return 0u;
+        const uint32_t sel = L == 0 ? 0x0c0c0602u : (L == 1 ? 0x0c0c0501u : 0x0c0c0400u);
+        const uint32_t lo = __builtin_amdgcn_perm(y[c1], y[c0], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(y[c3], y[c2], sel);
+        return __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ (L == 0 ? 0u : 0x80808080u);
+      };
+      uint32_t* img = reinterpret_cast<uint32_t*>(&sm.u.qi[0][0]);
+      const int lane0 = 16 * (n >> 2) + 4 * g;   // reader lanes: row (head g, limb L), group n / 4
+#pragma unroll
+      for (int L = 0; L < 4; ++L) {
+        if constexpr (BITS == 4) {   // op o: channels o, o+2, o+4, o+6 of the lane, dword n % 4
+#pragma unroll
+          for (int op = 0; op < kOps; ++op)
+            img[((wave * kOps + op) * 64 + lane0 + L) * 4 + (n & 3)] = word(op, op + 2, op + 4, op + 6, L);
+        } else {                     // op (n/2) % 2: channels 0..3 and 4..7 as dwords 2 (n%2) + {0, 1}
+          const int op = (n >> 1) & 1, i0 = 2 * (n & 1);
+          img[((wave * kOps + op) * 64 + lane0 + L) * 4 + i0] = word(0, 1, 2, 3, L);
+          img[((wave * kOps + op) * 64 + lane0 + L) * 4 + i0 + 1] = word(4, 5, 6, 7, L);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kC; k += 4)
+        *reinterpret_cast<v4i*>(&sm.u.qi[qhead][kC * n + k]) = v4i{qi[k], qi[k + 1], qi[k + 2], qi[k + 3]};
+    }
     // sum of the query over each group (|sum| <= D * 2^22: exact in int32);
     // a lane's kC channels lie in group kC n / GS
     int32_t gsum[kNG];
@@ -299,8 +335,10 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   }
   __syncthreads();
 
-  // A operand of QK: row (head hs, limb lam), k-slots of lane group g: the
-  // lane's D/4 consecutive channels, read from LDS as whole vectors
+  // A operand of QK: row (head hs, limb lam), k-slots of lane group g.  At
+  // head_dim 128 the query waves wrote every lane's operand words into an
+  // LDS image, so each wave reads one 16-byte vector per set and product;
+  // at 64 each wave builds them from the fixed-point query.
   const LimbSel limb(lam);
   v4i aq[NS][kNG][kOps];   // per group: the operand with other groups' channels zeroed
   float qA[NS], qS[NS][kNG];
@@ -309,6 +347,16 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
     qA[st] = sm.hA[4 * st + g];          // C-layout head of this lane: row group g
 #pragma unroll
     for (int gi = 0; gi < kNG; ++gi) qS[st][gi] = sm.hS[4 * st + g][gi];
+    if constexpr (kOpImage) {
+      const v4i* img = reinterpret_cast<const v4i*>(&sm.u.qi[0][0]);
+#pragma unroll
+      for (int op = 0; op < kOps; ++op) {
+        const v4i vv = img[(st * kOps + op) * 64 + lane];
+#pragma unroll
+        for (int gi = 0; gi < kNG; ++gi) aq[st][gi][op] = (kNG == 1 || (D / 4) * g / (GS ? GS : D) == gi) ? vv : v4i{0, 0, 0, 0};
+      }
+      continue;
+    }
     int32_t qc[D / 4];
     const v4i* src = reinterpret_cast<const v4i*>(&sm.u.qi[4 * st + hs][(D / 4) * g]);
 #pragma unroll
@@ -447,13 +495,13 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
       mc = row_max16(mc);
       const float mnew = fmaxf(m_run[st], mc);
       const float muse = mnew == kNegInf ? 0.0f : mnew;
-      alpha[st] = exp2f(m_run[st] - muse);
+      alpha[st] = fast_exp2(m_run[st] - muse);
       m_run[st] = mnew;
       if constexpr (kOnePass) {   // one scale/zero per vector: a single pass over the step
         float psum = 0.0f, zsum = 0.0f, wmax = 0.0f, w[kStep];
 #pragma unroll
         for (int i = 0; i < kStep; ++i) {
-          const float pp = exp2f(lg[st][i] - muse);
+          const float pp = fast_exp2(lg[st][i] - muse);
           psum += pp;
           const uint32_t vm = sb.vm[i][0];
           const float vzero = BITS == 8 ? __builtin_fmaf(128.0f, half_lo(vm), half_hi(vm)) : half_hi(vm);
@@ -475,7 +523,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
       float pp[kStep], psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < kStep; ++i) {
-        pp[i] = exp2f(lg[st][i] - muse);
+        pp[i] = fast_exp2(lg[st][i] - muse);
         psum += pp[i];
       }
       l_run[st] = __builtin_fmaf(l_run[st], alpha[st], psum);
@@ -624,7 +672,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
     float f[kWaves], lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      f[w] = exp2f(sm.u.merge.m[w][j] - muse);
+      f[w] = fast_exp2(sm.u.merge.m[w][j] - muse);
       lsum = __builtin_fmaf(sm.u.merge.l[w][j], f[w], lsum);
     }
     float o[kC];

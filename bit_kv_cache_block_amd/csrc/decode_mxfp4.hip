@@ -278,12 +278,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
       mc = row_max16(mc);
       const float mnew = fmaxf(m_run[st], mc);
       const float muse = mnew == kNegInf ? 0.0f : mnew;
-      alpha[st] = exp2f(m_run[st] - muse);
+      alpha[st] = fast_exp2(m_run[st] - muse);
       m_run[st] = mnew;
       float pp[kStep], psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < kStep; ++i) {
-        pp[i] = tail && lg[st][i] == kNegInf ? 0.0f : exp2f(lg[st][i] - muse);
+        pp[i] = tail && lg[st][i] == kNegInf ? 0.0f : fast_exp2(lg[st][i] - muse);
         psum += pp[i];
       }
       l_run[st] = __builtin_fmaf(l_run[st], alpha[st], psum);
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
     float f[kWaves], lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      f[w] = exp2f(sm.u.merge.m[w][j] - muse);
+      f[w] = fast_exp2(sm.u.merge.m[w][j] - muse);
       lsum = __builtin_fmaf(sm.u.merge.l[w][j], f[w], lsum);
     }
     float o[kC];

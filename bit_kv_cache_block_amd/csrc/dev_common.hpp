@@ -249,6 +249,13 @@ struct LimbSel {
   }
 };
 
+// 2^x with the hardware's v_exp_f32 alone.  exp2f adds a rescaling around it
+// so that results below 2^-126 come out as denormals; the softmax weights and
+// rescale factors here are relative to a running maximum, so such values are
+// below 2^-126 of the weights that matter, and flushing them changes nothing
+// at the accuracy the decode keeps.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // max / sum over the 16 lanes of a row, result in every lane of the row
 __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp_f<kDppXor1>(x));

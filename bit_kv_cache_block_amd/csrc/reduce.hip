@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
                           : hi > lo && max(s * sp, pfirst) < min(npg, (s + 1) * sp);
       const float mn = ok ? fmaxf(m, ms) : m;
       const float mu = mn == -__builtin_inff() ? 0.0f : mn;
-      const float fo = exp2f(m - mu), fs = exp2f(ms - mu);
+      const float fo = fast_exp2(m - mu), fs = fast_exp2(ms - mu);
       l = ok ? __builtin_fmaf(l, fo, ls * fs) : l;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = ok ? __builtin_fmaf(o[i], fo, x[i] * fs) : o[i];
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < G; ++k) {
-      const float f = exp2f(sm_m[r][k] - mu);
+      const float f = fast_exp2(sm_m[r][k] - mu);
       lsum = __builtin_fmaf(sm_l[r][k], f, lsum);
       const v4f y = *reinterpret_cast<const v4f*>(&sm_o[r][k][4 * c]);
 #pragma unroll
