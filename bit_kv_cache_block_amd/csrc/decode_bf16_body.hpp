@@ -108,6 +108,9 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeArgs& a, uint32_t w
     }
     return;
   }
+  // a sequence whose pages all lie in one split is finished here (the split
+  // merge skips its rows); windowed calls always store partials
+  const bool direct = !a.force_partial && (a.nsplit == 1 || (npg - 1) / sp == 0);
 
   const int span = p1 - p0;
   const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
@@ -322,7 +325,7 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeArgs& a, uint32_t w
       lsum = __builtin_fmaf(sm.u.merge.l[w][j], f, lsum);
       osum = __builtin_fmaf(sm.u.merge.acc[w][j][c], f, osum);
     }
-    if (a.nsplit == 1 && !a.force_partial) {
+    if (direct) {
       a.out[(hq0 + j) * D + c] = lsum > 0.0f ? osum / lsum : 0.0f;
     } else {
       const int64_t idx = (hq0 + j) * a.part_stride + a.part_slot0 + s;

@@ -44,17 +44,29 @@ __device__ __forceinline__ float side_scale(uint32_t w) {
   return GS ? fabsf(half_lo(w)) : half_lo(w);
 }
 
-template <int D, int NS, int NG>
+// Bytes of one page in a wave's LDS stage (staged builds): K codes and V
+// codes (16 bytes per lane each, where the lane's own loads would put them)
+// and one 4-byte-per-lane load of the sidecars.
+template <int D>
+constexpr int stage_page_bytes() { return 2 * kPage * (D / 2) + 256; }
+
+// STAGE: the staged build, whose page stage (in flight during the query's
+// prologue) shares its LDS with the merge only, not with the query scratch.
+template <int D, int NS, int NG, bool STAGE>
 struct alignas(16) Smem {
   static constexpr int kGP = 4 * NS;
+  struct Merge {
+    float acc[kWaves][kGP][D];
+    float m[kWaves][kGP];
+    float l[kWaves][kGP];
+  };
   union {
-    int32_t qi[kGP][D];
-    struct {
-      float acc[kWaves][kGP][D];
-      float m[kWaves][kGP];
-      float l[kWaves][kGP];
-    } merge;
+    int32_t qi[STAGE ? 1 : kGP][D];
+    Merge merge;
+    uint8_t stage[STAGE ? kWaves : 1][4][stage_page_bytes<D>()];   // [wave][page of the step]
   } u;
+  int32_t qi_own[STAGE ? kGP : 1][D];
+  uint8_t qstage[STAGE ? NS : 1][64 * 16];   // the query waves' query rows (staged build)
   float hA[kGP], hS[kGP][NG];
   uint32_t wl[kWaves][NS][NG][4][4][16];   // [wave][set][group][limb][head][token] = 4 pages' bytes
 };
@@ -91,6 +103,12 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   // registers allow two waves per SIMD with or without the second buffer
   // (the build held to three waves per SIMD keeps one)
   constexpr bool kPrefetch = NS == 2 && BITS == 4 && GS == 0 && WPE == 1;
+  // The two-set INT4 build held to three waves per SIMD stages the next
+  // step's pages in LDS (direct-to-LDS buffer loads hold no VGPRs while they
+  // fly), so it keeps a step in flight while it computes without the second
+  // register buffer that would cost it the third wave.
+  constexpr bool kStage = NS == 2 && BITS == 4 && GS == 0 && D == 128 && WPE == 3;
+  static_assert(!kStage || kStep == 4, "stage of four pages");
   constexpr int kNT = D / 16;          // PV tiles = output channels per lane
   constexpr int kOps = D / 64;         // QK MFMAs per page and head group
   constexpr int kGP = 4 * NS;          // padded heads per KV head
@@ -100,7 +118,9 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   // scratch it replaces) that every wave then reads
   constexpr bool kOpImage = D == 128;
   static_assert(!kOpImage || NS * kOps * 64 * 16 == sizeof(int32_t) * 4 * NS * D, "operand image size");
-  __shared__ Smem<D, NS, kNG> sm;
+  __shared__ Smem<D, NS, kNG, kStage> sm;
+  // the query scratch (fixed-point query, or the operand image)
+  int32_t (*const qscr)[D] = kStage ? sm.qi_own : sm.u.qi;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -119,13 +139,17 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
 
   // ---- prologue: loads that do not depend on seq_lens go out first ----------
-  // query: wave w < NS takes heads 4w .. 4w+3 of the group, one per row of 16
-  // lanes; lane (g, n) holds channels [kC n, kC n + kC) of head 4w + g.
-  // Padding heads read head G-1 and are zeroed below.
   const bool qwave = wave < NS;
   const int qhead = 4 * wave + g;
+  // query: wave w < NS takes heads 4w .. 4w+3 of the group, one per row of 16
+  // lanes; lane (g, n) holds channels [kC n, kC n + kC) of head 4w + g.
+  // Padding heads read head G-1 and are zeroed below.  (The staged build
+  // brings it in through LDS once the workgroup is known to have pages.)
   uint32_t qraw[kC / 2];
-  if (qwave) {
+  if constexpr (kStage) {
+#pragma unroll
+    for (int i = 0; i < kC / 2; ++i) qraw[i] = 0u;
+  } else if (qwave) {
     const uint16_t* qp = a.q + (hq0 + min(qhead, G - 1)) * D + kC * n;
     if constexpr (kC == 8) {
       const u32x4 t = *reinterpret_cast<const u32x4*>(qp);
@@ -140,6 +164,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
 #pragma unroll
     for (int i = 0; i < kC / 2; ++i) qraw[i] = 0u;
   }
+
   // Page ids come by scalar loads (wave-uniform addresses, always inside the
   // row), a step ahead of the page loads that use them, so they never wait
   // behind vector loads.  The first step's ids are fetched at once for the
@@ -182,6 +207,24 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
       for (int e = tid; e < G * D; e += 64 * kWaves) a.out[hq0 * D + e] = 0.0f;
     }
     return;
+  }
+  // A sequence whose pages all lie in one split is finished here (normalised
+  // output, no partial; the split merge skips its rows): in a ragged batch
+  // cut for its longest sequence most rows are such.  Windowed calls always
+  // store partials.
+  const int busy_splits = (npg - 1) / sp - (lo / kPage) / sp + 1;
+  const bool direct = !a.force_partial && (a.nsplit == 1 || busy_splits == 1);
+
+  // The staged build's query goes out only now (no stage or query load may
+  // be in flight when a workgroup of an empty split exits): through LDS,
+  // so that its wait below leaves the first step's stage loads in flight.
+  if constexpr (kStage) {
+    if (qwave) {
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + hq0 * D, G * D * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, (__attribute__((address_space(3))) void*)(&sm.qstage[wave][0]), 16,
+          static_cast<uint32_t>((min(qhead, G - 1) * D + kC * n) * 2), 0, 0, 0);
+    }
   }
 
   // ---- this wave's share of the split's pages ---------------------------------
@@ -246,13 +289,69 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
       }
     }
   };
+  // Staged build: every step's pages go through this wave's LDS stage.
+  struct StageMeta { bool pv[kStep]; bool all_ok; };
+  uint8_t* const stage = kStage ? &sm.u.stage[wave][0][0] : nullptr;
+  constexpr int kSP = stage_page_bytes<D>();
+  const uint32_t side_off = lane < 32 ? static_cast<uint32_t>(2 * kPage * kCodeBytes + 4 * lane)
+                                      : static_cast<uint32_t>(kSlab);
+  auto stage_issue = [&](int p, auto id_of, StageMeta& mt) {
+    mt.all_ok = true;
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) {
+      const int id = id_of(i);
+      mt.pv[i] = id >= 0 && id < a.num_pages;
+      mt.all_ok = mt.all_ok && mt.pv[i];
+      const uint8_t* sl = pool_h + static_cast<int64_t>(mt.pv[i] ? id : 0) * page_stride;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, mt.pv[i] ? kSlab : 0);
+      uint8_t* dst = stage + i * kSP;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst), 16, k_off,
+                                               0, 0, kStreamOnce);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024), 16,
+                                               v_off, 0, 0, kStreamOnce);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 2048), 4,
+                                               side_off, 0, 0, kStreamOnce);
+    }
+  };
+  auto stage_read = [&](Buf& sb, const StageMeta& mt) {
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) {
+      const uint8_t* src = stage + i * kSP;
+      sb.kx[i][0] = *reinterpret_cast<const u32x4*>(src + 16 * lane);
+      sb.vx[i][0] = *reinterpret_cast<const u32x4*>(src + 1024 + 16 * lane);
+      sb.km[i][0] = *reinterpret_cast<const uint32_t*>(src + 2048 + 4 * n);
+      sb.vm[i][0] = *reinterpret_cast<const uint32_t*>(src + 2048 + 4 * kPage + 4 * n);
+      sb.pv[i] = mt.pv[i];
+    }
+    sb.all_ok = mt.all_ok;
+  };
   // The first step's page loads go out before the query is waited for: the
   // query was requested first, so its wait leaves the pages in flight, and
-  // its rotation and limbs are computed while they arrive.
+  // its rotation and limbs are computed while they arrive.  (A staged wave
+  // with no pages sends nothing: no stage load may be in flight when the
+  // merge reuses the stage's LDS.)
   Buf buf0;
-  load_with(buf0, pw0, [&](int i) { return pw0 + i < pw1 ? idA[i] : -1; });
+  [[maybe_unused]] StageMeta mt;
+  if constexpr (kStage) {
+    if (pw0 < pw1) stage_issue(pw0, [&](int i) { return pw0 + i < pw1 ? idA[i] : -1; }, mt);
+  } else {
+    load_with(buf0, pw0, [&](int i) { return pw0 + i < pw1 ? idA[i] : -1; });
+  }
   ids4(pw0 + kStep, pw1, idB);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kStage) {
+    if (qwave) {
+      // the query's load was issued before the twelve stage loads of the
+      // first step (none when the wave has no pages)
+      __builtin_amdgcn_sched_barrier(0);
+      if (pw0 < pw1) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4 t = *reinterpret_cast<const u32x4*>(&sm.qstage[wave][16 * lane]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qraw[i] = t[i];
+    }
+  }
   float qv[kC];
 #pragma unroll
   for (int k = 0; k < kC; ++k) {
@@ -303,7 +402,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
         const uint32_t hi = __builtin_amdgcn_perm(y[c3], y[c2], sel);
         return __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ (L == 0 ? 0u : 0x80808080u);
       };
-      uint32_t* img = reinterpret_cast<uint32_t*>(&sm.u.qi[0][0]);
+      uint32_t* img = reinterpret_cast<uint32_t*>(&qscr[0][0]);
       const int lane0 = 16 * (n >> 2) + 4 * g;   // reader lanes: row (head g, limb L), group n / 4
 #pragma unroll
       for (int L = 0; L < 4; ++L) {
@@ -320,7 +419,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
     } else {
 #pragma unroll
       for (int k = 0; k < kC; k += 4)
-        *reinterpret_cast<v4i*>(&sm.u.qi[qhead][kC * n + k]) = v4i{qi[k], qi[k + 1], qi[k + 2], qi[k + 3]};
+        *reinterpret_cast<v4i*>(&qscr[qhead][kC * n + k]) = v4i{qi[k], qi[k + 1], qi[k + 2], qi[k + 3]};
     }
     // sum of the query over each group (|sum| <= D * 2^22: exact in int32);
     // a lane's kC channels lie in group kC n / GS
@@ -333,7 +432,15 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
       for (int gi = 0; gi < kNG; ++gi) sm.hS[qhead][gi] = static_cast<float>(gsum[gi]);
     }
   }
-  __syncthreads();
+  if constexpr (kStage) {
+    // the query's results are LDS writes: wait for those alone (a full
+    // __syncthreads would also drain the first step's stage loads)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  } else {
+    __syncthreads();
+  }
 
   // A operand of QK: row (head hs, limb lam), k-slots of lane group g.  At
   // head_dim 128 the query waves wrote every lane's operand words into an
@@ -348,7 +455,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
 #pragma unroll
     for (int gi = 0; gi < kNG; ++gi) qS[st][gi] = sm.hS[4 * st + g][gi];
     if constexpr (kOpImage) {
-      const v4i* img = reinterpret_cast<const v4i*>(&sm.u.qi[0][0]);
+      const v4i* img = reinterpret_cast<const v4i*>(&qscr[0][0]);
 #pragma unroll
       for (int op = 0; op < kOps; ++op) {
         const v4i vv = img[(st * kOps + op) * 64 + lane];
@@ -358,7 +465,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
       continue;
     }
     int32_t qc[D / 4];
-    const v4i* src = reinterpret_cast<const v4i*>(&sm.u.qi[4 * st + hs][(D / 4) * g]);
+    const v4i* src = reinterpret_cast<const v4i*>(&qscr[4 * st + hs][(D / 4) * g]);
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
       const v4i x = src[t];
@@ -614,7 +721,31 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
     else
       compute(sb, p, std::false_type{});
   };
-  if constexpr (kPrefetch) {
+  if constexpr (kStage) {
+    // Each step's pages land in this wave's LDS stage while the step before
+    // it is computed: K and V codes with one 16-byte load per lane each
+    // (lane L's bytes at 16 L, the bytes it would load itself), the 128
+    // sidecar bytes with one 4-byte load by lanes 0..31 (lanes 32..63 read
+    // past the descriptor's end: nothing).  The compiler does not track
+    // these loads: vmcnt(0) waits for the staged step (no other vector
+    // memory operation is in flight in the loop), lgkmcnt(0) for the reads
+    // out of the stage before the next step's loads overwrite it.
+    for (int p = pw0; p < pw1; p += kStep) {
+      // this step's pages have landed in the stage: into registers, then the
+      // next step's loads go to the stage while this one is computed
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      stage_read(buf0, mt);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if (p + kStep < pw1)
+        stage_issue(p + kStep, [&](int i) { return p + kStep + i < pw1 ? idB[i] : -1; }, mt);
+      ids4(p + 2 * kStep, pw1, idB);
+      step(buf0, p);
+    }
+  } else if constexpr (kPrefetch) {
     // The next step's loads go out before this step is computed, so a wave
     // keeps a step in flight while it computes, and the ids of the step after
     // that are fetched meanwhile.  With two sets of heads a step computes long
@@ -693,7 +824,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
       fwht_row_any<kC>(o, a.block, n);
       scale = block_norm(a.block);
     }
-    if (a.nsplit == 1 && !a.force_partial) {
+    if (direct) {
       scale *= lsum > 0.0f ? 1.0f / lsum : 0.0f;
       if (j < G) {
         float* dst = a.out + (hq0 + j) * D + kC * n;

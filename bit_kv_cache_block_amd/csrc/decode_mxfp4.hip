@@ -124,6 +124,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
     }
     return;
   }
+  // a sequence whose pages all lie in one split is finished here (the split
+  // merge skips its rows)
+  const bool direct = a.nsplit == 1 || (npg - 1) / sp == 0;
   const int span = p1 - p0;
   const int per_wave = ((span + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
   const int pw0 = p0 + wave * per_wave;
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
       fwht_row_any<kC>(o, a.block, n);
       scale = block_norm(a.block);
     }
-    if (a.nsplit == 1) {
+    if (direct) {
       scale *= lsum > 0.0f ? 1.0f / lsum : 0.0f;
       if (j < G) {
         float* dst = a.out + (hq0 + j) * D + kC * n;

@@ -45,11 +45,23 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
                            : a.split_pages;
   float m = -__builtin_inff(), l = 0.0f;
   v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
+  bool done = false;   // the decode already wrote this row
   if (live) {
     const int b = static_cast<int>(bh / a.num_q_heads);
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
     // the splits that held pages of this sequence
+    int lo, hi;
+    int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
+    const int npg = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
+    // a sequence whose pages lie in one split was finished by the decode,
+    // unless the decode was told to store partials only (windowed calls)
+    done = !a.force_partial && hi > lo && (npg - 1) / sp == pfirst / sp;
+  }
+  if (live && !done) {
+    const int b = static_cast<int>(bh / a.num_q_heads);
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
     int lo, hi;
     int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
     const int npg = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
@@ -78,7 +90,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
   }
   float* dst = a.out + bh * D + 4 * c;
   if constexpr (G == 1) {
-    if (!live) return;
+    if (!live || done) return;
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;   // an empty sequence stores zeros
     *reinterpret_cast<v4f*>(dst) = v4f{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
   } else {
@@ -88,7 +100,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
       sm_l[r][g] = l;
     }
     __syncthreads();
-    if (!live || g != 0) return;
+    if (!live || done || g != 0) return;
     float mstar = sm_m[r][0];
 #pragma unroll
     for (int k = 1; k < G; ++k) mstar = fmaxf(mstar, sm_m[r][k]);
