@@ -41,15 +41,15 @@
 namespace kvq {
 
 hipError_t launch_decode_int4(const DecodeArgs& a, hipStream_t s) {
-  return a.balance ? launch_decode_quant_balanced(a, 4, 0, s) : launch_format<false>(a, 4, 0, s);
+  return a.balance ? launch_decode_quant_balanced(a, 4, 0, s) : launch_format<kMapPlanned>(a, 4, 0, s);
 }
 
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t s) {
-  return a.balance ? launch_decode_quant_balanced(a, 8, 0, s) : launch_format<false>(a, 8, 0, s);
+  return a.balance ? launch_decode_quant_balanced(a, 8, 0, s) : launch_format<kMapPlanned>(a, 8, 0, s);
 }
 
 hipError_t launch_decode_int4g(const DecodeArgs& a, hipStream_t s) {
-  return a.balance ? launch_decode_quant_balanced(a, 4, a.group, s) : launch_format<false>(a, 4, a.group, s);
+  return a.balance ? launch_decode_quant_balanced(a, 4, a.group, s) : launch_format<kMapPlanned>(a, 4, a.group, s);
 }
 
 }  // namespace kvq

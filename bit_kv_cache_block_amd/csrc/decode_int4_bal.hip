@@ -7,7 +7,7 @@
 namespace kvq {
 
 hipError_t launch_decode_quant_balanced(const DecodeArgs& a, int bits, int gs, hipStream_t s) {
-  return launch_format<true>(a, bits, gs, s);
+  return launch_format<kMapBalanced>(a, bits, gs, s);
 }
 
 }  // namespace kvq

@@ -83,10 +83,11 @@ struct StepBuf {
 };
 
 // WPE: waves per SIMD the register allocation must allow (1 = no limit);
-// BAL: a balanced call (balanced_split_pages), built apart so that the
-// planned calls carry none of its code
-template <int D, int NS, bool QBF16, int BITS, int GS, int WPE, bool BAL>
+// MAP: how workgroup `wid` finds its work (kMapPlanned, kMapBalanced,
+// kMapStream), each built apart so that a call carries no other's code
+template <int D, int NS, bool QBF16, int BITS, int GS, int WPE, int MAP>
 __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t wid) {
+  constexpr bool BAL = MAP == kMapBalanced;
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
   static_assert(GS == 0 || (BITS == 4 && (GS == 32 || GS == 64) && GS <= D), "groups of 32 or 64 channels, 4-bit");
   constexpr int kCodeBytes = D * BITS / 8;           // one vector's codes
@@ -126,98 +127,66 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63;
   const int g = lane >> 4, n = lane & 15, hs = n >> 2, lam = n & 3;
-  // Work item (split s, sequence b, KV head), KV head fastest and split
-  // slowest, last split first.  Each split is one contiguous run of
-  // workgroups that the round-robin dispatch spreads over every XCD and CU
-  // (with the split fastest, a period of 2, 4 or 8 left most CUs with the
-  // empty splits of short sequences only), and the later splits, busy only
-  // for the longest sequences, start first instead of last.
-  const int kvh = static_cast<int>(wid % a.num_kv_heads);
-  const int b = static_cast<int>((wid / a.num_kv_heads) % a.batch);
-  const int s_plan = a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
-
-  // ---- prologue: loads that do not depend on seq_lens go out first ----------
   const bool qwave = wave < NS;
   const int qhead = 4 * wave + g;
+  const int G = a.num_q_heads / a.num_kv_heads;
   // query: wave w < NS takes heads 4w .. 4w+3 of the group, one per row of 16
   // lanes; lane (g, n) holds channels [kC n, kC n + kC) of head 4w + g.
   // Padding heads read head G-1 and are zeroed below.  (The staged build
-  // brings it in through LDS once the workgroup is known to have pages.)
-  uint32_t qraw[kC / 2];
-  if constexpr (kStage) {
+  // brings it in through LDS once the workgroup is known to have work.)
+  auto load_query = [&](int64_t hq0, uint32_t (&qraw)[kC / 2]) {
+    if constexpr (kStage) {
 #pragma unroll
-    for (int i = 0; i < kC / 2; ++i) qraw[i] = 0u;
-  } else if (qwave) {
-    const uint16_t* qp = a.q + (hq0 + min(qhead, G - 1)) * D + kC * n;
-    if constexpr (kC == 8) {
-      const u32x4 t = *reinterpret_cast<const u32x4*>(qp);
+      for (int i = 0; i < kC / 2; ++i) qraw[i] = 0u;
+    } else if (qwave) {
+      const uint16_t* qp = a.q + (hq0 + min(qhead, G - 1)) * D + kC * n;
+      if constexpr (kC == 8) {
+        const u32x4 t = *reinterpret_cast<const u32x4*>(qp);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qraw[i] = t[i];
+        for (int i = 0; i < 4; ++i) qraw[i] = t[i];
+      } else {
+        const u32x2 t = *reinterpret_cast<const u32x2*>(qp);
+        qraw[0] = t[0];
+        qraw[1] = t[1];
+      }
     } else {
-      const u32x2 t = *reinterpret_cast<const u32x2*>(qp);
-      qraw[0] = t[0];
-      qraw[1] = t[1];
+#pragma unroll
+      for (int i = 0; i < kC / 2; ++i) qraw[i] = 0u;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kC / 2; ++i) qraw[i] = 0u;
-  }
-
-  // Page ids come by scalar loads (wave-uniform addresses, always inside the
-  // row), a step ahead of the page loads that use them, so they never wait
-  // behind vector loads.  The first step's ids are fetched at once for the
-  // range a full-length split of the host's plan gives this wave, and again
-  // only if the sequence is shorter (its balanced range starts elsewhere) or
-  // the split grew.
-  const int p0_plan = s_plan * a.split_pages;
-  const int per_wave_plan = ((a.split_pages + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  using ConstI32 = const __attribute__((address_space(4))) int32_t;
-  ConstI32* bt_s = (ConstI32*)bt;   // generic to constant address space
-  // raw entries of pages p .. p+3, indexes clamped below lim (pages at or
-  // past the range are dropped where the ids are used)
-  auto ids4 = [&](int p, int lim, int32_t (&id)[kStep]) {
-#pragma unroll
-    for (int i = 0; i < kStep; ++i) id[i] = bt_s[min(p + i, lim - 1)];
   };
-  const int cb = p0_plan + wave * per_wave_plan;
-  int32_t idA[kStep], idB[kStep];
-  ids4(cb, min(p0_plan + a.split_pages, a.bt_stride), idA);
-  // pages per split, and the split: last first, unless the device grew the
-  // splits (then the later ones are empty, and first-split-first keeps them
-  // from holding the machine before the work starts)
-  const int sp = BAL ? balanced_split_pages(a.split_pages, a.seq_lens, a.batch, a.max_seq_len,
-                                            a.num_kv_heads)
-                     : a.split_pages;
-  const bool grown = BAL && sp != a.split_pages;
-  const int s = grown ? static_cast<int>(wid / a.num_kv_heads / a.batch) : s_plan;
-  const int p0 = s * sp;
 
-  int len = a.seq_lens[b];
-  len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-  int lo, hi;   // the tokens this pass reads (all of them unless windows take some)
-  int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
-  const int npg = (hi + kPage - 1) / kPage;
-  const int q0 = max(p0, lo / kPage);
-  const int p1 = min(npg, p0 + sp);
-  if (q0 >= p1 || hi <= lo) {
-    if (a.nsplit == 1 && !a.force_partial) {   // empty sequence: zero output rows
-      for (int e = tid; e < G * D; e += 64 * kWaves) a.out[hq0 * D + e] = 0.0f;
-    }
-    return;
-  }
-  // A sequence whose pages all lie in one split is finished here (normalised
-  // output, no partial; the split merge skips its rows): in a ragged batch
-  // cut for its longest sequence most rows are such.  Windowed calls always
-  // store partials.
-  const int busy_splits = (npg - 1) / sp - (lo / kPage) / sp + 1;
-  const bool direct = !a.force_partial && (a.nsplit == 1 || busy_splits == 1);
+  using ConstI32 = const __attribute__((address_space(4))) int32_t;
+  // raw entries of pages p .. p+3 of a block-table row, indexes clamped below
+  // lim (pages at or past the range are dropped where the ids are used);
+  // page ids come by scalar loads (wave-uniform addresses, always inside the
+  // row)
+  auto ids4_of = [&](ConstI32* row, int p, int lim, int32_t (&id)[kStep]) {
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) id[i] = row[min(p + i, lim - 1)];
+  };
 
+  // One work item: pages [q0, p1) of sequence b (tokens [lo, hi) of it
+  // count) for KV head kvh, its result stored normalised in the output rows
+  // (direct) or as a partial at part_base + head * part_mul.  qraw holds the
+  // query row already loaded (not in the staged build), idA the ids of pages
+  // cb .. cb+3.
+  // tid_r and wave_r are the thread and wave ids, passed in so that a caller
+  // running several items can keep what depends on them inside its loop.
+  auto run = [&](const int kvh, const int64_t hq0, ConstI32* const bt_s, const int q0, const int p1,
+                 const int lo, const int hi, const bool direct, const int64_t part_base, const int part_mul,
+                 uint32_t (&qraw)[kC / 2], int32_t (&idA)[kStep], const int cb, const bool grown,
+                 const int tid_r, const int wave_r) {
+  const int tid = tid_r;
+  const int wave = wave_r;
+  const int lane = tid & 63;
+  const int g = lane >> 4, n = lane & 15, hs = n >> 2, lam = n & 3;
+  const bool qwave = wave < NS;
+  const int qhead = 4 * wave + g;
+  auto ids4 = [&](int p, int lim, int32_t (&id)[kStep]) { ids4_of(bt_s, p, lim, id); };
+  int32_t idB[kStep];
   // The staged build's query goes out only now (no stage or query load may
-  // be in flight when a workgroup of an empty split exits): through LDS,
-  // so that its wait below leaves the first step's stage loads in flight.
+  // be in flight when a workgroup with no work exits): through LDS, so that
+  // its wait below leaves the first step's stage loads in flight.
   if constexpr (kStage) {
     if (qwave) {
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + hq0 * D, G * D * 2);
@@ -833,7 +802,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
           *reinterpret_cast<v4f*>(dst + k) = v4f{o[k] * scale, o[k + 1] * scale, o[k + 2] * scale, o[k + 3] * scale};
       }
     } else if (j < G) {
-      const int64_t idx = (hq0 + j) * a.part_stride + a.part_slot0 + s;
+      const int64_t idx = part_base + static_cast<int64_t>(j) * part_mul;
       float* dst = a.part_acc + idx * D + kC * n;
 #pragma unroll
       for (int k = 0; k < kC; k += 4)
@@ -842,6 +811,111 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
         a.part_ml[idx * 2 + 0] = mstar;
         a.part_ml[idx * 2 + 1] = lsum;
       }
+    }
+  }
+  };   // run
+
+  if constexpr (MAP != kMapStream) {
+    // Work item (split s, sequence b, KV head), KV head fastest and split
+    // slowest, last split first.  Each split is one contiguous run of
+    // workgroups that the round-robin dispatch spreads over every XCD and CU
+    // (with the split fastest, a period of 2, 4 or 8 left most CUs with the
+    // empty splits of short sequences only), and the later splits, busy only
+    // for the longest sequences, start first instead of last.
+    const int kvh = static_cast<int>(wid % a.num_kv_heads);
+    const int b = static_cast<int>((wid / a.num_kv_heads) % a.batch);
+    const int s_plan = a.nsplit - 1 - static_cast<int>(wid / a.num_kv_heads / a.batch);
+    const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
+    // ---- prologue: loads that do not depend on seq_lens go out first --------
+    uint32_t qraw[kC / 2];
+    load_query(hq0, qraw);
+    // The first step's ids are fetched at once for the range a full-length
+    // split of the host's plan gives this wave (a step ahead of the page loads
+    // that use them, so they never wait behind vector loads), and again only
+    // if the sequence is shorter (its balanced range starts elsewhere) or the
+    // split grew.
+    const int p0_plan = s_plan * a.split_pages;
+    const int per_wave_plan = ((a.split_pages + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
+    ConstI32* bt_s = (ConstI32*)(a.block_table + static_cast<int64_t>(b) * a.bt_stride);
+    const int cb = p0_plan + wave * per_wave_plan;
+    int32_t idA[kStep];
+    ids4_of(bt_s, cb, min(p0_plan + a.split_pages, a.bt_stride), idA);
+    // pages per split, and the split: last first, unless the device grew the
+    // splits (then the later ones are empty, and first-split-first keeps them
+    // from holding the machine before the work starts)
+    const int sp = BAL ? balanced_split_pages(a.split_pages, a.seq_lens, a.batch, a.max_seq_len,
+                                              a.num_kv_heads)
+                       : a.split_pages;
+    const bool grown = BAL && sp != a.split_pages;
+    const int s = grown ? static_cast<int>(wid / a.num_kv_heads / a.batch) : s_plan;
+    const int p0 = s * sp;
+
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+    int lo, hi;   // the tokens this pass reads (all of them unless windows take some)
+    int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
+    const int npg = (hi + kPage - 1) / kPage;
+    const int q0 = max(p0, lo / kPage);
+    const int p1 = min(npg, p0 + sp);
+    if (q0 >= p1 || hi <= lo) {
+      if (a.nsplit == 1 && !a.force_partial) {   // empty sequence: zero output rows
+        for (int e = tid; e < G * D; e += 64 * kWaves) a.out[hq0 * D + e] = 0.0f;
+      }
+      return;
+    }
+    // A sequence whose pages all lie in one split is finished here (normalised
+    // output, no partial; the split merge skips its rows): in a ragged batch
+    // cut for its longest sequence most rows are such.  Windowed calls always
+    // store partials.
+    const int busy_splits = (npg - 1) / sp - (lo / kPage) / sp + 1;
+    const bool direct = !a.force_partial && (a.nsplit == 1 || busy_splits == 1);
+    run(kvh, hq0, bt_s, q0, p1, lo, hi, direct, hq0 * a.part_stride + a.part_slot0 + s, a.part_stride, qraw,
+        idA, cb, grown, tid, wave);
+  } else {
+    // Stream-K: the pages of the batch, sequence after sequence, form one
+    // run of T pages per KV head, cut into sk_ranges ranges of R pages;
+    // workgroup wid takes range wid / num_kv_heads of KV head wid %
+    // num_kv_heads and walks the sequences that meet it.  Every workgroup
+    // gets the same number of pages whatever the lengths (a ragged batch
+    // leaves no workgroup idle and none with a long tail), and none exists
+    // for pages that are not there.  A sequence inside one range is
+    // finished there; one cut by range ends leaves a partial per range it
+    // meets: slot 0 of the range for the piece at the range's start, slot 1
+    // for a piece that starts later (then it runs to the range's end).
+    const int kvh = static_cast<int>(wid % a.num_kv_heads);
+    const int r = static_cast<int>(wid / a.num_kv_heads);
+    const StreamRange rg = stream_range(a.seq_lens, a.batch, a.max_seq_len, a.sk_ranges, r);
+    if (rg.first >= rg.end) return;   // past the batch's pages (wave-uniform)
+    int b = rg.b, sb = rg.start_b;
+    bool later = false;
+    int32_t idA[kStep] = {0, 0, 0, 0};
+    while (sb < rg.end) {   // sb < T: b < batch
+      int len = a.seq_lens[b];
+      len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+      const int np = (len + kPage - 1) / kPage;
+      if (np > 0) {
+        const int s0 = max(sb, rg.first), s1 = min(sb + np, rg.end);
+        if (kvh == 0 && s0 == sb && tid == 0) {   // the merge's record of the sequence
+          const int rf = sb / rg.pages, rl = (sb + np - 1) / rg.pages;
+          a.sk_rec[2 * b] = rf;
+          a.sk_rec[2 * b + 1] = 2 * (rl - rf + 1) + (sb != rf * rg.pages ? 1 : 0);
+        }
+        if (later) __syncthreads();   // the last item's merge is done with the LDS
+        later = true;
+        const int64_t hq0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * G;
+        uint32_t qraw[kC / 2];
+        load_query(hq0, qraw);
+        ConstI32* bt_s = (ConstI32*)(a.block_table + static_cast<int64_t>(b) * a.bt_stride);
+        const bool whole = s0 == sb && s1 == sb + np;
+        const int64_t slot = ((static_cast<int64_t>(kvh) * a.sk_ranges + r) * 2 + (s0 == rg.first ? 0 : 1)) * G;
+        // values that depend on the thread alone are computed again for each
+        // item rather than held (in registers, or spilled) across the walk
+        int tid_l = tid, wave_l = wave;
+        asm volatile("" : "+v"(tid_l), "+s"(wave_l));
+        run(kvh, hq0, bt_s, s0 - sb, s1 - sb, 0, len, whole, slot, 1, qraw, idA, -1, false, tid_l, wave_l);
+      }
+      sb += np;
+      ++b;
     }
   }
 }

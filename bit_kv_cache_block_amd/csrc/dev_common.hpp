@@ -197,6 +197,62 @@ __device__ __forceinline__ int balanced_split_pages(int sp, const int32_t* seq_l
   return even > sp ? static_cast<int>(even) : sp;
 }
 
+// Stream-K range r of a batch (the plain INT4-family decode): the pages of
+// the sequences, one after another (ceil(len / 16) each, len clamped to
+// [0, max_seq_len]), form a run of T pages, cut into ranges of
+// pages = max(16, ceil(T / ranges)); range r is [first, end).  b is the
+// sequence holding page `first` and start_b that sequence's first page in the
+// run (first >= end: the range is empty, b and start_b unset).  Every lane of
+// the wave takes part; the results are wave-uniform.
+struct StreamRange {
+  int pages, first, end, b, start_b;
+};
+__device__ __forceinline__ int stream_pages_of(const int32_t* seq_lens, int b, int batch, int max_seq_len) {
+  int len = b < batch ? seq_lens[b] : 0;
+  len = len < 0 ? 0 : (len > max_seq_len ? max_seq_len : len);
+  return (len + kPage - 1) / kPage;
+}
+__device__ __forceinline__ StreamRange stream_range(const int32_t* seq_lens, int batch, int max_seq_len,
+                                                    int ranges, int r) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  for (int c = 0; c < batch; c += 64) {
+    int np = stream_pages_of(seq_lens, c + lane, batch, max_seq_len);
+#pragma unroll
+    for (int m = 1; m < 64; m *= 2) np += __shfl_xor(np, m);
+    total += np;
+  }
+  total = __builtin_amdgcn_readfirstlane(total);
+  StreamRange rg;
+  rg.pages = max(kPage, (total + ranges - 1) / ranges);
+  rg.first = r * rg.pages;
+  rg.end = min(rg.first + rg.pages, total);
+  rg.b = 0;
+  rg.start_b = 0;
+  if (rg.first >= rg.end) return rg;
+  // the first sequence whose pages end after `first`
+  int carry = 0;
+  for (int c = 0; c < batch; c += 64) {
+    const int np = stream_pages_of(seq_lens, c + lane, batch, max_seq_len);
+    int incl = np;   // inclusive prefix over the 64 lanes
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+      const int y = __shfl_up(incl, d);
+      incl += lane >= d ? y : 0;
+    }
+    const int chunk = __builtin_amdgcn_readlane(incl, 63);
+    if (carry + chunk > rg.first) {
+      const uint64_t hit = __ballot(carry + incl > rg.first);
+      const int l0 = static_cast<int>(__builtin_ctzll(hit));
+      rg.b = c + l0;
+      rg.start_b = carry + __builtin_amdgcn_readlane(incl - np, l0);
+      break;
+    }
+    carry += chunk;
+  }
+  return rg;
+}
+
 // Tokens [lo, hi) of a sequence of `len` tokens that an INT4 pass reads
 // when the first skip_first and the last skip_last tokens are left to the
 // high-precision windows (both zero: all of them).

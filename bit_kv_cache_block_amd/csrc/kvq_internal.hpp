@@ -76,7 +76,26 @@ struct DecodeArgs {
   int32_t win_len;
   // The splits may grow with the batch's whole work (balanced_split_pages).
   int32_t balance;
+  // Stream-K mapping of the plain INT4-family decode (sk_ranges > 0): the
+  // batch's pages, one sequence after another, cut per KV head into
+  // sk_ranges ranges of equal length, one workgroup each.  The partial of
+  // (KV head, range, slot, head of the group) is at
+  // ((kvh * sk_ranges + range) * 2 + slot) * G + head; sk_rec[2b] is the
+  // first range sequence b meets, sk_rec[2b + 1] twice the number of ranges
+  // it meets plus 1 if its piece in the first one is in slot 1 (written by
+  // the decode for every sequence with pages, read by the merge).
+  int32_t sk_ranges;
+  int32_t* sk_rec;
 };
+
+// How a decode workgroup finds its work: the host's split plan, the plan's
+// splits grown on the device (balanced_split_pages), or stream-K ranges.
+constexpr int kMapPlanned = 0;
+constexpr int kMapBalanced = 1;
+constexpr int kMapStream = 2;
+// Stream-K: at most this many workgroups (ranges times KV heads, rounded up
+// to whole KV heads) -- the workspace is sized for it.
+constexpr int kStreamMaxWorkgroups = 2048;
 
 // Split-K plan shared by the launch and the workspace query.
 struct SplitPlan {
@@ -98,6 +117,13 @@ hipError_t launch_decode_int4g(const DecodeArgs& a, hipStream_t s);
 // The balanced build (a.balance set) of the three above: codes of `bits` bits
 // with one scale and zero per `gs` channels (0: per token).
 hipError_t launch_decode_quant_balanced(const DecodeArgs& a, int bits, int gs, hipStream_t s);
+// The stream-K build of the three (a.sk_ranges set by stream_ranges of the
+// same format): a grid of num_kv_heads * sk_ranges workgroups.
+hipError_t launch_decode_quant_stream(const DecodeArgs& a, int bits, int gs, hipStream_t s);
+// Ranges per KV head for the stream-K build of a format on the current
+// device: as many workgroups as the device holds at once, at most
+// kStreamMaxWorkgroups (rounded up to whole KV heads).
+hipError_t stream_ranges(const DecodeArgs& a, int bits, int gs, int32_t* ranges);
 hipError_t launch_decode_mxfp4(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t s);

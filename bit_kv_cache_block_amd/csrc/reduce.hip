@@ -14,6 +14,11 @@
 // at most about four splits: a merge of few rows and many splits (small
 // batches cut finely) is a couple of memory round trips rather than one per
 // split.
+//
+// After a stream-K decode (SK) a row's partials are those of the ranges its
+// sequence met, found from the decode's record of the sequence; a sequence
+// inside one range was finished by the decode, one with no pages gets zeros
+// here.
 #include "dev_common.hpp"
 #include "kvq_internal.hpp"
 
@@ -22,7 +27,7 @@ namespace {
 
 constexpr int kReduceThreads = 256;
 
-template <int D, int G>
+template <int D, int G, bool SK>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
   constexpr int kL = D / 4;                          // lanes per split group
   constexpr int kRows = kReduceThreads / (kL * G);   // rows per workgroup
@@ -39,53 +44,84 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * kRows + r;
   const bool live = bh < rows;
 
-  // (every lane of the wave takes part in reading the lengths)
-  const int sp = a.balance ? balanced_split_pages(a.split_pages, a.seq_lens, a.batch, a.max_seq_len,
-                                                  a.num_kv_heads)
-                           : a.split_pages;
   float m = -__builtin_inff(), l = 0.0f;
   v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
   bool done = false;   // the decode already wrote this row
-  if (live) {
-    const int b = static_cast<int>(bh / a.num_q_heads);
-    int len = a.seq_lens[b];
-    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-    // the splits that held pages of this sequence
-    int lo, hi;
-    int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
-    const int npg = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
-    // a sequence whose pages lie in one split was finished by the decode,
-    // unless the decode was told to store partials only (windowed calls)
-    done = !a.force_partial && hi > lo && (npg - 1) / sp == pfirst / sp;
-  }
-  if (live && !done) {
-    const int b = static_cast<int>(bh / a.num_q_heads);
-    int len = a.seq_lens[b];
-    len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-    int lo, hi;
-    int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
-    const int npg = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
-    const float* ml = a.part_ml + bh * a.part_stride * 2;
-    const float* pa = a.part_acc + bh * a.part_stride * D + 4 * c;
-    // Every slot's loads are issued (the workspace holds part_stride slots
-    // per row) and only valid slots are folded in, by selection rather than
-    // a zero weight, so stale bytes never enter the sums; without a branch in
-    // the loop the unrolled iterations' loads are all in flight together.
+  if constexpr (SK) {
+    if (live) {
+      const int b = static_cast<int>(bh / a.num_q_heads);
+      const int h = static_cast<int>(bh % a.num_q_heads);
+      const int gq = a.num_q_heads / a.num_kv_heads;
+      const int kvh = h / gq, j = h % gq;
+      int cnt = 0, rf = 0, fs = 0;
+      if (stream_pages_of(a.seq_lens, b, a.batch, a.max_seq_len) > 0) {
+        rf = a.sk_rec[2 * b];
+        cnt = a.sk_rec[2 * b + 1] >> 1;
+        fs = a.sk_rec[2 * b + 1] & 1;
+      }
+      done = cnt == 1;
+      if (!done) {
 #pragma unroll 4
-    for (int s = g; s < a.part_stride; s += G) {
-      const float ms = ml[2 * s], ls = ml[2 * s + 1];
-      const v4f x = *reinterpret_cast<const v4f*>(pa + static_cast<int64_t>(s) * D);
-      // INT4 split s, or (windowed calls) the window pass's slot, the last
-      const bool ok = (a.has_window && s == a.part_stride - 1)
-                          ? min(len, a.win_len) > 0
-                          : hi > lo && max(s * sp, pfirst) < min(npg, (s + 1) * sp);
-      const float mn = ok ? fmaxf(m, ms) : m;
-      const float mu = mn == -__builtin_inff() ? 0.0f : mn;
-      const float fo = fast_exp2(m - mu), fs = fast_exp2(ms - mu);
-      l = ok ? __builtin_fmaf(l, fo, ls * fs) : l;
+        for (int k = g; k < cnt; k += G) {
+          const int64_t idx = ((static_cast<int64_t>(kvh) * a.sk_ranges + rf + k) * 2 + (k == 0 ? fs : 0)) * gq + j;
+          const float ms = a.part_ml[2 * idx], ls = a.part_ml[2 * idx + 1];
+          const v4f x = *reinterpret_cast<const v4f*>(a.part_acc + idx * D + 4 * c);
+          const float mn = fmaxf(m, ms);
+          const float mu = mn == -__builtin_inff() ? 0.0f : mn;
+          const float fo = fast_exp2(m - mu), fs2 = fast_exp2(ms - mu);
+          l = __builtin_fmaf(l, fo, ls * fs2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = ok ? __builtin_fmaf(o[i], fo, x[i] * fs) : o[i];
-      m = mn;
+          for (int i = 0; i < 4; ++i) o[i] = __builtin_fmaf(o[i], fo, x[i] * fs2);
+          m = mn;
+        }
+      }
+    }
+  } else {
+    // (every lane of the wave takes part in reading the lengths)
+    const int sp = a.balance ? balanced_split_pages(a.split_pages, a.seq_lens, a.batch, a.max_seq_len,
+                                                    a.num_kv_heads)
+                             : a.split_pages;
+    if (live) {
+      const int b = static_cast<int>(bh / a.num_q_heads);
+      int len = a.seq_lens[b];
+      len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+      // the splits that held pages of this sequence
+      int lo, hi;
+      int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
+      const int npg = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
+      // a sequence whose pages lie in one split was finished by the decode,
+      // unless the decode was told to store partials only (windowed calls)
+      done = !a.force_partial && hi > lo && (npg - 1) / sp == pfirst / sp;
+    }
+    if (live && !done) {
+      const int b = static_cast<int>(bh / a.num_q_heads);
+      int len = a.seq_lens[b];
+      len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+      int lo, hi;
+      int4_token_range(len, a.skip_first, a.skip_last, lo, hi);
+      const int npg = (hi + kPage - 1) / kPage, pfirst = lo / kPage;
+      const float* ml = a.part_ml + bh * a.part_stride * 2;
+      const float* pa = a.part_acc + bh * a.part_stride * D + 4 * c;
+      // Every slot's loads are issued (the workspace holds part_stride slots
+      // per row) and only valid slots are folded in, by selection rather than
+      // a zero weight, so stale bytes never enter the sums; without a branch in
+      // the loop the unrolled iterations' loads are all in flight together.
+#pragma unroll 4
+      for (int s = g; s < a.part_stride; s += G) {
+        const float ms = ml[2 * s], ls = ml[2 * s + 1];
+        const v4f x = *reinterpret_cast<const v4f*>(pa + static_cast<int64_t>(s) * D);
+        // INT4 split s, or (windowed calls) the window pass's slot, the last
+        const bool ok = (a.has_window && s == a.part_stride - 1)
+                            ? min(len, a.win_len) > 0
+                            : hi > lo && max(s * sp, pfirst) < min(npg, (s + 1) * sp);
+        const float mn = ok ? fmaxf(m, ms) : m;
+        const float mu = mn == -__builtin_inff() ? 0.0f : mn;
+        const float fo = fast_exp2(m - mu), fs = fast_exp2(ms - mu);
+        l = ok ? __builtin_fmaf(l, fo, ls * fs) : l;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = ok ? __builtin_fmaf(o[i], fo, x[i] * fs) : o[i];
+        m = mn;
+      }
     }
   }
   float* dst = a.out + bh * D + 4 * c;
@@ -125,7 +161,10 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   constexpr int kRows = kReduceThreads / (D / 4 * G);
   const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
   const dim3 grid(static_cast<unsigned>((rows + kRows - 1) / kRows));
-  reduce_kernel<D, G><<<grid, kReduceThreads, 0, s>>>(a);
+  if (a.sk_ranges > 0)
+    reduce_kernel<D, G, true><<<grid, kReduceThreads, 0, s>>>(a);
+  else
+    reduce_kernel<D, G, false><<<grid, kReduceThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

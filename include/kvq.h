@@ -226,8 +226,15 @@ kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const vo
  *               used can be smaller).  A batch of at most 32 sequences cut
  *               into 16 or more partitions may have them grown on the
  *               device from the batch's total length, so that the busy
- *               ones stay about 512 workgroups' worth.  The partitioning
- *               changes only the rounding of the result.
+ *               ones stay about 512 workgroups' worth.  With 0, a batch of
+ *               at least 256 (sequence, KV head) pairs whose longest
+ *               sequence would be cut takes the stream-K mapping instead
+ *               (this decode, the INT8 and the grouped INT4 ones): the
+ *               batch's pages, one sequence after another, are cut per KV
+ *               head into equal ranges, one per workgroup the device holds
+ *               at once, and sequences met by several ranges are merged
+ *               from their partials.  The partitioning changes only the
+ *               rounding of the result.
  * out:          device fp32 [batch][num_q_heads][head_dim], 16-byte aligned.
  * workspace:    device scratch of at least kvq_decode_workspace_bytes(...)
  *               for the same arguments, 16-byte aligned; its contents are
@@ -247,8 +254,9 @@ kvq_status kvq_decode_attn(const kvq_int4_cache* cache, const void* q, kvq_dtype
  * static device array of KVQ_NOALLOC_SCRATCH_BYTES that the library holds on
  * each GPU it runs on until the process ends (its address is looked up on
  * the first call on each device, with that device current).  The call
- * allocates nothing.  A call whose split plan needs more scratch than that
- * (kvq_decode_workspace_bytes of the same arguments) returns
+ * allocates nothing.  A call whose plan needs more scratch than that (the
+ * planned splits' partials, or with the stream-K mapping two partials per
+ * range of the largest grid plus 8 bytes per sequence) returns
  * KVQ_ERR_WORKSPACE_TOO_SMALL before anything is launched.  Every call on a
  * GPU shares that GPU's scratch and the partials of one call are read only
  * by that call, so nothing needs clearing between calls; calls that overlap
@@ -260,7 +268,12 @@ kvq_status kvq_decode_attn_noalloc(const kvq_int4_cache* cache, const void* q, k
                                    int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
                                    void* stream);
 
-/* Workspace bytes kvq_decode_attn / kvq_decode_attn_bf16 need (0 allowed). */
+/* Workspace bytes the decodes of this header need for these arguments (0
+ * allowed): the larger of the planned splits' partials and, where the
+ * stream-K mapping applies (num_splits 0, see kvq_decode_attn), its
+ * partials -- (head_dim + 2) floats for two slots per query head and range
+ * of a grid of at most 2048 workgroups rounded up to whole KV heads -- and
+ * two int32 per sequence.  One size serves every decode of the header. */
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_seq_len, int32_t num_splits);
 

@@ -195,17 +195,28 @@ def test_bf16_entry_points_validate():
                                   FAKE, 0, None) == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
 
 
-@pytest.mark.parametrize("batch,hkv,maxlen", [(64, 8, 4096), (8, 8, 131072), (256, 8, 32768),
-                                               (1, 8, 32768), (4, 2, 256), (3, 1, 1)])
-def test_workspace_covers_every_split(batch, hkv, maxlen):
-    """The workspace holds (D + 2) floats per (sequence, head, split), and the
-    split plan covers the longest sequence with splits of whole 4-page steps."""
+@pytest.mark.parametrize("batch,hkv,maxlen,stream", [(64, 8, 4096, False), (8, 8, 131072, False),
+                                                      (256, 8, 32768, True), (32, 8, 32768, True),
+                                                      (16, 8, 32768, False), (1, 8, 32768, False),
+                                                      (4, 2, 256, False), (3, 1, 1, False)])
+def test_workspace_covers_every_split(batch, hkv, maxlen, stream):
+    """With a split count given, the workspace holds (D + 2) floats per
+    (sequence, head, split), and the split plan covers the longest sequence
+    with splits of whole 4-page steps.  With the automatic plan of a batch of
+    at least 256 (sequence, KV head) pairs whose longest sequence is cut, it
+    also holds the stream-K partials: (D + 2) floats for two slots per range
+    and query head of the largest grid (2048 workgroups, whole KV heads) and
+    two int32 per sequence."""
     hq, d = hkv * 4, 128
     ws = kvq.kvq_decode_workspace_bytes(batch, hq, hkv, d, maxlen, 0)
-    assert ws % (batch * hq * (d + 2) * 4) == 0
-    nsplit = max(1, ws // (batch * hq * (d + 2) * 4))   # 0 bytes: unsplit, no workspace
-    pages = (maxlen + 15) // 16
-    assert 1 <= nsplit <= max(1, (pages + 3) // 4)
+    sk = -(-2048 // hkv) * hkv * 2 * (hq // hkv) * (d + 2) * 4 + batch * 8
+    if stream:
+        assert ws >= sk
+    if ws != sk:   # the planned splits (of a decode with no stream-K build) need more
+        assert ws % (batch * hq * (d + 2) * 4) == 0
+        nsplit = ws // (batch * hq * (d + 2) * 4)
+        pages = (maxlen + 15) // 16
+        assert (1 if ws else 0) <= nsplit <= max(1, (pages + 3) // 4)
     for s in (1, 2, 5):
         ws_s = kvq.kvq_decode_workspace_bytes(batch, hq, hkv, d, maxlen, s)
         assert ws_s // (batch * hq * (d + 2) * 4) <= s
@@ -245,12 +256,14 @@ def test_windowed_decode_rejects_mismatched_window_pool():
 def test_windowed_workspace_holds_a_partial_per_split_and_the_window():
     """The INT4 pass always stores partials and the window pass stores one
     more per row (the split merge finishes the call), so even one split needs
-    two slots; split counts match kvq_decode_attn's."""
+    two slots; split counts match kvq_decode_attn's plan (a batch this small
+    takes no stream-K mapping)."""
+    row = 4 * 8 * (64 + 2) * 4
     for maxlen in (16, 4096, 131072):
-        plain = kvq.kvq_decode_workspace_bytes(4, 8, 2, 64, maxlen, 0)
-        win = kvq.kvq_decode_windowed_workspace_bytes(4, 8, 2, 64, maxlen, 0)
-        row = 4 * 8 * (64 + 2) * 4
-        assert win == (plain if plain else row) + row
+        for s in (0, 2, 5):
+            plain = kvq.kvq_decode_workspace_bytes(4, 8, 2, 64, maxlen, s)
+            win = kvq.kvq_decode_windowed_workspace_bytes(4, 8, 2, 64, maxlen, s)
+            assert win == (plain if plain else row) + row
 
 
 # ---------------------------------------------------------------- binding checks

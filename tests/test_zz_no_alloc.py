@@ -22,13 +22,16 @@ FAKE = 1 << 20
 def test_noalloc_refuses_oversized_plans_on_the_host():
     """Batch 256 of 64 query heads cut into 8 splits needs 68 MB of partials,
     more than the 64 MiB scratch: refused with KVQ_ERR_WORKSPACE_TOO_SMALL
-    (no GPU involved; nothing is launched)."""
-    need = kvq.kvq_decode_workspace_bytes(256, 64, 8, 128, 32768, 0)
+    (no GPU involved; nothing is launched).  The automatic plan of the same
+    batch (stream-K partials, two per range) fits."""
+    need = kvq.kvq_decode_workspace_bytes(256, 64, 8, 128, 32768, 8)
     assert need > kvq.NOALLOC_SCRATCH_BYTES
+    stream_need = 256 * 2 * 64 * (128 + 2) * 4 + 256 * 8   # 2048 ranges x heads, 2 slots each
+    assert stream_need <= kvq.NOALLOC_SCRATCH_BYTES
     desc = kvq._QuantDesc(FAKE, 100000, 16, 8, 128, 64)
     L = kvq.lib()
     st = L.kvq_decode_attn_noalloc(C.byref(desc), FAKE, kvq.KVQ_BF16, 64, FAKE, 2048, FAKE, 256, 32768,
-                                   0.088, 0, FAKE, None)
+                                   0.088, 8, FAKE, None)
     assert st == kvq.KVQ_ERR_WORKSPACE_TOO_SMALL
     assert b"static scratch" in L.kvq_last_error()
 
