@@ -26,8 +26,11 @@ only the concurrency sweep; ``--mode serving --batch B --cache C`` the
 70B-shaped serving step of one batch size and cache kind; ``--mode variant
 --cache C`` one decode variant (int8, int4g64, mxfp4, windowed, bf16) on the
 headline workload; ``--mode ceiling`` what the memory system gives the
-path's access patterns (probe kernels); ``--mode copy`` runs a plain 1 GiB
-device copy used to calibrate the FETCH_SIZE / WRITE_SIZE counters.
+path's access patterns (probe kernels); ``--mode quality`` the accuracy
+report alone (reconstruction and attention error of every cache kind on the
+prefill, long-context and serving data; also in the full line); ``--mode
+copy`` runs a plain 1 GiB device copy used to calibrate the FETCH_SIZE /
+WRITE_SIZE counters.
 """
 from __future__ import annotations
 
@@ -679,13 +682,202 @@ def _cpu_model():
     return platform.machine()
 
 
+# ---------------------------------------------------------------- accuracy
+# What each cache does to the numbers, measured from the library's own pools:
+# the stored codes and sidecars of a sample of tokens decoded here in torch
+# from the page layouts the header documents (not through the test oracle),
+# and each cache's decode attention against the bf16-KV decode of the same
+# tokens.
+
+def hadamard_rotate(torch, x, block):
+    """x [..., D] in the basis a pool of Hadamard block b stores:
+    blockdiag(H_b) / sqrt(b) x with H_b in Sylvester order (H_1 = [1],
+    H_2n = [[H, H], [H, -H]]); b = 0 leaves x as it is."""
+    if block == 0:
+        return x
+    h = torch.ones((1, 1), dtype=torch.float64, device=x.device)
+    while h.shape[0] < block:
+        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+    h = (h / math.sqrt(block)).to(torch.float32)
+    shp = x.shape
+    return (x.reshape(*shp[:-1], shp[-1] // block, block) @ h).reshape(shp)
+
+
+_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def dequant_pool(torch, kind, cache, slots, group=64):
+    """K and V [n][Hkv][D] (fp32, the pool's basis) of the tokens in `slots`
+    (int64 tensor on the pool's device), read from the pool bytes: kind
+    int4 (token-wise INT4, also the scale-search pool), int8, int4g (grouped,
+    |scale| as the decode takes it) or mxfp4."""
+    P, D, hkv = 16, cache.head_dim, cache.num_kv_heads
+    pool = cache.pool.view(cache.num_pages, hkv, -1)
+    dev = pool.device
+    page, off = slots // P, slots % P
+    S = pool[page]                                    # [n][Hkv][slab]
+    n = S.shape[0]
+    ar = lambda m: torch.arange(m, device=dev)
+
+    def take(idx):                                    # byte offsets [n][m] -> [n][Hkv][m]
+        return torch.gather(S, 2, idx[:, None, :].expand(-1, hkv, -1)).long()
+
+    def nibbles(b):                                   # [..., m] bytes -> [..., 2m], low nibble first
+        return torch.stack([b & 15, b >> 4], -1).reshape(*b.shape[:-1], -1)
+
+    def halves(base):                                 # fp16 (scale, zero) at byte base + [0, 4)
+        b = take(base[:, None] + ar(4)[None, :]).to(torch.uint8)
+        return b.contiguous().view(torch.float16).float()   # [n][Hkv][2]
+
+    def grouped_v(codes_at):                          # word w*P + t: channels w + (D/8) j
+        w = ar(D // 8)
+        idx = codes_at + 4 * (w[None, :, None] * P + off[:, None, None]) + ar(4)[None, None, :]
+        nib = nibbles(take(idx.reshape(n, -1)).reshape(n, hkv, D // 8, 4))   # [n][Hkv][D/8][8]
+        return nib.transpose(2, 3).reshape(n, hkv, D)
+
+    if kind in ("int4", "int4g", "mxfp4"):
+        kc = nibbles(take(off[:, None] * (D // 2) + ar(D // 2)[None, :]))
+    if kind == "int4":
+        w = ar(D // 8)
+        idx = P * D // 2 + 4 * (w[None, :, None] * P + off[:, None, None]) + ar(4)[None, None, :]
+        vc = nibbles(take(idx.reshape(n, -1)))
+        ks, vs = halves(P * D + 4 * off), halves(P * D + 4 * P + 4 * off)
+        return (kc * ks[..., :1] + ks[..., 1:], vc * vs[..., :1] + vs[..., 1:])
+    if kind == "int8":
+        kc = take(off[:, None] * D + ar(D)[None, :])
+        w, h = ar(D // 8), ar(2)
+        word = (w[:, None] * P + off[:, None, None]) * 2 + h[None, :]     # [n][D/8][2]
+        vc = take((P * D + 4 * word[..., None] + ar(4)).reshape(n, -1))
+        ks, vs = halves(2 * P * D + 4 * off), halves(2 * P * D + 4 * P + 4 * off)
+        return (kc * ks[..., :1] + ks[..., 1:], vc * vs[..., :1] + vs[..., 1:])
+    vc = grouped_v(P * D // 2)
+    if kind == "int4g":
+        ng = D // group
+
+        def side(base):   # (scale, zero) of token t, group i at base + 4 (t * ng + i)
+            start = base + 4 * (off[:, None] * ng + ar(ng)[None, :])          # [n][ng]
+            b = take((start[..., None] + ar(4)).reshape(n, -1)).to(torch.uint8).reshape(n, hkv, ng, 4)
+            return b.contiguous().view(torch.float16).float()                 # [n][Hkv][ng][2]
+
+        ks, vs = side(P * D), side(P * D + 4 * P * ng)
+
+        def apply(c, sz):
+            c = c.float().reshape(n, hkv, ng, group)
+            return (c * sz[..., :1].abs() + sz[..., 1:]).reshape(n, hkv, D)
+
+        return apply(kc, ks), apply(vc, vs)
+    # mxfp4: E2M1 codes, one E8M0 exponent per 32 channels
+    lut = torch.tensor(_E2M1, device=dev)
+
+    def e2m1(c):
+        return lut[c & 7] * torch.where((c & 8) != 0, -1.0, 1.0)
+
+    nb = D // 32
+
+    def scales(base):
+        e = take(base + off[:, None] * nb + ar(nb)[None, :]).float()
+        return torch.exp2(e - 127.0).repeat_interleave(32, dim=2)
+
+    return e2m1(kc) * scales(P * D), e2m1(vc) * scales(P * D + P * D // 32)
+
+
+QUALITY_CACHES = (
+    # name, pool kind, Hadamard block, append entry, decode entry
+    ("int4_plain", "int4", 0, "kvq_append_paged", "kvq_decode_attn"),
+    ("int4_block64", "int4", 64, "kvq_append_paged", "kvq_decode_attn"),
+    ("int4_block64_key_search", "int4", 64, "kvq_append_paged_int4_search", "kvq_decode_attn"),
+    ("int4_groups64_block64", "int4g", 64, "kvq_append_paged_int4g", "kvq_decode_attn_int4g"),
+    ("int4_groups64_block64_hybrid", "int4g", 64, "kvq_append_paged_int4g_hybrid", "kvq_decode_attn_int4g"),
+    ("int8_block64", "int8", 64, "kvq_append_paged_int8", "kvq_decode_attn_int8"),
+    ("mxfp4_block64", "mxfp4", 64, "kvq_append_paged_mxfp4", "kvq_decode_attn_mxfp4"),
+)
+
+
+def quality_of(torch, kvq, name, k, v, slot_mapping, num_pages, hq, q, block_table, seq_lens,
+               max_seq_len, sample=8192, seed=11):
+    """Reconstruction and attention error of every cache kind on one set of
+    tokens: relative MSE of K and V (sum of squared errors over the sample /
+    sum of squares of the input; the rotation is orthonormal, so this equals
+    the error in the original basis) and the decode output's relative L2 and
+    largest absolute difference from the bf16-KV decode."""
+    hkv, d = k.shape[1], k.shape[2]
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    pick = torch.randperm(k.shape[0], generator=g)[:sample].to(k.device)
+    keep = slot_mapping[pick] >= 0
+    pick = pick[keep]
+    slots = slot_mapping[pick].long()
+    bt = block_table
+    ref_cache = kvq.Bf16Cache(num_pages, hkv, d, "cuda")
+    kvq.kvq_append_paged_bf16(ref_cache, k, v, slot_mapping)
+    ref = kvq.kvq_decode_attn_bf16(ref_cache, q, bt, seq_lens, max_seq_len)
+    del ref_cache
+    xk, xv = k[pick].float(), v[pick].float()
+    res = {"workload": name, "tokens_sampled": int(pick.numel())}
+    for cname, kind, blk, app, dec in QUALITY_CACHES:
+        if kind == "int4":
+            cache = kvq.Int4Cache(num_pages, hkv, d, blk, "cuda")
+        elif kind == "int8":
+            cache = kvq.Int8Cache(num_pages, hkv, d, blk, "cuda")
+        elif kind == "int4g":
+            cache = kvq.Int4GroupedCache(num_pages, hkv, d, blk, 64, "cuda")
+        else:
+            cache = kvq.MxFp4Cache(num_pages, hkv, d, blk, "cuda")
+        getattr(kvq, app)(cache, k, v, slot_mapping)
+        dk, dv = dequant_pool(torch, kind, cache, slots)
+        rk, rv = hadamard_rotate(torch, xk, blk), hadamard_rotate(torch, xv, blk)
+        out = getattr(kvq, dec)(cache, q, bt, seq_lens, max_seq_len)
+        torch.cuda.synchronize()
+        res[cname] = {
+            "k_rel_mse": float(((dk - rk) ** 2).sum() / (xk ** 2).sum()),
+            "v_rel_mse": float(((dv - rv) ** 2).sum() / (xv ** 2).sum()),
+            "attn_rel_l2": float((out - ref).norm() / ref.norm()),
+            "attn_max_abs": float((out - ref).abs().max()),
+        }
+        del cache
+    torch.cuda.empty_cache()
+    return res
+
+
+def quality_report(torch, kvq, workloads):
+    """The accuracy of every cache kind on the prefill (Student-t), the
+    long-context (per-channel scales) and the 70B-shaped serving (lognormal
+    lengths) data; the prefill has no queries, so its attention uses 32
+    query heads (GQA 4) drawn N(0, 1) from a fixed seed."""
+    rep = {}
+    pw = workloads.prefill_append(PREFILL_SEEDS[0], device="cuda", block=64)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    q = torch.randn((pw.batch, 32, pw.d), generator=g, device="cuda").to(torch.bfloat16)
+    rep["prefill_student_t"] = quality_of(
+        torch, kvq, "32768 tokens over 16 sequences, 8 kv heads, head_dim 128, bf16 Student-t(3); "
+        "32 query heads N(0,1)", pw.k, pw.v, pw.slot_mapping, pw.num_pages, 32, q,
+        torch.from_numpy(pw.block_table).cuda(), torch.from_numpy(pw.seq_lens).cuda(), pw.max_seq_len)
+    del pw
+    lw = workloads.long_context_decode(4, device="cuda", batch=8, context=131072, block=64)
+    rep["long_context_channel_scales"] = quality_of(
+        torch, kvq, "8 x 131072 tokens, 32 q / 8 kv heads, head_dim 128, per-channel scales in [0.1, 10]",
+        lw.k, lw.v, lw.slot_mapping, lw.num_pages, lw.hq, lw.q, torch.from_numpy(lw.block_table).cuda(),
+        torch.from_numpy(lw.seq_lens).cuda(), lw.max_seq_len)
+    del lw
+    torch.cuda.empty_cache()
+    fill, st = workloads.concurrency_step(5, device="cuda", batch=32, block=64, steps=1)
+    s0 = st[0]
+    k = torch.cat([fill.k, s0.k]).contiguous()
+    v = torch.cat([fill.v, s0.v]).contiguous()
+    sm = torch.cat([fill.slot_mapping, s0.slot_mapping]).contiguous()
+    rep["serving_70b_lognormal"] = quality_of(
+        torch, kvq, "batch 32, lognormal contexts (median 2048, cap 32768) + 1 step, 64 q / 8 kv heads, "
+        "head_dim 128", k, v, sm, s0.num_pages, s0.hq, s0.q, torch.from_numpy(s0.block_table).cuda(),
+        torch.from_numpy(s0.seq_lens).cuda(), s0.max_seq_len)
+    return rep
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--mode", choices=["full", "decode", "prefill", "copy", "concurrency", "serving",
-                                       "variant", "ceiling"], default="full")
+                                       "variant", "ceiling", "quality"], default="full")
     ap.add_argument("--batch", type=int, default=256, help="serving mode: batch size")
     ap.add_argument("--cache", default="int4_block64",
                     help="serving mode: int4_block64, int4_plain or bf16; variant mode: int8, "
@@ -715,6 +907,10 @@ def main(argv=None):
 
     if args.mode == "ceiling":
         print(json.dumps({"mode": "ceiling", **ceiling_mode(torch)}))
+        return 0
+
+    if args.mode == "quality":
+        print(json.dumps({"mode": "quality", **quality_report(torch, kvq, workloads)}))
         return 0
 
     if args.mode == "serving":
@@ -832,6 +1028,8 @@ def main(argv=None):
     torch.cuda.empty_cache()
     long_ctx = long_context_rate(torch, kvq, workloads)
     conc = concurrency_sweep(torch, kvq, workloads)
+    torch.cuda.empty_cache()
+    quality = quality_report(torch, kvq, workloads)
 
     traffic = _traffic(dec_bytes)
     line = {
@@ -875,6 +1073,7 @@ def main(argv=None):
         "mxfp4": mxfp4,
         "long_context_decode": long_ctx,
         "concurrency_sweep": conc,
+        "quality": quality,
         "bf16_kv": {"gb_s": round(bf16_bytes / (ms_bf16 * 1e-3) / 1e9, 1),
                     "us": round(ms_bf16 * 1e3, 2), "bytes": bf16_bytes,
                     "int4_speedup": round(ms_bf16 / dec_mean, 3)},
@@ -884,7 +1083,7 @@ def main(argv=None):
             "kernel_us_back_to_back": round(dec_b2b_ms * 1e3, 2),
             "frac_kernel": round(dec_bytes / (dec_b2b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_quant_kernel<128, 1, true, 4, 0, 1, false> (one kvq_decode_attn call; at this shape the split "
+            "kernel": "decode_quant_kernel<128, 1, true, 4, 0, 1, 0> (one kvq_decode_attn call; at this shape the split "
                       "plan is one split per (sequence, KV head), so no reduce kernel runs)",
         },
     }
