@@ -109,6 +109,18 @@ def _traffic(alg_bytes: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _time_back_to_back(torch, fn, iters):
+    """Mean ms per call of iters consecutive calls of fn() between one pair of
+    HIP events on the current stream (no event between the calls)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
 def _time_events(torch, fn, iters):
     """Mean ms of fn() over iters launches, HIP events on the current stream."""
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
@@ -190,7 +202,11 @@ def prefill_rates(torch, kvq, workloads, blocks=(64, 0), iters=50, chunk=10):
     """Rotate+quantize append of 32768 ragged tokens (8 KV heads, d 128) into a
     page-16 pool, for each Hadamard block in ``blocks``: Mtokens/s and GB/s
     over PREFILL_RING input/cache sets.  The blocks are timed in alternating runs of
-    ``chunk`` calls so that they see the same clocks."""
+    ``chunk`` consecutive calls so that they see the same clocks: ``us`` is the
+    mean per call of a run timed as a whole (one event pair around the run,
+    as a prefill appends layer after layer), ``us_per_call_events`` the mean
+    with an event pair around every call (which adds the events' gap between
+    calls)."""
     sets = {}
     for blk in blocks:
         sets[blk] = []
@@ -206,19 +222,24 @@ def prefill_rates(torch, kvq, workloads, blocks=(64, 0), iters=50, chunk=10):
         for i in range(10):
             run(blk, i)
     tot = {blk: [] for blk in blocks}
+    per_call = {blk: [] for blk in blocks}
     for i0 in range(0, iters, chunk):
         for blk in blocks:
             n = min(chunk, iters - i0)
+            tot[blk].append((_time_back_to_back(torch, lambda i: run(blk, i0 + i), n), n))
+        for blk in blocks:
+            n = min(chunk, iters - i0)
             mean_ms, _ = _time_events(torch, lambda i: run(blk, i0 + i), n)
-            tot[blk].append((mean_ms, n))
+            per_call[blk].append((mean_ms, n))
     res = {}
     for blk in blocks:
         mean_ms = sum(m * n for m, n in tot[blk]) / sum(n for _, n in tot[blk])
+        ev_ms = sum(m * n for m, n in per_call[blk]) / sum(n for _, n in per_call[blk])
         w = sets[blk][0][0]
         tok = w.num_tokens
         nbytes = append_bytes(tok, w.hkv, w.d, int4_bytes_per_vector(w.d))
         res[blk] = {"mtok_s": tok / (mean_ms * 1e-3) / 1e6, "gb_s": nbytes / (mean_ms * 1e-3) / 1e9,
-                    "us": mean_ms * 1e3, "bytes": nbytes, "tokens": tok}
+                    "us": mean_ms * 1e3, "us_per_call_events": ev_ms * 1e3, "bytes": nbytes, "tokens": tok}
     return res
 
 
@@ -272,7 +293,8 @@ def windowed_rate(torch, kvq, workloads, db, iters, plain_gb_s, plain_bytes, w_s
 def variant_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes, kind):
     """A cache variant on the headline workload (Hadamard block 64):
     decode-only loop over two cache copies, and the prefill append of 32768
-    ragged tokens over two input/cache sets.  kind "int8": token-wise INT8
+    ragged tokens over PREFILL_RING input/cache sets (consecutive calls timed
+    as a whole).  kind "int8": token-wise INT8
     (D code bytes + 4 sidecar bytes per vector); "int4g64": INT4 with one
     scale/zero per 64 channels (D/2 + 4 D/64 bytes); "mxfp4": E2M1 codes with
     one E8M0 byte per 32 channels (D/2 + D/32 bytes)."""
@@ -315,7 +337,7 @@ def variant_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes, kind)
 
     for i in range(10):
         app(i)
-    ms, _ = _time_events(torch, app, iters)
+    ms = _time_back_to_back(torch, app, iters)   # consecutive appends, as the headline prefill
     pw = sets[0][0]
     abytes = append_bytes(pw.num_tokens, pw.hkv, pw.d, vec_bytes)
     res["prefill_append"] = {"us": round(ms * 1e3, 2), "mtok_s": round(pw.num_tokens / (ms * 1e-3) / 1e6, 1),

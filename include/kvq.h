@@ -268,8 +268,13 @@ kvq_status kvq_decode_attn_noalloc(const kvq_int4_cache* cache, const void* q, k
                                    int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
                                    void* stream);
 
-/* Workspace bytes the decodes of this header need for these arguments (0
- * allowed): the larger of the planned splits' partials and, where the
+/* kvq_decode_workspace_bytes -- workspace of the split-K decode.  No passage
+ * of the pages fixes how a decode is partitioned: splitting a sequence's
+ * pages over workgroups and merging their partial softmax states (maximum,
+ * sum, unnormalised output) by the log-sum-exp rule is this library's
+ * design for long contexts and ragged batches, and the workspace holds
+ * those partials.  Bytes the decodes of this header need for these
+ * arguments (0 allowed): the larger of the planned splits' partials and, where the
  * stream-K mapping applies (num_splits 0, see kvq_decode_attn), its
  * partials -- (head_dim + 2) floats for two slots per query head and range
  * of a grid of at most 2048 workgroups rounded up to whole KV heads -- and
@@ -427,13 +432,25 @@ kvq_status kvq_decode_attn_mxfp4(const kvq_mxfp4_cache* cache, const void* q, kv
                                  int32_t max_seq_len, float sm_scale, int32_t num_splits, float* out,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* bf16 baseline of kvq_append_paged: copies K and V (fp16 input is rounded
- * to bf16, nearest even) into the bf16 pool.  Same argument rules. */
+/*
+ * kvq_append_paged_bf16 / kvq_decode_attn_bf16 -- the unquantized baseline
+ * the quantized caches are measured against ("InnerQ", Table 4: the FP16
+ * GEMV kernel as the latency baseline of the fused dequantize kernels;
+ * "BitDecoding-FP4", Abstract: accuracy and serving throughput stated
+ * relative to a BF16 KV cache).  Here the baseline cache holds bf16 (half
+ * the bytes of fp32, the same as fp16) in the bf16 pool layout above.
+ *
+ * kvq_append_paged_bf16 copies K and V into the bf16 pool (fp16 input is
+ * rounded to bf16, nearest even); same argument rules as kvq_append_paged.
+ */
 kvq_status kvq_append_paged_bf16(const kvq_bf16_cache* cache, const void* k, const void* v,
                                  kvq_dtype dtype, int64_t token_stride,
                                  const int32_t* slot_mapping, int32_t num_tokens, void* stream);
 
-/* bf16 baseline of kvq_decode_attn (no rotation).  Same argument rules. */
+/* kvq_decode_attn_bf16: kvq_decode_attn over the bf16 pool (no rotation,
+ * no dequantization: exact attention over the stored bf16 values up to fp32
+ * rounding).  Same argument rules and workspace size; it always takes the
+ * planned split mapping. */
 kvq_status kvq_decode_attn_bf16(const kvq_bf16_cache* cache, const void* q, kvq_dtype dtype,
                                 int32_t num_q_heads, const int32_t* block_table,
                                 int32_t max_pages_per_seq, const int32_t* seq_lens,
