@@ -24,7 +24,7 @@ def _setup(kind, fill):
     return cache, fns
 
 
-@pytest.mark.parametrize("batch", [1, 8])
+@pytest.mark.parametrize("batch", [1, 8, 32])
 @pytest.mark.parametrize("kind", ["int4_rot", "int4_plain", "bf16"])
 def test_graph_replay_matches_eager(kind, batch):
     fill, st = workloads.concurrency_step(5, device=DEV, batch=batch, block=64, steps=3)
