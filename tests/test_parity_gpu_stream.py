@@ -185,3 +185,32 @@ def test_stream_repeated_calls_are_identical():
                        w.slot_mapping.numpy())
     want_b = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table, lens_b, w.sm_scale)
     _close(outs[1].astype(np.float64), want_b, "stream call 2")
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_stream_random_ragged_batches(seed):
+    """Seeded random batches that take the stream-K mapping: 64 to 160
+    sequences over 4 KV heads, GQA 4 or 8, rotated or not, lognormal lengths
+    with zeros, single tokens and one sequence past 4096 tokens, and a few
+    absent pages; range ends then fall at many places relative to sequence
+    and page boundaries."""
+    rng = np.random.default_rng(1000 + seed)
+    batch = int(rng.integers(64, 161))
+    hq = int(rng.choice([16, 32]))
+    block = int(rng.choice([0, 64]))
+    lens = np.clip(np.round(np.exp(rng.normal(math.log(150.0), 1.2, batch))), 0, 2500).astype(np.int32)
+    lens[rng.integers(0, batch, 3)] = 0
+    lens[rng.integers(0, batch, 3)] = 1
+    lens[int(rng.integers(0, batch))] = int(rng.integers(4200, 9000))
+    w = workloads.random_decode(70 + seed, batch=batch, hq=hq, hkv=4, d=128, block=block, seq_lens=lens)
+    assert _streamed(batch, 4, w.max_seq_len)
+    print(f"stream random seed {seed}: B{batch} hq{hq} b{block} max {w.max_seq_len} "
+          f"tokens {int(lens.sum())}", flush=True)
+    bt = w.block_table.copy()
+    for _ in range(4):   # absent pages inside some sequences' ranges
+        b = int(rng.integers(0, batch))
+        npg = (int(lens[b]) + 15) // 16
+        if npg:
+            bt[b][int(rng.integers(0, npg))] = -1 if rng.random() < 0.5 else w.num_pages + 3
+    cache, dec, want = _run("int4", w, bt)
+    _close(_decode(dec, cache, w, bt), want, f"stream random seed {seed}")
