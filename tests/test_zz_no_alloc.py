@@ -70,3 +70,43 @@ def test_noalloc_equals_the_workspace_entry_point_twice():
         rel = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)
         print(f"[noalloc seed {seed}] max-abs {err.max():.3e} rel-L2 {rel:.3e}", flush=True)
         assert err.max() <= 2e-3 and rel <= 1e-3
+
+
+@pytest.mark.gpu
+def test_noalloc_stream_k_plan_twice():
+    """The automatic plan of a batch of 256 (sequence, KV head) pairs whose
+    longest sequence is cut takes the stream-K mapping: its partials and the
+    merge's per-sequence records go to the static scratch in that layout.
+    Bit-identical to kvq_decode_attn on two calls in a row, the second with a
+    smaller batch (the first call's records stay in the scratch), and within
+    the tolerance of the oracle."""
+    oracle.build(force=False)
+    rng = np.random.default_rng(17)
+    for batch in (72, 64):   # the second is smaller
+        lens = np.clip(np.round(np.exp(rng.normal(np.log(200.0), 1.0, batch))), 1, 2000).astype(np.int32)
+        lens[5] = 0
+        lens[9] = 6000
+        w = workloads.random_decode(64 + batch, batch=batch, hq=16, hkv=4, d=128, block=64, seq_lens=lens)
+        assert batch * w.hkv >= 256 and (w.max_seq_len + 15) // 16 > 256   # the stream-K rule
+        cache = kvq.Int4Cache(w.num_pages, w.hkv, w.d, 64, DEV)
+        kvq.kvq_append_paged(cache, w.k.to(DEV), w.v.to(DEV), w.slot_mapping.to(DEV))
+        pool = oracle.new_int4_pool(w.num_pages, w.hkv, w.d)
+        oracle.append_int4(pool, w.num_pages, w.hkv, w.d, 64, bits(w.k), bits(w.v), oracle.BF16,
+                           w.slot_mapping.numpy())
+        want = oracle.decode_int4(pool, w.hkv, w.d, 64, bits(w.q), oracle.BF16, w.block_table, w.seq_lens,
+                                  w.sm_scale)
+        q = w.q.to(DEV)
+        bt = torch.from_numpy(w.block_table).to(DEV)
+        sl = torch.from_numpy(w.seq_lens).to(DEV)
+        out_na = torch.full((w.batch, w.hq, w.d), float("nan"), dtype=torch.float32, device=DEV)
+        torch.cuda.synchronize()
+        print(f"noalloc stream-K batch {batch}", flush=True)
+        kvq.kvq_decode_attn_noalloc(cache, q, bt, sl, w.max_seq_len, w.sm_scale, out=out_na)
+        ref = kvq.kvq_decode_attn(cache, q, bt, sl, w.max_seq_len, w.sm_scale)
+        torch.cuda.synchronize()
+        got, ref = out_na.cpu().numpy(), ref.cpu().numpy()
+        assert np.array_equal(got, ref), f"batch {batch}: differs from kvq_decode_attn"
+        err = np.abs(got.astype(np.float64) - want)
+        rel = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)
+        print(f"[noalloc stream-K batch {batch}] max-abs {err.max():.3e} rel-L2 {rel:.3e}", flush=True)
+        assert err.max() <= 2e-3 and rel <= 1e-3
