@@ -148,8 +148,11 @@ size_t workspace_bytes(int32_t batch, int32_t hq, int32_t d, const SplitPlan& p)
 // and the merge's record of each sequence.
 bool stream_call(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t num_splits) {
   const int64_t pages_max = (static_cast<int64_t>(max_seq_len) + 15) / 16;
+  // the run of a KV head (pages plus a fixed cost per sequence) stays far
+  // inside the device's 32-bit arithmetic
+  const int64_t cost = std::max(kStreamItemCost1, kStreamItemCost2);
   return num_splits == 0 && static_cast<int64_t>(batch) * hkv >= 256 &&
-         static_cast<int64_t>(batch) * pages_max < (int64_t{1} << 30) &&
+         static_cast<int64_t>(batch) * (pages_max + cost) < (int64_t{1} << 30) &&
          plan_splits(batch, hkv, max_seq_len, 0).nsplit > 1;
 }
 
@@ -218,11 +221,12 @@ kvq_status launch_decode(Pool kind, const void* pool, int32_t num_pages, int32_t
   if (use_sk) {
     const int bits = kind == Pool::kInt8 ? 8 : 4;
     const int gs = kind == Pool::kInt4g ? group : 0;
-    int32_t ranges = 0;
-    hipError_t e = stream_ranges(a, bits, gs, &ranges);
+    int32_t ranges = 0, per_slot = 1;
+    hipError_t e = stream_ranges(a, bits, gs, &ranges, &per_slot);
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
     const int64_t slots = stream_slots(hq, hkv);
     a.sk_ranges = ranges;
+    a.sk_per_slot = per_slot;
     a.part_acc = static_cast<float*>(workspace);
     a.part_ml = static_cast<float*>(workspace) + slots * d;
     a.sk_rec = reinterpret_cast<int32_t*>(static_cast<float*>(workspace) + slots * (d + 2));

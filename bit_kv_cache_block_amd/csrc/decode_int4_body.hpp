@@ -872,33 +872,42 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
     run(kvh, hq0, bt_s, q0, p1, lo, hi, direct, hq0 * a.part_stride + a.part_slot0 + s, a.part_stride, qraw,
         idA, cb, grown, tid, wave);
   } else {
-    // Stream-K: the pages of the batch, sequence after sequence, form one
-    // run of T pages per KV head, cut into sk_ranges ranges of R pages;
-    // workgroup wid takes range wid / num_kv_heads of KV head wid %
-    // num_kv_heads and walks the sequences that meet it.  Every workgroup
-    // gets the same number of pages whatever the lengths (a ragged batch
-    // leaves no workgroup idle and none with a long tail), and none exists
-    // for pages that are not there.  A sequence inside one range is
-    // finished there; one cut by range ends leaves a partial per range it
-    // meets: slot 0 of the range for the piece at the range's start, slot 1
-    // for a piece that starts later (then it runs to the range's end).
+    // Stream-K: the sequences of the batch, one after another, each as a
+    // fixed cost and then its pages, form one run per KV head, cut into
+    // sk_ranges ranges; workgroup wid takes range wid / num_kv_heads of KV
+    // head wid % num_kv_heads and walks the sequences that meet it.  The
+    // ranges are sized for the time the workgroups of each dispatch slot
+    // take (stream_range), whatever the lengths: pages, plus what a
+    // workgroup spends on each sequence whatever its length (the cost, in
+    // pages, of its query prologue, its merge and its last step's unused
+    // page slots), so a range of many short sequences holds fewer pages.  A
+    // sequence inside one range is finished there; one cut by range ends
+    // leaves a partial per range it meets: slot 0 of the range for the piece
+    // at the range's start, slot 1 for a piece that starts later (then it
+    // runs to the range's end).
+    constexpr int kItemCost = NS == 2 ? kStreamItemCost2 : kStreamItemCost1;
+    constexpr int kSkew = NS == 1 ? kStreamSkew1 : kStreamSkew2;
     const int kvh = static_cast<int>(wid % a.num_kv_heads);
     const int r = static_cast<int>(wid / a.num_kv_heads);
-    const StreamRange rg = stream_range(a.seq_lens, a.batch, a.max_seq_len, a.sk_ranges, r);
-    if (rg.first >= rg.end) return;   // past the batch's pages (wave-uniform)
+    const StreamRange rg = stream_range(a.seq_lens, a.batch, a.max_seq_len, a.sk_ranges, a.sk_per_slot, kSkew, r,
+                                        kItemCost);
+    if (rg.first >= rg.end) return;   // past the batch's work (wave-uniform)
     int b = rg.b, sb = rg.start_b;
     bool later = false;
     int32_t idA[kStep] = {0, 0, 0, 0};
-    while (sb < rg.end) {   // sb < T: b < batch
+    while (sb < rg.end) {   // sb < total: b < batch
       int len = a.seq_lens[b];
       len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
       const int np = (len + kPage - 1) / kPage;
-      if (np > 0) {
-        const int s0 = max(sb, rg.first), s1 = min(sb + np, rg.end);
-        if (kvh == 0 && s0 == sb && tid == 0) {   // the merge's record of the sequence
-          const int rf = sb / rg.pages, rl = (sb + np - 1) / rg.pages;
-          a.sk_rec[2 * b] = rf;
-          a.sk_rec[2 * b + 1] = 2 * (rl - rf + 1) + (sb != rf * rg.pages ? 1 : 0);
+      const int sp0 = sb + kItemCost;   // the sequence's first page in the run
+      const int s0 = max(sp0, rg.first), s1 = min(sp0 + np, rg.end);
+      if (np > 0 && s0 < s1) {
+        if (kvh == 0 && s0 == sp0) {   // the merge's record of the sequence (its first range is r)
+          const int rl = stream_range_of(rg, sp0 + np - 1);
+          if (tid == 0) {
+            a.sk_rec[2 * b] = r;
+            a.sk_rec[2 * b + 1] = 2 * (rl - r + 1) + (sp0 != rg.first ? 1 : 0);
+          }
         }
         if (later) __syncthreads();   // the last item's merge is done with the LDS
         later = true;
@@ -906,15 +915,15 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
         uint32_t qraw[kC / 2];
         load_query(hq0, qraw);
         ConstI32* bt_s = (ConstI32*)(a.block_table + static_cast<int64_t>(b) * a.bt_stride);
-        const bool whole = s0 == sb && s1 == sb + np;
+        const bool whole = s0 == sp0 && s1 == sp0 + np;
         const int64_t slot = ((static_cast<int64_t>(kvh) * a.sk_ranges + r) * 2 + (s0 == rg.first ? 0 : 1)) * G;
         // values that depend on the thread alone are computed again for each
         // item rather than held (in registers, or spilled) across the walk
         int tid_l = tid, wave_l = wave;
         asm volatile("" : "+v"(tid_l), "+s"(wave_l));
-        run(kvh, hq0, bt_s, s0 - sb, s1 - sb, 0, len, whole, slot, 1, qraw, idA, -1, false, tid_l, wave_l);
+        run(kvh, hq0, bt_s, s0 - sp0, s1 - sp0, 0, len, whole, slot, 1, qraw, idA, -1, false, tid_l, wave_l);
       }
-      sb += np;
+      sb += np > 0 ? np + kItemCost : 0;
       ++b;
     }
   }

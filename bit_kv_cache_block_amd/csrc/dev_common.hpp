@@ -197,43 +197,90 @@ __device__ __forceinline__ int balanced_split_pages(int sp, const int32_t* seq_l
   return even > sp ? static_cast<int>(even) : sp;
 }
 
-// Stream-K range r of a batch (the plain INT4-family decode): the pages of
-// the sequences, one after another (ceil(len / 16) each, len clamped to
-// [0, max_seq_len]), form a run of T pages, cut into ranges of
-// pages = max(16, ceil(T / ranges)); range r is [first, end).  b is the
-// sequence holding page `first` and start_b that sequence's first page in the
-// run (first >= end: the range is empty, b and start_b unset).  Every lane of
-// the wave takes part; the results are wave-uniform.
+// Stream-K cut of a batch (the plain INT4-family decode).  The sequences,
+// one after another, each as item_cost units and then its ceil(len / 16)
+// pages (len clamped to [0, max_seq_len]; nothing for an empty sequence),
+// form a run of `total` units per KV head, cut into `nr` ranges, one per
+// workgroup, so that a range's work is its pages plus a fixed cost for each
+// sequence that starts in it.
+//   The ranges are not equal.  The workgroups of one launch that share a CU
+// all start at once (range r's workgroups are dispatched in slot r / rs of
+// their CUs), and on equal priority a SIMD issues from its oldest wave
+// first: with equal ranges the workgroups of the first slot finished long
+// before those of the last, and the kernel waited for these.  So slot k of
+// `occ` weighs 64 + skew * (occ - 1 - k) (in 64ths of a range): each slot's
+// ranges take the share its workgroups get through in the same time.  A
+// small run (under 64 units a range) is cut into equal ranges of
+// max(16, ceil(total / nr)) units instead (`unit`), trailing ones empty.
+// Every lane of the wave takes part in stream_range; the results are
+// wave-uniform.
 struct StreamRange {
-  int pages, first, end, b, start_b;
+  int first, end;     // this range: units [first, end) (first >= end: empty)
+  int b, start_b;     // the first sequence meeting it, and where that sequence starts
+  int total, nr, rs, occ, skew, unit;
 };
 __device__ __forceinline__ int stream_pages_of(const int32_t* seq_lens, int b, int batch, int max_seq_len) {
   int len = b < batch ? seq_lens[b] : 0;
   len = len < 0 ? 0 : (len > max_seq_len ? max_seq_len : len);
   return (len + kPage - 1) / kPage;
 }
+__device__ __forceinline__ int stream_cost_of(const int32_t* seq_lens, int b, int batch, int max_seq_len,
+                                              int item_cost) {
+  const int np = stream_pages_of(seq_lens, b, batch, max_seq_len);
+  return np > 0 ? np + item_cost : 0;
+}
+// the weight of ranges [0, r), 0 <= r <= nr
+__device__ __forceinline__ int64_t stream_weight_before(const StreamRange& g, int r) {
+  const int k = min(r / g.rs, g.occ - 1);
+  const int64_t full = 64 * static_cast<int64_t>(k) +
+                       static_cast<int64_t>(g.skew) * (static_cast<int64_t>(k) * (g.occ - 1) - k * (k - 1) / 2);
+  return g.rs * full + static_cast<int64_t>(r - k * g.rs) * (64 + g.skew * (g.occ - 1 - k));
+}
+// the first unit of range r, 0 <= r <= nr (range nr: the run's end)
+__device__ __forceinline__ int stream_first(const StreamRange& g, int r) {
+  if (g.unit > 0) return min(r * g.unit, g.total);
+  return static_cast<int>(static_cast<int64_t>(g.total) * stream_weight_before(g, r) /
+                          stream_weight_before(g, g.nr));
+}
+// the range holding unit x, 0 <= x < total
+__device__ __forceinline__ int stream_range_of(const StreamRange& g, int x) {
+  if (g.unit > 0) return x / g.unit;
+  const int64_t wt = stream_weight_before(g, g.nr);
+  const int64_t y = static_cast<int64_t>(x) * wt / g.total;   // x's weight coordinate (rounded down)
+  int k = 0;
+  while (k + 1 < g.occ && stream_weight_before(g, (k + 1) * g.rs) <= y) ++k;
+  int r = k * g.rs + static_cast<int>((y - stream_weight_before(g, k * g.rs)) / (64 + g.skew * (g.occ - 1 - k)));
+  r = min(max(r, 0), g.nr - 1);
+  while (r > 0 && stream_first(g, r) > x) --r;
+  while (r + 1 < g.nr && stream_first(g, r + 1) <= x) ++r;
+  return r;
+}
 __device__ __forceinline__ StreamRange stream_range(const int32_t* seq_lens, int batch, int max_seq_len,
-                                                    int ranges, int r) {
+                                                    int ranges, int per_slot, int skew, int r, int item_cost) {
   const int lane = threadIdx.x & 63;
   int total = 0;
   for (int c = 0; c < batch; c += 64) {
-    int np = stream_pages_of(seq_lens, c + lane, batch, max_seq_len);
+    int np = stream_cost_of(seq_lens, c + lane, batch, max_seq_len, item_cost);
 #pragma unroll
     for (int m = 1; m < 64; m *= 2) np += __shfl_xor(np, m);
     total += np;
   }
-  total = __builtin_amdgcn_readfirstlane(total);
   StreamRange rg;
-  rg.pages = max(kPage, (total + ranges - 1) / ranges);
-  rg.first = r * rg.pages;
-  rg.end = min(rg.first + rg.pages, total);
+  rg.total = __builtin_amdgcn_readfirstlane(total);
+  rg.nr = ranges;
+  rg.rs = max(1, per_slot);
+  rg.occ = (ranges + rg.rs - 1) / rg.rs;
+  rg.skew = skew;
+  rg.unit = rg.total < 64 * ranges ? max(kPage, (rg.total + ranges - 1) / ranges) : 0;
+  rg.first = stream_first(rg, r);
+  rg.end = stream_first(rg, r + 1);
   rg.b = 0;
   rg.start_b = 0;
   if (rg.first >= rg.end) return rg;
-  // the first sequence whose pages end after `first`
+  // the first sequence whose units end after `first`
   int carry = 0;
   for (int c = 0; c < batch; c += 64) {
-    const int np = stream_pages_of(seq_lens, c + lane, batch, max_seq_len);
+    const int np = stream_cost_of(seq_lens, c + lane, batch, max_seq_len, item_cost);
     int incl = np;   // inclusive prefix over the 64 lanes
 #pragma unroll
     for (int d = 1; d < 64; d *= 2) {

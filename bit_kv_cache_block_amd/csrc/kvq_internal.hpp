@@ -78,13 +78,16 @@ struct DecodeArgs {
   int32_t balance;
   // Stream-K mapping of the plain INT4-family decode (sk_ranges > 0): the
   // batch's pages, one sequence after another, cut per KV head into
-  // sk_ranges ranges of equal length, one workgroup each.  The partial of
+  // sk_ranges ranges (stream_range), one workgroup each.  The partial of
   // (KV head, range, slot, head of the group) is at
   // ((kvh * sk_ranges + range) * 2 + slot) * G + head; sk_rec[2b] is the
   // first range sequence b meets, sk_rec[2b + 1] twice the number of ranges
   // it meets plus 1 if its piece in the first one is in slot 1 (written by
   // the decode for every sequence with pages, read by the merge).
   int32_t sk_ranges;
+  // ranges per dispatch slot (the workgroups a CU holds at once take slots
+  // 0, 1, ... of it in launch order: sk_ranges / sk_per_slot of them)
+  int32_t sk_per_slot;
   int32_t* sk_rec;
 };
 
@@ -96,6 +99,16 @@ constexpr int kMapStream = 2;
 // Stream-K: at most this many workgroups (ranges times KV heads, rounded up
 // to whole KV heads) -- the workspace is sized for it.
 constexpr int kStreamMaxWorkgroups = 2048;
+// What a stream-K workgroup spends on a sequence whatever its length (query
+// prologue, merge, the unused page slots of its last step), in pages of
+// work, for the one-set and the two-set builds: the run's cost of a sequence
+// beside its pages.
+constexpr int kStreamItemCost1 = 16;
+constexpr int kStreamItemCost2 = 20;
+// How much more range each earlier dispatch slot of a CU takes than the next
+// (64ths), one-set and two-set builds.
+constexpr int kStreamSkew1 = 24;
+constexpr int kStreamSkew2 = 24;
 
 // Split-K plan shared by the launch and the workspace query.
 struct SplitPlan {
@@ -122,8 +135,9 @@ hipError_t launch_decode_quant_balanced(const DecodeArgs& a, int bits, int gs, h
 hipError_t launch_decode_quant_stream(const DecodeArgs& a, int bits, int gs, hipStream_t s);
 // Ranges per KV head for the stream-K build of a format on the current
 // device: as many workgroups as the device holds at once, at most
-// kStreamMaxWorkgroups (rounded up to whole KV heads).
-hipError_t stream_ranges(const DecodeArgs& a, int bits, int gs, int32_t* ranges);
+// kStreamMaxWorkgroups (rounded up to whole KV heads); per_slot: the ranges
+// of one dispatch slot (ranges / workgroups per CU, rounded up).
+hipError_t stream_ranges(const DecodeArgs& a, int bits, int gs, int32_t* ranges, int32_t* per_slot);
 hipError_t launch_decode_mxfp4(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t s);

@@ -230,10 +230,12 @@ kvq_status kvq_append_paged(const kvq_int4_cache* cache, const void* k, const vo
  *               at least 256 (sequence, KV head) pairs whose longest
  *               sequence would be cut takes the stream-K mapping instead
  *               (this decode, the INT8 and the grouped INT4 ones): the
- *               batch's pages, one sequence after another, are cut per KV
- *               head into equal ranges, one per workgroup the device holds
- *               at once, and sequences met by several ranges are merged
- *               from their partials.  The partitioning changes only the
+ *               batch's pages, one sequence after another (each sequence
+ *               also counted as a fixed number of pages of work), are cut
+ *               per KV head into ranges, one per workgroup the device holds
+ *               at once (longer for the workgroups dispatched first on
+ *               each CU, which the hardware issues first), and sequences
+ *               met by several ranges are merged from their partials.  The partitioning changes only the
  *               rounding of the result.
  * out:          device fp32 [batch][num_q_heads][head_dim], 16-byte aligned.
  * workspace:    device scratch of at least kvq_decode_workspace_bytes(...)

@@ -2,8 +2,10 @@
 oracle, through the C ABI.  The automatic plan takes it for a batch of at
 least 256 (sequence, KV head) pairs whose longest sequence the plan would cut
 (here: max_seq_len above 4096, so at least two 256-page splits): the batch's
-pages, one sequence after another, are cut per KV head into equal ranges, one
-workgroup each, and a sequence met by several ranges is merged from their
+pages, one sequence after another (each also counted as a fixed cost), are
+cut per KV head into ranges, one workgroup each (equal ranges for a small
+run; for a large one, longer ranges for the workgroups dispatched first on
+each CU), and a sequence met by several ranges is merged from their
 partials.  Ragged lognormal batches with empty sequences, single-token
 sequences, absent pages and one sequence spanning many ranges; GQA 4, 8 and
 16 (one, two and four sets of heads), head_dim 64 and 128, token-wise INT4
@@ -214,3 +216,55 @@ def test_stream_random_ragged_batches(seed):
             bt[b][int(rng.integers(0, npg))] = -1 if rng.random() < 0.5 else w.num_pages + 3
     cache, dec, want = _run("int4", w, bt)
     _close(_decode(dec, cache, w, bt), want, f"stream random seed {seed}")
+
+
+def _sampled_oracle(w, bt, rows):
+    """The oracle's pool and attention for the sequences in `rows` only: their
+    tokens appended from host copies, their rows of the block table decoded."""
+    cum = np.concatenate([[0], np.cumsum(w.seq_lens.astype(np.int64))])
+    toks = np.concatenate([np.arange(cum[b], cum[b + 1]) for b in rows]).astype(np.int64)
+    sel = torch.from_numpy(toks)
+    k, v = w.k.index_select(0, sel.to(w.k.device)).cpu(), w.v.index_select(0, sel.to(w.v.device)).cpu()
+    sm = w.slot_mapping.cpu().numpy()[toks]
+    pool = oracle.new_int4_pool(w.num_pages, w.hkv, w.d)
+    oracle.append_int4(pool, w.num_pages, w.hkv, w.d, w.block, bits(k), bits(v), oracle.BF16, sm)
+    q = w.q.cpu()[torch.from_numpy(np.asarray(rows))]
+    want = oracle.decode_int4(pool, w.hkv, w.d, w.block, bits(q), oracle.BF16, np.ascontiguousarray(bt[rows]),
+                              np.ascontiguousarray(w.seq_lens[rows]), w.sm_scale)
+    return pool, want
+
+
+@pytest.mark.parametrize("hq,block", [(32, 64), (16, 128)])
+def test_stream_weighted_ranges_large_batch(hq, block):
+    """A batch large enough (at least 64 units of the run per range whatever
+    the device's occupancy: over 32768 pages per KV head) that the stream-K
+    cut gives each dispatch slot its own range length, with a sequence that
+    spans many ranges, an empty one and single-token ones.  Pages of the
+    sampled sequences bit-exact against the oracle's, their attention within
+    tolerance of the oracle's."""
+    batch, hkv = 104, 4
+    rng = np.random.default_rng(4242 + hq)
+    lens = np.clip(np.round(np.exp(rng.normal(math.log(5000.0), 0.6, batch))), 1, 20000).astype(np.int32)
+    lens[3] = 0
+    lens[5] = 1
+    lens[8] = 1
+    lens[40] = 60000
+    assert int(((lens + 15) // 16).sum()) > 32768
+    w = workloads.random_decode(80 + hq, device=DEV, batch=batch, hq=hq, hkv=hkv, d=128, block=block, seq_lens=lens)
+    assert _streamed(batch, hkv, w.max_seq_len)
+    print(f"stream weighted hq{hq} b{block}: tokens {int(lens.sum())} pages {int(((lens + 15) // 16).sum())}",
+          flush=True)
+    cache = kvq.Int4Cache(w.num_pages, hkv, 128, block, DEV)
+    kvq.kvq_append_paged(cache, w.k, w.v, w.slot_mapping)
+    bt = w.block_table
+    got = _decode(kvq.kvq_decode_attn, cache, w, bt)
+    assert np.isfinite(got).all() and not got[3].any()
+    rows = [3, 5, 8, 40] + [int(x) for x in rng.choice([b for b in range(batch) if b not in (3, 5, 8, 40)], 5,
+                                                       replace=False)]
+    pool, want = _sampled_oracle(w, bt, rows)
+    gpu_pool = cache.pool.cpu().numpy().reshape(w.num_pages, -1)
+    ora_pool = pool.reshape(w.num_pages, -1)
+    for b in rows:
+        pages = bt[b][: (int(lens[b]) + 15) // 16]
+        assert np.array_equal(gpu_pool[pages], ora_pool[pages]), f"pages of sequence {b}"
+    _close(got[rows], want, f"stream weighted hq{hq} b{block}")
