@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libkvq.so")
 PROBE_LIB = os.path.join(PKG, "libkvq_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 
-SOURCES = ["api.cpp", "append.hip", "decode_int4.hip", "decode_int4_bal.hip", "decode_int4_sk.hip", "decode_mxfp4.hip", "decode_bf16.hip", "decode_windowed.hip", "reduce.hip"]
+SOURCES = ["api.cpp", "append.hip", "decode_int4.hip", "decode_int4_sk.hip", "decode_mxfp4.hip", "decode_bf16.hip", "decode_windowed.hip", "reduce.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

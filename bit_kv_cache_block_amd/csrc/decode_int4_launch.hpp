@@ -1,10 +1,10 @@
 // Launch of the INT4-family decode kernel (token-wise INT4, INT8 and grouped
 // INT4 codes; the kernel itself is decode_quant_body): the number of query
 // heads per KV head picks the sets of four heads a workgroup carries, the
-// grid size the register budget.  The planned build (decode_int4.hip), the
-// balanced build (decode_int4_bal.hip) and the stream-K build
-// (decode_int4_sk.hip) each instantiate it with their own MAP, in
-// translation units of their own that compile side by side.
+// grid size the register budget.  The planned and balanced builds
+// (decode_int4.hip) and the stream-K build (decode_int4_sk.hip) each
+// instantiate it with their own MAP, in two translation units that compile
+// side by side.
 #pragma once
 #include "decode_int4_body.hpp"
 
