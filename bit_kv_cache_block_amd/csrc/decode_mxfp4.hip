@@ -63,17 +63,15 @@ struct MxStep {
 };
 
 // E2M1 codes (a nibble per byte) -> int8 twice their value: sign-magnitude
-// through two byte lookups and a per-byte select.  The select mask is the
-// sign bit (bit 3 of each byte) spread over its byte by v_perm's
-// sign-replicating selectors, which copy bit 7 of byte 1, 3 (second source)
-// or 5, 7 (first source) of the pair: shifted left by 12 and by 4, the codes'
-// bytes 0, 2 and 1, 3 put their sign bits there.  (A multiply by 0xFF would
-// take a quarter-rate instruction per word.)
+// through two byte lookups and a per-byte select, whose mask is the sign bit
+// (bit 3 of each byte) times 0xFF.  (Spreading the sign bits with v_perm's
+// sign-replicating selectors instead, two shifts and a permute, avoids the
+// quarter-rate multiply but measured 2.5% slower on the whole decode.)
 __device__ __forceinline__ uint32_t e2m1x2_to_i8(uint32_t codes) {
   const uint32_t mag = codes & 0x07070707u;
   const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, mag);   // 0 1 2 3 4 6 8 12
   const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, mag);   // their negatives
-  const uint32_t sel = __builtin_amdgcn_perm(codes << 12, codes << 4, 0x090B080Au);
+  const uint32_t sel = ((codes >> 3) & 0x01010101u) * 0xFFu;
   return (neg & sel) | (pos & ~sel);
 }
 
