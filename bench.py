@@ -576,7 +576,11 @@ def ceiling_mode(torch, iters=20):
     2176-byte page slabs in a seeded random order (1.14 GB, four layers'
     worth of the headline cache), a streaming read of 4 GiB, and streaming
     reads with a 4:1 and a 1:1 read:write mix (the append moves about 4 bytes
-    in per byte out).  TB/s of the bytes each probe moves."""
+    in per byte out), the pieces in flight spread over the grid; then the
+    4:1 mix with each workgroup on a contiguous stretch, its output
+    contiguous or in 1 KiB pieces at seeded permuted places (as page slabs of
+    a permuted page table), with plain and non-temporal stores.  TB/s of the
+    bytes each probe moves."""
     import ctypes as C
     import numpy as np
     import bit_kv_cache_block_amd as kvq_pkg
@@ -585,6 +589,7 @@ def ceiling_mode(torch, iters=20):
     p, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
     L.kvq_probe_gather.argtypes = [p, i32, p, i32, i32, p, p]
     L.kvq_probe_stream.argtypes = [p, i64, i32, p, i32, p, p]
+    L.kvq_probe_stream_block.argtypes = [p, i64, p, i32, i32, p, p]
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
     grid = 2048
     sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
@@ -624,6 +629,18 @@ def ceiling_mode(torch, iters=20):
 
         res[f"stream_{ratio}to1_read_write_tb_s"] = timed(mix, items * 16 * (ratio + 1))
         del dst
+    items = (1 << 32) // 16 // 4
+    dst = torch.empty(items * 16, dtype=torch.uint8, device="cuda")
+    perm = torch.from_numpy(rng.permutation(items // 64).astype(np.int32)).to("cuda")
+    for scatter in (False, True):
+        for nt in (0, 1):
+            def blk():
+                assert L.kvq_probe_stream_block(p(src.data_ptr()), items, p(dst.data_ptr()), 1024, nt,
+                                                p(perm.data_ptr()) if scatter else None, stream) == 0
+
+            key = "stream_4to1_block_" + ("scatter1k" if scatter else "contiguous") + ("_nt" if nt else "")
+            res[key + "_tb_s"] = timed(blk, items * 16 * 5)
+    del dst, perm
     return res
 
 

@@ -3,8 +3,13 @@
 // ceiling mode calls them):
 //   - gather: the decode's pattern, a read of page slabs in a permuted order,
 //     four slabs per wave step, non-temporal buffer loads;
-//   - stream: the append's pattern, a streaming read with a fixed read:write
-//     ratio (4:1 for 2-byte inputs against 4-bit codes), or a pure read.
+//   - stream: a streaming read with a fixed read:write ratio (4:1 for 2-byte
+//     inputs against 4-bit codes), or a pure read, the pieces in flight
+//     spread over the grid;
+//   - stream_block: the same mix with each workgroup on its own contiguous
+//     stretch, stores plain or non-temporal, the output contiguous or in
+//     1 KiB pieces at permuted places (the append writes page slabs of a
+//     permuted page table).
 // Each probe reduces what it reads with xor so that no load is dead code, and
 // stores one word per thread (gather, pure stream) or its write share.
 #include <hip/hip_runtime.h>
@@ -68,6 +73,38 @@ __global__ __launch_bounds__(256) void stream_kernel(const u32x4* src, int64_t i
   if (!dst) sink[tid] = all[0] ^ all[1] ^ all[2] ^ all[3];
 }
 
+// Workgroup b reads pieces [b * per_block, (b + 1) * per_block) of each of
+// the RATIO stretches (four pieces per thread in flight) and writes their
+// xor to the same piece of dst, or with perm to piece perm[j / 64] * 64 +
+// j % 64 (1 KiB pieces at permuted places; perm holds items / 64 entries).
+template <int RATIO, bool NT>
+__global__ __launch_bounds__(256) void stream_block_kernel(const u32x4* src, int64_t items, u32x4* dst,
+                                                           int64_t per_block, const int32_t* perm) {
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * per_block;
+  const int64_t b1 = b0 + per_block < items ? b0 + per_block : items;
+  for (int64_t j0 = b0 + threadIdx.x; j0 < b1; j0 += 4 * 256) {
+    u32x4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = j0 + u * 256;
+      x[u] = u32x4{0u, 0u, 0u, 0u};
+      if (j < b1) {
+#pragma unroll
+        for (int r = 0; r < RATIO; ++r) x[u] ^= __builtin_nontemporal_load(&src[r * items + j]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = j0 + u * 256;
+      if (j < b1) {
+        const int64_t d = perm ? static_cast<int64_t>(perm[j >> 6]) * 64 + (j & 63) : j;
+        if constexpr (NT) __builtin_nontemporal_store(x[u], &dst[d]);
+        else dst[d] = x[u];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,6 +144,22 @@ int kvq_probe_stream(const void* src, int64_t items, int32_t ratio, void* dst, i
     case 4: stream_kernel<4><<<grid, 256, 0, s>>>(in, items, out, k); break;
     default: return 1;
   }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// The 4:1 mix with one contiguous stretch per workgroup (items a multiple
+// of 64): nt selects non-temporal stores; perm (items / 64 entries, a
+// permutation of 0 .. items / 64 - 1) scatters the output in 1 KiB pieces,
+// null keeps it contiguous.
+int kvq_probe_stream_block(const void* src, int64_t items, void* dst, int32_t grid, int32_t nt,
+                           const int32_t* perm, void* stream) {
+  if (!src || !dst || items <= 0 || items % 64 != 0 || grid <= 0) return 1;
+  const auto* in = static_cast<const u32x4*>(src);
+  auto* out = static_cast<u32x4*>(dst);
+  const int64_t per_block = ((items + grid - 1) / grid + 63) / 64 * 64;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nt) stream_block_kernel<4, true><<<grid, 256, 0, s>>>(in, items, out, per_block, perm);
+  else stream_block_kernel<4, false><<<grid, 256, 0, s>>>(in, items, out, per_block, perm);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
