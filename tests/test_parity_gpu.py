@@ -185,6 +185,21 @@ def test_decode_tiny(block):
         assert_close(gpu_decode(cache, w, splits), want, f"tiny b{block} S{splits}")
 
 
+@pytest.mark.parametrize("d,block", [(128, 16), (128, 32), (128, 64), (128, 128), (64, 16), (64, 32), (64, 64)])
+def test_decode_forced_splits_every_block(d, block):
+    """Split partials of a rotated pool, each rotated back before the merge
+    combines them: every block size, two and five splits, GQA 4 and 8,
+    against the oracle."""
+    for hq in (8, 16):
+        w = workloads.random_decode(90 + block, batch=3, hq=hq, hkv=2, d=d, block=block, seq_lens=[700, 300, 1000])
+        cache = gpu_int4_cache(w, block)
+        pool = oracle_int4_pool(w, block)
+        want = oracle.decode_int4(pool, w.hkv, w.d, block, bits(w.q), _odt(w.q), w.block_table,
+                                  w.seq_lens, w.sm_scale)
+        for splits in (2, 5):
+            assert_close(gpu_decode(cache, w, splits), want, f"splits d{d} b{block} hq{hq} S{splits}")
+
+
 @pytest.mark.parametrize("block", [0, 16, 32, 64, 128])
 def test_decode_llama_shape(block):
     w = workloads.llama8b_decode(2, batch=3, context=4096, block=block)

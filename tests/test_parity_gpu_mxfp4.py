@@ -196,3 +196,14 @@ def test_mxfp4_full_size_llama_layer_sampled():
     mask[sample] = 1
     want = oracle_attn(pool, w, 64, mask=mask)
     assert_close(out.cpu().numpy().astype(np.float64)[sample], want[sample], "mxfp4 full llama sampled")
+
+
+@pytest.mark.parametrize("block", [32, 128])
+def test_mxfp4_decode_forced_splits_every_block(block):
+    """Split partials of a rotated MXFP4 pool, each rotated back before the
+    merge: forced splits at blocks 32 and 128 against the oracle."""
+    w = workloads.random_decode(91, batch=3, hq=16, hkv=2, d=128, block=block, seq_lens=[700, 300, 1000])
+    cache = gpu_cache(w, block)
+    want = oracle_attn(oracle_pool(w, block), w, block)
+    for splits in (2, 5):
+        assert_close(gpu_decode(cache, w, splits), want, f"mxfp4 b{block} S{splits}")
