@@ -461,16 +461,19 @@ class ServingRing:
 
 
 def concurrency_sweep(torch, kvq, workloads, steps=48, warm=8, block_steps=8,
-                      batches=(1, 8, 32, 128, 256)):
+                      batches=(1, 8, 32, 128, 256), eager_rounds=6):
     """70B-shaped layer (64 q / 8 kv heads): per batch size and cache kind
     (rotated INT4, plain INT4, bf16), a ServingRing of layer caches; ``warm``
-    untimed steps on each, then ``steps`` more per kind in runs of
-    ``block_steps`` that alternate between the kinds, the first of each round
-    rotating (6 rounds: each kind first twice), so that all three see the
-    same clocks.  Tokens/s = batch / time per step (one layer).  The steps are
-    timed twice: called one by one from Python (the host's per-call cost
-    included; it bounds the small batches), and captured in HIP graphs and
-    replayed."""
+    untimed steps on each, then ``steps`` more per kind.  Tokens/s = batch /
+    time per step (one layer).  The steps are timed twice, the kinds
+    alternating with the first of each round rotating so that all three see
+    the same clocks: called one by one from Python (the host's per-call cost
+    included; it bounds the small batches), all ``steps`` in one window per
+    kind and round, ``eager_rounds`` rounds, the median window reported (a
+    window starts from an idle GPU, so short windows would weigh that start
+    on every few steps, and near the host's bound one round's jitter moves a
+    mean); and captured in HIP graphs of ``block_steps`` steps and replayed,
+    one graph per kind and round."""
     out = {"workload": "64 q / 8 kv heads, head_dim 128, lognormal contexts (median 2048, "
                        "sigma 1, cap 32768), page 16, one new token per sequence per step; "
                        "successive steps on successive layers of a ring of >= 1 GiB per cache kind",
@@ -491,8 +494,8 @@ def concurrency_sweep(torch, kvq, workloads, steps=48, warm=8, block_steps=8,
         for name in names:
             for i in range(warm):
                 run(name, i)
-        ms = {name: 0.0 for name in names}
-        for rnd, i0 in enumerate(range(warm, warm + steps, block_steps)):
+        wins = {name: [] for name in names}
+        for rnd in range(eager_rounds):
             # the variant that runs first after the synchronisation changes
             # from round to round, so none is always first
             order = names[rnd % len(names):] + names[:rnd % len(names)]
@@ -501,11 +504,12 @@ def concurrency_sweep(torch, kvq, workloads, steps=48, warm=8, block_steps=8,
                 e1 = torch.cuda.Event(enable_timing=True)
                 torch.cuda.synchronize()
                 e0.record()
-                for i in range(i0, min(i0 + block_steps, warm + steps)):
+                for i in range(warm, warm + steps):
                     run(name, i)
                 e1.record()
                 torch.cuda.synchronize()
-                ms[name] += e0.elapsed_time(e1)
+                wins[name].append(e0.elapsed_time(e1))
+        ms = {name: sorted(w)[len(w) // 2] for name, w in wins.items()}
         # The same steps captured in HIP graphs (one per run of block_steps)
         # and replayed in the same rotating order: the GPU time of a step
         # without the host's per-call cost, as a serving loop that replays
