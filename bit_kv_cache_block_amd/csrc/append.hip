@@ -67,6 +67,21 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
   return m | ((v < 0.0f && m != 0u) ? 8u : 0u);
 }
 
+// E2M1 codes of y0 / s and y1 / s in byte SEL of `old` (y0 in the low
+// nibble) by gfx950's conversion instruction, whose rounding is the rule
+// above (nearest, ties to mantissa bit 0, saturating at 6; checked on the
+// device against it at every tie) except that it keeps the sign of a zero,
+// which clear_negative_zeros then drops.  s = 2^X must be a normal float.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t old, float y0, float y1, float s) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y0, y1, s, SEL);
+}
+// Eight E2M1 codes of a word with a zero magnitude (-0, code 8) made +0.
+__device__ __forceinline__ uint32_t clear_negative_zeros(uint32_t w) {
+  const uint32_t keep = ((w & 0x77777777u) + 0x77777777u) & 0x88888888u;   // bit 3 of nonzero codes
+  return (w & 0x77777777u) | (w & keep);
+}
+
 // The asymmetric quantizer of one vector (or group), shared by both append
 // kernels so that their codes and sidecars agree bit for bit.  From the range
 // [mn, mx] of the (normalised) elements: zero point mn and scale
@@ -444,8 +459,35 @@ void append_quant_kernel(AppendArgs a) {
       }
       return tok_code<BITS, kExactNorm>(x[k], sb, zf[gl], inv[gl]);
     };
+    // MXFP4 codes through the conversion instruction, two per instruction,
+    // when every block of the lane has X > -124: then a code that is not
+    // zero comes from an element of at least 2^-125 (a normal float), and the
+    // scale 2^X is normal.  (Blocks of smaller elements, all-zero ones
+    // included, keep the comparisons: the instruction's handling of subnormal
+    // inputs is not relied on.)
+    [[maybe_unused]] bool mx_hw = false;
+    [[maybe_unused]] float mx_s[kGL];
+    if constexpr (MX) {
+      mx_hw = true;
+#pragma unroll
+      for (int gl = 0; gl < kGL; ++gl) {
+        mx_hw = mx_hw && xe[gl] > -124;
+        mx_s[gl] = ldexpf(1.0f, xe[gl] > -124 ? xe[gl] : 0);
+      }
+    }
+    auto mx_y = [&](int k) { return kExactNorm ? x[k] * sb : x[k]; };
     // the unit's results are stored at the start of the next iteration
-    if (GS == 0 || kind == 0) {   // consecutive channels: K, or V of the token-wise pools
+    if (MX && mx_hw && kind == 0) {   // K: word m holds elements 8m .. 8m+7 of one block
+#pragma unroll
+      for (int m = 0; m < kWords; ++m) {
+        const float sc = mx_s[(8 * m) / kGE];
+        uint32_t w = e2m1_pair<0>(0u, mx_y(8 * m), mx_y(8 * m + 1), sc);
+        w = e2m1_pair<1>(w, mx_y(8 * m + 2), mx_y(8 * m + 3), sc);
+        w = e2m1_pair<2>(w, mx_y(8 * m + 4), mx_y(8 * m + 5), sc);
+        w = e2m1_pair<3>(w, mx_y(8 * m + 6), mx_y(8 * m + 7), sc);
+        pend.words[m] = clear_negative_zeros(w);
+      }
+    } else if (GS == 0 || kind == 0) {   // consecutive channels: K, or V of the token-wise pools
 #pragma unroll
       for (int m = 0; m < kWords; ++m) {
         uint32_t c[kPer];
@@ -474,13 +516,21 @@ void append_quant_kernel(AppendArgs a) {
       // every word, and stores words 8hf .. 8hf+7 after swapping the other
       // half-words with its partner lane
       uint32_t hw[16];
+      if (MX && mx_hw) {   // (channels n2, n2 + 16 in block 0 of the lane, n2 + 32, n2 + 48 in block 1)
 #pragma unroll
-      for (int n2 = 0; n2 < 16; ++n2) {
-        const uint32_t t0 = __builtin_amdgcn_perm(code(n2 + 16), code(n2), 0x0c0c0400u);        // c0 | c1 << 8
-        const uint32_t t1 = __builtin_amdgcn_perm(code(n2 + 48), code(n2 + 32), 0x0c0c0400u);
-        const uint32_t b0 = (t0 | (t0 >> 4)) & 0xFFu;                                           // c0 | c1 << 4
-        const uint32_t b1 = (t1 | (t1 >> 4)) & 0xFFu;
-        hw[n2] = b0 | (b1 << 8);
+        for (int n2 = 0; n2 < 16; ++n2) {
+          const uint32_t w = e2m1_pair<0>(0u, mx_y(n2), mx_y(n2 + 16), mx_s[0]);
+          hw[n2] = clear_negative_zeros(e2m1_pair<1>(w, mx_y(n2 + 32), mx_y(n2 + 48), mx_s[kGL - 1]));
+        }
+      } else {
+#pragma unroll
+        for (int n2 = 0; n2 < 16; ++n2) {
+          const uint32_t t0 = __builtin_amdgcn_perm(code(n2 + 16), code(n2), 0x0c0c0400u);        // c0 | c1 << 8
+          const uint32_t t1 = __builtin_amdgcn_perm(code(n2 + 48), code(n2 + 32), 0x0c0c0400u);
+          const uint32_t b0 = (t0 | (t0 >> 4)) & 0xFFu;                                           // c0 | c1 << 4
+          const uint32_t b1 = (t1 | (t1 >> 4)) & 0xFFu;
+          hw[n2] = b0 | (b1 << 8);
+        }
       }
       uint32_t send[4], recv[4];
 #pragma unroll

@@ -207,3 +207,46 @@ def test_mxfp4_decode_forced_splits_every_block(block):
     want = oracle_attn(oracle_pool(w, block), w, block)
     for splits in (2, 5):
         assert_close(gpu_decode(cache, w, splits), want, f"mxfp4 b{block} S{splits}")
+
+
+def _crafted_block(rng, X):
+    """32 values of one MXFP4 block with shared exponent X (the largest is
+    7.5 * 2^X): every tie between E2M1 values, values next to the ties,
+    saturating ones, tiny ones that round to zero, both signs."""
+    t = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, 7.0, 0.5, 1.0, 1.5, 3.0, 4.0, 6.0, 0.125,
+                  0.0625, 0.0, 2.25, 2.75, 0.875, 1.125, 5.5, 4.5, 0.375, 0.625, 3.25, 3.75, 6.25, 0.1875,
+                  0.03125], np.float64)
+    sign = np.where(rng.random(t.size) < 0.5, -1.0, 1.0)
+    vals = np.concatenate([[7.5], sign * t])
+    rng.shuffle(vals)
+    return vals * 2.0 ** X
+
+
+@pytest.mark.parametrize("xs", [(-6, 0, 5, 12), (-123, -124, -125, -3), (0, 0, 0, 0)])
+def test_mxfp4_append_crafted_ties_bitexact(xs):
+    """Crafted blocks through the append (no rotation, so the values reach
+    the quantizer as written): every E2M1 tie of both signs, saturation,
+    values that round to zero (stored +0), and shared exponents on both sides
+    of -124 (subnormal elements at -125), bit-exact against the oracle's
+    pool."""
+    rng = np.random.default_rng(sum(abs(x) for x in xs) + 7)
+    tokens, hkv, d = 48, 2, 128
+    k = np.empty((tokens, hkv, d)); v = np.empty((tokens, hkv, d))
+    for t in range(tokens):
+        for h in range(hkv):
+            for blk in range(4):
+                X = xs[(blk + t + h) % 4]
+                k[t, h, 32 * blk:32 * blk + 32] = _crafted_block(rng, X)
+                v[t, h, 32 * blk:32 * blk + 32] = _crafted_block(rng, xs[(blk + 2 * t + h) % 4])
+    kb = torch.from_numpy(k).to(torch.bfloat16)
+    vb = torch.from_numpy(v).to(torch.bfloat16)
+    assert torch.equal(kb.to(torch.float64), torch.from_numpy(k)), "crafted values are bf16-exact"
+    w = workloads.random_decode(93, batch=3, hq=8, hkv=hkv, d=d, block=0, seq_lens=[16, 17, 15])
+    sm = w.slot_mapping
+    cache = kvq.MxFp4Cache(w.num_pages, hkv, d, 0, DEV)
+    kvq.kvq_append_paged_mxfp4(cache, kb.to(DEV), vb.to(DEV), sm.to(DEV))
+    torch.cuda.synchronize()
+    pool = oracle.new_mxfp4_pool(w.num_pages, hkv, d)
+    oracle.append_mxfp4(pool, w.num_pages, hkv, d, 0, bits(kb), bits(vb), oracle.BF16, sm.cpu().numpy())
+    print(f"mxfp4 crafted {xs}", flush=True)
+    assert_pool_equal(cache.pool, pool, f"crafted {xs}")
