@@ -384,7 +384,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
     float am = 0.0f;
 #pragma unroll
     for (int k = 0; k < kC; ++k) am = fmaxf(am, fabsf(v[k]));
-    am = row_max16(am);
+    am = row_max16_nonneg(am);   // (a maximum of |q|)
     int ex = 0;
     frexpf(am, &ex);                    // am < 2^ex
     ex = ex < -100 ? -100 : ex;         // keeps 2^(22-ex) finite; smaller q is ~0
@@ -581,7 +581,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
     // largest w of the head (power-of-two scale sw), three int8 limbs of it
     // into the LDS tile of (set st, group gi)
     auto store_limbs = [&](int st, int gi, const float* w, float wmax) {
-      wmax = row_max16(wmax);
+      wmax = row_max16_nonneg(wmax);   // (w = p * v_scale >= 0)
       int ew = 0;
       frexpf(wmax, &ew);                 // wmax < 2^ew
       ew = ew < -100 ? -100 : ew;        // such a step weighs < 2^-76 of the max

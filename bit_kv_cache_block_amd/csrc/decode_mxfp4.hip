@@ -199,8 +199,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
     float am = 0.0f;
 #pragma unroll
     for (int k = 0; k < kC; ++k) am = fmaxf(am, fabsf(v[k]));
-    am = fmaxf(am, dpp_f<kDppXor1>(am));
-    am = fmaxf(am, dpp_f<kDppXor2>(am));
+    am = u2f(max(f2u(am), dpp_u<kDppXor1>(f2u(am))));   // (|q| >= 0: its bits order like its values)
+    am = u2f(max(f2u(am), dpp_u<kDppXor2>(f2u(am))));
     int ex = 0;
     frexpf(am, &ex);                                  // am < 2^ex
     int s0 = am > 0.0f ? ex - 8 : -99;                // limb 0 below 2^8 (E4M3 max 448)
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
           w[i] = ldexpf(pp[i], e - 128);
           wmax = fmaxf(wmax, w[i]);
         }
-        wmax = row_max16(wmax);
+        wmax = row_max16_nonneg(wmax);   // (w = p * 2^(E - 128) >= 0)
         int ew = 0;
         frexpf(wmax, &ew);
         ew = ew < -100 ? -100 : ew;

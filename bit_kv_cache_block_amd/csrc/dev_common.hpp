@@ -366,6 +366,18 @@ __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
   return fmaxf(x, dpp_f<kDppRowMirror>(x));
 }
+// row_max16 of values known to be >= 0 (no NaN): for those the order of
+// the bit patterns as unsigned integers is the order of the values, so the
+// maximum is taken on the bits, where the lane moves need none of the
+// quieting of possible NaNs that a float maximum of a moved value costs
+// (one instruction per stage).  Bit-identical to row_max16 on such values.
+__device__ __forceinline__ float row_max16_nonneg(float x) {
+  uint32_t u = f2u(x);
+  u = max(u, dpp_u<kDppXor1>(u));
+  u = max(u, dpp_u<kDppXor2>(u));
+  u = max(u, dpp_u<kDppRowHalfMirror>(u));
+  return u2f(max(u, dpp_u<kDppRowMirror>(u)));
+}
 __device__ __forceinline__ float row_sum16(float x) {
   x += dpp_f<kDppXor1>(x);
   x += dpp_f<kDppXor2>(x);
