@@ -26,12 +26,6 @@ __device__ __forceinline__ uint16_t bf16_limb(float x, int lam) {
   return lam == 0 ? h : lam == 1 ? m : lam == 2 ? l : static_cast<uint16_t>(0);
 }
 
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, dpp_f<kDppXor1>(x));
-  x = fmaxf(x, dpp_f<kDppXor2>(x));
-  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
-  return fmaxf(x, dpp_f<kDppRowMirror>(x));
-}
 __device__ __forceinline__ float row_sum16(float x) {
   x += dpp_f<kDppXor1>(x);
   x += dpp_f<kDppXor2>(x);
@@ -243,7 +237,7 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeArgs& a, uint32_t w
       float mc = lg[st][0];
 #pragma unroll
       for (int i = 1; i < kStep; ++i) mc = fmaxf(mc, lg[st][i]);
-      mc = row_max16(mc);
+      mc = row_max16_ordered(mc);
       const float mnew = fmaxf(m_run[st], mc);
       const float muse = mnew == kNegInf ? 0.0f : mnew;
       alpha[st] = fast_exp2(m_run[st] - muse);

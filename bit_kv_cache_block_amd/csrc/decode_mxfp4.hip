@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
       float mc = lg[st][0];
 #pragma unroll
       for (int i = 1; i < kStep; ++i) mc = fmaxf(mc, lg[st][i]);
-      mc = row_max16(mc);
+      mc = row_max16_ordered(mc);
       const float mnew = fmaxf(m_run[st], mc);
       const float muse = mnew == kNegInf ? 0.0f : mnew;
       alpha[st] = fast_exp2(m_run[st] - muse);

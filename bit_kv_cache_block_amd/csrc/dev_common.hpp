@@ -359,18 +359,28 @@ struct LimbSel {
 // at the accuracy the decode keeps.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// max / sum over the 16 lanes of a row, result in every lane of the row
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, dpp_f<kDppXor1>(x));
-  x = fmaxf(x, dpp_f<kDppXor2>(x));
-  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
-  return fmaxf(x, dpp_f<kDppRowMirror>(x));
+// max / sum over the 16 lanes of a row, result in every lane of the row.
+// The maximum of any values but NaN is taken on keys that order as the
+// values do when read as signed integers (a negative value's magnitude bits
+// flipped; the map is its own inverse), so that each stage is an integer
+// maximum with the lane move folded in, where a float maximum of a moved
+// value also quiets possible NaNs (one more instruction per stage).  -0
+// orders below +0, a difference no caller can see (the maximum is subtracted
+// from logits or compared with -inf).
+__device__ __forceinline__ float row_max16_ordered(float x) {
+  const int32_t u = static_cast<int32_t>(f2u(x));
+  int32_t k = u ^ ((u >> 31) & 0x7FFFFFFF);
+  k = max(k, static_cast<int32_t>(dpp_u<kDppXor1>(static_cast<uint32_t>(k))));
+  k = max(k, static_cast<int32_t>(dpp_u<kDppXor2>(static_cast<uint32_t>(k))));
+  k = max(k, static_cast<int32_t>(dpp_u<kDppRowHalfMirror>(static_cast<uint32_t>(k))));
+  k = max(k, static_cast<int32_t>(dpp_u<kDppRowMirror>(static_cast<uint32_t>(k))));
+  return u2f(static_cast<uint32_t>(k ^ ((k >> 31) & 0x7FFFFFFF)));
 }
-// row_max16 of values known to be >= 0 (no NaN): for those the order of
+// The same of values known to be >= 0 (no NaN): for those the order of
 // the bit patterns as unsigned integers is the order of the values, so the
 // maximum is taken on the bits, where the lane moves need none of the
 // quieting of possible NaNs that a float maximum of a moved value costs
-// (one instruction per stage).  Bit-identical to row_max16 on such values.
+// (one instruction per stage).  Bit-identical to a float maximum on such values.
 __device__ __forceinline__ float row_max16_nonneg(float x) {
   uint32_t u = f2u(x);
   u = max(u, dpp_u<kDppXor1>(u));
