@@ -487,18 +487,44 @@ void append_quant_kernel(AppendArgs a) {
         w = e2m1_pair<3>(w, mx_y(8 * m + 6), mx_y(8 * m + 7), sc);
         pend.words[m] = clear_negative_zeros(w);
       }
-    } else if (GS == 0 || kind == 0) {   // consecutive channels: K, or V of the token-wise pools
+    } else if (MX && (GS == 0 || kind == 0)) {   // MXFP4 K without the conversion instruction
 #pragma unroll
       for (int m = 0; m < kWords; ++m) {
         uint32_t c[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i) c[i] = code(kPer * m + i);
+        pend.words[m] = pack8_nibbles(c);
+      }
+    } else if (GS == 0 || kind == 0) {   // consecutive channels: K, or V of the token-wise pools
+      // The code of tok_code through v_cvt_pk_u8_f32, which rounds to nearest
+      // even, clamps to [0, 255] and writes one byte of a word: for 4-bit
+      // codes the value is first clamped to [0, 15] (clamping then rounding
+      // equals rounding then clamping there), the even-numbered codes go to
+      // the bytes of one word and the odd ones to another, joined as nibbles.
+      auto qv = [&](int k) {
+        const int gl = k / kGE;
+        const float d = kExactNorm ? __builtin_fmaf(x[k], sb, -zf[gl]) : x[k] - zf[gl];
+        const float q = d * inv[gl];
+        return BITS == 4 ? __builtin_amdgcn_fmed3f(q, 0.0f, 15.0f) : q;
+      };
+#pragma unroll
+      for (int m = 0; m < kWords; ++m) {
+        const int k0 = kPer * m;
         if constexpr (BITS == 4) {
-          pend.words[m] = pack8_nibbles(c);
+          uint32_t ev = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0), 0, 0u);
+          ev = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0 + 2), 1, ev);
+          ev = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0 + 4), 2, ev);
+          ev = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0 + 6), 3, ev);
+          uint32_t od = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0 + 1), 0, 0u);
+          od = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0 + 3), 1, od);
+          od = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0 + 5), 2, od);
+          od = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0 + 7), 3, od);
+          pend.words[m] = ev | (od << 4);
         } else {
-          const uint32_t lo = __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u);   // c0.byte0, c1.byte0
-          const uint32_t hi = __builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u);
-          pend.words[m] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0), 0, 0u);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0 + 1), 1, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0 + 2), 2, w);
+          pend.words[m] = __builtin_amdgcn_cvt_pk_u8_f32(qv(k0 + 3), 3, w);
         }
       }
     } else if constexpr (GS != 0 && kLPV == 1) {
