@@ -161,6 +161,73 @@ def test_append_few_token_and_tile_kernels_bitexact(d, dtype, bits_):
             assert_pool_equal(cache.pool, pool, f"int{bits_} d{d} b{block} t{t}")
 
 
+def _tie_rows(rng, t, hkv, d, block, levels):
+    """Rows whose rotated values y sit on exact ties of the quantizer: y holds
+    integers lo + 2j over [lo, lo + 2 levels] with both ends in every group of
+    32 channels, so the fp16 scale is 2, the zero lo, and (y - lo) / 2 is an
+    integer or an integer plus one half (the odd offsets, about half of them).
+    The input is x = H y / sqrt(b) per block (H the Sylvester Hadamard matrix,
+    symmetric with H H = b I, so the block transform of x gives back y); at
+    b = 16 and 64 every x and every partial sum of the butterfly is a short
+    binary fraction, exact in fp16 and fp32."""
+    lo = rng.choice([0, -8, -15, 3], size=(t, hkv, 1)).astype(np.float64)
+    y = lo + 2.0 * rng.integers(0, levels + 1, size=(t, hkv, d)) - rng.integers(0, 2, size=(t, hkv, d))
+    y = np.clip(y, lo, lo + 2 * levels)
+    g = y.reshape(t, hkv, d // 32, 32)
+    g[..., 0] = lo
+    g[..., 17] = lo + 2 * levels
+    y = g.reshape(t, hkv, d)
+    x = y
+    if block > 0:
+        h = np.array([[1.0]])
+        while h.shape[0] < block:
+            h = np.block([[h, h], [h, -h]])
+        x = (y.reshape(t, hkv, d // block, block) @ h / np.sqrt(block)).reshape(t, hkv, d)
+    xh = x.astype(np.float16)
+    assert np.array_equal(xh.astype(np.float64), x), "crafted rows not exact in fp16"
+    return torch.from_numpy(xh), y
+
+
+@pytest.mark.parametrize("kind,block", [("int4", 0), ("int4", 16), ("int4", 64), ("int8", 0),
+                                        ("int4g", 0), ("int4g", 64)])
+def test_append_exact_ties_bitexact(kind, block):
+    """Codes that are exact ties k + 1/2 round to the even neighbour in both
+    append kernels (few-token and tile) as in the oracle, for the token-wise
+    INT4 and INT8 and the grouped INT4 pools, plain and rotated."""
+    rng = np.random.default_rng(11)
+    hkv, d, t_all = 2, 128, 1100
+    levels = 255 if kind == "int8" else 15
+    k, yk = _tie_rows(rng, t_all, hkv, d, block, levels)
+    v, _ = _tie_rows(rng, t_all, hkv, d, block, levels)
+    ties = (yk - yk.min(axis=2, keepdims=True)) % 2 == 1   # odd offsets from lo
+    assert ties.mean() > 0.3
+    if block > 0:   # the oracle's rotation gives back y exactly
+        for row, want in zip(k[:4].numpy().astype(np.float32).reshape(-1, d), yk[:4].reshape(-1, d)):
+            assert np.array_equal(oracle.rotate(row, block).astype(np.float64), want)
+    pages = (t_all + 15) // 16 + 4
+    slots = rng.permutation(pages * 16)[:t_all].astype(np.int32)
+    for t in (9, t_all):   # t <= 1024: few-token kernel
+        if kind == "int4":
+            cache = kvq.Int4Cache(pages, hkv, d, block, DEV)
+            kvq.kvq_append_paged(cache, k[:t].to(DEV), v[:t].to(DEV), torch.from_numpy(slots[:t]).to(DEV))
+            pool = oracle.new_int4_pool(pages, hkv, d)
+            oracle.append_int4(pool, pages, hkv, d, block, bits(k[:t]), bits(v[:t]), oracle.F16, slots[:t])
+        elif kind == "int8":
+            cache = kvq.Int8Cache(pages, hkv, d, block, DEV)
+            kvq.kvq_append_paged_int8(cache, k[:t].to(DEV), v[:t].to(DEV), torch.from_numpy(slots[:t]).to(DEV))
+            pool = oracle.new_int8_pool(pages, hkv, d)
+            oracle.append_int8(pool, pages, hkv, d, block, bits(k[:t]), bits(v[:t]), oracle.F16, slots[:t])
+        else:
+            cache = kvq.Int4GroupedCache(pages, hkv, d, block, 32, DEV)
+            kvq.kvq_append_paged_int4g(cache, k[:t].to(DEV), v[:t].to(DEV), torch.from_numpy(slots[:t]).to(DEV))
+            pool = oracle.new_int4g_pool(pages, hkv, d, 32)
+            oracle.append_int4g(pool, pages, hkv, d, block, 32, bits(k[:t]), bits(v[:t]), oracle.F16,
+                                slots[:t])
+        torch.cuda.synchronize()
+        print(f"ties {kind} b{block} t{t}", flush=True)
+        assert_pool_equal(cache.pool, pool, f"ties {kind} b{block} t{t}")
+
+
 def test_append_bf16_cache_matches_oracle():
     for w in (workloads.tiny_decode(1, block=0), workloads.llama8b_decode(2, batch=2, context=256)):
         cache = kvq.Bf16Cache(w.num_pages, w.hkv, w.d, DEV)
