@@ -152,7 +152,6 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   static_assert(!kStage || kStep == 4, "stage of four pages");
   constexpr int kNT = D / 16;          // PV tiles = output channels per lane
   constexpr int kOps = D / 64;         // QK MFMAs per page and head group
-  constexpr int kGP = 4 * NS;          // padded heads per KV head
   constexpr int kC = D / 16;           // channels per lane when a row of 16 lanes holds a vector
   // head_dim 128: the QK operand is built once, by the query waves, into an
   // LDS image of NS * kOps * 64 lanes * 16 bytes (the size of the query
@@ -166,7 +165,7 @@ __device__ __forceinline__ void decode_quant_body(const DecodeArgs& a, uint32_t 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63;
-  const int g = lane >> 4, n = lane & 15, hs = n >> 2, lam = n & 3;
+  const int g = lane >> 4, n = lane & 15;
   const bool qwave = wave < NS;
   const int qhead = 4 * wave + g;
   const int G = a.num_q_heads / a.num_kv_heads;
