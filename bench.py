@@ -292,7 +292,8 @@ def windowed_rate(torch, kvq, workloads, db, iters, plain_gb_s, plain_bytes, w_s
 
 def variant_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes, kind):
     """A cache variant on the headline workload (Hadamard block 64):
-    decode-only loop over two cache copies, and the prefill append of 32768
+    decode-only loop over two cache copies (timed per call with an event pair
+    around each, and as one run of back-to-back calls), and the prefill append of 32768
     ragged tokens over PREFILL_RING input/cache sets (consecutive calls timed
     as a whole).  kind "int8": token-wise INT8
     (D code bytes + 4 sidecar bytes per vector); "int4g64": INT4 with one
@@ -319,10 +320,13 @@ def variant_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes, kind)
     for i in range(10):
         dec(i)
     ms, _ = _time_events(torch, dec, iters)
+    b2b_ms = _time_back_to_back(torch, dec, iters)   # the same calls with no event between them
     nbytes = decode_bytes(w.seq_lens, w.hkv, w.hq, w.d, vec_bytes)
     res = {"decode": {"us": round(ms * 1e3, 2), "bytes": nbytes,
                       "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                       "pct_of_peak": round(100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                      "us_back_to_back": round(b2b_ms * 1e3, 2),
+                      "pct_of_peak_back_to_back": round(100.0 * nbytes / (b2b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                       "time_over_int4": round(ms * 1e3 / (int4_bytes / (int4_gb_s * 1e9) * 1e6), 4)}}
     del caches
     torch.cuda.empty_cache()
@@ -349,7 +353,7 @@ def variant_rates(torch, kvq, workloads, db, iters, int4_gb_s, int4_bytes, kind)
 
 def variant_decode(torch, kvq, workloads, db, kind, iters, warm):
     """One decode variant alone on the headline workload (block 64), two
-    cache copies alternating, timed per call: the kernels for profiles."""
+    cache copies alternating, timed per call (and back to back): the kernels for profiles."""
     w = db.w
     if kind == "windowed":
         res = windowed_rate(torch, kvq, workloads, db, iters, 1.0, 1)
@@ -380,8 +384,10 @@ def variant_decode(torch, kvq, workloads, db, kind, iters, warm):
     for i in range(warm):
         dec(i)
     ms, _ = _time_events(torch, dec, iters)
+    b2b_ms = _time_back_to_back(torch, dec, iters)
     nbytes = decode_bytes(w.seq_lens, w.hkv, w.hq, w.d, vec)
-    return {"us": round(ms * 1e3, 2), "bytes": nbytes, "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    return {"us": round(ms * 1e3, 2), "bytes": nbytes, "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "us_back_to_back": round(b2b_ms * 1e3, 2)}
 
 
 def long_context_rate(torch, kvq, workloads, iters=30):

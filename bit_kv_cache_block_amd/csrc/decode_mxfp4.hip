@@ -17,11 +17,13 @@
 //        the same tile; each lane then adds its head's four rows.
 //   PV:  the V scales run along channels (one per token and 32 channels), a
 //        direction the instruction's per-column scales cannot carry, so PV
-//        stays on the int8 MFMA: E2M1 codes become exact int8 values (twice
-//        the E2M1 value, by table lookup), the weights w = p * 2^(E-128) of
-//        each 32-channel block go through LDS as 23-bit fixed-point limbs, and
-//        the V codes are laid out so that each 16-channel output tile lies in
-//        one block.
+//        runs on the bf16 MFMA (v_mfma_f32_16x16x32_bf16): the weights
+//        w = p * 2^(E-128) of each 32-channel block go through LDS as three
+//        bf16 limbs (hi = bf16(w), then what it left, twice: 24 bits), rows
+//        of the A operand; the V codes, two pages' nibbles of one channel
+//        paired in a byte, become exact bf16 (twice the E2M1 value) by the
+//        FP4 conversion instruction.  The V codes are laid out so that each 16-channel output
+//        tile lies in one block.
 #include "dev_common.hpp"
 #include "kvq_internal.hpp"
 
@@ -31,6 +33,9 @@ namespace kvq {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaves = 4;
@@ -43,7 +48,10 @@ template <int NS>
 struct alignas(16) MxSmem {
   static constexpr int kGP = 4 * NS;
   union {
-    uint8_t qb[kGP][kLimbs][kD];   // FP8 limbs of the rotated query, by channel
+    uint8_t qb[kGP][kLimbs][kD];   // FP8 limbs of the rotated query, by channel (prologue)
+    // the PV weights of a step (A operand): [wave][set][block][page pair m]
+    // [limb][head][token], a dword holding the bf16 limb of pages 2m, 2m+1
+    uint32_t wb[kWaves][NS][kBlocks][2][4][4][16];
     struct {
       float acc[kWaves][kGP][kD];
       float m[kWaves][kGP];
@@ -51,7 +59,6 @@ struct alignas(16) MxSmem {
     } merge;
   } u;
   int32_t qexp[kGP][kBlocks];       // block exponent s0 of limb 0
-  uint32_t wl[kWaves][NS][kBlocks][4][4][16];   // [wave][set][block][limb][head][token]
 };
 
 struct MxStep {
@@ -62,17 +69,24 @@ struct MxStep {
   bool all_ok;
 };
 
-// E2M1 codes (a nibble per byte) -> int8 twice their value: sign-magnitude
-// through two byte lookups and a per-byte select, whose mask is the sign bit
-// (bit 3 of each byte) times 0xFF.  (Spreading the sign bits with v_perm's
-// sign-replicating selectors instead, two shifts and a permute, avoids the
-// quarter-rate multiply but measured 2.5% slower on the whole decode.)
-__device__ __forceinline__ uint32_t e2m1x2_to_i8(uint32_t codes) {
-  const uint32_t mag = codes & 0x07070707u;
-  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, mag);   // 0 1 2 3 4 6 8 12
-  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, mag);   // their negatives
-  const uint32_t sel = ((codes >> 3) & 0x01010101u) * 0xFFu;
-  return (neg & sel) | (pos & ~sel);
+// Two packed floats as bf16, rounded to nearest even (v_cvt_pk_bf16_f32),
+// and back.
+__device__ __forceinline__ uint32_t bf16_pair(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{x, y}, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t h) { return u2f(h << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t h) { return u2f(h & 0xFFFF0000u); }
+
+// Twice the two E2M1 codes of byte `sel` of w as bf16 (exact; low nibble
+// first), by v_cvt_scalef32_pk_bf16_fp4 at scale 2 (the byte is an immediate
+// of the instruction: sel must fold to a constant).
+__device__ __forceinline__ bf16x2 e2m1_pair_bf16(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 2.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 2.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 2.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 2.0f, 3);
+  }
 }
 
 // BAL: a balanced call (balanced_split_pages), built apart so that the
@@ -183,8 +197,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
     qv[k] = (qwave && qhead < G) ? x : 0.0f;
   }
 
-  for (int e = tid; e < kWaves * NS * kBlocks * 4 * 4 * 16; e += 64 * kWaves)
-    (&sm.wl[0][0][0][0][0][0])[e] = 0u;   // the limb-3 rows stay zero
   if (qwave) {
     float v[kC];
 #pragma unroll
@@ -243,6 +255,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
                        static_cast<int>(x1[0]), static_cast<int>(x1[1]), static_cast<int>(x1[2]), static_cast<int>(x1[3])};
       sa[st][ls] = sm.qexp[head][g] - 4 * L + 127;
     }
+  // the PV weight tiles share the query limbs' LDS: once every wave has read
+  // its QK operands, each wave zeroes the limb-3 rows of its own tiles (the
+  // fourth row of each head, never written)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int t = 0; t < kBlocks * 2; ++t) sm.u.wb[wave][st][t >> 1][t & 1][3][g][n] = 0u;
 
   float m_run[NS], l_run[NS], acc[NS][kNT];
 #pragma unroll
@@ -252,9 +274,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[st][t] = 0.0f;
   }
-  const v4i zero4 = {0, 0, 0, 0};
   const v4f zero4f = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int wl_row = (lam * 4 + hs) * 16 + 4 * g;
+  // PV A operand: lane (g, r) is row r = (head r/4, limb r%4), tokens 4g..4g+3
+  // of the two pages of a pair
+  const int wb_row = (lam * 4 + hs) * 16 + 4 * g;
 
   auto compute = [&](const MxStep& sb, int p, auto mask_tag) {
     constexpr bool tail = decltype(mask_tag)::value;
@@ -275,7 +298,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
       }
     }
 
-    float alpha[NS], sw[NS][kBlocks];
+    float alpha[NS];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       float mc = lg[st][0];
@@ -293,66 +316,74 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
         psum += pp[i];
       }
       l_run[st] = __builtin_fmaf(l_run[st], alpha[st], psum);
+      // w = p * 2^(E - 128) of each block (E - 128 is the E8M0 byte with its
+      // top bit flipped, as a signed byte; the V operand is twice the E2M1
+      // value) as three bf16 limbs (each limb the rounding of what the ones
+      // before left: exact differences), two pages to a dword, into the
+      // wave's weight tiles
 #pragma unroll
       for (int gi = 0; gi < kBlocks; ++gi) {
-        // w = p * 2^(E - 128): the int8 V operand is twice the E2M1 value
-        float w[kStep], wmax = 0.0f;
+        float w[kStep];
 #pragma unroll
         for (int i = 0; i < kStep; ++i) {
-          const int e = static_cast<int>((sb.vs[i] >> (8 * gi)) & 0xFFu);
-          w[i] = ldexpf(pp[i], e - 128);
-          wmax = fmaxf(wmax, w[i]);
+          const int e = static_cast<int8_t>(((sb.vs[i] ^ 0x80808080u) >> (8 * gi)) & 0xFFu);
+          w[i] = ldexpf(pp[i], e);
         }
-        wmax = row_max16_nonneg(wmax);   // (w = p * 2^(E - 128) >= 0)
-        int ew = 0;
-        frexpf(wmax, &ew);
-        ew = ew < -100 ? -100 : ew;
-        const float wsc = ldexpf(1.0f, 22 - ew);
-        sw[st][gi] = ldexpf(1.0f, ew - 22);
-        uint32_t y[kStep];
 #pragma unroll
-        for (int i = 0; i < kStep; ++i)
-          y[i] = static_cast<uint32_t>(static_cast<int32_t>(rintf(w[i] * wsc)) + 0x8080);
-        const uint32_t l0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0602u),
-                                                  __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0602u), 0x05040100u);
-        const uint32_t l1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0501u),
-                                                  __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0501u), 0x05040100u) ^ 0x80808080u;
-        const uint32_t l2w = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0400u),
-                                                   __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0400u), 0x05040100u) ^ 0x80808080u;
-        uint32_t* wl = &sm.wl[wave][st][gi][0][0][0];
-        wl[(0 * 4 + g) * 16 + n] = l0;
-        wl[(1 * 4 + g) * 16 + n] = l1;
-        wl[(2 * 4 + g) * 16 + n] = l2w;
+        for (int m = 0; m < 2; ++m) {
+          const uint32_t h0 = bf16_pair(w[2 * m], w[2 * m + 1]);
+          const float r0 = w[2 * m] - bf16_lo(h0), r1 = w[2 * m + 1] - bf16_hi(h0);
+          const uint32_t h1 = bf16_pair(r0, r1);
+          const uint32_t h2 = bf16_pair(r0 - bf16_lo(h1), r1 - bf16_hi(h1));
+          uint32_t* wt = &sm.u.wb[wave][st][gi][m][0][0][0];
+          wt[(0 * 4 + g) * 16 + n] = h0;
+          wt[(1 * 4 + g) * 16 + n] = h1;
+          wt[(2 * 4 + g) * 16 + n] = h2;
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
-    v4i apv[NS][kBlocks];
+    bf16x8 apv[NS][kBlocks][2];
 #pragma unroll
     for (int st = 0; st < NS; ++st)
 #pragma unroll
       for (int gi = 0; gi < kBlocks; ++gi)
-        apv[st][gi] = *reinterpret_cast<const v4i*>(&sm.wl[wave][st][gi][0][0][0] + wl_row);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          apv[st][gi][m] = *reinterpret_cast<const bf16x8*>(&sm.u.wb[wave][st][gi][m][0][0][0] + wb_row);
 
-    // V: per token r of the lane group, the four pages' codes of one channel
-    // pair in a word (nibble tau is channel n + 16 tau)
-    uint32_t vt[4][4];
+    // V: for token r of the lane group and page pair m, the bytes of vp[m][r]
+    // hold one channel's codes of pages 2m (low nibble) and 2m+1 (high):
+    // channel pairs 2j (word 0) and 2j+1 (word 1) of byte j, nibble tau of a
+    // page's word being channel n + 16 tau
+    uint32_t vp[2][4][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) transpose_bytes4(sb.vx[0][r], sb.vx[1][r], sb.vx[2][r], sb.vx[3][r], vt[r]);
-#pragma unroll
-    for (int tau = 0; tau < kNT; ++tau) {
-      v4i bv;
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t nib = ((tau & 1) ? (vt[r][tau >> 1] >> 4) : vt[r][tau >> 1]) & kLowNibbles;
-        bv[r] = static_cast<int32_t>(e2m1x2_to_i8(nib));
+        const uint32_t x = sb.vx[2 * m][r], y = sb.vx[2 * m + 1][r];
+        vp[m][r][0] = (x & kLowNibbles) | ((y << 4) & ~kLowNibbles);
+        vp[m][r][1] = ((x >> 4) & kLowNibbles) | (y & ~kLowNibbles);
       }
+#pragma unroll
+    for (int tau = 0; tau < kNT; ++tau) {
+      // B operand of pair m: k = 8g + 2r + (page - 2m), column n (channel n + 16 tau)
+      bf16x8 bv[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bf16x2 two = e2m1_pair_bf16(vp[m][r][tau & 1], tau >> 1);
+          bv[m][2 * r] = two[0];
+          bv[m][2 * r + 1] = two[1];
+        }
       const int gi = tau >> 1;   // channels n + 16 tau lie in block tau / 2
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const v4i c = mfma_i8(apv[st][gi], bv, zero4);
-        const float f = __builtin_fmaf(static_cast<float>((c[0] << 8) + c[1]), 256.0f, static_cast<float>(c[2]));
-        acc[st][tau] = __builtin_fmaf(f, sw[st][gi], acc[st][tau] * alpha[st]);
+        v4f c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apv[st][gi][0], bv[0], zero4f, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apv[st][gi][1], bv[1], c, 0, 0, 0);
+        acc[st][tau] = __builtin_fmaf(acc[st][tau], alpha[st], (c[0] + c[1]) + c[2]);
       }
     }
   };
