@@ -396,12 +396,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mxfp4_kernel(DecodeArgs a)
   };
   if constexpr (NS == 1) {
     // Two step buffers: the next step's loads go out before this step is
-    // computed (the E2M1 conversions and per-block limbs make a step long
-    // enough that two waves per SIMD leave the loads idle otherwise; the
-    // registers still allow two waves).  Loads of a step past the range
-    // have empty descriptors, so each wait leaves the next step in flight.
-    // (A third buffer, two steps ahead at the same two waves, measured
-    // slower: 68 against 64 us.)
+    // computed, so the two waves per SIMD (all the 512-workgroup grid of a
+    // one-set decode fills; the registers still allow two) keep loads in
+    // flight while they compute.  Loads of a step past the range have empty
+    // descriptors, so each wait leaves the next step in flight.  (One
+    // buffer measured 55.3 against 53.2 us, a third one two steps ahead
+    // slower too.)
     MxStep buf1;
     for (int p = pw0; p < pw1; p += 2 * kStep) {
       load(buf1, p + kStep, idB);
