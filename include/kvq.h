@@ -423,7 +423,8 @@ kvq_status kvq_append_paged_int4g_hybrid(const kvq_int4g_cache* cache, const voi
  * are bit-exact functions of the input.  kvq_decode_attn_mxfp4 is
  * kvq_decode_attn over this pool (head_dim 128; same arguments, accuracy and
  * workspace size); its QK product runs on the block-scaled FP4 matrix
- * instruction of gfx950.
+ * instruction of gfx950, its PV product on the bf16 one (V converted by the
+ * FP4-to-bf16 instruction, exact).
  */
 kvq_status kvq_append_paged_mxfp4(const kvq_mxfp4_cache* cache, const void* k, const void* v,
                                   kvq_dtype dtype, int64_t token_stride,
