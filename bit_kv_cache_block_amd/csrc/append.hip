@@ -119,11 +119,15 @@ __device__ __forceinline__ QParams tok_params(float mn, float mx) {
 // is far below half an ulp of any nonzero fp16 zero point, and with a zero
 // zero point both forms are the rounded product.)  Otherwise x is already the
 // normalised y.
+template <bool EXACT_NORM>
+__device__ __forceinline__ float tok_scaled(float x, float sb, float zf, float inv) {
+  const float d = EXACT_NORM ? __builtin_fmaf(x, sb, -zf) : x - zf;
+  return d * inv;
+}
 template <int BITS, bool EXACT_NORM>
 __device__ __forceinline__ uint32_t tok_code(float x, float sb, float zf, float inv) {
   constexpr float kTop = BITS == 4 ? 15.0f : 255.0f;
-  const float d = EXACT_NORM ? __builtin_fmaf(x, sb, -zf) : x - zf;
-  const float q = d * inv;
+  const float q = tok_scaled<EXACT_NORM>(x, sb, zf, inv);
   return f2u(__builtin_amdgcn_fmed3f(q + 8388608.0f, 8388608.0f, 8388608.0f + kTop));
 }
 
@@ -496,15 +500,15 @@ void append_quant_kernel(AppendArgs a) {
         pend.words[m] = pack8_nibbles(c);
       }
     } else if (GS == 0 || kind == 0) {   // consecutive channels: K, or V of the token-wise pools
-      // The code of tok_code through v_cvt_pk_u8_f32, which rounds to nearest
-      // even, clamps to [0, 255] and writes one byte of a word: for 4-bit
-      // codes the value is first clamped to [0, 15] (clamping then rounding
-      // equals rounding then clamping there), the even-numbered codes go to
-      // the bytes of one word and the odd ones to another, joined as nibbles.
+      // tok_code's codes, rounded by v_cvt_pk_u8_f32 instead: it rounds to
+      // nearest even, clamps to [0, 255] and writes one byte of a word.
+      // 4-bit values are clamped to [0, 15] first (on that range clamping
+      // before rounding gives what clamping after does); the even-numbered
+      // codes fill the bytes of one word, the odd ones another, and the two
+      // words are joined as nibbles.
       auto qv = [&](int k) {
         const int gl = k / kGE;
-        const float d = kExactNorm ? __builtin_fmaf(x[k], sb, -zf[gl]) : x[k] - zf[gl];
-        const float q = d * inv[gl];
+        const float q = tok_scaled<kExactNorm>(x[k], sb, zf[gl], inv[gl]);
         return BITS == 4 ? __builtin_amdgcn_fmed3f(q, 0.0f, 15.0f) : q;
       };
 #pragma unroll
